@@ -1,0 +1,213 @@
+"""Pins for the oracle's whole step.
+
+* Batched equals serial, byte for byte (the Kestrel page, "0.8MB 跑通 Qwen"
+  14-1, section 3: batched outputs were identical to serial ones; section 1:
+  only the compute is merged, the per-request state stays separate).
+* Invariance to the order of sequences in a step and to the block-table
+  permutation (Go under the hood 20.3.2: paging is addressing only).
+* The layer's composition, through special weight sets that reduce it to
+  library routines (numpy float64 products) and to the separately pinned
+  pieces.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from continuous_batching_decode_forward_amd import configs, synth
+
+CFG = configs.TINY
+
+
+@pytest.fixture(scope="module")
+def tiny_model():
+    return O.Model(CFG, synth.make_weights(CFG, seed=0))
+
+
+def make_sequences(seed, n_seq=4, lo=5, hi=40):
+    lens = synth.uniform_ints(seed, "ctx", n_seq, lo, hi)
+    return [synth.uniform_ints(seed, f"prompt.{i}", int(lens[i]), 0, CFG.vocab - 1)
+            for i in range(n_seq)]
+
+
+def serial_run(model, prompt, n_decode):
+    """Serial ground truth: logits after the prompt, then after each greedy
+    token fed back, one token per forward."""
+    kv = model.dense_kv(len(prompt) + n_decode + 1)
+    out = [O.serial_forward(model, kv, prompt, 0, last_only=False)[-1]]
+    pos = len(prompt)
+    for _ in range(n_decode):
+        t = O.argmax_f64(out[-1])
+        out.append(O.serial_forward(model, kv, [t], pos))
+        pos += 1
+    return out
+
+
+def paged_run(model, prompts, n_decode, block_perm, chunk=None, order=None, bs=4, nb=64):
+    """The same sequences through paged-batched steps. The prompts are
+    prefilled in chunks of `chunk` rows (all sequences' chunks share a step),
+    then every sequence decodes one row per step. `order` permutes the
+    sequences inside every step."""
+    n = len(prompts)
+    order = list(range(n)) if order is None else list(order)
+    per_seq = nb // n
+    tables = np.full((n, per_seq), -1, np.int32)
+    for i in range(n):
+        tables[i] = block_perm[i * per_seq:(i + 1) * per_seq]
+    pool = model.paged_pool(nb, bs)
+    ctx = [0] * n
+    logits = [[] for _ in range(n)]
+    chunk = chunk or max(len(p) for p in prompts)
+    while any(ctx[i] < len(prompts[i]) for i in range(n)):
+        seqs = [i for i in order if ctx[i] < len(prompts[i])]
+        nn = [min(chunk, len(prompts[i]) - ctx[i]) for i in seqs]
+        toks = np.concatenate([prompts[i][ctx[i]:ctx[i] + k] for i, k in zip(seqs, nn)])
+        want = [int(ctx[i] + k == len(prompts[i])) for i, k in zip(seqs, nn)]
+        lg, _ = O.paged_step(model, pool, tables[seqs], [ctx[i] for i in seqs], nn, toks, want)
+        o = 0
+        for i, k, w in zip(seqs, nn, want):
+            ctx[i] += k
+            if w:
+                logits[i].append(lg[o])
+                o += 1
+    for _ in range(n_decode):
+        toks = [O.argmax_f64(logits[i][-1]) for i in order]
+        lg, g = O.paged_step(model, pool, tables[order], [ctx[i] for i in order], [1] * n,
+                             toks, [1] * n)
+        for o, i in enumerate(order):
+            logits[i].append(lg[o])
+            ctx[i] += 1
+    return logits
+
+
+def test_paged_batched_equals_serial_byte_for_byte(tiny_model):
+    prompts = make_sequences(0)
+    perm = synth.permutation(0, "blocks", 64)
+    paged = paged_run(tiny_model, prompts, 20, perm)
+    for i, p in enumerate(prompts):
+        ser = serial_run(tiny_model, p, 20)
+        assert len(ser) == len(paged[i]) == 21
+        for step, (a, b) in enumerate(zip(ser, paged[i])):
+            assert np.array_equal(a, b), f"seq {i} step {step}"
+
+
+def test_chunking_order_and_block_permutation_change_nothing(tiny_model):
+    prompts = make_sequences(1)
+    ref = paged_run(tiny_model, prompts, 6, synth.permutation(1, "blocks", 64))
+    alt = paged_run(tiny_model, prompts, 6, synth.permutation(2, "blocks", 64), chunk=7,
+                    order=[2, 0, 3, 1])
+    for i in range(len(prompts)):
+        for a, b in zip(ref[i], alt[i]):
+            assert np.array_equal(a, b)
+
+
+def test_paged_step_rejects_bad_metadata(tiny_model):
+    pool = tiny_model.paged_pool(8, 4)
+    table = np.array([[0, 1]], np.int32)
+    with pytest.raises(ValueError):      # ctx + n_new beyond the table
+        O.paged_step(tiny_model, pool, table, [6], [3], [1, 2, 3], [1])
+    with pytest.raises(ValueError):      # block id outside the pool
+        O.paged_step(tiny_model, pool, np.array([[0, 9]], np.int32), [4], [1], [1], [1])
+    with pytest.raises(ValueError):      # token outside the vocabulary
+        O.paged_step(tiny_model, pool, table, [0], [1], [CFG.vocab], [1])
+
+
+# --------------------------------------------------- layer composition pins
+
+def one_layer(seed, zero=()):
+    cfg = CFG.with_layers(1)
+    w = synth.make_weights(cfg, seed)
+    for k in zero:
+        w[k] = [torch.zeros_like(t) for t in w[k]]
+    return cfg, w
+
+
+def f64(t):
+    return O.bf16_to_f64(t).reshape(t.shape if hasattr(t, "shape") else -1)
+
+
+def test_zero_projections_make_the_layer_identity():
+    """W_o = 0 and W_down = 0: both residual branches add zero, so the logits
+    are the LM head applied to the final norm of the token's embedding."""
+    cfg, w = one_layer(3, zero=("w_o", "w_down"))
+    m = O.Model(cfg, w)
+    tok = 123
+    lg = O.serial_forward(m, m.dense_kv(4), [tok], 0)
+    h = O.rmsnorm(w["embed"][tok], w["final_norm"], cfg.rms_eps)
+    ref = O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ O.bf16_to_f64(h)
+    assert np.allclose(lg, ref, rtol=0, atol=1e-12)
+
+
+def test_ffn_branch_is_silu_gate_times_up_then_down():
+    """With W_o = 0 only the FFN branch changes x; compare the logits with the
+    branch built from numpy products and the pinned pieces. Swapping gate and
+    up, or dropping the residual, fails this."""
+    cfg, w = one_layer(4, zero=("w_o",))
+    m = O.Model(cfg, w)
+    tok = 77
+    lg = O.serial_forward(m, m.dense_kv(4), [tok], 0)
+    x = O.as_u16(w["embed"][tok])
+    h = O.rmsnorm(x, w["ffn_norm"][0], cfg.rms_eps)
+    g = O.linear(h, w["w_gate"][0])
+    u = O.linear(h, w["w_up"][0])
+    rb = np.vectorize(lambda v: O.bf16_to_float(O.f64_to_bf16(v)))
+    g, u = rb(g), rb(u)
+    a = rb(g / (1.0 + np.exp(-g)) * u)
+    a16 = np.array([O.f64_to_bf16(v) for v in a], np.uint16)
+    down = rb(O.linear(a16, w["w_down"][0]))
+    x2 = np.array([O.f64_to_bf16(v) for v in O.bf16_to_f64(x) + down], np.uint16)
+    hf = O.rmsnorm(x2, w["final_norm"], cfg.rms_eps)
+    ref = O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ O.bf16_to_f64(hf)
+    assert np.allclose(lg, ref, rtol=0, atol=1e-9)
+    # the swapped SwiGLU gives visibly different logits
+    a_sw = rb(u / (1.0 + np.exp(-u)) * g)
+    assert np.max(np.abs(a_sw - a)) > 1e-3
+
+
+def test_attention_branch_reads_the_cached_prefix():
+    """With W_gate = 0 the FFN adds silu(0)*u = 0. Feed two tokens: the second
+    token's attention must average over both positions; compare with the
+    dense brute-force attention over the K/V the first forward cached."""
+    cfg, w = one_layer(5, zero=("w_gate",))
+    m = O.Model(cfg, w)
+    kv = m.dense_kv(4)
+    toks = [11, 2222]
+    lg = O.serial_forward(m, kv, toks, 0, last_only=False)
+    x = O.as_u16(w["embed"][toks[1]])
+    h = O.rmsnorm(x, w["attn_norm"][0], cfg.rms_eps)
+    qkv = O.linear(h, w["w_qkv"][0])
+    hq, hkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    q = np.array([O.f64_to_bf16(v) for v in qkv[:hq * hd]], np.uint16)
+    q = np.concatenate([O.rope(q[i * hd:(i + 1) * hd], 1, cfg.rope_base) for i in range(hq)])
+    K = kv[0, 0, :2].copy()
+    V = kv[0, 1, :2].copy()
+    # the cached K of position 1 is this token's rotated k
+    k1 = np.array([O.f64_to_bf16(v) for v in qkv[hq * hd:(hq + hkv) * hd]], np.uint16)
+    k1 = np.concatenate([O.rope(k1[i * hd:(i + 1) * hd], 1, cfg.rope_base) for i in range(hkv)])
+    assert np.array_equal(K[1].reshape(-1), k1)
+    o = O.attention_dense(q, K, V, hq, hkv, hd)
+    t = O.linear(o, w["w_o"][0])
+    x2 = np.array([O.f64_to_bf16(a + O.bf16_to_float(O.f64_to_bf16(b)))
+                   for a, b in zip(O.bf16_to_f64(x), t)], np.uint16)
+    hf = O.rmsnorm(x2, w["final_norm"], cfg.rms_eps)
+    ref = O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ O.bf16_to_f64(hf)
+    assert np.allclose(lg[1], ref, rtol=0, atol=1e-9)
+
+
+def test_layers_apply_in_order_with_their_own_weights():
+    """A 2-layer model whose layer 1 (then layer 0) has zero output
+    projections equals the 1-layer model made of the other layer alone."""
+    cfg2 = CFG.with_layers(2)
+    w = synth.make_weights(cfg2, 6)
+    toks = [5, 900, 17]
+
+    def run(cfg, weights):
+        m = O.Model(cfg, weights)
+        return O.serial_forward(m, m.dense_kv(8), toks, 0, last_only=False)
+
+    for keep in (0, 1):
+        wz = {k: (list(v) if isinstance(v, list) else v) for k, v in w.items()}
+        for k in ("w_o", "w_down"):
+            wz[k][1 - keep] = torch.zeros_like(wz[k][1 - keep])
+        w1 = {k: ([v[keep]] if isinstance(v, list) else v) for k, v in w.items()}
+        assert np.array_equal(run(cfg2, wz), run(CFG.with_layers(1), w1))
