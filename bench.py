@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of one continuous-batching decode step on one MI355X.
+
+Workload (default): one 8B-shaped decoder layer + LM head (d_model 4096,
+32/8 heads, head_dim 128, FFN 14336, vocab 128256), bf16 random-init weights
+~N(0, 0.02), B decode rows with contexts uniform in 512..4096 held as
+synthetic N(0,1) bf16 KV in 32-position blocks through shuffled block
+tables, greedy argmax. A step is one cbd_step_forward over all B rows with
+every input already in HBM. The headline is B = 64; B in {1, 8, 32, 64} is
+also reported.
+
+Prints one JSON line: decode tokens/s, ms per step, achieved HBM GB/s under
+the (W + B*A)/beta cost model, the dominant kernel's roofline (timed with HIP
+events on the step's stream during the timed steps), and the CPU oracle timed
+on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_pos(shape):
+    return 2 * shape.n_kv_heads * shape.head_dim * 2 * shape.n_layers
+
+
+def step_bytes(shape, ctx, n_out):
+    """Algorithmic HBM bytes of one decode step: every weight once, the
+    embedding rows, each row's cached KV (ctx + 1 positions read, one
+    appended) and the fp32 logits written."""
+    from continuous_batching_decode_forward_amd import synth
+    W = synth.weight_bytes(shape) + len(ctx) * shape.d_model * 2
+    kvb = kv_bytes_per_pos(shape)
+    A = sum((int(c) + 1) * kvb + kvb for c in ctx)
+    return W + A + n_out * shape.vocab * 4
+
+
+def lm_head_bytes(shape, n_out):
+    return shape.vocab * shape.d_model * 2 + n_out * shape.d_model * 2 + n_out * shape.vocab * 4
+
+
+def build_workload(shape, B, seed, device="cuda"):
+    import torch
+    from continuous_batching_decode_forward_amd import synth
+    bs = 32
+    ctx = synth.uniform_ints(seed, "ctx", B, 512, 4096)
+    need = [-(-(int(c) + 1) // bs) for c in ctx]
+    total = int(sum(need))
+    perm = synth.permutation(seed, "blocks", total)
+    mbps = -(-4097 // bs)
+    tables = np.full((B, mbps), -1, np.int32)
+    o = 0
+    for i in range(B):
+        tables[i, :need[i]] = perm[o:o + need[i]]
+        o += need[i]
+    tokens = synth.uniform_ints(seed, "tok", B, 0, shape.vocab - 1)
+    return dict(bs=bs, ctx=ctx, tables=tables, perm=perm, total=total, mbps=mbps,
+                tokens=tokens)
+
+
+def fill_pool(eng, seed, blocks):
+    import torch
+    from continuous_batching_decode_forward_amd import synth
+    s = eng.shape
+    bs, hkv, hd = eng.block_size, s.n_kv_heads, s.head_dim
+    dev = eng.kv_pool.device
+    blocks = torch.as_tensor(np.asarray(blocks, np.int64), device=dev)
+    kh = torch.arange(hkv, device=dev)
+    off = torch.arange(bs, device=dev)
+    dim = torch.arange(hd, device=dev)
+    for layer in range(s.n_layers):
+        k, v = eng.kv_views(layer)
+        for c0 in range(0, len(blocks), 2048):
+            b = blocks[c0:c0 + 2048]
+            k[b] = synth.kv_values(seed, layer, 0, b.view(-1, 1, 1, 1), kh.view(1, -1, 1, 1),
+                                   off.view(1, 1, -1, 1), dim.view(1, 1, 1, -1), hkv, bs, hd)
+            v[b] = synth.kv_values(seed, layer, 1, b.view(-1, 1, 1, 1), kh.view(1, -1, 1, 1),
+                                   off.view(1, 1, 1, -1), dim.view(1, 1, -1, 1), hkv, bs, hd)
+
+
+def time_steps(eng, meta, lg, tk, steps, warmup, stream, profile_class=None):
+    import torch
+    from continuous_batching_decode_forward_amd import binding as B
+    for _ in range(warmup):
+        eng.step_forward(meta, lg, tk, stream)
+    torch.cuda.synchronize()
+    if profile_class is not None:
+        B.cbd_profile_begin(eng.handle, profile_class)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eng.step_forward(meta, lg, tk, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / steps
+    kern = None
+    if profile_class is not None:
+        tot, n = B.cbd_profile_end(eng.handle)
+        kern = (tot / max(n, 1), n)
+    return ms, wall, kern
+
+
+def cpu_baseline(shape, wg, wl, seed, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same step: decode
+    rows of the B=64 workload, one at a time, until about budget_s seconds of
+    CPU work."""
+    import torch
+    import oracle as O
+    from continuous_batching_decode_forward_amd import synth
+    wc = {k: ([t.cpu() for t in v] if isinstance(v, list) else v.cpu()) for k, v in wg.items()}
+    om = O.Model(shape, wc)
+    bs, hkv, hd = wl["bs"], shape.n_kv_heads, shape.head_dim
+    done, spent = 0, 0.0
+    for i in range(len(wl["ctx"])):
+        c = int(wl["ctx"][i])
+        nb = -(-(c + 1) // bs)
+        pool = np.zeros((shape.n_layers, 2, nb, bs, hkv, hd), np.uint16)
+        ncached = -(-c // bs)
+        phys = torch.as_tensor(wl["tables"][i, :ncached].astype(np.int64))
+        for layer in range(shape.n_layers):
+            for kind in (0, 1):
+                vals = synth.kv_values(seed, layer, kind, phys.view(-1, 1, 1, 1),
+                                       torch.arange(hkv).view(1, 1, -1, 1),
+                                       torch.arange(bs).view(1, -1, 1, 1),
+                                       torch.arange(hd).view(1, 1, 1, -1), hkv, bs, hd)
+                pool[layer, kind, :ncached] = O.as_u16(vals).reshape(ncached, bs, hkv, hd)
+        table = np.arange(nb, dtype=np.int32).reshape(1, nb)
+        t0 = time.perf_counter()
+        O.paged_step(om, pool, table, [c], [1], [int(wl["tokens"][i])], [1])
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": done / spent, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{done} decode rows of the B=64 step (8B layer + LM head, contexts "
+                      f"U[512,4096]), each alone through the oracle's paged step; "
+                      f"{spent:.1f} s of CPU work"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--sweep", default="1,8,32,64")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the step runs on a single MI355X and this "
+              "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from continuous_batching_decode_forward_amd import binding as B
+    from continuous_batching_decode_forward_amd import configs, synth
+    from continuous_batching_decode_forward_amd.engine import Engine
+
+    shape = configs.LLAMA8B_1L
+    seed = 0
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] weights {shape.name} on GPU")
+    wg = synth.make_weights(shape, seed=seed, device="cuda")
+    Bmax = max([args.batch] + [int(b) for b in args.sweep.split(",") if b])
+    wl = build_workload(shape, Bmax, seed)
+    eng = Engine(shape, wg, block_size=wl["bs"], num_blocks=wl["total"],
+                 max_blocks_per_seq=wl["mbps"], max_slots=Bmax, max_rows=Bmax, max_seqs=Bmax,
+                 max_position=4097)
+    log(f"[bench] filling {wl['total']} KV blocks")
+    fill_pool(eng, seed, wl["perm"])
+    torch.cuda.synchronize()
+
+    def run(Bn, steps, warmup, profile_class=None):
+        meta = eng.upload_step(slots=list(range(Bn)), block_tables=wl["tables"][:Bn],
+                               ctx_lens=wl["ctx"][:Bn], n_new=[1] * Bn,
+                               tokens=wl["tokens"][:Bn], want_token=[1] * Bn)
+        lg = torch.empty((Bn, shape.vocab), dtype=torch.float32, device="cuda")
+        tk = torch.empty(Bn, dtype=torch.int32, device="cuda")
+        ms, wall, kern = time_steps(eng, meta, lg, tk, steps, warmup, stream, profile_class)
+        st = eng.status()
+        if st:
+            raise RuntimeError(f"device status {st:#x}")
+        byts = step_bytes(shape, wl["ctx"][:Bn], Bn)
+        return ms, wall, kern, byts
+
+    sweep = []
+    for b in [int(x) for x in args.sweep.split(",") if x]:
+        if b == args.batch:
+            continue
+        ms, wall, _, byts = run(b, max(10, args.steps // 2), args.warmup)
+        gbs = byts / (ms * 1e-3) / 1e9
+        sweep.append({"batch": b, "tokens_per_s": b / (ms * 1e-3), "ms_per_step": ms,
+                      "hbm_gbs": gbs, "roofline_frac": gbs / PEAK_HBM_GBS})
+        log(f"[bench] B={b}: {ms:.3f} ms/step, {b / (ms * 1e-3):.0f} tok/s, {gbs:.0f} GB/s")
+
+    Bn = args.batch
+    log(f"[bench] timed: B={Bn}, {args.warmup} warmup + {args.steps} steps")
+    ms, wall, kern, byts = run(Bn, args.steps, args.warmup, profile_class=B.CBD_KERNEL_LM_HEAD)
+    tokps = Bn / (ms * 1e-3)
+    gbs = byts / (ms * 1e-3) / 1e9
+    sweep.append({"batch": Bn, "tokens_per_s": tokps, "ms_per_step": ms, "hbm_gbs": gbs,
+                  "roofline_frac": gbs / PEAK_HBM_GBS})
+    sweep.sort(key=lambda r: r["batch"])
+    lm_ms, lm_n = kern
+    lm_bytes = lm_head_bytes(shape, Bn)
+    lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
+    log(f"[bench] B={Bn}: {ms:.3f} ms/step ({wall / args.steps * 1e3:.3f} ms wall), "
+        f"{tokps:.0f} tok/s, {gbs:.0f} GB/s; LM head {lm_ms * 1e3:.1f} us, {lm_gbs:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(shape, wg, wl, seed, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "decode tokens/s per step and HBM GB/s vs (W+B*A)/beta roofline, 8B-shape, 1 GPU",
+        "value": tokps,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "8b-layer+lmhead-decode", "batch": Bn, "ctx_range": [512, 4096],
+                   "block_size": 32, "greedy": True, "d_model": 4096, "n_heads": 32,
+                   "n_kv_heads": 8, "head_dim": 128, "ffn_dim": 14336, "vocab": 128256,
+                   "n_layers": 1},
+        "hbm_gbs": gbs,
+        "step_algorithmic_bytes": byts,
+        "step_roofline_frac": gbs / PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "kernel": "lm_head_gemm", "achieved": lm_gbs,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": lm_gbs / PEAK_HBM_GBS,
+                     "traffic": None, "avg_launch_us": lm_ms * 1e3, "launches": lm_n,
+                     "bytes_per_launch": lm_bytes},
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    eng.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

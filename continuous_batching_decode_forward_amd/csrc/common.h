@@ -1,0 +1,68 @@
+// common.h -- device helpers shared by the gfx950 kernels of the step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#define CBD_WAVE 64
+
+// bf16 <-> fp32. bf16 is the top half of a binary32; the narrowing rounds to
+// nearest even (NaN kept quiet).
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }
+
+// Two bf16 packed in a uint32 (low half first).
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// 16-byte load that asks the memory system not to keep the line (weights
+// are streamed once per step).
+__device__ __forceinline__ uint4 load_stream16(const uint16_t* p) {
+  u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ floatx4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Wave-wide reductions over 64 lanes (xor butterfly, fixed order).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, CBD_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, CBD_WAVE));
+  return v;
+}
+
+// Device status bits (same values as CBD_STATUS_* in cbd.h).
+#define ST_BAD_BLOCK 0x1u
+#define ST_BAD_TOKEN 0x2u
+#define ST_BAD_SLOT 0x4u
+#define ST_BAD_SHAPE 0x8u
+
+__device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bit) {
+  atomicOr(status, bit);
+}

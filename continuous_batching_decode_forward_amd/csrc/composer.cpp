@@ -1,0 +1,358 @@
+// composer.cpp -- the host step composer (Forma's "Scheduler", Go under the
+// hood section 20.3.2), plus the library's error reporting.
+//
+// Each plan: admit what the policy allows, then compose the step:
+//  1. prefill chunks of sequences that have no first token yet, in arrival
+//     order, each min(chunk_size, remaining prompt, remaining row budget);
+//  2. one row per decoding sequence while rows remain; sequences that have
+//     waited longest for a row go first (ties by ascending slot), so a row
+//     that does not fit waits one step and is then served -- nothing is ever
+//     evicted.
+// Admission under CBD_ADMIT_RESERVE takes ceil((prompt + max_new) / block)
+// blocks up front, which guarantees that every admitted request can finish
+// (the deadlock the section describes -- all slots busy, pool empty, nobody
+// can grow -- cannot arise). CBD_ADMIT_FREE_SLOT admits on a free slot and
+// takes blocks as rows first write into them, and can stall.
+// CBD_ADMIT_REQUEST_LEVEL admits a new group only once the batch is empty.
+#include <string.h>
+
+#include <algorithm>
+#include <deque>
+#include <list>
+#include <map>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "runtime.h"
+
+namespace cbd {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+}  // namespace cbd
+
+using namespace cbd;
+
+namespace {
+
+struct Request {
+  uint64_t id = 0;
+  std::vector<int32_t> prompt;
+  int32_t max_new = 0;
+  cbd_sampling sp{};
+  bool has_sp = false;
+  int32_t slot = -1;
+  std::vector<int32_t> blocks;
+  int32_t ctx = 0;        // positions cached
+  int32_t prefilled = 0;  // prompt tokens cached
+  std::vector<int32_t> generated;
+  int64_t last_row_step = -1;
+};
+
+struct Finished {
+  uint64_t id;
+  int32_t reason;
+  int32_t n_generated;
+};
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+}  // namespace
+
+struct cbd_sched {
+  cbd_sched_config cfg{};
+  cbd_engine* engine = nullptr;
+  SlotAllocator own_slots;
+  BlockAllocator own_blocks;
+  std::deque<std::unique_ptr<Request>> queue;
+  std::map<int32_t, std::unique_ptr<Request>> active;  // by slot
+  std::vector<Request*> order;                         // admitted, arrival order
+  std::deque<Finished> finished;
+  int64_t steps = 0, n_finished = 0;
+  bool planned = false;
+  // the last plan
+  std::vector<int32_t> p_slots, p_tables, p_ctx, p_new, p_tokens, p_want, p_step;
+  std::vector<uint64_t> p_ids;
+  std::vector<Request*> p_reqs;
+
+  int32_t blocks_available() const {
+    return engine ? cbd_blocks_available(engine) : own_blocks.available();
+  }
+  int32_t slots_free() const {
+    if (!engine) return own_slots.n_free();
+    return engine->slots.n_free();
+  }
+  bool take_blocks(int32_t n, std::vector<int32_t>& into) {
+    if (n <= 0) return true;
+    size_t at = into.size();
+    into.resize(at + (size_t)n);
+    bool ok = engine ? cbd_block_alloc(engine, n, into.data() + at) == CBD_OK
+                     : own_blocks.alloc(n, into.data() + at);
+    if (!ok) into.resize(at);
+    return ok;
+  }
+  void give_blocks(std::vector<int32_t>& b) {
+    if (b.empty()) return;
+    if (engine)
+      cbd_block_free(engine, (int32_t)b.size(), b.data());
+    else
+      own_blocks.release((int32_t)b.size(), b.data());
+    b.clear();
+  }
+  int32_t take_slot(const Request& r) {
+    if (!engine) return own_slots.alloc();
+    int32_t s = -1;
+    const cbd_sampling* p = r.has_sp ? &r.sp : nullptr;
+    return cbd_slot_alloc(engine, p, r.id, &s) == CBD_OK ? s : -1;
+  }
+  void give_slot(int32_t s) {
+    if (engine)
+      cbd_slot_free(engine, s);
+    else
+      own_slots.release(s);
+  }
+
+  void retire(Request* r, int32_t reason) {
+    give_blocks(r->blocks);
+    give_slot(r->slot);
+    finished.push_back({r->id, reason, (int32_t)r->generated.size()});
+    ++n_finished;
+    order.erase(std::find(order.begin(), order.end(), r));
+    active.erase(r->slot);  // destroys r
+  }
+
+  void admit() {
+    if (cfg.policy == CBD_ADMIT_REQUEST_LEVEL && !active.empty()) return;
+    while (!queue.empty() && slots_free() > 0) {
+      Request& r = *queue.front();
+      std::vector<int32_t> blocks;
+      if (cfg.policy != CBD_ADMIT_FREE_SLOT) {
+        int32_t need = ceil_div((int64_t)r.prompt.size() + r.max_new, cfg.block_size);
+        if (blocks_available() < need || !take_blocks(need, blocks)) break;
+      }
+      int32_t slot = take_slot(r);
+      if (slot < 0) {
+        give_blocks(blocks);
+        break;
+      }
+      std::unique_ptr<Request> up = std::move(queue.front());
+      queue.pop_front();
+      up->slot = slot;
+      up->blocks = std::move(blocks);
+      order.push_back(up.get());
+      active[slot] = std::move(up);
+    }
+  }
+
+  // Free-slot-only policy: make r hold blocks for n_pos positions.
+  bool grow(Request& r, int64_t n_pos) {
+    int32_t need = ceil_div(n_pos, cfg.block_size) - (int32_t)r.blocks.size();
+    if (need <= 0) return true;
+    if (blocks_available() < need) return false;
+    return take_blocks(need, r.blocks);
+  }
+
+  void emit(Request& r, const int32_t* toks, int32_t n, bool want) {
+    r.last_row_step = steps;
+    p_slots.push_back(r.slot);
+    size_t at = p_tables.size();
+    p_tables.resize(at + (size_t)cfg.max_blocks_per_seq, -1);
+    std::copy(r.blocks.begin(), r.blocks.end(), p_tables.begin() + (ptrdiff_t)at);
+    p_ctx.push_back(r.ctx);
+    p_new.push_back(n);
+    p_tokens.insert(p_tokens.end(), toks, toks + n);
+    p_want.push_back(want ? 1 : 0);
+    p_step.push_back((int32_t)r.generated.size());
+    p_ids.push_back(r.id);
+    p_reqs.push_back(&r);
+  }
+};
+
+extern "C" {
+
+int cbd_sched_create(const cbd_sched_config* cfg, cbd_engine* engine, const int32_t* block_order,
+                     cbd_sched** out) {
+  if (!cfg || !out) return fail(CBD_E_INVAL, "NULL config or output");
+  if (cfg->max_slots < 1 || cfg->block_size < 1 || cfg->num_blocks < 1 ||
+      cfg->max_blocks_per_seq < 1 || cfg->max_rows < 1 || cfg->chunk_size < 1 ||
+      cfg->policy < CBD_ADMIT_RESERVE || cfg->policy > CBD_ADMIT_REQUEST_LEVEL)
+    return fail(CBD_E_INVAL, "composer config out of range");
+  if (engine && (engine->cfg.block_size != cfg->block_size ||
+                 engine->cfg.num_blocks != cfg->num_blocks ||
+                 engine->cfg.max_slots < cfg->max_slots ||
+                 engine->cfg.max_blocks_per_seq < cfg->max_blocks_per_seq ||
+                 engine->cfg.max_rows < cfg->max_rows))
+    return fail(CBD_E_INVAL, "composer config does not match the engine");
+  std::unique_ptr<cbd_sched> s(new cbd_sched());
+  s->cfg = *cfg;
+  s->engine = engine;
+  if (!engine) {
+    s->own_slots.reset(cfg->max_slots);
+    if (!s->own_blocks.reset(cfg->num_blocks, block_order))
+      return fail(CBD_E_INVAL, "block_order is not a permutation of 0..num_blocks-1");
+  }
+  *out = s.release();
+  return CBD_OK;
+}
+
+int cbd_sched_destroy(cbd_sched* s) {
+  if (!s) return fail(CBD_E_INVAL, "composer is NULL");
+  while (!s->order.empty()) s->retire(s->order.front(), CBD_FINISH_ABORT);
+  delete s;
+  return CBD_OK;
+}
+
+int cbd_sched_submit(cbd_sched* s, const int32_t* prompt, int32_t prompt_len, int32_t max_new,
+                     const cbd_sampling* params, uint64_t request_id) {
+  if (!s || !prompt || prompt_len < 1 || max_new < 1)
+    return fail(CBD_E_INVAL, "empty prompt or max_new < 1");
+  int32_t need = ceil_div((int64_t)prompt_len + max_new, s->cfg.block_size);
+  if (need > s->cfg.max_blocks_per_seq || need > s->cfg.num_blocks)
+    return fail(CBD_E_INVAL, "prompt + answer can never fit a sequence's block table or the pool");
+  std::unique_ptr<Request> r(new Request());
+  r->id = request_id;
+  r->prompt.assign(prompt, prompt + prompt_len);
+  r->max_new = max_new;
+  if (params) {
+    r->sp = *params;
+    r->has_sp = true;
+  }
+  s->queue.push_back(std::move(r));
+  return CBD_OK;
+}
+
+int cbd_sched_plan(cbd_sched* s, cbd_plan* out) {
+  if (!s || !out) return fail(CBD_E_INVAL, "NULL composer or output");
+  s->admit();
+  s->p_slots.clear(); s->p_tables.clear(); s->p_ctx.clear(); s->p_new.clear();
+  s->p_tokens.clear(); s->p_want.clear(); s->p_step.clear(); s->p_ids.clear();
+  s->p_reqs.clear();
+  int32_t budget = s->cfg.max_rows, n_prefill = 0, n_decode = 0;
+  for (Request* r : s->order) {  // prefill chunks first, arrival order
+    if (budget <= 0) break;
+    const int32_t left = (int32_t)r->prompt.size() - r->prefilled;
+    if (left <= 0) continue;
+    const int32_t n = std::min({s->cfg.chunk_size, left, budget});
+    if (s->cfg.policy == CBD_ADMIT_FREE_SLOT && !s->grow(*r, (int64_t)r->ctx + n)) continue;
+    s->emit(*r, r->prompt.data() + r->prefilled, n, n == left);
+    budget -= n;
+    n_prefill += n;
+  }
+  std::vector<Request*> dec;
+  for (auto& kv : s->active)
+    if (kv.second->prefilled >= (int32_t)kv.second->prompt.size()) dec.push_back(kv.second.get());
+  std::stable_sort(dec.begin(), dec.end(), [](const Request* a, const Request* b) {
+    if (a->last_row_step != b->last_row_step) return a->last_row_step < b->last_row_step;
+    return a->slot < b->slot;
+  });
+  for (Request* r : dec) {  // then one row per decoding sequence
+    if (budget <= 0) break;
+    if (s->cfg.policy == CBD_ADMIT_FREE_SLOT && !s->grow(*r, (int64_t)r->ctx + 1)) continue;
+    s->emit(*r, &r->generated.back(), 1, true);
+    budget -= 1;
+    ++n_decode;
+  }
+  out->n_seqs = (int32_t)s->p_slots.size();
+  out->n_rows = (int32_t)s->p_tokens.size();
+  out->n_out = 0;
+  out->max_ctx = 0;
+  for (size_t i = 0; i < s->p_slots.size(); ++i) {
+    out->n_out += s->p_want[i];
+    out->max_ctx = std::max(out->max_ctx, s->p_ctx[i] + s->p_new[i]);
+  }
+  out->max_blocks_per_seq = s->cfg.max_blocks_per_seq;
+  out->n_prefill_rows = n_prefill;
+  out->n_decode_rows = n_decode;
+  out->stalled = (out->n_rows == 0 && !s->active.empty()) ? 1 : 0;
+  out->slots = s->p_slots.data();
+  out->block_tables = s->p_tables.data();
+  out->ctx_lens = s->p_ctx.data();
+  out->n_new = s->p_new.data();
+  out->tokens = s->p_tokens.data();
+  out->want_token = s->p_want.data();
+  out->step_ids = s->p_step.data();
+  out->request_ids = s->p_ids.data();
+  s->planned = true;
+  return CBD_OK;
+}
+
+int cbd_sched_commit(cbd_sched* s, const int32_t* tokens, int32_t n) {
+  if (!s) return fail(CBD_E_INVAL, "composer is NULL");
+  if (!s->planned) return fail(CBD_E_INVAL, "commit without a plan");
+  int32_t want = 0;
+  for (int32_t w : s->p_want) want += w;
+  if (n != want || (n > 0 && !tokens)) return fail(CBD_E_INVAL, "token count does not match the plan");
+  std::vector<std::pair<Request*, int32_t>> retire;
+  int32_t o = 0;
+  for (size_t i = 0; i < s->p_reqs.size(); ++i) {
+    Request* r = s->p_reqs[i];
+    r->ctx += s->p_new[i];
+    if (r->prefilled < (int32_t)r->prompt.size()) r->prefilled += s->p_new[i];
+    if (s->p_want[i]) {
+      int32_t t = tokens[o++];
+      r->generated.push_back(t);
+      if (t == s->cfg.eos_id)
+        retire.push_back({r, CBD_FINISH_EOS});
+      else if ((int32_t)r->generated.size() >= r->max_new)
+        retire.push_back({r, CBD_FINISH_LENGTH});
+    }
+  }
+  for (auto& pr : retire) s->retire(pr.first, pr.second);
+  s->p_reqs.clear();
+  s->planned = false;
+  ++s->steps;
+  return CBD_OK;
+}
+
+int cbd_sched_abort(cbd_sched* s, uint64_t request_id) {
+  if (!s) return fail(CBD_E_INVAL, "composer is NULL");
+  if (s->planned) return fail(CBD_E_INVAL, "abort between plan and commit");
+  for (Request* r : s->order)
+    if (r->id == request_id) {
+      s->retire(r, CBD_FINISH_ABORT);
+      return CBD_OK;
+    }
+  for (auto it = s->queue.begin(); it != s->queue.end(); ++it)
+    if ((*it)->id == request_id) {
+      s->finished.push_back({request_id, CBD_FINISH_ABORT, 0});
+      ++s->n_finished;
+      s->queue.erase(it);
+      return CBD_OK;
+    }
+  return fail(CBD_E_INVAL, "unknown request id");
+}
+
+int cbd_sched_pop_finished(cbd_sched* s, uint64_t* request_id, int32_t* reason,
+                           int32_t* n_generated) {
+  if (!s || !request_id || !reason || !n_generated) return fail(CBD_E_INVAL, "NULL argument");
+  if (s->finished.empty()) return 0;
+  Finished f = s->finished.front();
+  s->finished.pop_front();
+  *request_id = f.id;
+  *reason = f.reason;
+  *n_generated = f.n_generated;
+  return 1;
+}
+
+int cbd_sched_stats_get(const cbd_sched* s, cbd_sched_stats* out) {
+  if (!s || !out) return fail(CBD_E_INVAL, "NULL argument");
+  out->queued = (int32_t)s->queue.size();
+  out->active = (int32_t)s->active.size();
+  out->free_slots = s->slots_free();
+  out->free_blocks = s->blocks_available();
+  out->steps = s->steps;
+  out->finished = s->n_finished;
+  return CBD_OK;
+}
+
+const char* cbd_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

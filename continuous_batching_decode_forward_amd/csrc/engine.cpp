@@ -1,0 +1,467 @@
+// engine.cpp -- configuration checks, buffer layouts, engine lifecycle, slot
+// and block allocation, and the per-step launch sequence.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "runtime.h"
+
+namespace cbd {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int validate_config(const cbd_config* c) {
+  if (!c) return fail(CBD_E_INVAL, "config is NULL");
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 1 || c->ffn_dim < 1 || c->vocab < 2 || c->block_size < 1 ||
+      c->num_blocks < 1 || c->max_blocks_per_seq < 1 || c->max_slots < 1 || c->max_rows < 1 ||
+      c->max_seqs < 1 || c->max_position < 1 || !(c->rms_eps > 0.f) || !(c->rope_base > 1.0))
+    return fail(CBD_E_INVAL, "config has a non-positive size or parameter");
+  if (c->n_heads % c->n_kv_heads)
+    return fail(CBD_E_INVAL, "n_heads must be a multiple of n_kv_heads");
+  const int G = c->n_heads / c->n_kv_heads;
+  if (16 % G)
+    return fail(CBD_E_UNSUPPORTED, "query heads per KV head must divide 16 (1, 2, 4, 8, 16)");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(CBD_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->block_size != 4 && c->block_size != 8 && c->block_size != 16 && c->block_size != 32 &&
+      c->block_size != 64)
+    return fail(CBD_E_UNSUPPORTED, "block_size must be 4, 8, 16, 32 or 64");
+  if (c->d_model % 16 || c->ffn_dim % 16 || c->vocab % 16)
+    return fail(CBD_E_UNSUPPORTED, "d_model, ffn_dim and vocab must be multiples of 16");
+  if (c->d_model > 8192) return fail(CBD_E_UNSUPPORTED, "d_model above 8192");
+  if (c->max_seqs > c->max_rows) return fail(CBD_E_INVAL, "max_seqs exceeds max_rows");
+  return CBD_OK;
+}
+
+static int32_t attn_cap_splits(const cbd_config& c) {
+  int32_t s = (c.max_position + 127) / 128;
+  return std::max(1, std::min(64, s));
+}
+
+WorkspaceLayout workspace_layout(const cbd_config& c) {
+  WorkspaceLayout L;
+  const size_t R = (size_t)c.max_rows, S = (size_t)c.max_seqs;
+  const size_t d = (size_t)c.d_model, hd = (size_t)c.head_dim;
+  const size_t qkv_n = (size_t)(c.n_heads + 2 * c.n_kv_heads) * hd;
+  const size_t qd = (size_t)c.n_heads * hd;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.status = take(sizeof(uint32_t));
+  L.row_seq = take(R * 4);
+  L.row_pos = take(R * 4);
+  L.seq_row0 = take(S * 4);
+  L.out_row = take(R * 4);
+  L.out_seq = take(R * 4);
+  L.item0 = take((S + 1) * 4);
+  L.x = take(R * d * 2);
+  L.h = take(R * d * 2);
+  L.qkv = take(R * qkv_n * 2);
+  L.q = take(R * qd * 2);
+  L.attn = take(R * qd * 2);
+  L.ffn = take(R * (size_t)c.ffn_dim * 2);
+  L.lm_in = take(S * d * 2);
+  L.logits = take(S * (size_t)c.vocab * 4);
+  L.amax_stride = (c.vocab + 15) / 16;
+  L.amax_val = take(S * (size_t)L.amax_stride * 4);
+  L.amax_idx = take(S * (size_t)L.amax_stride * 4);
+  size_t maxn = std::max({(size_t)2 * c.ffn_dim, qkv_n, d});
+  L.gemm_part_floats = std::max<size_t>((size_t)16 << 20, 4 * R * maxn);
+  L.gemm_part = take(L.gemm_part_floats * 4);
+  L.attn_max_splits = attn_cap_splits(c);
+  const size_t cols = R * (size_t)c.n_heads * (size_t)L.attn_max_splits;
+  L.attn_ml = take(cols * 2 * 4);
+  L.attn_o = take(cols * hd * 4);
+  L.rope = take((size_t)c.max_position * (hd / 2) * 8);
+  L.smp = take(S * (size_t)sampler_row_floats(c.vocab) * 4);
+  L.total = o;
+  return L;
+}
+
+SlotLayout slot_layout(const cbd_config& c) {
+  SlotLayout L;
+  L.params = 0;
+  L.counts = align256((size_t)c.max_slots * sizeof(SlotParams));
+  L.total = L.counts + align256((size_t)c.max_slots * (size_t)c.vocab * 4);
+  return L;
+}
+
+size_t kv_pool_bytes(const cbd_config& c) {
+  return (size_t)c.n_layers * 2 * (size_t)c.num_blocks * (size_t)c.n_kv_heads *
+         (size_t)c.block_size * (size_t)c.head_dim * 2;
+}
+
+}  // namespace cbd
+
+using namespace cbd;
+
+uint16_t* cbd_engine::pool_k(int layer) const {
+  size_t region = (size_t)cfg.num_blocks * cfg.n_kv_heads * cfg.block_size * cfg.head_dim;
+  return reinterpret_cast<uint16_t*>(kv_pool) + (size_t)layer * 2 * region;
+}
+
+uint16_t* cbd_engine::pool_v(int layer) const {
+  size_t region = (size_t)cfg.num_blocks * cfg.n_kv_heads * cfg.block_size * cfg.head_dim;
+  return reinterpret_cast<uint16_t*>(kv_pool) + ((size_t)layer * 2 + 1) * region;
+}
+
+cbd_engine::~cbd_engine() {
+  for (hipEvent_t ev : prof_events) (void)hipEventDestroy(ev);
+}
+
+// Record one event of a start/stop pair when `cls` is being profiled.
+hipError_t cbd_engine::prof_mark(int32_t cls, hipStream_t st) {
+  if (cls != prof_class || prof_class == 0) return hipSuccess;
+  if (prof_used >= 2 * 65536) return hipSuccess;
+  if (prof_used == prof_events.size()) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return e;
+    prof_events.push_back(ev);
+  }
+  return hipEventRecord(prof_events[prof_used++], st);
+}
+
+#define HIP_TRY(expr)                                                        \
+  do {                                                                       \
+    hipError_t e_ = (expr);                                                  \
+    if (e_ != hipSuccess)                                                    \
+      return fail(CBD_E_DEVICE, std::string(#expr ": ") + hipGetErrorString(e_)); \
+  } while (0)
+
+extern "C" {
+
+int cbd_kv_pool_bytes(const cbd_config* cfg, size_t* bytes) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(CBD_E_INVAL, "bytes is NULL");
+  *bytes = kv_pool_bytes(*cfg);
+  return CBD_OK;
+}
+
+int cbd_slot_state_bytes(const cbd_config* cfg, size_t* bytes) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(CBD_E_INVAL, "bytes is NULL");
+  *bytes = slot_layout(*cfg).total;
+  return CBD_OK;
+}
+
+int cbd_workspace_bytes(const cbd_config* cfg, size_t* bytes) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!bytes) return fail(CBD_E_INVAL, "bytes is NULL");
+  *bytes = workspace_layout(*cfg).total;
+  return CBD_OK;
+}
+
+int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* kv_pool,
+                      void* slot_state, void* workspace, const int32_t* block_order,
+                      void* stream, cbd_engine** out) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!w || !kv_pool || !slot_state || !workspace || !out)
+    return fail(CBD_E_INVAL, "NULL weights, buffer or output handle");
+  if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->w_qkv || !w->w_o ||
+      !w->ffn_norm || !w->w_gate || !w->w_up || !w->w_down)
+    return fail(CBD_E_INVAL, "a weight pointer is NULL");
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if (!w->attn_norm[l] || !w->w_qkv[l] || !w->w_o[l] || !w->ffn_norm[l] || !w->w_gate[l] ||
+        !w->w_up[l] || !w->w_down[l])
+      return fail(CBD_E_INVAL, "a per-layer weight pointer is NULL");
+  for (const void* p : {(const void*)kv_pool, (const void*)slot_state, (const void*)workspace})
+    if ((uintptr_t)p % 256) return fail(CBD_E_INVAL, "device buffers must be 256-byte aligned");
+
+  cbd_engine* e = new cbd_engine();
+  e->cfg = *cfg;
+  e->md = ModelDims{cfg->d_model, cfg->n_heads, cfg->n_kv_heads, cfg->head_dim, cfg->ffn_dim,
+                    cfg->vocab, cfg->block_size, cfg->num_blocks, cfg->max_slots,
+                    cfg->max_position, cfg->rms_eps};
+  e->ws = workspace_layout(*cfg);
+  e->sl = slot_layout(*cfg);
+  e->embed = (const uint16_t*)w->embed;
+  e->final_norm = (const uint16_t*)w->final_norm;
+  e->lm_head = (const uint16_t*)w->lm_head;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    e->attn_norm.push_back((const uint16_t*)w->attn_norm[l]);
+    e->w_qkv.push_back((const uint16_t*)w->w_qkv[l]);
+    e->w_o.push_back((const uint16_t*)w->w_o[l]);
+    e->ffn_norm.push_back((const uint16_t*)w->ffn_norm[l]);
+    e->w_gate.push_back((const uint16_t*)w->w_gate[l]);
+    e->w_up.push_back((const uint16_t*)w->w_up[l]);
+    e->w_down.push_back((const uint16_t*)w->w_down[l]);
+  }
+  e->kv_pool = (uint8_t*)kv_pool;
+  e->slot_state = (uint8_t*)slot_state;
+  e->workspace = (uint8_t*)workspace;
+  e->stream = (hipStream_t)stream;
+  e->slots.reset(cfg->max_slots);
+  if (!e->blocks.reset(cfg->num_blocks, block_order)) {
+    delete e;
+    return fail(CBD_E_INVAL, "block_order is not a permutation of 0..num_blocks-1");
+  }
+  e->host_params.assign((size_t)cfg->max_slots, SlotParams{});
+
+  // RoPE table: angle pos * base^(-2i/hd) in double, stored as fp32 (cos, sin).
+  const int half = cfg->head_dim / 2;
+  std::vector<float> cs((size_t)cfg->max_position * half * 2);
+  for (int i = 0; i < half; ++i) {
+    const double inv_freq = pow(cfg->rope_base, -2.0 * i / (double)cfg->head_dim);
+    for (int p = 0; p < cfg->max_position; ++p) {
+      const double th = (double)p * inv_freq;
+      cs[((size_t)p * half + i) * 2] = (float)cos(th);
+      cs[((size_t)p * half + i) * 2 + 1] = (float)sin(th);
+    }
+  }
+  hipError_t he = hipMemcpyAsync(e->workspace + e->ws.rope, cs.data(), cs.size() * sizeof(float),
+                                 hipMemcpyHostToDevice, e->stream);
+  if (he == hipSuccess)
+    he = launch_fill_u32(e->wsp<uint32_t>(e->ws.status), 0u, 1, e->stream);
+  if (he == hipSuccess)
+    he = launch_fill_u32((uint32_t*)e->slot_state, 0u, e->sl.total / 4, e->stream);
+  if (he == hipSuccess) he = hipStreamSynchronize(e->stream);
+  if (he != hipSuccess) {
+    delete e;
+    return fail(CBD_E_DEVICE, std::string("engine set-up: ") + hipGetErrorString(he));
+  }
+  *out = e;
+  return CBD_OK;
+}
+
+int cbd_engine_destroy(cbd_engine* e) {
+  if (!e) return fail(CBD_E_INVAL, "engine is NULL");
+  delete e;
+  return CBD_OK;
+}
+
+int cbd_slot_alloc(cbd_engine* e, const cbd_sampling* p, uint64_t request_id, int32_t* slot_out) {
+  if (!e || !slot_out) return fail(CBD_E_INVAL, "NULL engine or output");
+  cbd_sampling sp = p ? *p : cbd_sampling{0.f, 1.f, 0, 0.f, 0.f, 1.f, 0};
+  if (!(sp.temperature >= 0.f) || sp.top_k < 0 || !(sp.penalty_decay >= 0.f))
+    return fail(CBD_E_INVAL, "sampling parameters out of range");
+  int32_t s = e->slots.alloc();
+  if (s < 0) return fail(CBD_E_NOSLOT, "every slot is taken");
+  SlotParams& hp = e->host_params[(size_t)s];
+  hp = SlotParams{sp.temperature, sp.top_p, sp.top_k, sp.freq_penalty, sp.presence_penalty,
+                  sp.penalty_decay, sp.seed, request_id};
+  hipError_t he = hipMemcpyAsync(e->slot_state + e->sl.params + (size_t)s * sizeof(SlotParams),
+                                 &hp, sizeof(SlotParams), hipMemcpyHostToDevice, e->stream);
+  if (he == hipSuccess)
+    he = launch_fill_u32((uint32_t*)(e->slot_state + e->sl.counts) + (size_t)s * e->cfg.vocab, 0u,
+                         (size_t)e->cfg.vocab, e->stream);
+  if (he != hipSuccess) {
+    e->slots.release(s);
+    return fail(CBD_E_DEVICE, std::string("slot reset: ") + hipGetErrorString(he));
+  }
+  *slot_out = s;
+  return CBD_OK;
+}
+
+int cbd_slot_free(cbd_engine* e, int32_t slot) {
+  if (!e) return fail(CBD_E_INVAL, "engine is NULL");
+  if (!e->slots.release(slot)) return fail(CBD_E_INVAL, "slot is not allocated");
+  return CBD_OK;
+}
+
+int cbd_block_alloc(cbd_engine* e, int32_t n, int32_t* ids_out) {
+  if (!e || (n > 0 && !ids_out) || n < 0) return fail(CBD_E_INVAL, "bad block_alloc arguments");
+  if (!e->blocks.alloc(n, ids_out)) return fail(CBD_E_NOBLOCKS, "not enough free blocks");
+  return CBD_OK;
+}
+
+int cbd_block_free(cbd_engine* e, int32_t n, const int32_t* ids) {
+  if (!e || (n > 0 && !ids) || n < 0) return fail(CBD_E_INVAL, "bad block_free arguments");
+  if (!e->blocks.release(n, ids)) return fail(CBD_E_INVAL, "freeing a block that is not allocated");
+  return CBD_OK;
+}
+
+int cbd_blocks_available(const cbd_engine* e) {
+  if (!e) return fail(CBD_E_INVAL, "engine is NULL");
+  return e->blocks.available();
+}
+
+int cbd_engine_status(cbd_engine* e, void* stream, uint32_t* flags) {
+  if (!e || !flags) return fail(CBD_E_INVAL, "NULL engine or output");
+  hipStream_t st = (hipStream_t)stream;
+  uint32_t v = 0;
+  HIP_TRY(hipMemcpyAsync(&v, e->wsp<uint32_t>(e->ws.status), 4, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  HIP_TRY(launch_fill_u32(e->wsp<uint32_t>(e->ws.status), 0u, 1, st));
+  *flags = v;
+  return CBD_OK;
+}
+
+// ---------------------------------------------------------------- the step
+
+static AttnPlan plan_attention(const cbd_engine* e, const cbd_step* s) {
+  const cbd_config& c = e->cfg;
+  AttnPlan ap;
+  ap.max_splits = e->ws.attn_max_splits;
+  ap.max_ctx = s->max_ctx;
+  // Enough work items to fill the chip (about 4096) without slivers shorter
+  // than 64 keys; never more splits than the partial buffers hold.
+  long long want = (long long)s->max_ctx * s->n_seqs * c.n_kv_heads / 4096;
+  int32_t len = (int32_t)std::max<long long>(64, std::min<long long>(4096, want));
+  len = (len + 31) / 32 * 32;
+  int32_t floor_len = (s->max_ctx + ap.max_splits - 1) / ap.max_splits;
+  floor_len = (floor_len + 31) / 32 * 32;
+  ap.split_len = std::max(len, floor_len);
+  const int G = c.n_heads / c.n_kv_heads;
+  const long long qt = ((long long)s->n_rows * G + 15) / 16 + s->n_seqs;
+  const long long sp = (s->max_ctx + ap.split_len - 1) / ap.split_len;
+  ap.grid_items = (int32_t)std::min<long long>(qt * sp * c.n_kv_heads, 1LL << 30);
+  return ap;
+}
+
+int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_t* tokens_out,
+                     void* stream) {
+  if (!e || !s) return fail(CBD_E_INVAL, "NULL engine or step");
+  const cbd_config& c = e->cfg;
+  if (s->n_seqs < 1 || s->n_seqs > c.max_seqs) return fail(CBD_E_INVAL, "n_seqs out of range");
+  if (s->n_rows < s->n_seqs || s->n_rows > c.max_rows) return fail(CBD_E_INVAL, "n_rows out of range");
+  if (s->n_out < 0 || s->n_out > s->n_seqs) return fail(CBD_E_INVAL, "n_out out of range");
+  if (s->max_ctx < 1 || s->max_ctx > c.max_position)
+    return fail(CBD_E_INVAL, "max_ctx must be in 1..max_position");
+  if (s->max_blocks_per_seq < 1 || s->max_blocks_per_seq > c.max_blocks_per_seq)
+    return fail(CBD_E_INVAL, "max_blocks_per_seq out of range");
+  if (s->mode != CBD_MODE_GREEDY && s->mode != CBD_MODE_SAMPLE)
+    return fail(CBD_E_INVAL, "unknown mode");
+  if (!s->slots || !s->block_tables || !s->ctx_lens || !s->n_new || !s->tokens ||
+      !s->want_token || (s->mode == CBD_MODE_SAMPLE && !s->step_ids))
+    return fail(CBD_E_INVAL, "a step array is NULL");
+  if (s->n_out > 0 && !tokens_out) return fail(CBD_E_INVAL, "tokens_out is NULL");
+
+  hipStream_t st = (hipStream_t)stream;
+  const int R = s->n_rows;
+  uint32_t* status = e->wsp<uint32_t>(e->ws.status);
+  StepMeta m{s->n_seqs, s->n_rows, s->n_out, s->max_blocks_per_seq, s->slots, s->block_tables,
+             s->ctx_lens, s->n_new, s->tokens, s->want_token, s->step_ids};
+  RowMaps maps{e->wsp<int32_t>(e->ws.row_seq), e->wsp<int32_t>(e->ws.row_pos),
+               e->wsp<int32_t>(e->ws.seq_row0), e->wsp<int32_t>(e->ws.out_row),
+               e->wsp<int32_t>(e->ws.out_seq), e->wsp<int32_t>(e->ws.item0)};
+  const AttnPlan ap = plan_attention(e, s);
+  uint16_t* x = e->wsp<uint16_t>(e->ws.x);
+  uint16_t* h = e->wsp<uint16_t>(e->ws.h);
+  uint16_t* qkv = e->wsp<uint16_t>(e->ws.qkv);
+  uint16_t* q = e->wsp<uint16_t>(e->ws.q);
+  uint16_t* attn = e->wsp<uint16_t>(e->ws.attn);
+  uint16_t* ffn = e->wsp<uint16_t>(e->ws.ffn);
+  float* gpart = e->wsp<float>(e->ws.gemm_part);
+  const int qkv_n = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int qd = c.n_heads * c.head_dim;
+
+  HIP_TRY(launch_prep(m, maps, e->md, ap, status, st));
+  HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
+  HIP_TRY(launch_embed_norm(s->tokens, maps.row_seq, R, e->embed, e->attn_norm[0], e->md, x, h,
+                            status, st));
+  HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (l > 0) HIP_TRY(launch_rmsnorm(x, nullptr, R, e->attn_norm[l], c.d_model, c.rms_eps, h, st));
+    GemmArgs g{};
+    g.partials = gpart;
+    g.partials_cap = e->ws.gemm_part_floats;
+    g.X = h; g.R = R; g.K = c.d_model; g.W = e->w_qkv[l]; g.N = qkv_n; g.epi = EPI_BF16; g.Y = qkv;
+    HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
+    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
+    HIP_TRY(launch_rope_append(qkv, R, m, maps, e->wsp<float>(e->ws.rope), e->md, q, e->pool_k(l),
+                               e->pool_v(l), status, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
+    HIP_TRY(launch_attention(q, R, m, maps, e->md, ap, e->pool_k(l), e->pool_v(l),
+                             e->wsp<float>(e->ws.attn_ml), e->wsp<float>(e->ws.attn_o), attn,
+                             status, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
+    g.X = attn; g.K = qd; g.W = e->w_o[l]; g.N = c.d_model; g.epi = EPI_RESID; g.Y = x;
+    HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
+    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
+    HIP_TRY(launch_rmsnorm(x, nullptr, R, e->ffn_norm[l], c.d_model, c.rms_eps, h, st));
+    g.X = h; g.K = c.d_model; g.W = e->w_gate[l]; g.W2 = e->w_up[l]; g.N = c.ffn_dim;
+    g.epi = EPI_SWIGLU; g.Y = ffn;
+    HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
+    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
+    g.X = ffn; g.K = c.ffn_dim; g.W = e->w_down[l]; g.W2 = nullptr; g.N = c.d_model;
+    g.epi = EPI_RESID; g.Y = x;
+    HIP_TRY(e->prof_mark(CBD_KERNEL_DOWN, st));
+    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_DOWN, st));
+  }
+  if (s->n_out == 0) return CBD_OK;
+  uint16_t* lm_in = e->wsp<uint16_t>(e->ws.lm_in);
+  HIP_TRY(launch_rmsnorm(x, maps.out_row, s->n_out, e->final_norm, c.d_model, c.rms_eps, lm_in, st));
+  float* logits = logits_out;
+  if (!logits && s->mode == CBD_MODE_SAMPLE) logits = e->wsp<float>(e->ws.logits);
+  GemmArgs g{};
+  g.X = lm_in; g.R = s->n_out; g.K = c.d_model; g.W = e->lm_head; g.N = c.vocab;
+  g.epi = EPI_LOGITS; g.logits = logits;
+  g.amax_val = e->wsp<float>(e->ws.amax_val);
+  g.amax_idx = e->wsp<int32_t>(e->ws.amax_idx);
+  g.amax_stride = e->ws.amax_stride;
+  g.partials = gpart;
+  g.partials_cap = e->ws.gemm_part_floats;
+  HIP_TRY(e->prof_mark(CBD_KERNEL_LM_HEAD, st));
+  HIP_TRY(launch_gemm(g, st));
+  HIP_TRY(e->prof_mark(CBD_KERNEL_LM_HEAD, st));
+  HIP_TRY(e->prof_mark(CBD_KERNEL_SAMPLE, st));
+  if (s->mode == CBD_MODE_GREEDY) {
+    HIP_TRY(launch_argmax_reduce(g.amax_val, g.amax_idx, gemm_amax_tiles(s->n_out, c.vocab),
+                                 e->ws.amax_stride, s->n_out, tokens_out, st));
+  } else {
+    HIP_TRY(launch_sampler(logits, s->n_out, c.vocab, s->slots, s->step_ids, maps.out_seq,
+                           reinterpret_cast<const SlotParams*>(e->slot_state + e->sl.params),
+                           reinterpret_cast<float*>(e->slot_state + e->sl.counts), c.max_slots,
+                           e->wsp<float>(e->ws.smp), tokens_out, status, st));
+  }
+  HIP_TRY(e->prof_mark(CBD_KERNEL_SAMPLE, st));
+  return CBD_OK;
+}
+
+int cbd_sample_logits(cbd_engine* e, const float* logits, int32_t n, const int32_t* slots,
+                      const int32_t* step_ids, int32_t* tokens_out, void* stream) {
+  if (!e || !logits || !slots || !step_ids || !tokens_out || n < 1 || n > e->cfg.max_seqs)
+    return fail(CBD_E_INVAL, "bad sample_logits arguments");
+  HIP_TRY(launch_sampler(logits, n, e->cfg.vocab, slots, step_ids, nullptr,
+                         reinterpret_cast<const SlotParams*>(e->slot_state + e->sl.params),
+                         reinterpret_cast<float*>(e->slot_state + e->sl.counts), e->cfg.max_slots,
+                         e->wsp<float>(e->ws.smp), tokens_out, e->wsp<uint32_t>(e->ws.status),
+                         (hipStream_t)stream));
+  return CBD_OK;
+}
+
+int cbd_profile_begin(cbd_engine* e, int32_t kernel_class) {
+  if (!e || kernel_class < CBD_KERNEL_QKV || kernel_class > CBD_KERNEL_NORM)
+    return fail(CBD_E_INVAL, "unknown kernel class");
+  e->prof_class = kernel_class;
+  e->prof_used = 0;
+  return CBD_OK;
+}
+
+int cbd_profile_end(cbd_engine* e, double* total_ms, int32_t* launches) {
+  if (!e || !total_ms || !launches) return fail(CBD_E_INVAL, "NULL argument");
+  double sum = 0.0;
+  const size_t pairs = e->prof_used / 2;
+  for (size_t i = 0; i < pairs; ++i) {
+    HIP_TRY(hipEventSynchronize(e->prof_events[2 * i + 1]));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, e->prof_events[2 * i], e->prof_events[2 * i + 1]));
+    sum += ms;
+  }
+  e->prof_class = 0;
+  e->prof_used = 0;
+  *total_ms = sum;
+  *launches = (int32_t)pairs;
+  return CBD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,339 @@
+// gemm.hip -- the weight-streaming skinny GEMM of the step, on MFMA.
+//
+//   Y[r][n] = sum_k X[r][k] * W[n][k]      X: [R][K] bf16 (a few rows)
+//                                          W: [N][K] bf16 (read once)
+//
+// Decode is weight-bandwidth bound: every weight byte is used by the R rows of
+// the step (Go under the hood 20.3.2: one weight read serves the whole batch),
+// so the kernel streams W from HBM exactly once per column tile and keeps X
+// close (it is small and shared by every workgroup through L2 and L1).
+//
+// Mapping onto v_mfma_f32_16x16x32_bf16: the A operand is a 16-row fragment
+// of W (16 output columns), the B operand a 16-row fragment of X, so one
+// instruction yields a 16 (columns) x 16 (rows) tile. Lane l holds 8
+// consecutive k of row (l % 16) of each operand; the four lane groups
+// (l / 16) hold consecutive 8-k pieces, so one 16-byte load per lane covers
+// 64 contiguous bytes of 16 weight rows. A 64-k super-step issues two such
+// loads per fragment (the two halves of each row's 128-byte line) and feeds
+// two MFMAs.
+//
+// A wave owns NT column fragments x RT row fragments. KW waves of a workgroup
+// split K and reduce through LDS in fixed wave order; S workgroups along
+// grid.y split K further and leave fp32 partials that a second kernel sums in
+// fixed split order and passes through the epilogue. Epilogues: bf16 store,
+// residual add (x = bf16(x + bf16(acc))), SwiGLU over a gate/up pair
+// (a = bf16(silu(bf16(g)) * bf16(u))), and fp32 logits with per-tile argmax
+// partials (lowest id on ties).
+#include "common.h"
+#include "kernels.h"
+
+namespace cbd {
+
+template <int EPI>
+struct EpiTraits {
+  static constexpr int NM = EPI == EPI_SWIGLU ? 2 : 1;  // weight matrices
+};
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+
+// Apply the epilogue to 4 consecutive columns n..n+3 of row r.
+template <int EPI>
+__device__ __forceinline__ void epilogue4(const GemmArgs& a, int r, int n, const float* v0,
+                                          const float* v1) {
+  if (EPI == EPI_BF16) {
+    uint2 o = make_uint2(pack_bf2(v0[0], v0[1]), pack_bf2(v0[2], v0[3]));
+    *reinterpret_cast<uint2*>(a.Y + (size_t)r * a.N + n) = o;
+  } else if (EPI == EPI_RESID) {
+    uint2* p = reinterpret_cast<uint2*>(a.Y + (size_t)r * a.N + n);
+    uint2 x = *p;
+    float y0 = lo_bf(x.x) + round_bf(v0[0]);
+    float y1 = hi_bf(x.x) + round_bf(v0[1]);
+    float y2 = lo_bf(x.y) + round_bf(v0[2]);
+    float y3 = hi_bf(x.y) + round_bf(v0[3]);
+    *p = make_uint2(pack_bf2(y0, y1), pack_bf2(y2, y3));
+  } else if (EPI == EPI_SWIGLU) {
+    float o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = silu_f(round_bf(v0[i])) * round_bf(v1[i]);
+    *reinterpret_cast<uint2*>(a.Y + (size_t)r * a.N + n) =
+        make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+  } else {  // EPI_LOGITS
+    if (a.logits)
+      *reinterpret_cast<float4*>(a.logits + (size_t)r * a.N + n) =
+          make_float4(v0[0], v0[1], v0[2], v0[3]);
+  }
+}
+
+template <int RT, int NT, int KW, int EPI>
+__global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S) {
+  constexpr int NM = EpiTraits<EPI>::NM;
+  extern __shared__ float lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * (16 * NT);
+  const int ks = blockIdx.y;
+  const int r0 = blockIdx.z * (16 * RT);
+  const int K = a.K, N = a.N, R = a.R;
+
+  const int kw_len = kc / KW;  // multiple of 8 (K % 16 == 0, kc % (16 KW) == 0)
+  const int kbeg = ks * kc + wave * kw_len;
+  const int kend = min(K, kbeg + kw_len);
+
+  const uint16_t* wrow[NM][NT];
+  bool wok[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    int n = n0 + 16 * nt + lr;
+    wok[nt] = n < N;
+    size_t off = (size_t)(wok[nt] ? n : 0) * K;
+    wrow[0][nt] = a.W + off;
+    if (NM == 2) wrow[NM - 1][nt] = a.W2 + off;
+  }
+  const uint16_t* xrow[RT];
+  bool xok[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int r = r0 + 16 * rt + lr;
+    xok[rt] = r < R;
+    xrow[rt] = a.X + (size_t)(xok[rt] ? r : 0) * K;
+  }
+
+  floatx4_t acc[NM][NT][RT];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int U = 2;  // super-steps whose loads are issued together
+  for (int k = kbeg; k < kend; k += 64 * U) {
+    uint4 wv[U][NM][NT][2];
+    uint4 xv[U][RT][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = k + 64 * u + 32 * h + 8 * lg;  // 8 k of this lane
+        const bool kin = kk < kend;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            wv[u][m][nt][h] = (kin && wok[nt]) ? load_stream16(wrow[m][nt] + kk)
+                                                 : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          xv[u][rt][h] = (kin && xok[rt]) ? *reinterpret_cast<const uint4*>(xrow[rt] + kk)
+                                          : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              acc[m][nt][rt] = mfma16x16x32(as_bf16x8(wv[u][m][nt][h]), as_bf16x8(xv[u][rt][h]),
+                                            acc[m][nt][rt]);
+  }
+
+  // Reduce the KW waves' partial sums through LDS, in wave order.
+  if (KW > 1) {
+    constexpr int TILE = NM * NT * RT * 4;  // floats per lane
+    if (wave > 0) {
+      float* dst = lds + ((size_t)(wave - 1) * 64 + lane) * TILE;
+      int q = 0;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[q++] = acc[m][nt][rt][i];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < KW; ++w) {
+      const float* src = lds + ((size_t)(w - 1) * 64 + lane) * TILE;
+      int q = 0;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][nt][rt][i] += src[q++];
+    }
+  }
+
+  // Lane l holds columns n0 + 16 nt + 4 lg + (0..3) of row r0 + 16 rt + lr.
+  if (S > 1) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          int r = r0 + 16 * rt + lr, n = n0 + 16 * nt + 4 * lg;
+          if (r < R && n < N)
+            *reinterpret_cast<float4*>(a.partials + (((size_t)ks * NM + m) * R + r) * N + n) =
+                make_float4(acc[m][nt][rt][0], acc[m][nt][rt][1], acc[m][nt][rt][2],
+                            acc[m][nt][rt][3]);
+        }
+    return;
+  }
+
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = r0 + 16 * rt + lr;
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + 16 * nt + 4 * lg;
+      float v0[4], v1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v0[i] = acc[0][nt][rt][i];
+        v1[i] = acc[NM - 1][nt][rt][i];
+      }
+      if (r < R && n < N) {
+        epilogue4<EPI>(a, r, n, v0, v1);
+        if (EPI == EPI_LOGITS) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (v0[i] > best) {  // ascending columns: first maximum wins
+              best = v0[i];
+              bidx = n + i;
+            }
+        }
+      }
+    }
+    if (EPI == EPI_LOGITS) {
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) {
+        float v = __shfl_xor(best, o, 64);
+        int i = __shfl_xor(bidx, o, 64);
+        if (v > best || (v == best && i < bidx)) {
+          best = v;
+          bidx = i;
+        }
+      }
+      if (lg == 0 && r < R) {
+        a.amax_val[(size_t)r * a.amax_stride + blockIdx.x] = best;
+        a.amax_idx[(size_t)r * a.amax_stride + blockIdx.x] = bidx;
+      }
+    }
+  }
+}
+
+// Sum the S split partials in split order, then the epilogue (no argmax:
+// the logits GEMM never splits K).
+template <int EPI>
+__global__ void gemm_reduce_kernel(GemmArgs a, int S) {
+  constexpr int NM = EpiTraits<EPI>::NM;
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // group of 4 columns
+  const int groups = a.N / 4;
+  if (q >= (size_t)a.R * groups) return;
+  const int r = (int)(q / groups), n = (int)(q % groups) * 4;
+  float v[NM][4];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[m][i] = 0.f;
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      float4 p = *reinterpret_cast<const float4*>(a.partials + (((size_t)s * NM + m) * a.R + r) * a.N + n);
+      v[m][0] += p.x;
+      v[m][1] += p.y;
+      v[m][2] += p.z;
+      v[m][3] += p.w;
+    }
+  epilogue4<EPI>(a, r, n, v[0], v[NM - 1]);
+}
+
+// ------------------------------------------------------------- host side
+
+struct Shape {
+  int RT, NT;
+};
+
+static Shape pick_shape(int R) {
+  if (R <= 16) return {1, 4};
+  if (R <= 32) return {2, 4};
+  if (R <= 64) return {4, 4};
+  return {8, 2};
+}
+
+int32_t gemm_amax_tiles(int32_t R, int32_t N) {
+  Shape s = pick_shape(R);
+  return (N + 16 * s.NT - 1) / (16 * s.NT);
+}
+
+template <int RT, int NT, int EPI>
+static hipError_t launch_shape(const GemmArgs& a, hipStream_t st) {
+  constexpr int NM = EpiTraits<EPI>::NM;
+  const int n_tiles = (a.N + 16 * NT - 1) / (16 * NT);
+  const int r_groups = (a.R + 16 * RT - 1) / (16 * RT);
+  const int base = n_tiles * r_groups;
+  // Aim at >= 2048 waves in flight (8 per CU): first split K inside the
+  // workgroup (up to 4 waves, >= 256 k each), then across workgroups
+  // (>= 512 k each) when the partials fit.
+  // LDS for the in-workgroup reduction stays within 64 KB.
+  const size_t lds_per_wave = (size_t)64 * NM * NT * RT * 4 * sizeof(float);
+  int KW = 1;
+  while (KW < 4 && base * KW < 2048 && a.K / (KW * 2) >= 256 &&
+         (size_t)(KW * 2 - 1) * lds_per_wave <= 65536)
+    KW *= 2;
+  int S = 1;
+  if (EPI != EPI_LOGITS) {
+    while (base * KW * S < 2048 && a.K / (S * 2) >= 512 &&
+           (size_t)(S * 2) * NM * a.R * a.N <= a.partials_cap)
+      S *= 2;
+  }
+  int kc = (a.K + S - 1) / S;
+  kc = (kc + 16 * KW - 1) / (16 * KW) * (16 * KW);
+  S = (a.K + kc - 1) / kc;
+  dim3 grid(n_tiles, S, r_groups);
+  size_t lds = KW > 1 ? (size_t)(KW - 1) * 64 * NM * NT * RT * 4 * sizeof(float) : 0;
+  switch (KW) {
+    case 1: gemm_kernel<RT, NT, 1, EPI><<<grid, 64, lds, st>>>(a, kc, S); break;
+    case 2: gemm_kernel<RT, NT, 2, EPI><<<grid, 128, lds, st>>>(a, kc, S); break;
+    default: gemm_kernel<RT, NT, 4, EPI><<<grid, 256, lds, st>>>(a, kc, S); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const size_t threads = (size_t)a.R * (a.N / 4);
+  gemm_reduce_kernel<EPI><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(a, S);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
+  Shape s = pick_shape(a.R);
+  if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
+  if (s.RT == 2) return launch_shape<2, 4, EPI>(a, st);
+  if (s.RT == 4) return launch_shape<4, 4, EPI>(a, st);
+  return launch_shape<8, 2, EPI>(a, st);
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+  if (a.R <= 0) return hipSuccess;
+  switch (a.epi) {
+    case EPI_BF16: return launch_epi<EPI_BF16>(a, st);
+    case EPI_RESID: return launch_epi<EPI_RESID>(a, st);
+    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, st);
+    default: return launch_epi<EPI_LOGITS>(a, st);
+  }
+}
+
+}  // namespace cbd

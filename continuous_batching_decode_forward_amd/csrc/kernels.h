@@ -1,0 +1,125 @@
+// kernels.h -- host-side launch interface of the step's gfx950 kernels.
+// Every launcher enqueues on the given stream and returns the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cbd {
+
+// ------------------------------------------------------------------ metadata
+
+struct StepMeta {
+  int32_t n_seqs, n_rows, n_out, max_blocks_per_seq;
+  const int32_t* slots;
+  const int32_t* block_tables;
+  const int32_t* ctx_lens;
+  const int32_t* n_new;
+  const int32_t* tokens;
+  const int32_t* want_token;
+  const int32_t* step_ids;
+};
+
+// Row maps built on the device from the step metadata (workspace).
+struct RowMaps {
+  int32_t* row_seq;    // [max_rows] sequence of each row, -1 = refused
+  int32_t* row_pos;    // [max_rows] position of each row
+  int32_t* seq_row0;   // [max_seqs] first row of each sequence
+  int32_t* out_row;    // [max_rows] row of the j-th emitting sequence, -1 = none
+  int32_t* out_seq;    // [max_rows] that sequence
+  int32_t* item0;      // [max_seqs + 1] first attention work item per sequence
+};
+
+struct ModelDims {
+  int32_t d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  int32_t block_size, num_blocks, max_slots, max_position;
+  float rms_eps;
+};
+
+// Attention work decomposition chosen by the host for one step.
+struct AttnPlan {
+  int32_t split_len;   // keys per work item (multiple of 32)
+  int32_t max_splits;  // stride of the partial buffers
+  int32_t grid_items;  // upper bound of the work items (launch size)
+  int32_t max_ctx;     // host bound on ctx + n_new that sized the launch
+};
+
+hipError_t launch_prep(const StepMeta& m, const RowMaps& maps, const ModelDims& md,
+                       const AttnPlan& ap, uint32_t* status, hipStream_t st);
+
+// x[r] = embed[tokens[r]], h[r] = rmsnorm(x[r]) * gain.
+hipError_t launch_embed_norm(const int32_t* tokens, const int32_t* row_seq, int32_t R,
+                             const uint16_t* embed, const uint16_t* gain, const ModelDims& md,
+                             uint16_t* x, uint16_t* h, uint32_t* status, hipStream_t st);
+
+// h[j] = rmsnorm(x[rows ? rows[j] : j]) * gain for j < R (rows[j] < 0: skipped).
+hipError_t launch_rmsnorm(const uint16_t* x, const int32_t* rows, int32_t R, const uint16_t* gain,
+                          int32_t d, float eps, uint16_t* h, hipStream_t st);
+
+// RoPE on q and k of every row at its position; q to q_out, k and v appended
+// into the layer's K and V regions of the pool through the block tables.
+hipError_t launch_rope_append(const uint16_t* qkv, int32_t R, const StepMeta& m,
+                              const RowMaps& maps, const float* rope_cs, const ModelDims& md,
+                              uint16_t* q_out, uint16_t* pool_k, uint16_t* pool_v,
+                              uint32_t* status, hipStream_t st);
+
+// Paged GQA attention for every row (decode rows and prefill chunks), split
+// over keys, then the split combine into out [R][n_heads*head_dim] bf16.
+hipError_t launch_attention(const uint16_t* q, int32_t R, const StepMeta& m, const RowMaps& maps,
+                            const ModelDims& md, const AttnPlan& ap, const uint16_t* pool_k,
+                            const uint16_t* pool_v, float* part_ml, float* part_o, uint16_t* out,
+                            uint32_t* status, hipStream_t st);
+
+// --------------------------------------------------------------------- GEMM
+
+enum GemmEpilogue { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+struct GemmArgs {
+  const uint16_t* X;  // [R][K] bf16
+  int32_t R, K;
+  const uint16_t* W;  // [N][K] bf16
+  const uint16_t* W2; // second matrix for EPI_SWIGLU (up), [N][K]
+  int32_t N;
+  int32_t epi;
+  uint16_t* Y;        // EPI_BF16 / EPI_SWIGLU out [R][N]; EPI_RESID in/out [R][N]
+  float* logits;      // EPI_LOGITS out [R][N] (nullable: argmax only)
+  float* amax_val;    // EPI_LOGITS per-(row, column tile) maxima [R][amax_stride]
+  int32_t* amax_idx;
+  int32_t amax_stride;
+  float* partials;    // split-K partial sums
+  size_t partials_cap;  // floats available there
+};
+
+// Tile columns covered by one argmax partial for a GEMM of R rows (the host
+// sizes amax buffers with this).
+int32_t gemm_amax_tiles(int32_t R, int32_t N);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
+// tokens[j] = lowest id of the row maximum over the argmax partials.
+hipError_t launch_argmax_reduce(const float* amax_val, const int32_t* amax_idx, int32_t n_tiles,
+                                int32_t stride, int32_t n, int32_t* tokens, hipStream_t st);
+
+// ------------------------------------------------------------------ sampler
+
+// Per-slot sampler state in the caller's slot buffer.
+struct SlotParams {
+  float temperature, top_p;
+  int32_t top_k;
+  float freq_penalty, presence_penalty, penalty_decay;
+  uint64_t seed;
+  uint64_t request_id;
+};
+
+// Floats of sampler scratch per row for a vocabulary of V.
+int32_t sampler_row_floats(int32_t V);
+hipError_t launch_sampler(const float* logits, int32_t n, int32_t V, const int32_t* slots,
+                          const int32_t* step_ids, const int32_t* out_seq, const SlotParams* params,
+                          float* counts, int32_t max_slots, float* scratch, int32_t* tokens,
+                          uint32_t* status, hipStream_t st);
+
+// -------------------------------------------------------------------- misc
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t st);
+
+}  // namespace cbd

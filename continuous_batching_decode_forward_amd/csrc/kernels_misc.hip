@@ -1,0 +1,363 @@
+// kernels_misc.hip -- step metadata preparation, embedding + RMSNorm,
+// RMSNorm, RoPE + KV append, argmax combine, fills.
+#include "common.h"
+#include "kernels.h"
+
+namespace cbd {
+
+// ------------------------------------------------------------------- prep
+//
+// One workgroup turns the per-sequence metadata into per-row maps: the
+// sequence and position of every row (rows are the sequences' n_new entries
+// laid end to end, in order), the row each emitting sequence takes its token
+// from (its last row), and the first attention work item of each sequence.
+// Sequences whose metadata is out of range keep their place in the row
+// layout but are refused: their rows get row_seq = -1 and no work items.
+
+#define PREP_THREADS 1024
+
+__device__ int block_exclusive_scan(int v, int* buf, int* total) {
+  int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int o = 1; o < PREP_THREADS; o <<= 1) {
+    int add = t >= o ? buf[t - o] : 0;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  int incl = buf[t];
+  *total = buf[PREP_THREADS - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps maps,
+                                                            ModelDims md, AttnPlan ap,
+                                                            uint32_t* status) {
+  __shared__ int buf[PREP_THREADS];
+  const int t = threadIdx.x;
+  const int n = m.n_seqs;
+  const int per = (n + PREP_THREADS - 1) / PREP_THREADS;
+  const int s0 = min(n, t * per), s1 = min(n, s0 + per);
+  const int G = md.n_heads / md.n_kv_heads;  // query heads per KV head
+  const int cap = m.max_blocks_per_seq * md.block_size;
+
+  int rows = 0, items = 0, outs = 0;
+  for (int s = s0; s < s1; ++s) {
+    int nn = m.n_new[s], ctx = m.ctx_lens[s];
+    int nn_layout = max(0, min(nn, m.n_rows));
+    bool ok = nn >= 1 && ctx >= 0 && ctx + nn <= cap &&
+              ctx + nn <= ap.max_splits * ap.split_len && ctx + nn <= md.max_position &&
+              ctx + nn <= ap.max_ctx;
+    int slot = m.slots[s];
+    if (slot < 0 || slot >= md.max_slots) {
+      ok = false;
+      raise_status(status, ST_BAD_SLOT);
+    } else if (!ok) {
+      raise_status(status, ST_BAD_SHAPE);
+    }
+    rows += nn_layout;
+    if (ok) {
+      int qtiles = (nn * G + 15) / 16;
+      int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
+      items += md.n_kv_heads * qtiles * splits;
+    }
+    outs += m.want_token[s] ? 1 : 0;
+  }
+  int tot_rows, tot_items, tot_outs;
+  int r = block_exclusive_scan(rows, buf, &tot_rows);
+  int it = block_exclusive_scan(items, buf, &tot_items);
+  int o = block_exclusive_scan(outs, buf, &tot_outs);
+  const bool counts_ok = tot_rows == m.n_rows && tot_outs == m.n_out;
+  if (t == 0 && !counts_ok) raise_status(status, ST_BAD_SHAPE);
+
+  for (int s = s0; s < s1; ++s) {
+    int nn = m.n_new[s], ctx = m.ctx_lens[s];
+    int nn_layout = max(0, min(nn, m.n_rows));
+    int slot = m.slots[s];
+    bool ok = counts_ok && nn >= 1 && ctx >= 0 && ctx + nn <= cap &&
+              ctx + nn <= ap.max_splits * ap.split_len && ctx + nn <= md.max_position &&
+              ctx + nn <= ap.max_ctx && slot >= 0 && slot < md.max_slots;
+    maps.item0[s] = it;
+    maps.seq_row0[s] = r;
+    for (int i = 0; i < nn_layout; ++i) {
+      if (r + i < m.n_rows) {
+        maps.row_seq[r + i] = ok ? s : -1;
+        maps.row_pos[r + i] = ctx + i;
+      }
+    }
+    if (ok) {
+      int qtiles = (nn * G + 15) / 16;
+      int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
+      it += md.n_kv_heads * qtiles * splits;
+    }
+    if (m.want_token[s]) {
+      if (o < m.n_out) {
+        maps.out_row[o] = ok ? r + nn_layout - 1 : -1;
+        maps.out_seq[o] = s;
+      }
+      ++o;
+    }
+    r += nn_layout;
+  }
+  __syncthreads();
+  if (t == 0) maps.item0[n] = counts_ok ? tot_items : 0;
+  if (!counts_ok) {  // the layout cannot be trusted: refuse every row
+    for (int i = t; i < m.n_rows; i += PREP_THREADS) maps.row_seq[i] = -1;
+    for (int i = t; i < m.n_out; i += PREP_THREADS) maps.out_row[i] = -1;
+    for (int i = t; i < n; i += PREP_THREADS) maps.item0[i] = 0;
+  } else {
+    for (int i = tot_rows + t; i < m.n_rows; i += PREP_THREADS) maps.row_seq[i] = -1;
+  }
+}
+
+hipError_t launch_prep(const StepMeta& m, const RowMaps& maps, const ModelDims& md,
+                       const AttnPlan& ap, uint32_t* status, hipStream_t st) {
+  prep_kernel<<<1, PREP_THREADS, 0, st>>>(m, maps, md, ap, status);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RMSNorm
+//
+// One workgroup of 256 threads per row. Each thread holds up to 32 values
+// (d_model <= 8192, d_model % 8 == 0): mean of squares in fp32, then
+// y = bf16(x * (1 / sqrt(ms + eps)) * g).
+
+#define NORM_THREADS 256
+#define NORM_MAX_CHUNKS 4  // 16-byte chunks per thread: d <= 256 * 8 * 4
+
+__device__ float block_sum_256(float v, float* red) {
+  v = wave_sum(v);
+  int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return s;
+}
+
+__device__ void norm_row(const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, int d,
+                         float eps, uint16_t* __restrict__ h, float* red) {
+  const int nch = d >> 3;
+  uint4 xv[NORM_MAX_CHUNKS];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NORM_MAX_CHUNKS; ++c) {
+    int ch = threadIdx.x + c * NORM_THREADS;
+    xv[c] = make_uint4(0, 0, 0, 0);
+    if (ch < nch) {
+      xv[c] = reinterpret_cast<const uint4*>(x)[ch];
+      uint32_t w[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float a = lo_bf(w[k]), b = hi_bf(w[k]);
+        ss += a * a + b * b;
+      }
+    }
+  }
+  float tot = block_sum_256(ss, red);
+  float inv = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+  for (int c = 0; c < NORM_MAX_CHUNKS; ++c) {
+    int ch = threadIdx.x + c * NORM_THREADS;
+    if (ch < nch) {
+      uint4 gv = reinterpret_cast<const uint4*>(g)[ch];
+      uint32_t w[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+      uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = pack_bf2(lo_bf(w[k]) * inv * lo_bf(gw[k]), hi_bf(w[k]) * inv * hi_bf(gw[k]));
+      reinterpret_cast<uint4*>(h)[ch] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(NORM_THREADS) void embed_norm_kernel(
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ row_seq,
+    const uint16_t* __restrict__ embed, const uint16_t* __restrict__ gain, int d, int vocab,
+    float eps, uint16_t* __restrict__ x, uint16_t* __restrict__ h, uint32_t* status) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  uint16_t* xr = x + (size_t)r * d;
+  int tok = tokens[r];
+  bool ok = row_seq[r] >= 0;
+  if (ok && (tok < 0 || tok >= vocab)) {
+    if (threadIdx.x == 0) raise_status(status, ST_BAD_TOKEN);
+    ok = false;
+  }
+  const int nch = d >> 3;
+  for (int ch = threadIdx.x; ch < nch; ch += NORM_THREADS)
+    reinterpret_cast<uint4*>(xr)[ch] =
+        ok ? reinterpret_cast<const uint4*>(embed + (size_t)tok * d)[ch] : make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  norm_row(xr, gain, d, eps, h + (size_t)r * d, red);
+}
+
+hipError_t launch_embed_norm(const int32_t* tokens, const int32_t* row_seq, int32_t R,
+                             const uint16_t* embed, const uint16_t* gain, const ModelDims& md,
+                             uint16_t* x, uint16_t* h, uint32_t* status, hipStream_t st) {
+  if (R <= 0) return hipSuccess;
+  embed_norm_kernel<<<R, NORM_THREADS, 0, st>>>(tokens, row_seq, embed, gain, md.d_model,
+                                                 md.vocab, md.rms_eps, x, h, status);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(NORM_THREADS) void rmsnorm_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ rows,
+    const uint16_t* __restrict__ gain, int d, float eps, uint16_t* __restrict__ h) {
+  __shared__ float red[4];
+  const int j = blockIdx.x;
+  int src = rows ? rows[j] : j;
+  if (src < 0) {  // refused row: zeros, so later stages see finite values
+    for (int ch = threadIdx.x; ch < (d >> 3); ch += NORM_THREADS)
+      reinterpret_cast<uint4*>(h + (size_t)j * d)[ch] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+  norm_row(x + (size_t)src * d, gain, d, eps, h + (size_t)j * d, red);
+}
+
+hipError_t launch_rmsnorm(const uint16_t* x, const int32_t* rows, int32_t R, const uint16_t* gain,
+                          int32_t d, float eps, uint16_t* h, hipStream_t st) {
+  if (R <= 0) return hipSuccess;
+  rmsnorm_kernel<<<R, NORM_THREADS, 0, st>>>(x, rows, gain, d, eps, h);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- RoPE + KV append
+//
+// Block (hd/2, 4): x = pair index i (element i pairs with i + hd/2), y = one
+// of four head slots. Head slots 0..Hq-1 are query heads (rotated into
+// q_out), then Hkv key heads (rotated, written into the K tile
+// [block][kvh][pos % bs][hd]) and Hkv value heads (written, dimension-major,
+// into the V tile [block][kvh][hd][pos % bs]). The rotation reads a host-built
+// table of (cos, sin) per (position, i).
+
+__global__ void rope_append_kernel(const uint16_t* __restrict__ qkv, int R,
+                                   const int32_t* __restrict__ row_seq,
+                                   const int32_t* __restrict__ row_pos,
+                                   const int32_t* __restrict__ tables, int max_blocks_per_seq,
+                                   const float2* __restrict__ rope_cs, int hq, int hkv, int hd,
+                                   int bs, int num_blocks, uint16_t* __restrict__ q_out,
+                                   uint16_t* __restrict__ pool_k, uint16_t* __restrict__ pool_v,
+                                   uint32_t* status) {
+  const int slots = hq + 2 * hkv;
+  const int groups = (slots + 3) / 4;
+  const int r = blockIdx.x / groups;
+  const int j = (blockIdx.x % groups) * 4 + threadIdx.y;
+  const int i = threadIdx.x;
+  const int half = hd >> 1;
+  if (r >= R || j >= slots) return;
+  const int s = row_seq[r];
+  if (s < 0) return;
+  const int pos = row_pos[r];
+  const uint16_t* src = qkv + (size_t)r * slots * hd + (size_t)j * hd;
+  float a = bf2f(src[i]), b = bf2f(src[i + half]);
+  if (j < hq + hkv) {
+    float2 cs = rope_cs[(size_t)pos * half + i];
+    float ra = a * cs.x - b * cs.y;
+    float rb = b * cs.x + a * cs.y;
+    a = ra;
+    b = rb;
+  }
+  if (j < hq) {
+    uint16_t* dst = q_out + (size_t)r * hq * hd + (size_t)j * hd;
+    dst[i] = f2bf(a);
+    dst[i + half] = f2bf(b);
+    return;
+  }
+  const int blk = tables[(size_t)s * max_blocks_per_seq + pos / bs];
+  if (blk < 0 || blk >= num_blocks) {
+    if (i == 0) raise_status(status, ST_BAD_BLOCK);
+    return;
+  }
+  const int off = pos % bs;
+  if (j < hq + hkv) {
+    const int g = j - hq;
+    uint16_t* dst = pool_k + (((size_t)blk * hkv + g) * bs + off) * hd;
+    dst[i] = f2bf(a);
+    dst[i + half] = f2bf(b);
+  } else {
+    const int g = j - hq - hkv;
+    uint16_t* dst = pool_v + ((size_t)blk * hkv + g) * hd * bs + off;
+    dst[(size_t)i * bs] = f2bf(a);
+    dst[(size_t)(i + half) * bs] = f2bf(b);
+  }
+}
+
+hipError_t launch_rope_append(const uint16_t* qkv, int32_t R, const StepMeta& m,
+                              const RowMaps& maps, const float* rope_cs, const ModelDims& md,
+                              uint16_t* q_out, uint16_t* pool_k, uint16_t* pool_v,
+                              uint32_t* status, hipStream_t st) {
+  if (R <= 0) return hipSuccess;
+  const int slots = md.n_heads + 2 * md.n_kv_heads;
+  const int groups = (slots + 3) / 4;
+  dim3 block(md.head_dim / 2, 4);
+  rope_append_kernel<<<R * groups, block, 0, st>>>(
+      qkv, R, maps.row_seq, maps.row_pos, m.block_tables, m.max_blocks_per_seq,
+      reinterpret_cast<const float2*>(rope_cs), md.n_heads, md.n_kv_heads, md.head_dim,
+      md.block_size, md.num_blocks, q_out, pool_k, pool_v, status);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------- argmax combine
+//
+// One wave per row: the maximum over the per-tile partials, lowest id on
+// equal values (ids are unique per partial, so the order is total).
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* __restrict__ val,
+                                                           const int32_t* __restrict__ idx,
+                                                           int n_tiles, int stride,
+                                                           int32_t* __restrict__ tokens) {
+  const int j = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int t = threadIdx.x; t < n_tiles; t += 64) {
+    float v = val[(size_t)j * stride + t];
+    int i = idx[(size_t)j * stride + t];
+    if (better(v, i, bv, bi)) {
+      bv = v;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v = __shfl_xor(bv, o, 64);
+    int i = __shfl_xor(bi, o, 64);
+    if (better(v, i, bv, bi)) {
+      bv = v;
+      bi = i;
+    }
+  }
+  if (threadIdx.x == 0) tokens[j] = bi == 0x7fffffff ? 0 : bi;
+}
+
+hipError_t launch_argmax_reduce(const float* amax_val, const int32_t* amax_idx, int32_t n_tiles,
+                                int32_t stride, int32_t n, int32_t* tokens, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  argmax_reduce_kernel<<<n, 64, 0, st>>>(amax_val, amax_idx, n_tiles, stride, tokens);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- fill
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t step = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += step) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  fill_u32_kernel<<<(unsigned)blocks, 256, 0, st>>>(p, value, n);
+  return hipGetLastError();
+}
+
+}  // namespace cbd

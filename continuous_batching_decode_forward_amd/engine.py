@@ -1,0 +1,144 @@
+"""Python-side plumbing around the C ABI: device buffers come from PyTorch
+(memory and streams only), everything else goes through libcbd.so.
+
+    eng = Engine(shape, weights, block_size=32, num_blocks=..., ...)
+    meta = eng.upload_step(slots, tables, ctx_lens, n_new, tokens, want, step_ids)
+    eng.step_forward(meta, logits_out, tokens_out)
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream) -> C.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class StepMeta:
+    """Device copy of one step's metadata (one int32 buffer) + host scalars."""
+    buf: torch.Tensor
+    step: B.cbd_step
+    n_seqs: int
+    n_rows: int
+    n_out: int
+
+
+class Engine:
+    def __init__(self, shape, weights: dict, *, block_size: int, num_blocks: int,
+                 max_blocks_per_seq: int, max_slots: int, max_rows: int, max_seqs: int,
+                 max_position: int, block_order=None, device="cuda", stream=None):
+        self.shape = shape
+        self.device = torch.device(device)
+        cfg = B.cbd_config()
+        cfg.n_layers, cfg.d_model, cfg.n_heads = shape.n_layers, shape.d_model, shape.n_heads
+        cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim = shape.n_kv_heads, shape.head_dim, shape.ffn_dim
+        cfg.vocab, cfg.block_size, cfg.num_blocks = shape.vocab, block_size, num_blocks
+        cfg.max_blocks_per_seq, cfg.max_slots, cfg.max_rows = max_blocks_per_seq, max_slots, max_rows
+        cfg.max_seqs, cfg.max_position = max_seqs, max_position
+        cfg.rms_eps, cfg.rope_base = shape.rms_eps, shape.rope_base
+        self.cfg = cfg
+        self.block_size, self.num_blocks = block_size, num_blocks
+        self.max_blocks_per_seq = max_blocks_per_seq
+        self.kv_pool = torch.empty(B.cbd_kv_pool_bytes(cfg), dtype=torch.uint8, device=self.device)
+        self.slot_state = torch.empty(B.cbd_slot_state_bytes(cfg), dtype=torch.uint8,
+                                      device=self.device)
+        self.workspace = torch.empty(B.cbd_workspace_bytes(cfg), dtype=torch.uint8,
+                                     device=self.device)
+        self.weights = weights  # keep alive
+        w = B.cbd_weights()
+        w.embed, w.final_norm, w.lm_head = (weights["embed"].data_ptr(),
+                                            weights["final_norm"].data_ptr(),
+                                            weights["lm_head"].data_ptr())
+        self._arrs = {}
+        for k in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate", "w_up", "w_down"):
+            arr = (C.c_void_p * shape.n_layers)(*[t.data_ptr() for t in weights[k]])
+            self._arrs[k] = arr
+            setattr(w, k, C.cast(arr, C.POINTER(C.c_void_p)))
+        self._w = w
+        self.stream = stream
+        self.handle = B.cbd_engine_create(cfg, w, _ptr(self.kv_pool), _ptr(self.slot_state),
+                                          _ptr(self.workspace), block_order,
+                                          _stream_ptr(stream))
+
+    # ---------------------------------------------------------- pool views
+    def kv_views(self, layer: int):
+        """(K, V) bf16 views of one layer's pool regions:
+        K [num_blocks][Hkv][block_size][hd], V [num_blocks][Hkv][hd][block_size]."""
+        s = self.shape
+        per = self.num_blocks * s.n_kv_heads * self.block_size * s.head_dim
+        flat = self.kv_pool.view(torch.bfloat16)
+        k = flat[(2 * layer) * per:(2 * layer + 1) * per].view(
+            self.num_blocks, s.n_kv_heads, self.block_size, s.head_dim)
+        v = flat[(2 * layer + 1) * per:(2 * layer + 2) * per].view(
+            self.num_blocks, s.n_kv_heads, s.head_dim, self.block_size)
+        return k, v
+
+    # ---------------------------------------------------------------- step
+    def upload_step(self, slots, block_tables, ctx_lens, n_new, tokens, want_token,
+                    step_ids=None, mode=B.CBD_MODE_GREEDY, max_ctx=None, stream=None) -> StepMeta:
+        """Copy host metadata into one device int32 buffer and describe it."""
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        n = len(ctx_lens)
+        parts = [np.asarray(slots, np.int32), bt.reshape(-1), np.asarray(ctx_lens, np.int32),
+                 np.asarray(n_new, np.int32), np.asarray(tokens, np.int32),
+                 np.asarray(want_token, np.int32),
+                 np.asarray(step_ids if step_ids is not None else np.zeros(n), np.int32)]
+        host = np.concatenate(parts)
+        buf = torch.from_numpy(host).to(self.device, non_blocking=False)
+        offs = np.cumsum([0] + [len(p) for p in parts])
+        st = B.cbd_step()
+        st.n_seqs = n
+        st.n_rows = int(np.sum(n_new))
+        st.n_out = int(np.count_nonzero(want_token))
+        ctx = np.asarray(ctx_lens, np.int64) + np.asarray(n_new, np.int64)
+        st.max_ctx = int(max_ctx if max_ctx is not None else ctx.max())
+        st.max_blocks_per_seq = bt.shape[1]
+        st.mode = mode
+        base = buf.data_ptr()
+        names = ["slots", "block_tables", "ctx_lens", "n_new", "tokens", "want_token", "step_ids"]
+        for name, o in zip(names, offs[:-1]):
+            setattr(st, name, base + 4 * int(o))
+        return StepMeta(buf, st, n, st.n_rows, st.n_out)
+
+    def step_forward(self, meta: StepMeta, logits_out: torch.Tensor | None,
+                     tokens_out: torch.Tensor, stream=None) -> None:
+        B.cbd_step_forward(self.handle, meta.step, _ptr(logits_out), _ptr(tokens_out),
+                           _stream_ptr(stream))
+
+    def sample_logits(self, logits: torch.Tensor, slots: torch.Tensor, step_ids: torch.Tensor,
+                      tokens_out: torch.Tensor, stream=None) -> None:
+        B.cbd_sample_logits(self.handle, _ptr(logits), logits.shape[0], _ptr(slots),
+                            _ptr(step_ids), _ptr(tokens_out), _stream_ptr(stream))
+
+    def status(self, stream=None) -> int:
+        return B.cbd_engine_status(self.handle, _stream_ptr(stream))
+
+    def slot_counts(self) -> torch.Tensor:
+        """The per-slot penalty counts [max_slots][vocab] fp32 (a view)."""
+        s = self.cfg
+        params_bytes = (s.max_slots * 40 + 255) // 256 * 256
+        return self.slot_state[params_bytes:params_bytes + s.max_slots * s.vocab * 4].view(
+            torch.float32).view(s.max_slots, s.vocab)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            B.cbd_engine_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

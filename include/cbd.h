@@ -1,0 +1,319 @@
+/*
+ * cbd.h -- C ABI of the continuous-batching decode forward step for AMD
+ * MI355X (gfx950).
+ *
+ * One call of cbd_step_forward is one iteration of iteration-level
+ * scheduling: it reads the decoder weights once and produces one next token
+ * for each in-flight sequence that asks for one (Go under the hood,
+ * section 20.3.2: a step costs about (W + B*A)/beta -- W weight bytes, A
+ * per-sequence bytes, beta bandwidth -- so B sequences share one weight
+ * read). Per-sequence KV state lives in a paged pool of fixed-size blocks
+ * reached through per-sequence block tables (same section: PagedAttention's
+ * fixed-size blocks allocated on demand). A prefill chunk may share the step
+ * with decode rows, and a batched sampler closes it (RWKV-Runner Albatross
+ * article, "Worker main loop": penalties, temperature, top-p/top-k sampling
+ * over the decode segment).
+ *
+ * Conventions for every function below:
+ *  - Return value: CBD_OK (0) or a negative CBD_E_* code; the message of
+ *    the last failure on the calling thread is cbd_last_error().
+ *    No C++ exception crosses this boundary.
+ *  - "device" pointers are HIP device memory; "host" pointers are ordinary
+ *    host memory. The caller allocates and owns every device buffer
+ *    (weights, KV pool, slot state, workspace, step metadata, outputs) and
+ *    keeps it alive until the work that uses it has completed. The library
+ *    allocates no device memory; it owns only host-side state (allocator
+ *    free lists, the composer, the handle).
+ *  - Streams are hipStream_t passed as void*; NULL is the default stream.
+ *    Device work is enqueued asynchronously on the given stream.
+ *  - One engine is driven by one host thread at a time (the Kestrel page,
+ *    "0.8MB 跑通 Qwen" 14-1 section 2: a single engine thread is the only
+ *    caller of the batched forward). Calls on one engine from several
+ *    threads at once are not supported.
+ *  - bf16 is the 16-bit brain float, stored as uint16_t bit patterns.
+ */
+#ifndef CBD_H
+#define CBD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CBD_OK 0
+#define CBD_E_INVAL (-1)       /* bad argument, shape or metadata */
+#define CBD_E_NOSLOT (-2)      /* every slot is taken */
+#define CBD_E_NOBLOCKS (-3)    /* the block pool cannot satisfy the request;
+                                  the caller waits, nothing is evicted */
+#define CBD_E_UNSUPPORTED (-4) /* a shape outside what the kernels support;
+                                  never silently replaced by another path */
+#define CBD_E_DEVICE (-5)      /* a HIP runtime error */
+
+/* Device-side status bits reported by cbd_engine_status (set by kernels
+ * that met metadata they refused to act on; the offending rows are skipped
+ * and their outputs are left unspecified). */
+#define CBD_STATUS_BAD_BLOCK 0x1u   /* block id outside [0, num_blocks) */
+#define CBD_STATUS_BAD_TOKEN 0x2u   /* token id outside [0, vocab) */
+#define CBD_STATUS_BAD_SLOT 0x4u    /* slot outside [0, max_slots) */
+#define CBD_STATUS_BAD_SHAPE 0x8u   /* n_new < 1, ctx < 0, ctx + n_new beyond
+                                       the table, or the row/output counts
+                                       disagree with the host scalars */
+
+/* ------------------------------------------------------------------ config */
+
+typedef struct cbd_config {
+  /* decoder shape: pre-norm blocks (RMSNorm -> attention -> residual,
+   * RMSNorm -> SwiGLU FFN -> residual), final RMSNorm, untied LM head */
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_heads;    /* query heads */
+  int32_t n_kv_heads; /* KV heads; query head h reads KV head h*n_kv/n_heads */
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t ffn_dim;
+  int32_t vocab;      /* embedding rows = LM-head rows */
+  /* paged KV pool */
+  int32_t block_size; /* positions per block: 4, 8, 16, 32 or 64 */
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  /* per-step limits */
+  int32_t max_slots;  /* sequences that may hold sampler state */
+  int32_t max_rows;   /* rows per step (decode rows + prefill tokens) */
+  int32_t max_seqs;   /* sequences per step */
+  int32_t max_position; /* positions covered by the RoPE table */
+  float rms_eps;
+  float pad0_;
+  double rope_base;
+} cbd_config;
+
+/* Weights: every pointer is device memory holding bf16, row-major.
+ * Per-layer fields are HOST arrays of n_layers device pointers; the engine
+ * copies the pointer values at create time. */
+typedef struct cbd_weights {
+  const void* embed;        /* [vocab][d_model] */
+  const void* final_norm;   /* [d_model] */
+  const void* lm_head;      /* [vocab][d_model] */
+  const void* const* attn_norm; /* [d_model] */
+  const void* const* w_qkv;     /* [(n_heads + 2*n_kv_heads)*head_dim][d_model]:
+                                   q rows, then k rows, then v rows */
+  const void* const* w_o;       /* [d_model][n_heads*head_dim] */
+  const void* const* ffn_norm;  /* [d_model] */
+  const void* const* w_gate;    /* [ffn_dim][d_model] */
+  const void* const* w_up;      /* [ffn_dim][d_model] */
+  const void* const* w_down;    /* [d_model][ffn_dim] */
+} cbd_weights;
+
+/* Per-slot sampling parameters (Albatross adapter defaults: temperature
+ * 1.0, top_p 0.3, top_k 0, frequency penalty 1, penalty decay 0.996). */
+typedef struct cbd_sampling {
+  float temperature;      /* 0 = greedy on the penalised logits */
+  float top_p;            /* >= 1 disables top-p */
+  int32_t top_k;          /* 0 disables top-k */
+  float freq_penalty;
+  float presence_penalty;
+  float penalty_decay;
+  uint64_t seed;          /* key of the counter-based draw */
+} cbd_sampling;
+
+/* Buffer sizes for a configuration (bytes). The KV pool layout is
+ * [n_layers][2][num_blocks][n_kv_heads][tile], one tile per (block, KV
+ * head): K tiles are [block_size][head_dim] (position-major), V tiles are
+ * [head_dim][block_size] (dimension-major), all bf16. The block-id space is
+ * shared by all layers. */
+int cbd_kv_pool_bytes(const cbd_config* cfg, size_t* bytes);
+int cbd_slot_state_bytes(const cbd_config* cfg, size_t* bytes);
+int cbd_workspace_bytes(const cbd_config* cfg, size_t* bytes);
+
+/* ------------------------------------------------------------------ engine */
+
+typedef struct cbd_engine cbd_engine;
+
+/* Create an engine over caller-owned device buffers of at least the sizes
+ * above. block_order (host, nullable) seeds the FIFO block free list with a
+ * permutation of 0..num_blocks-1 (NULL: ascending). stream: where the
+ * engine's own set-up work and slot resets are enqueued. Returns
+ * CBD_E_UNSUPPORTED for shapes the kernels do not handle (head_dim not in
+ * {64, 128}, n_heads/n_kv_heads not dividing 16, d_model or ffn_dim not a
+ * multiple of 64, ...). */
+int cbd_engine_create(const cbd_config* cfg, const cbd_weights* weights, void* kv_pool,
+                      void* slot_state, void* workspace, const int32_t* block_order,
+                      void* stream, cbd_engine** out);
+int cbd_engine_destroy(cbd_engine* e);
+
+/* Slots (per-sequence sampler state: penalty counts over the vocabulary
+ * and the sampling parameters; the Albatross worker keeps them as
+ * preallocated per-slot tensors). cbd_slot_alloc returns the lowest free
+ * slot id, stores params and request_id (the draw's counter) and enqueues a
+ * reset of the slot's counts to zero on the engine stream.
+ * cbd_slot_free may be called at any step boundary (a request aborted by
+ * its client stops alone). */
+int cbd_slot_alloc(cbd_engine* e, const cbd_sampling* params, uint64_t request_id,
+                   int32_t* slot_out);
+int cbd_slot_free(cbd_engine* e, int32_t slot);
+
+/* Blocks. cbd_block_alloc is all-or-nothing: it pops n ids from the front
+ * of the FIFO free list into ids_out (host) or returns CBD_E_NOBLOCKS and
+ * takes none. cbd_block_free appends ids (host) to the back, in order;
+ * freeing an id that is not allocated is CBD_E_INVAL. */
+int cbd_block_alloc(cbd_engine* e, int32_t n, int32_t* ids_out);
+int cbd_block_free(cbd_engine* e, int32_t n, const int32_t* ids);
+int cbd_blocks_available(const cbd_engine* e);
+
+/* ------------------------------------------------------------------- step */
+
+#define CBD_MODE_GREEDY 0 /* argmax of the raw logits, lowest id on ties */
+#define CBD_MODE_SAMPLE 1 /* the per-slot batched sampler */
+
+/* One step. Host scalars size the launch; the arrays are DEVICE memory.
+ * Sequences are taken in the given order; sequence s contributes n_new[s]
+ * consecutive entries of `tokens` (decode rows: 1; a prefill chunk: up to
+ * 512), at positions ctx_lens[s] .. ctx_lens[s] + n_new[s] - 1, where
+ * ctx_lens[s] counts the positions already in the pool. Row i of a chunk
+ * attends to positions 0 .. ctx_lens[s] + i. Every row's K and V are
+ * appended through the sequence's block table before attention. */
+typedef struct cbd_step {
+  int32_t n_seqs;             /* 1 .. max_seqs */
+  int32_t n_rows;             /* sum of n_new, 1 .. max_rows */
+  int32_t n_out;              /* number of sequences with want_token != 0 */
+  int32_t max_ctx;            /* host upper bound of ctx_lens[s] + n_new[s] */
+  int32_t max_blocks_per_seq; /* row stride of block_tables */
+  int32_t mode;               /* CBD_MODE_GREEDY or CBD_MODE_SAMPLE */
+  const int32_t* slots;        /* [n_seqs] sampler slot of each sequence */
+  const int32_t* block_tables; /* [n_seqs][max_blocks_per_seq] block ids */
+  const int32_t* ctx_lens;     /* [n_seqs] */
+  const int32_t* n_new;        /* [n_seqs] */
+  const int32_t* tokens;       /* [n_rows] */
+  const int32_t* want_token;   /* [n_seqs] 0/1: emit a token from the last row */
+  const int32_t* step_ids;     /* [n_seqs] index of the token being generated
+                                  (the draw's counter); unused when greedy */
+} cbd_step;
+
+/* Run one step on `stream`. Outputs (device) have one entry per sequence
+ * with want_token, in sequence order: logits_out [n_out][vocab] fp32
+ * (nullable when not wanted) and tokens_out [n_out] int32. Asynchronous.
+ * Host-checkable errors return CBD_E_INVAL before anything is enqueued;
+ * bad device metadata is refused row by row on the device and reported
+ * through cbd_engine_status. */
+int cbd_step_forward(cbd_engine* e, const cbd_step* step, float* logits_out,
+                     int32_t* tokens_out, void* stream);
+
+/* The batched sampler alone, over caller-given fp32 logits [n][vocab]
+ * (device): row j uses slot slots[j] and draw counter step_ids[j] (device
+ * arrays). Updates the slots' penalty counts like a sampled step. */
+int cbd_sample_logits(cbd_engine* e, const float* logits, int32_t n, const int32_t* slots,
+                      const int32_t* step_ids, int32_t* tokens_out, void* stream);
+
+/* Wait for the engine's device status word on `stream`, return it in
+ * *flags and clear it (CBD_STATUS_* bits). */
+int cbd_engine_status(cbd_engine* e, void* stream, uint32_t* flags);
+
+const char* cbd_last_error(void);
+
+/* ------------------------------------------------------------- profiling */
+
+/* Kernel classes that can be timed inside cbd_step_forward. */
+#define CBD_KERNEL_QKV 1       /* QKV projection */
+#define CBD_KERNEL_ROPE 2      /* RoPE + KV append */
+#define CBD_KERNEL_ATTN 3      /* paged attention + split combine */
+#define CBD_KERNEL_O 4         /* O projection + residual */
+#define CBD_KERNEL_GATEUP 5    /* gate/up projection + SwiGLU */
+#define CBD_KERNEL_DOWN 6      /* down projection + residual */
+#define CBD_KERNEL_LM_HEAD 7   /* final norm's consumer: LM head + argmax partials */
+#define CBD_KERNEL_SAMPLE 8    /* argmax combine or the sampler */
+#define CBD_KERNEL_NORM 9      /* embedding + RMSNorms */
+
+/* From now on, every launch of that class inside cbd_step_forward is
+ * bracketed by a pair of HIP events recorded on the step's stream (a marker
+ * each, nothing else changes). At most 65536 launches are kept. */
+int cbd_profile_begin(cbd_engine* e, int32_t kernel_class);
+/* Stop recording, wait for the recorded events, and return the summed
+ * duration (milliseconds) and the number of launches timed. */
+int cbd_profile_end(cbd_engine* e, double* total_ms, int32_t* launches);
+
+/* --------------------------------------------------------------- composer */
+
+/* The host step composer: Forma's "Scheduler" (Go under the hood section
+ * 20.3.2), kept apart from the step so that an admission bug and a batching
+ * bug can be told apart. */
+
+#define CBD_ADMIT_RESERVE 0       /* reserve prompt + answer blocks at
+                                     admission (every admitted request can
+                                     finish) */
+#define CBD_ADMIT_FREE_SLOT 1     /* admit on any free slot, take blocks on
+                                     demand (can exhaust the pool) */
+#define CBD_ADMIT_REQUEST_LEVEL 2 /* static batching: admit a new group only
+                                     when the batch is empty */
+
+#define CBD_FINISH_EOS 1
+#define CBD_FINISH_LENGTH 2
+#define CBD_FINISH_ABORT 3
+
+typedef struct cbd_sched_config {
+  int32_t max_slots;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t max_rows;   /* row budget of one step */
+  int32_t chunk_size; /* prefill chunk length (Forma: 512) */
+  int32_t eos_id;
+  int32_t policy;     /* CBD_ADMIT_* */
+} cbd_sched_config;
+
+/* One planned step, in host memory owned by the composer and valid until
+ * the next cbd_sched_plan. Copy the arrays to the device and fill a
+ * cbd_step from them. block_tables is [n_seqs][max_blocks_per_seq], unused
+ * entries -1. */
+typedef struct cbd_plan {
+  int32_t n_seqs, n_rows, n_out, max_ctx, max_blocks_per_seq;
+  int32_t n_prefill_rows, n_decode_rows;
+  int32_t stalled; /* no row can run although sequences are active */
+  const int32_t* slots;
+  const int32_t* block_tables;
+  const int32_t* ctx_lens;
+  const int32_t* n_new;
+  const int32_t* tokens;
+  const int32_t* want_token;
+  const int32_t* step_ids;
+  const uint64_t* request_ids;
+} cbd_plan;
+
+typedef struct cbd_sched_stats {
+  int32_t queued, active, free_slots, free_blocks;
+  int64_t steps, finished;
+} cbd_sched_stats;
+
+typedef struct cbd_sched cbd_sched;
+
+/* engine (nullable): when given, slots and blocks come from the engine's
+ * allocators (slot allocation resets the slot's sampler state on the
+ * device), and block_order is ignored; when NULL the composer keeps its own
+ * host-only allocators seeded by block_order (nullable, ascending). */
+int cbd_sched_create(const cbd_sched_config* cfg, cbd_engine* engine,
+                     const int32_t* block_order, cbd_sched** out);
+int cbd_sched_destroy(cbd_sched* s);
+/* Queue a request (host prompt). CBD_E_INVAL if the prompt is empty,
+ * max_new < 1 or prompt + answer can never fit a sequence's table or the
+ * pool. params may be NULL (greedy defaults). */
+int cbd_sched_submit(cbd_sched* s, const int32_t* prompt, int32_t prompt_len,
+                     int32_t max_new, const cbd_sampling* params, uint64_t request_id);
+/* Retire nothing, admit what the policy allows, compose the next step. */
+int cbd_sched_plan(cbd_sched* s, cbd_plan* out);
+/* Hand back the step's tokens (host, n = plan.n_out, sequence order):
+ * append, advance positions, retire on EOS or length (freeing slot and
+ * blocks). */
+int cbd_sched_commit(cbd_sched* s, const int32_t* tokens, int32_t n);
+/* Abort a queued or active request at a step boundary. CBD_E_INVAL if
+ * unknown. */
+int cbd_sched_abort(cbd_sched* s, uint64_t request_id);
+/* Pop the oldest finished request: returns 1 and fills the outputs, or 0
+ * when none is left. */
+int cbd_sched_pop_finished(cbd_sched* s, uint64_t* request_id, int32_t* reason,
+                           int32_t* n_generated);
+int cbd_sched_stats_get(const cbd_sched* s, cbd_sched_stats* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CBD_H */

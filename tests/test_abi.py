@@ -1,0 +1,76 @@
+"""The C-ABI library loads without a GPU and exports every function that
+include/cbd.h declares; host-side argument checks and size queries work."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from continuous_batching_decode_forward_amd import binding as B
+from continuous_batching_decode_forward_amd import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "cbd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cbd_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    L = B.lib()
+    names = declared_functions()
+    assert len(names) >= 20
+    bound = {n for n, _, _ in B.SIGNATURES}
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+        assert n in bound, f"{n} has no binding"
+
+
+def make_cfg(shape=configs.LLAMA8B_1L, **kw):
+    c = B.cbd_config()
+    c.n_layers, c.d_model, c.n_heads = shape.n_layers, shape.d_model, shape.n_heads
+    c.n_kv_heads, c.head_dim, c.ffn_dim, c.vocab = (shape.n_kv_heads, shape.head_dim,
+                                                    shape.ffn_dim, shape.vocab)
+    c.block_size, c.num_blocks, c.max_blocks_per_seq = 32, 1000, 129
+    c.max_slots, c.max_rows, c.max_seqs, c.max_position = 64, 64, 64, 4200
+    c.rms_eps, c.rope_base = 1e-5, 10000.0
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_size_queries_follow_the_documented_layout():
+    c = make_cfg()
+    kv = B.cbd_kv_pool_bytes(c)
+    assert kv == 1 * 2 * 1000 * 8 * 32 * 128 * 2
+    assert B.cbd_slot_state_bytes(c) >= 64 * 128256 * 4
+    assert B.cbd_workspace_bytes(c) > 64 * 4096 * 2
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, B.CBD_E_UNSUPPORTED), ("block_size", 12, B.CBD_E_UNSUPPORTED),
+    ("n_kv_heads", 3, B.CBD_E_INVAL), ("n_kv_heads", 1, B.CBD_E_UNSUPPORTED),
+    ("d_model", 4100, B.CBD_E_UNSUPPORTED), ("num_blocks", 0, B.CBD_E_INVAL),
+    ("max_seqs", 65, B.CBD_E_INVAL)])
+def test_config_errors(field, value, code):
+    c = make_cfg(**{field: value})
+    with pytest.raises(B.CbdError) as ei:
+        B.cbd_workspace_bytes(c)
+    assert ei.value.code == code
+    assert B.cbd_last_error()
+
+
+def test_engine_create_rejects_null_buffers():
+    c = make_cfg()
+    w = B.cbd_weights()
+    h = C.c_void_p()
+    rc = B.lib().cbd_engine_create(C.byref(c), C.byref(w), None, None, None, None, None,
+                                   C.byref(h))
+    assert rc == B.CBD_E_INVAL
+
+
+def test_step_rejects_null_engine():
+    st = B.cbd_step()
+    assert B.lib().cbd_step_forward(None, C.byref(st), None, None, None) == B.CBD_E_INVAL

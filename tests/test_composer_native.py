@@ -1,0 +1,142 @@
+"""The native composer (cbd_sched_*, host C++) against the composer's
+reference model, bit for bit: slots, block tables, row order, positions,
+want flags, step ids, admissions and retirements, on the scaled-down figure
+constants of Go under the hood 20.3.2 and on seeded random request streams."""
+import numpy as np
+import pytest
+
+from continuous_batching_decode_forward_amd import binding as B
+from continuous_batching_decode_forward_amd import synth
+from oracle.composer_ref import ComposerRef
+
+POLICIES = [B.CBD_ADMIT_RESERVE, B.CBD_ADMIT_FREE_SLOT, B.CBD_ADMIT_REQUEST_LEVEL]
+
+
+def fake_token(rid, pos, n_gen, eos_every):
+    if eos_every and (rid * 13 + n_gen * 7) % eos_every == 0 and n_gen > 0:
+        return 0
+    return 1 + (rid * 7919 + pos * 104729) % 997
+
+
+def run_both(requests, *, slots, bs, pool, rows, chunk, policy, mbps, order, steps=300,
+             eos_every=0):
+    cfg = B.cbd_sched_config()
+    cfg.max_slots, cfg.block_size, cfg.num_blocks = slots, bs, pool
+    cfg.max_blocks_per_seq, cfg.max_rows, cfg.chunk_size = mbps, rows, chunk
+    cfg.eos_id, cfg.policy = 0, policy
+    nat = B.cbd_sched_create(cfg, None, order)
+    ref = ComposerRef(slots, bs, pool, rows, chunk, 0, policy, block_order=list(order),
+                      max_blocks_per_seq=mbps)
+    pending = sorted(range(len(requests)), key=lambda i: requests[i][0])
+    fin_nat, fin_ref = [], []
+    try:
+        for step in range(steps):
+            while pending and requests[pending[0]][0] <= step:
+                i = pending.pop(0)
+                _, prompt, mx = requests[i]
+                B.cbd_sched_submit(nat, prompt, mx, None, i)
+                ref.submit(i, prompt, mx)
+            p = B.cbd_sched_plan(nat)
+            q = ref.plan()
+            n = p.n_seqs
+            assert n == len(q.slots)
+            assert n == 0 or list(p.slots[:n]) == q.slots
+            assert list(p.ctx_lens[:n]) == q.ctx_lens
+            assert list(p.n_new[:n]) == q.n_new
+            assert list(p.tokens[:p.n_rows]) == q.tokens
+            assert list(p.want_token[:n]) == q.want_token
+            assert list(p.step_ids[:n]) == q.step_ids
+            assert list(p.request_ids[:n]) == q.request_ids
+            tab = np.ctypeslib.as_array(p.block_tables, shape=(n * mbps,)) if n else []
+            for s in range(n):
+                row = tab[s * mbps:(s + 1) * mbps]
+                k = len(q.block_tables[s])
+                assert list(row[:k]) == q.block_tables[s] and np.all(row[k:] == -1)
+            assert bool(p.stalled) == q.stalled
+            if q.stalled:
+                return "stalled", fin_nat, fin_ref
+            toks = []
+            for s in range(n):
+                if q.want_token[s]:
+                    toks.append(fake_token(q.request_ids[s], q.ctx_lens[s] + q.n_new[s] - 1,
+                                           q.step_ids[s], eos_every))
+            B.cbd_sched_commit(nat, toks)
+            ref.commit(toks)
+            while True:
+                f = B.cbd_sched_pop_finished(nat)
+                if f is None:
+                    break
+                fin_nat.append(f)
+            while ref.finished:
+                rid, why, gen = ref.finished.pop(0)
+                fin_ref.append((rid, why, len(gen)))
+            assert fin_nat == fin_ref
+            st = B.cbd_sched_stats_get(nat)
+            assert st.free_blocks == len(ref.free_blocks)
+            assert st.active == len(ref.active) and st.queued == len(ref.queue)
+            if not pending and not ref.queue and not ref.active:
+                return "done", fin_nat, fin_ref
+        return "running", fin_nat, fin_ref
+    finally:
+        B.cbd_sched_destroy(nat)
+
+
+FIGURE = [(0, 10, 30), (0, 14, 26), (1, 6, 34), (2, 16, 22), (3, 9, 28), (5, 12, 30), (6, 7, 31)]
+
+
+@pytest.mark.parametrize("policy", POLICIES)
+def test_figure_scenario_matches_reference(policy):
+    reqs = [(a, [1 + (i * 31 + j) % 50 for j in range(pl)], mx)
+            for i, (a, pl, mx) in enumerate(FIGURE)]
+    order = list(synth.permutation(0, "figure", 24))
+    state, fin, _ = run_both(reqs, slots=4, bs=4, pool=24, rows=12, chunk=8, policy=policy,
+                             mbps=24, order=order)
+    if policy == B.CBD_ADMIT_FREE_SLOT:
+        assert state == "stalled"
+    else:
+        assert state == "done" and len(fin) == len(FIGURE)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+@pytest.mark.parametrize("policy", POLICIES)
+def test_random_streams_match_reference(seed, policy):
+    n = 40
+    arr = synth.uniform_ints(seed, "arrive", n, 0, 60)
+    plen = synth.uniform_ints(seed, "plen", n, 1, 70)
+    mx = synth.uniform_ints(seed, "maxnew", n, 1, 40)
+    reqs = [(int(arr[i]), list(synth.uniform_ints(seed, f"p{i}", int(plen[i]), 1, 500)),
+             int(mx[i])) for i in range(n)]
+    pool = 160
+    state, fin, _ = run_both(reqs, slots=8, bs=8, pool=pool, rows=40, chunk=16, policy=policy,
+                             mbps=20, order=list(synth.permutation(seed, "b", pool)),
+                             eos_every=9, steps=600)
+    if policy != B.CBD_ADMIT_FREE_SLOT:
+        assert state == "done" and len(fin) == n
+
+
+def test_submit_and_commit_errors():
+    cfg = B.cbd_sched_config()
+    cfg.max_slots, cfg.block_size, cfg.num_blocks = 2, 4, 8
+    cfg.max_blocks_per_seq, cfg.max_rows, cfg.chunk_size, cfg.eos_id = 4, 8, 8, 0
+    s = B.cbd_sched_create(cfg, None, None)
+    try:
+        with pytest.raises(B.CbdError):
+            B.cbd_sched_submit(s, [], 4, None, 1)
+        with pytest.raises(B.CbdError):
+            B.cbd_sched_submit(s, [1] * 10, 10, None, 1)   # 5 blocks > 4 per sequence
+        with pytest.raises(B.CbdError):
+            B.cbd_sched_commit(s, [1])                       # no plan yet
+        B.cbd_sched_submit(s, [1, 2, 3], 2, None, 7)
+        p = B.cbd_sched_plan(s)
+        assert p.n_seqs == 1 and p.n_out == 1
+        with pytest.raises(B.CbdError):
+            B.cbd_sched_commit(s, [1, 2])                    # wrong count
+        B.cbd_sched_commit(s, [5])
+        B.cbd_sched_abort(s, 7)
+        assert B.cbd_sched_pop_finished(s) == (7, B.CBD_FINISH_ABORT, 1)
+        with pytest.raises(B.CbdError):
+            B.cbd_sched_abort(s, 7)
+        st = B.cbd_sched_stats_get(s)
+        assert st.free_blocks == 8 and st.free_slots == 2
+    finally:
+        B.cbd_sched_destroy(s)

@@ -1,0 +1,151 @@
+"""GPU parity on the tiny 2-layer decoder (d_model 256, 4/2 heads, head_dim
+64, FFN 688, vocab 4096; 4-position blocks over a shuffled 64-block pool):
+prefill through the chunk path, then 20 greedy decode steps, every step
+compared with the oracle's paged-batched step on the same metadata. Tokens
+are teacher-forced with the oracle's, so one near tie cannot desynchronise
+the rest."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from continuous_batching_decode_forward_amd import binding as B
+from continuous_batching_decode_forward_amd import configs, synth
+
+from gpu_util import compare_logits, make_engine, resolvable_rows, weights_to
+
+pytestmark = pytest.mark.gpu
+
+CFG = configs.TINY
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w = synth.make_weights(CFG, seed=0)
+    return w, O.Model(CFG, w), weights_to(w, "cuda")
+
+
+def run_schedule(tiny, prompts, n_decode, chunk, bs, nb, seed, order=None):
+    """Drive both sides through the same steps; return per-step stats."""
+    w, om, wg = tiny
+    n = len(prompts)
+    perm = synth.permutation(seed, "blocks", nb)
+    per = nb // n
+    tables = np.stack([perm[i * per:(i + 1) * per] for i in range(n)]).astype(np.int32)
+    eng = make_engine(CFG, wg, block_size=bs, num_blocks=nb, max_blocks_per_seq=per,
+                      max_rows=256, max_seqs=8, max_position=per * bs)
+    pool = om.paged_pool(nb, bs)
+    ctx = [0] * n
+    last = [None] * n
+    order = list(range(n)) if order is None else order
+    results = []
+    for step in range(10_000):
+        seqs, nn, toks, want = [], [], [], []
+        budget = 10_000
+        for i in order:      # prefill chunks first, then decode rows
+            if ctx[i] < len(prompts[i]):
+                k = min(chunk, len(prompts[i]) - ctx[i])
+                seqs.append(i); nn.append(k); toks += list(prompts[i][ctx[i]:ctx[i] + k])
+                want.append(int(ctx[i] + k == len(prompts[i])))
+        for i in order:
+            if ctx[i] >= len(prompts[i]) and last[i] is not None and \
+                    ctx[i] < len(prompts[i]) + n_decode:
+                seqs.append(i); nn.append(1); toks.append(last[i]); want.append(1)
+        if not seqs:
+            break
+        ref_lg, ref_tok = O.paged_step(om, pool, tables[seqs], [ctx[i] for i in seqs], nn,
+                                       toks, want)
+        meta = eng.upload_step(slots=seqs, block_tables=tables[seqs],
+                               ctx_lens=[ctx[i] for i in seqs], n_new=nn, tokens=toks,
+                               want_token=want)
+        n_out = meta.n_out
+        lg = torch.empty((max(n_out, 1), CFG.vocab), dtype=torch.float32, device="cuda")
+        tk = torch.full((max(n_out, 1),), -1, dtype=torch.int32, device="cuda")
+        eng.step_forward(meta, lg, tk)
+        torch.cuda.synchronize()
+        assert eng.status() == 0
+        g_lg, g_tk = lg[:n_out].cpu().numpy(), tk[:n_out].cpu().numpy()
+        if n_out:
+            ok, mx, row_err = compare_logits(g_lg, ref_lg)
+            res = resolvable_rows(ref_lg, row_err)
+            # the argmax of the GPU's own fp32 logits, lowest id on ties
+            own = np.array([O.argmax_f32(r) for r in g_lg])
+            results.append((step, ok, mx, int(res.sum()), int((g_tk != ref_tok)[res].sum()),
+                            bool(np.array_equal(own, g_tk))))
+        o = 0
+        for i, k, wt in zip(seqs, nn, want):
+            ctx[i] += k
+            if wt:
+                last[i] = int(ref_tok[o])  # teacher forcing with the oracle's token
+                o += 1
+    eng.close()
+    return results
+
+
+def check(results):
+    assert results
+    for step, ok, mx, n_res, n_bad, own_ok in results:
+        assert ok, f"step {step}: logits outside tolerance (max abs err {mx:.3g})"
+        assert n_bad == 0, f"step {step}: {n_bad} resolvable greedy ids differ"
+        assert own_ok, f"step {step}: the argmax kernel disagrees with argmax of its logits"
+
+
+def prompts_for(seed, n=4, lo=5, hi=40):
+    lens = synth.uniform_ints(seed, "ctx", n, lo, hi)
+    return [synth.uniform_ints(seed, f"prompt.{i}", int(lens[i]), 0, CFG.vocab - 1)
+            for i in range(n)]
+
+
+def test_tiny_prefill_then_20_greedy_steps(tiny):
+    res = run_schedule(tiny, prompts_for(0), 20, chunk=64, bs=4, nb=64, seed=0)
+    assert len(res) == 21
+    check(res)
+
+
+def test_tiny_chunked_prefill_mixed_with_decode(tiny):
+    """8-token chunks: later steps carry prefill chunks and decode rows
+    together, and chunks start at offsets inside blocks."""
+    res = run_schedule(tiny, prompts_for(1), 12, chunk=8, bs=4, nb=64, seed=1, order=[2, 0, 3, 1])
+    check(res)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_tiny_block_sizes_and_ragged_contexts(tiny, bs):
+    # contexts around block boundaries: bs-1, bs, bs+1, and a single token
+    prompts = [synth.uniform_ints(bs, f"p{i}", L, 0, CFG.vocab - 1)
+               for i, L in enumerate([bs - 1, bs, bs + 1, 1])]
+    res = run_schedule(tiny, prompts, 5, chunk=7, bs=bs, nb=64 if bs < 32 else 32, seed=bs)
+    check(res)
+
+
+def test_device_refuses_bad_metadata_without_faulting(tiny):
+    w, om, wg = tiny
+    eng = make_engine(CFG, wg, block_size=4, num_blocks=16, max_blocks_per_seq=4, max_rows=16,
+                      max_seqs=4, max_position=16)
+    tk = torch.zeros(2, dtype=torch.int32, device="cuda")
+    # block id 99 is outside the 16-block pool
+    meta = eng.upload_step(slots=[0, 1], block_tables=[[0, 1, 2, 3], [99, 5, 6, 7]],
+                           ctx_lens=[0, 0], n_new=[2, 2], tokens=[1, 2, 3, 4], want_token=[1, 1])
+    eng.step_forward(meta, None, tk)
+    assert eng.status() & B.CBD_STATUS_BAD_BLOCK
+    # token outside the vocabulary
+    meta = eng.upload_step(slots=[0], block_tables=[[0, 1, 2, 3]], ctx_lens=[0], n_new=[1],
+                           tokens=[CFG.vocab + 5], want_token=[1])
+    eng.step_forward(meta, None, tk)
+    assert eng.status() & B.CBD_STATUS_BAD_TOKEN
+    # ctx + n_new beyond the block table
+    meta = eng.upload_step(slots=[0], block_tables=[[0, 1, 2, 3]], ctx_lens=[15], n_new=[2],
+                           tokens=[1, 2], want_token=[1], max_ctx=16)
+    eng.step_forward(meta, None, tk)
+    assert eng.status() & B.CBD_STATUS_BAD_SHAPE
+    # host-side checks
+    with pytest.raises(B.CbdError):
+        bad = eng.upload_step(slots=[0], block_tables=[[0, 1, 2, 3]], ctx_lens=[0], n_new=[1],
+                              tokens=[1], want_token=[1], max_ctx=999)
+        eng.step_forward(bad, None, tk)
+    # a clean step still works afterwards
+    meta = eng.upload_step(slots=[0], block_tables=[[0, 1, 2, 3]], ctx_lens=[0], n_new=[3],
+                           tokens=[1, 2, 3], want_token=[1])
+    eng.step_forward(meta, None, tk)
+    assert eng.status() == 0
+    eng.close()
