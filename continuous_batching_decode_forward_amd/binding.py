@@ -41,6 +41,14 @@ CBD_KERNEL_LM_HEAD = 7
 CBD_KERNEL_SAMPLE = 8
 CBD_KERNEL_NORM = 9
 
+CBD_BUF_X = 1
+CBD_BUF_H = 2
+CBD_BUF_QKV = 3
+CBD_BUF_Q = 4
+CBD_BUF_ATTN = 5
+CBD_BUF_FFN = 6
+CBD_BUF_LM_IN = 7
+
 CBD_FINISH_EOS = 1
 CBD_FINISH_LENGTH = 2
 CBD_FINISH_ABORT = 3
@@ -111,8 +119,9 @@ SIGNATURES = [
     ("cbd_kv_pool_bytes", C.c_int, [C.POINTER(cbd_config), C.POINTER(C.c_size_t)]),
     ("cbd_slot_state_bytes", C.c_int, [C.POINTER(cbd_config), C.POINTER(C.c_size_t)]),
     ("cbd_workspace_bytes", C.c_int, [C.POINTER(cbd_config), C.POINTER(C.c_size_t)]),
+    ("cbd_packed_weights_bytes", C.c_int, [C.POINTER(cbd_config), C.POINTER(C.c_size_t)]),
     ("cbd_engine_create", C.c_int, [C.POINTER(cbd_config), C.POINTER(cbd_weights), VP, VP, VP,
-                                    I32P, VP, C.POINTER(VP)]),
+                                    VP, I32P, VP, C.POINTER(VP)]),
     ("cbd_engine_destroy", C.c_int, [VP]),
     ("cbd_slot_alloc", C.c_int, [VP, C.POINTER(cbd_sampling), C.c_uint64, I32P]),
     ("cbd_slot_free", C.c_int, [VP, C.c_int32]),
@@ -123,6 +132,7 @@ SIGNATURES = [
     ("cbd_sample_logits", C.c_int, [VP, VP, C.c_int32, VP, VP, VP, VP]),
     ("cbd_engine_status", C.c_int, [VP, VP, C.POINTER(C.c_uint32)]),
     ("cbd_last_error", C.c_char_p, []),
+    ("cbd_debug_buffer", C.c_int, [VP, C.c_int32, C.POINTER(VP), C.POINTER(C.c_size_t)]),
     ("cbd_profile_begin", C.c_int, [VP, C.c_int32]),
     ("cbd_profile_end", C.c_int, [VP, C.POINTER(C.c_double), I32P]),
     ("cbd_sched_create", C.c_int, [C.POINTER(cbd_sched_config), VP, I32P, C.POINTER(VP)]),
@@ -186,12 +196,20 @@ def cbd_workspace_bytes(cfg: cbd_config) -> int:
     return n.value
 
 
-def cbd_engine_create(cfg, weights, kv_pool, slot_state, workspace, block_order, stream) -> int:
+def cbd_packed_weights_bytes(cfg: cbd_config) -> int:
+    n = C.c_size_t()
+    _call("cbd_packed_weights_bytes", C.byref(cfg), C.byref(n))
+    return n.value
+
+
+def cbd_engine_create(cfg, weights, packed, kv_pool, slot_state, workspace, block_order,
+                      stream) -> int:
     h = VP()
     order = None
     if block_order is not None:
         order = (C.c_int32 * len(block_order))(*[int(b) for b in block_order])
-    _call("cbd_engine_create", C.byref(cfg), C.byref(weights), kv_pool, slot_state, workspace,
+    _call("cbd_engine_create", C.byref(cfg), C.byref(weights), packed, kv_pool, slot_state,
+          workspace,
           C.cast(order, I32P) if order is not None else None, stream, C.byref(h))
     return h.value
 
@@ -242,6 +260,12 @@ def cbd_engine_status(engine, stream) -> int:
 
 def cbd_last_error() -> str:
     return lib().cbd_last_error().decode()
+
+
+def cbd_debug_buffer(engine, which: int):
+    p, n = VP(), C.c_size_t()
+    _call("cbd_debug_buffer", engine, int(which), C.byref(p), C.byref(n))
+    return p.value, n.value
 
 
 def cbd_profile_begin(engine, kernel_class: int) -> None:

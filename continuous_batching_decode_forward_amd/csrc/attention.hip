@@ -22,7 +22,8 @@
 // PV MFMA needs (no shuffles), and the V tile is stored dimension-major in
 // the pool so that its A operand is one 16-byte load per lane. Softmax is
 // online in base 2 (scores pre-scaled by log2(e)/sqrt(hd)); P enters the PV
-// MFMA as a pair of bf16 terms (hi + lo) and the running sums use fp32 P.
+// MFMA as three bf16 terms that sum to its fp32 value, and the running sums
+// use fp32 P.
 #include "common.h"
 #include "kernels.h"
 
@@ -210,28 +211,31 @@ __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = exp2f(m_run - m_use);
     m_run = m_new;
-    // P = P_hi + P_lo, both bf16: the PV product keeps ~16 significant bits
-    // of each weight, so the bf16 rounding of the attention output is decided
-    // as it would be with fp32 weights.
-    uint32_t ph[4], pl[4];
+    // P = P1 + P2 + P3, three bf16 terms: together they carry P's full fp32
+    // significand, so the PV product rounds like an fp32 weighted sum.
+    uint32_t p1[4], p2[4], p3[4];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float a = exp2f(sv[2 * e] - m_use);
       const float b = exp2f(sv[2 * e + 1] - m_use);
       psum += a + b;
-      const float ah = round_bf(a), bh = round_bf(b);
-      ph[e] = pack_bf2(ah, bh);
-      pl[e] = pack_bf2(a - ah, b - bh);
+      const float a1 = round_bf(a), b1 = round_bf(b);
+      const float a2 = round_bf(a - a1), b2 = round_bf(b - b1);
+      p1[e] = pack_bf2(a1, b1);
+      p2[e] = pack_bf2(a2, b2);
+      p3[e] = pack_bf2(a - a1 - a2, b - b1 - b2);
     }
     l_run = l_run * alpha + psum;
-    const bf16x8_t pf_hi = as_bf16x8(make_uint4(ph[0], ph[1], ph[2], ph[3]));
-    const bf16x8_t pf_lo = as_bf16x8(make_uint4(pl[0], pl[1], pl[2], pl[3]));
+    const bf16x8_t pf1 = as_bf16x8(make_uint4(p1[0], p1[1], p1[2], p1[3]));
+    const bf16x8_t pf2 = as_bf16x8(make_uint4(p2[0], p2[1], p2[2], p2[3]));
+    const bf16x8_t pf3 = as_bf16x8(make_uint4(p3[0], p3[1], p3[2], p3[3]));
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       o[t] = o[t] * alpha;
-      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf_hi, o[t]);
-      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf_lo, o[t]);
+      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf1, o[t]);
+      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf2, o[t]);
+      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf3, o[t]);
     }
   }
   if (bad_block) raise_status(status, ST_BAD_BLOCK);

@@ -94,6 +94,29 @@ SlotLayout slot_layout(const cbd_config& c) {
   return L;
 }
 
+PackedLayout packed_layout(const cbd_config& c) {
+  PackedLayout L;
+  const int qkv_n = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int qd = c.n_heads * c.head_dim;
+  size_t o = 0;
+  auto take = [&](int N, int K) {
+    size_t at = o;
+    o += packed_elems(N, K);
+    o = (o + 127) & ~(size_t)127;  // 256-byte aligned
+    return at;
+  };
+  for (int l = 0; l < c.n_layers; ++l) {
+    L.qkv.push_back(take(qkv_n, c.d_model));
+    L.o.push_back(take(c.d_model, qd));
+    L.gate.push_back(take(c.ffn_dim, c.d_model));
+    L.up.push_back(take(c.ffn_dim, c.d_model));
+    L.down.push_back(take(c.d_model, c.ffn_dim));
+  }
+  L.lm_head = take(c.vocab, c.d_model);
+  L.total_elems = o;
+  return L;
+}
+
 size_t kv_pool_bytes(const cbd_config& c) {
   return (size_t)c.n_layers * 2 * (size_t)c.num_blocks * (size_t)c.n_kv_heads *
          (size_t)c.block_size * (size_t)c.head_dim * 2;
@@ -163,12 +186,20 @@ int cbd_workspace_bytes(const cbd_config* cfg, size_t* bytes) {
   return CBD_OK;
 }
 
-int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* kv_pool,
-                      void* slot_state, void* workspace, const int32_t* block_order,
-                      void* stream, cbd_engine** out) {
+int cbd_packed_weights_bytes(const cbd_config* cfg, size_t* bytes) {
   int rc = validate_config(cfg);
   if (rc) return rc;
-  if (!w || !kv_pool || !slot_state || !workspace || !out)
+  if (!bytes) return fail(CBD_E_INVAL, "bytes is NULL");
+  *bytes = packed_layout(*cfg).total_elems * 2;
+  return CBD_OK;
+}
+
+int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* packed_weights,
+                      void* kv_pool, void* slot_state, void* workspace,
+                      const int32_t* block_order, void* stream, cbd_engine** out) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!w || !packed_weights || !kv_pool || !slot_state || !workspace || !out)
     return fail(CBD_E_INVAL, "NULL weights, buffer or output handle");
   if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->w_qkv || !w->w_o ||
       !w->ffn_norm || !w->w_gate || !w->w_up || !w->w_down)
@@ -177,7 +208,8 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* kv_pool
     if (!w->attn_norm[l] || !w->w_qkv[l] || !w->w_o[l] || !w->ffn_norm[l] || !w->w_gate[l] ||
         !w->w_up[l] || !w->w_down[l])
       return fail(CBD_E_INVAL, "a per-layer weight pointer is NULL");
-  for (const void* p : {(const void*)kv_pool, (const void*)slot_state, (const void*)workspace})
+  for (const void* p : {(const void*)packed_weights, (const void*)kv_pool,
+                        (const void*)slot_state, (const void*)workspace})
     if ((uintptr_t)p % 256) return fail(CBD_E_INVAL, "device buffers must be 256-byte aligned");
 
   cbd_engine* e = new cbd_engine();
@@ -199,6 +231,8 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* kv_pool
     e->w_up.push_back((const uint16_t*)w->w_up[l]);
     e->w_down.push_back((const uint16_t*)w->w_down[l]);
   }
+  e->packed = (uint16_t*)packed_weights;
+  e->pl = packed_layout(*cfg);
   e->kv_pool = (uint8_t*)kv_pool;
   e->slot_state = (uint8_t*)slot_state;
   e->workspace = (uint8_t*)workspace;
@@ -223,6 +257,24 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* kv_pool
   }
   hipError_t he = hipMemcpyAsync(e->workspace + e->ws.rope, cs.data(), cs.size() * sizeof(float),
                                  hipMemcpyHostToDevice, e->stream);
+  // Pack every projection matrix into the GEMM's tile order.
+  const int qkv_n = (cfg->n_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
+  const int qd = cfg->n_heads * cfg->head_dim;
+  for (int l = 0; l < cfg->n_layers && he == hipSuccess; ++l) {
+    he = launch_pack(e->w_qkv[l], qkv_n, cfg->d_model, e->packed + e->pl.qkv[l], e->stream);
+    if (he == hipSuccess)
+      he = launch_pack(e->w_o[l], cfg->d_model, qd, e->packed + e->pl.o[l], e->stream);
+    if (he == hipSuccess)
+      he = launch_pack(e->w_gate[l], cfg->ffn_dim, cfg->d_model, e->packed + e->pl.gate[l],
+                       e->stream);
+    if (he == hipSuccess)
+      he = launch_pack(e->w_up[l], cfg->ffn_dim, cfg->d_model, e->packed + e->pl.up[l], e->stream);
+    if (he == hipSuccess)
+      he = launch_pack(e->w_down[l], cfg->d_model, cfg->ffn_dim, e->packed + e->pl.down[l],
+                       e->stream);
+  }
+  if (he == hipSuccess)
+    he = launch_pack(e->lm_head, cfg->vocab, cfg->d_model, e->packed + e->pl.lm_head, e->stream);
   if (he == hipSuccess)
     he = launch_fill_u32(e->wsp<uint32_t>(e->ws.status), 0u, 1, e->stream);
   if (he == hipSuccess)
@@ -368,7 +420,7 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
     GemmArgs g{};
     g.partials = gpart;
     g.partials_cap = e->ws.gemm_part_floats;
-    g.X = h; g.R = R; g.K = c.d_model; g.W = e->w_qkv[l]; g.N = qkv_n; g.epi = EPI_BF16; g.Y = qkv;
+    g.X = h; g.R = R; g.K = c.d_model; g.W = e->packed + e->pl.qkv[l]; g.N = qkv_n; g.epi = EPI_BF16; g.Y = qkv;
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
@@ -381,17 +433,18 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
                              e->wsp<float>(e->ws.attn_ml), e->wsp<float>(e->ws.attn_o), attn,
                              status, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
-    g.X = attn; g.K = qd; g.W = e->w_o[l]; g.N = c.d_model; g.epi = EPI_RESID; g.Y = x;
+    g.X = attn; g.K = qd; g.W = e->packed + e->pl.o[l]; g.N = c.d_model; g.epi = EPI_RESID; g.Y = x;
     HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
     HIP_TRY(launch_rmsnorm(x, nullptr, R, e->ffn_norm[l], c.d_model, c.rms_eps, h, st));
-    g.X = h; g.K = c.d_model; g.W = e->w_gate[l]; g.W2 = e->w_up[l]; g.N = c.ffn_dim;
+    g.X = h; g.K = c.d_model; g.W = e->packed + e->pl.gate[l]; g.W2 = e->packed + e->pl.up[l];
+    g.N = c.ffn_dim;
     g.epi = EPI_SWIGLU; g.Y = ffn;
     HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
-    g.X = ffn; g.K = c.ffn_dim; g.W = e->w_down[l]; g.W2 = nullptr; g.N = c.d_model;
+    g.X = ffn; g.K = c.ffn_dim; g.W = e->packed + e->pl.down[l]; g.W2 = nullptr; g.N = c.d_model;
     g.epi = EPI_RESID; g.Y = x;
     HIP_TRY(e->prof_mark(CBD_KERNEL_DOWN, st));
     HIP_TRY(launch_gemm(g, st));
@@ -403,7 +456,7 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
   float* logits = logits_out;
   if (!logits && s->mode == CBD_MODE_SAMPLE) logits = e->wsp<float>(e->ws.logits);
   GemmArgs g{};
-  g.X = lm_in; g.R = s->n_out; g.K = c.d_model; g.W = e->lm_head; g.N = c.vocab;
+  g.X = lm_in; g.R = s->n_out; g.K = c.d_model; g.W = e->packed + e->pl.lm_head; g.N = c.vocab;
   g.epi = EPI_LOGITS; g.logits = logits;
   g.amax_val = e->wsp<float>(e->ws.amax_val);
   g.amax_idx = e->wsp<int32_t>(e->ws.amax_idx);
@@ -415,7 +468,7 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
   HIP_TRY(e->prof_mark(CBD_KERNEL_LM_HEAD, st));
   HIP_TRY(e->prof_mark(CBD_KERNEL_SAMPLE, st));
   if (s->mode == CBD_MODE_GREEDY) {
-    HIP_TRY(launch_argmax_reduce(g.amax_val, g.amax_idx, gemm_amax_tiles(s->n_out, c.vocab),
+    HIP_TRY(launch_argmax_reduce(g.amax_val, g.amax_idx, gemm_amax_tiles(s->n_out, c.vocab, c.d_model),
                                  e->ws.amax_stride, s->n_out, tokens_out, st));
   } else {
     HIP_TRY(launch_sampler(logits, s->n_out, c.vocab, s->slots, s->step_ids, maps.out_seq,
@@ -436,6 +489,28 @@ int cbd_sample_logits(cbd_engine* e, const float* logits, int32_t n, const int32
                          reinterpret_cast<float*>(e->slot_state + e->sl.counts), e->cfg.max_slots,
                          e->wsp<float>(e->ws.smp), tokens_out, e->wsp<uint32_t>(e->ws.status),
                          (hipStream_t)stream));
+  return CBD_OK;
+}
+
+int cbd_debug_buffer(cbd_engine* e, int32_t which, void** ptr, size_t* bytes) {
+  if (!e || !ptr || !bytes) return fail(CBD_E_INVAL, "NULL argument");
+  const cbd_config& c = e->cfg;
+  const size_t R = (size_t)c.max_rows;
+  const size_t qkv_n = (size_t)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const size_t qd = (size_t)c.n_heads * c.head_dim;
+  size_t off, n;
+  switch (which) {
+    case CBD_BUF_X: off = e->ws.x; n = R * c.d_model; break;
+    case CBD_BUF_H: off = e->ws.h; n = R * c.d_model; break;
+    case CBD_BUF_QKV: off = e->ws.qkv; n = R * qkv_n; break;
+    case CBD_BUF_Q: off = e->ws.q; n = R * qd; break;
+    case CBD_BUF_ATTN: off = e->ws.attn; n = R * qd; break;
+    case CBD_BUF_FFN: off = e->ws.ffn; n = R * c.ffn_dim; break;
+    case CBD_BUF_LM_IN: off = e->ws.lm_in; n = (size_t)c.max_seqs * c.d_model; break;
+    default: return fail(CBD_E_INVAL, "unknown buffer");
+  }
+  *ptr = e->workspace + off;
+  *bytes = n * 2;
   return CBD_OK;
 }
 

@@ -12,10 +12,12 @@
 // of W (16 output columns), the B operand a 16-row fragment of X, so one
 // instruction yields a 16 (columns) x 16 (rows) tile. Lane l holds 8
 // consecutive k of row (l % 16) of each operand; the four lane groups
-// (l / 16) hold consecutive 8-k pieces, so one 16-byte load per lane covers
-// 64 contiguous bytes of 16 weight rows. A 64-k super-step issues two such
-// loads per fragment (the two halves of each row's 128-byte line) and feeds
-// two MFMAs.
+// (l / 16) hold consecutive 8-k pieces. The weights are stored pre-packed in
+// exactly that operand order (16 x 32 tiles, lane-major), so every
+// wave-wide weight load is one contiguous 1 KB tile and a wave streams each
+// 16-row block front to back -- the DRAM sees long sequential runs instead
+// of 16 scattered 64-byte pieces per instruction. Two register stages of
+// loads are kept in flight while the previous stage feeds the MFMAs.
 //
 // A wave owns NT column fragments x RT row fragments. KW waves of a workgroup
 // split K and reduce through LDS in fixed wave order; S workgroups along
@@ -75,27 +77,29 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
   const int r0 = blockIdx.z * (16 * RT);
   const int K = a.K, N = a.N, R = a.R;
 
-  const int kw_len = kc / KW;  // multiple of 8 (K % 16 == 0, kc % (16 KW) == 0)
+  const int kw_len = kc / KW;  // a multiple of 64: waves start on tile boundaries
   const int kbeg = ks * kc + wave * kw_len;
   const int kend = min(K, kbeg + kw_len);
 
-  const uint16_t* wrow[NM][NT];
-  bool wok[NT];
+  // Weight pointers into the packed layout, at this wave's first tile and
+  // this lane's 16 bytes: a wave-wide load reads one whole 1 KB tile. Row
+  // blocks past N read block 0 (valid memory; those outputs are never
+  // stored). Activation rows past R likewise read row 0.
+  const int KT = (K + 31) / 32;
+  const uint16_t* wp[NM][NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    int n = n0 + 16 * nt + lr;
-    wok[nt] = n < N;
-    size_t off = (size_t)(wok[nt] ? n : 0) * K;
-    wrow[0][nt] = a.W + off;
-    if (NM == 2) wrow[NM - 1][nt] = a.W2 + off;
+    int nb = (n0 >> 4) + nt;
+    if (nb * 16 >= N) nb = 0;
+    const size_t off = ((size_t)nb * KT + kbeg / 32) * 512 + lane * 8;
+    wp[0][nt] = a.W + off;
+    if (NM == 2) wp[NM - 1][nt] = a.W2 + off;
   }
-  const uint16_t* xrow[RT];
-  bool xok[RT];
+  const uint16_t* xp[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    int r = r0 + 16 * rt + lr;
-    xok[rt] = r < R;
-    xrow[rt] = a.X + (size_t)(xok[rt] ? r : 0) * K;
+    const int r = r0 + 16 * rt + lr;
+    xp[rt] = a.X + (size_t)(r < R ? r : 0) * K + kbeg + 8 * lg;
   }
 
   floatx4_t acc[NM][NT][RT];
@@ -106,30 +110,32 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int U = 2;  // super-steps whose loads are issued together
-  for (int k = kbeg; k < kend; k += 64 * U) {
-    uint4 wv[U][NM][NT][2];
-    uint4 xv[U][RT][2];
+  // One stage = ST super-steps of 64 k; two stages in registers, so the
+  // loads of stage i+1 are in flight while stage i feeds the MFMAs.
+  constexpr int ST = RT <= 2 ? 2 : 1;
+  struct Stage {
+    uint4 w[ST][NM][NT][2];
+    uint4 x[ST][RT][2];
+  };
+  auto load = [&](Stage& sg, int k) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < ST; ++u)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int kk = k + 64 * u + 32 * h + 8 * lg;  // 8 k of this lane
-        const bool kin = kk < kend;
+        const int off = k + 64 * u + 32 * h;
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
-            wv[u][m][nt][h] = (kin && wok[nt]) ? load_stream16(wrow[m][nt] + kk)
-                                                 : make_uint4(0, 0, 0, 0);
+            sg.w[u][m][nt][h] = load_stream16(wp[m][nt] + (size_t)(off / 32) * 512);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          xv[u][rt][h] = (kin && xok[rt]) ? *reinterpret_cast<const uint4*>(xrow[rt] + kk)
-                                          : make_uint4(0, 0, 0, 0);
+          sg.x[u][rt][h] = *reinterpret_cast<const uint4*>(xp[rt] + off);
       }
-    }
+  };
+  auto compute = [&](const Stage& sg) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < ST; ++u)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -138,8 +144,44 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
           for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-              acc[m][nt][rt] = mfma16x16x32(as_bf16x8(wv[u][m][nt][h]), as_bf16x8(xv[u][rt][h]),
-                                            acc[m][nt][rt]);
+              acc[m][nt][rt] = mfma16x16x32(as_bf16x8(sg.w[u][m][nt][h]),
+                                            as_bf16x8(sg.x[u][rt][h]), acc[m][nt][rt]);
+  };
+
+  const int span = kend - kbeg;  // this wave's k count (a multiple of 8, or <= 0)
+  const int stride = 64 * ST;
+  const int nfull = span > 0 ? span / stride : 0;
+  {
+    Stage A, B;
+    int it = 0;
+    if (nfull > 0) load(A, 0);
+    for (; it + 2 <= nfull; it += 2) {
+      load(B, (it + 1) * stride);
+      compute(A);
+      if (it + 2 < nfull) load(A, (it + 2) * stride);
+      compute(B);
+    }
+    if (it < nfull) compute(A);
+  }
+  // Tail: the last < 64*ST k, in 32-k halves predicated per lane group.
+  for (int k = nfull * stride; k < span; k += 32) {
+    const bool kin = k + 8 * lg < span;
+    uint4 w[NM][NT], x[RT];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        w[m][nt] = kin ? load_stream16(wp[m][nt] + (size_t)(k / 32) * 512) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+      x[rt] = kin ? *reinterpret_cast<const uint4*>(xp[rt] + k) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc[m][nt][rt] = mfma16x16x32(as_bf16x8(w[m][nt]), as_bf16x8(x[rt]), acc[m][nt][rt]);
   }
 
   // Reduce the KW waves' partial sums through LDS, in wave order.
@@ -263,19 +305,50 @@ __global__ void gemm_reduce_kernel(GemmArgs a, int S) {
 
 // ------------------------------------------------------------- host side
 
+size_t packed_elems(int32_t N, int32_t K) {
+  return (size_t)((N + 15) / 16) * (size_t)((K + 31) / 32) * 512;
+}
+
+__global__ void pack_kernel(const uint16_t* __restrict__ W, int N, int K,
+                            uint16_t* __restrict__ out, size_t n16) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte piece
+  if (i >= n16) return;
+  const int KT = (K + 31) / 32;
+  const int lane = (int)(i & 63);
+  const size_t tile = i >> 6;
+  const int kb = (int)(tile % KT);
+  const int nb = (int)(tile / KT);
+  const int n = nb * 16 + (lane & 15);
+  const int k = kb * 32 + 8 * (lane >> 4);
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (n < N && k < K) v = *reinterpret_cast<const uint4*>(W + (size_t)n * K + k);
+  reinterpret_cast<uint4*>(out)[i] = v;
+}
+
+hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, hipStream_t st) {
+  const size_t n16 = packed_elems(N, K) / 8;
+  pack_kernel<<<(unsigned)((n16 + 255) / 256), 256, 0, st>>>(W, N, K, out, n16);
+  return hipGetLastError();
+}
+
 struct Shape {
   int RT, NT;
 };
 
-static Shape pick_shape(int R) {
+// Tile shape by rows and weight size: up to 16 rows one row fragment; beyond
+// that, matrices that fit comfortably in the 256 MB Infinity Cache are
+// streamed once per 16-row group (the repeats hit the cache), larger ones
+// keep all rows in one wave (4 row fragments, or 8 past 64 rows).
+static Shape pick_shape(int R, int N, int K, int NM) {
+  const size_t wbytes = (size_t)N * K * 2 * NM;
   if (R <= 16) return {1, 4};
-  if (R <= 32) return {2, 4};
-  if (R <= 64) return {4, 4};
+  if (wbytes < ((size_t)128 << 20)) return {1, 4};
+  if (R <= 64) return NM == 2 ? Shape{4, 2} : Shape{4, 4};
   return {8, 2};
 }
 
-int32_t gemm_amax_tiles(int32_t R, int32_t N) {
-  Shape s = pick_shape(R);
+int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K) {
+  Shape s = pick_shape(R, N, K, 1);
   return (N + 16 * s.NT - 1) / (16 * s.NT);
 }
 
@@ -285,13 +358,13 @@ static hipError_t launch_shape(const GemmArgs& a, hipStream_t st) {
   const int n_tiles = (a.N + 16 * NT - 1) / (16 * NT);
   const int r_groups = (a.R + 16 * RT - 1) / (16 * RT);
   const int base = n_tiles * r_groups;
-  // Aim at >= 2048 waves in flight (8 per CU): first split K inside the
-  // workgroup (up to 4 waves, >= 256 k each), then across workgroups
-  // (>= 512 k each) when the partials fit.
+  // Enough waves to cover the chip: when the column tiles alone give fewer
+  // than ~1024 waves, split K inside the workgroup (up to 4 waves, >= 256 k
+  // each) and then across workgroups (>= 512 k each) when the partials fit.
   // LDS for the in-workgroup reduction stays within 64 KB.
   const size_t lds_per_wave = (size_t)64 * NM * NT * RT * 4 * sizeof(float);
   int KW = 1;
-  while (KW < 4 && base * KW < 2048 && a.K / (KW * 2) >= 256 &&
+  while (base * KW < 1024 && KW < 4 && a.K / (KW * 2) >= 256 &&
          (size_t)(KW * 2 - 1) * lds_per_wave <= 65536)
     KW *= 2;
   int S = 1;
@@ -300,8 +373,9 @@ static hipError_t launch_shape(const GemmArgs& a, hipStream_t st) {
            (size_t)(S * 2) * NM * a.R * a.N <= a.partials_cap)
       S *= 2;
   }
+  // Waves start on 64-k (two-tile) boundaries.
   int kc = (a.K + S - 1) / S;
-  kc = (kc + 16 * KW - 1) / (16 * KW) * (16 * KW);
+  kc = (kc + 64 * KW - 1) / (64 * KW) * (64 * KW);
   S = (a.K + kc - 1) / kc;
   dim3 grid(n_tiles, S, r_groups);
   size_t lds = KW > 1 ? (size_t)(KW - 1) * 64 * NM * NT * RT * 4 * sizeof(float) : 0;
@@ -319,10 +393,10 @@ static hipError_t launch_shape(const GemmArgs& a, hipStream_t st) {
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
-  Shape s = pick_shape(a.R);
+  const Shape s = pick_shape(a.R, a.N, a.K, EpiTraits<EPI>::NM);
   if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
-  if (s.RT == 2) return launch_shape<2, 4, EPI>(a, st);
-  if (s.RT == 4) return launch_shape<4, 4, EPI>(a, st);
+  if (s.RT == 4 && s.NT == 4) return launch_shape<4, 4, EPI>(a, st);
+  if (s.RT == 4) return launch_shape<4, 2, EPI>(a, st);
   return launch_shape<8, 2, EPI>(a, st);
 }
 

@@ -75,11 +75,18 @@ hipError_t launch_attention(const uint16_t* q, int32_t R, const StepMeta& m, con
 
 enum GemmEpilogue { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
+// Weights reach the GEMM in a packed layout: tiles of 16 rows x 32 k, tile
+// (nb, kb) at element offset (nb * ceil(K/32) + kb) * 512, and inside a tile
+// lane l's 8 values (row nb*16 + l%16, k kb*32 + 8*(l/16) .. +8) at l * 8.
+// Rows past N and k past K are zero.
+size_t packed_elems(int32_t N, int32_t K);
+hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, hipStream_t st);
+
 struct GemmArgs {
   const uint16_t* X;  // [R][K] bf16
   int32_t R, K;
-  const uint16_t* W;  // [N][K] bf16
-  const uint16_t* W2; // second matrix for EPI_SWIGLU (up), [N][K]
+  const uint16_t* W;  // [N][K] bf16, packed
+  const uint16_t* W2; // second packed matrix for EPI_SWIGLU (up), [N][K]
   int32_t N;
   int32_t epi;
   uint16_t* Y;        // EPI_BF16 / EPI_SWIGLU out [R][N]; EPI_RESID in/out [R][N]
@@ -91,9 +98,8 @@ struct GemmArgs {
   size_t partials_cap;  // floats available there
 };
 
-// Tile columns covered by one argmax partial for a GEMM of R rows (the host
-// sizes amax buffers with this).
-int32_t gemm_amax_tiles(int32_t R, int32_t N);
+// Number of argmax partials per row the logits GEMM writes (column tiles).
+int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 
 // tokens[j] = lowest id of the row maximum over the argmax partials.

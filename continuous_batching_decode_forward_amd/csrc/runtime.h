@@ -101,6 +101,14 @@ struct SlotLayout {
   size_t params, counts, total;
 };
 
+// Element offsets of every projection matrix in the packed-weights buffer.
+struct PackedLayout {
+  std::vector<size_t> qkv, o, gate, up, down;  // per layer
+  size_t lm_head;
+  size_t total_elems;
+};
+PackedLayout packed_layout(const cbd_config& c);
+
 int validate_config(const cbd_config* c);
 WorkspaceLayout workspace_layout(const cbd_config& c);
 SlotLayout slot_layout(const cbd_config& c);
@@ -118,6 +126,8 @@ struct cbd_engine {
   const uint16_t* final_norm;
   const uint16_t* lm_head;
   std::vector<const uint16_t*> attn_norm, w_qkv, w_o, ffn_norm, w_gate, w_up, w_down;
+  uint16_t* packed;
+  cbd::PackedLayout pl;
   uint8_t* kv_pool;
   uint8_t* slot_state;
   uint8_t* workspace;

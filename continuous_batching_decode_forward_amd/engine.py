@@ -51,6 +51,8 @@ class Engine:
         self.cfg = cfg
         self.block_size, self.num_blocks = block_size, num_blocks
         self.max_blocks_per_seq = max_blocks_per_seq
+        self.packed = torch.empty(B.cbd_packed_weights_bytes(cfg), dtype=torch.uint8,
+                                  device=self.device)
         self.kv_pool = torch.empty(B.cbd_kv_pool_bytes(cfg), dtype=torch.uint8, device=self.device)
         self.slot_state = torch.empty(B.cbd_slot_state_bytes(cfg), dtype=torch.uint8,
                                       device=self.device)
@@ -68,7 +70,8 @@ class Engine:
             setattr(w, k, C.cast(arr, C.POINTER(C.c_void_p)))
         self._w = w
         self.stream = stream
-        self.handle = B.cbd_engine_create(cfg, w, _ptr(self.kv_pool), _ptr(self.slot_state),
+        self.handle = B.cbd_engine_create(cfg, w, _ptr(self.packed), _ptr(self.kv_pool),
+                                          _ptr(self.slot_state),
                                           _ptr(self.workspace), block_order,
                                           _stream_ptr(stream))
 
@@ -131,6 +134,16 @@ class Engine:
         params_bytes = (s.max_slots * 40 + 255) // 256 * 256
         return self.slot_state[params_bytes:params_bytes + s.max_slots * s.vocab * 4].view(
             torch.float32).view(s.max_slots, s.vocab)
+
+    def debug_buffer(self, which: int, rows: int, width: int) -> torch.Tensor:
+        """A copy of the first `rows` rows of an internal bf16 activation buffer."""
+        ptr, nbytes = B.cbd_debug_buffer(self.handle, which)
+        base = self.workspace.data_ptr()
+        off = ptr - base
+        assert 0 <= off and off + rows * width * 2 <= self.workspace.numel() and \
+            rows * width * 2 <= nbytes
+        return self.workspace[off:off + rows * width * 2].view(torch.bfloat16).view(
+            rows, width).clone()
 
     def close(self):
         if getattr(self, "handle", None):

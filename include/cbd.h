@@ -122,6 +122,13 @@ typedef struct cbd_sampling {
  * [head_dim][block_size] (dimension-major), all bf16. The block-id space is
  * shared by all layers. */
 int cbd_kv_pool_bytes(const cbd_config* cfg, size_t* bytes);
+/* The packed-weights buffer: every projection matrix (QKV, O, gate, up,
+ * down per layer, and the LM head) rearranged once, at engine creation, into
+ * the GEMM's tile order (16 rows x 32 k tiles in MFMA operand order; see the
+ * engine source). After cbd_engine_create returns, the engine reads only the
+ * embedding, the norm gains and this buffer, so the caller may release the
+ * row-major projection matrices. */
+int cbd_packed_weights_bytes(const cbd_config* cfg, size_t* bytes);
 int cbd_slot_state_bytes(const cbd_config* cfg, size_t* bytes);
 int cbd_workspace_bytes(const cbd_config* cfg, size_t* bytes);
 
@@ -130,15 +137,16 @@ int cbd_workspace_bytes(const cbd_config* cfg, size_t* bytes);
 typedef struct cbd_engine cbd_engine;
 
 /* Create an engine over caller-owned device buffers of at least the sizes
- * above. block_order (host, nullable) seeds the FIFO block free list with a
+ * above (all 256-byte aligned); fills packed_weights from the weights and
+ * waits for that on `stream` before returning. block_order (host, nullable) seeds the FIFO block free list with a
  * permutation of 0..num_blocks-1 (NULL: ascending). stream: where the
  * engine's own set-up work and slot resets are enqueued. Returns
  * CBD_E_UNSUPPORTED for shapes the kernels do not handle (head_dim not in
  * {64, 128}, n_heads/n_kv_heads not dividing 16, d_model or ffn_dim not a
  * multiple of 64, ...). */
-int cbd_engine_create(const cbd_config* cfg, const cbd_weights* weights, void* kv_pool,
-                      void* slot_state, void* workspace, const int32_t* block_order,
-                      void* stream, cbd_engine** out);
+int cbd_engine_create(const cbd_config* cfg, const cbd_weights* weights, void* packed_weights,
+                      void* kv_pool, void* slot_state, void* workspace,
+                      const int32_t* block_order, void* stream, cbd_engine** out);
 int cbd_engine_destroy(cbd_engine* e);
 
 /* Slots (per-sequence sampler state: penalty counts over the vocabulary
@@ -209,6 +217,21 @@ int cbd_sample_logits(cbd_engine* e, const float* logits, int32_t n, const int32
 int cbd_engine_status(cbd_engine* e, void* stream, uint32_t* flags);
 
 const char* cbd_last_error(void);
+
+/* ----------------------------------------------------------- inspection */
+
+/* Activation buffers inside the workspace, as the last step left them (for
+ * multi-layer models: the last layer's). Row i is the i-th row of the step
+ * (for CBD_BUF_LM_IN: the i-th emitting sequence). bf16 unless noted. */
+#define CBD_BUF_X 1      /* residual stream after the step [max_rows][d_model] */
+#define CBD_BUF_H 2      /* last RMSNorm output, the FFN input [max_rows][d_model] */
+#define CBD_BUF_QKV 3    /* QKV projection [max_rows][(n_heads+2*n_kv_heads)*head_dim] */
+#define CBD_BUF_Q 4      /* rotated queries [max_rows][n_heads*head_dim] */
+#define CBD_BUF_ATTN 5   /* attention output [max_rows][n_heads*head_dim] */
+#define CBD_BUF_FFN 6    /* SwiGLU output [max_rows][ffn_dim] */
+#define CBD_BUF_LM_IN 7  /* final-norm rows fed to the LM head [max_seqs][d_model] */
+/* Device address and size in bytes of one of them (no copy, no sync). */
+int cbd_debug_buffer(cbd_engine* e, int32_t which, void** ptr, size_t* bytes);
 
 /* ------------------------------------------------------------- profiling */
 

@@ -73,7 +73,8 @@ class OrSampleInfo(C.Structure):
                 ("sum_topk", C.c_float), ("target", C.c_float), ("cum_before", C.c_float),
                 ("cum_after", C.c_float), ("sum_kept", C.c_float), ("r", C.c_float),
                 ("cdf_lo", C.c_float), ("cdf_hi", C.c_float), ("p1", C.c_float),
-                ("p2", C.c_float), ("u", C.c_float)]
+                ("p2", C.c_float), ("u", C.c_float), ("n_cut", C.c_int32),
+                ("n_before", C.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

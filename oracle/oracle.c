@@ -26,9 +26,11 @@
  *    mode's, so the two agree byte for byte.
  *  - The sampler (temperature, top-k, top-p, frequency/presence penalty with
  *    decay) follows the Albatross worker description (RWKV-Runner Albatross
- *    article, "Worker main loop" and adapter defaults), in fp32, the
- *    precision of the GPU sampler, because its floating point decides an
- *    integer token.
+ *    article, "Worker main loop" and adapter defaults). Its per-id values
+ *    (penalised logit, z, e, counts) are fp32, the precision of the GPU
+ *    sampler, because they decide an integer token; the masses summed over
+ *    the vocabulary are accumulated in double so that each decision is the
+ *    one the exact sum of those fp32 values makes.
  *  - The draw: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11,
  *    "Parallel random numbers: as easy as 1, 2, 3"), counter = (request id,
  *    step id, 0, 0), key = (seed, 0).
@@ -576,6 +578,8 @@ typedef struct {
   float cdf_lo, cdf_hi;   /* chosen id's interval of the ascending-id CDF */
   float p1, p2;           /* two largest e / sum_all */
   float u;
+  int32_t n_cut;          /* ids summed before the top-p crossing id */
+  int32_t n_before;       /* kept ids before the chosen one (ascending id) */
 } or_sample_info;
 
 typedef struct {
@@ -591,17 +595,21 @@ static int cmp_desc(const void* a, const void* b) {
   return (x->id > y->id) - (x->id < y->id);
 }
 
-/* One row of the batched sampler, fp32, sequential, in this order:
- *  S1 penalty   l' = l - f*c - q*[c > 0]
- *  S2 T == 0    greedy on l' (lowest id); else z = l' / T
- *  S3 softmax   e = exp(z - max z) (unnormalised)
+/* One row of the batched sampler, in this order:
+ *  S1 penalty   l' = l - f*c - q*[c > 0]                       (fp32)
+ *  S2 T == 0    greedy on l' (lowest id); else z = l' / T       (fp32)
+ *  S3 softmax   e = exp(z - max z), unnormalised               (fp32)
  *  S4 top-k     keep the k largest by (e desc, id asc) when 0 < k < V
  *  S5 top-p     when p < 1: in (e desc, id asc) order keep the shortest
- *               prefix whose running mass reaches p * (mass kept by S4);
- *               the crossing id is kept
+ *               prefix whose mass reaches p * (mass kept by S4); the
+ *               crossing id is kept
  *  S6 draw      u from Philox; r = u * kept mass; the first kept id in
  *               ascending id order whose running kept mass exceeds r
- *  S7 counts    c = c * decay for every id, then c[token] += 1
+ *  S7 counts    c = c * decay for every id, then c[token] += 1  (fp32)
+ * The masses in S4-S6 are sums of the fp32 values e; they are accumulated
+ * exactly enough (double) that the decisions are those of the mathematical
+ * sums (a sequential fp32 sum over a large vocabulary loses every term below
+ * half an ulp of the running total and drifts by ~1e-4).
  * counts (in/out, [V]) may be NULL: then no penalty and no update. */
 int32_t or_sample_f32(const float* logits, int32_t V, float* counts,
                       const or_sampling* sp, uint64_t request_id,
@@ -633,48 +641,48 @@ int32_t or_sample_f32(const float* logits, int32_t V, float* counts,
       e[v] = z;
       if (z > zmax) zmax = z;
     }
-    float sum_all = 0.0f;
+    double sum_all = 0.0;
     for (int32_t v = 0; v < V; ++v) {
       e[v] = expf(e[v] - zmax);
       sum_all += e[v];
       kept[v] = 1;
     }
-    di.sum_all = sum_all;
-    int need_sort = (sp->top_k > 0 && sp->top_k < V) || sp->top_p < 1.0f;
+    di.sum_all = (float)sum_all;
     for (int32_t v = 0; v < V; ++v) {
       ord[v].e = e[v];
       ord[v].id = v;
     }
     qsort(ord, (size_t)V, sizeof(ev_t), cmp_desc);
-    di.p1 = ord[0].e / sum_all;
-    di.p2 = V > 1 ? ord[1].e / sum_all : 0.0f;
+    di.p1 = (float)(ord[0].e / sum_all);
+    di.p2 = V > 1 ? (float)(ord[1].e / sum_all) : 0.0f;
     int32_t nk = V;
-    if (need_sort && sp->top_k > 0 && sp->top_k < V) {
+    if (sp->top_k > 0 && sp->top_k < V) {
       nk = sp->top_k;
       for (int32_t i = nk; i < V; ++i) kept[ord[i].id] = 0;
     }
-    float sum_topk = 0.0f;
+    double sum_topk = 0.0;
     for (int32_t v = 0; v < V; ++v)
       if (kept[v]) sum_topk += e[v];
-    di.sum_topk = sum_topk;
+    di.sum_topk = (float)sum_topk;
     if (sp->top_p < 1.0f) {
-      float target = sp->top_p * sum_topk;
-      float run = 0.0f;
+      double target = (double)sp->top_p * sum_topk;
+      double run = 0.0;
       int32_t cut = nk - 1;
       for (int32_t i = 0; i < nk; ++i) {
-        float before = run;
+        double before = run;
         run += ord[i].e;
         if (run >= target) {
           cut = i;
-          di.cum_before = before;
-          di.cum_after = run;
+          di.n_cut = i;
+          di.cum_before = (float)before;
+          di.cum_after = (float)run;
           break;
         }
       }
       for (int32_t i = cut + 1; i < nk; ++i) kept[ord[i].id] = 0;
-      di.target = target;
+      di.target = (float)target;
     }
-    float sum_kept = 0.0f;
+    double sum_kept = 0.0;
     int32_t n_kept = 0;
     for (int32_t v = 0; v < V; ++v)
       if (kept[v]) {
@@ -682,30 +690,31 @@ int32_t or_sample_f32(const float* logits, int32_t V, float* counts,
         ++n_kept;
       }
     float u = or_uniform24(sp->seed, request_id, step_id);
-    float r = u * sum_kept;
-    float run = 0.0f;
+    double r = (double)u * sum_kept;
+    double run = 0.0;
     token = -1;
-    int32_t last = -1;
+    int32_t last = -1, seen = 0;
     for (int32_t v = 0; v < V; ++v) {
       if (!kept[v]) continue;
-      float lo = run;
+      double lo = run;
       run += e[v];
       last = v;
+      di.n_before = seen++;
       if (run > r) {
         token = v;
-        di.cdf_lo = lo;
-        di.cdf_hi = run;
+        di.cdf_lo = (float)lo;
+        di.cdf_hi = (float)run;
         break;
       }
     }
-    if (token < 0) { /* r reached the rounded total: take the last kept id */
+    if (token < 0) { /* r reached the total: take the last kept id */
       token = last;
-      di.cdf_lo = run - e[last];
-      di.cdf_hi = run;
+      di.cdf_lo = (float)(run - e[last]);
+      di.cdf_hi = (float)run;
     }
     di.n_kept = n_kept;
-    di.sum_kept = sum_kept;
-    di.r = r;
+    di.sum_kept = (float)sum_kept;
+    di.r = (float)r;
     di.u = u;
   }
   if (counts) {

@@ -66,7 +66,7 @@ def test_engine_create_rejects_null_buffers():
     c = make_cfg()
     w = B.cbd_weights()
     h = C.c_void_p()
-    rc = B.lib().cbd_engine_create(C.byref(c), C.byref(w), None, None, None, None, None,
+    rc = B.lib().cbd_engine_create(C.byref(c), C.byref(w), None, None, None, None, None, None,
                                    C.byref(h))
     assert rc == B.CBD_E_INVAL
 

@@ -28,16 +28,19 @@ VARIANTS = [BASE, replace(BASE, top_k=50), replace(BASE, temperature=0.7, top_p=
             replace(BASE, temperature=0.0), replace(BASE, top_k=1), replace(BASE, top_p=1e-6)]
 
 
-def margin_ok(info, sp, tol=1e-3):
-    """Whether the oracle's draw is decided away from every boundary: the
-    chosen id's CDF interval and, with top-p, the cut. Greedy rows (T = 0)
-    take the same fp32 operations on both sides and are always compared."""
+def margin_ok(info, sp, tol=2e-5):
+    """Whether the oracle's draw is decided away from every boundary by more
+    than the GPU's blocked fp32 sums can move it (a few 1e-6 of the total;
+    the oracle sums exactly): the chosen id's CDF interval and, with top-p,
+    the cut. Greedy rows (T = 0) take the same fp32 operations on both sides
+    and are always compared."""
     if sp.temperature == 0.0:
         return True
     ok = (info["r"] - info["cdf_lo"]) > tol * info["sum_kept"]
     ok &= (info["cdf_hi"] - info["r"]) > tol * info["sum_kept"]
     if sp.top_p < 1.0:
-        ok &= (info["target"] - info["cum_before"]) > tol * info["sum_topk"]
+        if info["n_cut"] > 0:  # an earlier id could become the crossing one
+            ok &= (info["target"] - info["cum_before"]) > tol * info["sum_topk"]
         ok &= (info["cum_after"] - info["target"]) > tol * info["sum_topk"]
     return bool(ok)
 
@@ -86,6 +89,8 @@ def test_sampler_matches_oracle_on_identical_logits(engine):
     engine.sample_logits(lg_d, sl_d, st_d, out)
     torch.cuda.synchronize()
     assert engine.status() == 0
+    for s_ in slots:
+        B.cbd_slot_free(engine.handle, s_)
     g_tok = out.cpu().numpy()
     g_counts = cview[torch.tensor(slots, device="cuda").long()].cpu().numpy()
     checked = agree = 0
@@ -98,10 +103,9 @@ def test_sampler_matches_oracle_on_identical_logits(engine):
         if g_tok[i] == tok:
             agree += 1
             assert np.array_equal(g_counts[i], c), f"row {i}: counts differ"
+    print(f"sampler rows decidable: {checked} of {n}")
     assert checked >= int(0.9 * n), f"only {checked} of {n} rows were decidable"
     assert agree >= checked
-    for s_ in slots:
-        B.cbd_slot_free(engine.handle, s_)
 
 
 def test_sampler_distribution_over_many_draws(engine):
