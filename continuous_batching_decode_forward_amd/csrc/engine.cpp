@@ -80,7 +80,7 @@ WorkspaceLayout workspace_layout(const cbd_config& c) {
   const size_t cols = R * (size_t)c.n_heads * (size_t)L.attn_max_splits;
   L.attn_ml = take(cols * 2 * 4);
   L.attn_o = take(cols * hd * 4);
-  L.rope = take((size_t)c.max_position * (hd / 2) * 8);
+  L.rope = take((size_t)c.max_position * (hd / 2) * 16);
   L.smp = take(S * (size_t)sampler_row_floats(c.vocab) * 4);
   L.total = o;
   return L;
@@ -244,18 +244,18 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* packed_
   }
   e->host_params.assign((size_t)cfg->max_slots, SlotParams{});
 
-  // RoPE table: angle pos * base^(-2i/hd) in double, stored as fp32 (cos, sin).
+  // RoPE table: angle pos * base^(-2i/hd), (cos, sin) in double.
   const int half = cfg->head_dim / 2;
-  std::vector<float> cs((size_t)cfg->max_position * half * 2);
+  std::vector<double> cs((size_t)cfg->max_position * half * 2);
   for (int i = 0; i < half; ++i) {
     const double inv_freq = pow(cfg->rope_base, -2.0 * i / (double)cfg->head_dim);
     for (int p = 0; p < cfg->max_position; ++p) {
       const double th = (double)p * inv_freq;
-      cs[((size_t)p * half + i) * 2] = (float)cos(th);
-      cs[((size_t)p * half + i) * 2 + 1] = (float)sin(th);
+      cs[((size_t)p * half + i) * 2] = cos(th);
+      cs[((size_t)p * half + i) * 2 + 1] = sin(th);
     }
   }
-  hipError_t he = hipMemcpyAsync(e->workspace + e->ws.rope, cs.data(), cs.size() * sizeof(float),
+  hipError_t he = hipMemcpyAsync(e->workspace + e->ws.rope, cs.data(), cs.size() * sizeof(double),
                                  hipMemcpyHostToDevice, e->stream);
   // Pack every projection matrix into the GEMM's tile order.
   const int qkv_n = (cfg->n_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
@@ -425,7 +425,7 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
-    HIP_TRY(launch_rope_append(qkv, R, m, maps, e->wsp<float>(e->ws.rope), e->md, q, e->pool_k(l),
+    HIP_TRY(launch_rope_append(qkv, R, m, maps, e->wsp<double>(e->ws.rope), e->md, q, e->pool_k(l),
                                e->pool_v(l), status, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));

@@ -102,17 +102,40 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
     xp[rt] = a.X + (size_t)(r < R ? r : 0) * K + kbeg + 8 * lg;
   }
 
-  floatx4_t acc[NM][NT][RT];
+  // Outputs that are rounded to bf16 accumulate with compensation: each
+  // 64-k (or 128-k) stage is summed by the MFMAs into a fresh accumulator and
+  // then added to the running sum with Kahan's correction, so the result is
+  // within a few fp32 ulps of the exact dot product and rounds to the same
+  // bf16 value as the exact one except right at a rounding boundary. The fp32
+  // logits of the LM head accumulate directly.
+  constexpr bool COMP = EPI != EPI_LOGITS;
+  floatx4_t acc[NM][NT][RT], cmp[NM][NT][RT];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < RT; ++rt) {
+        acc[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        cmp[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      }
+  auto kahan_add = [&](const floatx4_t (&t)[NM][NT][RT]) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const floatx4_t y = t[m][nt][rt] - cmp[m][nt][rt];
+          const floatx4_t s2 = acc[m][nt][rt] + y;
+          cmp[m][nt][rt] = (s2 - acc[m][nt][rt]) - y;
+          acc[m][nt][rt] = s2;
+        }
+  };
 
   // One stage = ST super-steps of 64 k; two stages in registers, so the
   // loads of stage i+1 are in flight while stage i feeds the MFMAs.
-  constexpr int ST = RT <= 2 ? 2 : 1;
+  constexpr int ST = (RT <= 2 && !COMP) ? 2 : 1;
   struct Stage {
     uint4 w[ST][NM][NT][2];
     uint4 x[ST][RT][2];
@@ -134,18 +157,41 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
       }
   };
   auto compute = [&](const Stage& sg) {
+    if (COMP) {
+      floatx4_t t[NM][NT][RT];
 #pragma unroll
-    for (int u = 0; u < ST; ++u)
+      for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+          for (int rt = 0; rt < RT; ++rt) t[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
+      for (int u = 0; u < ST; ++u)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-              acc[m][nt][rt] = mfma16x16x32(as_bf16x8(sg.w[u][m][nt][h]),
-                                            as_bf16x8(sg.x[u][rt][h]), acc[m][nt][rt]);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt)
+                t[m][nt][rt] = mfma16x16x32(as_bf16x8(sg.w[u][m][nt][h]),
+                                            as_bf16x8(sg.x[u][rt][h]), t[m][nt][rt]);
+      kahan_add(t);
+    } else {
+#pragma unroll
+      for (int u = 0; u < ST; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt)
+                acc[m][nt][rt] = mfma16x16x32(as_bf16x8(sg.w[u][m][nt][h]),
+                                              as_bf16x8(sg.x[u][rt][h]), acc[m][nt][rt]);
+    }
   };
 
   const int span = kend - kbeg;  // this wave's k count (a multiple of 8, or <= 0)
@@ -175,14 +221,24 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
       x[rt] = kin ? *reinterpret_cast<const uint4*>(xp[rt] + k) : make_uint4(0, 0, 0, 0);
+    floatx4_t t[NM][NT][RT];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          acc[m][nt][rt] = mfma16x16x32(as_bf16x8(w[m][nt]), as_bf16x8(x[rt]), acc[m][nt][rt]);
+          t[m][nt][rt] = mfma16x16x32(as_bf16x8(w[m][nt]), as_bf16x8(x[rt]),
+                                      floatx4_t{0.f, 0.f, 0.f, 0.f});
+    kahan_add(t);
   }
+  // Fold the compensation into the sum.
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[m][nt][rt] -= cmp[m][nt][rt];
 
   // Reduce the KW waves' partial sums through LDS, in wave order.
   if (KW > 1) {
@@ -335,20 +391,23 @@ struct Shape {
   int RT, NT;
 };
 
-// Tile shape by rows and weight size: up to 16 rows one row fragment; beyond
-// that, matrices that fit comfortably in the 256 MB Infinity Cache are
-// streamed once per 16-row group (the repeats hit the cache), larger ones
-// keep all rows in one wave (4 row fragments, or 8 past 64 rows).
-static Shape pick_shape(int R, int N, int K, int NM) {
-  const size_t wbytes = (size_t)N * K * 2 * NM;
+// Tile shape by rows, weight size and epilogue. Up to 16 rows: one row
+// fragment, four column fragments. Beyond that the bf16-output projections
+// (compensated accumulation, so at most 8 accumulator tiles per wave) take
+// two row fragments and stream the weights once per 32-row group -- the
+// repeats of a matrix up to 256 MB are served by the Infinity Cache -- while
+// the LM head (fp32 logits, plain accumulation) keeps up to 64 rows in one
+// wave (4 row fragments).
+static Shape pick_shape(int R, int N, int K, int NM, bool comp) {
+  (void)N;
+  (void)K;
   if (R <= 16) return {1, 4};
-  if (wbytes < ((size_t)128 << 20)) return {1, 4};
-  if (R <= 64) return NM == 2 ? Shape{4, 2} : Shape{4, 4};
-  return {8, 2};
+  if (comp) return NM == 2 ? Shape{2, 2} : Shape{2, 4};
+  return {4, 4};
 }
 
 int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K) {
-  Shape s = pick_shape(R, N, K, 1);
+  Shape s = pick_shape(R, N, K, 1, false);
   return (N + 16 * s.NT - 1) / (16 * s.NT);
 }
 
@@ -393,11 +452,17 @@ static hipError_t launch_shape(const GemmArgs& a, hipStream_t st) {
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
-  const Shape s = pick_shape(a.R, a.N, a.K, EpiTraits<EPI>::NM);
-  if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
-  if (s.RT == 4 && s.NT == 4) return launch_shape<4, 4, EPI>(a, st);
-  if (s.RT == 4) return launch_shape<4, 2, EPI>(a, st);
-  return launch_shape<8, 2, EPI>(a, st);
+  const Shape s = pick_shape(a.R, a.N, a.K, EpiTraits<EPI>::NM, EPI != EPI_LOGITS);
+  if constexpr (EPI == EPI_LOGITS) {
+    if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
+    return launch_shape<4, 4, EPI>(a, st);
+  } else if constexpr (EpiTraits<EPI>::NM == 2) {
+    if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
+    return launch_shape<2, 2, EPI>(a, st);
+  } else {
+    if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
+    return launch_shape<2, 4, EPI>(a, st);
+  }
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {

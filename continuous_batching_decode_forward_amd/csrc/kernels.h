@@ -60,7 +60,7 @@ hipError_t launch_rmsnorm(const uint16_t* x, const int32_t* rows, int32_t R, con
 // RoPE on q and k of every row at its position; q to q_out, k and v appended
 // into the layer's K and V regions of the pool through the block tables.
 hipError_t launch_rope_append(const uint16_t* qkv, int32_t R, const StepMeta& m,
-                              const RowMaps& maps, const float* rope_cs, const ModelDims& md,
+                              const RowMaps& maps, const double* rope_cs, const ModelDims& md,
                               uint16_t* q_out, uint16_t* pool_k, uint16_t* pool_v,
                               uint32_t* status, hipStream_t st);
 

@@ -232,13 +232,15 @@ hipError_t launch_rmsnorm(const uint16_t* x, const int32_t* rows, int32_t R, con
 // q_out), then Hkv key heads (rotated, written into the K tile
 // [block][kvh][pos % bs][hd]) and Hkv value heads (written, dimension-major,
 // into the V tile [block][kvh][hd][pos % bs]). The rotation reads a host-built
-// table of (cos, sin) per (position, i).
+// fp64 table of (cos, sin) per (position, i) and is evaluated in fp64: the
+// rotation a*cos - b*sin can cancel, and a query that rounds differently moves
+// every score of its head.
 
 __global__ void rope_append_kernel(const uint16_t* __restrict__ qkv, int R,
                                    const int32_t* __restrict__ row_seq,
                                    const int32_t* __restrict__ row_pos,
                                    const int32_t* __restrict__ tables, int max_blocks_per_seq,
-                                   const float2* __restrict__ rope_cs, int hq, int hkv, int hd,
+                                   const double2* __restrict__ rope_cs, int hq, int hkv, int hd,
                                    int bs, int num_blocks, uint16_t* __restrict__ q_out,
                                    uint16_t* __restrict__ pool_k, uint16_t* __restrict__ pool_v,
                                    uint32_t* status) {
@@ -255,11 +257,12 @@ __global__ void rope_append_kernel(const uint16_t* __restrict__ qkv, int R,
   const uint16_t* src = qkv + (size_t)r * slots * hd + (size_t)j * hd;
   float a = bf2f(src[i]), b = bf2f(src[i + half]);
   if (j < hq + hkv) {
-    float2 cs = rope_cs[(size_t)pos * half + i];
-    float ra = a * cs.x - b * cs.y;
-    float rb = b * cs.x + a * cs.y;
-    a = ra;
-    b = rb;
+    const double2 cs = rope_cs[(size_t)pos * half + i];
+    const double da = a, db = b;
+    // fp64 -> fp32 -> bf16: the double rounding can only matter within
+    // 2^-29 of a bf16 halfway point.
+    a = (float)(da * cs.x - db * cs.y);
+    b = (float)(db * cs.x + da * cs.y);
   }
   if (j < hq) {
     uint16_t* dst = q_out + (size_t)r * hq * hd + (size_t)j * hd;
@@ -287,7 +290,7 @@ __global__ void rope_append_kernel(const uint16_t* __restrict__ qkv, int R,
 }
 
 hipError_t launch_rope_append(const uint16_t* qkv, int32_t R, const StepMeta& m,
-                              const RowMaps& maps, const float* rope_cs, const ModelDims& md,
+                              const RowMaps& maps, const double* rope_cs, const ModelDims& md,
                               uint16_t* q_out, uint16_t* pool_k, uint16_t* pool_v,
                               uint32_t* status, hipStream_t st) {
   if (R <= 0) return hipSuccess;
@@ -296,7 +299,7 @@ hipError_t launch_rope_append(const uint16_t* qkv, int32_t R, const StepMeta& m,
   dim3 block(md.head_dim / 2, 4);
   rope_append_kernel<<<R * groups, block, 0, st>>>(
       qkv, R, maps.row_seq, maps.row_pos, m.block_tables, m.max_blocks_per_seq,
-      reinterpret_cast<const float2*>(rope_cs), md.n_heads, md.n_kv_heads, md.head_dim,
+      reinterpret_cast<const double2*>(rope_cs), md.n_heads, md.n_kv_heads, md.head_dim,
       md.block_size, md.num_blocks, q_out, pool_k, pool_v, status);
   return hipGetLastError();
 }

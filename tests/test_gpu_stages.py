@@ -71,6 +71,19 @@ def test_every_stage_of_an_8b_layer_within_bf16_rounding(big):
         ("attn", B.CBD_BUF_ATTN, hq * hd), ("h2", B.CBD_BUF_H, d), ("a", B.CBD_BUF_FFN, F),
         ("x2", B.CBD_BUF_X, d), ("hf", B.CBD_BUF_LM_IN, d)]}
     eng.close()
+    # a second engine whose down projection is zero leaves x1 (the residual
+    # after attention) in the residual buffer
+    wz = dict(wg)
+    wz["w_down"] = [torch.zeros_like(t) for t in wg["w_down"]]
+    eng = make_engine(SHAPE, wz, block_size=bs, num_blocks=len(perm), max_blocks_per_seq=mbps,
+                      max_rows=16, max_seqs=16, max_position=4097)
+    fill_pool(eng, seed, perm)
+    meta = eng.upload_step(slots=list(range(Bn)), block_tables=tables, ctx_lens=ctx,
+                           n_new=[1] * Bn, tokens=tokens, want_token=[1] * Bn)
+    eng.step_forward(meta, None, tk)
+    torch.cuda.synchronize()
+    gpu["x1"] = eng.debug_buffer(B.CBD_BUF_X, Bn, d)
+    eng.close()
     stats = {k: [] for k in gpu}
     for i in range(Bn):
         x0 = O.as_u16(wc["embed"][int(tokens[i])])
@@ -92,6 +105,11 @@ def test_every_stage_of_an_8b_layer_within_bf16_rounding(big):
         stats["attn"].append(stage_error(gpu["attn"][i], attn))
         t = to_u16(O.linear(attn, wc["w_o"][0]))
         x1 = to_u16(O.bf16_to_f64(x0) + O.bf16_to_f64(t))
+        stats["x1"].append(stage_error(gpu["x1"][i], x1))
+        dx = np.nonzero(O.as_u16(gpu["x1"][i]) != x1)[0]
+        if len(dx):
+            print(f"row {i}: x1 differs at {len(dx)} columns, by 64-column tile:",
+                  np.bincount(dx // 64, minlength=d // 64).nonzero()[0][:20])
         h2 = O.rmsnorm(x1, wc["ffn_norm"][0], SHAPE.rms_eps)
         stats["h2"].append(stage_error(gpu["h2"][i], h2))
         g = O.bf16_to_f64(to_u16(O.linear(h2, wc["w_gate"][0])))
