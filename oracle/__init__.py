@@ -4,9 +4,9 @@ TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
 CPU-baseline leg import this package. The product path never does, and this
 package imports nothing from the product.
 
-The arithmetic lives in oracle.c (plain C loops, double accumulation, bf16
-storage at the model's rounding points); composer_ref.py holds the
-scheduling policy as a plain Python simulation.
+The arithmetic lives in oracle.c (plain C loops, double activations and
+accumulation; bf16 only for the weights and the KV cache); composer_ref.py
+holds the scheduling policy as a plain Python simulation.
 """
 from __future__ import annotations
 
@@ -85,11 +85,11 @@ def _declare(L):
     L.or_bf16_to_f64.restype = C.c_double
     L.or_f64_to_bf16.argtypes = [C.c_double]
     L.or_f64_to_bf16.restype = C.c_uint16
-    L.or_rmsnorm.argtypes = [U16P, U16P, C.c_int32, C.c_double, U16P]
-    L.or_linear.argtypes = [U16P, C.c_int32, U16P, C.c_int32, F64P]
-    L.or_rope.argtypes = [U16P, C.c_int32, C.c_int32, C.c_double]
-    L.or_attention_dense.argtypes = [U16P, U16P, U16P, C.c_int32, C.c_int32, C.c_int32,
-                                     C.c_int32, U16P]
+    L.or_rmsnorm.argtypes = [F64P, U16P, C.c_int32, C.c_double, F64P]
+    L.or_linear.argtypes = [F64P, C.c_int32, U16P, C.c_int32, F64P]
+    L.or_rope.argtypes = [F64P, C.c_int32, C.c_int32, C.c_double]
+    L.or_attention_dense.argtypes = [F64P, U16P, U16P, C.c_int32, C.c_int32, C.c_int32,
+                                     C.c_int32, F64P]
     L.or_serial_forward.argtypes = [C.POINTER(OrModel), U16P, C.c_int32, I32P, C.c_int32,
                                     C.c_int32, C.c_int32, F64P]
     L.or_paged_step.argtypes = [C.POINTER(OrModel), U16P, C.c_int32, C.c_int32, C.c_int32,
@@ -198,36 +198,49 @@ def paged_step(model: Model, pool: np.ndarray, block_tables: np.ndarray, ctx_len
 
 # ---------------------------------------------------------------- pieces
 
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float64).reshape(-1)
+
+
 def rmsnorm(x, g, eps: float) -> np.ndarray:
-    x, g = as_u16(x), as_u16(g)
+    """x (double [d]) normalised and scaled by the bf16 gain g."""
+    x, g = _f64(x), as_u16(g)
     y = np.empty_like(x)
-    lib().or_rmsnorm(_p(x, U16P), _p(g, U16P), x.size, eps, _p(y, U16P))
+    lib().or_rmsnorm(_p(x, F64P), _p(g, U16P), x.size, eps, _p(y, F64P))
     return y
 
 
 def linear(x, W) -> np.ndarray:
-    x, W = as_u16(x), as_u16(W)
+    """W (bf16 [N][K]) times x (double [K])."""
+    x, W = _f64(x), as_u16(W)
+    assert W.shape[1] == x.size
     y = np.empty(W.shape[0], np.float64)
-    lib().or_linear(_p(x, U16P), W.shape[1], _p(W, U16P), W.shape[0], _p(y, F64P))
+    lib().or_linear(_p(x, F64P), W.shape[1], _p(W, U16P), W.shape[0], _p(y, F64P))
     return y
 
 
 def rope(v, pos: int, base: float) -> np.ndarray:
-    v = as_u16(v).copy()
-    lib().or_rope(_p(v, U16P), v.size, pos, base)
+    v = _f64(v).copy()
+    lib().or_rope(_p(v, F64P), v.size, pos, base)
     return v
 
 
 def attention_dense(q, K, V, n_heads: int, n_kv_heads: int, head_dim: int) -> np.ndarray:
-    """q [Hq*hd], K/V [n][Hkv][hd] bf16 -> [Hq*hd] bf16 (uint16)."""
-    q, K, V = as_u16(q), as_u16(K), as_u16(V)
-    out = np.empty(n_heads * head_dim, np.uint16)
+    """q [Hq*hd] double, K/V [n][Hkv][hd] bf16 -> [Hq*hd] double."""
+    q, K, V = _f64(q), as_u16(K), as_u16(V)
+    out = np.empty(n_heads * head_dim, np.float64)
     n = K.shape[0]
-    rc = lib().or_attention_dense(_p(q, U16P), _p(K, U16P), _p(V, U16P), n, n_heads,
-                                  n_kv_heads, head_dim, _p(out, U16P))
+    rc = lib().or_attention_dense(_p(q, F64P), _p(K, U16P), _p(V, U16P), n, n_heads,
+                                  n_kv_heads, head_dim, _p(out, F64P))
     if rc != 0:
         raise ValueError("or_attention_dense failed")
     return out
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round doubles to bf16 (nearest even) and return the bf16 bits."""
+    a = _f64(x)
+    return np.array([lib().or_f64_to_bf16(float(v)) for v in a], np.uint16)
 
 
 def f64_to_bf16(x: float) -> int:

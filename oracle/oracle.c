@@ -36,10 +36,14 @@
  *    step id, 0, 0), key = (seed, 0).
  *
  * Arithmetic: every dot product accumulates in double, in ascending index
- * order. Values are rounded to bf16 (round to nearest even, directly from
- * the double) exactly where the model stores an activation: norm outputs,
- * every projection output, RoPE outputs, attention outputs, the SwiGLU
- * product and the residual stream. Logits are not rounded (double).
+ * order, and every activation stays a double: the norm outputs, the
+ * projections, the rotated query, the attention output, the SwiGLU product
+ * and the residual stream are never rounded. bf16 appears only where the
+ * model stores values in memory that the step streams: the weights (given)
+ * and the KV cache, where each appended K (after RoPE) and V is rounded to
+ * bf16 (round to nearest even, directly from the double). Logits are
+ * doubles; the greedy id is the lowest id of the maximum of the logits
+ * rounded to binary32, the precision in which the GPU takes that decision.
  * OpenMP runs only across independent rows, heads or output elements,
  * never inside a reduction.
  */
@@ -116,50 +120,48 @@ typedef struct {
   const uint16_t* const* w_down;    /* per layer [d_model][ffn] */
 } or_model;
 
-/* RMSNorm: y_i = x_i / sqrt(mean(x^2) + eps) * g_i, stored as bf16. */
-void or_rmsnorm(const uint16_t* x, const uint16_t* g, int32_t d, double eps,
-                uint16_t* y) {
+/* RMSNorm: y_i = x_i / sqrt(mean(x^2) + eps) * g_i. */
+void or_rmsnorm(const double* x, const uint16_t* g, int32_t d, double eps, double* y) {
   double ss = 0.0;
-  for (int32_t i = 0; i < d; ++i) ss += bf(x[i]) * bf(x[i]);
+  for (int32_t i = 0; i < d; ++i) ss += x[i] * x[i];
   double inv = 1.0 / sqrt(ss / (double)d + eps);
-  for (int32_t i = 0; i < d; ++i) y[i] = tobf(bf(x[i]) * inv * bf(g[i]));
+  for (int32_t i = 0; i < d; ++i) y[i] = x[i] * inv * bf(g[i]);
 }
 
-/* y[n] = sum_k x[k] * W[n][k], W row-major [N][K], double accumulation. */
-void or_linear(const uint16_t* x, int32_t K, const uint16_t* W, int32_t N,
-               double* y) {
+/* y[n] = sum_k x[k] * W[n][k], W row-major [N][K] bf16. */
+void or_linear(const double* x, int32_t K, const uint16_t* W, int32_t N, double* y) {
   for (int32_t n = 0; n < N; ++n) {
     const uint16_t* w = W + (size_t)n * K;
     double s = 0.0;
-    for (int32_t k = 0; k < K; ++k) s += bf(x[k]) * bf(w[k]);
+    for (int32_t k = 0; k < K; ++k) s += x[k] * bf(w[k]);
     y[n] = s;
   }
 }
 
 /* RoPE, rotate-half pairing: element i pairs with i + hd/2, angle
  * pos * base^(-2i/hd). (a, b) -> (a cos - b sin, b cos + a sin). */
-void or_rope(uint16_t* v, int32_t hd, int32_t pos, double base) {
+void or_rope(double* v, int32_t hd, int32_t pos, double base) {
   int32_t half = hd / 2;
   for (int32_t i = 0; i < half; ++i) {
     double inv_freq = pow(base, -2.0 * (double)i / (double)hd);
     double th = (double)pos * inv_freq;
     double c = cos(th), s = sin(th);
-    double a = bf(v[i]), b = bf(v[i + half]);
-    v[i] = tobf(a * c - b * s);
-    v[i + half] = tobf(b * c + a * s);
+    double a = v[i], b = v[i + half];
+    v[i] = a * c - b * s;
+    v[i + half] = b * c + a * s;
   }
 }
 
 /* One query head over n keys: softmax(q.k_j / sqrt(hd)) weighted sum of v_j.
  * keys[j] / vals[j] point at hd bf16 values each. */
-static void attend_head(const uint16_t* q, const uint16_t* const* keys,
+static void attend_head(const double* q, const uint16_t* const* keys,
                         const uint16_t* const* vals, int32_t n, int32_t hd,
-                        double* s /* scratch [n] */, uint16_t* out) {
+                        double* s /* scratch [n] */, double* out) {
   double scale = 1.0 / sqrt((double)hd);
   double m = -INFINITY;
   for (int32_t j = 0; j < n; ++j) {
     double dot = 0.0;
-    for (int32_t i = 0; i < hd; ++i) dot += bf(q[i]) * bf(keys[j][i]);
+    for (int32_t i = 0; i < hd; ++i) dot += q[i] * bf(keys[j][i]);
     s[j] = dot * scale;
     if (s[j] > m) m = s[j];
   }
@@ -171,15 +173,14 @@ static void attend_head(const uint16_t* q, const uint16_t* const* keys,
   for (int32_t i = 0; i < hd; ++i) {
     double acc = 0.0;
     for (int32_t j = 0; j < n; ++j) acc += s[j] * bf(vals[j][i]);
-    out[i] = tobf(acc / den);
+    out[i] = acc / den;
   }
 }
 
-/* Dense attention for tests: q [Hq][hd], K/V [n][Hkv][hd]; query head h
- * reads KV head h*Hkv/Hq (query heads grouped contiguously). */
-int or_attention_dense(const uint16_t* q, const uint16_t* K, const uint16_t* V,
-                       int32_t n, int32_t n_heads, int32_t n_kv_heads,
-                       int32_t hd, uint16_t* out) {
+/* Dense attention for tests: q [Hq][hd] (double), K/V [n][Hkv][hd] bf16;
+ * query head h reads KV head h*Hkv/Hq (query heads grouped contiguously). */
+int or_attention_dense(const double* q, const uint16_t* K, const uint16_t* V, int32_t n,
+                       int32_t n_heads, int32_t n_kv_heads, int32_t hd, double* out) {
   if (n <= 0 || n_heads % n_kv_heads) return OR_EINVAL;
   const uint16_t** kp = malloc(sizeof(*kp) * (size_t)n);
   const uint16_t** vp = malloc(sizeof(*vp) * (size_t)n);
@@ -241,32 +242,33 @@ static int32_t qkv_width(const or_model* m) {
 }
 
 /* Stage A of a layer for one row: norm, QKV projection, RoPE at `pos`,
- * then append this row's K and V at `pos`. Leaves the rotated query in q. */
+ * then append this row's K and V at `pos` (rounded to bf16, the cache's
+ * storage type). Leaves the rotated query in q. */
 static int row_pre_attention(const or_model* m, int32_t layer, const or_kv* kv,
-                             const uint16_t* x, int32_t pos, uint16_t* q,
-                             uint16_t* hbuf, double* acc) {
-  int32_t d = m->d_model, hd = m->head_dim, hq = m->n_heads,
-          hkv = m->n_kv_heads;
+                             const double* x, int32_t pos, double* q, double* hbuf,
+                             double* acc) {
+  int32_t d = m->d_model, hd = m->head_dim, hq = m->n_heads, hkv = m->n_kv_heads;
   or_rmsnorm(x, m->attn_norm[layer], d, m->rms_eps, hbuf);
   or_linear(hbuf, d, m->w_qkv[layer], qkv_width(m), acc);
-  for (int32_t i = 0; i < hq * hd; ++i) q[i] = tobf(acc[i]);
+  memcpy(q, acc, sizeof(double) * (size_t)hq * hd);
   for (int32_t h = 0; h < hq; ++h) or_rope(q + (size_t)h * hd, hd, pos, m->rope_base);
   for (int32_t g = 0; g < hkv; ++g) {
     uint16_t* kd = kv_at(m, kv, layer, 0, pos, g);
     uint16_t* vd = kv_at(m, kv, layer, 1, pos, g);
     if (!kd || !vd) return OR_EINVAL;
+    double* k = acc + (size_t)(hq + g) * hd;
+    or_rope(k, hd, pos, m->rope_base);
     for (int32_t i = 0; i < hd; ++i) {
-      kd[i] = tobf(acc[hq * hd + g * hd + i]);
-      vd[i] = tobf(acc[(hq + hkv) * hd + g * hd + i]);
+      kd[i] = tobf(k[i]);
+      vd[i] = tobf(acc[(size_t)(hq + hkv + g) * hd + i]);
     }
-    or_rope(kd, hd, pos, m->rope_base);
   }
   return OR_OK;
 }
 
 /* Stage B: every query head of the row attends over positions 0..pos. */
 static int row_attention(const or_model* m, int32_t layer, const or_kv* kv,
-                         const uint16_t* q, int32_t pos, uint16_t* o) {
+                         const double* q, int32_t pos, double* o) {
   int32_t n = pos + 1, hd = m->head_dim;
   const uint16_t** kp = malloc(sizeof(*kp) * (size_t)n);
   const uint16_t** vp = malloc(sizeof(*vp) * (size_t)n);
@@ -292,62 +294,70 @@ static int row_attention(const or_model* m, int32_t layer, const or_kv* kv,
 }
 
 /* Stage C: O projection + residual, norm, SwiGLU FFN + residual. */
-static void row_post_attention(const or_model* m, int32_t layer, uint16_t* x,
-                               const uint16_t* o, uint16_t* hbuf, double* acc,
-                               double* acc2, uint16_t* abuf) {
+static void row_post_attention(const or_model* m, int32_t layer, double* x, const double* o,
+                               double* hbuf, double* acc, double* acc2) {
   int32_t d = m->d_model, f = m->ffn_dim, qd = m->n_heads * m->head_dim;
   or_linear(o, qd, m->w_o[layer], d, acc);
-  for (int32_t i = 0; i < d; ++i) x[i] = tobf(bf(x[i]) + bf(tobf(acc[i])));
+  for (int32_t i = 0; i < d; ++i) x[i] += acc[i];
   or_rmsnorm(x, m->ffn_norm[layer], d, m->rms_eps, hbuf);
   or_linear(hbuf, d, m->w_gate[layer], f, acc);
   or_linear(hbuf, d, m->w_up[layer], f, acc2);
   for (int32_t i = 0; i < f; ++i) {
-    double g = bf(tobf(acc[i])), u = bf(tobf(acc2[i]));
-    double silu = g / (1.0 + exp(-g));
-    abuf[i] = tobf(silu * u);
+    double g = acc[i];
+    acc[i] = g / (1.0 + exp(-g)) * acc2[i]; /* silu(gate) * up */
   }
-  or_linear(abuf, f, m->w_down[layer], d, acc);
-  for (int32_t i = 0; i < d; ++i) x[i] = tobf(bf(x[i]) + bf(tobf(acc[i])));
+  or_linear(acc, f, m->w_down[layer], d, acc2);
+  for (int32_t i = 0; i < d; ++i) x[i] += acc2[i];
 }
 
 /* Final RMSNorm and LM head: logits[v] = sum_k norm(x)[k] * W_lm[v][k]. */
-static void row_logits(const or_model* m, const uint16_t* x, double* logits) {
+static void row_logits(const or_model* m, const double* x, double* logits) {
   int32_t d = m->d_model;
-  uint16_t* h = malloc(sizeof(uint16_t) * (size_t)d);
+  double* h = malloc(sizeof(double) * (size_t)d);
   or_rmsnorm(x, m->final_norm, d, m->rms_eps, h);
 #pragma omp parallel for schedule(static)
   for (int32_t v = 0; v < m->vocab; ++v) {
     const uint16_t* w = m->lm_head + (size_t)v * d;
     double s = 0.0;
-    for (int32_t k = 0; k < d; ++k) s += bf(h[k]) * bf(w[k]);
+    for (int32_t k = 0; k < d; ++k) s += h[k] * bf(w[k]);
     logits[v] = s;
   }
   free(h);
 }
 
+/* The greedy decision: lowest id of the maximum of the logits rounded to
+ * binary32. */
+static int32_t greedy_id(const double* lg, int32_t V) {
+  int32_t best = 0;
+  float bv = (float)lg[0];
+  for (int32_t v = 1; v < V; ++v)
+    if ((float)lg[v] > bv) {
+      bv = (float)lg[v];
+      best = v;
+    }
+  return best;
+}
+
 typedef struct {
-  uint16_t *q, *h, *o, *a;
-  double *acc, *acc2;
+  double *q, *h, *o, *acc, *acc2;
 } scratch_t;
 
 static int scratch_alloc(const or_model* m, scratch_t* s) {
   int32_t w = qkv_width(m);
   int32_t big = w > m->ffn_dim ? w : m->ffn_dim;
   if (m->d_model > big) big = m->d_model;
-  s->q = malloc(sizeof(uint16_t) * (size_t)m->n_heads * m->head_dim);
-  s->o = malloc(sizeof(uint16_t) * (size_t)m->n_heads * m->head_dim);
-  s->h = malloc(sizeof(uint16_t) * (size_t)m->d_model);
-  s->a = malloc(sizeof(uint16_t) * (size_t)m->ffn_dim);
+  s->q = malloc(sizeof(double) * (size_t)m->n_heads * m->head_dim);
+  s->o = malloc(sizeof(double) * (size_t)m->n_heads * m->head_dim);
+  s->h = malloc(sizeof(double) * (size_t)m->d_model);
   s->acc = malloc(sizeof(double) * (size_t)big);
   s->acc2 = malloc(sizeof(double) * (size_t)big);
-  return (s->q && s->o && s->h && s->a && s->acc && s->acc2) ? OR_OK : OR_EINVAL;
+  return (s->q && s->o && s->h && s->acc && s->acc2) ? OR_OK : OR_EINVAL;
 }
 
 static void scratch_free(scratch_t* s) {
   free(s->q);
   free(s->o);
   free(s->h);
-  free(s->a);
   free(s->acc);
   free(s->acc2);
 }
@@ -357,6 +367,11 @@ static int model_ok(const or_model* m) {
          m->n_kv_heads > 0 && m->n_heads % m->n_kv_heads == 0 &&
          m->head_dim > 0 && m->head_dim % 2 == 0 && m->ffn_dim > 0 &&
          m->vocab > 0;
+}
+
+static void embed_row(const or_model* m, int32_t tok, double* x) {
+  const uint16_t* e = m->embed + (size_t)tok * m->d_model;
+  for (int32_t i = 0; i < m->d_model; ++i) x[i] = bf(e[i]);
 }
 
 /* ------------------------------------------------------------ serial mode */
@@ -372,7 +387,7 @@ int or_serial_forward(const or_model* m, uint16_t* kv_dense, int32_t max_pos,
     return OR_EINVAL;
   or_kv kv = {0, max_pos, kv_dense, 0, 0, NULL, 0};
   scratch_t s;
-  uint16_t* x = malloc(sizeof(uint16_t) * (size_t)m->d_model);
+  double* x = malloc(sizeof(double) * (size_t)m->d_model);
   if (scratch_alloc(m, &s) != OR_OK || !x) return OR_EINVAL;
   int rc = OR_OK;
   for (int32_t t = 0; t < n && rc == OR_OK; ++t) {
@@ -381,11 +396,11 @@ int or_serial_forward(const or_model* m, uint16_t* kv_dense, int32_t max_pos,
       rc = OR_EINVAL;
       break;
     }
-    memcpy(x, m->embed + (size_t)tok * m->d_model, sizeof(uint16_t) * (size_t)m->d_model);
+    embed_row(m, tok, x);
     for (int32_t l = 0; l < m->n_layers && rc == OR_OK; ++l) {
       rc = row_pre_attention(m, l, &kv, x, pos, s.q, s.h, s.acc);
       if (rc == OR_OK) rc = row_attention(m, l, &kv, s.q, pos, s.o);
-      if (rc == OR_OK) row_post_attention(m, l, x, s.o, s.h, s.acc, s.acc2, s.a);
+      if (rc == OR_OK) row_post_attention(m, l, x, s.o, s.h, s.acc, s.acc2);
     }
     if (rc == OR_OK && logits && (!last_only || t == n - 1))
       row_logits(m, x, logits + (last_only ? 0 : (size_t)t * m->vocab));
@@ -405,8 +420,8 @@ int or_serial_forward(const or_model* m, uint16_t* kv_dense, int32_t max_pos,
  * each row over its own positions 0..pos through its block table, which
  * makes a prefill chunk causal; (C) the rest of the layer. Sequences with
  * want_token[s] != 0 emit logits for their last row, in sequence order,
- * into logits_out [n_out][vocab]; greedy_out (optional) gets the lowest id of
- * the maximum. pool: [L][2][num_blocks][bs][Hkv][hd]. */
+ * into logits_out [n_out][vocab]; greedy_out (optional) gets the greedy id.
+ * pool: [L][2][num_blocks][bs][Hkv][hd]. */
 int or_paged_step(const or_model* m, uint16_t* pool, int32_t num_blocks,
                   int32_t block_size, int32_t n_seqs, const int32_t* block_tables,
                   int32_t max_blocks_per_seq, const int32_t* ctx_lens,
@@ -422,9 +437,9 @@ int or_paged_step(const or_model* m, uint16_t* pool, int32_t num_blocks,
     R += n_new[s];
   }
   int32_t d = m->d_model, qd = m->n_heads * m->head_dim;
-  uint16_t* X = malloc(sizeof(uint16_t) * (size_t)R * d);
-  uint16_t* Q = malloc(sizeof(uint16_t) * (size_t)R * qd);
-  uint16_t* O = malloc(sizeof(uint16_t) * (size_t)R * qd);
+  double* X = malloc(sizeof(double) * (size_t)R * d);
+  double* Q = malloc(sizeof(double) * (size_t)R * qd);
+  double* O = malloc(sizeof(double) * (size_t)R * qd);
   int32_t* row_seq = malloc(sizeof(int32_t) * (size_t)R);
   int32_t* row_pos = malloc(sizeof(int32_t) * (size_t)R);
   or_kv* kvs = malloc(sizeof(or_kv) * (size_t)n_seqs);
@@ -440,8 +455,7 @@ int or_paged_step(const or_model* m, uint16_t* pool, int32_t num_blocks,
       if (tokens[r] < 0 || tokens[r] >= m->vocab) rc = OR_EINVAL;
     }
   }
-  for (int32_t r = 0; r < R && rc == OR_OK; ++r)
-    memcpy(X + (size_t)r * d, m->embed + (size_t)tokens[r] * d, sizeof(uint16_t) * (size_t)d);
+  for (int32_t r = 0; r < R && rc == OR_OK; ++r) embed_row(m, tokens[r], X + (size_t)r * d);
 
   for (int32_t l = 0; l < m->n_layers && rc == OR_OK; ++l) {
 #pragma omp parallel
@@ -450,20 +464,19 @@ int or_paged_step(const or_model* m, uint16_t* pool, int32_t num_blocks,
       int lrc = scratch_alloc(m, &sc);
 #pragma omp for schedule(static)
       for (int32_t r = 0; r < R; ++r) {
-        int e = row_pre_attention(m, l, &kvs[row_seq[r]], X + (size_t)r * d,
-                                  row_pos[r], Q + (size_t)r * qd, sc.h, sc.acc);
+        int e = row_pre_attention(m, l, &kvs[row_seq[r]], X + (size_t)r * d, row_pos[r],
+                                  Q + (size_t)r * qd, sc.h, sc.acc);
         if (e != OR_OK) lrc = e;
       }
 #pragma omp for schedule(dynamic)
       for (int32_t r = 0; r < R; ++r) {
-        int e = row_attention(m, l, &kvs[row_seq[r]], Q + (size_t)r * qd,
-                              row_pos[r], O + (size_t)r * qd);
+        int e = row_attention(m, l, &kvs[row_seq[r]], Q + (size_t)r * qd, row_pos[r],
+                              O + (size_t)r * qd);
         if (e != OR_OK) lrc = e;
       }
 #pragma omp for schedule(static)
       for (int32_t r = 0; r < R; ++r)
-        row_post_attention(m, l, X + (size_t)r * d, O + (size_t)r * qd, sc.h,
-                           sc.acc, sc.acc2, sc.a);
+        row_post_attention(m, l, X + (size_t)r * d, O + (size_t)r * qd, sc.h, sc.acc, sc.acc2);
       if (lrc != OR_OK) {
 #pragma omp atomic write
         rc = lrc;
@@ -478,12 +491,7 @@ int or_paged_step(const or_model* m, uint16_t* pool, int32_t num_blocks,
       if (!want_token[s]) continue;
       double* lg = logits_out + (size_t)o * m->vocab;
       row_logits(m, X + (size_t)(r - 1) * d, lg);
-      if (greedy_out) {
-        int32_t best = 0;
-        for (int32_t v = 1; v < m->vocab; ++v)
-          if (lg[v] > lg[best]) best = v;
-        greedy_out[o] = best;
-      }
+      if (greedy_out) greedy_out[o] = greedy_id(lg, m->vocab);
       ++o;
     }
   }

@@ -53,13 +53,13 @@ def test_bf16_matches_torch_on_float32_values():
 def test_linear_matches_numpy_float64():
     rng = np.random.default_rng(2)
     K, N = 300, 37
-    x = bf16_bits(rng.standard_normal(K).astype(np.float32))
+    x = rng.standard_normal(K)
     W = bf16_bits(rng.standard_normal((N, K)).astype(np.float32))
-    got = O.linear(x, W)
-    ref = O.bf16_to_f64(W).reshape(N, K) @ O.bf16_to_f64(x)
+    got = O.linear(x, W.reshape(N, K))
+    ref = O.bf16_to_f64(W).reshape(N, K) @ x
     assert np.allclose(got, ref, rtol=0, atol=1e-12)
     # a transposed operand would not agree
-    assert not np.allclose(got, (O.bf16_to_f64(W).reshape(N, K).T[:N, :N] @ O.bf16_to_f64(x)[:N]))
+    assert not np.allclose(got, (O.bf16_to_f64(W).reshape(N, K).T[:N, :N] @ x[:N]))
 
 
 # ----------------------------------------------------------------- rmsnorm
@@ -67,30 +67,34 @@ def test_linear_matches_numpy_float64():
 def test_rmsnorm_unit_gain_gives_unit_mean_square():
     rng = np.random.default_rng(3)
     for d in (64, 256, 4096):
-        x = bf16_bits((rng.standard_normal(d) * 3.7).astype(np.float32))
+        x = rng.standard_normal(d) * 3.7
         g = bf16_bits(np.ones(d, np.float32))
-        y = O.bf16_to_f64(O.rmsnorm(x, g, 1e-5))
-        assert abs(np.mean(y * y) - 1.0) < 5e-3
-        # direction kept: y is a positive multiple of x (within bf16 rounding)
-        xs = O.bf16_to_f64(x)
-        assert np.all(np.sign(y[xs != 0]) == np.sign(xs[xs != 0]))
+        y = O.rmsnorm(x, g, 1e-5)
+        # mean(y^2) = ms / (ms + eps) exactly
+        ms = np.mean(x * x)
+        assert abs(np.mean(y * y) - ms / (ms + 1e-5)) < 1e-12
+        # direction kept: y is a positive multiple of x
+        ratio = y / x
+        assert np.allclose(ratio, ratio[0], rtol=1e-12) and ratio[0] > 0
 
 
 def test_rmsnorm_gain_is_elementwise_and_eps_matters_for_tiny_inputs():
     rng = np.random.default_rng(4)
     d = 128
-    x = bf16_bits(rng.standard_normal(d).astype(np.float32))
+    x = rng.standard_normal(d)
     g1 = bf16_bits(np.ones(d, np.float32))
     g2 = bf16_bits(np.full(d, 2.0, np.float32))
-    y1, y2 = O.bf16_to_f64(O.rmsnorm(x, g1, 1e-5)), O.bf16_to_f64(O.rmsnorm(x, g2, 1e-5))
-    assert np.array_equal(2.0 * y1, y2)          # doubling is exact in bf16
+    y1, y2 = O.rmsnorm(x, g1, 1e-5), O.rmsnorm(x, g2, 1e-5)
+    assert np.array_equal(2.0 * y1, y2)          # doubling is exact
     gz = np.ones(d, np.float32)
     gz[5] = 0
-    yz = O.bf16_to_f64(O.rmsnorm(x, bf16_bits(gz), 1e-5))
+    yz = O.rmsnorm(x, bf16_bits(gz), 1e-5)
     assert yz[5] == 0 and np.array_equal(np.delete(yz, 5), np.delete(y1, 5))
     # all-zero input: eps keeps it finite and the output is zero
-    z = O.rmsnorm(np.zeros(d, np.uint16), g1, 1e-5)
-    assert np.all(O.bf16_to_f64(z) == 0)
+    assert np.all(O.rmsnorm(np.zeros(d), g1, 1e-5) == 0)
+    # a tiny input is damped by eps: y = x / sqrt(ms + eps)
+    t = np.full(d, 1e-4)
+    assert abs(O.rmsnorm(t, g1, 1e-5)[0] - 1e-4 / math.sqrt(1e-8 + 1e-5)) < 1e-15
 
 
 # -------------------------------------------------------------------- rope
@@ -98,47 +102,54 @@ def test_rmsnorm_gain_is_elementwise_and_eps_matters_for_tiny_inputs():
 def test_rope_position_zero_is_identity_and_pairing():
     hd = 64
     rng = np.random.default_rng(5)
-    v = bf16_bits(rng.standard_normal(hd).astype(np.float32))
+    v = rng.standard_normal(hd)
     assert np.array_equal(O.rope(v, 0, 10000.0), v)
-    # element 0 turns by exactly `pos` radians against element hd/2
-    e = np.zeros(hd, np.float32)
-    e[0] = 1.0
-    r = O.bf16_to_f64(O.rope(bf16_bits(e), 1, 10000.0))
-    assert abs(r[0] - math.cos(1.0)) < 4e-3 and abs(r[hd // 2] - math.sin(1.0)) < 4e-3
-    assert np.count_nonzero(r) == 2
+    # element 0 turns by exactly `pos` radians against element hd/2; element
+    # i turns by pos * base^(-2i/hd)
+    for i in (0, 5, 31):
+        e = np.zeros(hd)
+        e[i] = 1.0
+        ang = 7 * 10000.0 ** (-2 * i / hd)
+        r = O.rope(e, 7, 10000.0)
+        assert abs(r[i] - math.cos(ang)) < 1e-14 and abs(r[i + hd // 2] - math.sin(ang)) < 1e-14
+        assert np.count_nonzero(r) == 2
+    # the second half rotates the other way round: (0, 1) -> (-sin, cos)
+    e = np.zeros(hd)
+    e[hd // 2] = 1.0
+    r = O.rope(e, 1, 10000.0)
+    assert abs(r[0] + math.sin(1.0)) < 1e-14 and abs(r[hd // 2] - math.cos(1.0)) < 1e-14
 
 
 def test_rope_preserves_pair_norms_and_relative_positions():
     hd = 128
     rng = np.random.default_rng(6)
-    q = bf16_bits(rng.standard_normal(hd).astype(np.float32))
-    k = bf16_bits(rng.standard_normal(hd).astype(np.float32))
+    q = rng.standard_normal(hd)
+    k = rng.standard_normal(hd)
     for pos in (1, 17, 3000):
-        rq = O.bf16_to_f64(O.rope(q, pos, 10000.0))
-        a = O.bf16_to_f64(q)
-        n0 = a[:hd // 2] ** 2 + a[hd // 2:] ** 2
+        rq = O.rope(q, pos, 10000.0)
+        n0 = q[:hd // 2] ** 2 + q[hd // 2:] ** 2
         n1 = rq[:hd // 2] ** 2 + rq[hd // 2:] ** 2
-        assert np.allclose(n0, n1, rtol=2e-2, atol=1e-3)
+        assert np.allclose(n0, n1, rtol=1e-12, atol=0)
     # q(p+t).k(p'+t) = q(p).k(p') for any shift t
     def dot(p1, p2):
-        return float(np.dot(O.bf16_to_f64(O.rope(q, p1, 1e4)), O.bf16_to_f64(O.rope(k, p2, 1e4))))
+        return float(np.dot(O.rope(q, p1, 1e4), O.rope(k, p2, 1e4)))
     base = dot(10, 3)
     for t in (1, 50, 700):
-        assert abs(dot(10 + t, 3 + t) - base) < 0.05 * (1 + abs(base))
+        assert abs(dot(10 + t, 3 + t) - base) < 1e-9 * (1 + abs(base))
     assert abs(dot(11, 3) - base) > 1e-3          # it does depend on the offset
 
 
 # --------------------------------------------------------------- attention
 
-def brute_attention(q, K, V, hq, hkv, hd):
+def brute_attention(q, K, V, hq, hkv, hd, group=None):
     """softmax(q k^T / sqrt(hd)) v per head in numpy float64; query head h
-    reads KV head h // (hq // hkv)."""
-    qf = O.bf16_to_f64(q).reshape(hq, hd)
+    reads KV head group(h), by default h // (hq // hkv)."""
+    qf = np.asarray(q, np.float64).reshape(hq, hd)
     Kf = O.bf16_to_f64(K).reshape(-1, hkv, hd)
     Vf = O.bf16_to_f64(V).reshape(-1, hkv, hd)
     out = np.empty((hq, hd))
     for h in range(hq):
-        g = h // (hq // hkv)
+        g = group(h) if group else h // (hq // hkv)
         s = Kf[:, g, :] @ qf[h] / math.sqrt(hd)
         p = np.exp(s - s.max())
         p /= p.sum()
@@ -150,27 +161,31 @@ def brute_attention(q, K, V, hq, hkv, hd):
                                          (130, 32, 8, 128)])
 def test_attention_matches_dense_brute_force(n, hq, hkv, hd):
     rng = np.random.default_rng(n + hq)
-    q = bf16_bits(rng.standard_normal(hq * hd).astype(np.float32))
+    q = rng.standard_normal(hq * hd)
     K = bf16_bits(rng.standard_normal((n, hkv, hd)).astype(np.float32))
     V = bf16_bits(rng.standard_normal((n, hkv, hd)).astype(np.float32))
-    got = O.bf16_to_f64(O.attention_dense(q, K, V, hq, hkv, hd)).reshape(hq, hd)
+    got = O.attention_dense(q, K, V, hq, hkv, hd).reshape(hq, hd)
     ref = brute_attention(q, K, V, hq, hkv, hd)
-    assert np.allclose(got, ref, rtol=8e-3, atol=8e-3)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
     if n == 1:   # a single key: the output is that value vector
         for h in range(hq):
             assert np.array_equal(got[h], O.bf16_to_f64(V)[0, h // (hq // hkv)])
+    # the wrong group mapping (h % hkv instead of h // G) disagrees
+    if hkv > 1 and n > 1:
+        wrong = brute_attention(q, K, V, hq, hkv, hd, group=lambda h: h % hkv)
+        assert not np.allclose(got, wrong, atol=1e-6)
 
 
 def test_attention_equal_keys_average_values():
     n, hq, hkv, hd = 9, 4, 2, 64
     rng = np.random.default_rng(11)
-    q = bf16_bits(rng.standard_normal(hq * hd).astype(np.float32))
+    q = rng.standard_normal(hq * hd)
     K = np.repeat(bf16_bits(rng.standard_normal((1, hkv, hd)).astype(np.float32)), n, 0)
     V = bf16_bits(rng.standard_normal((n, hkv, hd)).astype(np.float32))
-    got = O.bf16_to_f64(O.attention_dense(q, K, V, hq, hkv, hd)).reshape(hq, hd)
+    got = O.attention_dense(q, K, V, hq, hkv, hd).reshape(hq, hd)
     mean = O.bf16_to_f64(V).reshape(n, hkv, hd).mean(0)
     for h in range(hq):
-        assert np.allclose(got[h], mean[h // 2], atol=4e-3)
+        assert np.allclose(got[h], mean[h // 2], rtol=0, atol=1e-14)
 
 
 # ------------------------------------------------------------------ argmax

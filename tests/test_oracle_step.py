@@ -122,8 +122,8 @@ def one_layer(seed, zero=()):
     return cfg, w
 
 
-def f64(t):
-    return O.bf16_to_f64(t).reshape(t.shape if hasattr(t, "shape") else -1)
+def lm(w, cfg, hf):
+    return O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ hf
 
 
 def test_zero_projections_make_the_layer_identity():
@@ -133,9 +133,8 @@ def test_zero_projections_make_the_layer_identity():
     m = O.Model(cfg, w)
     tok = 123
     lg = O.serial_forward(m, m.dense_kv(4), [tok], 0)
-    h = O.rmsnorm(w["embed"][tok], w["final_norm"], cfg.rms_eps)
-    ref = O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ O.bf16_to_f64(h)
-    assert np.allclose(lg, ref, rtol=0, atol=1e-12)
+    h = O.rmsnorm(O.bf16_to_f64(w["embed"][tok]), w["final_norm"], cfg.rms_eps)
+    assert np.allclose(lg, lm(w, cfg, h), rtol=0, atol=1e-12)
 
 
 def test_ffn_branch_is_silu_gate_times_up_then_down():
@@ -146,22 +145,19 @@ def test_ffn_branch_is_silu_gate_times_up_then_down():
     m = O.Model(cfg, w)
     tok = 77
     lg = O.serial_forward(m, m.dense_kv(4), [tok], 0)
-    x = O.as_u16(w["embed"][tok])
+    x = O.bf16_to_f64(w["embed"][tok])
     h = O.rmsnorm(x, w["ffn_norm"][0], cfg.rms_eps)
-    g = O.linear(h, w["w_gate"][0])
-    u = O.linear(h, w["w_up"][0])
-    rb = np.vectorize(lambda v: O.bf16_to_float(O.f64_to_bf16(v)))
-    g, u = rb(g), rb(u)
-    a = rb(g / (1.0 + np.exp(-g)) * u)
-    a16 = np.array([O.f64_to_bf16(v) for v in a], np.uint16)
-    down = rb(O.linear(a16, w["w_down"][0]))
-    x2 = np.array([O.f64_to_bf16(v) for v in O.bf16_to_f64(x) + down], np.uint16)
-    hf = O.rmsnorm(x2, w["final_norm"], cfg.rms_eps)
-    ref = O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ O.bf16_to_f64(hf)
-    assert np.allclose(lg, ref, rtol=0, atol=1e-9)
-    # the swapped SwiGLU gives visibly different logits
-    a_sw = rb(u / (1.0 + np.exp(-u)) * g)
+    g = O.bf16_to_f64(w["w_gate"][0]).reshape(cfg.ffn_dim, cfg.d_model) @ h
+    u = O.bf16_to_f64(w["w_up"][0]).reshape(cfg.ffn_dim, cfg.d_model) @ h
+    a = g / (1.0 + np.exp(-g)) * u
+    down = O.bf16_to_f64(w["w_down"][0]).reshape(cfg.d_model, cfg.ffn_dim) @ a
+    hf = O.rmsnorm(x + down, w["final_norm"], cfg.rms_eps)
+    assert np.allclose(lg, lm(w, cfg, hf), rtol=0, atol=1e-9)
+    # the swapped SwiGLU and the dropped residual give visibly different logits
+    a_sw = u / (1.0 + np.exp(-u)) * g
     assert np.max(np.abs(a_sw - a)) > 1e-3
+    no_res = lm(w, cfg, O.rmsnorm(down, w["final_norm"], cfg.rms_eps))
+    assert np.max(np.abs(no_res - lg)) > 1e-2
 
 
 def test_attention_branch_reads_the_cached_prefix():
@@ -173,25 +169,27 @@ def test_attention_branch_reads_the_cached_prefix():
     kv = m.dense_kv(4)
     toks = [11, 2222]
     lg = O.serial_forward(m, kv, toks, 0, last_only=False)
-    x = O.as_u16(w["embed"][toks[1]])
-    h = O.rmsnorm(x, w["attn_norm"][0], cfg.rms_eps)
-    qkv = O.linear(h, w["w_qkv"][0])
     hq, hkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
-    q = np.array([O.f64_to_bf16(v) for v in qkv[:hq * hd]], np.uint16)
-    q = np.concatenate([O.rope(q[i * hd:(i + 1) * hd], 1, cfg.rope_base) for i in range(hq)])
+    wqkv = O.bf16_to_f64(w["w_qkv"][0]).reshape(-1, cfg.d_model)
+    x = O.bf16_to_f64(w["embed"][toks[1]])
+    qkv = wqkv @ O.rmsnorm(x, w["attn_norm"][0], cfg.rms_eps)
+    q = np.concatenate([O.rope(qkv[i * hd:(i + 1) * hd], 1, cfg.rope_base) for i in range(hq)])
     K = kv[0, 0, :2].copy()
     V = kv[0, 1, :2].copy()
-    # the cached K of position 1 is this token's rotated k
-    k1 = np.array([O.f64_to_bf16(v) for v in qkv[hq * hd:(hq + hkv) * hd]], np.uint16)
-    k1 = np.concatenate([O.rope(k1[i * hd:(i + 1) * hd], 1, cfg.rope_base) for i in range(hkv)])
-    assert np.array_equal(K[1].reshape(-1), k1)
+    # the cached K of position 1 is this token's rotated k rounded to bf16,
+    # its V the plain v rounded to bf16
+    k1 = np.concatenate([O.rope(qkv[(hq + i) * hd:(hq + i + 1) * hd], 1, cfg.rope_base)
+                         for i in range(hkv)])
+    assert np.array_equal(K[1].reshape(-1), O.bf16_round(k1))
+    assert np.array_equal(V[1].reshape(-1), O.bf16_round(qkv[(hq + hkv) * hd:]))
+    # and position 0 holds token 0's, rotated by angle 0
+    x0 = O.bf16_to_f64(w["embed"][toks[0]])
+    qkv0 = wqkv @ O.rmsnorm(x0, w["attn_norm"][0], cfg.rms_eps)
+    assert np.array_equal(K[0].reshape(-1), O.bf16_round(qkv0[hq * hd:(hq + hkv) * hd]))
     o = O.attention_dense(q, K, V, hq, hkv, hd)
-    t = O.linear(o, w["w_o"][0])
-    x2 = np.array([O.f64_to_bf16(a + O.bf16_to_float(O.f64_to_bf16(b)))
-                   for a, b in zip(O.bf16_to_f64(x), t)], np.uint16)
-    hf = O.rmsnorm(x2, w["final_norm"], cfg.rms_eps)
-    ref = O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ O.bf16_to_f64(hf)
-    assert np.allclose(lg[1], ref, rtol=0, atol=1e-9)
+    t = O.bf16_to_f64(w["w_o"][0]).reshape(cfg.d_model, hq * hd) @ o
+    hf = O.rmsnorm(x + t, w["final_norm"], cfg.rms_eps)
+    assert np.allclose(lg[1], lm(w, cfg, hf), rtol=0, atol=1e-9)
 
 
 def test_layers_apply_in_order_with_their_own_weights():
