@@ -15,7 +15,8 @@
 //
 // One wave per work item, 32 keys per iteration, two MFMAs shapes:
 //   S[32 keys][16 cols] = K . Q^T       v_mfma_f32_16x16x32_bf16, A = K rows,
-//                                       B = Q, K-dim = head_dim
+//                                       B = Q (its hi and lo bf16 terms, two
+//                                       MFMAs), K-dim = head_dim
 //   O^T[hd][16 cols]   += V^T . P^T     A = V^T rows, B = P, K-dim = 32 keys
 // The key order inside the S tiles is chosen so that the four lane groups
 // end up holding 8 consecutive keys each, which is exactly the B operand the
@@ -45,7 +46,8 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ item0, int n
 
 template <int HD, bool WIDE_BLOCKS>
 __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
-    const uint16_t* __restrict__ q, StepMeta m, RowMaps maps, ModelDims md, AttnPlan ap,
+    const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, StepMeta m,
+    RowMaps maps, ModelDims md, AttnPlan ap,
     const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v,
     float* __restrict__ part_ml, float* __restrict__ part_o, uint32_t* status) {
   constexpr int QK_STEPS = HD / 32;  // MFMAs over head_dim
@@ -77,15 +79,18 @@ __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
   const int k_hi = min(k_lo + ap.split_len, ctx + last_row + 1);
   const int c_end = c_ok ? min(k_hi, ctx + c_row + 1) : k_lo;  // keys [k_lo, c_end)
 
-  // Q as the B operand: lane (lr, lg) holds d = lg*HD/4 + 8j .. +8 of its column.
-  bf16x8_t qf[QK_STEPS];
+  // Q as the B operand: lane (lr, lg) holds d = lg*HD/4 + 8j .. +8 of its
+  // column, as the hi and the lo bf16 terms of the fp32 query.
+  bf16x8_t qf[2][QK_STEPS];
   {
-    const uint16_t* qp = q + ((size_t)(row0 + (c_ok ? c_row : 0)) * md.n_heads + c_head) * HD +
-                         lg * (HD / 4);
+    const size_t at = ((size_t)(row0 + (c_ok ? c_row : 0)) * md.n_heads + c_head) * HD +
+                      lg * (HD / 4);
 #pragma unroll
     for (int j = 0; j < QK_STEPS; ++j) {
-      uint4 v = c_ok ? reinterpret_cast<const uint4*>(qp)[j] : make_uint4(0, 0, 0, 0);
-      qf[j] = as_bf16x8(v);
+      qf[0][j] = as_bf16x8(c_ok ? reinterpret_cast<const uint4*>(q_hi + at)[j]
+                                : make_uint4(0, 0, 0, 0));
+      qf[1][j] = as_bf16x8(c_ok ? reinterpret_cast<const uint4*>(q_lo + at)[j]
+                                : make_uint4(0, 0, 0, 0));
     }
   }
 
@@ -191,7 +196,10 @@ __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
     for (int t = 0; t < 2; ++t) {
       sacc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < QK_STEPS; ++j) sacc[t] = mfma16x16x32(as_bf16x8(kf[t][j]), qf[j], sacc[t]);
+      for (int j = 0; j < QK_STEPS; ++j) {
+        sacc[t] = mfma16x16x32(as_bf16x8(kf[t][j]), qf[0][j], sacc[t]);
+        sacc[t] = mfma16x16x32(as_bf16x8(kf[t][j]), qf[1][j], sacc[t]);
+      }
     }
     // lane (lr, lg) now holds column lr for keys p0 + 8 lg + jj, jj = i + 4 t
     float sv[8];
@@ -263,17 +271,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
                                                            AttnPlan ap, int R,
                                                            const float* __restrict__ part_ml,
                                                            const float* __restrict__ part_o,
-                                                           uint16_t* __restrict__ out) {
+                                                           uint16_t* __restrict__ out_hi,
+                                                           uint16_t* __restrict__ out_lo) {
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= R * md.n_heads) return;
   const int r = w / md.n_heads, h = w % md.n_heads;
   constexpr int PER = HD / 64;  // dims per lane
-  uint16_t* dst = out + ((size_t)r * md.n_heads + h) * HD;
+  const size_t at = ((size_t)r * md.n_heads + h) * HD + lane * PER;
   const int s = maps.row_seq[r];
   if (s < 0) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) dst[lane * PER + e] = 0;
+    for (int e = 0; e < PER; ++e) out_hi[at + e] = out_lo[at + e] = 0;
     return;
   }
   const int pos = maps.row_pos[r];
@@ -293,40 +302,48 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
   }
   const float inv = 1.0f / den;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) dst[lane * PER + e] = f2bf(acc[e] * inv);
+  for (int e = 0; e < PER; ++e) {
+    bf16_t hi, lo;
+    split_bf(acc[e] * inv, hi, lo);
+    out_hi[at + e] = hi;
+    out_lo[at + e] = lo;
+  }
 }
 
 template <int HD>
-static hipError_t launch_hd(const uint16_t* q, int32_t R, const StepMeta& m, const RowMaps& maps,
-                            const ModelDims& md, const AttnPlan& ap, const uint16_t* pool_k,
-                            const uint16_t* pool_v, float* part_ml, float* part_o, uint16_t* out,
+static hipError_t launch_hd(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R,
+                            const StepMeta& m, const RowMaps& maps, const ModelDims& md,
+                            const AttnPlan& ap, const uint16_t* pool_k, const uint16_t* pool_v,
+                            float* part_ml, float* part_o, uint16_t* out_hi, uint16_t* out_lo,
                             uint32_t* status, hipStream_t st) {
   const int blocks = (ap.grid_items + ATT_WAVES - 1) / ATT_WAVES;
   if (blocks > 0) {
     if (md.block_size % 8 == 0)
-      attention_kernel<HD, true><<<blocks, 64 * ATT_WAVES, 0, st>>>(q, m, maps, md, ap, pool_k,
-                                                                     pool_v, part_ml, part_o,
-                                                                     status);
+      attention_kernel<HD, true><<<blocks, 64 * ATT_WAVES, 0, st>>>(
+          q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status);
     else
-      attention_kernel<HD, false><<<blocks, 64 * ATT_WAVES, 0, st>>>(q, m, maps, md, ap, pool_k,
-                                                                      pool_v, part_ml, part_o,
-                                                                      status);
+      attention_kernel<HD, false><<<blocks, 64 * ATT_WAVES, 0, st>>>(
+          q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int waves = R * md.n_heads;
-  attn_combine_kernel<HD><<<(waves + 3) / 4, 256, 0, st>>>(m, maps, md, ap, R, part_ml, part_o, out);
+  attn_combine_kernel<HD><<<(waves + 3) / 4, 256, 0, st>>>(m, maps, md, ap, R, part_ml, part_o,
+                                                            out_hi, out_lo);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const uint16_t* q, int32_t R, const StepMeta& m, const RowMaps& maps,
-                            const ModelDims& md, const AttnPlan& ap, const uint16_t* pool_k,
-                            const uint16_t* pool_v, float* part_ml, float* part_o, uint16_t* out,
+hipError_t launch_attention(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R,
+                            const StepMeta& m, const RowMaps& maps, const ModelDims& md,
+                            const AttnPlan& ap, const uint16_t* pool_k, const uint16_t* pool_v,
+                            float* part_ml, float* part_o, uint16_t* out_hi, uint16_t* out_lo,
                             uint32_t* status, hipStream_t st) {
   if (R <= 0) return hipSuccess;
   if (md.head_dim == 128)
-    return launch_hd<128>(q, R, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, out, status, st);
-  return launch_hd<64>(q, R, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, out, status, st);
+    return launch_hd<128>(q_hi, q_lo, R, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, out_hi,
+                          out_lo, status, st);
+  return launch_hd<64>(q_hi, q_lo, R, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, out_hi,
+                       out_lo, status, st);
 }
 
 }  // namespace cbd

@@ -33,6 +33,30 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// An fp32 activation travels to the MFMAs as two bf16 terms: hi = bf16(v)
+// and lo = bf16(v - hi). v - hi is exact in fp32, so hi + lo equals v to
+// within 2^-17 |v|, and a product with a bf16 weight is the sum of two bf16
+// products, each exact in the fp32 accumulator.
+__device__ __forceinline__ void split_bf(float v, bf16_t& hi, bf16_t& lo) {
+  hi = f2bf(v);
+  lo = f2bf(v - bf2f(hi));
+}
+
+// Split four consecutive values and store them to the hi and lo planes
+// (8-byte stores; p must be 8-byte aligned in both planes).
+__device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, size_t at, float a,
+                                             float b, float c, float d) {
+  bf16_t h[4], l[4];
+  split_bf(a, h[0], l[0]);
+  split_bf(b, h[1], l[1]);
+  split_bf(c, h[2], l[2]);
+  split_bf(d, h[3], l[3]);
+  *reinterpret_cast<uint2*>(hi + at) =
+      make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+  *reinterpret_cast<uint2*>(lo + at) =
+      make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
+}
+
 // 16-byte load that asks the memory system not to keep the line (weights
 // are streamed once per step).
 __device__ __forceinline__ uint4 load_stream16(const uint16_t* p) {

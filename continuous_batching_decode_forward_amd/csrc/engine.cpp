@@ -62,13 +62,15 @@ WorkspaceLayout workspace_layout(const cbd_config& c) {
   L.out_row = take(R * 4);
   L.out_seq = take(R * 4);
   L.item0 = take((S + 1) * 4);
-  L.x = take(R * d * 2);
-  L.h = take(R * d * 2);
-  L.qkv = take(R * qkv_n * 2);
-  L.q = take(R * qd * 2);
-  L.attn = take(R * qd * 2);
-  L.ffn = take(R * (size_t)c.ffn_dim * 2);
-  L.lm_in = take(S * d * 2);
+  // fp32 buffers [rows][w] and split buffers (hi plane [rows][w] bf16, then
+  // the lo plane) both take 4 bytes per element.
+  L.x = take(R * d * 4);
+  L.h = take(R * d * 4);
+  L.qkv = take(R * qkv_n * 4);
+  L.q = take(R * qd * 4);
+  L.attn = take(R * qd * 4);
+  L.ffn = take(R * (size_t)c.ffn_dim * 4);
+  L.lm_in = take(S * d * 4);
   L.logits = take(S * (size_t)c.vocab * 4);
   L.amax_stride = (c.vocab + 15) / 16;
   L.amax_val = take(S * (size_t)L.amax_stride * 4);
@@ -400,63 +402,74 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
                e->wsp<int32_t>(e->ws.seq_row0), e->wsp<int32_t>(e->ws.out_row),
                e->wsp<int32_t>(e->ws.out_seq), e->wsp<int32_t>(e->ws.item0)};
   const AttnPlan ap = plan_attention(e, s);
-  uint16_t* x = e->wsp<uint16_t>(e->ws.x);
-  uint16_t* h = e->wsp<uint16_t>(e->ws.h);
-  uint16_t* qkv = e->wsp<uint16_t>(e->ws.qkv);
-  uint16_t* q = e->wsp<uint16_t>(e->ws.q);
-  uint16_t* attn = e->wsp<uint16_t>(e->ws.attn);
-  uint16_t* ffn = e->wsp<uint16_t>(e->ws.ffn);
-  float* gpart = e->wsp<float>(e->ws.gemm_part);
   const int qkv_n = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   const int qd = c.n_heads * c.head_dim;
+  const size_t MR = (size_t)c.max_rows;
+  float* x = e->wsp<float>(e->ws.x);
+  float* qkv = e->wsp<float>(e->ws.qkv);
+  // split buffers: the lo plane follows the hi plane
+  uint16_t* h = e->wsp<uint16_t>(e->ws.h);
+  uint16_t* h_lo = h + MR * c.d_model;
+  uint16_t* q = e->wsp<uint16_t>(e->ws.q);
+  uint16_t* q_lo = q + MR * qd;
+  uint16_t* attn = e->wsp<uint16_t>(e->ws.attn);
+  uint16_t* attn_lo = attn + MR * qd;
+  uint16_t* ffn = e->wsp<uint16_t>(e->ws.ffn);
+  uint16_t* ffn_lo = ffn + MR * c.ffn_dim;
+  float* gpart = e->wsp<float>(e->ws.gemm_part);
 
   HIP_TRY(launch_prep(m, maps, e->md, ap, status, st));
   HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
   HIP_TRY(launch_embed_norm(s->tokens, maps.row_seq, R, e->embed, e->attn_norm[0], e->md, x, h,
-                            status, st));
+                            h_lo, status, st));
   HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
   for (int l = 0; l < c.n_layers; ++l) {
-    if (l > 0) HIP_TRY(launch_rmsnorm(x, nullptr, R, e->attn_norm[l], c.d_model, c.rms_eps, h, st));
+    if (l > 0)
+      HIP_TRY(launch_rmsnorm(x, nullptr, R, e->attn_norm[l], c.d_model, c.rms_eps, h, h_lo, st));
     GemmArgs g{};
     g.partials = gpart;
     g.partials_cap = e->ws.gemm_part_floats;
-    g.X = h; g.R = R; g.K = c.d_model; g.W = e->packed + e->pl.qkv[l]; g.N = qkv_n; g.epi = EPI_BF16; g.Y = qkv;
+    g.X = h; g.Xlo = h_lo; g.R = R; g.K = c.d_model; g.W = e->packed + e->pl.qkv[l]; g.N = qkv_n;
+    g.epi = EPI_F32; g.Y = qkv;
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
-    HIP_TRY(launch_rope_append(qkv, R, m, maps, e->wsp<double>(e->ws.rope), e->md, q, e->pool_k(l),
-                               e->pool_v(l), status, st));
+    HIP_TRY(launch_rope_append(qkv, R, m, maps, e->wsp<double>(e->ws.rope), e->md, q, q_lo,
+                               e->pool_k(l), e->pool_v(l), status, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
-    HIP_TRY(launch_attention(q, R, m, maps, e->md, ap, e->pool_k(l), e->pool_v(l),
+    HIP_TRY(launch_attention(q, q_lo, R, m, maps, e->md, ap, e->pool_k(l), e->pool_v(l),
                              e->wsp<float>(e->ws.attn_ml), e->wsp<float>(e->ws.attn_o), attn,
-                             status, st));
+                             attn_lo, status, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
-    g.X = attn; g.K = qd; g.W = e->packed + e->pl.o[l]; g.N = c.d_model; g.epi = EPI_RESID; g.Y = x;
-    HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
-    HIP_TRY(launch_gemm(g, st));
-    HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
-    HIP_TRY(launch_rmsnorm(x, nullptr, R, e->ffn_norm[l], c.d_model, c.rms_eps, h, st));
-    g.X = h; g.K = c.d_model; g.W = e->packed + e->pl.gate[l]; g.W2 = e->packed + e->pl.up[l];
-    g.N = c.ffn_dim;
-    g.epi = EPI_SWIGLU; g.Y = ffn;
-    HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
-    HIP_TRY(launch_gemm(g, st));
-    HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
-    g.X = ffn; g.K = c.ffn_dim; g.W = e->packed + e->pl.down[l]; g.W2 = nullptr; g.N = c.d_model;
+    g.X = attn; g.Xlo = attn_lo; g.K = qd; g.W = e->packed + e->pl.o[l]; g.N = c.d_model;
     g.epi = EPI_RESID; g.Y = x;
+    HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
+    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
+    HIP_TRY(launch_rmsnorm(x, nullptr, R, e->ffn_norm[l], c.d_model, c.rms_eps, h, h_lo, st));
+    g.X = h; g.Xlo = h_lo; g.K = c.d_model; g.W = e->packed + e->pl.gate[l];
+    g.W2 = e->packed + e->pl.up[l]; g.N = c.ffn_dim;
+    g.epi = EPI_SWIGLU; g.Y = nullptr; g.Yh = ffn; g.Yl = ffn_lo;
+    HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
+    HIP_TRY(launch_gemm(g, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
+    g.X = ffn; g.Xlo = ffn_lo; g.K = c.ffn_dim; g.W = e->packed + e->pl.down[l]; g.W2 = nullptr;
+    g.N = c.d_model; g.epi = EPI_RESID; g.Y = x; g.Yh = g.Yl = nullptr;
     HIP_TRY(e->prof_mark(CBD_KERNEL_DOWN, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_DOWN, st));
   }
   if (s->n_out == 0) return CBD_OK;
   uint16_t* lm_in = e->wsp<uint16_t>(e->ws.lm_in);
-  HIP_TRY(launch_rmsnorm(x, maps.out_row, s->n_out, e->final_norm, c.d_model, c.rms_eps, lm_in, st));
+  uint16_t* lm_in_lo = lm_in + (size_t)c.max_seqs * c.d_model;
+  HIP_TRY(launch_rmsnorm(x, maps.out_row, s->n_out, e->final_norm, c.d_model, c.rms_eps, lm_in,
+                         lm_in_lo, st));
   float* logits = logits_out;
   if (!logits && s->mode == CBD_MODE_SAMPLE) logits = e->wsp<float>(e->ws.logits);
   GemmArgs g{};
-  g.X = lm_in; g.R = s->n_out; g.K = c.d_model; g.W = e->packed + e->pl.lm_head; g.N = c.vocab;
+  g.X = lm_in; g.Xlo = lm_in_lo; g.R = s->n_out; g.K = c.d_model; g.W = e->packed + e->pl.lm_head; g.N = c.vocab;
   g.epi = EPI_LOGITS; g.logits = logits;
   g.amax_val = e->wsp<float>(e->ws.amax_val);
   g.amax_idx = e->wsp<int32_t>(e->ws.amax_idx);
@@ -510,7 +523,7 @@ int cbd_debug_buffer(cbd_engine* e, int32_t which, void** ptr, size_t* bytes) {
     default: return fail(CBD_E_INVAL, "unknown buffer");
   }
   *ptr = e->workspace + off;
-  *bytes = n * 2;
+  *bytes = n * 4;
   return CBD_OK;
 }
 

@@ -1,6 +1,6 @@
 // gemm.hip -- the weight-streaming skinny GEMM of the step, on MFMA.
 //
-//   Y[r][n] = sum_k X[r][k] * W[n][k]      X: [R][K] bf16 (a few rows)
+//   Y[r][n] = sum_k X[r][k] * W[n][k]      X: [R][K] fp32 as bf16 hi + lo
 //                                          W: [N][K] bf16 (read once)
 //
 // Decode is weight-bandwidth bound: every weight byte is used by the R rows of
@@ -19,12 +19,20 @@
 // of 16 scattered 64-byte pieces per instruction. Two register stages of
 // loads are kept in flight while the previous stage feeds the MFMAs.
 //
+// The activations are fp32 values carried as two bf16 planes (hi, lo), so
+// each weight fragment meets two B operands: acc += W.X_hi, acc += W.X_lo.
+// Both products are exact in the fp32 accumulator, and the result is the
+// fp32 dot product of W with X to within 2^-17 relative per term. The
+// second MFMA costs nothing while the weights stream from HBM (a 16 x 32
+// weight tile per 2 x 16 rows of MFMA work leaves the matrix cores idle
+// most of the time at these row counts).
+//
 // A wave owns NT column fragments x RT row fragments. KW waves of a workgroup
 // split K and reduce through LDS in fixed wave order; S workgroups along
 // grid.y split K further and leave fp32 partials that a second kernel sums in
-// fixed split order and passes through the epilogue. Epilogues: bf16 store,
-// residual add (x = bf16(x + bf16(acc))), SwiGLU over a gate/up pair
-// (a = bf16(silu(bf16(g)) * bf16(u))), and fp32 logits with per-tile argmax
+// fixed split order and passes through the epilogue. Epilogues: fp32 store,
+// fp32 residual add (x += acc), SwiGLU over a gate/up pair
+// (a = silu(g) * u, stored split), and fp32 logits with per-tile argmax
 // partials (lowest id on ties).
 #include "common.h"
 #include "kernels.h"
@@ -42,27 +50,23 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 template <int EPI>
 __device__ __forceinline__ void epilogue4(const GemmArgs& a, int r, int n, const float* v0,
                                           const float* v1) {
-  if (EPI == EPI_BF16) {
-    uint2 o = make_uint2(pack_bf2(v0[0], v0[1]), pack_bf2(v0[2], v0[3]));
-    *reinterpret_cast<uint2*>(a.Y + (size_t)r * a.N + n) = o;
+  const size_t at = (size_t)r * a.N + n;
+  if (EPI == EPI_F32) {
+    *reinterpret_cast<float4*>(a.Y + at) = make_float4(v0[0], v0[1], v0[2], v0[3]);
   } else if (EPI == EPI_RESID) {
-    uint2* p = reinterpret_cast<uint2*>(a.Y + (size_t)r * a.N + n);
-    uint2 x = *p;
-    float y0 = lo_bf(x.x) + round_bf(v0[0]);
-    float y1 = hi_bf(x.x) + round_bf(v0[1]);
-    float y2 = lo_bf(x.y) + round_bf(v0[2]);
-    float y3 = hi_bf(x.y) + round_bf(v0[3]);
-    *p = make_uint2(pack_bf2(y0, y1), pack_bf2(y2, y3));
+    float4* p = reinterpret_cast<float4*>(a.Y + at);
+    float4 x = *p;
+    x.x += v0[0];
+    x.y += v0[1];
+    x.z += v0[2];
+    x.w += v0[3];
+    *p = x;
   } else if (EPI == EPI_SWIGLU) {
-    float o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = silu_f(round_bf(v0[i])) * round_bf(v1[i]);
-    *reinterpret_cast<uint2*>(a.Y + (size_t)r * a.N + n) =
-        make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+    store_split4(a.Yh, a.Yl, at, silu_f(v0[0]) * v1[0], silu_f(v0[1]) * v1[1],
+                 silu_f(v0[2]) * v1[2], silu_f(v0[3]) * v1[3]);
   } else {  // EPI_LOGITS
     if (a.logits)
-      *reinterpret_cast<float4*>(a.logits + (size_t)r * a.N + n) =
-          make_float4(v0[0], v0[1], v0[2], v0[3]);
+      *reinterpret_cast<float4*>(a.logits + at) = make_float4(v0[0], v0[1], v0[2], v0[3]);
   }
 }
 
@@ -95,50 +99,29 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
     wp[0][nt] = a.W + off;
     if (NM == 2) wp[NM - 1][nt] = a.W2 + off;
   }
-  const uint16_t* xp[RT];
+  const uint16_t* xp[RT][2];  // hi and lo planes
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = r0 + 16 * rt + lr;
-    xp[rt] = a.X + (size_t)(r < R ? r : 0) * K + kbeg + 8 * lg;
+    const size_t off = (size_t)(r < R ? r : 0) * K + kbeg + 8 * lg;
+    xp[rt][0] = a.X + off;
+    xp[rt][1] = a.Xlo + off;
   }
 
-  // Outputs that are rounded to bf16 accumulate with compensation: each
-  // 64-k (or 128-k) stage is summed by the MFMAs into a fresh accumulator and
-  // then added to the running sum with Kahan's correction, so the result is
-  // within a few fp32 ulps of the exact dot product and rounds to the same
-  // bf16 value as the exact one except right at a rounding boundary. The fp32
-  // logits of the LM head accumulate directly.
-  constexpr bool COMP = EPI != EPI_LOGITS;
-  floatx4_t acc[NM][NT][RT], cmp[NM][NT][RT];
+  floatx4_t acc[NM][NT][RT];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        acc[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        cmp[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      }
-  auto kahan_add = [&](const floatx4_t (&t)[NM][NT][RT]) {
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const floatx4_t y = t[m][nt][rt] - cmp[m][nt][rt];
-          const floatx4_t s2 = acc[m][nt][rt] + y;
-          cmp[m][nt][rt] = (s2 - acc[m][nt][rt]) - y;
-          acc[m][nt][rt] = s2;
-        }
-  };
+      for (int rt = 0; rt < RT; ++rt) acc[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   // One stage = ST super-steps of 64 k; two stages in registers, so the
   // loads of stage i+1 are in flight while stage i feeds the MFMAs.
-  constexpr int ST = (RT <= 2 && !COMP) ? 2 : 1;
+  constexpr int ST = RT * NM <= 1 ? 2 : 1;
   struct Stage {
     uint4 w[ST][NM][NT][2];
-    uint4 x[ST][RT][2];
+    uint4 x[ST][RT][2][2];  // [u][rt][32-k half][hi, lo]
   };
   auto load = [&](Stage& sg, int k) {
 #pragma unroll
@@ -153,36 +136,18 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
             sg.w[u][m][nt][h] = load_stream16(wp[m][nt] + (size_t)(off / 32) * 512);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          sg.x[u][rt][h] = *reinterpret_cast<const uint4*>(xp[rt] + off);
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl)
+            sg.x[u][rt][h][pl] = *reinterpret_cast<const uint4*>(xp[rt][pl] + off);
       }
   };
   auto compute = [&](const Stage& sg) {
-    if (COMP) {
-      floatx4_t t[NM][NT][RT];
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+    for (int u = 0; u < ST; ++u)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) t[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < ST; ++u)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-              for (int rt = 0; rt < RT; ++rt)
-                t[m][nt][rt] = mfma16x16x32(as_bf16x8(sg.w[u][m][nt][h]),
-                                            as_bf16x8(sg.x[u][rt][h]), t[m][nt][rt]);
-      kahan_add(t);
-    } else {
-#pragma unroll
-      for (int u = 0; u < ST; ++u)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
           for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -190,8 +155,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
 #pragma unroll
               for (int rt = 0; rt < RT; ++rt)
                 acc[m][nt][rt] = mfma16x16x32(as_bf16x8(sg.w[u][m][nt][h]),
-                                              as_bf16x8(sg.x[u][rt][h]), acc[m][nt][rt]);
-    }
+                                              as_bf16x8(sg.x[u][rt][h][pl]), acc[m][nt][rt]);
   };
 
   const int span = kend - kbeg;  // this wave's k count (a multiple of 8, or <= 0)
@@ -212,7 +176,7 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
   // Tail: the last < 64*ST k, in 32-k halves predicated per lane group.
   for (int k = nfull * stride; k < span; k += 32) {
     const bool kin = k + 8 * lg < span;
-    uint4 w[NM][NT], x[RT];
+    uint4 w[NM][NT], x[RT][2];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -220,25 +184,19 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
         w[m][nt] = kin ? load_stream16(wp[m][nt] + (size_t)(k / 32) * 512) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
-      x[rt] = kin ? *reinterpret_cast<const uint4*>(xp[rt] + k) : make_uint4(0, 0, 0, 0);
-    floatx4_t t[NM][NT][RT];
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+      for (int pl = 0; pl < 2; ++pl)
+        x[rt][pl] = kin ? *reinterpret_cast<const uint4*>(xp[rt][pl] + k) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+    for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          t[m][nt][rt] = mfma16x16x32(as_bf16x8(w[m][nt]), as_bf16x8(x[rt]),
-                                      floatx4_t{0.f, 0.f, 0.f, 0.f});
-    kahan_add(t);
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            acc[m][nt][rt] = mfma16x16x32(as_bf16x8(w[m][nt]), as_bf16x8(x[rt][pl]), acc[m][nt][rt]);
   }
-  // Fold the compensation into the sum.
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[m][nt][rt] -= cmp[m][nt][rt];
 
   // Reduce the KW waves' partial sums through LDS, in wave order.
   if (KW > 1) {
@@ -391,23 +349,20 @@ struct Shape {
   int RT, NT;
 };
 
-// Tile shape by rows, weight size and epilogue. Up to 16 rows: one row
-// fragment, four column fragments. Beyond that the bf16-output projections
-// (compensated accumulation, so at most 8 accumulator tiles per wave) take
-// two row fragments and stream the weights once per 32-row group -- the
-// repeats of a matrix up to 256 MB are served by the Infinity Cache -- while
-// the LM head (fp32 logits, plain accumulation) keeps up to 64 rows in one
-// wave (4 row fragments).
-static Shape pick_shape(int R, int N, int K, int NM, bool comp) {
-  (void)N;
-  (void)K;
+// Tile shape by rows. Up to 16 rows: one row fragment, four column
+// fragments. Beyond that up to 64 rows share one weight read per wave (four
+// row fragments; two for the dual-matrix SwiGLU, whose accumulators double),
+// and row groups past 64 re-read the weights -- the repeats are served by
+// the Infinity Cache for matrices up to its size.
+static Shape pick_shape(int R, int NM) {
   if (R <= 16) return {1, 4};
-  if (comp) return NM == 2 ? Shape{2, 2} : Shape{2, 4};
+  if (NM == 2) return {2, 4};
   return {4, 4};
 }
 
 int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K) {
-  Shape s = pick_shape(R, N, K, 1, false);
+  (void)K;
+  Shape s = pick_shape(R, 1);
   return (N + 16 * s.NT - 1) / (16 * s.NT);
 }
 
@@ -452,23 +407,16 @@ static hipError_t launch_shape(const GemmArgs& a, hipStream_t st) {
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
-  const Shape s = pick_shape(a.R, a.N, a.K, EpiTraits<EPI>::NM, EPI != EPI_LOGITS);
-  if constexpr (EPI == EPI_LOGITS) {
-    if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
-    return launch_shape<4, 4, EPI>(a, st);
-  } else if constexpr (EpiTraits<EPI>::NM == 2) {
-    if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
-    return launch_shape<2, 2, EPI>(a, st);
-  } else {
-    if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
-    return launch_shape<2, 4, EPI>(a, st);
-  }
+  const Shape s = pick_shape(a.R, EpiTraits<EPI>::NM);
+  if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
+  if constexpr (EpiTraits<EPI>::NM == 2) return launch_shape<2, 4, EPI>(a, st);
+  else return launch_shape<4, 4, EPI>(a, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.R <= 0) return hipSuccess;
   switch (a.epi) {
-    case EPI_BF16: return launch_epi<EPI_BF16>(a, st);
+    case EPI_F32: return launch_epi<EPI_F32>(a, st);
     case EPI_RESID: return launch_epi<EPI_RESID>(a, st);
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, st);
     default: return launch_epi<EPI_LOGITS>(a, st);

@@ -48,32 +48,41 @@ struct AttnPlan {
 hipError_t launch_prep(const StepMeta& m, const RowMaps& maps, const ModelDims& md,
                        const AttnPlan& ap, uint32_t* status, hipStream_t st);
 
-// x[r] = embed[tokens[r]], h[r] = rmsnorm(x[r]) * gain.
+// Activation storage. The residual stream x and the QKV projection are fp32
+// [rows][width]. Activations that feed an MFMA contraction (norm outputs,
+// rotated queries, attention output, SwiGLU product) are "split": two bf16
+// planes hi [rows][width] and lo [rows][width] with hi + lo = the fp32 value
+// (split_bf in common.h).
+
+// x[r] = embed[tokens[r]] (fp32), h[r] = rmsnorm(x[r]) * gain (split).
 hipError_t launch_embed_norm(const int32_t* tokens, const int32_t* row_seq, int32_t R,
                              const uint16_t* embed, const uint16_t* gain, const ModelDims& md,
-                             uint16_t* x, uint16_t* h, uint32_t* status, hipStream_t st);
+                             float* x, uint16_t* h_hi, uint16_t* h_lo, uint32_t* status,
+                             hipStream_t st);
 
-// h[j] = rmsnorm(x[rows ? rows[j] : j]) * gain for j < R (rows[j] < 0: skipped).
-hipError_t launch_rmsnorm(const uint16_t* x, const int32_t* rows, int32_t R, const uint16_t* gain,
-                          int32_t d, float eps, uint16_t* h, hipStream_t st);
+// h[j] = rmsnorm(x[rows ? rows[j] : j]) * gain for j < R (rows[j] < 0: zeros).
+hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int32_t R, const uint16_t* gain,
+                          int32_t d, float eps, uint16_t* h_hi, uint16_t* h_lo, hipStream_t st);
 
-// RoPE on q and k of every row at its position; q to q_out, k and v appended
-// into the layer's K and V regions of the pool through the block tables.
-hipError_t launch_rope_append(const uint16_t* qkv, int32_t R, const StepMeta& m,
-                              const RowMaps& maps, const double* rope_cs, const ModelDims& md,
-                              uint16_t* q_out, uint16_t* pool_k, uint16_t* pool_v,
+// RoPE on q and k of every row at its position; q to q_out (split), k and v
+// rounded to bf16 and appended into the layer's K and V regions of the pool
+// through the block tables.
+hipError_t launch_rope_append(const float* qkv, int32_t R, const StepMeta& m, const RowMaps& maps,
+                              const double* rope_cs, const ModelDims& md, uint16_t* q_hi,
+                              uint16_t* q_lo, uint16_t* pool_k, uint16_t* pool_v,
                               uint32_t* status, hipStream_t st);
 
 // Paged GQA attention for every row (decode rows and prefill chunks), split
-// over keys, then the split combine into out [R][n_heads*head_dim] bf16.
-hipError_t launch_attention(const uint16_t* q, int32_t R, const StepMeta& m, const RowMaps& maps,
-                            const ModelDims& md, const AttnPlan& ap, const uint16_t* pool_k,
-                            const uint16_t* pool_v, float* part_ml, float* part_o, uint16_t* out,
+// over keys, then the split combine into out [R][n_heads*head_dim] (split).
+hipError_t launch_attention(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R,
+                            const StepMeta& m, const RowMaps& maps, const ModelDims& md,
+                            const AttnPlan& ap, const uint16_t* pool_k, const uint16_t* pool_v,
+                            float* part_ml, float* part_o, uint16_t* out_hi, uint16_t* out_lo,
                             uint32_t* status, hipStream_t st);
 
 // --------------------------------------------------------------------- GEMM
 
-enum GemmEpilogue { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum GemmEpilogue { EPI_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
 // Weights reach the GEMM in a packed layout: tiles of 16 rows x 32 k, tile
 // (nb, kb) at element offset (nb * ceil(K/32) + kb) * 512, and inside a tile
@@ -83,18 +92,21 @@ size_t packed_elems(int32_t N, int32_t K);
 hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, hipStream_t st);
 
 struct GemmArgs {
-  const uint16_t* X;  // [R][K] bf16
+  const uint16_t* X;    // [R][K] split activation: hi plane
+  const uint16_t* Xlo;  //                          lo plane
   int32_t R, K;
-  const uint16_t* W;  // [N][K] bf16, packed
-  const uint16_t* W2; // second packed matrix for EPI_SWIGLU (up), [N][K]
+  const uint16_t* W;    // [N][K] bf16, packed
+  const uint16_t* W2;   // second packed matrix for EPI_SWIGLU (up), [N][K]
   int32_t N;
   int32_t epi;
-  uint16_t* Y;        // EPI_BF16 / EPI_SWIGLU out [R][N]; EPI_RESID in/out [R][N]
-  float* logits;      // EPI_LOGITS out [R][N] (nullable: argmax only)
-  float* amax_val;    // EPI_LOGITS per-(row, column tile) maxima [R][amax_stride]
+  float* Y;             // EPI_F32 out [R][N]; EPI_RESID in/out [R][N] (fp32)
+  uint16_t* Yh;         // EPI_SWIGLU out [R][N] split: hi plane
+  uint16_t* Yl;         //                              lo plane
+  float* logits;        // EPI_LOGITS out [R][N] (nullable: argmax only)
+  float* amax_val;      // EPI_LOGITS per-(row, column tile) maxima [R][amax_stride]
   int32_t* amax_idx;
   int32_t amax_stride;
-  float* partials;    // split-K partial sums
+  float* partials;      // split-K partial sums
   size_t partials_cap;  // floats available there
 };
 

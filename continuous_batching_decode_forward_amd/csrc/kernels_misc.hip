@@ -120,12 +120,13 @@ hipError_t launch_prep(const StepMeta& m, const RowMaps& maps, const ModelDims& 
 
 // ---------------------------------------------------------------- RMSNorm
 //
-// One workgroup of 256 threads per row. Each thread holds up to 32 values
-// (d_model <= 8192, d_model % 8 == 0): mean of squares in fp32, then
-// y = bf16(x * (1 / sqrt(ms + eps)) * g).
+// One workgroup of 256 threads per row. Each thread holds up to 32 fp32
+// values (d_model <= 8192, d_model % 4 == 0), in 16-byte chunks t, t + 256,
+// ...: mean of squares in fp32, then y = x * (1 / sqrt(ms + eps)) * g,
+// stored split (hi, lo planes) for the GEMM that consumes it.
 
 #define NORM_THREADS 256
-#define NORM_MAX_CHUNKS 4  // 16-byte chunks per thread: d <= 256 * 8 * 4
+#define NORM_MAX_CHUNKS 8  // float4 chunks per thread: d <= 256 * 4 * 8
 
 __device__ float block_sum_256(float v, float* red) {
   v = wave_sum(v);
@@ -137,23 +138,19 @@ __device__ float block_sum_256(float v, float* red) {
   return s;
 }
 
-__device__ void norm_row(const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, int d,
-                         float eps, uint16_t* __restrict__ h, float* red) {
-  const int nch = d >> 3;
-  uint4 xv[NORM_MAX_CHUNKS];
+__device__ void norm_row(const float* __restrict__ x, const uint16_t* __restrict__ g, int d,
+                         float eps, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
+                         float* red) {
+  const int nch = d >> 2;
+  float4 xv[NORM_MAX_CHUNKS];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < NORM_MAX_CHUNKS; ++c) {
     int ch = threadIdx.x + c * NORM_THREADS;
-    xv[c] = make_uint4(0, 0, 0, 0);
+    xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (ch < nch) {
-      xv[c] = reinterpret_cast<const uint4*>(x)[ch];
-      uint32_t w[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float a = lo_bf(w[k]), b = hi_bf(w[k]);
-        ss += a * a + b * b;
-      }
+      xv[c] = reinterpret_cast<const float4*>(x)[ch];
+      ss += xv[c].x * xv[c].x + xv[c].y * xv[c].y + xv[c].z * xv[c].z + xv[c].w * xv[c].w;
     }
   }
   float tot = block_sum_256(ss, red);
@@ -162,14 +159,10 @@ __device__ void norm_row(const uint16_t* __restrict__ x, const uint16_t* __restr
   for (int c = 0; c < NORM_MAX_CHUNKS; ++c) {
     int ch = threadIdx.x + c * NORM_THREADS;
     if (ch < nch) {
-      uint4 gv = reinterpret_cast<const uint4*>(g)[ch];
-      uint32_t w[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
-      uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-      uint32_t o[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        o[k] = pack_bf2(lo_bf(w[k]) * inv * lo_bf(gw[k]), hi_bf(w[k]) * inv * hi_bf(gw[k]));
-      reinterpret_cast<uint4*>(h)[ch] = make_uint4(o[0], o[1], o[2], o[3]);
+      uint2 gv = reinterpret_cast<const uint2*>(g)[ch];
+      store_split4(h_hi, h_lo, (size_t)ch * 4, xv[c].x * inv * lo_bf(gv.x),
+                   xv[c].y * inv * hi_bf(gv.x), xv[c].z * inv * lo_bf(gv.y),
+                   xv[c].w * inv * hi_bf(gv.y));
     }
   }
 }
@@ -177,51 +170,61 @@ __device__ void norm_row(const uint16_t* __restrict__ x, const uint16_t* __restr
 __global__ __launch_bounds__(NORM_THREADS) void embed_norm_kernel(
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ row_seq,
     const uint16_t* __restrict__ embed, const uint16_t* __restrict__ gain, int d, int vocab,
-    float eps, uint16_t* __restrict__ x, uint16_t* __restrict__ h, uint32_t* status) {
+    float eps, float* __restrict__ x, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
+    uint32_t* status) {
   __shared__ float red[4];
   const int r = blockIdx.x;
-  uint16_t* xr = x + (size_t)r * d;
+  float* xr = x + (size_t)r * d;
   int tok = tokens[r];
   bool ok = row_seq[r] >= 0;
   if (ok && (tok < 0 || tok >= vocab)) {
     if (threadIdx.x == 0) raise_status(status, ST_BAD_TOKEN);
     ok = false;
   }
-  const int nch = d >> 3;
-  for (int ch = threadIdx.x; ch < nch; ch += NORM_THREADS)
-    reinterpret_cast<uint4*>(xr)[ch] =
-        ok ? reinterpret_cast<const uint4*>(embed + (size_t)tok * d)[ch] : make_uint4(0, 0, 0, 0);
-  __syncthreads();
-  norm_row(xr, gain, d, eps, h + (size_t)r * d, red);
+  // Each thread writes exactly the chunks norm_row reads back in this thread.
+  const int nch = d >> 2;
+  for (int ch = threadIdx.x; ch < nch; ch += NORM_THREADS) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ok) {
+      uint2 e = reinterpret_cast<const uint2*>(embed + (size_t)tok * d)[ch];
+      v = make_float4(lo_bf(e.x), hi_bf(e.x), lo_bf(e.y), hi_bf(e.y));
+    }
+    reinterpret_cast<float4*>(xr)[ch] = v;
+  }
+  norm_row(xr, gain, d, eps, h_hi + (size_t)r * d, h_lo + (size_t)r * d, red);
 }
 
 hipError_t launch_embed_norm(const int32_t* tokens, const int32_t* row_seq, int32_t R,
                              const uint16_t* embed, const uint16_t* gain, const ModelDims& md,
-                             uint16_t* x, uint16_t* h, uint32_t* status, hipStream_t st) {
+                             float* x, uint16_t* h_hi, uint16_t* h_lo, uint32_t* status,
+                             hipStream_t st) {
   if (R <= 0) return hipSuccess;
   embed_norm_kernel<<<R, NORM_THREADS, 0, st>>>(tokens, row_seq, embed, gain, md.d_model,
-                                                 md.vocab, md.rms_eps, x, h, status);
+                                                 md.vocab, md.rms_eps, x, h_hi, h_lo, status);
   return hipGetLastError();
 }
 
 __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ rows,
-    const uint16_t* __restrict__ gain, int d, float eps, uint16_t* __restrict__ h) {
+    const float* __restrict__ x, const int32_t* __restrict__ rows,
+    const uint16_t* __restrict__ gain, int d, float eps, uint16_t* __restrict__ h_hi,
+    uint16_t* __restrict__ h_lo) {
   __shared__ float red[4];
   const int j = blockIdx.x;
   int src = rows ? rows[j] : j;
   if (src < 0) {  // refused row: zeros, so later stages see finite values
-    for (int ch = threadIdx.x; ch < (d >> 3); ch += NORM_THREADS)
-      reinterpret_cast<uint4*>(h + (size_t)j * d)[ch] = make_uint4(0, 0, 0, 0);
+    for (int ch = threadIdx.x; ch < (d >> 2); ch += NORM_THREADS) {
+      reinterpret_cast<uint2*>(h_hi + (size_t)j * d)[ch] = make_uint2(0, 0);
+      reinterpret_cast<uint2*>(h_lo + (size_t)j * d)[ch] = make_uint2(0, 0);
+    }
     return;
   }
-  norm_row(x + (size_t)src * d, gain, d, eps, h + (size_t)j * d, red);
+  norm_row(x + (size_t)src * d, gain, d, eps, h_hi + (size_t)j * d, h_lo + (size_t)j * d, red);
 }
 
-hipError_t launch_rmsnorm(const uint16_t* x, const int32_t* rows, int32_t R, const uint16_t* gain,
-                          int32_t d, float eps, uint16_t* h, hipStream_t st) {
+hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int32_t R, const uint16_t* gain,
+                          int32_t d, float eps, uint16_t* h_hi, uint16_t* h_lo, hipStream_t st) {
   if (R <= 0) return hipSuccess;
-  rmsnorm_kernel<<<R, NORM_THREADS, 0, st>>>(x, rows, gain, d, eps, h);
+  rmsnorm_kernel<<<R, NORM_THREADS, 0, st>>>(x, rows, gain, d, eps, h_hi, h_lo);
   return hipGetLastError();
 }
 
@@ -229,21 +232,20 @@ hipError_t launch_rmsnorm(const uint16_t* x, const int32_t* rows, int32_t R, con
 //
 // Block (hd/2, 4): x = pair index i (element i pairs with i + hd/2), y = one
 // of four head slots. Head slots 0..Hq-1 are query heads (rotated into
-// q_out), then Hkv key heads (rotated, written into the K tile
-// [block][kvh][pos % bs][hd]) and Hkv value heads (written, dimension-major,
-// into the V tile [block][kvh][hd][pos % bs]). The rotation reads a host-built
-// fp64 table of (cos, sin) per (position, i) and is evaluated in fp64: the
-// rotation a*cos - b*sin can cancel, and a query that rounds differently moves
-// every score of its head.
+// q_out, split), then Hkv key heads (rotated, rounded to bf16 into the K
+// tile [block][kvh][pos % bs][hd]) and Hkv value heads (rounded to bf16,
+// dimension-major, into the V tile [block][kvh][hd][pos % bs]). The rotation
+// reads a host-built fp64 table of (cos, sin) per (position, i) and is
+// evaluated in fp64, so a cached key is its exact rotation rounded once.
 
-__global__ void rope_append_kernel(const uint16_t* __restrict__ qkv, int R,
+__global__ void rope_append_kernel(const float* __restrict__ qkv, int R,
                                    const int32_t* __restrict__ row_seq,
                                    const int32_t* __restrict__ row_pos,
                                    const int32_t* __restrict__ tables, int max_blocks_per_seq,
                                    const double2* __restrict__ rope_cs, int hq, int hkv, int hd,
-                                   int bs, int num_blocks, uint16_t* __restrict__ q_out,
-                                   uint16_t* __restrict__ pool_k, uint16_t* __restrict__ pool_v,
-                                   uint32_t* status) {
+                                   int bs, int num_blocks, uint16_t* __restrict__ q_hi,
+                                   uint16_t* __restrict__ q_lo, uint16_t* __restrict__ pool_k,
+                                   uint16_t* __restrict__ pool_v, uint32_t* status) {
   const int slots = hq + 2 * hkv;
   const int groups = (slots + 3) / 4;
   const int r = blockIdx.x / groups;
@@ -254,20 +256,25 @@ __global__ void rope_append_kernel(const uint16_t* __restrict__ qkv, int R,
   const int s = row_seq[r];
   if (s < 0) return;
   const int pos = row_pos[r];
-  const uint16_t* src = qkv + (size_t)r * slots * hd + (size_t)j * hd;
-  float a = bf2f(src[i]), b = bf2f(src[i + half]);
+  const float* src = qkv + (size_t)r * slots * hd + (size_t)j * hd;
+  float a = src[i], b = src[i + half];
   if (j < hq + hkv) {
     const double2 cs = rope_cs[(size_t)pos * half + i];
     const double da = a, db = b;
-    // fp64 -> fp32 -> bf16: the double rounding can only matter within
-    // 2^-29 of a bf16 halfway point.
+    // fp64 -> fp32 -> bf16 for keys: the double rounding can only matter
+    // within 2^-29 of a bf16 halfway point.
     a = (float)(da * cs.x - db * cs.y);
     b = (float)(db * cs.x + da * cs.y);
   }
   if (j < hq) {
-    uint16_t* dst = q_out + (size_t)r * hq * hd + (size_t)j * hd;
-    dst[i] = f2bf(a);
-    dst[i + half] = f2bf(b);
+    const size_t at = (size_t)r * hq * hd + (size_t)j * hd;
+    bf16_t h, l;
+    split_bf(a, h, l);
+    q_hi[at + i] = h;
+    q_lo[at + i] = l;
+    split_bf(b, h, l);
+    q_hi[at + i + half] = h;
+    q_lo[at + i + half] = l;
     return;
   }
   const int blk = tables[(size_t)s * max_blocks_per_seq + pos / bs];
@@ -289,9 +296,9 @@ __global__ void rope_append_kernel(const uint16_t* __restrict__ qkv, int R,
   }
 }
 
-hipError_t launch_rope_append(const uint16_t* qkv, int32_t R, const StepMeta& m,
-                              const RowMaps& maps, const double* rope_cs, const ModelDims& md,
-                              uint16_t* q_out, uint16_t* pool_k, uint16_t* pool_v,
+hipError_t launch_rope_append(const float* qkv, int32_t R, const StepMeta& m, const RowMaps& maps,
+                              const double* rope_cs, const ModelDims& md, uint16_t* q_hi,
+                              uint16_t* q_lo, uint16_t* pool_k, uint16_t* pool_v,
                               uint32_t* status, hipStream_t st) {
   if (R <= 0) return hipSuccess;
   const int slots = md.n_heads + 2 * md.n_kv_heads;
@@ -300,7 +307,7 @@ hipError_t launch_rope_append(const uint16_t* qkv, int32_t R, const StepMeta& m,
   rope_append_kernel<<<R * groups, block, 0, st>>>(
       qkv, R, maps.row_seq, maps.row_pos, m.block_tables, m.max_blocks_per_seq,
       reinterpret_cast<const double2*>(rope_cs), md.n_heads, md.n_kv_heads, md.head_dim,
-      md.block_size, md.num_blocks, q_out, pool_k, pool_v, status);
+      md.block_size, md.num_blocks, q_hi, q_lo, pool_k, pool_v, status);
   return hipGetLastError();
 }
 

@@ -135,15 +135,24 @@ class Engine:
         return self.slot_state[params_bytes:params_bytes + s.max_slots * s.vocab * 4].view(
             torch.float32).view(s.max_slots, s.vocab)
 
-    def debug_buffer(self, which: int, rows: int, width: int) -> torch.Tensor:
-        """A copy of the first `rows` rows of an internal bf16 activation buffer."""
+    # Buffers that hold fp32 values as two bf16 planes (hi, then lo).
+    _SPLIT = (B.CBD_BUF_H, B.CBD_BUF_Q, B.CBD_BUF_ATTN, B.CBD_BUF_FFN, B.CBD_BUF_LM_IN)
+
+    def debug_buffer(self, which: int, rows: int, width: int) -> np.ndarray:
+        """The first `rows` rows of an internal activation buffer as float64
+        values (a split buffer's value is hi + lo, summed exactly)."""
         ptr, nbytes = B.cbd_debug_buffer(self.handle, which)
-        base = self.workspace.data_ptr()
-        off = ptr - base
-        assert 0 <= off and off + rows * width * 2 <= self.workspace.numel() and \
-            rows * width * 2 <= nbytes
-        return self.workspace[off:off + rows * width * 2].view(torch.bfloat16).view(
-            rows, width).clone()
+        off = ptr - self.workspace.data_ptr()
+        assert 0 <= off and off + nbytes <= self.workspace.numel() and rows * width * 4 <= nbytes
+        buf = self.workspace[off:off + nbytes]
+        if which not in self._SPLIT:
+            return buf[:rows * width * 4].view(torch.float32).view(rows, width).cpu().numpy() \
+                .astype(np.float64)
+        plane = nbytes // 2
+        def part(o):
+            u = buf[o:o + rows * width * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+            return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return (part(0) + part(plane)).reshape(rows, width)
 
     def close(self):
         if getattr(self, "handle", None):

@@ -31,6 +31,12 @@
  *    caller of the batched forward). Calls on one engine from several
  *    threads at once are not supported.
  *  - bf16 is the 16-bit brain float, stored as uint16_t bit patterns.
+ *  - Precision: the bytes the step streams -- weights and the KV cache --
+ *    are bf16 (a cached K or V value is rounded to bf16 once, when it is
+ *    appended). Activations between the step's kernels are fp32; the
+ *    matrix-core contractions take them as two bf16 terms (hi + lo) and
+ *    accumulate in fp32. Logits are fp32; the greedy id is the lowest id of
+ *    their maximum.
  */
 #ifndef CBD_H
 #define CBD_H
@@ -222,14 +228,19 @@ const char* cbd_last_error(void);
 
 /* Activation buffers inside the workspace, as the last step left them (for
  * multi-layer models: the last layer's). Row i is the i-th row of the step
- * (for CBD_BUF_LM_IN: the i-th emitting sequence). bf16 unless noted. */
-#define CBD_BUF_X 1      /* residual stream after the step [max_rows][d_model] */
-#define CBD_BUF_H 2      /* last RMSNorm output, the FFN input [max_rows][d_model] */
-#define CBD_BUF_QKV 3    /* QKV projection [max_rows][(n_heads+2*n_kv_heads)*head_dim] */
-#define CBD_BUF_Q 4      /* rotated queries [max_rows][n_heads*head_dim] */
-#define CBD_BUF_ATTN 5   /* attention output [max_rows][n_heads*head_dim] */
-#define CBD_BUF_FFN 6    /* SwiGLU output [max_rows][ffn_dim] */
-#define CBD_BUF_LM_IN 7  /* final-norm rows fed to the LM head [max_seqs][d_model] */
+ * (for CBD_BUF_LM_IN: the i-th emitting sequence). Activations are fp32
+ * values. "fp32" buffers hold float [rows][w]. "split" buffers hold the
+ * value as two bf16 terms: a hi plane [rows][w] followed by a lo plane
+ * [rows][w], value = hi + lo (hi = bf16(v), lo = bf16(v - hi)); the
+ * contractions consume them that way. rows = max_rows (max_seqs for
+ * CBD_BUF_LM_IN). */
+#define CBD_BUF_X 1      /* fp32: residual stream after the step [rows][d_model] */
+#define CBD_BUF_H 2      /* split: last RMSNorm output, the FFN input [rows][d_model] */
+#define CBD_BUF_QKV 3    /* fp32: QKV projection [rows][(n_heads+2*n_kv_heads)*head_dim] */
+#define CBD_BUF_Q 4      /* split: rotated queries [rows][n_heads*head_dim] */
+#define CBD_BUF_ATTN 5   /* split: attention output [rows][n_heads*head_dim] */
+#define CBD_BUF_FFN 6    /* split: SwiGLU output [rows][ffn_dim] */
+#define CBD_BUF_LM_IN 7  /* split: final-norm rows fed to the LM head [rows][d_model] */
 /* Device address and size in bytes of one of them (no copy, no sync). */
 int cbd_debug_buffer(cbd_engine* e, int32_t which, void** ptr, size_t* bytes);
 

@@ -1,10 +1,23 @@
 """Stage-by-stage GPU parity on one 8B-shaped layer: every activation the
-step stores (QKV projection, rotated queries, attention output, FFN input,
+step keeps (QKV projection, rotated queries, attention output, FFN input,
 SwiGLU output, residual stream, final-norm rows) against the oracle's pieces
-applied to the oracle's own previous stage, as the largest difference over
-the vector's rms (one bf16 ulp at that scale is ~2^-8). Where both sides
-round nearly the same real number to bf16 they may differ by one ulp when it
-sits near a rounding boundary; anything larger, or widespread, is a defect."""
+applied to the oracle's own previous stage.
+
+Activations are fp32 on the device and reach the matrix cores as bf16
+hi + lo pairs (16 significant bits), so a stage carries a relative error of
+order 1e-5. The error measure is max_i |gpu_i - ref_i| / (|ref_i| + rms(ref))
+(relative for large elements, relative to the vector's scale for small
+ones), and the bar, 2^-12, is 16 times tighter than one bf16 ulp (2^-8): a
+stage that rounded through bf16 anywhere fails it.
+
+The one bf16 storage point inside a layer is the KV-cache append: the new
+position's K (after RoPE) and V are rounded to bf16 from the device's fp32
+value on one side and from the exact value on the other, and where that
+value lies within ~1e-5 of a rounding boundary the two caches differ by one
+ulp in that element. Its effect on the attention output is bounded per head
+from the oracle's values (the bound below); with the K/V projection rows
+set to zero the appended K and V are exactly zero on both sides and every
+stage meets the fp32 bar."""
 import numpy as np
 import pytest
 import torch
@@ -20,18 +33,47 @@ pytestmark = pytest.mark.gpu
 SHAPE = configs.LLAMA8B_1L
 
 
-def stage_error(gpu_bf16: torch.Tensor, ref_u16: np.ndarray):
-    """(max |gpu - oracle| / rms(oracle), fraction of elements that differ).
-    One bf16 ulp at the vector's own scale is about 2^-8 = 0.0039."""
-    g = O.bf16_to_f64(gpu_bf16).reshape(-1)
-    o = O.bf16_to_f64(ref_u16).reshape(-1)
+def stage_error(gpu: np.ndarray, ref: np.ndarray, slack=None) -> float:
+    """max_i (|gpu_i - ref_i| - slack_i) / (|ref_i| + rms(ref))."""
+    g = np.asarray(gpu, np.float64).reshape(-1)
+    o = np.asarray(ref, np.float64).reshape(-1)
     rms = float(np.sqrt(np.mean(o * o))) or 1.0
     d = np.abs(g - o)
-    return float(d.max() / rms), float((d > 0).mean())
+    if slack is not None:
+        d = np.maximum(d - slack.reshape(-1), 0.0)
+    return float((d / (np.abs(o) + rms)).max())
 
 
-def to_u16(x):
-    return np.array([O.f64_to_bf16(v) for v in x], np.uint16)
+STAGE_TOL = 2.0 ** -12
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def append_flip_bound(q, K, V, k_new, v_new, hq, hkv, hd):
+    """Per output element, the first-order change of the attention output
+    when the appended key and value move by up to one bf16 ulp per element:
+    p_new * (|ds| * |v_new - o| + ulp(v_new)), ds = sum_i |q_i| ulp(k_i) /
+    sqrt(hd), p_new the new position's softmax weight (times 1.5 for the
+    second-order terms)."""
+    qf = np.asarray(q, np.float64).reshape(hq, hd)
+    Kf = O.bf16_to_f64(K).reshape(-1, hkv, hd)
+    Vf = O.bf16_to_f64(V).reshape(-1, hkv, hd)
+    kn = np.asarray(k_new, np.float64).reshape(hkv, hd)
+    vn = np.asarray(v_new, np.float64).reshape(hkv, hd)
+    out = np.empty((hq, hd))
+    for h in range(hq):
+        g = h // (hq // hkv)
+        s = Kf[:, g, :] @ qf[h] / np.sqrt(hd)
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        o = p @ Vf[:, g, :]
+        ds = np.sum(np.abs(qf[h]) * bf16_ulp(kn[g])) / np.sqrt(hd)
+        out[h] = 1.5 * p[-1] * (ds * np.abs(Vf[-1, g, :] - o) + bf16_ulp(vn[g]))
+    return out.reshape(-1)
 
 
 @pytest.fixture(scope="module")
@@ -41,9 +83,9 @@ def big():
     return wg, wc
 
 
-def test_every_stage_of_an_8b_layer_within_bf16_rounding(big):
-    wg, wc = big
-    Bn, bs, seed = 4, 32, 11
+def run_layer(wg, wc, seed=11, Bn=4, bs=32):
+    """One decode step of the 1-layer model over Bn sequences with synthetic
+    cached contexts; returns the device's stages and the oracle's."""
     ctx = synth.uniform_ints(seed, "ctx", Bn, 512, 4096)
     need = [-(-(int(c) + 1) // bs) for c in ctx]
     perm = synth.permutation(seed, "blocks", sum(need))
@@ -71,58 +113,56 @@ def test_every_stage_of_an_8b_layer_within_bf16_rounding(big):
         ("attn", B.CBD_BUF_ATTN, hq * hd), ("h2", B.CBD_BUF_H, d), ("a", B.CBD_BUF_FFN, F),
         ("x2", B.CBD_BUF_X, d), ("hf", B.CBD_BUF_LM_IN, d)]}
     eng.close()
-    # a second engine whose down projection is zero leaves x1 (the residual
-    # after attention) in the residual buffer
-    wz = dict(wg)
-    wz["w_down"] = [torch.zeros_like(t) for t in wg["w_down"]]
-    eng = make_engine(SHAPE, wz, block_size=bs, num_blocks=len(perm), max_blocks_per_seq=mbps,
-                      max_rows=16, max_seqs=16, max_position=4097)
-    fill_pool(eng, seed, perm)
-    meta = eng.upload_step(slots=list(range(Bn)), block_tables=tables, ctx_lens=ctx,
-                           n_new=[1] * Bn, tokens=tokens, want_token=[1] * Bn)
-    eng.step_forward(meta, None, tk)
-    torch.cuda.synchronize()
-    gpu["x1"] = eng.debug_buffer(B.CBD_BUF_X, Bn, d)
-    eng.close()
-    stats = {k: [] for k in gpu}
+    refs = []
     for i in range(Bn):
-        x0 = O.as_u16(wc["embed"][int(tokens[i])])
+        r = {}
+        x0 = O.bf16_to_f64(wc["embed"][int(tokens[i])])
         h = O.rmsnorm(x0, wc["attn_norm"][0], SHAPE.rms_eps)
-        qkv = to_u16(O.linear(h, wc["w_qkv"][0]))
-        stats["qkv"].append(stage_error(gpu["qkv"][i], qkv))
+        r["qkv"] = qkv = O.linear(h, wc["w_qkv"][0])
         pos = int(ctx[i])
-        q = np.concatenate([O.rope(qkv[j * hd:(j + 1) * hd], pos, SHAPE.rope_base)
-                            for j in range(hq)])
-        stats["q"].append(stage_error(gpu["q"][i], q))
+        r["q"] = q = np.concatenate([O.rope(qkv[j * hd:(j + 1) * hd], pos, SHAPE.rope_base)
+                                     for j in range(hq)])
         k_new = np.concatenate([O.rope(qkv[(hq + j) * hd:(hq + j + 1) * hd], pos, SHAPE.rope_base)
-                                for j in range(hkv)]).reshape(1, hkv, hd)
-        v_new = qkv[(hq + hkv) * hd:].reshape(1, hkv, hd)
+                                for j in range(hkv)])
+        v_new = qkv[(hq + hkv) * hd:]
         Kc = O.as_u16(synth.logical_kv(seed, 0, 0, tables[i], pos, hkv, bs, hd))
         Vc = O.as_u16(synth.logical_kv(seed, 0, 1, tables[i], pos, hkv, bs, hd))
-        K = np.concatenate([Kc, k_new])
-        V = np.concatenate([Vc, v_new])
-        attn = O.attention_dense(q, K, V, hq, hkv, hd)
-        stats["attn"].append(stage_error(gpu["attn"][i], attn))
-        t = to_u16(O.linear(attn, wc["w_o"][0]))
-        x1 = to_u16(O.bf16_to_f64(x0) + O.bf16_to_f64(t))
-        stats["x1"].append(stage_error(gpu["x1"][i], x1))
-        dx = np.nonzero(O.as_u16(gpu["x1"][i]) != x1)[0]
-        if len(dx):
-            print(f"row {i}: x1 differs at {len(dx)} columns, by 64-column tile:",
-                  np.bincount(dx // 64, minlength=d // 64).nonzero()[0][:20])
-        h2 = O.rmsnorm(x1, wc["ffn_norm"][0], SHAPE.rms_eps)
-        stats["h2"].append(stage_error(gpu["h2"][i], h2))
-        g = O.bf16_to_f64(to_u16(O.linear(h2, wc["w_gate"][0])))
-        u = O.bf16_to_f64(to_u16(O.linear(h2, wc["w_up"][0])))
-        a = to_u16(g / (1.0 + np.exp(-g)) * u)
-        stats["a"].append(stage_error(gpu["a"][i], a))
-        dn = to_u16(O.linear(a, wc["w_down"][0]))
-        x2 = to_u16(O.bf16_to_f64(x1) + O.bf16_to_f64(dn))
-        stats["x2"].append(stage_error(gpu["x2"][i], x2))
-        hf = O.rmsnorm(x2, wc["final_norm"], SHAPE.rms_eps)
-        stats["hf"].append(stage_error(gpu["hf"][i], hf))
-    report = {k: (max(e for e, _ in v), max(f for _, f in v)) for k, v in stats.items()}
-    print("stage: (max error / rms, fraction of elements differing)", report)
-    for k, (err, frac) in report.items():
-        assert err <= 2.0 ** -6, f"{k}: max error {err:.3g} of the rms"
-        assert frac < 0.02, f"{k}: {frac:.3%} of elements differ"
+        K = np.concatenate([Kc, O.bf16_round(k_new).reshape(1, hkv, hd)])
+        V = np.concatenate([Vc, O.bf16_round(v_new).reshape(1, hkv, hd)])
+        r["attn"] = attn = O.attention_dense(q, K, V, hq, hkv, hd)
+        r["attn_bound"] = append_flip_bound(q, K, V, k_new, v_new, hq, hkv, hd)
+        x1 = x0 + O.linear(attn, wc["w_o"][0])
+        r["h2"] = h2 = O.rmsnorm(x1, wc["ffn_norm"][0], SHAPE.rms_eps)
+        g = O.linear(h2, wc["w_gate"][0])
+        u = O.linear(h2, wc["w_up"][0])
+        r["a"] = a = g / (1.0 + np.exp(-g)) * u
+        r["x2"] = x2 = x1 + O.linear(a, wc["w_down"][0])
+        r["hf"] = O.rmsnorm(x2, wc["final_norm"], SHAPE.rms_eps)
+        refs.append(r)
+    return gpu, refs
+
+
+def test_stages_up_to_attention_within_fp32_error_and_the_append_bound(big):
+    wg, wc = big
+    gpu, refs = run_layer(wg, wc)
+    report = {}
+    for k in ("qkv", "q", "attn"):
+        report[k] = max(stage_error(gpu[k][i], r[k], r["attn_bound"] if k == "attn" else None)
+                        for i, r in enumerate(refs))
+    print("stage: error measure", {k: f"{v:.2e}" for k, v in report.items()})
+    for k, err in report.items():
+        assert err <= STAGE_TOL, f"{k}: error {err:.3g}"
+
+
+def test_every_stage_within_fp32_error_when_the_append_is_exact(big):
+    wg, wc = big
+    hq, hkv, hd = SHAPE.n_heads, SHAPE.n_kv_heads, SHAPE.head_dim
+    wq = wg["w_qkv"][0].clone()
+    wq[hq * hd:] = 0   # k_new = v_new = 0 exactly: the appended position has score 0, value 0
+    wg2 = dict(wg, w_qkv=[wq])
+    wc2 = dict(wc, w_qkv=[wq.cpu()])
+    gpu, refs = run_layer(wg2, wc2, seed=12)
+    report = {k: max(stage_error(gpu[k][i], r[k]) for i, r in enumerate(refs)) for k in gpu}
+    print("stage: error measure", {k: f"{v:.2e}" for k, v in report.items()})
+    for k, err in report.items():
+        assert err <= STAGE_TOL, f"{k}: error {err:.3g}"
