@@ -70,6 +70,78 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int r, int n, const
   }
 }
 
+// Write a wave's accumulators: lane l holds columns n0 + 16 nt + 4 lg + (0..3)
+// of row r0 + 16 rt + lr. With a K split (S > 1) they go to the partials of
+// split ks; otherwise through the epilogue, and the logits epilogue also
+// leaves this wave's per-row maximum (lowest column on ties) in argmax
+// partial `tile`.
+template <int RT, int NT, int EPI>
+__device__ __forceinline__ void store_tile(const GemmArgs& a,
+                                           const floatx4_t (&acc)[EpiTraits<EPI>::NM][NT][RT],
+                                           int r0, int n0, int ks, int S, int tile) {
+  constexpr int NM = EpiTraits<EPI>::NM;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int R = a.R, N = a.N;
+  if (S > 1) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          int r = r0 + 16 * rt + lr, n = n0 + 16 * nt + 4 * lg;
+          if (r < R && n < N)
+            *reinterpret_cast<float4*>(a.partials + (((size_t)ks * NM + m) * R + r) * N + n) =
+                make_float4(acc[m][nt][rt][0], acc[m][nt][rt][1], acc[m][nt][rt][2],
+                            acc[m][nt][rt][3]);
+        }
+    return;
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = r0 + 16 * rt + lr;
+    float best = -INFINITY;
+    int bidx = 0x7fffffff;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + 16 * nt + 4 * lg;
+      float v0[4], v1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v0[i] = acc[0][nt][rt][i];
+        v1[i] = acc[NM - 1][nt][rt][i];
+      }
+      if (r < R && n < N) {
+        epilogue4<EPI>(a, r, n, v0, v1);
+        if (EPI == EPI_LOGITS) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (v0[i] > best) {  // ascending columns: first maximum wins
+              best = v0[i];
+              bidx = n + i;
+            }
+        }
+      }
+    }
+    if (EPI == EPI_LOGITS) {
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) {
+        float v = __shfl_xor(best, o, 64);
+        int i = __shfl_xor(bidx, o, 64);
+        if (v > best || (v == best && i < bidx)) {
+          best = v;
+          bidx = i;
+        }
+      }
+      if (lg == 0 && r < R) {
+        a.amax_val[(size_t)r * a.amax_stride + tile] = best;
+        a.amax_idx[(size_t)r * a.amax_stride + tile] = bidx;
+      }
+    }
+  }
+}
+
 template <int RT, int NT, int KW, int EPI>
 __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S) {
   constexpr int NM = EpiTraits<EPI>::NM;
@@ -230,65 +302,150 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
     }
   }
 
-  // Lane l holds columns n0 + 16 nt + 4 lg + (0..3) of row r0 + 16 rt + lr.
-  if (S > 1) {
+  store_tile<RT, NT, EPI>(a, acc, r0, n0, ks, S, blockIdx.x);
+}
+
+// ------------------------------------------------------- the wide-row path
+//
+// For 17..64 rows per weight read. A workgroup is NW = 4 waves side by side
+// along N (each NT column fragments) over the same K range and all RT row
+// fragments, so the activation tile of a 64-k stage (RT x 16 rows x 64 k, hi
+// and lo: RT x 4 KB) is fetched once per workgroup into LDS instead of once
+// per wave. The LDS tile is kept in MFMA operand order -- block
+// (rt, plane, 32-k half) is 64 lanes x 16 bytes -- so each wave reads its B
+// operands with one conflict-free 16-byte LDS read per lane.
+//
+// Each wave streams its weights through a ring of D register stages (64 k
+// each), issuing stage c + D - 1 before it computes stage c, so D - 1 stages
+// of weight reads are in flight per wave. The activation copy for a stage is
+// issued with that stage's weights (the vector-memory counter retires loads
+// in order, so a later-issued activation load would hold back the wait for
+// the weights behind it). Per stage: copy the arrived activation rows into
+// LDS buffer c % 2, barrier, then the MFMAs of stage c.
+#define WIDE_NW 4
+
+template <int RT, int NT, int D, int EPI>
+__global__ __launch_bounds__(64 * WIDE_NW) void gemm_wide_kernel(GemmArgs a, int kc, int S) {
+  constexpr int NM = EpiTraits<EPI>::NM;
+  constexpr int BLK = RT * 4;  // LDS blocks per stage: (rt, plane, half)
+  __shared__ uint4 xs[2][BLK * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int tile = blockIdx.x * WIDE_NW + wave;  // this wave's column tile
+  const int n0 = tile * (16 * NT);
+  const int ks = blockIdx.y;
+  const int r0 = blockIdx.z * (16 * RT);
+  const int K = a.K, N = a.N, R = a.R;
+  const int kbeg = ks * kc;                 // a multiple of 64
+  const int kend = min(K, kbeg + kc);
+  const int nst = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
+
+  const int KT = (K + 31) / 32;
+  const uint16_t* wp[NM][NT];
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+  for (int nt = 0; nt < NT; ++nt) {
+    int nb = (n0 >> 4) + nt;
+    if (nb * 16 >= N) nb = 0;  // past N: read block 0, never stored
+    const size_t off = ((size_t)nb * KT + kbeg / 32) * 512 + lane * 8;
+    wp[0][nt] = a.W + off;
+    if (NM == 2) wp[NM - 1][nt] = a.W2 + off;
+  }
+  // This thread's share of the activation copy: block b = wave + 4 i of
+  // every stage, lane `lane` of it. Rows past R read row 0 and are zeroed
+  // when written to LDS.
+  const uint16_t* xsrc[RT];
+  bool xrow[RT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          int r = r0 + 16 * rt + lr, n = n0 + 16 * nt + 4 * lg;
-          if (r < R && n < N)
-            *reinterpret_cast<float4*>(a.partials + (((size_t)ks * NM + m) * R + r) * N + n) =
-                make_float4(acc[m][nt][rt][0], acc[m][nt][rt][1], acc[m][nt][rt][2],
-                            acc[m][nt][rt][3]);
-        }
-    return;
+  for (int i = 0; i < RT; ++i) {
+    const int b = wave + WIDE_NW * i;
+    const int rt = b >> 2, pl = (b >> 1) & 1;
+    const int r = r0 + 16 * rt + lr;
+    xrow[i] = r < R;
+    xsrc[i] = (pl ? a.Xlo : a.X) + (size_t)(xrow[i] ? r : 0) * K;
   }
 
+  floatx4_t acc[NM][NT][RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = r0 + 16 * rt + lr;
-    float best = -INFINITY;
-    int bidx = 0x7fffffff;
+  for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = n0 + 16 * nt + 4 * lg;
-      float v0[4], v1[4];
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v0[i] = acc[0][nt][rt][i];
-        v1[i] = acc[NM - 1][nt][rt][i];
-      }
-      if (r < R && n < N) {
-        epilogue4<EPI>(a, r, n, v0, v1);
-        if (EPI == EPI_LOGITS) {
+      for (int rt = 0; rt < RT; ++rt) acc[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  // The loads carry no conditions (a condition would become a branch, and
+  // the counter waits at its join drain every outstanding load): weight
+  // tiles are clamped into the matrix and activation pieces into the row,
+  // and pieces at or beyond kend are zeroed when the activations are
+  // written to LDS -- weights there then meet zeros.
+  uint4 w[D][NM][NT][2];
+  uint4 xc[D][RT];
+  auto load = [&](int j, int c) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (v0[i] > best) {  // ascending columns: first maximum wins
-              best = v0[i];
-              bidx = n + i;
-            }
-        }
+    for (int h = 0; h < 2; ++h) {
+      const int t = min(kbeg / 32 + 2 * c + h, KT - 1) - kbeg / 32;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          w[j][m][nt][h] = load_stream16(wp[m][nt] + (size_t)t * 512);
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int b = wave + WIDE_NW * i;
+      const int k = min(kbeg + 64 * c + 32 * (b & 1) + 8 * lg, K - 8);
+      xc[j][i] = *reinterpret_cast<const uint4*>(xsrc[i] + k);
+    }
+  };
+  auto stage = [&](int j, int c) {
+    uint4* buf = xs[c & 1];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int b = wave + WIDE_NW * i;
+      const bool ok = xrow[i] && kbeg + 64 * c + 32 * (b & 1) + 8 * lg < kend;
+      buf[b * 64 + lane] = ok ? xc[j][i] : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 xf[RT][2];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) xf[rt][pl] = buf[((rt * 2 + pl) * 2 + h) * 64 + lane];
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              acc[m][nt][rt] = mfma16x16x32(as_bf16x8(w[j][m][nt][h]), as_bf16x8(xf[rt][pl]),
+                                            acc[m][nt][rt]);
+    }
+  };
+
+  if (nst > 0) {
+    // Stage s lives in ring slot s % D; the loads of stage c + D - 1 are
+    // issued before stage c is computed (clamped to the last stage near the
+    // end: those repeats are cache hits and never computed).
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) load(j, min(j, nst - 1));
+    const int groups = nst / D;
+    for (int g = 0; g < groups; ++g) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int c = g * D + j;
+        load((j + D - 1) % D, min(c + D - 1, nst - 1));
+        stage(j, c);
       }
     }
-    if (EPI == EPI_LOGITS) {
+    const int rest = nst - groups * D;  // < D, already loaded in slots 0..rest-1
 #pragma unroll
-      for (int o = 16; o < 64; o <<= 1) {
-        float v = __shfl_xor(best, o, 64);
-        int i = __shfl_xor(bidx, o, 64);
-        if (v > best || (v == best && i < bidx)) {
-          best = v;
-          bidx = i;
-        }
-      }
-      if (lg == 0 && r < R) {
-        a.amax_val[(size_t)r * a.amax_stride + blockIdx.x] = best;
-        a.amax_idx[(size_t)r * a.amax_stride + blockIdx.x] = bidx;
-      }
-    }
+    for (int j = 0; j < D - 1; ++j)
+      if (j < rest) stage(j, groups * D + j);
   }
+  store_tile<RT, NT, EPI>(a, acc, r0, n0, ks, S, tile);
 }
 
 // Sum the S split partials in split order, then the epilogue (no argmax:
@@ -349,21 +506,31 @@ struct Shape {
   int RT, NT;
 };
 
-// Tile shape by rows. Up to 16 rows: one row fragment, four column
-// fragments. Beyond that up to 64 rows share one weight read per wave (four
-// row fragments; two for the dual-matrix SwiGLU, whose accumulators double),
+// Up to 16 rows: the per-wave kernel with one row fragment and four column
+// fragments (the waves of a workgroup split K). Beyond 16 rows: the wide-row
+// kernel, 64 rows (four row fragments; two up to 32 rows) per weight read,
 // and row groups past 64 re-read the weights -- the repeats are served by
 // the Infinity Cache for matrices up to its size.
-static Shape pick_shape(int R, int NM) {
-  if (R <= 16) return {1, 4};
-  if (NM == 2) return {2, 4};
-  return {4, 4};
+static bool use_wide(int R) { return R > 16; }
+
+static Shape wide_shape(int R, int NM) {
+  return {R <= 32 ? 2 : 4, NM == 2 ? 2 : 4};
 }
 
 int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K) {
   (void)K;
-  Shape s = pick_shape(R, 1);
-  return (N + 16 * s.NT - 1) / (16 * s.NT);
+  if (use_wide(R)) {
+    const int cols = 16 * wide_shape(R, 1).NT;
+    return (N + cols * WIDE_NW - 1) / (cols * WIDE_NW) * WIDE_NW;
+  }
+  return (N + 63) / 64;
+}
+
+template <int EPI>
+static hipError_t launch_reduce(const GemmArgs& a, int S, hipStream_t st) {
+  const size_t threads = (size_t)a.R * (a.N / 4);
+  gemm_reduce_kernel<EPI><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(a, S);
+  return hipGetLastError();
 }
 
 template <int RT, int NT, int EPI>
@@ -400,17 +567,45 @@ static hipError_t launch_shape(const GemmArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
-  const size_t threads = (size_t)a.R * (a.N / 4);
-  gemm_reduce_kernel<EPI><<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(a, S);
-  return hipGetLastError();
+  return launch_reduce<EPI>(a, S, st);
+}
+
+// The wide-row kernel over (column groups of 4 waves) x (K splits) x (row
+// groups). A K split is used only while the column groups alone leave the
+// chip short of workgroups and each split keeps >= 1024 k; the logits never
+// split (their argmax is fused).
+template <int RT, int NT, int D, int EPI>
+static hipError_t launch_wide(const GemmArgs& a, int S_force, hipStream_t st) {
+  constexpr int NM = EpiTraits<EPI>::NM;
+  const int cols = 16 * NT * WIDE_NW;
+  const int n_groups = (a.N + cols - 1) / cols;
+  const int r_groups = (a.R + 16 * RT - 1) / (16 * RT);
+  int S = 1;
+  if (S_force > 0) {
+    S = S_force;
+  } else if (EPI != EPI_LOGITS) {
+    while (n_groups * r_groups * S < 512 && a.K / (S * 2) >= 1024 &&
+           (size_t)(S * 2) * NM * a.R * a.N <= a.partials_cap)
+      S *= 2;
+  }
+  if (EPI == EPI_LOGITS) S = 1;
+  int kc = (a.K + S - 1) / S;
+  kc = (kc + 63) / 64 * 64;
+  S = (a.K + kc - 1) / kc;
+  if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) return hipErrorInvalidValue;
+  dim3 grid(n_groups, S, r_groups);
+  gemm_wide_kernel<RT, NT, D, EPI><<<grid, 64 * WIDE_NW, 0, st>>>(a, kc, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  return launch_reduce<EPI>(a, S, st);
 }
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
-  const Shape s = pick_shape(a.R, EpiTraits<EPI>::NM);
-  if (s.RT == 1) return launch_shape<1, 4, EPI>(a, st);
-  if constexpr (EpiTraits<EPI>::NM == 2) return launch_shape<2, 4, EPI>(a, st);
-  else return launch_shape<4, 4, EPI>(a, st);
+  if (!use_wide(a.R)) return launch_shape<1, 4, EPI>(a, st);
+  constexpr int NT = EpiTraits<EPI>::NM == 2 ? 2 : 4;
+  if (a.R <= 32) return launch_wide<2, NT, 4, EPI>(a, 0, st);
+  return launch_wide<4, NT, 4, EPI>(a, 0, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
