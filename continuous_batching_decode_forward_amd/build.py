@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcbd.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.environ.get("HIPCC", os.path.join(ROCM, "bin", "hipcc"))
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}"]
 # Packed fp32 instructions stay off in device code.
@@ -35,8 +36,8 @@ def _compile(src: str) -> str:
     cmd = [HIPCC] + COMMON
     if src.endswith(".hip"):
         cmd += DEVICE + ["-x", "hip"]
-    else:
-        cmd += ["-D__HIP_PLATFORM_AMD__"]
+    else:  # host-only C++ (the HIP runtime API, no device code)
+        cmd += ["-x", "c++", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]
     cmd += ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

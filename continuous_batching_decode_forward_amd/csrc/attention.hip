@@ -31,9 +31,11 @@
 namespace cbd {
 
 #define ATT_WAVES 4
+#define ATT_LDS_SEQS 1024  // item0 staged in LDS for up to this many sequences
 
-__device__ __forceinline__ int find_seq(const int32_t* __restrict__ item0, int n, int item) {
-  int lo = 0, hi = n - 1;  // largest s with item0[s] <= item
+// Largest s with item0[s] <= item (item0 ascending, item0[0] = 0).
+__device__ __forceinline__ int find_seq(const int32_t* item0, int n, int item) {
+  int lo = 0, hi = n - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
     if (item0[mid] <= item)
@@ -44,207 +46,271 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ item0, int n
   return lo;
 }
 
-template <int HD, bool WIDE_BLOCKS>
+// A value the whole wave shares, moved to a scalar register.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// One 32-key step's operands in registers: K rows of the two S tiles and
+// the V^T pieces.
+template <int HD>
+struct KVTile {
+  uint4 k[2][HD / 32];
+  uint4 v[HD / 16];
+};
+
+// The loads are unconditional and branch-free: a key past the item's range
+// reads a valid pool location (its score is masked to -inf, and its V
+// element is zeroed on the last step), and a block id outside the pool is
+// replaced by block 0 and reported. Block ids come from the wave's slice of
+// the block table staged in LDS, so no K/V address waits on a global load.
+template <int HD, int BS>
 __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
     const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, StepMeta m,
-    RowMaps maps, ModelDims md, AttnPlan ap,
-    const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v,
-    float* __restrict__ part_ml, float* __restrict__ part_o, uint32_t* status) {
+    RowMaps maps, ModelDims md, AttnPlan ap, const uint16_t* __restrict__ pool_k,
+    const uint16_t* __restrict__ pool_v, float* __restrict__ part_ml,
+    float* __restrict__ part_o, uint32_t* status) {
   constexpr int QK_STEPS = HD / 32;  // MFMAs over head_dim
   constexpr int DT = HD / 16;        // output d tiles
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int s_item0[ATT_LDS_SEQS + 1];
+  __shared__ int s_tbl[ATT_WAVES][ATT_TBL];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int item = blockIdx.x * ATT_WAVES + wave;
   const int n_seqs = m.n_seqs;
-  if (item >= maps.item0[n_seqs]) return;
-  const int s = find_seq(maps.item0, n_seqs, item);
+  const bool lds_seqs = n_seqs <= ATT_LDS_SEQS;
+  if (lds_seqs)
+    for (int i = threadIdx.x; i <= n_seqs; i += 64 * ATT_WAVES) s_item0[i] = maps.item0[i];
+  __syncthreads();
+  // Everything that selects the work item is the same for the whole wave;
+  // readfirstlane makes that explicit so that the key loop is a scalar loop.
+  const int total = uniform(lds_seqs ? s_item0[n_seqs] : maps.item0[n_seqs]);
+  const int item = blockIdx.x * ATT_WAVES + wave;
+  if (item >= total) return;  // no barrier below this point
+  const int s = uniform(lds_seqs ? find_seq(s_item0, n_seqs, item)
+                                 : find_seq(maps.item0, n_seqs, item));
   const int G = md.n_heads / md.n_kv_heads;
   const int rpt = 16 / G;  // rows per query tile
-  const int nn = m.n_new[s], ctx = m.ctx_lens[s];
+  const int nn = uniform(m.n_new[s]), ctx = uniform(m.ctx_lens[s]);
   const int qtiles = (nn * G + 15) / 16;
   const int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
-  int local = item - maps.item0[s];
+  int local = item - uniform(lds_seqs ? s_item0[s] : maps.item0[s]);
   const int qt = local % qtiles;
   local /= qtiles;
   const int sp = local % splits;
   const int g = local / splits;
 
-  // This lane's query column.
-  const int c_row = qt * rpt + lr / G;  // row within the sequence
+  // This lane's query column: row c_row of the sequence, query head c_head.
+  const int c_row = qt * rpt + lr / G;
   const int c_head = g * G + lr % G;
   const bool c_ok = lr < rpt * G && c_row < nn;
-  const int row0 = maps.seq_row0[s];
+  const int row0 = uniform(maps.seq_row0[s]);
   const int last_row = min(nn, (qt + 1) * rpt) - 1;
   const int k_lo = sp * ap.split_len;
   const int k_hi = min(k_lo + ap.split_len, ctx + last_row + 1);
   const int c_end = c_ok ? min(k_hi, ctx + c_row + 1) : k_lo;  // keys [k_lo, c_end)
 
-  // Q as the B operand: lane (lr, lg) holds d = lg*HD/4 + 8j .. +8 of its
-  // column, as the hi and the lo bf16 terms of the fp32 query.
+  // Q as the B operand of S = K.Q^T: lane (lr, lg) holds d = 32 j + 8 lg .. +8
+  // of its column for step j, as the hi and lo bf16 terms.
   bf16x8_t qf[2][QK_STEPS];
   {
-    const size_t at = ((size_t)(row0 + (c_ok ? c_row : 0)) * md.n_heads + c_head) * HD +
-                      lg * (HD / 4);
+    const size_t at = ((size_t)(row0 + min(c_row, nn - 1)) * md.n_heads + c_head) * HD + 8 * lg;
 #pragma unroll
     for (int j = 0; j < QK_STEPS; ++j) {
-      qf[0][j] = as_bf16x8(c_ok ? reinterpret_cast<const uint4*>(q_hi + at)[j]
-                                : make_uint4(0, 0, 0, 0));
-      qf[1][j] = as_bf16x8(c_ok ? reinterpret_cast<const uint4*>(q_lo + at)[j]
-                                : make_uint4(0, 0, 0, 0));
+      qf[0][j] = as_bf16x8(*reinterpret_cast<const uint4*>(q_hi + at + 32 * j));
+      qf[1][j] = as_bf16x8(*reinterpret_cast<const uint4*>(q_lo + at + 32 * j));
     }
   }
 
+  // The wave's block-table slice: entries for blocks b0 .. b0 + nb - 1.
   const int32_t* table = m.block_tables + (size_t)s * m.max_blocks_per_seq;
-  const int bs = md.block_size;
-  const size_t kv_head_stride = (size_t)bs * HD;  // one (block, kv head) tile
+  const int b0 = k_lo / BS;
+  const int nb = (k_hi - 1) / BS - b0 + 1;  // <= ATT_TBL (host-side split cap)
+  if (nb > ATT_TBL) {  // the host caps split_len; refuse rather than overrun LDS
+    if (lane == 0) raise_status(status, ST_BAD_SHAPE);
+    return;
+  }
+  int* tbl = s_tbl[wave];
+  bool bad_block = false;
+  for (int i = lane; i < nb; i += 64) {
+    int blk = table[b0 + i];
+    if (blk < 0 || blk >= md.num_blocks) {
+      bad_block = true;
+      blk = 0;
+    }
+    tbl[i] = blk;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const size_t head_stride = (size_t)BS * HD;  // one (block, kv head) tile
+  const size_t kv_off = (size_t)g * head_stride;
+  const size_t blk_stride = (size_t)md.n_kv_heads * head_stride;
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
+  const int last = k_hi - 1;
+
+  // Per-lane constant parts of the K and V^T addresses inside a block.
+  // K row of tile t for this lane: key 8 (lr / 4) + lr % 4 + 4 t of the step.
+  const int krow0 = 8 * (lr >> 2) + (lr & 3);
+  auto load = [&](KVTile<HD>& T, int p0) {
+    if constexpr (BS >= 32) {
+      // A 32-key step lies in one block (steps start on multiples of 32):
+      // one block id for the wave, keys past the range read stale but valid
+      // slots of the same block.
+      const int blk = uniform(tbl[p0 / BS - b0]);
+      const uint16_t* kb = pool_k + (size_t)blk * blk_stride + kv_off + (size_t)(p0 % BS) * HD;
+      const uint16_t* vb = pool_v + (size_t)blk * blk_stride + kv_off + (p0 % BS);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < QK_STEPS; ++j)
+          T.k[t][j] = load_stream16(kb + (size_t)(krow0 + 4 * t) * HD + 8 * lg + 32 * j);
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+        T.v[t] = load_stream16(vb + (size_t)(16 * t + lr) * BS + 8 * lg);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int p = min(p0 + krow0 + 4 * t, last);
+        const int blk = tbl[p / BS - b0];
+        const uint16_t* kp = pool_k + (size_t)blk * blk_stride + kv_off + (size_t)(p % BS) * HD + 8 * lg;
+#pragma unroll
+        for (int j = 0; j < QK_STEPS; ++j) T.k[t][j] = load_stream16(kp + 32 * j);
+      }
+      // V^T pieces: row d = 16 t + lr, keys pv .. pv + 7 (pv = p0 + 8 lg)
+      const int pv = min(p0 + 8 * lg, last & ~7);
+      if constexpr (BS >= 8) {
+        const int blk = tbl[pv / BS - b0];
+        const uint16_t* vp = pool_v + (size_t)blk * blk_stride + kv_off + (size_t)lr * BS + (pv % BS);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) T.v[t] = load_stream16(vp + (size_t)16 * t * BS);
+      } else {  // 4-position blocks: two 8-byte halves
+        const int blk0 = tbl[pv / BS - b0];
+        const int blk1 = tbl[min(pv + 4, last) / BS - b0];
+        const uint16_t* v0 = pool_v + (size_t)blk0 * blk_stride + kv_off + (size_t)lr * BS;
+        const uint16_t* v1 = pool_v + (size_t)blk1 * blk_stride + kv_off + (size_t)lr * BS;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          const uint2 a = *reinterpret_cast<const uint2*>(v0 + (size_t)16 * t * BS);
+          const uint2 b = *reinterpret_cast<const uint2*>(v1 + (size_t)16 * t * BS);
+          T.v[t] = make_uint4(a.x, a.y, b.x, b.y);
+        }
+      }
+    }
+  };
 
   floatx4_t o[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  bool bad_block = false;
+  // Steps that end at or before every column's limit need no score mask.
+  // Idle columns (c_ok false) take k_hi: their values are never written.
+  const int col_end = c_ok ? c_end : k_hi;
+  int mask_from = col_end;
+#pragma unroll
+  for (int o_ = 1; o_ < 16; o_ <<= 1) mask_from = min(mask_from, __shfl_xor(mask_from, o_, 64));
+  mask_from = uniform(mask_from);
 
-  for (int p0 = k_lo; p0 < k_hi; p0 += 32) {
-    // ---- K rows for the two S tiles: row m -> key p0 + 8(m/4) + m%4 + 4t
-    uint4 kf[2][QK_STEPS];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int p = p0 + 8 * (lr >> 2) + (lr & 3) + 4 * t;
-      bool ok = p < k_hi;
-      int blk = ok ? table[p / bs] : 0;
-      if (ok && (blk < 0 || blk >= md.num_blocks)) {
-        bad_block = true;
-        ok = false;
-      }
-      const uint16_t* kp = pool_k + ((size_t)blk * md.n_kv_heads + g) * kv_head_stride +
-                           (size_t)(p % bs) * HD + lg * (HD / 4);
-#pragma unroll
-      for (int j = 0; j < QK_STEPS; ++j)
-        kf[t][j] = ok ? reinterpret_cast<const uint4*>(kp)[j] : make_uint4(0, 0, 0, 0);
-    }
-    // ---- V^T rows for the PV MFMA: d = 16 dt + lr, keys p0 + 8 lg .. +8
-    uint4 vf[DT];
-    {
-      const int pv = p0 + 8 * lg;
-      if (WIDE_BLOCKS) {  // 8 | block_size: the 8 keys share one block
-        bool ok = pv < k_hi;
-        int blk = ok ? table[pv / bs] : 0;
-        if (ok && (blk < 0 || blk >= md.num_blocks)) {
-          bad_block = true;
-          ok = false;
-        }
-        const uint16_t* vp = pool_v + ((size_t)blk * md.n_kv_heads + g) * kv_head_stride +
-                             (size_t)lr * bs + (pv % bs);
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-          vf[t] = ok ? *reinterpret_cast<const uint4*>(vp + (size_t)16 * t * bs)
-                     : make_uint4(0, 0, 0, 0);
-        // keys at or beyond k_hi inside the 8: zero them (they may hold stale data)
-        if (ok && pv + 8 > k_hi) {
-          int valid = k_hi - pv;  // 1..7
-#pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            uint32_t w[4] = {vf[t].x, vf[t].y, vf[t].z, vf[t].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (2 * e >= valid) w[e] = 0;
-              else if (2 * e + 1 >= valid) w[e] &= 0xffffu;
-            }
-            vf[t] = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        }
-      } else {  // 4-position blocks: two half loads
-#pragma unroll
-        for (int t = 0; t < DT; ++t) vf[t] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int ph = pv + 4 * half;
-          bool ok = ph < k_hi;
-          int blk = ok ? table[ph / bs] : 0;
-          if (ok && (blk < 0 || blk >= md.num_blocks)) {
-            bad_block = true;
-            ok = false;
-          }
-          const uint16_t* vp = pool_v + ((size_t)blk * md.n_kv_heads + g) * kv_head_stride +
-                               (size_t)lr * bs + (ph % bs);
-          int valid = min(4, k_hi - ph);
-#pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            uint2 v = ok ? *reinterpret_cast<const uint2*>(vp + (size_t)16 * t * bs)
-                         : make_uint2(0, 0);
-            if (ok && valid < 4) {
-              if (valid <= 0) v = make_uint2(0, 0);
-              else if (valid == 1) v = make_uint2(v.x & 0xffffu, 0);
-              else if (valid == 2) v = make_uint2(v.x, 0);
-              else v = make_uint2(v.x, v.y & 0xffffu);
-            }
-            if (half == 0) {
-              vf[t].x = v.x;
-              vf[t].y = v.y;
-            } else {
-              vf[t].z = v.x;
-              vf[t].w = v.y;
-            }
-          }
-        }
-      }
-    }
-    // ---- S = K . Q^T for the two tiles
+  auto compute = [&](KVTile<HD>& T, int p0) {
     floatx4_t sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sacc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < QK_STEPS; ++j) {
-        sacc[t] = mfma16x16x32(as_bf16x8(kf[t][j]), qf[0][j], sacc[t]);
-        sacc[t] = mfma16x16x32(as_bf16x8(kf[t][j]), qf[1][j], sacc[t]);
+        sacc[t] = mfma16x16x32(as_bf16x8(T.k[t][j]), qf[0][j], sacc[t]);
+        sacc[t] = mfma16x16x32(as_bf16x8(T.k[t][j]), qf[1][j], sacc[t]);
       }
     }
-    // lane (lr, lg) now holds column lr for keys p0 + 8 lg + jj, jj = i + 4 t
+    // lane (lr, lg) holds column lr for keys p0 + 8 lg + i + 4 t
     float sv[8];
-    float cmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = p0 + 8 * lg + i + 4 * t;
-        float v = (p < c_end) ? sacc[t][i] * scale : -INFINITY;
-        sv[i + 4 * t] = v;
-        cmax = fmaxf(cmax, v);
+      for (int i = 0; i < 4; ++i) sv[i + 4 * t] = sacc[t][i] * scale;
+    if (p0 + 32 > mask_from) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int p = p0 + 8 * lg + (e & 3) + 4 * (e >> 2);
+        if (p >= col_end) sv[e] = -INFINITY;
       }
+    }
+    float cmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
     const float m_new = fmaxf(m_run, cmax);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
-    // P = P1 + P2 + P3, three bf16 terms: together they carry P's full fp32
-    // significand, so the PV product rounds like an fp32 weighted sum.
+    // Stale V elements of keys past the range (last step only) are zeroed:
+    // their P is 0, but 0 * NaN would not be.
+    if (p0 + 32 > k_hi) {
+      const int valid = k_hi - (p0 + 8 * lg);  // keys of this lane's piece in range
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        uint32_t w[4] = {T.v[t].x, T.v[t].y, T.v[t].z, T.v[t].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t keep = 2 * e + 1 < valid ? 0xffffffffu : (2 * e < valid ? 0xffffu : 0u);
+          w[e] &= keep;
+        }
+        T.v[t] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    // P = P1 + P2 + P3 exactly: each term keeps the top 8 significant bits
+    // of what the previous ones left (truncation; the last remainder has at
+    // most 8 bits and is itself a bf16), so the PV product accumulates like
+    // an fp32 weighted sum. The terms of two keys pack into one register.
     uint32_t p1[4], p2[4], p3[4];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float a = exp2f(sv[2 * e] - m_use);
-      const float b = exp2f(sv[2 * e + 1] - m_use);
+      const float a = __builtin_amdgcn_exp2f(sv[2 * e] - m_use);
+      const float b = __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_use);
       psum += a + b;
-      const float a1 = round_bf(a), b1 = round_bf(b);
-      const float a2 = round_bf(a - a1), b2 = round_bf(b - b1);
-      p1[e] = pack_bf2(a1, b1);
-      p2[e] = pack_bf2(a2, b2);
-      p3[e] = pack_bf2(a - a1 - a2, b - b1 - b2);
+      const float a1 = __uint_as_float(__float_as_uint(a) & 0xffff0000u);
+      const float b1 = __uint_as_float(__float_as_uint(b) & 0xffff0000u);
+      const float ra = a - a1, rb = b - b1;
+      const float a2 = __uint_as_float(__float_as_uint(ra) & 0xffff0000u);
+      const float b2 = __uint_as_float(__float_as_uint(rb) & 0xffff0000u);
+      const float a3 = ra - a2, b3 = rb - b2;
+      // the high halves of a (low 16 bits of the result) and b (high 16)
+      p1[e] = __builtin_amdgcn_perm(__float_as_uint(b1), __float_as_uint(a1), 0x07060302u);
+      p2[e] = __builtin_amdgcn_perm(__float_as_uint(b2), __float_as_uint(a2), 0x07060302u);
+      p3[e] = __builtin_amdgcn_perm(__float_as_uint(b3), __float_as_uint(a3), 0x07060302u);
     }
     l_run = l_run * alpha + psum;
+    // Rescale the running output only when some column's maximum moved.
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[t] = o[t] * alpha;
+    }
     const bf16x8_t pf1 = as_bf16x8(make_uint4(p1[0], p1[1], p1[2], p1[3]));
     const bf16x8_t pf2 = as_bf16x8(make_uint4(p2[0], p2[1], p2[2], p2[3]));
     const bf16x8_t pf3 = as_bf16x8(make_uint4(p3[0], p3[1], p3[2], p3[3]));
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      o[t] = o[t] * alpha;
-      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf1, o[t]);
-      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf2, o[t]);
-      o[t] = mfma16x16x32(as_bf16x8(vf[t]), pf3, o[t]);
+    for (int t = 0; t < DT; ++t) o[t] = mfma16x16x32(as_bf16x8(T.v[t]), pf1, o[t]);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = mfma16x16x32(as_bf16x8(T.v[t]), pf2, o[t]);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = mfma16x16x32(as_bf16x8(T.v[t]), pf3, o[t]);
+  };
+
+  // Two tiles in flight: the loads of step i + 1 are issued before step i is
+  // computed (near the end they repeat the last step's addresses, which
+  // the cache serves; those repeats are never computed).
+  {
+    const int n_it = (k_hi - k_lo + 31) / 32;
+    KVTile<HD> A, B;
+    load(A, k_lo);
+    int i = 0;
+    for (; i + 2 <= n_it; i += 2) {
+      load(B, k_lo + 32 * (i + 1));
+      compute(A, k_lo + 32 * i);
+      load(A, min(k_lo + 32 * (i + 2), last));
+      compute(B, k_lo + 32 * (i + 1));
     }
+    if (i < n_it) compute(A, k_lo + 32 * i);
   }
   if (bad_block) raise_status(status, ST_BAD_BLOCK);
 
@@ -310,6 +376,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
   }
 }
 
+template <int HD, int BS>
+static void launch_items(int blocks, const uint16_t* q_hi, const uint16_t* q_lo, const StepMeta& m,
+                         const RowMaps& maps, const ModelDims& md, const AttnPlan& ap,
+                         const uint16_t* pool_k, const uint16_t* pool_v, float* part_ml,
+                         float* part_o, uint32_t* status, hipStream_t st) {
+  attention_kernel<HD, BS><<<blocks, 64 * ATT_WAVES, 0, st>>>(q_hi, q_lo, m, maps, md, ap, pool_k,
+                                                             pool_v, part_ml, part_o, status);
+}
+
 template <int HD>
 static hipError_t launch_hd(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R,
                             const StepMeta& m, const RowMaps& maps, const ModelDims& md,
@@ -318,12 +393,14 @@ static hipError_t launch_hd(const uint16_t* q_hi, const uint16_t* q_lo, int32_t 
                             uint32_t* status, hipStream_t st) {
   const int blocks = (ap.grid_items + ATT_WAVES - 1) / ATT_WAVES;
   if (blocks > 0) {
-    if (md.block_size % 8 == 0)
-      attention_kernel<HD, true><<<blocks, 64 * ATT_WAVES, 0, st>>>(
-          q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status);
-    else
-      attention_kernel<HD, false><<<blocks, 64 * ATT_WAVES, 0, st>>>(
-          q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status);
+    switch (md.block_size) {
+      case 4: launch_items<HD, 4>(blocks, q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status, st); break;
+      case 8: launch_items<HD, 8>(blocks, q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status, st); break;
+      case 16: launch_items<HD, 16>(blocks, q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status, st); break;
+      case 32: launch_items<HD, 32>(blocks, q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status, st); break;
+      case 64: launch_items<HD, 64>(blocks, q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status, st); break;
+      default: return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -64,6 +64,34 @@ __device__ __forceinline__ uint4 load_stream16(const uint16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane i of the
+// wave writes lds_base + 16 i (lds_base must be the same for the whole
+// wave). Counts as a vector-memory load for s_waitcnt vmcnt. Issued as
+// inline assembly on purpose: the compiler would otherwise make every later
+// LDS access wait for all outstanding loads (it cannot tell which LDS
+// bytes the copy writes), so the caller orders the copy itself with
+// wait_vmem and a barrier.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+#endif
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+#if defined(__HIP_DEVICE_COMPILE__)
+  // s_waitcnt simm16: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+#endif
+}
+
 __device__ __forceinline__ floatx4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

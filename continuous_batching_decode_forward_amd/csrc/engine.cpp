@@ -14,6 +14,17 @@ namespace cbd {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Key splits per (row, head) the partial buffers hold.
+static int32_t attn_cap_splits(const cbd_config& c) {
+  int32_t s = (c.max_position + 127) / 128;
+  return std::max(1, std::min(64, s));
+}
+
+// Longest key split: a split spans at most ATT_TBL blocks.
+static int32_t attn_split_cap(const cbd_config& c) {
+  return (ATT_TBL - 1) * c.block_size / 32 * 32;
+}
+
 int validate_config(const cbd_config* c) {
   if (!c) return fail(CBD_E_INVAL, "config is NULL");
   if (c->n_layers < 1 || c->d_model < 1 || c->n_heads < 1 || c->n_kv_heads < 1 ||
@@ -35,12 +46,9 @@ int validate_config(const cbd_config* c) {
     return fail(CBD_E_UNSUPPORTED, "d_model, ffn_dim and vocab must be multiples of 16");
   if (c->d_model > 8192) return fail(CBD_E_UNSUPPORTED, "d_model above 8192");
   if (c->max_seqs > c->max_rows) return fail(CBD_E_INVAL, "max_seqs exceeds max_rows");
+  if ((long long)attn_cap_splits(*c) * attn_split_cap(*c) < c->max_position)
+    return fail(CBD_E_UNSUPPORTED, "max_position too long for this block size");
   return CBD_OK;
-}
-
-static int32_t attn_cap_splits(const cbd_config& c) {
-  int32_t s = (c.max_position + 127) / 128;
-  return std::max(1, std::min(64, s));
 }
 
 WorkspaceLayout workspace_layout(const cbd_config& c) {
@@ -367,7 +375,7 @@ static AttnPlan plan_attention(const cbd_engine* e, const cbd_step* s) {
   len = (len + 31) / 32 * 32;
   int32_t floor_len = (s->max_ctx + ap.max_splits - 1) / ap.max_splits;
   floor_len = (floor_len + 31) / 32 * 32;
-  ap.split_len = std::max(len, floor_len);
+  ap.split_len = std::max(std::min(len, attn_split_cap(c)), floor_len);
   const int G = c.n_heads / c.n_kv_heads;
   const long long qt = ((long long)s->n_rows * G + 15) / 16 + s->n_seqs;
   const long long sp = (s->max_ctx + ap.split_len - 1) / ap.split_len;

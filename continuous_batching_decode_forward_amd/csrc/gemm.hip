@@ -305,40 +305,43 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
   store_tile<RT, NT, EPI>(a, acc, r0, n0, ks, S, blockIdx.x);
 }
 
-// ------------------------------------------------------- the wide-row path
+// ------------------------------------------------------- the stream path
 //
-// For 17..64 rows per weight read. A workgroup is NW = 4 waves side by side
-// along N (each NT column fragments) over the same K range and all RT row
-// fragments, so the activation tile of a 64-k stage (RT x 16 rows x 64 k, hi
-// and lo: RT x 4 KB) is fetched once per workgroup into LDS instead of once
-// per wave. The LDS tile is kept in MFMA operand order -- block
-// (rt, plane, 32-k half) is 64 lanes x 16 bytes -- so each wave reads its B
-// operands with one conflict-free 16-byte LDS read per lane.
-//
-// Each wave streams its weights through a ring of D register stages (64 k
-// each), issuing stage c + D - 1 before it computes stage c, so D - 1 stages
-// of weight reads are in flight per wave. The activation copy for a stage is
-// issued with that stage's weights (the vector-memory counter retires loads
-// in order, so a later-issued activation load would hold back the wait for
-// the weights behind it). Per stage: copy the arrived activation rows into
-// LDS buffer c % 2, barrier, then the MFMAs of stage c.
-#define WIDE_NW 4
+// One kernel for any row count. A workgroup is 4 waves side by side along N
+// (each NT column fragments, RT row fragments) over one K range. Per 64-k
+// stage the workgroup's activation tile (RT x 16 rows x 64 k, hi and lo:
+// RT x 4 KB, kept in MFMA operand order -- block (rt, plane, 32-k half) is
+// 64 lanes x 16 bytes) is copied by direct global->LDS loads into a ring of
+// D LDS stages, with no registers involved; each wave's weights stream
+// through a ring of D register stages. The loads of stage c + D - 1 are
+// issued right after the barrier of stage c, so D - 2 later stages stay in
+// flight while stage c waits: the wait is an explicit vector-memory count
+// (the LDS copies carry no register the compiler could wait on), exact
+// because every stage issues the same number of loads per wave and the
+// barrier orders the stages. Stages are padded to a multiple of D; the
+// activation pieces at or beyond kend (padding, a K tail) are zeroed in LDS
+// after their copy lands, so the weights read there meet zeros.
+#define STREAM_NW 4
 
 template <int RT, int NT, int D, int EPI>
-__global__ __launch_bounds__(64 * WIDE_NW) void gemm_wide_kernel(GemmArgs a, int kc, int S) {
+__global__ __launch_bounds__(64 * STREAM_NW) void gemm_stream_kernel(GemmArgs a, int kc, int S) {
   constexpr int NM = EpiTraits<EPI>::NM;
-  constexpr int BLK = RT * 4;  // LDS blocks per stage: (rt, plane, half)
-  __shared__ uint4 xs[2][BLK * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int BLK = RT * 4;                 // 1 KB LDS blocks per stage
+  constexpr int LPS = NM * NT * 2 + RT;       // loads per stage per wave
+  static_assert(D >= 3, "ring depth");
+  extern __shared__ uint4 xs[];               // [D][BLK][64]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int tile = blockIdx.x * WIDE_NW + wave;  // this wave's column tile
+  const int tile = blockIdx.x * STREAM_NW + wave;
   const int n0 = tile * (16 * NT);
   const int ks = blockIdx.y;
   const int r0 = blockIdx.z * (16 * RT);
   const int K = a.K, N = a.N, R = a.R;
-  const int kbeg = ks * kc;                 // a multiple of 64
+  const int kbeg = ks * kc;                   // a multiple of 64
   const int kend = min(K, kbeg + kc);
-  const int nst = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
+  const int nst0 = kend > kbeg ? (kend - kbeg + 63) / 64 : 0;
+  const int nst = (nst0 + D - 1) / D * D;     // padded to whole ring turns
 
   const int KT = (K + 31) / 32;
   const uint16_t* wp[NM][NT];
@@ -350,18 +353,16 @@ __global__ __launch_bounds__(64 * WIDE_NW) void gemm_wide_kernel(GemmArgs a, int
     wp[0][nt] = a.W + off;
     if (NM == 2) wp[NM - 1][nt] = a.W2 + off;
   }
-  // This thread's share of the activation copy: block b = wave + 4 i of
-  // every stage, lane `lane` of it. Rows past R read row 0 and are zeroed
-  // when written to LDS.
+  // This wave copies blocks b = wave + 4 i of every stage; lane `lane` of
+  // block (rt, pl, h) is row r0 + 16 rt + lr, k + 32 h + 8 lg. Rows past R
+  // read row R - 1 (their outputs are never stored).
   const uint16_t* xsrc[RT];
-  bool xrow[RT];
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
-    const int b = wave + WIDE_NW * i;
+    const int b = wave + STREAM_NW * i;
     const int rt = b >> 2, pl = (b >> 1) & 1;
-    const int r = r0 + 16 * rt + lr;
-    xrow[i] = r < R;
-    xsrc[i] = (pl ? a.Xlo : a.X) + (size_t)(xrow[i] ? r : 0) * K;
+    const int r = min(r0 + 16 * rt + lr, R - 1);
+    xsrc[i] = (pl ? a.Xlo : a.X) + (size_t)r * K;
   }
 
   floatx4_t acc[NM][NT][RT];
@@ -372,14 +373,9 @@ __global__ __launch_bounds__(64 * WIDE_NW) void gemm_wide_kernel(GemmArgs a, int
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // The loads carry no conditions (a condition would become a branch, and
-  // the counter waits at its join drain every outstanding load): weight
-  // tiles are clamped into the matrix and activation pieces into the row,
-  // and pieces at or beyond kend are zeroed when the activations are
-  // written to LDS -- weights there then meet zeros.
   uint4 w[D][NM][NT][2];
-  uint4 xc[D][RT];
-  auto load = [&](int j, int c) {
+  // Issue every load of stage c (clamped into range; see above) into slot j.
+  auto issue = [&](int j, int c) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = min(kbeg / 32 + 2 * c + h, KT - 1) - kbeg / 32;
@@ -391,20 +387,13 @@ __global__ __launch_bounds__(64 * WIDE_NW) void gemm_wide_kernel(GemmArgs a, int
     }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      const int b = wave + WIDE_NW * i;
+      const int b = wave + STREAM_NW * i;
       const int k = min(kbeg + 64 * c + 32 * (b & 1) + 8 * lg, K - 8);
-      xc[j][i] = *reinterpret_cast<const uint4*>(xsrc[i] + k);
+      copy16_to_lds(xsrc[i] + k, xs + ((size_t)j * BLK + b) * 64);
     }
   };
-  auto stage = [&](int j, int c) {
-    uint4* buf = xs[c & 1];
-#pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const int b = wave + WIDE_NW * i;
-      const bool ok = xrow[i] && kbeg + 64 * c + 32 * (b & 1) + 8 * lg < kend;
-      buf[b * 64 + lane] = ok ? xc[j][i] : make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();
+  auto compute = [&](int j, int c) {
+    const uint4* buf = xs + (size_t)j * BLK * 64;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint4 xf[RT][2];
@@ -426,25 +415,29 @@ __global__ __launch_bounds__(64 * WIDE_NW) void gemm_wide_kernel(GemmArgs a, int
   };
 
   if (nst > 0) {
-    // Stage s lives in ring slot s % D; the loads of stage c + D - 1 are
-    // issued before stage c is computed (clamped to the last stage near the
-    // end: those repeats are cache hits and never computed).
 #pragma unroll
-    for (int j = 0; j < D - 1; ++j) load(j, min(j, nst - 1));
-    const int groups = nst / D;
-    for (int g = 0; g < groups; ++g) {
+    for (int j = 0; j < D - 1; ++j) issue(j, j);
+    for (int c0 = 0; c0 < nst; c0 += D) {
 #pragma unroll
       for (int j = 0; j < D; ++j) {
-        const int c = g * D + j;
-        load((j + D - 1) % D, min(c + D - 1, nst - 1));
-        stage(j, c);
+        const int c = c0 + j;
+        // Stage c's loads were followed by those of stages c + 1 .. c + D - 2.
+        wait_vmem<(D - 2) * LPS>();
+        if (kbeg + 64 * c + 64 > kend) {  // K tail or padding: zero what lies past kend
+#pragma unroll
+          for (int i = 0; i < RT; ++i) {
+            const int b = wave + STREAM_NW * i;
+            if (kbeg + 64 * c + 32 * (b & 1) + 8 * lg >= kend)
+              xs[((size_t)j * BLK + b) * 64 + lane] = make_uint4(0, 0, 0, 0);
+          }
+        }
+        __syncthreads();
+        issue((j + D - 1) % D, min(c + D - 1, nst - 1));
+        compute(j, c);
       }
     }
-    const int rest = nst - groups * D;  // < D, already loaded in slots 0..rest-1
-#pragma unroll
-    for (int j = 0; j < D - 1; ++j)
-      if (j < rest) stage(j, groups * D + j);
   }
+  wait_vmem<0>();  // no LDS copy may land after the workgroup exits
   store_tile<RT, NT, EPI>(a, acc, r0, n0, ks, S, tile);
 }
 
@@ -502,28 +495,63 @@ hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, h
   return hipGetLastError();
 }
 
-struct Shape {
-  int RT, NT;
+// How one projection runs: the per-wave kernel (RT = 1: up to 16 rows; KW
+// waves of a workgroup split K and reduce through LDS) or the stream kernel
+// (RT = 2 or 4 row fragments; 4 column-split waves share the activation
+// tile), with S workgroups splitting K further (partials summed by a second
+// kernel in split order). Chosen from the row count and the matrix shape
+// after measuring the step's matrices on MI355X: small weight reads are
+// dominated by the first loads' latency and the launch, so they want many
+// waves each reading a few tens of KB, in a single launch where possible.
+struct GemmPlan {
+  bool stream;
+  int RT, NT, KW, D, S;
 };
 
-// Up to 16 rows: the per-wave kernel with one row fragment and four column
-// fragments (the waves of a workgroup split K). Beyond 16 rows: the wide-row
-// kernel, 64 rows (four row fragments; two up to 32 rows) per weight read,
-// and row groups past 64 re-read the weights -- the repeats are served by
-// the Infinity Cache for matrices up to its size.
-static bool use_wide(int R) { return R > 16; }
-
-static Shape wide_shape(int R, int NM) {
-  return {R <= 32 ? 2 : 4, NM == 2 ? 2 : 4};
+static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
+  GemmPlan p{};
+  const bool vocab = logits && N >= 32768;  // the LM head: wide, argmax fused
+  if (R <= 16) {
+    p.stream = false;
+    p.RT = 1;
+    p.D = 0;
+    if (vocab) {
+      p.NT = R <= 8 ? 1 : 4;
+      p.KW = R <= 8 ? 4 : 1;
+      p.S = 1;
+    } else {
+      const bool long_k = K >= 8192;
+      p.NT = R <= 8 ? 1 : 2;
+      p.KW = long_k ? (R <= 8 ? 4 : 8) : (NM == 2 && R <= 8 ? 8 : 4);
+      p.S = long_k && R > 8 ? 2 : 1;
+    }
+  } else {
+    p.stream = true;
+    p.KW = 1;
+    p.RT = R <= 32 ? 2 : 4;
+    if (vocab || logits) {
+      p.NT = 4;
+    } else if (NM == 2) {
+      p.NT = 2;
+    } else {
+      p.NT = (p.RT == 2 && K >= 8192) ? 1 : 2;
+    }
+    p.D = p.NT == 1 ? 8 : (NM == 2 && p.RT == 2 ? 8 : 4);
+    p.S = 1;
+    if (!logits) {
+      const int groups = (N + 64 * p.NT - 1) / (64 * p.NT) * ((R + 16 * p.RT - 1) / (16 * p.RT));
+      while (groups * p.S < 256 && K / (p.S * 2) >= 512) p.S *= 2;
+    }
+  }
+  if (logits) p.S = 1;
+  return p;
 }
 
 int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K) {
-  (void)K;
-  if (use_wide(R)) {
-    const int cols = 16 * wide_shape(R, 1).NT;
-    return (N + cols * WIDE_NW - 1) / (cols * WIDE_NW) * WIDE_NW;
-  }
-  return (N + 63) / 64;
+  const GemmPlan p = plan_gemm(R, N, K, 1, true);
+  const int cols = 16 * p.NT;
+  if (p.stream) return (N + cols * STREAM_NW - 1) / (cols * STREAM_NW) * STREAM_NW;
+  return (N + cols - 1) / cols;
 }
 
 template <int EPI>
@@ -533,68 +561,42 @@ static hipError_t launch_reduce(const GemmArgs& a, int S, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int RT, int NT, int EPI>
-static hipError_t launch_shape(const GemmArgs& a, hipStream_t st) {
+// K range per split: a multiple of `align`; returns the split count that
+// covers K (the requested one, possibly fewer).
+static int split_k(int K, int S, int align, int* kc) {
+  int c = (K + S - 1) / S;
+  c = (c + align - 1) / align * align;
+  *kc = c;
+  return (K + c - 1) / c;
+}
+
+template <int NT, int KW, int EPI>
+static hipError_t launch_per_wave(const GemmArgs& a, int S, hipStream_t st) {
   constexpr int NM = EpiTraits<EPI>::NM;
   const int n_tiles = (a.N + 16 * NT - 1) / (16 * NT);
-  const int r_groups = (a.R + 16 * RT - 1) / (16 * RT);
-  const int base = n_tiles * r_groups;
-  // Enough waves to cover the chip: when the column tiles alone give fewer
-  // than ~1024 waves, split K inside the workgroup (up to 4 waves, >= 256 k
-  // each) and then across workgroups (>= 512 k each) when the partials fit.
-  // LDS for the in-workgroup reduction stays within 64 KB.
-  const size_t lds_per_wave = (size_t)64 * NM * NT * RT * 4 * sizeof(float);
-  int KW = 1;
-  while (base * KW < 1024 && KW < 4 && a.K / (KW * 2) >= 256 &&
-         (size_t)(KW * 2 - 1) * lds_per_wave <= 65536)
-    KW *= 2;
-  int S = 1;
-  if (EPI != EPI_LOGITS) {
-    while (base * KW * S < 2048 && a.K / (S * 2) >= 512 &&
-           (size_t)(S * 2) * NM * a.R * a.N <= a.partials_cap)
-      S *= 2;
-  }
-  // Waves start on 64-k (two-tile) boundaries.
-  int kc = (a.K + S - 1) / S;
-  kc = (kc + 64 * KW - 1) / (64 * KW) * (64 * KW);
-  S = (a.K + kc - 1) / kc;
-  dim3 grid(n_tiles, S, r_groups);
-  size_t lds = KW > 1 ? (size_t)(KW - 1) * 64 * NM * NT * RT * 4 * sizeof(float) : 0;
-  switch (KW) {
-    case 1: gemm_kernel<RT, NT, 1, EPI><<<grid, 64, lds, st>>>(a, kc, S); break;
-    case 2: gemm_kernel<RT, NT, 2, EPI><<<grid, 128, lds, st>>>(a, kc, S); break;
-    default: gemm_kernel<RT, NT, 4, EPI><<<grid, 256, lds, st>>>(a, kc, S); break;
-  }
+  const int r_groups = (a.R + 15) / 16;
+  int kc;
+  S = split_k(a.K, S, 64 * KW, &kc);
+  if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 64 * KW, &kc);
+  const size_t lds = KW > 1 ? (size_t)(KW - 1) * 64 * NM * NT * 4 * sizeof(float) : 0;
+  gemm_kernel<1, NT, KW, EPI><<<dim3(n_tiles, S, r_groups), 64 * KW, lds, st>>>(a, kc, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   return launch_reduce<EPI>(a, S, st);
 }
 
-// The wide-row kernel over (column groups of 4 waves) x (K splits) x (row
-// groups). A K split is used only while the column groups alone leave the
-// chip short of workgroups and each split keeps >= 1024 k; the logits never
-// split (their argmax is fused).
 template <int RT, int NT, int D, int EPI>
-static hipError_t launch_wide(const GemmArgs& a, int S_force, hipStream_t st) {
+static hipError_t launch_stream(const GemmArgs& a, int S, hipStream_t st) {
   constexpr int NM = EpiTraits<EPI>::NM;
-  const int cols = 16 * NT * WIDE_NW;
+  const int cols = 16 * NT * STREAM_NW;
   const int n_groups = (a.N + cols - 1) / cols;
   const int r_groups = (a.R + 16 * RT - 1) / (16 * RT);
-  int S = 1;
-  if (S_force > 0) {
-    S = S_force;
-  } else if (EPI != EPI_LOGITS) {
-    while (n_groups * r_groups * S < 512 && a.K / (S * 2) >= 1024 &&
-           (size_t)(S * 2) * NM * a.R * a.N <= a.partials_cap)
-      S *= 2;
-  }
-  if (EPI == EPI_LOGITS) S = 1;
-  int kc = (a.K + S - 1) / S;
-  kc = (kc + 63) / 64 * 64;
-  S = (a.K + kc - 1) / kc;
-  if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) return hipErrorInvalidValue;
-  dim3 grid(n_groups, S, r_groups);
-  gemm_wide_kernel<RT, NT, D, EPI><<<grid, 64 * WIDE_NW, 0, st>>>(a, kc, S);
+  int kc;
+  S = split_k(a.K, S, 64, &kc);
+  if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 64, &kc);
+  const size_t lds = (size_t)D * RT * 4 * 1024;  // <= 64 KB for the shapes instantiated
+  gemm_stream_kernel<RT, NT, D, EPI><<<dim3(n_groups, S, r_groups), 64 * STREAM_NW, lds, st>>>(
+      a, kc, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   return launch_reduce<EPI>(a, S, st);
@@ -602,10 +604,25 @@ static hipError_t launch_wide(const GemmArgs& a, int S_force, hipStream_t st) {
 
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
-  if (!use_wide(a.R)) return launch_shape<1, 4, EPI>(a, st);
-  constexpr int NT = EpiTraits<EPI>::NM == 2 ? 2 : 4;
-  if (a.R <= 32) return launch_wide<2, NT, 4, EPI>(a, 0, st);
-  return launch_wide<4, NT, 4, EPI>(a, 0, st);
+  constexpr int NM = EpiTraits<EPI>::NM;
+  const GemmPlan p = plan_gemm(a.R, a.N, a.K, NM, EPI == EPI_LOGITS);
+  if (!p.stream) {
+#define PW(NT_, KW_) \
+  if (p.NT == NT_ && p.KW == KW_) return launch_per_wave<NT_, KW_, EPI>(a, p.S, st);
+    PW(1, 4) PW(1, 8) PW(2, 4) PW(2, 8) PW(4, 1)
+#undef PW
+    return launch_per_wave<2, 4, EPI>(a, p.S, st);
+  }
+#define ST(RT_, NT_, D_) \
+  if (p.RT == RT_ && p.NT == NT_ && p.D == D_) return launch_stream<RT_, NT_, D_, EPI>(a, p.S, st);
+  if constexpr (NM == 2) {
+    ST(2, 2, 8) ST(4, 2, 4)
+    return launch_stream<4, 2, 4, EPI>(a, p.S, st);
+  } else {
+    ST(2, 1, 8) ST(2, 2, 4) ST(2, 4, 4) ST(4, 2, 4) ST(4, 4, 4)
+    return launch_stream<4, 2, 4, EPI>(a, p.S, st);
+  }
+#undef ST
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {

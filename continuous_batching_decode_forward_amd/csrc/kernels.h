@@ -37,6 +37,11 @@ struct ModelDims {
   float rms_eps;
 };
 
+// Block-table entries one attention work item stages in LDS (a wave's
+// slice); split_len is capped so that a split spans at most this many
+// blocks.
+#define ATT_TBL 512
+
 // Attention work decomposition chosen by the host for one step.
 struct AttnPlan {
   int32_t split_len;   // keys per work item (multiple of 32)
