@@ -50,7 +50,41 @@ def step_bytes(shape, ctx, n_out):
 
 
 def lm_head_bytes(shape, n_out):
-    return shape.vocab * shape.d_model * 2 + n_out * shape.d_model * 2 + n_out * shape.vocab * 4
+    """LM head per launch: the bf16 weight once, the fp32 activation rows
+    (as their bf16 hi and lo halves) and the fp32 logits written."""
+    return shape.vocab * shape.d_model * 2 + n_out * shape.d_model * 4 + n_out * shape.vocab * 4
+
+
+# The dominant kernel's HBM traffic comes from rocprofv3 counter runs kept in
+# profiles/ (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by what the same
+# counters read for a device-to-device copy of known size). It is reported
+# only while the sources it was measured on are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_gemm_8b_b64_traffic.md")
+TRAFFIC_SOURCES = ["continuous_batching_decode_forward_amd/csrc/gemm.hip",
+                   "continuous_batching_decode_forward_amd/csrc/common.h",
+                   "continuous_batching_decode_forward_amd/csrc/kernels.h"]
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(batch):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith('{"traffic"'):
+                    rec = json.loads(line)["traffic"]
+                    if rec.get("sources") == sources_digest() and rec.get("batch") == batch:
+                        return rec["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def build_workload(shape, B, seed, device="cuda"):
@@ -163,7 +197,13 @@ def main():
     ap.add_argument("--sweep", default="1,8,32,64")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--print-sources-digest", action="store_true")
     args = ap.parse_args()
+    if args.print_sources_digest:
+        print(sources_digest())
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the step runs on a single MI355X and this "
@@ -179,6 +219,15 @@ def main():
     seed = 0
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 1073741824 bytes read, 1073741824 written")
+        del src, dst
+        torch.cuda.empty_cache()
     log(f"[bench] weights {shape.name} on GPU")
     wg = synth.make_weights(shape, seed=seed, device="cuda")
     Bmax = max([args.batch] + [int(b) for b in args.sweep.split(",") if b])
@@ -255,7 +304,8 @@ def main():
         "step_roofline_frac": gbs / PEAK_HBM_GBS,
         "roofline": {"bound": "hbm", "kernel": "lm_head_gemm", "achieved": lm_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": lm_gbs / PEAK_HBM_GBS,
-                     "traffic": None, "avg_launch_us": lm_ms * 1e3, "launches": lm_n,
+                     "traffic": measured_traffic(Bn), "avg_launch_us": lm_ms * 1e3,
+                     "launches": lm_n,
                      "bytes_per_launch": lm_bytes},
         "cpu_baseline": cpu,
         "sweep": sweep,
