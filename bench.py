@@ -87,15 +87,16 @@ def measured_traffic(batch):
     return None
 
 
-def build_workload(shape, B, seed, device="cuda"):
-    import torch
+def build_workload(shape, B, seed, ctx_range=(512, 4096), bs=32):
+    """B decode rows with contexts uniform in ctx_range (inclusive), their
+    blocks drawn from a seeded permutation of a pool that holds exactly
+    their contexts plus the appended position."""
     from continuous_batching_decode_forward_amd import synth
-    bs = 32
-    ctx = synth.uniform_ints(seed, "ctx", B, 512, 4096)
+    ctx = synth.uniform_ints(seed, "ctx", B, ctx_range[0], ctx_range[1])
     need = [-(-(int(c) + 1) // bs) for c in ctx]
     total = int(sum(need))
     perm = synth.permutation(seed, "blocks", total)
-    mbps = -(-4097 // bs)
+    mbps = -(-(ctx_range[1] + 1) // bs)
     tables = np.full((B, mbps), -1, np.int32)
     o = 0
     for i in range(B):
@@ -103,7 +104,7 @@ def build_workload(shape, B, seed, device="cuda"):
         o += need[i]
     tokens = synth.uniform_ints(seed, "tok", B, 0, shape.vocab - 1)
     return dict(bs=bs, ctx=ctx, tables=tables, perm=perm, total=total, mbps=mbps,
-                tokens=tokens)
+                tokens=tokens, max_position=ctx_range[1] + 1)
 
 
 def fill_pool(eng, seed, blocks):
@@ -188,6 +189,76 @@ def cpu_baseline(shape, wg, wl, seed, budget_s):
                       f"{spent:.1f} s of CPU work"}
 
 
+def penalty_history(seed, B, V, n_hist, decay):
+    """Per-row penalty counts after a seeded history of n_hist generated
+    tokens: each step c <- fl(c * decay), then c[token] += 1."""
+    from continuous_batching_decode_forward_amd import synth
+    counts = np.zeros((B, V), np.float32)
+    hist = synth.uniform_ints(seed, "history", B * n_hist, 0, V - 1).reshape(B, n_hist)
+    d = np.float32(decay)
+    rows = np.arange(B)
+    for t in range(n_hist):
+        counts *= d
+        counts[rows, hist[:, t]] += np.float32(1.0)
+    return counts
+
+
+def bench_sampled(args):
+    """The KV-dominated sampled step: one 8B-shaped layer + LM head over a
+    65536-token vocabulary, B = 256 decode rows with contexts uniform in
+    8192..32768, sampler T = 1.0, top_p = 0.3, top_k = 0, frequency penalty
+    1.0, decay 0.996 on a seeded 64-token history per row."""
+    import torch
+    from continuous_batching_decode_forward_amd import binding as B
+    from continuous_batching_decode_forward_amd import configs, synth
+    from continuous_batching_decode_forward_amd.engine import Engine
+    shape, wlc = configs.LLAMA8B_1L_V64K, configs.SAMPLE_8B_B256
+    seed, Bn = 0, wlc.batch[0]
+    stream = torch.cuda.current_stream()
+    log(f"[bench] weights {shape.name} on GPU")
+    wg = synth.make_weights(shape, seed=seed, device="cuda")
+    wl = build_workload(shape, Bn, seed, ctx_range=wlc.ctx_range, bs=wlc.block_size)
+    eng = Engine(shape, wg, block_size=wl["bs"], num_blocks=wl["total"],
+                 max_blocks_per_seq=wl["mbps"], max_slots=Bn, max_rows=Bn, max_seqs=Bn,
+                 max_position=wl["max_position"])
+    log(f"[bench] filling {wl['total']} KV blocks "
+        f"({wl['total'] * shape.kv_bytes_per_pos * wl['bs'] / 1e9:.1f} GB)")
+    fill_pool(eng, seed, wl["perm"])
+    sp = wlc.sampling
+    params = B.cbd_sampling()
+    params.temperature, params.top_p, params.top_k = sp.temperature, sp.top_p, sp.top_k
+    params.freq_penalty, params.presence_penalty = sp.freq_penalty, sp.presence_penalty
+    params.penalty_decay, params.seed = sp.penalty_decay, sp.seed
+    slots = [B.cbd_slot_alloc(eng.handle, params, r) for r in range(Bn)]
+    counts0 = torch.from_numpy(penalty_history(seed, Bn, shape.vocab, 64, sp.penalty_decay))
+    counts0 = counts0.to("cuda")
+    eng.slot_counts()[slots] = counts0
+    meta = eng.upload_step(slots=slots, block_tables=wl["tables"], ctx_lens=wl["ctx"],
+                           n_new=[1] * Bn, tokens=wl["tokens"], want_token=[1] * Bn,
+                           step_ids=[64] * Bn, mode=B.CBD_MODE_SAMPLE)
+    tk = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    ms, wall, kern = time_steps(eng, meta, None, tk, args.steps, args.warmup, stream)
+    times = {}
+    for name in ("ATTN", "LM_HEAD", "SAMPLE", "GATEUP", "DOWN", "QKV", "O"):
+        _, _, k = time_steps(eng, meta, None, tk, 5, 1, stream,
+                             profile_class=getattr(B, "CBD_KERNEL_" + name))
+        times[name.lower() + "_us"] = round(k[0] * 1e3, 1)
+    if eng.status():
+        raise RuntimeError("device status set")
+    byts = step_bytes(shape, wl["ctx"], Bn) + 3 * Bn * shape.vocab * 4  # + sampler state r/w
+    kv = sum((int(c) + 1) * shape.kv_bytes_per_pos for c in wl["ctx"])
+    out = {"workload": wlc.name, "batch": Bn, "ctx_range": list(wlc.ctx_range),
+           "ms_per_step": ms, "tokens_per_s": Bn / (ms * 1e-3),
+           "step_algorithmic_bytes": byts, "hbm_gbs": byts / (ms * 1e-3) / 1e9,
+           "roofline_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+           "kv_bytes": kv, "attention_gbs": kv / (times["attn_us"] * 1e-6) / 1e9,
+           "sampler_gbs": 3 * Bn * shape.vocab * 4 / (times["sample_us"] * 1e-6) / 1e9,
+           "kernel_us": times}
+    eng.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +271,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--print-sources-digest", action="store_true")
+    ap.add_argument("--workload", default="8b-layer+lmhead-decode",
+                    choices=["8b-layer+lmhead-decode", "8b-layer+lmhead65536-b256-sampled"],
+                    help="the headline decode sweep (default) or another configured workload")
     args = ap.parse_args()
     if args.print_sources_digest:
         print(sources_digest())
@@ -214,6 +288,10 @@ def main():
     from continuous_batching_decode_forward_amd import binding as B
     from continuous_batching_decode_forward_amd import configs, synth
     from continuous_batching_decode_forward_amd.engine import Engine
+
+    if args.workload != "8b-layer+lmhead-decode":
+        torch.cuda.set_device(0)
+        return bench_sampled(args)
 
     shape = configs.LLAMA8B_1L
     seed = 0

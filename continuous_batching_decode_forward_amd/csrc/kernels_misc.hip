@@ -313,23 +313,27 @@ hipError_t launch_rope_append(const float* qkv, int32_t R, const StepMeta& m, co
 
 // ---------------------------------------------------------- argmax combine
 //
-// One wave per row: the maximum over the per-tile partials, lowest id on
-// equal values (ids are unique per partial, so the order is total).
+// One workgroup of 256 threads per row: the maximum over the per-tile
+// partials, lowest id on equal values (ids are unique per partial, so the
+// order is total). Each thread scans a strided share, the four waves reduce
+// by shuffles and then through LDS.
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-__global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* __restrict__ val,
-                                                           const int32_t* __restrict__ idx,
-                                                           int n_tiles, int stride,
-                                                           int32_t* __restrict__ tokens) {
+__global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* __restrict__ val,
+                                                            const int32_t* __restrict__ idx,
+                                                            int n_tiles, int stride,
+                                                            int32_t* __restrict__ tokens) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
   const int j = blockIdx.x;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int t = threadIdx.x; t < n_tiles; t += 64) {
-    float v = val[(size_t)j * stride + t];
-    int i = idx[(size_t)j * stride + t];
+  for (int t = threadIdx.x; t < n_tiles; t += 256) {
+    const float v = val[(size_t)j * stride + t];
+    const int i = idx[(size_t)j * stride + t];
     if (better(v, i, bv, bi)) {
       bv = v;
       bi = i;
@@ -337,20 +341,32 @@ __global__ __launch_bounds__(64) void argmax_reduce_kernel(const float* __restri
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    float v = __shfl_xor(bv, o, 64);
-    int i = __shfl_xor(bi, o, 64);
+    const float v = __shfl_xor(bv, o, 64);
+    const int i = __shfl_xor(bi, o, 64);
     if (better(v, i, bv, bi)) {
       bv = v;
       bi = i;
     }
   }
-  if (threadIdx.x == 0) tokens[j] = bi == 0x7fffffff ? 0 : bi;
+  if ((threadIdx.x & 63) == 0) {
+    sv[threadIdx.x >> 6] = bv;
+    si[threadIdx.x >> 6] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], bv, bi)) {
+        bv = sv[w];
+        bi = si[w];
+      }
+    tokens[j] = bi == 0x7fffffff ? 0 : bi;
+  }
 }
 
 hipError_t launch_argmax_reduce(const float* amax_val, const int32_t* amax_idx, int32_t n_tiles,
                                 int32_t stride, int32_t n, int32_t* tokens, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  argmax_reduce_kernel<<<n, 64, 0, st>>>(amax_val, amax_idx, n_tiles, stride, tokens);
+  argmax_reduce_kernel<<<n, 256, 0, st>>>(amax_val, amax_idx, n_tiles, stride, tokens);
   return hipGetLastError();
 }
 

@@ -14,15 +14,21 @@
 //      in ascending id order whose running kept mass exceeds r
 //   S7 c = c * decay for every id, then c[token] += 1
 //
-// One workgroup of 1024 threads per row. Thread t owns the contiguous ids
-// [t*PER, (t+1)*PER), so every ascending-id question (the CDF of S6, ties at
-// a threshold) is one block scan of per-thread totals. The row's e values
-// live in a workspace scratch row (L2-resident) between passes; dropped ids
-// hold -1. Top-k and top-p thresholds come from a radix select on the bit
-// patterns of e (non-negative floats order like their bits): four 8-bit
-// passes over LDS histograms, counting ids for top-k and summing mass for
-// top-p; ties at the threshold are kept in ascending id order. No sort of
-// the vocabulary.
+// One workgroup of 1024 threads (16 waves) per row. Wave w owns the
+// contiguous ids [w*C, (w+1)*C), C = 64*K, and lane l of it takes ids
+// w*C + 64k + l, k = 0..K-1: every global access is coalesced, and the
+// ascending-id order is (wave, k, lane), so ascending-id questions (the CDF
+// of S6, ties at a threshold) take a ballot or a wave prefix per k plus a
+// prefix over the 16 waves. The row's e values live in a workspace row
+// (indexed by id, L2-resident between passes; 64 values per thread do not
+// fit the 128 registers a 1024-thread workgroup leaves); dropped ids hold
+// -1. Top-k and top-p thresholds come from a
+// bisection over the bit patterns of e (non-negative floats order like
+// their bits): each step one count or mass sum over the row, with no atomics
+// and no sort; ties at the threshold are kept in ascending id order.
+// Masses (S4-S6) accumulate in double, so the decisions are those of the
+// exact sums up to rounding of order 1e-16; the fp32 products of S1 and S7
+// are rounded before the following add (no fused multiply-add), as written.
 #include "common.h"
 #include "kernels.h"
 
@@ -58,24 +64,29 @@ __device__ __forceinline__ float draw_uniform24(uint64_t seed, uint64_t request_
 // ------------------------------------------------------- block reductions
 
 struct SmpShared {
+  double red_d[SMP_WAVES];
+  double wave_d[SMP_WAVES];
   float red_f[SMP_WAVES];
   int red_i[SMP_WAVES];
-  float scan_f[SMP_THREADS];
-  int scan_i[SMP_THREADS];
-  unsigned hist_cnt[256];
-  float hist_mass[256];
-  unsigned sel_digit;
-  unsigned sel_above_cnt;
-  float sel_above_mass;
+  int wave_i[SMP_WAVES];
 };
 
-__device__ float smp_block_sum(float v, SmpShared& sh) {
-  v = wave_sum(v);
-  if ((threadIdx.x & 63) == 0) sh.red_f[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float s = 0.f;
+// An fp32 product rounded on its own: the empty asm hides it from
+// contraction into a following add.
+__device__ __forceinline__ float mul_rounded(float a, float b) {
+  float t = a * b;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+__device__ double smp_block_sum_d(double v, SmpShared& sh) {
 #pragma unroll
-  for (int w = 0; w < SMP_WAVES; ++w) s += sh.red_f[w];
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) sh.red_d[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < SMP_WAVES; ++w) s += sh.red_d[w];
   __syncthreads();
   return s;
 }
@@ -87,6 +98,18 @@ __device__ float smp_block_max(float v, SmpShared& sh) {
   float s = -INFINITY;
 #pragma unroll
   for (int w = 0; w < SMP_WAVES; ++w) s = fmaxf(s, sh.red_f[w]);
+  __syncthreads();
+  return s;
+}
+
+__device__ int smp_block_sum_i(int v, SmpShared& sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) sh.red_i[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int w = 0; w < SMP_WAVES; ++w) s += sh.red_i[w];
   __syncthreads();
   return s;
 }
@@ -115,139 +138,251 @@ __device__ int smp_block_max_i(int v, SmpShared& sh) {
   return s;
 }
 
-// Exclusive prefix over threads, in thread order (Hillis-Steele).
-__device__ float smp_excl_scan_f(float v, SmpShared& sh) {
-  const int t = threadIdx.x;
-  sh.scan_f[t] = v;
-  __syncthreads();
-  for (int o = 1; o < SMP_THREADS; o <<= 1) {
-    float add = t >= o ? sh.scan_f[t - o] : 0.f;
-    __syncthreads();
-    sh.scan_f[t] += add;
-    __syncthreads();
-  }
-  float r = sh.scan_f[t] - v;
-  __syncthreads();
-  return r;
-}
-
-__device__ int smp_excl_scan_i(int v, SmpShared& sh) {
-  const int t = threadIdx.x;
-  sh.scan_i[t] = v;
-  __syncthreads();
-  for (int o = 1; o < SMP_THREADS; o <<= 1) {
-    int add = t >= o ? sh.scan_i[t - o] : 0;
-    __syncthreads();
-    sh.scan_i[t] += add;
-    __syncthreads();
-  }
-  int r = sh.scan_i[t] - v;
-  __syncthreads();
-  return r;
-}
-
-// Radix select over the bit patterns of the kept e values (e >= 0) of the
-// row; each thread reads its own ids [id0, id0 + per) from the scratch row.
-// BY_MASS = false: the largest pattern tau with count(e >= tau) >= need.
-// BY_MASS = true:  the largest pattern tau with mass(e >= tau) >= need.
-// Also returns what lies strictly above tau (count and mass).
-template <bool BY_MASS>
-__device__ uint32_t radix_select(const float* __restrict__ e, int id0, int per, float need,
-                                 SmpShared& sh, unsigned* above_cnt, float* above_mass) {
-  uint32_t prefix = 0;
-  unsigned acnt = 0;
-  float amass = 0.f;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = threadIdx.x; b < 256; b += SMP_THREADS) {
-      sh.hist_cnt[b] = 0;
-      sh.hist_mass[b] = 0.f;
-    }
-    __syncthreads();
-    const uint32_t hmask = shift == 24 ? 0u : (0xffffffffu << (shift + 8));
-    for (int i = 0; i < per; i += 4) {
-      const float4 v4 = *reinterpret_cast<const float4*>(e + id0 + i);
-      const float vs[4] = {v4.x, v4.y, v4.z, v4.w};
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float v = vs[k];
-        const uint32_t bits = __float_as_uint(v);
-        if (v >= 0.f && (bits & hmask) == prefix) {
-          const uint32_t dgt = (bits >> shift) & 255u;
-          if (BY_MASS)
-            atomicAdd(&sh.hist_mass[dgt], v);
-          else
-            atomicAdd(&sh.hist_cnt[dgt], 1u);
-        }
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      unsigned c = acnt;
-      float ms = amass;
-      int d = 255;
-      for (; d > 0; --d) {
-        bool reach = BY_MASS ? (ms + sh.hist_mass[d] >= need)
-                             : (c + sh.hist_cnt[d] >= (unsigned)need);
-        if (reach) break;
-        c += sh.hist_cnt[d];
-        ms += sh.hist_mass[d];
-      }
-      sh.sel_digit = (unsigned)d;
-      sh.sel_above_cnt = c;
-      sh.sel_above_mass = ms;
-    }
-    __syncthreads();
-    prefix |= sh.sel_digit << shift;
-    acnt = sh.sel_above_cnt;
-    amass = sh.sel_above_mass;
-    __syncthreads();
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
   }
-  *above_cnt = acnt;
-  *above_mass = amass;
-  return prefix;
+  return v;
 }
 
-// Keep ids with e above tau and the first eq_keep ids (ascending id order)
-// whose e equals tau; drop the rest (e = -1). Returns the kept mass of this
-// thread's ids.
-__device__ float keep_threshold(float* __restrict__ e, int id0, int per, uint32_t tau,
-                                int eq_keep, SmpShared& sh) {
-  int eq_own = 0;
-  for (int i = 0; i < per; ++i) {
-    const float v = e[id0 + i];
-    if (v >= 0.f && __float_as_uint(v) == tau) ++eq_own;
+// The per-thread row values: registers for K <= SMP_KREG, else the
+// workspace row (coalesced, indexed by id).
+#define SMP_KREG 64
+
+// Loops over a thread's K values: with registers the bound is the constant
+// SMP_KREG (fully unrolled, so the array is indexed statically) and the
+// iterations past K are skipped.
+#define SMP_FOR_K(k)                                                   \
+  _Pragma("unroll") for (int k = 0; k < (REGS ? SMP_KREG : K); ++k) \
+    if (!REGS || k < K)
+
+template <bool REGS>
+struct RowVals {
+  float r[REGS ? SMP_KREG : 1];
+  float* g;  // workspace row base (ids), used when !REGS
+  __device__ __forceinline__ float get(int k, int id) const {
+    if constexpr (REGS) return r[k];
+    else return g[id];
   }
-  int eq_before = smp_excl_scan_i(eq_own, sh);
-  float own = 0.f;
-  for (int i = 0; i < per; ++i) {
-    const float v = e[id0 + i];
-    if (!(v >= 0.f)) continue;
-    const uint32_t b = __float_as_uint(v);
-    bool keep = b > tau;
-    if (b == tau) {
-      keep = eq_before < eq_keep;
-      ++eq_before;
+  __device__ __forceinline__ void set(int k, int id, float v) {
+    if constexpr (REGS) r[k] = v;
+    else g[id] = v;
+  }
+};
+
+// Largest bit pattern tau (non-negative floats) with F(tau) >= need, where
+// F(tau) = count (BY_MASS false) or mass (true) of the kept values >= tau.
+// Bisection between the smallest and largest kept pattern; each step is one
+// reduction over the row.
+template <bool BY_MASS, bool REGS>
+__device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K, int base, double need,
+                                  SmpShared& sh) {
+  uint32_t lo = 0x7f800000u, hi = 0u;
+  SMP_FOR_K(k) {
+    const float v = e.get(k, base + 64 * k);
+    if (v >= 0.f) {
+      lo = min(lo, __float_as_uint(v));
+      hi = max(hi, __float_as_uint(v));
     }
+  }
+  lo = (uint32_t)-smp_block_max_i(-(int)lo, sh);  // block min (patterns < 2^31)
+  hi = (uint32_t)smp_block_max_i((int)hi, sh) + 1u;  // F(hi) = 0 < need
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + (hi - lo) / 2u;
+    double f = 0.0;
+    int c = 0;
+    SMP_FOR_K(k) {
+      const float v = e.get(k, base + 64 * k);
+      if (v >= 0.f && __float_as_uint(v) >= mid) {
+        if (BY_MASS) f += v;
+        else ++c;
+      }
+    }
+    const bool ok = BY_MASS ? (smp_block_sum_d(f, sh) >= need) : (smp_block_sum_i(c, sh) >= (int)need);
+    if (ok)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// Keep the values above tau and the first eq_keep values equal to tau in
+// ascending id order; drop the rest (-1). Returns this thread's kept mass.
+template <bool REGS>
+__device__ __forceinline__ double smp_keep(RowVals<REGS>& e, int K, int base, uint32_t tau, int eq_keep,
+                          SmpShared& sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int eq_wave = 0;  // equals in this wave's range (same in every lane)
+  SMP_FOR_K(k) {
+    const float v = e.get(k, base + 64 * k);
+    eq_wave += __popcll(__ballot(v >= 0.f && __float_as_uint(v) == tau));
+  }
+  if (lane == 0) sh.wave_i[w] = eq_wave;
+  __syncthreads();
+  int eq_before = 0;
+  for (int x = 0; x < w; ++x) eq_before += sh.wave_i[x];
+  __syncthreads();
+  double own = 0.0;
+  SMP_FOR_K(k) {
+    const int id = base + 64 * k;
+    const float v = e.get(k, id);
+    const bool is_eq = v >= 0.f && __float_as_uint(v) == tau;
+    const uint64_t m = __ballot(is_eq);
+    bool keep = v >= 0.f && __float_as_uint(v) > tau;
+    if (is_eq) keep = eq_before + __popcll(m & below) < eq_keep;
+    eq_before += __popcll(m);
     if (keep)
       own += v;
-    else
-      e[id0 + i] = -1.f;
+    else if (v >= 0.f)
+      e.set(k, id, -1.f);
   }
   return own;
 }
 
+template <bool REGS>
+__device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, float* __restrict__ crow,
+                            float* __restrict__ scratch_row, int V, int K, const SlotParams& P,
+                            uint32_t step, int32_t* __restrict__ token_out, SmpShared& sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int base = w * 64 * K + lane;  // this thread's id at k = 0; ids step by 64
+  RowVals<REGS> e;
+  e.g = scratch_row;
+
+  // S1 penalties (+ S2 division)
+  float zmax = -INFINITY;
+  SMP_FOR_K(k) {
+    const int id = base + 64 * k;
+    float z = -INFINITY;
+    if (id < V) {
+      const float c = crow[id];
+      float l = lrow[id] - mul_rounded(P.freq_penalty, c);
+      if (c > 0.f) l = l - P.presence_penalty;
+      z = P.temperature == 0.f ? l : l / P.temperature;
+    }
+    e.set(k, id, z);
+    zmax = fmaxf(zmax, z);
+  }
+  zmax = smp_block_max(zmax, sh);
+  int token;
+  if (P.temperature == 0.f) {  // greedy on the penalised logits, lowest id
+    int cand = 0x7fffffff;
+    SMP_FOR_K(k) {
+      const int id = base + 64 * k;
+      if (id < V && e.get(k, id) == zmax) cand = min(cand, id);
+    }
+    token = smp_block_min_i(cand, sh);
+    if (token == 0x7fffffff) token = 0;
+  } else {
+    // S3
+    double own = 0.0;
+    SMP_FOR_K(k) {
+      const int id = base + 64 * k;
+      float v = -1.f;
+      if (id < V) {
+        v = expf(e.get(k, id) - zmax);
+        own += v;
+      }
+      e.set(k, id, v);
+    }
+    double sum_k = smp_block_sum_d(own, sh);
+    // S4 top-k
+    if (P.top_k > 0 && P.top_k < V) {
+      const uint32_t tau = smp_threshold<false>(e, K, base, (float)P.top_k, sh);
+      int above = 0;
+      SMP_FOR_K(k) {
+        const float v = e.get(k, base + 64 * k);
+        if (v >= 0.f && __float_as_uint(v) > tau) ++above;
+      }
+      above = smp_block_sum_i(above, sh);
+      own = smp_keep(e, K, base, tau, P.top_k - above, sh);
+      sum_k = smp_block_sum_d(own, sh);
+    }
+    // S5 top-p
+    if (P.top_p < 1.f) {
+      const double target = (double)P.top_p * sum_k;
+      const uint32_t tau = smp_threshold<true>(e, K, base, target, sh);
+      const double tauf = (double)__uint_as_float(tau);
+      double above = 0.0;
+      SMP_FOR_K(k) {
+        const float v = e.get(k, base + 64 * k);
+        if (v >= 0.f && __float_as_uint(v) > tau) above += v;
+      }
+      above = smp_block_sum_d(above, sh);
+      // ids equal to tau needed to reach the target, in ascending id order
+      const double need = target - above;
+      int eq_keep = 1;
+      if (tauf > 0.0 && need > tauf) eq_keep = (int)ceil(need / tauf);
+      own = smp_keep(e, K, base, tau, eq_keep, sh);
+    }
+    // S6 draw over the ascending-id CDF of the kept mass
+    double wsum = own;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
+    if (lane == 0) sh.wave_d[w] = wsum;
+    __syncthreads();
+    double total = 0.0, prefix = 0.0;
+#pragma unroll
+    for (int x = 0; x < SMP_WAVES; ++x) {
+      if (x < w) prefix += sh.wave_d[x];
+      total += sh.wave_d[x];
+    }
+    __syncthreads();
+    const float u = draw_uniform24(P.seed, P.request_id, step);
+    const double r = (double)u * total;
+    int cand = 0x7fffffff, last = -1;
+    if (prefix + wsum > r) {  // this wave's range reaches past r
+      double carry = prefix;
+      SMP_FOR_K(k) {
+        const int id = base + 64 * k;
+        const float v = e.get(k, id);
+        const double kv = v >= 0.f ? (double)v : 0.0;
+        const double run = carry + wave_incl_scan(kv);
+        const uint64_t hit = __ballot(v >= 0.f && run > r);
+        if (hit) {
+          const int first = __ffsll((long long)hit) - 1;
+          cand = base - lane + 64 * k + first;
+          break;
+        }
+        carry = __shfl(run, 63, 64);  // run already holds carry
+      }
+    }
+    SMP_FOR_K(k) {
+      const int id = base + 64 * k;
+      if (e.get(k, id) >= 0.f) last = id;
+    }
+    token = smp_block_min_i(cand, sh);
+    if (token == 0x7fffffff) token = smp_block_max_i(last, sh);
+    if (token < 0) token = 0;
+  }
+  // S7 counts: decay every id, then count the token
+  SMP_FOR_K(k) {
+    const int id = base + 64 * k;
+    if (id < V) {
+      float c = mul_rounded(crow[id], P.penalty_decay);
+      if (id == token) c = c + 1.0f;
+      crow[id] = c;
+    }
+  }
+  if (threadIdx.x == 0) *token_out = token;
+}
+
 __global__ __launch_bounds__(SMP_THREADS) void sampler_kernel(
-    const float* __restrict__ logits, int V, int per, const int32_t* __restrict__ slots,
+    const float* __restrict__ logits, int V, int K, const int32_t* __restrict__ slots,
     const int32_t* __restrict__ step_ids, const int32_t* __restrict__ out_seq,
     const SlotParams* __restrict__ params, float* __restrict__ counts, int max_slots,
     float* __restrict__ scratch, int32_t* __restrict__ tokens, uint32_t* status) {
   __shared__ SmpShared sh;
   const int j = blockIdx.x;
-  const int t = threadIdx.x;
   const int sidx = out_seq ? out_seq[j] : j;
   const int slot = slots[sidx];
   if (slot < 0 || slot >= max_slots) {
-    if (t == 0) {
+    if (threadIdx.x == 0) {
       raise_status(status, ST_BAD_SLOT);
       tokens[j] = 0;
     }
@@ -257,99 +392,13 @@ __global__ __launch_bounds__(SMP_THREADS) void sampler_kernel(
   const uint32_t step = (uint32_t)step_ids[sidx];
   const float* lrow = logits + (size_t)j * V;
   float* crow = counts + (size_t)slot * V;
-  float* e = scratch + (size_t)j * per * SMP_THREADS;
-  const int id0 = t * per;
-
-  // S1 penalties (+ S2 division), into the scratch row
-  float zmax = -INFINITY;
-  for (int i = 0; i < per; ++i) {
-    const int id = id0 + i;
-    float z = -INFINITY;
-    if (id < V) {
-      const float c = crow[id];
-      float l = lrow[id] - P.freq_penalty * c;
-      if (c > 0.f) l = l - P.presence_penalty;
-      z = P.temperature == 0.f ? l : l / P.temperature;
-    }
-    e[id] = z;
-    zmax = fmaxf(zmax, z);
-  }
-  zmax = smp_block_max(zmax, sh);
-  int token;
-  if (P.temperature == 0.f) {  // greedy on the penalised logits, lowest id
-    int cand = 0x7fffffff;
-    for (int i = per - 1; i >= 0; --i)
-      if (id0 + i < V && e[id0 + i] == zmax) cand = id0 + i;
-    token = smp_block_min_i(cand, sh);
-    if (token == 0x7fffffff) token = 0;
-  } else {
-    // S3
-    float own = 0.f;
-    for (int i = 0; i < per; ++i) {
-      const int id = id0 + i;
-      float v = -1.f;
-      if (id < V) {
-        v = expf(e[id] - zmax);
-        own += v;
-      }
-      e[id] = v;
-    }
-    float sum_k = smp_block_sum(own, sh);
-    // S4 top-k
-    if (P.top_k > 0 && P.top_k < V) {
-      unsigned above;
-      float unused;
-      const uint32_t tau = radix_select<false>(e, id0, per, (float)P.top_k, sh, &above, &unused);
-      own = keep_threshold(e, id0, per, tau, P.top_k - (int)above, sh);
-      sum_k = smp_block_sum(own, sh);
-    }
-    // S5 top-p
-    if (P.top_p < 1.f) {
-      const float target = P.top_p * sum_k;
-      unsigned unused_c;
-      float above_mass;
-      const uint32_t tau = radix_select<true>(e, id0, per, target, sh, &unused_c, &above_mass);
-      const float tauf = __uint_as_float(tau);
-      // ids equal to tau needed to reach the target, in ascending id order
-      const float need = target - above_mass;
-      int eq_keep = 1;
-      if (tauf > 0.f && need > tauf) eq_keep = (int)ceilf(need / tauf);
-      own = keep_threshold(e, id0, per, tau, eq_keep, sh);
-    }
-    // S6 draw over the ascending-id CDF of the kept mass
-    const float total = smp_block_sum(own, sh);
-    const float excl = smp_excl_scan_f(own, sh);
-    const float u = draw_uniform24(P.seed, P.request_id, step);
-    const float r = u * total;
-    int cand = 0x7fffffff, last = -1;
-    float run = excl;
-    for (int i = 0; i < per; ++i) {
-      const float v = e[id0 + i];
-      if (!(v >= 0.f)) continue;
-      run += v;
-      last = id0 + i;
-      if (run > r) {
-        cand = id0 + i;
-        break;
-      }
-    }
-    token = smp_block_min_i(cand, sh);
-    if (token == 0x7fffffff) token = smp_block_max_i(last, sh);
-    if (token < 0) token = 0;
-  }
-  // S7 counts: decay every id, then count the token
-  for (int id = t; id < V; id += SMP_THREADS) {
-    float c = crow[id] * P.penalty_decay;
-    if (id == token) c = c + 1.0f;
-    crow[id] = c;
-  }
-  if (t == 0) tokens[j] = token;
+  float* srow = scratch + (size_t)j * K * SMP_THREADS;
+  sampler_row<false>(lrow, crow, srow, V, K, P, step, tokens + j, sh);
 }
 
 int32_t sampler_row_floats(int32_t V) {
-  int per = (V + SMP_THREADS - 1) / SMP_THREADS;
-  per = (per + 3) / 4 * 4;
-  return per * SMP_THREADS;
+  const int K = (V + SMP_THREADS - 1) / SMP_THREADS;
+  return K * SMP_THREADS;
 }
 
 hipError_t launch_sampler(const float* logits, int32_t n, int32_t V, const int32_t* slots,
@@ -357,8 +406,8 @@ hipError_t launch_sampler(const float* logits, int32_t n, int32_t V, const int32
                           float* counts, int32_t max_slots, float* scratch, int32_t* tokens,
                           uint32_t* status, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  const int per = sampler_row_floats(V) / SMP_THREADS;
-  sampler_kernel<<<n, SMP_THREADS, 0, st>>>(logits, V, per, slots, step_ids, out_seq, params,
+  const int K = sampler_row_floats(V) / SMP_THREADS;
+  sampler_kernel<<<n, SMP_THREADS, 0, st>>>(logits, V, K, slots, step_ids, out_seq, params,
                                              counts, max_slots, scratch, tokens, status);
   return hipGetLastError();
 }

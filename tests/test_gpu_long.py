@@ -1,0 +1,113 @@
+"""The KV-dominated sampled step at full size: one 8B-shaped layer + LM head
+over a 65536-token vocabulary, 256 decode rows with contexts uniform in
+8192..32768 (21.5 GB of cached K/V in a shuffled 32-position block pool),
+sampler T = 1.0, top_p = 0.3, top_k = 0, frequency penalty 1.0, decay 0.996
+on a seeded 64-token history per row.
+
+Checks at this size:
+  * the rows with the three shortest contexts: logits within the stated
+    tolerance of the oracle (|d| <= 2e-2 + 1e-2 |ref|), computed row by row;
+  * every row: the sampled token lies in the top-p set of its own penalised
+    distribution (computed here in plain numpy from the step's logits, a
+    property any correct sampler output has), unless the running mass
+    passes top_p within the fp32 summation error of the cut;
+  * every row: the penalty counts became fl(c * decay), then + 1 at the
+    sampled token, bit for bit;
+  * the device status stays clear.
+The sampler's exact token choice is pinned separately on identical logits
+(test_gpu_sampler.py)."""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import oracle as O
+from continuous_batching_decode_forward_amd import binding as B
+from continuous_batching_decode_forward_amd import configs, synth
+from continuous_batching_decode_forward_amd.engine import Engine
+
+from gpu_util import compare_logits, oracle_pool
+
+pytestmark = pytest.mark.gpu
+
+SHAPE = configs.LLAMA8B_1L_V64K
+WL = configs.SAMPLE_8B_B256
+
+
+def top_p_set(logits, counts, sp):
+    """Indices of the top-p kept set (by penalised probability, descending)
+    and the running mass at each kept position, in float64."""
+    lp = logits.astype(np.float64) - sp.freq_penalty * counts - sp.presence_penalty * (counts > 0)
+    z = lp / sp.temperature
+    p = np.exp(z - z.max())
+    order = np.lexsort((np.arange(len(p)), -p))
+    cum = np.cumsum(p[order])
+    total = cum[-1]
+    cut = int(np.searchsorted(cum, sp.top_p * total)) + 1
+    return order, cum / total, cut
+
+
+def test_sampled_b256_long_contexts():
+    torch.cuda.set_device(0)
+    seed, Bn = 3, WL.batch[0]
+    wg = synth.make_weights(SHAPE, seed=seed, device="cuda")
+    wl = bench.build_workload(SHAPE, Bn, seed, ctx_range=WL.ctx_range, bs=WL.block_size)
+    eng = Engine(SHAPE, wg, block_size=wl["bs"], num_blocks=wl["total"],
+                 max_blocks_per_seq=wl["mbps"], max_slots=Bn, max_rows=Bn, max_seqs=Bn,
+                 max_position=wl["max_position"])
+    try:
+        bench.fill_pool(eng, seed, wl["perm"])
+        sp = WL.sampling
+        params = B.cbd_sampling()
+        params.temperature, params.top_p, params.top_k = sp.temperature, sp.top_p, sp.top_k
+        params.freq_penalty, params.presence_penalty = sp.freq_penalty, sp.presence_penalty
+        params.penalty_decay, params.seed = sp.penalty_decay, sp.seed
+        slots = [B.cbd_slot_alloc(eng.handle, params, r) for r in range(Bn)]
+        c0 = bench.penalty_history(seed, Bn, SHAPE.vocab, 64, sp.penalty_decay)
+        eng.slot_counts()[slots] = torch.from_numpy(c0).cuda()
+        meta = eng.upload_step(slots=slots, block_tables=wl["tables"], ctx_lens=wl["ctx"],
+                               n_new=[1] * Bn, tokens=wl["tokens"], want_token=[1] * Bn,
+                               step_ids=[64] * Bn, mode=B.CBD_MODE_SAMPLE)
+        lg = torch.empty((Bn, SHAPE.vocab), dtype=torch.float32, device="cuda")
+        tk = torch.empty(Bn, dtype=torch.int32, device="cuda")
+        eng.step_forward(meta, lg, tk)
+        torch.cuda.synchronize()
+        assert eng.status() == 0
+        g_lg = lg.cpu().numpy()
+        g_tk = tk.cpu().numpy()
+        c1 = eng.slot_counts()[slots].cpu().numpy()
+    finally:
+        eng.close()
+
+    # counts: decay then +1, exactly
+    want = c0 * np.float32(sp.penalty_decay)
+    want[np.arange(Bn), g_tk] += np.float32(1.0)
+    assert np.array_equal(c1, want)
+
+    # every token lies inside its row's top-p set (away from the cut)
+    checked = 0
+    for i in range(Bn):
+        order, cum, cut = top_p_set(g_lg[i], c0[i].astype(np.float64), sp)
+        pos = int(np.nonzero(order == g_tk[i])[0][0])
+        # the cut is ambiguous only where the running mass passes top_p
+        # within the summation error (fp32 sums over 65536 terms: ~1e-6)
+        edge = abs(cum[cut - 1] - sp.top_p) < 2e-6 or (cut >= 2 and abs(cum[cut - 2] - sp.top_p) < 2e-6)
+        if edge:
+            continue
+        checked += 1
+        assert pos < cut, f"row {i}: token {g_tk[i]} is outside the top-p set"
+    assert checked >= Bn * 0.9
+
+    # logits of the three shortest-context rows against the oracle
+    rows = [int(r) for r in np.argsort(wl["ctx"])[:3]]
+    wc = {k: ([t.cpu() for t in v] if isinstance(v, list) else v.cpu()) for k, v in wg.items()}
+    model = O.Model(SHAPE, wc)
+    tabs = [wl["tables"][i] for i in rows]
+    cached = [int(wl["ctx"][i]) for i in rows]
+    pool, compact = oracle_pool(SHAPE, seed, tabs, cached, wl["bs"], [1] * len(rows))
+    ref_lg, _ = O.paged_step(model, pool, compact, cached, [1] * len(rows),
+                             [int(wl["tokens"][i]) for i in rows], [1] * len(rows))
+    ok, mx, _ = compare_logits(g_lg[rows], ref_lg)
+    print(f"long sampled step: max abs logit error {mx:.2e} on rows with ctx {cached}; "
+          f"{checked}/{Bn} tokens checked against their top-p sets")
+    assert ok, f"max abs logit error {mx:.3g}"
