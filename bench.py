@@ -259,6 +259,89 @@ def bench_sampled(args):
     print(json.dumps(out), flush=True)
 
 
+def cb_requests(seed, n, vocab, prompt_range=(16, 512), new_range=(2, 300)):
+    """A seeded closed-loop request stream: prompt lengths and answer budgets
+    uniform in the given ranges, prompt ids uniform over the vocabulary."""
+    from continuous_batching_decode_forward_amd import synth
+    lens = synth.uniform_ints(seed, "plen", n, *prompt_range)
+    news = synth.uniform_ints(seed, "maxnew", n, *new_range)
+    return [(i, synth.uniform_ints(seed, f"prompt{i}", int(lens[i]), 0, vocab - 1),
+             int(news[i])) for i in range(n)]
+
+
+def bench_cb2b(args):
+    """Continuous batching on the full 2B-shaped decoder (28 layers, d_model
+    2048, 16/8 heads, FFN 6144, vocab 151936): B slots, prompts 16..512,
+    answers 2..300 tokens (EOS id 0), 32-position blocks, 16 blocks per slot,
+    answer blocks reserved at admission, 512-token chunks, 512 + B rows per
+    step, a closed-loop queue (never empty), greedy. Each step is one native
+    cbd_sched_step (plan, upload, step, tokens back, commit), timed on the
+    host clock around the call."""
+    import torch
+    from continuous_batching_decode_forward_amd import configs, synth
+    from continuous_batching_decode_forward_amd.engine import ComposerLoop, Engine
+    shape, wlc = configs.QWEN2B, configs.CB_2B
+    seed, bs, chunk = 0, wlc.block_size, 512
+    n_steps = args.cb_steps
+    log(f"[bench] weights {shape.name} on GPU")
+    wg = synth.make_weights(shape, seed=seed, device="cuda")
+    mbps = -(-(wlc.ctx_range[1] + 300) // bs)
+    for Bn in [int(b) for b in args.cb_slots.split(",")]:
+        pool = 16 * Bn
+        order = synth.permutation(seed, "blocks", pool).astype(np.int32)
+        eng = Engine(shape, wg, block_size=bs, num_blocks=pool, max_blocks_per_seq=mbps,
+                     max_slots=Bn, max_rows=chunk + Bn, max_seqs=Bn, max_position=mbps * bs,
+                     block_order=order)
+        reqs = cb_requests(seed + Bn, 4096, shape.vocab)
+
+        def run(steps, first):
+            loop = ComposerLoop(eng, max_rows=chunk + Bn, chunk_size=chunk, eos_id=0)
+            nxt, rec = first, []
+            try:
+                for _ in range(steps):
+                    while loop.stats().queued < Bn:  # closed loop: the queue never empties
+                        rid, prompt, mx = reqs[nxt % len(reqs)]
+                        loop.submit(prompt, mx, None, nxt)
+                        nxt += 1
+                    t0 = time.perf_counter()
+                    p = loop.step()
+                    dt = time.perf_counter() - t0
+                    n = p.n_seqs
+                    ctx = list(p.ctx_lens[:n]) if p.n_prefill_rows == 0 else []
+                    rec.append((dt, p.n_prefill_rows, p.n_decode_rows, p.n_out, ctx))
+                fin = loop.pop_finished()
+            finally:
+                loop.close()
+            return rec, fin
+
+        run(8, 10_000)  # warm-up on its own composer; closing it frees every slot and block
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        rec, fin = run(n_steps, 0)
+        wall = time.perf_counter() - t0
+        if eng.status():
+            raise RuntimeError("device status set")
+        gen = sum(r[3] for r in rec)
+        dec = [r for r in rec if r[1] == 0 and r[2] > 0]
+        mixed = [r for r in rec if r[1] > 0]
+        d_time = sum(r[0] for r in dec)
+        d_rows = sum(r[2] for r in dec)
+        d_bytes = sum(step_bytes(shape, r[4], r[3]) for r in dec)
+        out = {"workload": wlc.name, "slots": Bn, "steps": n_steps, "wall_s": wall,
+               "generated_tokens": gen, "tokens_per_s": gen / wall,
+               "finished_requests": len(fin),
+               "decode_only_steps": len(dec),
+               "decode_ms_per_step": 1e3 * d_time / max(len(dec), 1),
+               "decode_tokens_per_s": d_rows / d_time if d_time else None,
+               "decode_hbm_gbs": d_bytes / d_time / 1e9 if d_time else None,
+               "decode_roofline_frac": d_bytes / d_time / 1e9 / PEAK_HBM_GBS if d_time else None,
+               "mixed_steps": len(mixed),
+               "mixed_ms_per_step": 1e3 * sum(r[0] for r in mixed) / max(len(mixed), 1),
+               "prefill_rows": sum(r[1] for r in rec)}
+        eng.close()
+        print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,8 +355,11 @@ def main():
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--print-sources-digest", action="store_true")
     ap.add_argument("--workload", default="8b-layer+lmhead-decode",
-                    choices=["8b-layer+lmhead-decode", "8b-layer+lmhead65536-b256-sampled"],
+                    choices=["8b-layer+lmhead-decode", "8b-layer+lmhead65536-b256-sampled",
+                             "2b-28layer-continuous-batching"],
                     help="the headline decode sweep (default) or another configured workload")
+    ap.add_argument("--cb-slots", default="8,32", help="slot counts of the 2B loop workload")
+    ap.add_argument("--cb-steps", type=int, default=256, help="steps of the 2B loop workload")
     args = ap.parse_args()
     if args.print_sources_digest:
         print(sources_digest())
@@ -289,9 +375,12 @@ def main():
     from continuous_batching_decode_forward_amd import configs, synth
     from continuous_batching_decode_forward_amd.engine import Engine
 
-    if args.workload != "8b-layer+lmhead-decode":
+    if args.workload == "8b-layer+lmhead65536-b256-sampled":
         torch.cuda.set_device(0)
         return bench_sampled(args)
+    if args.workload == "2b-28layer-continuous-batching":
+        torch.cuda.set_device(0)
+        return bench_cb2b(args)
 
     shape = configs.LLAMA8B_1L
     seed = 0

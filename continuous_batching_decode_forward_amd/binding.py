@@ -144,6 +144,8 @@ SIGNATURES = [
     ("cbd_sched_abort", C.c_int, [VP, C.c_uint64]),
     ("cbd_sched_pop_finished", C.c_int, [VP, U64P, I32P, I32P]),
     ("cbd_sched_stats_get", C.c_int, [VP, C.POINTER(cbd_sched_stats)]),
+    ("cbd_sched_meta_ints", C.c_int, [C.POINTER(cbd_sched_config), C.POINTER(C.c_size_t)]),
+    ("cbd_sched_step", C.c_int, [VP, C.c_int32, VP, VP, VP, VP, VP, C.POINTER(cbd_plan)]),
 ]
 
 _lib = None
@@ -323,3 +325,18 @@ def cbd_sched_stats_get(sched) -> cbd_sched_stats:
     s = cbd_sched_stats()
     _call("cbd_sched_stats_get", sched, C.byref(s))
     return s
+
+
+def cbd_sched_meta_ints(cfg: cbd_sched_config) -> int:
+    n = C.c_size_t()
+    _call("cbd_sched_meta_ints", C.byref(cfg), C.byref(n))
+    return n.value
+
+
+def cbd_sched_step(sched, mode: int, meta_dev, host_stage, tokens_dev, logits_out,
+                   stream) -> cbd_plan:
+    """Pointers are integers or None (device / host addresses)."""
+    p = cbd_plan()
+    _call("cbd_sched_step", sched, int(mode), meta_dev, host_stage, tokens_dev, logits_out,
+          stream, C.byref(p))
+    return p

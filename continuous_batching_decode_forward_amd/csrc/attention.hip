@@ -106,6 +106,10 @@ __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
   const int last_row = min(nn, (qt + 1) * rpt) - 1;
   const int k_lo = sp * ap.split_len;
   const int k_hi = min(k_lo + ap.split_len, ctx + last_row + 1);
+  // The items of a sequence span every (query tile, split) pair; the early
+  // tiles of a chunk longer than one split have no keys in its later splits.
+  // Such a wave stages no block-table entries and must not issue a load.
+  if (k_lo >= k_hi) return;
   const int c_end = c_ok ? min(k_hi, ctx + c_row + 1) : k_lo;  // keys [k_lo, c_end)
 
   // Q as the B operand of S = K.Q^T: lane (lr, lg) holds d = 32 j + 8 lg .. +8
@@ -298,16 +302,19 @@ __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
 
   // Two tiles in flight: the loads of step i + 1 are issued before step i is
   // computed (near the end they repeat the last step's addresses, which
-  // the cache serves; those repeats are never computed).
+  // the cache serves; those repeats are never computed). Every load starts
+  // on a step boundary: the block-size >= 32 path's per-lane offsets assume
+  // it (a start past the boundary would read beyond the block's tile).
   {
     const int n_it = (k_hi - k_lo + 31) / 32;
+    const int last_step = k_lo + 32 * (n_it - 1);
     KVTile<HD> A, B;
     load(A, k_lo);
     int i = 0;
     for (; i + 2 <= n_it; i += 2) {
       load(B, k_lo + 32 * (i + 1));
       compute(A, k_lo + 32 * i);
-      load(A, min(k_lo + 32 * (i + 2), last));
+      load(A, min(k_lo + 32 * (i + 2), last_step));
       compute(B, k_lo + 32 * (i + 1));
     }
     if (i < n_it) compute(A, k_lo + 32 * i);

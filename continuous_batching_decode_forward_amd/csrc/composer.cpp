@@ -353,6 +353,61 @@ int cbd_sched_stats_get(const cbd_sched* s, cbd_sched_stats* out) {
   return CBD_OK;
 }
 
+int cbd_sched_meta_ints(const cbd_sched_config* cfg, size_t* ints_out) {
+  if (!cfg || !ints_out || cfg->max_slots < 1 || cfg->max_blocks_per_seq < 1 || cfg->max_rows < 1)
+    return fail(CBD_E_INVAL, "NULL or out-of-range composer config");
+  *ints_out = (size_t)cfg->max_slots * (5 + (size_t)cfg->max_blocks_per_seq) + cfg->max_rows;
+  return CBD_OK;
+}
+
+int cbd_sched_step(cbd_sched* s, int32_t mode, int32_t* meta_dev, int32_t* host_stage,
+                   int32_t* tokens_dev, float* logits_out, void* stream, cbd_plan* plan_out) {
+  if (!s || !meta_dev || !host_stage || !tokens_dev)
+    return fail(CBD_E_INVAL, "NULL composer or staging buffer");
+  if (!s->engine) return fail(CBD_E_INVAL, "cbd_sched_step needs a composer created with an engine");
+  if (mode != CBD_MODE_GREEDY && mode != CBD_MODE_SAMPLE) return fail(CBD_E_INVAL, "bad mode");
+  cbd_plan p;
+  int rc = cbd_sched_plan(s, &p);
+  if (rc != CBD_OK) return rc;
+  if (plan_out) *plan_out = p;
+  if (p.n_rows == 0) return cbd_sched_commit(s, nullptr, 0);
+  const size_t n = (size_t)p.n_seqs, mb = (size_t)p.max_blocks_per_seq;
+  size_t o = 0;
+  auto put = [&](const int32_t* src, size_t cnt) {
+    memcpy(host_stage + o, src, cnt * sizeof(int32_t));
+    const size_t at = o;
+    o += cnt;
+    return meta_dev + at;
+  };
+  cbd_step st;
+  st.n_seqs = p.n_seqs;
+  st.n_rows = p.n_rows;
+  st.n_out = p.n_out;
+  st.max_ctx = p.max_ctx;
+  st.max_blocks_per_seq = p.max_blocks_per_seq;
+  st.mode = mode;
+  st.slots = put(p.slots, n);
+  st.block_tables = put(p.block_tables, n * mb);
+  st.ctx_lens = put(p.ctx_lens, n);
+  st.n_new = put(p.n_new, n);
+  st.tokens = put(p.tokens, (size_t)p.n_rows);
+  st.want_token = put(p.want_token, n);
+  st.step_ids = put(p.step_ids, n);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t he = hipMemcpyAsync(meta_dev, host_stage, o * sizeof(int32_t), hipMemcpyHostToDevice, hs);
+  if (he != hipSuccess) return fail(CBD_E_DEVICE, std::string("step metadata upload: ") + hipGetErrorString(he));
+  rc = cbd_step_forward(s->engine, &st, logits_out, tokens_dev, stream);
+  if (rc != CBD_OK) return rc;
+  if (p.n_out > 0) {
+    he = hipMemcpyAsync(host_stage, tokens_dev, (size_t)p.n_out * sizeof(int32_t),
+                        hipMemcpyDeviceToHost, hs);
+    if (he != hipSuccess) return fail(CBD_E_DEVICE, std::string("token download: ") + hipGetErrorString(he));
+  }
+  he = hipStreamSynchronize(hs);
+  if (he != hipSuccess) return fail(CBD_E_DEVICE, std::string("step: ") + hipGetErrorString(he));
+  return cbd_sched_commit(s, host_stage, p.n_out);
+}
+
 const char* cbd_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

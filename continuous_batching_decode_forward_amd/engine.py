@@ -164,3 +164,59 @@ class Engine:
             self.close()
         except Exception:
             pass
+
+
+class ComposerLoop:
+    """The host step composer attached to an engine and stepped natively:
+    each step() is one cbd_sched_step (plan, upload, step, tokens back,
+    commit). The staging buffers are allocated here with torch: the device
+    metadata buffer, page-locked host staging and the device token row."""
+
+    def __init__(self, eng: Engine, *, max_rows: int, chunk_size: int, eos_id: int,
+                 policy: int = B.CBD_ADMIT_RESERVE, max_slots: int | None = None,
+                 max_blocks_per_seq: int | None = None):
+        cfg = B.cbd_sched_config()
+        cfg.max_slots = max_slots or eng.cfg.max_slots
+        cfg.block_size, cfg.num_blocks = eng.block_size, eng.num_blocks
+        cfg.max_blocks_per_seq = max_blocks_per_seq or eng.max_blocks_per_seq
+        cfg.max_rows, cfg.chunk_size, cfg.eos_id, cfg.policy = max_rows, chunk_size, eos_id, policy
+        self.cfg, self.eng = cfg, eng
+        self.handle = B.cbd_sched_create(cfg, eng.handle)
+        n = B.cbd_sched_meta_ints(cfg)
+        self.meta_dev = torch.empty(n, dtype=torch.int32, device=eng.device)
+        self.host = torch.empty(n, dtype=torch.int32, pin_memory=True)
+        self.tokens_dev = torch.empty(cfg.max_slots, dtype=torch.int32, device=eng.device)
+
+    def submit(self, prompt, max_new: int, params=None, request_id: int = 0) -> None:
+        B.cbd_sched_submit(self.handle, prompt, max_new, params, request_id)
+
+    def step(self, mode=B.CBD_MODE_GREEDY, logits_out: torch.Tensor | None = None,
+             stream=None) -> B.cbd_plan:
+        return B.cbd_sched_step(self.handle, mode, self.meta_dev.data_ptr(),
+                                self.host.data_ptr(), self.tokens_dev.data_ptr(),
+                                None if logits_out is None else logits_out.data_ptr(),
+                                _stream_ptr(stream).value)
+
+    def last_tokens(self, n: int) -> np.ndarray:
+        """The tokens the last step committed (host staging copy)."""
+        return self.host[:n].numpy().copy()
+
+    def pop_finished(self) -> list:
+        out = []
+        while (f := B.cbd_sched_pop_finished(self.handle)) is not None:
+            out.append(f)
+        return out
+
+    def stats(self) -> B.cbd_sched_stats:
+        return B.cbd_sched_stats_get(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            B.cbd_sched_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

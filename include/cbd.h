@@ -346,6 +346,31 @@ int cbd_sched_pop_finished(cbd_sched* s, uint64_t* request_id, int32_t* reason,
                            int32_t* n_generated);
 int cbd_sched_stats_get(const cbd_sched* s, cbd_sched_stats* out);
 
+/* The loop of Go under the hood section 20.3.2 (plan a step, run it on the
+ * batch, hand its tokens back) as one host call, for a composer created
+ * with an engine.
+ *
+ * cbd_sched_meta_ints: the int32 count of the staging buffers below,
+ * max_slots * (5 + max_blocks_per_seq) + max_rows.
+ *
+ * cbd_sched_step: plan (admit, compose); pack the plan's arrays (slots,
+ * block tables, ctx_lens, n_new, tokens, want_token, step_ids, in that
+ * order) into host_stage (host, cbd_sched_meta_ints int32; page-locked
+ * memory makes the upload asynchronous) and copy them to meta_dev (device,
+ * same size); run cbd_step_forward with `mode` on `stream`; copy the step's
+ * tokens (tokens_dev: device int32 [max_slots]) back into host_stage; wait
+ * for the stream; commit them. logits_out (device [max_slots][vocab] fp32)
+ * is nullable. plan_out (nullable) receives the plan that ran; its arrays
+ * stay valid until the next plan. A step with no rows (nothing admitted, or
+ * stalled under CBD_ADMIT_FREE_SLOT: see plan_out->stalled) runs nothing and
+ * commits an empty step. All buffers are the caller's. Blocks until the
+ * step's tokens are on the host. Errors: CBD_E_INVAL (NULL argument, no
+ * engine, bad mode), CBD_E_DEVICE; after an error inside the step the plan
+ * stays uncommitted and the composer should be destroyed. */
+int cbd_sched_meta_ints(const cbd_sched_config* cfg, size_t* ints_out);
+int cbd_sched_step(cbd_sched* s, int32_t mode, int32_t* meta_dev, int32_t* host_stage,
+                   int32_t* tokens_dev, float* logits_out, void* stream, cbd_plan* plan_out);
+
 #ifdef __cplusplus
 }
 #endif
