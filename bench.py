@@ -259,6 +259,114 @@ def bench_sampled(args):
     print(json.dumps(out), flush=True)
 
 
+def build_mixed(shape, seed, n_dec=48, ctx_range=(1024, 8192), prompt=4096, chunk=512, bs=32):
+    """The mixed step's inputs: n_dec decode rows with contexts uniform in
+    ctx_range (blocks for their cached positions and the positions the
+    prompt's steps append), and one prompt of `prompt` uniform ids prefilled
+    in chunks of `chunk` rows, one chunk per step (offsets 0, chunk, ...).
+    Blocks come from one seeded permutation of the pool; sequence 0 is the
+    prompt, sequences 1..n_dec the decode rows."""
+    from continuous_batching_decode_forward_amd import synth
+    n_steps = prompt // chunk
+    ctx = synth.uniform_ints(seed, "ctx", n_dec, ctx_range[0], ctx_range[1])
+    need = [-(-prompt // bs)] + [-(-(int(c) + n_steps) // bs) for c in ctx]
+    total = int(sum(need))
+    perm = synth.permutation(seed, "blocks", total)
+    mbps = max(need)
+    tables = np.full((n_dec + 1, mbps), -1, np.int32)
+    o = 0
+    for i in range(n_dec + 1):
+        tables[i, :need[i]] = perm[o:o + need[i]]
+        o += need[i]
+    cached = perm[need[0]:]  # the decode rows' blocks hold synthetic K/V
+    prompt_ids = synth.uniform_ints(seed, "prompt", prompt, 0, shape.vocab - 1)
+    dec_tokens = synth.uniform_ints(seed, "dectok", n_dec * n_steps, 0,
+                                    shape.vocab - 1).reshape(n_steps, n_dec)
+    return dict(bs=bs, ctx=ctx, tables=tables, total=total, mbps=mbps, cached=cached,
+                prompt=prompt_ids, dec_tokens=dec_tokens, chunk=chunk, n_steps=n_steps,
+                max_position=max(prompt, int(ctx.max()) + n_steps))
+
+
+def mixed_step(wl, j, with_chunk=True):
+    """Step j of the mixed workload: (slots, tables, ctx_lens, n_new, tokens,
+    want_token) -- the chunk at offset j * chunk first, then every decode row
+    at its context + j."""
+    n_dec, ch = len(wl["ctx"]), wl["chunk"]
+    seqs = ([0] if with_chunk else []) + list(range(1, n_dec + 1))
+    ctx = ([j * ch] if with_chunk else []) + [int(c) + j for c in wl["ctx"]]
+    nn = ([ch] if with_chunk else []) + [1] * n_dec
+    toks = (list(wl["prompt"][j * ch:(j + 1) * ch]) if with_chunk else []) + \
+        [int(t) for t in wl["dec_tokens"][j]]
+    want = ([int(j == wl["n_steps"] - 1)] if with_chunk else []) + [1] * n_dec
+    return seqs, wl["tables"][seqs], ctx, nn, toks, want
+
+
+def bench_mixed8b(args):
+    """The mixed step on the full 8B shape (32 layers, d_model 4096, 32/8
+    heads, FFN 14336, vocab 128256): 48 decode rows with contexts uniform in
+    1024..8192 plus one 512-token chunk of a 4096-token prompt, 560 rows per
+    step, 32-position blocks; the prompt runs as 8 consecutive steps
+    (offsets 0..3584). Each step is timed as it is and without its chunk (the
+    same 48 decode rows alone); the difference is the chunk's time."""
+    import torch
+    from continuous_batching_decode_forward_amd import configs, synth
+    from continuous_batching_decode_forward_amd.engine import Engine
+    shape, wlc = configs.LLAMA8B, configs.MIXED_8B
+    seed = 0
+    stream = torch.cuda.current_stream()
+    log(f"[bench] weights {shape.name} on GPU")
+    wg = synth.make_weights(shape, seed=seed, device="cuda")
+    wl = build_mixed(shape, seed, n_dec=wlc.batch[0], ctx_range=wlc.ctx_range, bs=wlc.block_size)
+    n_dec = len(wl["ctx"])
+    eng = Engine(shape, wg, block_size=wl["bs"], num_blocks=wl["total"],
+                 max_blocks_per_seq=wl["mbps"], max_slots=n_dec + 1, max_rows=wl["chunk"] + n_dec,
+                 max_seqs=n_dec + 1, max_position=wl["max_position"])
+    log(f"[bench] filling {len(wl['cached'])} KV blocks "
+        f"({len(wl['cached']) * shape.kv_bytes_per_pos * wl['bs'] / 1e9:.1f} GB)")
+    fill_pool(eng, seed, wl["cached"])
+    tk = torch.empty(n_dec + 1, dtype=torch.int32, device="cuda")
+    reps = max(args.steps, 8)
+    d, hq, hd, L = shape.d_model, shape.n_heads, shape.head_dim, shape.n_layers
+    ws = synth.weight_shapes(shape)
+    lin = 2 * L * sum(int(np.prod(ws[k])) for k in ("w_qkv", "w_o", "w_gate", "w_up", "w_down"))
+    rows = []
+    for j in range(wl["n_steps"]):
+        seqs, tab, ctx, nn, toks, want = mixed_step(wl, j)
+        meta = eng.upload_step(slots=seqs, block_tables=tab, ctx_lens=ctx, n_new=nn, tokens=toks,
+                               want_token=want)
+        ms_mixed, _, _ = time_steps(eng, meta, None, tk, reps, 1, stream)
+        seqs_d, tab_d, ctx_d, nn_d, toks_d, want_d = mixed_step(wl, j, with_chunk=False)
+        meta_d = eng.upload_step(slots=seqs_d, block_tables=tab_d, ctx_lens=ctx_d, n_new=nn_d,
+                                 tokens=toks_d, want_token=want_d)
+        ms_dec, _, _ = time_steps(eng, meta_d, None, tk, reps, 1, stream)
+        # redo the mixed step last, so the chunk's K/V is in place for step j + 1
+        eng.step_forward(meta, None, tk, stream)
+        o = j * wl["chunk"]
+        attn = sum(4 * hq * hd * (o + i + 1) for i in range(wl["chunk"])) * L
+        chunk_flops = wl["chunk"] * lin + attn + (2 * shape.vocab * d if want[0] else 0)
+        dec_bytes = step_bytes(shape, ctx_d, n_dec)
+        chunk_ms = ms_mixed - ms_dec
+        rows.append({"offset": o, "ms_mixed": ms_mixed, "ms_decode_only": ms_dec,
+                     "chunk_ms": chunk_ms, "chunk_tflop": chunk_flops / 1e12,
+                     "chunk_mfma_util": chunk_flops / (chunk_ms * 1e-3) / 2.5e15 if chunk_ms > 0 else None,
+                     "decode_gbs": dec_bytes / (ms_dec * 1e-3) / 1e9})
+        log(f"[bench] offset {o}: mixed {ms_mixed:.2f} ms, decode-only {ms_dec:.2f} ms")
+    torch.cuda.synchronize()
+    if eng.status():
+        raise RuntimeError("device status set")
+    mean = lambda k: float(np.mean([r[k] for r in rows]))
+    out = {"workload": wlc.name, "decode_rows": n_dec, "chunk": wl["chunk"], "rows": wl["chunk"] + n_dec,
+           "ms_per_step_mean": mean("ms_mixed"), "ms_decode_only_mean": mean("ms_decode_only"),
+           "chunk_ms_mean": mean("chunk_ms"),
+           "chunk_mfma_util_mean": float(np.mean([r["chunk_mfma_util"] or 0 for r in rows])),
+           "decode_gbs_mean": mean("decode_gbs"),
+           "decode_roofline_frac": mean("decode_gbs") / PEAK_HBM_GBS,
+           "decode_tokens_per_s_mixed": n_dec / (mean("ms_mixed") * 1e-3),
+           "steps": rows}
+    eng.close()
+    print(json.dumps(out), flush=True)
+
+
 def cb_requests(seed, n, vocab, prompt_range=(16, 512), new_range=(2, 300)):
     """A seeded closed-loop request stream: prompt lengths and answer budgets
     uniform in the given ranges, prompt ids uniform over the vocabulary."""
@@ -356,7 +464,8 @@ def main():
     ap.add_argument("--print-sources-digest", action="store_true")
     ap.add_argument("--workload", default="8b-layer+lmhead-decode",
                     choices=["8b-layer+lmhead-decode", "8b-layer+lmhead65536-b256-sampled",
-                             "2b-28layer-continuous-batching"],
+                             "2b-28layer-continuous-batching",
+                             "8b-32layer-mixed-48dec+512chunk"],
                     help="the headline decode sweep (default) or another configured workload")
     ap.add_argument("--cb-slots", default="8,32", help="slot counts of the 2B loop workload")
     ap.add_argument("--cb-steps", type=int, default=256, help="steps of the 2B loop workload")
@@ -378,6 +487,9 @@ def main():
     if args.workload == "8b-layer+lmhead65536-b256-sampled":
         torch.cuda.set_device(0)
         return bench_sampled(args)
+    if args.workload == "8b-32layer-mixed-48dec+512chunk":
+        torch.cuda.set_device(0)
+        return bench_mixed8b(args)
     if args.workload == "2b-28layer-continuous-batching":
         torch.cuda.set_device(0)
         return bench_cb2b(args)
