@@ -82,6 +82,19 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_base) {
 #endif
 }
 
+// The same copy with the non-temporal cache policy: for data read once
+// (a weight stream), so that it does not push reused data out of L2.
+__device__ __forceinline__ void copy16_to_lds_nt(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+#endif
+}
+
 // Wait until at most N vector-memory loads of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmem() {

@@ -441,6 +441,140 @@ __global__ __launch_bounds__(64 * STREAM_NW) void gemm_stream_kernel(GemmArgs a,
   store_tile<RT, NT, EPI>(a, acc, r0, n0, ks, S, tile);
 }
 
+// ------------------------------------------------------- the dense path
+//
+// For many rows (a prefill chunk, a large batch) the projection is a dense
+// contraction and the aim is MFMA time. A workgroup of 4 waves (2 along N
+// x 2 along R) owns a 256-column x 16 RF-row tile; each wave a 128-column x
+// 8 RF-row block: per 32-k stage it reads 8 weight fragments and RF
+// activation fragments (RF/2 row fragments x hi, lo) from LDS and issues
+// 8 RF MFMAs, so the MFMA time of a stage is twice its LDS read time and
+// the activation tile is fetched once per 256 columns. Both operands reach
+// LDS by direct global->LDS copies into a D-stage ring: 16 weight tiles
+// (1 KB each, straight from the packed layout) and RF fragments per plane.
+// The ring discipline is the stream path's: stage c + D - 1 is issued right
+// after the barrier of stage c, and the wait for stage c is an exact
+// vector-memory count (every issue is the same LPS copies per wave; past
+// the last stage the last stage is re-issued, never computed).
+// The workgroups that share a weight tile (its row groups and K splits) are
+// numbered so that they land on one XCD (workgroup i runs on XCD i mod 8):
+// their repeated weight reads meet in that XCD's L2. Past K the packed
+// weights are zero and activation reads are clamped into the row, so a K
+// tail needs no masking (K is a multiple of 8 and every split but the last
+// ends on a 32-k boundary).
+#define DENSE_TN 256
+
+#define DENSE_WAVES 8
+
+template <int RF, int D, int EPI>
+__global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a, int kc, int S,
+                                                                      int n_tiles, int r_groups) {
+  constexpr int NM = EpiTraits<EPI>::NM;
+  constexpr int NT = 8 / NM;       // column fragments per matrix per wave
+  constexpr int WR = DENSE_WAVES / 2;  // waves along R
+  constexpr int RH = RF / WR;      // row fragments per wave
+  constexpr int TW = 16;           // weight tiles per stage
+  constexpr int TS = TW + 2 * RF;  // 1 KB tiles per stage
+  constexpr int LPS = TS / DENSE_WAVES;  // copies per stage per wave
+  static_assert(TS % DENSE_WAVES == 0 && RF % WR == 0, "tile counts");
+  static_assert(D >= 3 && (D - 2) * LPS < 64, "ring depth");
+  extern __shared__ uint4 ring[];  // [D][TS][64]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave & 1, wr = wave >> 1;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int id = blockIdx.x;
+  const int per = r_groups * S;
+  const int q = id >> 3;
+  const int n_tile = (q / per) * 8 + (id & 7);
+  if (n_tile >= n_tiles) return;  // padding of the XCD numbering; no barrier yet
+  const int rg = (q % per) / S, ks = (q % per) % S;
+  const int K = a.K, R = a.R, N = a.N;
+  const int r_base = rg * 16 * RF;
+  const int kbeg = ks * kc;  // a multiple of 32
+  const int kend = min(K, kbeg + kc);
+  const int nst = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
+  const int KT = (K + 31) / 32;
+  constexpr int CB = 2 * NT;  // 16-column blocks per matrix per workgroup
+
+  // Copy sources: this wave issues tiles t = wave + 8 i; t < 16 are weight
+  // tiles (matrix t / CB, column block t % CB), the rest activation
+  // fragments (u = t - 16: row fragment u / 2, plane u % 2).
+  const uint16_t* src[LPS];
+#pragma unroll
+  for (int i = 0; i < LPS; ++i) {
+    const int t = wave + DENSE_WAVES * i;
+    if (i < TW / DENSE_WAVES) {
+      const int m = t / CB;
+      int nb = n_tile * CB + t % CB;
+      if (nb * 16 >= N) nb = 0;  // past N: read block 0, never stored
+      src[i] = (m ? a.W2 : a.W) + ((size_t)nb * KT + kbeg / 32) * 512 + lane * 8;
+    } else {
+      const int u = t - TW;
+      const int r = min(r_base + 16 * (u >> 1) + lr, R - 1);
+      src[i] = ((u & 1) ? a.Xlo : a.X) + (size_t)r * K;
+    }
+  }
+  auto issue = [&](int slot, int c) {
+#pragma unroll
+    for (int i = 0; i < LPS; ++i) {
+      const int t = wave + DENSE_WAVES * i;
+      if (i < TW / DENSE_WAVES)  // weights: streamed once, kept out of L2's way
+        copy16_to_lds_nt(src[i] + (size_t)c * 512, ring + ((size_t)slot * TS + t) * 64);
+      else  // activations: re-read by every column tile, kept in L2
+        copy16_to_lds(src[i] + min(kbeg + 32 * c + 8 * lg, K - 8),
+                      ring + ((size_t)slot * TS + t) * 64);
+    }
+  };
+
+  floatx4_t acc[NM][NT][RH];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int rh = 0; rh < RH; ++rh) acc[m][nt][rh] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  // The hi products of every accumulator, then the lo products: two MFMAs
+  // on one accumulator are 8 RH apart, never back to back.
+  auto compute = [&](int slot) {
+    const uint4* buf = ring + (size_t)slot * TS * 64;
+    uint4 wf[NM][NT], xf[2][RH];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) wf[m][nt] = buf[(m * CB + wn * NT + nt) * 64 + lane];
+#pragma unroll
+    for (int rh = 0; rh < RH; ++rh)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) xf[pl][rh] = buf[(TW + 2 * (wr * RH + rh) + pl) * 64 + lane];
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int rh = 0; rh < RH; ++rh)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[m][nt][rh] = mfma16x16x32(as_bf16x8(wf[m][nt]), as_bf16x8(xf[pl][rh]), acc[m][nt][rh]);
+  };
+
+  if (nst > 0) {
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) issue(j, min(j, nst - 1));
+    for (int c = 0; c < nst; ++c) {
+      // Stage c's copies were followed by those of stages c + 1 .. c + D - 2.
+      wait_vmem<(D - 2) * LPS>();
+      __syncthreads();
+      issue((c + D - 1) % D, min(c + D - 1, nst - 1));
+      compute(c % D);
+    }
+  }
+  wait_vmem<0>();  // no LDS copy may land after the workgroup exits
+  store_tile<RH, NT, EPI>(a, acc, r_base + 16 * RH * wr, n_tile * (DENSE_TN / NM) + 16 * NT * wn,
+                          ks, S, n_tile * 2 + wn);
+}
+
 // Sum the S split partials in split order, then the epilogue (no argmax:
 // the logits GEMM never splits K).
 template <int EPI>
@@ -505,12 +639,41 @@ hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, h
 // waves each reading a few tens of KB, in a single launch where possible.
 struct GemmPlan {
   bool stream;
+  bool dense;
   int RT, NT, KW, D, S;
 };
+
+// Rows at or above which the dense path runs.
+#define DENSE_MIN_ROWS 128
 
 static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
   GemmPlan p{};
   const bool vocab = logits && N >= 32768;  // the LM head: wide, argmax fused
+  // Row fragments per dense workgroup: the fewest padded rows, then the
+  // larger tile (fewer weight re-reads).
+  int best = 0, waste = 1 << 30;
+  for (int rf : {16, 12, 8}) {
+    const int w = (R + 16 * rf - 1) / (16 * rf) * 16 * rf - R;
+    if (w < waste) {
+      waste = w;
+      best = rf;
+    }
+  }
+  const int dense_tiles =
+      (N + DENSE_TN / NM - 1) / (DENSE_TN / NM) * ((R + 16 * best - 1) / (16 * best));
+  // The dense path wants enough tiles to spread without deep K splits (or a
+  // long K, where splitting is cheap); narrow matrices at moderate row
+  // counts stay on the stream path.
+  if (R >= DENSE_MIN_ROWS && (dense_tiles >= 32 || K >= 8192)) {
+    p.dense = true;
+    p.RT = best;
+    p.NT = 4 / NM;
+    p.D = best == 8 ? 4 : 3;
+    p.S = 1;
+    if (!logits)
+      while (dense_tiles * p.S < 256 && K / (p.S * 2) >= 256) p.S *= 2;
+    return p;
+  }
   if (R <= 16) {
     p.stream = false;
     p.RT = 1;
@@ -549,6 +712,7 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
 
 int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K) {
   const GemmPlan p = plan_gemm(R, N, K, 1, true);
+  if (p.dense) return (N + DENSE_TN - 1) / DENSE_TN * 2;
   const int cols = 16 * p.NT;
   if (p.stream) return (N + cols * STREAM_NW - 1) / (cols * STREAM_NW) * STREAM_NW;
   return (N + cols - 1) / cols;
@@ -602,10 +766,38 @@ static hipError_t launch_stream(const GemmArgs& a, int S, hipStream_t st) {
   return launch_reduce<EPI>(a, S, st);
 }
 
+template <int RF, int D, int EPI>
+static hipError_t launch_dense(const GemmArgs& a, int S, hipStream_t st) {
+  constexpr int NM = EpiTraits<EPI>::NM;
+  const int n_tiles = (a.N + DENSE_TN / NM - 1) / (DENSE_TN / NM);
+  const int r_groups = (a.R + 16 * RF - 1) / (16 * RF);
+  int kc;
+  S = split_k(a.K, S, 32, &kc);
+  if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 32, &kc);
+  const size_t lds = (size_t)D * (16 + 2 * RF) * 1024;
+  static bool lds_set = false;  // above 64 KB the launch must be allowed first
+  if (!lds_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dense_kernel<RF, D, EPI>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    lds_set = true;
+  }
+  const unsigned grid = (unsigned)((n_tiles + 7) / 8 * 8 * r_groups * S);
+  gemm_dense_kernel<RF, D, EPI><<<grid, 64 * DENSE_WAVES, lds, st>>>(a, kc, S, n_tiles, r_groups);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  return launch_reduce<EPI>(a, S, st);
+}
+
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
   constexpr int NM = EpiTraits<EPI>::NM;
   const GemmPlan p = plan_gemm(a.R, a.N, a.K, NM, EPI == EPI_LOGITS);
+  if (p.dense) {
+    if (p.RT == 16) return launch_dense<16, 3, EPI>(a, p.S, st);
+    if (p.RT == 12) return launch_dense<12, 3, EPI>(a, p.S, st);
+    return launch_dense<8, 4, EPI>(a, p.S, st);
+  }
   if (!p.stream) {
 #define PW(NT_, KW_) \
   if (p.NT == NT_ && p.KW == KW_) return launch_per_wave<NT_, KW_, EPI>(a, p.S, st);
