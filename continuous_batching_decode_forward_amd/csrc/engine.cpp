@@ -70,6 +70,7 @@ WorkspaceLayout workspace_layout(const cbd_config& c) {
   L.out_row = take(R * 4);
   L.out_seq = take(R * 4);
   L.item0 = take((S + 1) * 4);
+  L.row_out = take(R * 4);
   // fp32 buffers [rows][w] and split buffers (hi plane [rows][w] bf16, then
   // the lo plane) both take 4 bytes per element.
   L.x = take(R * d * 4);
@@ -408,7 +409,8 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
              s->ctx_lens, s->n_new, s->tokens, s->want_token, s->step_ids};
   RowMaps maps{e->wsp<int32_t>(e->ws.row_seq), e->wsp<int32_t>(e->ws.row_pos),
                e->wsp<int32_t>(e->ws.seq_row0), e->wsp<int32_t>(e->ws.out_row),
-               e->wsp<int32_t>(e->ws.out_seq), e->wsp<int32_t>(e->ws.item0)};
+               e->wsp<int32_t>(e->ws.out_seq), e->wsp<int32_t>(e->ws.item0),
+               e->wsp<int32_t>(e->ws.row_out)};
   const AttnPlan ap = plan_attention(e, s);
   const int qkv_n = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   const int qd = c.n_heads * c.head_dim;
@@ -431,20 +433,26 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
   HIP_TRY(launch_embed_norm(s->tokens, maps.row_seq, R, e->embed, e->attn_norm[0], e->md, x, h,
                             h_lo, status, st));
   HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
+  // The norm in front of each projection is fused into the kernel that
+  // finishes the previous residual projection (or the embedding gather):
+  // per layer QKV -> RoPE/append (+ the QKV split sum) -> attention -> O ->
+  // residual + pre-FFN norm -> gate/up -> down -> residual + the next norm.
+  uint16_t* lm_in = e->wsp<uint16_t>(e->ws.lm_in);
+  uint16_t* lm_in_lo = lm_in + (size_t)c.max_seqs * c.d_model;
+  int32_t splits = 1;
   for (int l = 0; l < c.n_layers; ++l) {
-    if (l > 0)
-      HIP_TRY(launch_rmsnorm(x, nullptr, R, e->attn_norm[l], c.d_model, c.rms_eps, h, h_lo, st));
     GemmArgs g{};
     g.partials = gpart;
     g.partials_cap = e->ws.gemm_part_floats;
+    g.splits_out = &splits;
     g.X = h; g.Xlo = h_lo; g.R = R; g.K = c.d_model; g.W = e->packed + e->pl.qkv[l]; g.N = qkv_n;
     g.epi = EPI_F32; g.Y = qkv;
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
-    HIP_TRY(launch_rope_append(qkv, R, m, maps, e->wsp<double>(e->ws.rope), e->md, q, q_lo,
-                               e->pool_k(l), e->pool_v(l), status, st));
+    HIP_TRY(launch_rope_append(qkv, gpart, splits, R, m, maps, e->wsp<double>(e->ws.rope), e->md,
+                               q, q_lo, e->pool_k(l), e->pool_v(l), status, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
     HIP_TRY(launch_attention(q, q_lo, R, m, maps, e->md, ap, e->pool_k(l), e->pool_v(l),
@@ -456,24 +464,31 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
     HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
-    HIP_TRY(launch_rmsnorm(x, nullptr, R, e->ffn_norm[l], c.d_model, c.rms_eps, h, h_lo, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
+    HIP_TRY(launch_resid_norm(x, gpart, splits, R, nullptr, nullptr, 0, e->ffn_norm[l], c.d_model,
+                              c.rms_eps, h, h_lo, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
     g.X = h; g.Xlo = h_lo; g.K = c.d_model; g.W = e->packed + e->pl.gate[l];
     g.W2 = e->packed + e->pl.up[l]; g.N = c.ffn_dim;
-    g.epi = EPI_SWIGLU; g.Y = nullptr; g.Yh = ffn; g.Yl = ffn_lo;
+    g.epi = EPI_SWIGLU; g.Y = nullptr; g.Yh = ffn; g.Yl = ffn_lo; g.splits_out = nullptr;
     HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
     g.X = ffn; g.Xlo = ffn_lo; g.K = c.ffn_dim; g.W = e->packed + e->pl.down[l]; g.W2 = nullptr;
-    g.N = c.d_model; g.epi = EPI_RESID; g.Y = x; g.Yh = g.Yl = nullptr;
+    g.N = c.d_model; g.epi = EPI_RESID; g.Y = x; g.Yh = g.Yl = nullptr; g.splits_out = &splits;
     HIP_TRY(e->prof_mark(CBD_KERNEL_DOWN, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_DOWN, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
+    if (l + 1 < c.n_layers)
+      HIP_TRY(launch_resid_norm(x, gpart, splits, R, nullptr, nullptr, 0, e->attn_norm[l + 1],
+                                c.d_model, c.rms_eps, h, h_lo, st));
+    else  // the final norm, only for the emitting rows, into the LM head's rows
+      HIP_TRY(launch_resid_norm(x, gpart, splits, R, maps.row_out, maps.out_row, s->n_out,
+                                e->final_norm, c.d_model, c.rms_eps, lm_in, lm_in_lo, st));
+    HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
   }
   if (s->n_out == 0) return CBD_OK;
-  uint16_t* lm_in = e->wsp<uint16_t>(e->ws.lm_in);
-  uint16_t* lm_in_lo = lm_in + (size_t)c.max_seqs * c.d_model;
-  HIP_TRY(launch_rmsnorm(x, maps.out_row, s->n_out, e->final_norm, c.d_model, c.rms_eps, lm_in,
-                         lm_in_lo, st));
   float* logits = logits_out;
   if (!logits && s->mode == CBD_MODE_SAMPLE) logits = e->wsp<float>(e->ws.logits);
   GemmArgs g{};

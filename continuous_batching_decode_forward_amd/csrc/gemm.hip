@@ -725,6 +725,18 @@ static hipError_t launch_reduce(const GemmArgs& a, int S, hipStream_t st) {
   return hipGetLastError();
 }
 
+// After the GEMM launch: the split-K sum, unless the caller takes the
+// partials (splits_out, fp32 and residual epilogues only).
+template <int EPI>
+static hipError_t finish_splits(const GemmArgs& a, int S, hipStream_t st) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool defer = a.splits_out && (EPI == EPI_F32 || EPI == EPI_RESID);
+  if (defer) *a.splits_out = S;
+  if (S == 1 || defer) return hipSuccess;
+  return launch_reduce<EPI>(a, S, st);
+}
+
 // K range per split: a multiple of `align`; returns the split count that
 // covers K (the requested one, possibly fewer).
 static int split_k(int K, int S, int align, int* kc) {
@@ -744,9 +756,7 @@ static hipError_t launch_per_wave(const GemmArgs& a, int S, hipStream_t st) {
   if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 64 * KW, &kc);
   const size_t lds = KW > 1 ? (size_t)(KW - 1) * 64 * NM * NT * 4 * sizeof(float) : 0;
   gemm_kernel<1, NT, KW, EPI><<<dim3(n_tiles, S, r_groups), 64 * KW, lds, st>>>(a, kc, S);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S == 1) return e;
-  return launch_reduce<EPI>(a, S, st);
+  return finish_splits<EPI>(a, S, st);
 }
 
 template <int RT, int NT, int D, int EPI>
@@ -761,9 +771,7 @@ static hipError_t launch_stream(const GemmArgs& a, int S, hipStream_t st) {
   const size_t lds = (size_t)D * RT * 4 * 1024;  // <= 64 KB for the shapes instantiated
   gemm_stream_kernel<RT, NT, D, EPI><<<dim3(n_groups, S, r_groups), 64 * STREAM_NW, lds, st>>>(
       a, kc, S);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S == 1) return e;
-  return launch_reduce<EPI>(a, S, st);
+  return finish_splits<EPI>(a, S, st);
 }
 
 template <int RF, int D, int EPI>
@@ -784,9 +792,7 @@ static hipError_t launch_dense(const GemmArgs& a, int S, hipStream_t st) {
   }
   const unsigned grid = (unsigned)((n_tiles + 7) / 8 * 8 * r_groups * S);
   gemm_dense_kernel<RF, D, EPI><<<grid, 64 * DENSE_WAVES, lds, st>>>(a, kc, S, n_tiles, r_groups);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S == 1) return e;
-  return launch_reduce<EPI>(a, S, st);
+  return finish_splits<EPI>(a, S, st);
 }
 
 template <int EPI>

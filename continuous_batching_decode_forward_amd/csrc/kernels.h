@@ -29,6 +29,7 @@ struct RowMaps {
   int32_t* out_row;    // [max_rows] row of the j-th emitting sequence, -1 = none
   int32_t* out_seq;    // [max_rows] that sequence
   int32_t* item0;      // [max_seqs + 1] first attention work item per sequence
+  int32_t* row_out;    // [max_rows] output index of each row, -1 = emits nothing
 };
 
 struct ModelDims {
@@ -69,13 +70,27 @@ hipError_t launch_embed_norm(const int32_t* tokens, const int32_t* row_seq, int3
 hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int32_t R, const uint16_t* gain,
                           int32_t d, float eps, uint16_t* h_hi, uint16_t* h_lo, hipStream_t st);
 
+// The end of a residual projection and the norm that follows it, per row r:
+// x[r] += sum over s < S of part[s][r] (S > 1: the projection's split-K
+// partials, summed in split order; S <= 1: the projection already added
+// itself to x), then h[dst] = rmsnorm(x[r]) * gain (split), with dst =
+// row_out ? row_out[r] : r and no norm where dst < 0. With row_out, the
+// n_out output rows whose out_row is -1 (refused) are zeroed.
+hipError_t launch_resid_norm(float* x, const float* part, int32_t S, int32_t R,
+                             const int32_t* row_out, const int32_t* out_row, int32_t n_out,
+                             const uint16_t* gain, int32_t d, float eps, uint16_t* h_hi,
+                             uint16_t* h_lo, hipStream_t st);
+
 // RoPE on q and k of every row at its position; q to q_out (split), k and v
 // rounded to bf16 and appended into the layer's K and V regions of the pool
-// through the block tables.
-hipError_t launch_rope_append(const float* qkv, int32_t R, const StepMeta& m, const RowMaps& maps,
-                              const double* rope_cs, const ModelDims& md, uint16_t* q_hi,
-                              uint16_t* q_lo, uint16_t* pool_k, uint16_t* pool_v,
-                              uint32_t* status, hipStream_t st);
+// through the block tables. S > 1: the projection is the sum of the S split
+// partials part[s][r][.] (in split order), also stored into qkv; otherwise
+// it is read from qkv.
+hipError_t launch_rope_append(float* qkv, const float* part, int32_t S, int32_t R,
+                              const StepMeta& m, const RowMaps& maps, const double* rope_cs,
+                              const ModelDims& md, uint16_t* q_hi, uint16_t* q_lo,
+                              uint16_t* pool_k, uint16_t* pool_v, uint32_t* status,
+                              hipStream_t st);
 
 // Paged GQA attention for every row (decode rows and prefill chunks), split
 // over keys, then the split combine into out [R][n_heads*head_dim] (split).
@@ -113,6 +128,8 @@ struct GemmArgs {
   int32_t amax_stride;
   float* partials;      // split-K partial sums
   size_t partials_cap;  // floats available there
+  int32_t* splits_out;  // nullable: the launch leaves S > 1 partials unsummed
+                        // for the caller (EPI_F32, EPI_RESID) and stores S here
 };
 
 // Number of argmax partials per row the logits GEMM writes (column tiles).

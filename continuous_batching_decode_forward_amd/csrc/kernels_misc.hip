@@ -1,5 +1,7 @@
 // kernels_misc.hip -- step metadata preparation, embedding + RMSNorm,
 // RMSNorm, RoPE + KV append, argmax combine, fills.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -92,10 +94,13 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps 
       int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
       it += md.n_kv_heads * qtiles * splits;
     }
+    for (int i = 0; i < nn_layout; ++i)
+      if (r + i < m.n_rows) maps.row_out[r + i] = -1;
     if (m.want_token[s]) {
       if (o < m.n_out) {
         maps.out_row[o] = ok ? r + nn_layout - 1 : -1;
         maps.out_seq[o] = s;
+        if (ok && r + nn_layout - 1 < m.n_rows) maps.row_out[r + nn_layout - 1] = o;
       }
       ++o;
     }
@@ -104,11 +109,17 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps 
   __syncthreads();
   if (t == 0) maps.item0[n] = counts_ok ? tot_items : 0;
   if (!counts_ok) {  // the layout cannot be trusted: refuse every row
-    for (int i = t; i < m.n_rows; i += PREP_THREADS) maps.row_seq[i] = -1;
+    for (int i = t; i < m.n_rows; i += PREP_THREADS) {
+      maps.row_seq[i] = -1;
+      maps.row_out[i] = -1;
+    }
     for (int i = t; i < m.n_out; i += PREP_THREADS) maps.out_row[i] = -1;
     for (int i = t; i < n; i += PREP_THREADS) maps.item0[i] = 0;
   } else {
-    for (int i = tot_rows + t; i < m.n_rows; i += PREP_THREADS) maps.row_seq[i] = -1;
+    for (int i = tot_rows + t; i < m.n_rows; i += PREP_THREADS) {
+      maps.row_seq[i] = -1;
+      maps.row_out[i] = -1;
+    }
   }
 }
 
@@ -228,6 +239,100 @@ hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int32_t R, const 
   return hipGetLastError();
 }
 
+// One workgroup per row, one float4 chunk of the row per thread (up to
+// RN_MAX_CHUNKS when the row is wider than the workgroup): the residual sum
+// (the split partials of a chunk are all loaded, then added in split order),
+// then the norm of the new x. Wide workgroups keep many loads in flight,
+// since only one workgroup per row works here.
+#define RN_MAX_CHUNKS 4
+
+__global__ __launch_bounds__(1024) void resid_norm_kernel(
+    float* __restrict__ x, const float* __restrict__ part, int S, int R,
+    const int32_t* __restrict__ row_out, const int32_t* __restrict__ out_row,
+    const uint16_t* __restrict__ gain, int d, float eps, uint16_t* __restrict__ h_hi,
+    uint16_t* __restrict__ h_lo) {
+  __shared__ float red[16];
+  const int T = blockDim.x, t = threadIdx.x;
+  const int nch = d >> 2;
+  const int r = blockIdx.x;
+  if (r >= R) {  // output o = r - R with no row (refused): zeros, finite downstream
+    const int o = r - R;
+    if (out_row[o] >= 0) return;
+    for (int ch = t; ch < nch; ch += T) {
+      reinterpret_cast<uint2*>(h_hi + (size_t)o * d)[ch] = make_uint2(0, 0);
+      reinterpret_cast<uint2*>(h_lo + (size_t)o * d)[ch] = make_uint2(0, 0);
+    }
+    return;
+  }
+  float* xr = x + (size_t)r * d;
+  const size_t pstride = (size_t)R * d;
+  float4 xv[RN_MAX_CHUNKS];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < RN_MAX_CHUNKS; ++c) {
+    const int ch = t + c * T;
+    xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ch < nch) {
+      float4 v = reinterpret_cast<const float4*>(xr)[ch];
+      if (S > 1) {
+        const float4* p = reinterpret_cast<const float4*>(part + (size_t)r * d) + ch;
+        for (int k0 = 0; k0 < S; k0 += 4) {
+          float4 q[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (k0 + u < S) q[u] = p[(k0 + u) * (pstride / 4)];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (k0 + u < S) {
+              v.x += q[u].x;
+              v.y += q[u].y;
+              v.z += q[u].z;
+              v.w += q[u].w;
+            }
+        }
+        reinterpret_cast<float4*>(xr)[ch] = v;
+      }
+      xv[c] = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+  }
+  const int dst = row_out ? row_out[r] : r;
+  if (dst < 0) return;  // the whole workgroup: no barrier below is skipped by part of it
+  ss = wave_sum(ss);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < (T >> 6); ++w) tot += red[w];
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  uint16_t* hh = h_hi + (size_t)dst * d;
+  uint16_t* hl = h_lo + (size_t)dst * d;
+#pragma unroll
+  for (int c = 0; c < RN_MAX_CHUNKS; ++c) {
+    const int ch = t + c * T;
+    if (ch < nch) {
+      const uint2 gv = reinterpret_cast<const uint2*>(gain)[ch];
+      store_split4(hh, hl, (size_t)ch * 4, xv[c].x * inv * lo_bf(gv.x), xv[c].y * inv * hi_bf(gv.x),
+                   xv[c].z * inv * lo_bf(gv.y), xv[c].w * inv * hi_bf(gv.y));
+    }
+  }
+}
+
+hipError_t launch_resid_norm(float* x, const float* part, int32_t S, int32_t R,
+                             const int32_t* row_out, const int32_t* out_row, int32_t n_out,
+                             const uint16_t* gain, int32_t d, float eps, uint16_t* h_hi,
+                             uint16_t* h_lo, hipStream_t st) {
+  if (R <= 0) return hipSuccess;
+  const int nch = d / 4;
+  int T = (nch + RN_MAX_CHUNKS - 1) / RN_MAX_CHUNKS;  // threads for at most RN_MAX_CHUNKS each
+  T = std::max(T, std::min(nch, 1024));               // and up to one chunk per thread
+  T = std::min(1024, (T + 63) / 64 * 64);
+  if ((size_t)T * RN_MAX_CHUNKS < (size_t)nch) return hipErrorInvalidValue;
+  const int extra = row_out ? n_out : 0;
+  resid_norm_kernel<<<R + extra, T, 0, st>>>(x, part, S, R, row_out, out_row, gain, d, eps, h_hi,
+                                             h_lo);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------- RoPE + KV append
 //
 // Block (hd/2, 4): x = pair index i (element i pairs with i + hd/2), y = one
@@ -238,7 +343,8 @@ hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int32_t R, const 
 // reads a host-built fp64 table of (cos, sin) per (position, i) and is
 // evaluated in fp64, so a cached key is its exact rotation rounded once.
 
-__global__ void rope_append_kernel(const float* __restrict__ qkv, int R,
+__global__ void rope_append_kernel(float* __restrict__ qkv, const float* __restrict__ part, int S,
+                                   int R,
                                    const int32_t* __restrict__ row_seq,
                                    const int32_t* __restrict__ row_pos,
                                    const int32_t* __restrict__ tables, int max_blocks_per_seq,
@@ -256,8 +362,23 @@ __global__ void rope_append_kernel(const float* __restrict__ qkv, int R,
   const int s = row_seq[r];
   if (s < 0) return;
   const int pos = row_pos[r];
-  const float* src = qkv + (size_t)r * slots * hd + (size_t)j * hd;
-  float a = src[i], b = src[i + half];
+  float* src = qkv + (size_t)r * slots * hd + (size_t)j * hd;
+  float a, b;
+  if (S > 1) {  // the projection's split partials, summed in split order
+    const size_t stride = (size_t)R * slots * hd;
+    const float* p = part + (size_t)r * slots * hd + (size_t)j * hd;
+    a = p[i];
+    b = p[i + half];
+    for (int k = 1; k < S; ++k) {
+      a += p[k * stride + i];
+      b += p[k * stride + i + half];
+    }
+    src[i] = a;  // the projection itself, for inspection
+    src[i + half] = b;
+  } else {
+    a = src[i];
+    b = src[i + half];
+  }
   if (j < hq + hkv) {
     const double2 cs = rope_cs[(size_t)pos * half + i];
     const double da = a, db = b;
@@ -296,16 +417,17 @@ __global__ void rope_append_kernel(const float* __restrict__ qkv, int R,
   }
 }
 
-hipError_t launch_rope_append(const float* qkv, int32_t R, const StepMeta& m, const RowMaps& maps,
-                              const double* rope_cs, const ModelDims& md, uint16_t* q_hi,
-                              uint16_t* q_lo, uint16_t* pool_k, uint16_t* pool_v,
-                              uint32_t* status, hipStream_t st) {
+hipError_t launch_rope_append(float* qkv, const float* part, int32_t S, int32_t R,
+                              const StepMeta& m, const RowMaps& maps, const double* rope_cs,
+                              const ModelDims& md, uint16_t* q_hi, uint16_t* q_lo,
+                              uint16_t* pool_k, uint16_t* pool_v, uint32_t* status,
+                              hipStream_t st) {
   if (R <= 0) return hipSuccess;
   const int slots = md.n_heads + 2 * md.n_kv_heads;
   const int groups = (slots + 3) / 4;
   dim3 block(md.head_dim / 2, 4);
   rope_append_kernel<<<R * groups, block, 0, st>>>(
-      qkv, R, maps.row_seq, maps.row_pos, m.block_tables, m.max_blocks_per_seq,
+      qkv, part, S, R, maps.row_seq, maps.row_pos, m.block_tables, m.max_blocks_per_seq,
       reinterpret_cast<const double2*>(rope_cs), md.n_heads, md.n_kv_heads, md.head_dim,
       md.block_size, md.num_blocks, q_hi, q_lo, pool_k, pool_v, status);
   return hipGetLastError();
