@@ -19,10 +19,11 @@
 // w*C + 64k + l, k = 0..K-1: every global access is coalesced, and the
 // ascending-id order is (wave, k, lane), so ascending-id questions (the CDF
 // of S6, ties at a threshold) take a ballot or a wave prefix per k plus a
-// prefix over the 16 waves. The row's e values live in a workspace row
-// (indexed by id, L2-resident between passes; 64 values per thread do not
-// fit the 128 registers a 1024-thread workgroup leaves); dropped ids hold
-// -1. Top-k and top-p thresholds come from a
+// prefix over the 16 waves. The row's e values (dropped ids hold -1) live
+// on chip when V <= 65536: a thread's first 28 in registers, the other 36
+// in LDS (144 KB per workgroup), so the passes below never leave the CU;
+// larger vocabularies keep them in a workspace row indexed by id (coalesced,
+// L2/MALL-resident between passes). Top-k and top-p thresholds come from a
 // bisection over the bit patterns of e (non-negative floats order like
 // their bits): each step one count or mass sum over the row, with no atomics
 // and no sort; ties at the threshold are kept in ascending id order.
@@ -149,28 +150,41 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
   return v;
 }
 
-// The per-thread row values: registers for K <= SMP_KREG, else the
-// workspace row (coalesced, indexed by id).
+// The per-thread row values (ids base + 64 k, k < K). REGS (K <= SMP_KREG):
+// the first SMP_KR in registers, the rest in LDS ([k - SMP_KR][thread], the
+// caller's slice); otherwise the workspace row, indexed by id.
 #define SMP_KREG 64
+#define SMP_KR 28
 
-// Loops over a thread's K values: with registers the bound is the constant
-// SMP_KREG (fully unrolled, so the array is indexed statically) and the
-// iterations past K are skipped.
+// Loops over a thread's K values. With REGS the bound is the constant
+// SMP_KREG, fully unrolled so that the register array is indexed statically,
+// the iterations past K are skipped, and each body starts with a scheduling
+// barrier: without it the compiler hoists every iteration's compares and
+// ballots at once, which does not fit the 128 registers a 1024-thread
+// workgroup leaves each wave.
 #define SMP_FOR_K(k)                                                   \
   _Pragma("unroll") for (int k = 0; k < (REGS ? SMP_KREG : K); ++k) \
     if (!REGS || k < K)
 
 template <bool REGS>
 struct RowVals {
-  float r[REGS ? SMP_KREG : 1];
-  float* g;  // workspace row base (ids), used when !REGS
+  float r[REGS ? SMP_KR : 1];
+  float* g;  // REGS: this thread's LDS slice; otherwise the workspace row
   __device__ __forceinline__ float get(int k, int id) const {
-    if constexpr (REGS) return r[k];
-    else return g[id];
+    if constexpr (REGS)
+      return k < SMP_KR ? r[k] : g[(k - SMP_KR) * SMP_THREADS];
+    else
+      return g[id];
   }
   __device__ __forceinline__ void set(int k, int id, float v) {
-    if constexpr (REGS) r[k] = v;
-    else g[id] = v;
+    if constexpr (REGS) {
+      if (k < SMP_KR)
+        r[k] = v;
+      else
+        g[(k - SMP_KR) * SMP_THREADS] = v;
+    } else {
+      g[id] = v;
+    }
   }
 };
 
@@ -182,7 +196,7 @@ template <bool BY_MASS, bool REGS>
 __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K, int base, double need,
                                   SmpShared& sh) {
   uint32_t lo = 0x7f800000u, hi = 0u;
-  SMP_FOR_K(k) {
+  SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
     const float v = e.get(k, base + 64 * k);
     if (v >= 0.f) {
       lo = min(lo, __float_as_uint(v));
@@ -195,7 +209,7 @@ __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K,
     const uint32_t mid = lo + (hi - lo) / 2u;
     double f = 0.0;
     int c = 0;
-    SMP_FOR_K(k) {
+    SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
       const float v = e.get(k, base + 64 * k);
       if (v >= 0.f && __float_as_uint(v) >= mid) {
         if (BY_MASS) f += v;
@@ -219,7 +233,7 @@ __device__ __forceinline__ double smp_keep(RowVals<REGS>& e, int K, int base, ui
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int eq_wave = 0;  // equals in this wave's range (same in every lane)
-  SMP_FOR_K(k) {
+  SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
     const float v = e.get(k, base + 64 * k);
     eq_wave += __popcll(__ballot(v >= 0.f && __float_as_uint(v) == tau));
   }
@@ -229,7 +243,7 @@ __device__ __forceinline__ double smp_keep(RowVals<REGS>& e, int K, int base, ui
   for (int x = 0; x < w; ++x) eq_before += sh.wave_i[x];
   __syncthreads();
   double own = 0.0;
-  SMP_FOR_K(k) {
+  SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
     const int id = base + 64 * k;
     const float v = e.get(k, id);
     const bool is_eq = v >= 0.f && __float_as_uint(v) == tau;
@@ -252,11 +266,11 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int base = w * 64 * K + lane;  // this thread's id at k = 0; ids step by 64
   RowVals<REGS> e;
-  e.g = scratch_row;
+  e.g = scratch_row;  // REGS: the caller passes its LDS slice base + threadIdx.x
 
   // S1 penalties (+ S2 division)
   float zmax = -INFINITY;
-  SMP_FOR_K(k) {
+  SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
     const int id = base + 64 * k;
     float z = -INFINITY;
     if (id < V) {
@@ -272,7 +286,7 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
   int token;
   if (P.temperature == 0.f) {  // greedy on the penalised logits, lowest id
     int cand = 0x7fffffff;
-    SMP_FOR_K(k) {
+    SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
       const int id = base + 64 * k;
       if (id < V && e.get(k, id) == zmax) cand = min(cand, id);
     }
@@ -281,7 +295,7 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
   } else {
     // S3
     double own = 0.0;
-    SMP_FOR_K(k) {
+    SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
       const int id = base + 64 * k;
       float v = -1.f;
       if (id < V) {
@@ -295,7 +309,7 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
     if (P.top_k > 0 && P.top_k < V) {
       const uint32_t tau = smp_threshold<false>(e, K, base, (float)P.top_k, sh);
       int above = 0;
-      SMP_FOR_K(k) {
+      SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
         const float v = e.get(k, base + 64 * k);
         if (v >= 0.f && __float_as_uint(v) > tau) ++above;
       }
@@ -309,7 +323,7 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
       const uint32_t tau = smp_threshold<true>(e, K, base, target, sh);
       const double tauf = (double)__uint_as_float(tau);
       double above = 0.0;
-      SMP_FOR_K(k) {
+      SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
         const float v = e.get(k, base + 64 * k);
         if (v >= 0.f && __float_as_uint(v) > tau) above += v;
       }
@@ -338,7 +352,7 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
     int cand = 0x7fffffff, last = -1;
     if (prefix + wsum > r) {  // this wave's range reaches past r
       double carry = prefix;
-      SMP_FOR_K(k) {
+      SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
         const int id = base + 64 * k;
         const float v = e.get(k, id);
         const double kv = v >= 0.f ? (double)v : 0.0;
@@ -352,7 +366,7 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
         carry = __shfl(run, 63, 64);  // run already holds carry
       }
     }
-    SMP_FOR_K(k) {
+    SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
       const int id = base + 64 * k;
       if (e.get(k, id) >= 0.f) last = id;
     }
@@ -361,7 +375,7 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
     if (token < 0) token = 0;
   }
   // S7 counts: decay every id, then count the token
-  SMP_FOR_K(k) {
+  SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
     const int id = base + 64 * k;
     if (id < V) {
       float c = mul_rounded(crow[id], P.penalty_decay);
@@ -372,12 +386,16 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
   if (threadIdx.x == 0) *token_out = token;
 }
 
+// REGS: the row values in registers and dynamic LDS (V <= SMP_KREG *
+// SMP_THREADS); otherwise in the workspace row of this output.
+template <bool REGS>
 __global__ __launch_bounds__(SMP_THREADS) void sampler_kernel(
     const float* __restrict__ logits, int V, int K, const int32_t* __restrict__ slots,
     const int32_t* __restrict__ step_ids, const int32_t* __restrict__ out_seq,
     const SlotParams* __restrict__ params, float* __restrict__ counts, int max_slots,
     float* __restrict__ scratch, int32_t* __restrict__ tokens, uint32_t* status) {
   __shared__ SmpShared sh;
+  extern __shared__ float smp_lds[];  // REGS: [SMP_KREG - SMP_KR][SMP_THREADS]
   const int j = blockIdx.x;
   const int sidx = out_seq ? out_seq[j] : j;
   const int slot = slots[sidx];
@@ -392,8 +410,8 @@ __global__ __launch_bounds__(SMP_THREADS) void sampler_kernel(
   const uint32_t step = (uint32_t)step_ids[sidx];
   const float* lrow = logits + (size_t)j * V;
   float* crow = counts + (size_t)slot * V;
-  float* srow = scratch + (size_t)j * K * SMP_THREADS;
-  sampler_row<false>(lrow, crow, srow, V, K, P, step, tokens + j, sh);
+  float* vals = REGS ? smp_lds + threadIdx.x : scratch + (size_t)j * K * SMP_THREADS;
+  sampler_row<REGS>(lrow, crow, vals, V, K, P, step, tokens + j, sh);
 }
 
 int32_t sampler_row_floats(int32_t V) {
@@ -407,8 +425,23 @@ hipError_t launch_sampler(const float* logits, int32_t n, int32_t V, const int32
                           uint32_t* status, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   const int K = sampler_row_floats(V) / SMP_THREADS;
-  sampler_kernel<<<n, SMP_THREADS, 0, st>>>(logits, V, K, slots, step_ids, out_seq, params,
-                                             counts, max_slots, scratch, tokens, status);
+  if (K <= SMP_KREG) {
+    const size_t lds = (size_t)(SMP_KREG - SMP_KR) * SMP_THREADS * sizeof(float);
+    static bool lds_set = false;  // above 64 KB the launch must be allowed first
+    if (!lds_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sampler_kernel<true>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      lds_set = true;
+    }
+    sampler_kernel<true><<<n, SMP_THREADS, lds, st>>>(logits, V, K, slots, step_ids, out_seq,
+                                                       params, counts, max_slots, scratch, tokens,
+                                                       status);
+  } else {
+    sampler_kernel<false><<<n, SMP_THREADS, 0, st>>>(logits, V, K, slots, step_ids, out_seq,
+                                                      params, counts, max_slots, scratch, tokens,
+                                                      status);
+  }
   return hipGetLastError();
 }
 

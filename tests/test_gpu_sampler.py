@@ -1,6 +1,7 @@
-"""GPU parity of the batched sampler on identical fp32 logits (vocab 65536;
-temperature 1.0, top_p 0.3, top_k 0, frequency penalty 1.0, decay 0.996 and
-variants), against the oracle's fp32 sampler. Token ids must agree wherever
+"""GPU parity of the batched sampler on identical fp32 logits (vocab 65536,
+whose rows the kernel holds on chip, and 151936, whose rows it keeps in the
+workspace; temperature 1.0, top_p 0.3, top_k 0, frequency penalty 1.0, decay
+0.996 and variants), against the oracle's fp32 sampler. Token ids must agree wherever
 the draw is not within 1e-3 (relative mass) of a boundary that decides it:
 the chosen id's CDF interval and the top-p cut. The penalty counts after the
 update must agree bit for bit on rows whose tokens agree."""
@@ -48,25 +49,38 @@ def margin_ok(info, sp, tol=5e-7):
     return bool(ok)
 
 
+def sampler_engine(shape):
+    w = synth.make_weights(shape, seed=3)
+    return make_engine(shape, weights_to(w, "cuda"), block_size=32, num_blocks=8,
+                       max_blocks_per_seq=8, max_rows=256, max_seqs=256, max_position=256,
+                       max_slots=256)
+
+
 @pytest.fixture(scope="module")
 def engine():
-    w = synth.make_weights(SHAPE, seed=3)
-    eng = make_engine(SHAPE, weights_to(w, "cuda"), block_size=32, num_blocks=8,
-                      max_blocks_per_seq=8, max_rows=256, max_seqs=256, max_position=256,
-                      max_slots=256)
+    eng = sampler_engine(SHAPE)
     yield eng
     eng.close()
 
 
-def test_sampler_matches_oracle_on_identical_logits(engine):
-    n = 256
+@pytest.fixture(scope="module")
+def engine_wide():
+    eng = sampler_engine(configs.ModelShape("tiny-v151936", 1, 256, 4, 2, 64, 688, 151936))
+    yield eng
+    eng.close()
+
+
+@pytest.mark.parametrize("vocab,n", [(V, 256), (151936, 48)])
+def test_sampler_matches_oracle_on_identical_logits(engine, engine_wide, vocab, n):
+    engine = engine if vocab == V else engine_wide
+    V_ = vocab
     rng_scale = synth.uniform_ints(5, "scale", n, 1, 4)
-    logits = np.empty((n, V), np.float32)
+    logits = np.empty((n, V_), np.float32)
     for i in range(n):
-        z = synth.normal_tensor(5, f"lg{i}", (V,), 1.0).float().numpy()
+        z = synth.normal_tensor(5, f"lg{i}", (V_,), 1.0).float().numpy()
         logits[i] = z * np.float32(rng_scale[i])
     # a 64-token history per row gives the counts (decay, then count)
-    counts = np.zeros((n, V), np.float32)
+    counts = np.zeros((n, V_), np.float32)
     hist = synth.uniform_ints(5, "hist", n * 64, 0, 2047).reshape(n, 64)
     for i in range(n):
         for t in hist[i]:
@@ -106,7 +120,7 @@ def test_sampler_matches_oracle_on_identical_logits(engine):
         if g_tok[i] == tok:
             agree += 1
             assert np.array_equal(g_counts[i], c), f"row {i}: counts differ"
-    print(f"sampler rows decidable: {checked} of {n}")
+    print(f"sampler rows decidable (vocab {V_}): {checked} of {n}")
     # flat kept sets (top_p 1.0 or 0.9) have ids worth ~1e-5 of the mass each,
     # so many of their draws land within the bound of an interval edge
     assert checked >= int(0.7 * n), f"only {checked} of {n} rows were decidable"
