@@ -336,6 +336,288 @@ __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
     *reinterpret_cast<float4*>(op + 16 * t) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
 }
 
+// ------------------------------------------------------------ block kernel
+//
+// Prefill chunks: a work item is (sequence, KV head g, block of 256 query
+// columns = 256/G consecutive rows x the G heads of g, key split), run by a
+// workgroup of 8 waves, each owning two 16-column tiles (the per-tile
+// kernel's tiles, so the MFMA algebra, the online softmax and the partial
+// layout are the same and the same combine follows). The workgroup stages
+// each 32-key step of K and V^T once in LDS for all 16 tiles, by direct
+// global->LDS copies (16 KB per step at head_dim 128: 2 per wave) into a
+// 6-step ring (4 steps in flight while one is computed), instead of every
+// tile reading its own copy of the prefix.
+// Per-lane copy sources lay the stage out conflict-free for the MFMA
+// operand reads: K as [8-dim chunk][key] and V^T as [8-key chunk][dim], so
+// the 16 lanes that read different keys (or dims) hit consecutive 16-byte
+// slots. Block sizes of 32 and up only (a 32-key step lies in one block).
+#define ATB_WAVES 8
+#define ATB_CT 2                              // 16-column tiles per wave
+#define ATB_COLS (ATB_WAVES * ATB_CT * 16)    // query columns per item
+static_assert(ATB_COLS == ATT_BLOCK_COLS, "the host plans items of ATT_BLOCK_COLS columns");
+#define ATB_STAGES 6
+
+template <int HD, int BS>
+__global__ __launch_bounds__(64 * ATB_WAVES) void attention_block_kernel(
+    const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, StepMeta m,
+    RowMaps maps, ModelDims md, AttnPlan ap, const uint16_t* __restrict__ pool_k,
+    const uint16_t* __restrict__ pool_v, float* __restrict__ part_ml,
+    float* __restrict__ part_o, uint32_t* status) {
+  static_assert(BS >= 32 && BS % 32 == 0, "a 32-key step must lie in one block");
+  constexpr int QK_STEPS = HD / 32;   // MFMAs over head_dim
+  constexpr int DT = HD / 16;         // output d tiles
+  constexpr int NK = HD / 8 * 32;     // 16-byte K slots per step ([chunk][key])
+  constexpr int NSLOT = 8 * HD;       // K + V^T slots per step
+  constexpr int CPW = NSLOT / 64 / ATB_WAVES;  // copies per wave per step
+  static_assert(NSLOT % (64 * ATB_WAVES) == 0, "copies per wave");
+  extern __shared__ uint4 ring_lds[];  // [ATB_STAGES][NSLOT]
+  __shared__ int s_tbl[ATT_TBL];
+  auto ring = [&](int j) { return ring_lds + (size_t)j * NSLOT; };
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n_seqs = m.n_seqs;
+  const int item = blockIdx.x;
+  const int total = uniform(maps.item0b[n_seqs]);
+  if (item >= total) return;  // the whole workgroup
+  const int s = uniform(find_seq(maps.item0b, n_seqs, item));
+  const int G = md.n_heads / md.n_kv_heads;
+  const int rpt = 16 / G;               // rows per 16-column tile
+  const int rpb = ATB_COLS / G;         // rows per item
+  const int nn = uniform(m.n_new[s]), ctx = uniform(m.ctx_lens[s]);
+  const int qblocks = (nn + rpb - 1) / rpb;
+  const int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
+  int local = item - uniform(maps.item0b[s]);
+  const int qb = local % qblocks;
+  local /= qblocks;
+  const int sp = local % splits;
+  const int g = local / splits;
+  const int row_lo = qb * rpb;
+  const int last_row = min(nn, row_lo + rpb) - 1;
+  const int k_lo = sp * ap.split_len;
+  const int k_hi = min(k_lo + ap.split_len, ctx + last_row + 1);
+  if (k_lo >= k_hi) return;  // no keys of this split for these rows: the whole workgroup
+
+  // The item's block-table slice.
+  const int32_t* table = m.block_tables + (size_t)s * m.max_blocks_per_seq;
+  const int b0 = k_lo / BS;
+  const int nb = (k_hi - 1) / BS - b0 + 1;  // <= ATT_TBL (host-side split cap)
+  if (nb > ATT_TBL) {
+    if (threadIdx.x == 0) raise_status(status, ST_BAD_SHAPE);
+    return;  // the whole workgroup
+  }
+  bool bad_block = false;
+  for (int i = threadIdx.x; i < nb; i += 64 * ATB_WAVES) {
+    int blk = table[b0 + i];
+    if (blk < 0 || blk >= md.num_blocks) {
+      bad_block = true;
+      blk = 0;
+    }
+    s_tbl[i] = blk;
+  }
+
+  // This wave's two tiles: column lr of tile ct is row c_row, head c_head.
+  const int row0 = uniform(maps.seq_row0[s]);
+  int c_row[ATB_CT], c_head[ATB_CT], col_end[ATB_CT], mask_from[ATB_CT], tile_hi[ATB_CT];
+  bool c_ok[ATB_CT];
+  bf16x8_t qf[ATB_CT][2][QK_STEPS];
+  int wave_hi = k_lo;
+#pragma unroll
+  for (int ct = 0; ct < ATB_CT; ++ct) {
+    const int t = wave * ATB_CT + ct;
+    const int tr0 = row_lo + t * rpt;  // the tile's first row
+    c_row[ct] = tr0 + lr / G;
+    c_head[ct] = g * G + lr % G;
+    c_ok[ct] = c_row[ct] <= last_row;
+    const int c_end = c_ok[ct] ? min(k_hi, ctx + c_row[ct] + 1) : k_lo;
+    // idle columns take k_hi: their values are never written
+    col_end[ct] = c_ok[ct] ? c_end : k_hi;
+    int mf = col_end[ct];
+#pragma unroll
+    for (int o_ = 1; o_ < 16; o_ <<= 1) mf = min(mf, __shfl_xor(mf, o_, 64));
+    mask_from[ct] = uniform(mf);
+    tile_hi[ct] = tr0 <= last_row ? min(k_hi, ctx + min(last_row, tr0 + rpt - 1) + 1) : k_lo;
+    wave_hi = max(wave_hi, tile_hi[ct]);
+    const size_t at =
+        ((size_t)(row0 + min(c_row[ct], nn - 1)) * md.n_heads + c_head[ct]) * HD + 8 * lg;
+#pragma unroll
+    for (int j = 0; j < QK_STEPS; ++j) {
+      qf[ct][0][j] = as_bf16x8(*reinterpret_cast<const uint4*>(q_hi + at + 32 * j));
+      qf[ct][1][j] = as_bf16x8(*reinterpret_cast<const uint4*>(q_lo + at + 32 * j));
+    }
+  }
+  __syncthreads();  // the table slice is staged
+
+  const size_t head_stride = (size_t)BS * HD;  // one (block, kv head) tile
+  const size_t blk_stride = (size_t)md.n_kv_heads * head_stride;
+  const uint16_t* kbase = pool_k + (size_t)g * head_stride;
+  const uint16_t* vbase = pool_v + (size_t)g * head_stride;
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);
+  const int n_it = (k_hi - k_lo + 31) / 32;
+
+  // Step c's copies into ring slot j: this wave's copies x = wave * CPW + i
+  // cover slots x * 64 + lane; K slots [chunk][key], then V^T [key chunk][dim].
+  auto issue = [&](int j, int c) {
+    const int p0 = k_lo + 32 * c;
+    const int blk = s_tbl[p0 / BS - b0];
+    const int off0 = p0 % BS;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int slot = (wave * CPW + i) * 64 + lane;
+      const uint16_t* src;
+      if (slot < NK) {
+        const int ch = slot / 32, key = slot % 32;
+        src = kbase + (size_t)blk * blk_stride + (size_t)(off0 + key) * HD + 8 * ch;
+      } else {
+        const int v = slot - NK, q = v / HD, d = v % HD;
+        src = vbase + (size_t)blk * blk_stride + (size_t)d * BS + off0 + 8 * q;
+      }
+      copy16_to_lds(src, ring(j) + (wave * CPW + i) * 64);
+    }
+  };
+
+  floatx4_t o[ATB_CT][DT];
+  float m_run[ATB_CT], l_run[ATB_CT];
+#pragma unroll
+  for (int ct = 0; ct < ATB_CT; ++ct) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[ct][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[ct] = -INFINITY;
+    l_run[ct] = 0.f;
+  }
+  const int krow0 = 8 * (lr >> 2) + (lr & 3);
+
+  // One 32-key step of one tile: scores, online softmax, PV (the per-tile
+  // kernel's arithmetic, with K and V^T fragments read from the stage).
+  auto tile_step = [&](int ct, const uint4 (&kf)[2][QK_STEPS], uint4 (&vf)[DT], int p0) {
+    floatx4_t sacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sacc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < QK_STEPS; ++j) {
+        sacc[t] = mfma16x16x32(as_bf16x8(kf[t][j]), qf[ct][0][j], sacc[t]);
+        sacc[t] = mfma16x16x32(as_bf16x8(kf[t][j]), qf[ct][1][j], sacc[t]);
+      }
+    }
+    float sv[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i + 4 * t] = sacc[t][i] * scale;
+    if (p0 + 32 > mask_from[ct]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int p = p0 + 8 * lg + (e & 3) + 4 * (e >> 2);
+        if (p >= col_end[ct]) sv[e] = -INFINITY;
+      }
+    }
+    float cmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float m_new = fmaxf(m_run[ct], cmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_use);
+    m_run[ct] = m_new;
+    uint32_t p1[4], p2[4], p3[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = __builtin_amdgcn_exp2f(sv[2 * e] - m_use);
+      const float b = __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_use);
+      psum += a + b;
+      const float a1 = __uint_as_float(__float_as_uint(a) & 0xffff0000u);
+      const float b1 = __uint_as_float(__float_as_uint(b) & 0xffff0000u);
+      const float ra = a - a1, rb = b - b1;
+      const float a2 = __uint_as_float(__float_as_uint(ra) & 0xffff0000u);
+      const float b2 = __uint_as_float(__float_as_uint(rb) & 0xffff0000u);
+      const float a3 = ra - a2, b3 = rb - b2;
+      p1[e] = __builtin_amdgcn_perm(__float_as_uint(b1), __float_as_uint(a1), 0x07060302u);
+      p2[e] = __builtin_amdgcn_perm(__float_as_uint(b2), __float_as_uint(a2), 0x07060302u);
+      p3[e] = __builtin_amdgcn_perm(__float_as_uint(b3), __float_as_uint(a3), 0x07060302u);
+    }
+    l_run[ct] = l_run[ct] * alpha + psum;
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[ct][t] = o[ct][t] * alpha;
+    }
+    const bf16x8_t pf1 = as_bf16x8(make_uint4(p1[0], p1[1], p1[2], p1[3]));
+    const bf16x8_t pf2 = as_bf16x8(make_uint4(p2[0], p2[1], p2[2], p2[3]));
+    const bf16x8_t pf3 = as_bf16x8(make_uint4(p3[0], p3[1], p3[2], p3[3]));
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[ct][t] = mfma16x16x32(as_bf16x8(vf[t]), pf1, o[ct][t]);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[ct][t] = mfma16x16x32(as_bf16x8(vf[t]), pf2, o[ct][t]);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[ct][t] = mfma16x16x32(as_bf16x8(vf[t]), pf3, o[ct][t]);
+  };
+
+  // The ring: step c + ATB_STAGES - 1 is issued right after the barrier of
+  // step c, and the wait for step c is an exact vector-memory count (every
+  // issue is CPW copies per wave; past the last step the last step is
+  // re-issued, never computed).
+#pragma unroll
+  for (int j = 0; j < ATB_STAGES - 1; ++j) issue(j, min(j, n_it - 1));
+  for (int c = 0; c < n_it; ++c) {
+    // step c's copies landed; those of the next ATB_STAGES - 2 steps may not have
+    wait_vmem<(ATB_STAGES - 2) * CPW>();
+    __syncthreads();
+    issue((c + ATB_STAGES - 1) % ATB_STAGES, min(c + ATB_STAGES - 1, n_it - 1));
+    const int p0 = k_lo + 32 * c;
+    if (p0 < wave_hi) {
+      const uint4* st = ring(c % ATB_STAGES);
+      uint4 kf[2][QK_STEPS], vf[DT];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < QK_STEPS; ++j) kf[t][j] = st[(4 * j + lg) * 32 + krow0 + 4 * t];
+#pragma unroll
+      for (int t = 0; t < DT; ++t) vf[t] = st[NK + lg * HD + 16 * t + lr];
+      // Stale V elements of keys past the range (last step only) are zeroed:
+      // their P is 0, but 0 * NaN would not be.
+      if (p0 + 32 > k_hi) {
+        const int valid = k_hi - (p0 + 8 * lg);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          uint32_t w[4] = {vf[t].x, vf[t].y, vf[t].z, vf[t].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t keep = 2 * e + 1 < valid ? 0xffffffffu : (2 * e < valid ? 0xffffu : 0u);
+            w[e] &= keep;
+          }
+          vf[t] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < ATB_CT; ++ct)
+        if (p0 < tile_hi[ct]) tile_step(ct, kf, vf, p0);
+    }
+  }
+  wait_vmem<0>();  // no LDS copy may land after the workgroup exits
+  if (bad_block) raise_status(status, ST_BAD_BLOCK);
+
+#pragma unroll
+  for (int ct = 0; ct < ATB_CT; ++ct) {
+    float l = l_run[ct];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int c_end = c_ok[ct] ? min(k_hi, ctx + c_row[ct] + 1) : k_lo;
+    if (!c_ok[ct] || k_lo >= c_end) continue;  // this column has no keys in this split
+    const size_t idx =
+        ((size_t)(row0 + c_row[ct]) * md.n_heads + c_head[ct]) * ap.max_splits + sp;
+    if (lg == 0) {
+      part_ml[2 * idx] = m_run[ct];
+      part_ml[2 * idx + 1] = l;
+    }
+    float* op = part_o + idx * HD + 4 * lg;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+      *reinterpret_cast<float4*>(op + 16 * t) =
+          make_float4(o[ct][t][0], o[ct][t][1], o[ct][t][2], o[ct][t][3]);
+  }
+}
+
 // Combine the splits of one (row, head): out = sum_j 2^(m_j - M) o_j /
 // sum_j 2^(m_j - M) l_j over the splits that hold keys of this row, in split
 // order. One wave per (row, head), 4 per workgroup.
@@ -392,12 +674,35 @@ static void launch_items(int blocks, const uint16_t* q_hi, const uint16_t* q_lo,
                                                              pool_v, part_ml, part_o, status);
 }
 
+// Dynamic LDS above 64 KB must be allowed per kernel before its first launch.
+static hipError_t allow_lds(const void* kernel, size_t bytes) {
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 template <int HD>
 static hipError_t launch_hd(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R,
                             const StepMeta& m, const RowMaps& maps, const ModelDims& md,
                             const AttnPlan& ap, const uint16_t* pool_k, const uint16_t* pool_v,
                             float* part_ml, float* part_o, uint16_t* out_hi, uint16_t* out_lo,
                             uint32_t* status, hipStream_t st) {
+  if (ap.block_rows > 0 && ap.grid_items_b > 0) {
+    const size_t lds = (size_t)ATB_STAGES * 8 * HD * 16;  // the K/V ring
+    if (md.block_size == 32) {
+      hipError_t e = allow_lds(reinterpret_cast<const void*>(&attention_block_kernel<HD, 32>), lds);
+      if (e != hipSuccess) return e;
+      attention_block_kernel<HD, 32><<<ap.grid_items_b, 64 * ATB_WAVES, lds, st>>>(
+          q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status);
+    } else if (md.block_size == 64) {
+      hipError_t e = allow_lds(reinterpret_cast<const void*>(&attention_block_kernel<HD, 64>), lds);
+      if (e != hipSuccess) return e;
+      attention_block_kernel<HD, 64><<<ap.grid_items_b, 64 * ATB_WAVES, lds, st>>>(
+          q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status);
+    } else {
+      return hipErrorInvalidValue;  // the host enables the block kernel for 32 and 64 only
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int blocks = (ap.grid_items + ATT_WAVES - 1) / ATT_WAVES;
   if (blocks > 0) {
     switch (md.block_size) {

@@ -71,6 +71,7 @@ WorkspaceLayout workspace_layout(const cbd_config& c) {
   L.out_seq = take(R * 4);
   L.item0 = take((S + 1) * 4);
   L.row_out = take(R * 4);
+  L.item0b = take((S + 1) * 4);
   // fp32 buffers [rows][w] and split buffers (hi plane [rows][w] bf16, then
   // the lo plane) both take 4 bytes per element.
   L.x = take(R * d * 4);
@@ -381,6 +382,15 @@ static AttnPlan plan_attention(const cbd_engine* e, const cbd_step* s) {
   const long long qt = ((long long)s->n_rows * G + 15) / 16 + s->n_seqs;
   const long long sp = (s->max_ctx + ap.split_len - 1) / ap.split_len;
   ap.grid_items = (int32_t)std::min<long long>(qt * sp * c.n_kv_heads, 1LL << 30);
+  // Prefill chunks of 32+ rows run on the block kernel (block sizes that
+  // are multiples of 32).
+  ap.block_rows = c.block_size % 32 == 0 ? ATT_BLOCK_COLS / G : 0;
+  ap.block_min = 32;
+  ap.grid_items_b = 0;
+  if (ap.block_rows > 0) {
+    const long long qb = s->n_rows / ap.block_rows + s->n_seqs;
+    ap.grid_items_b = (int32_t)std::min<long long>(qb * sp * c.n_kv_heads, 1LL << 30);
+  }
   return ap;
 }
 
@@ -410,7 +420,7 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
   RowMaps maps{e->wsp<int32_t>(e->ws.row_seq), e->wsp<int32_t>(e->ws.row_pos),
                e->wsp<int32_t>(e->ws.seq_row0), e->wsp<int32_t>(e->ws.out_row),
                e->wsp<int32_t>(e->ws.out_seq), e->wsp<int32_t>(e->ws.item0),
-               e->wsp<int32_t>(e->ws.row_out)};
+               e->wsp<int32_t>(e->ws.row_out), e->wsp<int32_t>(e->ws.item0b)};
   const AttnPlan ap = plan_attention(e, s);
   const int qkv_n = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   const int qd = c.n_heads * c.head_dim;

@@ -30,6 +30,7 @@ struct RowMaps {
   int32_t* out_seq;    // [max_rows] that sequence
   int32_t* item0;      // [max_seqs + 1] first attention work item per sequence
   int32_t* row_out;    // [max_rows] output index of each row, -1 = emits nothing
+  int32_t* item0b;     // [max_seqs + 1] first block work item per sequence (chunks)
 };
 
 struct ModelDims {
@@ -43,12 +44,19 @@ struct ModelDims {
 // blocks.
 #define ATT_TBL 512
 
+// Query columns (rows x heads of one KV head) per block-kernel work item.
+#define ATT_BLOCK_COLS 256
+
 // Attention work decomposition chosen by the host for one step.
 struct AttnPlan {
   int32_t split_len;   // keys per work item (multiple of 32)
   int32_t max_splits;  // stride of the partial buffers
   int32_t grid_items;  // upper bound of the work items (launch size)
   int32_t max_ctx;     // host bound on ctx + n_new that sized the launch
+  // Sequences with at least block_min new rows (prefill chunks) run on the
+  // block kernel, block_rows rows per work item (0: every sequence runs on
+  // the per-tile kernel); grid_items_b bounds its work items.
+  int32_t block_min, block_rows, grid_items_b;
 };
 
 hipError_t launch_prep(const StepMeta& m, const RowMaps& maps, const ModelDims& md,

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps 
   const int G = md.n_heads / md.n_kv_heads;  // query heads per KV head
   const int cap = m.max_blocks_per_seq * md.block_size;
 
-  int rows = 0, items = 0, outs = 0;
+  int rows = 0, items = 0, outs = 0, items_b = 0;
   for (int s = s0; s < s1; ++s) {
     int nn = m.n_new[s], ctx = m.ctx_lens[s];
     int nn_layout = max(0, min(nn, m.n_rows));
@@ -61,15 +61,18 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps 
     }
     rows += nn_layout;
     if (ok) {
-      int qtiles = (nn * G + 15) / 16;
       int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
-      items += md.n_kv_heads * qtiles * splits;
+      if (ap.block_rows > 0 && nn >= ap.block_min)
+        items_b += md.n_kv_heads * ((nn + ap.block_rows - 1) / ap.block_rows) * splits;
+      else
+        items += md.n_kv_heads * ((nn * G + 15) / 16) * splits;
     }
     outs += m.want_token[s] ? 1 : 0;
   }
-  int tot_rows, tot_items, tot_outs;
+  int tot_rows, tot_items, tot_outs, tot_items_b;
   int r = block_exclusive_scan(rows, buf, &tot_rows);
   int it = block_exclusive_scan(items, buf, &tot_items);
+  int itb = block_exclusive_scan(items_b, buf, &tot_items_b);
   int o = block_exclusive_scan(outs, buf, &tot_outs);
   const bool counts_ok = tot_rows == m.n_rows && tot_outs == m.n_out;
   if (t == 0 && !counts_ok) raise_status(status, ST_BAD_SHAPE);
@@ -82,6 +85,7 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps 
               ctx + nn <= ap.max_splits * ap.split_len && ctx + nn <= md.max_position &&
               ctx + nn <= ap.max_ctx && slot >= 0 && slot < md.max_slots;
     maps.item0[s] = it;
+    maps.item0b[s] = itb;
     maps.seq_row0[s] = r;
     for (int i = 0; i < nn_layout; ++i) {
       if (r + i < m.n_rows) {
@@ -90,9 +94,11 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps 
       }
     }
     if (ok) {
-      int qtiles = (nn * G + 15) / 16;
       int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
-      it += md.n_kv_heads * qtiles * splits;
+      if (ap.block_rows > 0 && nn >= ap.block_min)
+        itb += md.n_kv_heads * ((nn + ap.block_rows - 1) / ap.block_rows) * splits;
+      else
+        it += md.n_kv_heads * ((nn * G + 15) / 16) * splits;
     }
     for (int i = 0; i < nn_layout; ++i)
       if (r + i < m.n_rows) maps.row_out[r + i] = -1;
@@ -107,14 +113,17 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps 
     r += nn_layout;
   }
   __syncthreads();
-  if (t == 0) maps.item0[n] = counts_ok ? tot_items : 0;
+  if (t == 0) {
+    maps.item0[n] = counts_ok ? tot_items : 0;
+    maps.item0b[n] = counts_ok ? tot_items_b : 0;
+  }
   if (!counts_ok) {  // the layout cannot be trusted: refuse every row
     for (int i = t; i < m.n_rows; i += PREP_THREADS) {
       maps.row_seq[i] = -1;
       maps.row_out[i] = -1;
     }
     for (int i = t; i < m.n_out; i += PREP_THREADS) maps.out_row[i] = -1;
-    for (int i = t; i < n; i += PREP_THREADS) maps.item0[i] = 0;
+    for (int i = t; i < n; i += PREP_THREADS) maps.item0[i] = maps.item0b[i] = 0;
   } else {
     for (int i = tot_rows + t; i < m.n_rows; i += PREP_THREADS) {
       maps.row_seq[i] = -1;

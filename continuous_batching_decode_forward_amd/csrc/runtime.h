@@ -88,7 +88,7 @@ class BlockAllocator {
 
 // Offsets (bytes) of everything the engine keeps in the caller's workspace.
 struct WorkspaceLayout {
-  size_t status, row_seq, row_pos, seq_row0, out_row, out_seq, item0, row_out;
+  size_t status, row_seq, row_pos, seq_row0, out_row, out_seq, item0, row_out, item0b;
   size_t x, h, qkv, q, attn, ffn, lm_in, logits, amax_val, amax_idx;
   size_t gemm_part, attn_ml, attn_o, rope, smp;
   size_t total;
