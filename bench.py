@@ -309,6 +309,7 @@ def bench_mixed8b(args):
     (offsets 0..3584). Each step is timed as it is and without its chunk (the
     same 48 decode rows alone); the difference is the chunk's time."""
     import torch
+    from continuous_batching_decode_forward_amd import binding as B
     from continuous_batching_decode_forward_amd import configs, synth
     from continuous_batching_decode_forward_amd.engine import Engine
     shape, wlc = configs.LLAMA8B, configs.MIXED_8B
@@ -339,6 +340,13 @@ def bench_mixed8b(args):
         meta_d = eng.upload_step(slots=seqs_d, block_tables=tab_d, ctx_lens=ctx_d, n_new=nn_d,
                                  tokens=toks_d, want_token=want_d)
         ms_dec, _, _ = time_steps(eng, meta_d, None, tk, reps, 1, stream)
+        kern = None
+        if j in (0, wl["n_steps"] - 1):  # per-step time of each kernel class, all layers
+            kern = {}
+            for name in ("ATTN", "QKV", "O", "GATEUP", "DOWN", "ROPE", "NORM", "LM_HEAD"):
+                _, _, k = time_steps(eng, meta, None, tk, 3, 0, stream,
+                                     profile_class=getattr(B, "CBD_KERNEL_" + name))
+                kern[name.lower() + "_ms"] = round(k[0] * k[1] / 3, 3)
         # redo the mixed step last, so the chunk's K/V is in place for step j + 1
         eng.step_forward(meta, None, tk, stream)
         o = j * wl["chunk"]
@@ -350,6 +358,8 @@ def bench_mixed8b(args):
                      "chunk_ms": chunk_ms, "chunk_tflop": chunk_flops / 1e12,
                      "chunk_mfma_util": chunk_flops / (chunk_ms * 1e-3) / 2.5e15 if chunk_ms > 0 else None,
                      "decode_gbs": dec_bytes / (ms_dec * 1e-3) / 1e9})
+        if kern:
+            rows[-1]["kernel_ms"] = kern
         log(f"[bench] offset {o}: mixed {ms_mixed:.2f} ms, decode-only {ms_dec:.2f} ms")
     torch.cuda.synchronize()
     if eng.status():
