@@ -643,8 +643,9 @@ struct GemmPlan {
   int RT, NT, KW, D, S;
 };
 
-// Rows at or above which the dense path runs.
-#define DENSE_MIN_ROWS 128
+// Rows at or above which the dense path runs: past one stream row group
+// (64 rows) the stream path would fetch every weight once per group.
+#define DENSE_MIN_ROWS 65
 
 static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
   GemmPlan p{};
