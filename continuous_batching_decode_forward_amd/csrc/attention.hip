@@ -30,7 +30,6 @@
 
 namespace cbd {
 
-#define ATT_WAVES 4
 #define ATT_LDS_SEQS 1024  // item0 staged in LDS for up to this many sequences
 
 // Largest s with item0[s] <= item (item0 ascending, item0[0] = 0).
@@ -57,59 +56,64 @@ struct KVTile {
   uint4 v[HD / 16];
 };
 
+// The per-tile schedule. The key steps (32 keys) of every (sequence, query
+// tile) on this kernel are laid end to end in sequence order, the same for
+// each KV head: T steps per head, sequence s starting at step item0[s]. Each
+// head's T steps are cut into pieces of `len` steps, and piece q of head g
+// is run by wave g * per_head + q (mod the P launched waves, which take at
+// most `rounds` pieces each). A piece may cross (sequence, tile) boundaries;
+// each run of it inside one (sequence, tile) is a segment with its own
+// partial result, stored at split index "piece - first piece of that
+// (sequence, tile)". Equal pieces give every wave the same number of K/V
+// bytes, whatever the mix of context lengths.
+struct PieceSched {
+  int len, per_head;
+};
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// The fewest rounds of P waves whose pieces fit in `hi` steps, then the
+// shortest pieces (not below `lo`) that cover T in that many rounds.
+__device__ __forceinline__ PieceSched piece_sched(int T, const AttnPlan& ap, int kvh) {
+  const int wh = max(1, ap.grid_items / kvh);  // waves per KV head
+  int rounds = max(1, ceil_div(ceil_div(max(T, 1), wh), ap.piece_hi));
+  while (ceil_div(T, rounds * wh) > ap.piece_hi) ++rounds;
+  const int len = min(ap.piece_hi, max(ap.piece_lo, ceil_div(T, rounds * wh)));
+  return PieceSched{len, ceil_div(T, len)};
+}
+
+// Key steps of query tile qt of a sequence (its keys are positions
+// 0 .. ctx + its last row).
+__device__ __forceinline__ int tile_steps(int qt, int nn, int ctx, int rpt) {
+  return ceil_div(ctx + min(nn, (qt + 1) * rpt), 32);
+}
+
 // The loads are unconditional and branch-free: a key past the item's range
 // reads a valid pool location (its score is masked to -inf, and its V
 // element is zeroed on the last step), and a block id outside the pool is
 // replaced by block 0 and reported. Block ids come from the wave's slice of
 // the block table staged in LDS, so no K/V address waits on a global load.
+// The kernel is held to 256 registers (accumulators included) so that two
+// waves share each SIMD: one wave's loads stay in flight while the other
+// computes (at one wave per SIMD the key stream stalls on every step).
 template <int HD, int BS>
-__global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
-    const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, StepMeta m,
-    RowMaps maps, ModelDims md, AttnPlan ap, const uint16_t* __restrict__ pool_k,
-    const uint16_t* __restrict__ pool_v, float* __restrict__ part_ml,
-    float* __restrict__ part_o, uint32_t* status) {
+__device__ __forceinline__ void attend_segment(
+    const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, const StepMeta& m,
+    const RowMaps& maps, const ModelDims& md, const AttnPlan& ap,
+    const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v,
+    float* __restrict__ part_ml, float* __restrict__ part_o, uint32_t* status, int* tbl, int s,
+    int g, int qt, int nn, int ctx, int k_lo, int k_hi, int sp) {
   constexpr int QK_STEPS = HD / 32;  // MFMAs over head_dim
   constexpr int DT = HD / 16;        // output d tiles
-  __shared__ int s_item0[ATT_LDS_SEQS + 1];
-  __shared__ int s_tbl[ATT_WAVES][ATT_TBL];
   const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int n_seqs = m.n_seqs;
-  const bool lds_seqs = n_seqs <= ATT_LDS_SEQS;
-  if (lds_seqs)
-    for (int i = threadIdx.x; i <= n_seqs; i += 64 * ATT_WAVES) s_item0[i] = maps.item0[i];
-  __syncthreads();
-  // Everything that selects the work item is the same for the whole wave;
-  // readfirstlane makes that explicit so that the key loop is a scalar loop.
-  const int total = uniform(lds_seqs ? s_item0[n_seqs] : maps.item0[n_seqs]);
-  const int item = blockIdx.x * ATT_WAVES + wave;
-  if (item >= total) return;  // no barrier below this point
-  const int s = uniform(lds_seqs ? find_seq(s_item0, n_seqs, item)
-                                 : find_seq(maps.item0, n_seqs, item));
   const int G = md.n_heads / md.n_kv_heads;
   const int rpt = 16 / G;  // rows per query tile
-  const int nn = uniform(m.n_new[s]), ctx = uniform(m.ctx_lens[s]);
-  const int qtiles = (nn * G + 15) / 16;
-  const int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
-  int local = item - uniform(lds_seqs ? s_item0[s] : maps.item0[s]);
-  const int qt = local % qtiles;
-  local /= qtiles;
-  const int sp = local % splits;
-  const int g = local / splits;
-
   // This lane's query column: row c_row of the sequence, query head c_head.
   const int c_row = qt * rpt + lr / G;
   const int c_head = g * G + lr % G;
   const bool c_ok = lr < rpt * G && c_row < nn;
   const int row0 = uniform(maps.seq_row0[s]);
-  const int last_row = min(nn, (qt + 1) * rpt) - 1;
-  const int k_lo = sp * ap.split_len;
-  const int k_hi = min(k_lo + ap.split_len, ctx + last_row + 1);
-  // The items of a sequence span every (query tile, split) pair; the early
-  // tiles of a chunk longer than one split have no keys in its later splits.
-  // Such a wave stages no block-table entries and must not issue a load.
-  if (k_lo >= k_hi) return;
   const int c_end = c_ok ? min(k_hi, ctx + c_row + 1) : k_lo;  // keys [k_lo, c_end)
 
   // Q as the B operand of S = K.Q^T: lane (lr, lg) holds d = 32 j + 8 lg .. +8
@@ -127,12 +131,16 @@ __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
   // The wave's block-table slice: entries for blocks b0 .. b0 + nb - 1.
   const int32_t* table = m.block_tables + (size_t)s * m.max_blocks_per_seq;
   const int b0 = k_lo / BS;
-  const int nb = (k_hi - 1) / BS - b0 + 1;  // <= ATT_TBL (host-side split cap)
-  if (nb > ATT_TBL) {  // the host caps split_len; refuse rather than overrun LDS
+  const int nb = (k_hi - 1) / BS - b0 + 1;  // <= ATT_TBL (host-side piece cap)
+  if (nb > ATT_TBL) {  // the host caps piece_hi; refuse rather than overrun LDS
     if (lane == 0) raise_status(status, ST_BAD_SHAPE);
     return;
   }
-  int* tbl = s_tbl[wave];
+  // The previous segment's reads of the slice are done before it is
+  // overwritten (LDS operations of one wave complete in order).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   bool bad_block = false;
   for (int i = lane; i < nb; i += 64) {
     int blk = table[b0 + i];
@@ -323,7 +331,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (!c_ok || k_lo >= c_end) return;  // this column has no keys in this split
+  if (!c_ok || k_lo >= c_end) return;  // this column has no keys in this segment
   const size_t idx = ((size_t)(row0 + c_row) * md.n_heads + c_head) * ap.max_splits + sp;
   if (lg == 0) {
     part_ml[2 * idx] = m_run;
@@ -334,6 +342,60 @@ __global__ __launch_bounds__(64 * ATT_WAVES) void attention_kernel(
 #pragma unroll
   for (int t = 0; t < DT; ++t)
     *reinterpret_cast<float4*>(op + 16 * t) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+}
+
+// The kernel is held to 256 registers (accumulators included) so that two
+// waves share each SIMD: one wave's loads stay in flight while the other
+// computes (at one wave per SIMD the key stream stalls on every step).
+template <int HD, int BS>
+__global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(
+    const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, StepMeta m,
+    RowMaps maps, ModelDims md, AttnPlan ap, const uint16_t* __restrict__ pool_k,
+    const uint16_t* __restrict__ pool_v, float* __restrict__ part_ml,
+    float* __restrict__ part_o, uint32_t* status) {
+  __shared__ int s_item0[ATT_LDS_SEQS + 1];
+  __shared__ int s_tbl[ATT_WAVES][ATT_TBL];
+  const int wave = uniform(threadIdx.x >> 6);
+  const int n_seqs = m.n_seqs;
+  const bool lds_seqs = n_seqs <= ATT_LDS_SEQS;
+  if (lds_seqs)
+    for (int i = threadIdx.x; i <= n_seqs; i += 64 * ATT_WAVES) s_item0[i] = maps.item0[i];
+  __syncthreads();  // no barrier below this point
+  const int32_t* step0 = lds_seqs ? s_item0 : maps.item0;
+  // Everything that selects a segment is the same for the whole wave;
+  // readfirstlane makes that explicit so that the key loop is a scalar loop.
+  const int T = uniform(step0[n_seqs]);
+  const PieceSched ps = piece_sched(T, ap, md.n_kv_heads);
+  const int n_pieces = ps.per_head * md.n_kv_heads;
+  const int rpt = 16 / (md.n_heads / md.n_kv_heads);
+  for (int p = blockIdx.x * ATT_WAVES + wave; p < n_pieces; p += ap.grid_items) {
+    const int g = p / ps.per_head, q = p % ps.per_head;
+    int b = q * ps.len;
+    const int b_end = min(T, b + ps.len);
+    while (b < b_end) {
+      const int s = uniform(find_seq(step0, n_seqs, b));
+      const int nn = uniform(m.n_new[s]), ctx = uniform(m.ctx_lens[s]);
+      const int s0 = uniform(step0[s]);
+      const int off = b - s0;
+      int qt = 0, qstart = 0, st = tile_steps(0, nn, ctx, rpt);
+      while (off >= qstart + st) {
+        qstart += st;
+        st = tile_steps(++qt, nn, ctx, rpt);
+      }
+      const int rel = off - qstart;
+      const int seg = min(st - rel, b_end - b);
+      const int keys = ctx + min(nn, (qt + 1) * rpt);
+      const int sp = q - (s0 + qstart) / ps.len;
+      if (sp >= ap.max_splits) {  // the host's piece_lo rules this out
+        if ((threadIdx.x & 63) == 0) raise_status(status, ST_BAD_SHAPE);
+      } else {
+        attend_segment<HD, BS>(q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o,
+                               status, s_tbl[wave], s, g, qt, nn, ctx, 32 * rel,
+                               min(keys, 32 * (rel + seg)), sp);
+      }
+      b += seg;
+    }
+  }
 }
 
 // ------------------------------------------------------------ block kernel
@@ -619,8 +681,8 @@ __global__ __launch_bounds__(64 * ATB_WAVES) void attention_block_kernel(
 }
 
 // Combine the splits of one (row, head): out = sum_j 2^(m_j - M) o_j /
-// sum_j 2^(m_j - M) l_j over the splits that hold keys of this row, in split
-// order. One wave per (row, head), 4 per workgroup.
+// sum_j 2^(m_j - M) l_j over the partial results that hold keys of this row,
+// in key order. One wave per (row, head), 4 per workgroup.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps maps, ModelDims md,
                                                            AttnPlan ap, int R,
@@ -641,7 +703,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
     return;
   }
   const int pos = maps.row_pos[r];
-  const int n_sp = pos / ap.split_len + 1;  // splits holding keys 0..pos
+  const int nn = m.n_new[s];
+  int n_sp;  // partial results holding keys 0..pos
+  if (ap.block_rows > 0 && nn >= ap.block_min) {  // block kernel: splits of split_len keys
+    n_sp = pos / ap.split_len + 1;
+  } else {  // per-tile kernel: the pieces over this row's (sequence, tile) steps
+    const PieceSched ps = piece_sched(maps.item0[m.n_seqs], ap, md.n_kv_heads);
+    const int rpt = 16 / (md.n_heads / md.n_kv_heads);
+    const int qt = (r - maps.seq_row0[s]) / rpt;
+    const int ctx = m.ctx_lens[s];
+    int start = maps.item0[s];
+    for (int t = 0; t < qt; ++t) start += tile_steps(t, nn, ctx, rpt);
+    n_sp = (start + pos / 32) / ps.len - start / ps.len + 1;
+  }
   const size_t base = ((size_t)r * md.n_heads + h) * ap.max_splits;
   float M = -INFINITY;
   for (int j = 0; j < n_sp; ++j) M = fmaxf(M, part_ml[2 * (base + j)]);

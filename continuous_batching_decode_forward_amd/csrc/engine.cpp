@@ -15,9 +15,11 @@ namespace cbd {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Key splits per (row, head) the partial buffers hold.
+// Partial-result slots per (row, head): one per 128 positions (at most 64),
+// plus one for a piece of the per-tile schedule that starts inside the range.
 static int32_t attn_cap_splits(const cbd_config& c) {
   int32_t s = (c.max_position + 127) / 128;
-  return std::max(1, std::min(64, s));
+  return std::max(1, std::min(64, s)) + 1;
 }
 
 // Longest key split: a split spans at most ATT_TBL blocks.
@@ -46,7 +48,7 @@ int validate_config(const cbd_config* c) {
     return fail(CBD_E_UNSUPPORTED, "d_model, ffn_dim and vocab must be multiples of 16");
   if (c->d_model > 8192) return fail(CBD_E_UNSUPPORTED, "d_model above 8192");
   if (c->max_seqs > c->max_rows) return fail(CBD_E_INVAL, "max_seqs exceeds max_rows");
-  if ((long long)attn_cap_splits(*c) * attn_split_cap(*c) < c->max_position)
+  if ((long long)(attn_cap_splits(*c) - 1) * attn_split_cap(*c) < c->max_position)
     return fail(CBD_E_UNSUPPORTED, "max_position too long for this block size");
   return CBD_OK;
 }
@@ -249,6 +251,14 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* packed_
   e->slot_state = (uint8_t*)slot_state;
   e->workspace = (uint8_t*)workspace;
   e->stream = (hipStream_t)stream;
+  {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    e->attn_waves = cus * 4 * 2;
+  }
   e->slots.reset(cfg->max_slots);
   if (!e->blocks.reset(cfg->num_blocks, block_order)) {
     delete e;
@@ -370,8 +380,9 @@ static AttnPlan plan_attention(const cbd_engine* e, const cbd_step* s) {
   AttnPlan ap;
   ap.max_splits = e->ws.attn_max_splits;
   ap.max_ctx = s->max_ctx;
-  // Enough work items to fill the chip (about 4096) without slivers shorter
-  // than 64 keys; never more splits than the partial buffers hold.
+  // Block kernel (prefill chunks): keys split into split_len pieces, enough
+  // items to fill the chip (about 4096) without slivers shorter than 64
+  // keys; never more splits than the partial buffers hold.
   long long want = (long long)s->max_ctx * s->n_seqs * c.n_kv_heads / 4096;
   int32_t len = (int32_t)std::max<long long>(64, std::min<long long>(4096, want));
   len = (len + 31) / 32 * 32;
@@ -381,11 +392,24 @@ static AttnPlan plan_attention(const cbd_engine* e, const cbd_step* s) {
   const int G = c.n_heads / c.n_kv_heads;
   const long long qt = ((long long)s->n_rows * G + 15) / 16 + s->n_seqs;
   const long long sp = (s->max_ctx + ap.split_len - 1) / ap.split_len;
-  ap.grid_items = (int32_t)std::min<long long>(qt * sp * c.n_kv_heads, 1LL << 30);
+  // Per-tile kernel: equal pieces of each KV head's key steps (a piece at
+  // least 4 steps, and long enough that the pieces over one (sequence, tile)
+  // fit the partial slots; at most what a block-table slice in LDS covers),
+  // run by the chip's resident waves, or fewer when the step has few keys.
+  const int32_t steps_max = (s->max_ctx + 31) / 32;
+  ap.piece_hi = attn_split_cap(c) / 32;
+  ap.piece_lo = std::max<int32_t>(4, (steps_max + ap.max_splits - 2) / (ap.max_splits - 1));
+  const long long unit = (long long)c.n_kv_heads * ATT_WAVES;
+  const long long p_max = std::max<long long>(1, e->attn_waves / unit) * unit;
+  const long long p_want = c.n_kv_heads * ((qt * steps_max + ap.piece_lo - 1) / ap.piece_lo);
+  ap.grid_items = (int32_t)std::min(p_max, (p_want + unit - 1) / unit * unit);
   // Prefill chunks of 32+ rows run on the block kernel (block sizes that
-  // are multiples of 32).
-  ap.block_rows = c.block_size % 32 == 0 ? ATT_BLOCK_COLS / G : 0;
+  // are multiples of 32). Every sequence has at least one row, so a step
+  // with fewer than block_min + n_seqs - 1 rows has no such chunk: it
+  // launches no block kernel and every sequence runs on the per-tile kernel.
   ap.block_min = 32;
+  ap.block_rows = c.block_size % 32 == 0 ? ATT_BLOCK_COLS / G : 0;
+  if ((long long)s->n_rows - s->n_seqs + 1 < ap.block_min) ap.block_rows = 0;
   ap.grid_items_b = 0;
   if (ap.block_rows > 0) {
     const long long qb = s->n_rows / ap.block_rows + s->n_seqs;

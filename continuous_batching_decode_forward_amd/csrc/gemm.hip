@@ -321,10 +321,13 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S
 // barrier orders the stages. Stages are padded to a multiple of D; the
 // activation pieces at or beyond kend (padding, a K tail) are zeroed in LDS
 // after their copy lands, so the weights read there meet zeros.
+// Two waves per SIMD (256 registers, accumulators included): with the 64 KB
+// LDS ring of 64-row workgroups that is two workgroups per CU, so a grid of
+// up to 512 workgroups (the LM head's) runs in one round.
 #define STREAM_NW 4
 
 template <int RT, int NT, int D, int EPI>
-__global__ __launch_bounds__(64 * STREAM_NW) void gemm_stream_kernel(GemmArgs a, int kc, int S) {
+__global__ __launch_bounds__(64 * STREAM_NW) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_kernel(GemmArgs a, int kc, int S) {
   constexpr int NM = EpiTraits<EPI>::NM;
   constexpr int BLK = RT * 4;                 // 1 KB LDS blocks per stage
   constexpr int LPS = NM * NT * 2 + RT;       // loads per stage per wave
@@ -690,21 +693,19 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
       p.S = long_k && R > 8 ? 2 : 1;
     }
   } else {
+    // Measured at 32 and 64 rows on the 8B shapes: the gate/up pair runs
+    // best as 16-column waves over the whole K (224 workgroups, no partials
+    // and no separate SwiGLU pass); single matrices as 32-column waves with
+    // K split until the grid would pass one workgroup per CU.
     p.stream = true;
     p.KW = 1;
     p.RT = R <= 32 ? 2 : 4;
-    if (vocab || logits) {
-      p.NT = 4;
-    } else if (NM == 2) {
-      p.NT = 2;
-    } else {
-      p.NT = (p.RT == 2 && K >= 8192) ? 1 : 2;
-    }
-    p.D = p.NT == 1 ? 8 : (NM == 2 && p.RT == 2 ? 8 : 4);
+    p.NT = (vocab || logits) ? 4 : (NM == 2 ? 1 : 2);
+    p.D = 4;
     p.S = 1;
     if (!logits) {
       const int groups = (N + 64 * p.NT - 1) / (64 * p.NT) * ((R + 16 * p.RT - 1) / (16 * p.RT));
-      while (groups * p.S < 256 && K / (p.S * 2) >= 512) p.S *= 2;
+      while (groups * p.S * 2 <= 256 && K / (p.S * 2) >= 512) p.S *= 2;
     }
   }
   if (logits) p.S = 1;
@@ -815,10 +816,10 @@ static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
 #define ST(RT_, NT_, D_) \
   if (p.RT == RT_ && p.NT == NT_ && p.D == D_) return launch_stream<RT_, NT_, D_, EPI>(a, p.S, st);
   if constexpr (NM == 2) {
-    ST(2, 2, 8) ST(4, 2, 4)
-    return launch_stream<4, 2, 4, EPI>(a, p.S, st);
+    ST(2, 1, 4) ST(4, 1, 4)
+    return launch_stream<4, 1, 4, EPI>(a, p.S, st);
   } else {
-    ST(2, 1, 8) ST(2, 2, 4) ST(2, 4, 4) ST(4, 2, 4) ST(4, 4, 4)
+    ST(2, 2, 4) ST(2, 4, 4) ST(4, 2, 4) ST(4, 4, 4)
     return launch_stream<4, 2, 4, EPI>(a, p.S, st);
   }
 #undef ST

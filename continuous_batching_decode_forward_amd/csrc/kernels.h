@@ -28,7 +28,7 @@ struct RowMaps {
   int32_t* seq_row0;   // [max_seqs] first row of each sequence
   int32_t* out_row;    // [max_rows] row of the j-th emitting sequence, -1 = none
   int32_t* out_seq;    // [max_rows] that sequence
-  int32_t* item0;      // [max_seqs + 1] first attention work item per sequence
+  int32_t* item0;      // [max_seqs + 1] first key step per sequence of the per-tile schedule
   int32_t* row_out;    // [max_rows] output index of each row, -1 = emits nothing
   int32_t* item0b;     // [max_seqs + 1] first block work item per sequence (chunks)
 };
@@ -38,6 +38,9 @@ struct ModelDims {
   int32_t block_size, num_blocks, max_slots, max_position;
   float rms_eps;
 };
+
+// Waves per workgroup of the per-tile attention kernel.
+#define ATT_WAVES 4
 
 // Block-table entries one attention work item stages in LDS (a wave's
 // slice); split_len is capped so that a split spans at most this many
@@ -49,10 +52,14 @@ struct ModelDims {
 
 // Attention work decomposition chosen by the host for one step.
 struct AttnPlan {
-  int32_t split_len;   // keys per work item (multiple of 32)
+  int32_t split_len;   // keys per block-kernel work item (multiple of 32)
   int32_t max_splits;  // stride of the partial buffers
-  int32_t grid_items;  // upper bound of the work items (launch size)
+  int32_t grid_items;  // waves of the per-tile kernel (a multiple of its workgroup)
   int32_t max_ctx;     // host bound on ctx + n_new that sized the launch
+  // Piece lengths of the per-tile schedule, in 32-key steps: at least
+  // piece_lo (so that no (sequence, tile) spans more than max_splits
+  // pieces), at most piece_hi (a piece's block-table slice fits in LDS).
+  int32_t piece_lo, piece_hi;
   // Sequences with at least block_min new rows (prefill chunks) run on the
   // block kernel, block_rows rows per work item (0: every sequence runs on
   // the per-tile kernel); grid_items_b bounds its work items.

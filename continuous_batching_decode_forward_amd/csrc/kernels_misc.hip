@@ -12,110 +12,164 @@ namespace cbd {
 // One workgroup turns the per-sequence metadata into per-row maps: the
 // sequence and position of every row (rows are the sequences' n_new entries
 // laid end to end, in order), the row each emitting sequence takes its token
-// from (its last row), and the first attention work item of each sequence.
+// from (its last row), and where each sequence's attention work starts (its
+// first key step in the per-tile schedule, or its first block-kernel item).
 // Sequences whose metadata is out of range keep their place in the row
-// layout but are refused: their rows get row_seq = -1 and no work items.
+// layout but are refused: their rows get row_seq = -1 and no attention work.
 
 #define PREP_THREADS 1024
+#define PREP_WAVES (PREP_THREADS / 64)
+// Sequences with more rows than PREP_SHORT (prefill chunks) have their rows
+// written by a whole wave after the scan instead of by their own thread;
+// up to PREP_QUEUE of them per step (any further ones: their own thread).
+#define PREP_SHORT 4
+#define PREP_QUEUE 256
 
-__device__ int block_exclusive_scan(int v, int* buf, int* total) {
-  int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int o = 1; o < PREP_THREADS; o <<= 1) {
-    int add = t >= o ? buf[t - o] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+struct PrepQueued {
+  int s, r, n, ctx, seq, orow;
+};
+
+// Exclusive prefix sums over the workgroup of four per-thread counts, and
+// their totals: a shuffle scan inside each wave, then the 16 wave totals.
+__device__ int4 block_scan4(int4 v, int4* wave_tot, int4* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int4 inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a = __shfl_up(inc.x, o, 64), b = __shfl_up(inc.y, o, 64);
+    const int c = __shfl_up(inc.z, o, 64), d = __shfl_up(inc.w, o, 64);
+    if (lane >= o) {
+      inc.x += a;
+      inc.y += b;
+      inc.z += c;
+      inc.w += d;
+    }
   }
-  int incl = buf[t];
-  *total = buf[PREP_THREADS - 1];
+  if (lane == 63) wave_tot[wave] = inc;
   __syncthreads();
-  return incl - v;
+  int4 base = make_int4(0, 0, 0, 0), tot = make_int4(0, 0, 0, 0);
+#pragma unroll
+  for (int w = 0; w < PREP_WAVES; ++w) {
+    const int4 t = wave_tot[w];
+    if (w < wave) {
+      base.x += t.x;
+      base.y += t.y;
+      base.z += t.z;
+      base.w += t.w;
+    }
+    tot.x += t.x;
+    tot.y += t.y;
+    tot.z += t.z;
+    tot.w += t.w;
+  }
+  *total = tot;
+  return make_int4(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z,
+                   base.w + inc.w - v.w);
+}
+
+__device__ __forceinline__ void prep_write_row(const RowMaps& maps, int row, int seq, int pos,
+                                               int out) {
+  maps.row_seq[row] = seq;
+  maps.row_pos[row] = pos;
+  maps.row_out[row] = out;
 }
 
 __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps maps,
                                                             ModelDims md, AttnPlan ap,
                                                             uint32_t* status) {
-  __shared__ int buf[PREP_THREADS];
+  __shared__ int4 wave_tot[PREP_WAVES];
+  __shared__ PrepQueued queue[PREP_QUEUE];
+  __shared__ int q_cnt;
   const int t = threadIdx.x;
   const int n = m.n_seqs;
   const int per = (n + PREP_THREADS - 1) / PREP_THREADS;
   const int s0 = min(n, t * per), s1 = min(n, s0 + per);
   const int G = md.n_heads / md.n_kv_heads;  // query heads per KV head
   const int cap = m.max_blocks_per_seq * md.block_size;
+  if (t == 0) q_cnt = 0;  // ordered before any use by the scan's barrier
 
-  int rows = 0, items = 0, outs = 0, items_b = 0;
+  // A sequence is served when its counts fit the cache, the key splits, the
+  // positions and its slot; its attention goes to the block kernel when it
+  // has block_min rows or more and the plan has block items.
+  auto valid = [&](int s, int nn, int ctx) {
+    const int slot = m.slots[s];
+    return nn >= 1 && ctx >= 0 && ctx + nn <= cap && ctx + nn <= ap.max_splits * ap.split_len &&
+           ctx + nn <= md.max_position && ctx + nn <= ap.max_ctx && slot >= 0 &&
+           slot < md.max_slots;
+  };
+  // Block kernel: (row block, split, KV head) items. Per-tile kernel: the
+  // key steps of the sequence's query tiles (per KV head), tile qt holding
+  // keys 0 .. ctx + its last row.
+  auto add_items = [&](int nn, int ctx, int& steps, int& items_b) {
+    if (ap.block_rows > 0 && nn >= ap.block_min) {
+      const int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
+      items_b += md.n_kv_heads * ((nn + ap.block_rows - 1) / ap.block_rows) * splits;
+    } else {
+      const int rpt = 16 / G, qtiles = (nn * G + 15) / 16;
+      for (int qt = 0; qt < qtiles; ++qt) steps += (ctx + min(nn, (qt + 1) * rpt) + 31) / 32;
+    }
+  };
+
+  int4 cnt = make_int4(0, 0, 0, 0);  // rows, key steps, block items, outputs
   for (int s = s0; s < s1; ++s) {
-    int nn = m.n_new[s], ctx = m.ctx_lens[s];
-    int nn_layout = max(0, min(nn, m.n_rows));
-    bool ok = nn >= 1 && ctx >= 0 && ctx + nn <= cap &&
-              ctx + nn <= ap.max_splits * ap.split_len && ctx + nn <= md.max_position &&
-              ctx + nn <= ap.max_ctx;
-    int slot = m.slots[s];
-    if (slot < 0 || slot >= md.max_slots) {
-      ok = false;
+    const int nn = m.n_new[s], ctx = m.ctx_lens[s];
+    const int slot = m.slots[s];
+    const bool ok = valid(s, nn, ctx);
+    if (slot < 0 || slot >= md.max_slots)
       raise_status(status, ST_BAD_SLOT);
-    } else if (!ok) {
+    else if (!ok)
       raise_status(status, ST_BAD_SHAPE);
-    }
-    rows += nn_layout;
-    if (ok) {
-      int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
-      if (ap.block_rows > 0 && nn >= ap.block_min)
-        items_b += md.n_kv_heads * ((nn + ap.block_rows - 1) / ap.block_rows) * splits;
-      else
-        items += md.n_kv_heads * ((nn * G + 15) / 16) * splits;
-    }
-    outs += m.want_token[s] ? 1 : 0;
+    cnt.x += max(0, min(nn, m.n_rows));
+    if (ok) add_items(nn, ctx, cnt.y, cnt.z);
+    cnt.w += m.want_token[s] ? 1 : 0;
   }
-  int tot_rows, tot_items, tot_outs, tot_items_b;
-  int r = block_exclusive_scan(rows, buf, &tot_rows);
-  int it = block_exclusive_scan(items, buf, &tot_items);
-  int itb = block_exclusive_scan(items_b, buf, &tot_items_b);
-  int o = block_exclusive_scan(outs, buf, &tot_outs);
-  const bool counts_ok = tot_rows == m.n_rows && tot_outs == m.n_out;
+  int4 tot;
+  const int4 base = block_scan4(cnt, wave_tot, &tot);
+  const bool counts_ok = tot.x == m.n_rows && tot.w == m.n_out;
   if (t == 0 && !counts_ok) raise_status(status, ST_BAD_SHAPE);
 
+  int r = base.x, it = base.y, itb = base.z, o = base.w;
   for (int s = s0; s < s1; ++s) {
-    int nn = m.n_new[s], ctx = m.ctx_lens[s];
-    int nn_layout = max(0, min(nn, m.n_rows));
-    int slot = m.slots[s];
-    bool ok = counts_ok && nn >= 1 && ctx >= 0 && ctx + nn <= cap &&
-              ctx + nn <= ap.max_splits * ap.split_len && ctx + nn <= md.max_position &&
-              ctx + nn <= ap.max_ctx && slot >= 0 && slot < md.max_slots;
+    const int nn = m.n_new[s], ctx = m.ctx_lens[s];
+    const int nn_layout = max(0, min(nn, m.n_rows));
+    const bool ok = counts_ok && valid(s, nn, ctx);
     maps.item0[s] = it;
     maps.item0b[s] = itb;
     maps.seq_row0[s] = r;
-    for (int i = 0; i < nn_layout; ++i) {
-      if (r + i < m.n_rows) {
-        maps.row_seq[r + i] = ok ? s : -1;
-        maps.row_pos[r + i] = ctx + i;
-      }
-    }
-    if (ok) {
-      int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
-      if (ap.block_rows > 0 && nn >= ap.block_min)
-        itb += md.n_kv_heads * ((nn + ap.block_rows - 1) / ap.block_rows) * splits;
-      else
-        it += md.n_kv_heads * ((nn * G + 15) / 16) * splits;
-    }
-    for (int i = 0; i < nn_layout; ++i)
-      if (r + i < m.n_rows) maps.row_out[r + i] = -1;
+    int orow = -1;  // output index of the last row
     if (m.want_token[s]) {
       if (o < m.n_out) {
         maps.out_row[o] = ok ? r + nn_layout - 1 : -1;
         maps.out_seq[o] = s;
-        if (ok && r + nn_layout - 1 < m.n_rows) maps.row_out[r + nn_layout - 1] = o;
+        if (ok) orow = o;
       }
       ++o;
     }
+    if (counts_ok && nn_layout > 0) {  // with counts_ok every row lies below n_rows
+      int q = PREP_QUEUE;
+      if (nn_layout > PREP_SHORT) q = atomicAdd(&q_cnt, 1);
+      if (q < PREP_QUEUE) {
+        queue[q] = PrepQueued{s, r, nn_layout, ctx, ok ? s : -1, orow};
+      } else {
+        for (int i = 0; i < nn_layout; ++i)
+          prep_write_row(maps, r + i, ok ? s : -1, ctx + i, i == nn_layout - 1 ? orow : -1);
+      }
+    }
+    if (ok) add_items(nn, ctx, it, itb);
     r += nn_layout;
   }
   __syncthreads();
   if (t == 0) {
-    maps.item0[n] = counts_ok ? tot_items : 0;
-    maps.item0b[n] = counts_ok ? tot_items_b : 0;
+    maps.item0[n] = counts_ok ? tot.y : 0;
+    maps.item0b[n] = counts_ok ? tot.z : 0;
+  }
+  // The queued sequences' rows, one wave per sequence.
+  const int lane = t & 63, wave = t >> 6;
+  const int nq = min(q_cnt, PREP_QUEUE);
+  for (int e = wave; e < nq; e += PREP_WAVES) {
+    const PrepQueued qe = queue[e];
+    for (int i = lane; i < qe.n; i += 64)
+      prep_write_row(maps, qe.r + i, qe.seq, qe.ctx + i, i == qe.n - 1 ? qe.orow : -1);
   }
   if (!counts_ok) {  // the layout cannot be trusted: refuse every row
     for (int i = t; i < m.n_rows; i += PREP_THREADS) {
@@ -125,7 +179,7 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps 
     for (int i = t; i < m.n_out; i += PREP_THREADS) maps.out_row[i] = -1;
     for (int i = t; i < n; i += PREP_THREADS) maps.item0[i] = maps.item0b[i] = 0;
   } else {
-    for (int i = tot_rows + t; i < m.n_rows; i += PREP_THREADS) {
+    for (int i = tot.x + t; i < m.n_rows; i += PREP_THREADS) {
       maps.row_seq[i] = -1;
       maps.row_out[i] = -1;
     }
