@@ -14,10 +14,12 @@
 // consecutive k of row (l % 16) of each operand; the four lane groups
 // (l / 16) hold consecutive 8-k pieces. The weights are stored pre-packed in
 // exactly that operand order (16 x 32 tiles, lane-major), so every
-// wave-wide weight load is one contiguous 1 KB tile and a wave streams each
-// 16-row block front to back -- the DRAM sees long sequential runs instead
-// of 16 scattered 64-byte pieces per instruction. Two register stages of
-// loads are kept in flight while the previous stage feeds the MFMAs.
+// wave-wide weight load is one contiguous 1 KB tile. Tiles are grouped by
+// 16 column blocks (256 columns): a group stores the 16 blocks' tiles of
+// k-tile 0, then of k-tile 1, and so on, so that a workgroup that covers
+// 256 columns reads one contiguous 16 KB run per 32 k (the DRAM sees a few
+// long runs instead of 16 scattered ones; measured about 5-10% faster on the
+// LM head than blocks stored one after another).
 //
 // The activations are fp32 values carried as two bf16 planes (hi, lo), so
 // each weight fragment meets two B operands: acc += W.X_hi, acc += W.X_lo.
@@ -27,10 +29,10 @@
 // weight tile per 2 x 16 rows of MFMA work leaves the matrix cores idle
 // most of the time at these row counts).
 //
-// A wave owns NT column fragments x RT row fragments. KW waves of a workgroup
-// split K and reduce through LDS in fixed wave order; S workgroups along
-// grid.y split K further and leave fp32 partials that a second kernel sums in
-// fixed split order and passes through the epilogue. Epilogues: fp32 store,
+// Up to 64 rows run on the stream path below, more rows on the dense path.
+// S workgroups along K leave fp32 partials that a second kernel (or the
+// consumer of the result) sums in fixed split order and passes through the
+// epilogue. Epilogues: fp32 store,
 // fp32 residual add (x += acc), SwiGLU over a gate/up pair
 // (a = silu(g) * u, stored split), and fp32 logits with per-tile argmax
 // partials (lowest id on ties).
@@ -38,6 +40,13 @@
 #include "kernels.h"
 
 namespace cbd {
+
+// Element offset of k-tile kt of 16-column block nb in a packed matrix with
+// KT k-tiles, and the distance between consecutive k-tiles of one block.
+__device__ __forceinline__ size_t wtile(int nb, int kt, int KT) {
+  return (((size_t)(nb >> 4) * KT + kt) * 16 + (nb & 15)) * 512;
+}
+#define WT_NEXT (16 * 512)
 
 template <int EPI>
 struct EpiTraits {
@@ -142,169 +151,6 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a,
   }
 }
 
-template <int RT, int NT, int KW, int EPI>
-__global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a, int kc, int S) {
-  constexpr int NM = EpiTraits<EPI>::NM;
-  extern __shared__ float lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * (16 * NT);
-  const int ks = blockIdx.y;
-  const int r0 = blockIdx.z * (16 * RT);
-  const int K = a.K, N = a.N, R = a.R;
-
-  const int kw_len = kc / KW;  // a multiple of 64: waves start on tile boundaries
-  const int kbeg = ks * kc + wave * kw_len;
-  const int kend = min(K, kbeg + kw_len);
-
-  // Weight pointers into the packed layout, at this wave's first tile and
-  // this lane's 16 bytes: a wave-wide load reads one whole 1 KB tile. Row
-  // blocks past N read block 0 (valid memory; those outputs are never
-  // stored). Activation rows past R likewise read row 0.
-  const int KT = (K + 31) / 32;
-  const uint16_t* wp[NM][NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int nb = (n0 >> 4) + nt;
-    if (nb * 16 >= N) nb = 0;
-    const size_t off = ((size_t)nb * KT + kbeg / 32) * 512 + lane * 8;
-    wp[0][nt] = a.W + off;
-    if (NM == 2) wp[NM - 1][nt] = a.W2 + off;
-  }
-  const uint16_t* xp[RT][2];  // hi and lo planes
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = r0 + 16 * rt + lr;
-    const size_t off = (size_t)(r < R ? r : 0) * K + kbeg + 8 * lg;
-    xp[rt][0] = a.X + off;
-    xp[rt][1] = a.Xlo + off;
-  }
-
-  floatx4_t acc[NM][NT][RT];
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-  // One stage = ST super-steps of 64 k; two stages in registers, so the
-  // loads of stage i+1 are in flight while stage i feeds the MFMAs.
-  constexpr int ST = RT * NM <= 1 ? 2 : 1;
-  struct Stage {
-    uint4 w[ST][NM][NT][2];
-    uint4 x[ST][RT][2][2];  // [u][rt][32-k half][hi, lo]
-  };
-  auto load = [&](Stage& sg, int k) {
-#pragma unroll
-    for (int u = 0; u < ST; ++u)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int off = k + 64 * u + 32 * h;
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            sg.w[u][m][nt][h] = load_stream16(wp[m][nt] + (size_t)(off / 32) * 512);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int pl = 0; pl < 2; ++pl)
-            sg.x[u][rt][h][pl] = *reinterpret_cast<const uint4*>(xp[rt][pl] + off);
-      }
-  };
-  auto compute = [&](const Stage& sg) {
-#pragma unroll
-    for (int u = 0; u < ST; ++u)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-          for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-              for (int rt = 0; rt < RT; ++rt)
-                acc[m][nt][rt] = mfma16x16x32(as_bf16x8(sg.w[u][m][nt][h]),
-                                              as_bf16x8(sg.x[u][rt][h][pl]), acc[m][nt][rt]);
-  };
-
-  const int span = kend - kbeg;  // this wave's k count (a multiple of 8, or <= 0)
-  const int stride = 64 * ST;
-  const int nfull = span > 0 ? span / stride : 0;
-  {
-    Stage A, B;
-    int it = 0;
-    if (nfull > 0) load(A, 0);
-    for (; it + 2 <= nfull; it += 2) {
-      load(B, (it + 1) * stride);
-      compute(A);
-      if (it + 2 < nfull) load(A, (it + 2) * stride);
-      compute(B);
-    }
-    if (it < nfull) compute(A);
-  }
-  // Tail: the last < 64*ST k, in 32-k halves predicated per lane group.
-  for (int k = nfull * stride; k < span; k += 32) {
-    const bool kin = k + 8 * lg < span;
-    uint4 w[NM][NT], x[RT][2];
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        w[m][nt] = kin ? load_stream16(wp[m][nt] + (size_t)(k / 32) * 512) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int pl = 0; pl < 2; ++pl)
-        x[rt][pl] = kin ? *reinterpret_cast<const uint4*>(xp[rt][pl] + k) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-            acc[m][nt][rt] = mfma16x16x32(as_bf16x8(w[m][nt]), as_bf16x8(x[rt][pl]), acc[m][nt][rt]);
-  }
-
-  // Reduce the KW waves' partial sums through LDS, in wave order.
-  if (KW > 1) {
-    constexpr int TILE = NM * NT * RT * 4;  // floats per lane
-    if (wave > 0) {
-      float* dst = lds + ((size_t)(wave - 1) * 64 + lane) * TILE;
-      int q = 0;
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[q++] = acc[m][nt][rt][i];
-    }
-    __syncthreads();
-    if (wave > 0) return;
-#pragma unroll
-    for (int w = 1; w < KW; ++w) {
-      const float* src = lds + ((size_t)(w - 1) * 64 + lane) * TILE;
-      int q = 0;
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][nt][rt][i] += src[q++];
-    }
-  }
-
-  store_tile<RT, NT, EPI>(a, acc, r0, n0, ks, S, blockIdx.x);
-}
-
 // ------------------------------------------------------- the stream path
 //
 // One kernel for any row count. A workgroup is 4 waves side by side along N
@@ -352,7 +198,7 @@ __global__ __launch_bounds__(64 * STREAM_NW) __attribute__((amdgpu_waves_per_eu(
   for (int nt = 0; nt < NT; ++nt) {
     int nb = (n0 >> 4) + nt;
     if (nb * 16 >= N) nb = 0;  // past N: read block 0, never stored
-    const size_t off = ((size_t)nb * KT + kbeg / 32) * 512 + lane * 8;
+    const size_t off = wtile(nb, kbeg / 32, KT) + lane * 8;
     wp[0][nt] = a.W + off;
     if (NM == 2) wp[NM - 1][nt] = a.W2 + off;
   }
@@ -386,7 +232,7 @@ __global__ __launch_bounds__(64 * STREAM_NW) __attribute__((amdgpu_waves_per_eu(
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          w[j][m][nt][h] = load_stream16(wp[m][nt] + (size_t)t * 512);
+          w[j][m][nt][h] = load_stream16(wp[m][nt] + (size_t)t * WT_NEXT);
     }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
@@ -511,7 +357,7 @@ __global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a
       const int m = t / CB;
       int nb = n_tile * CB + t % CB;
       if (nb * 16 >= N) nb = 0;  // past N: read block 0, never stored
-      src[i] = (m ? a.W2 : a.W) + ((size_t)nb * KT + kbeg / 32) * 512 + lane * 8;
+      src[i] = (m ? a.W2 : a.W) + wtile(nb, kbeg / 32, KT) + lane * 8;
     } else {
       const int u = t - TW;
       const int r = min(r_base + 16 * (u >> 1) + lr, R - 1);
@@ -523,7 +369,7 @@ __global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a
     for (int i = 0; i < LPS; ++i) {
       const int t = wave + DENSE_WAVES * i;
       if (i < TW / DENSE_WAVES)  // weights: streamed once, kept out of L2's way
-        copy16_to_lds_nt(src[i] + (size_t)c * 512, ring + ((size_t)slot * TS + t) * 64);
+        copy16_to_lds_nt(src[i] + (size_t)c * WT_NEXT, ring + ((size_t)slot * TS + t) * 64);
       else  // activations: re-read by every column tile, kept in L2
         copy16_to_lds(src[i] + min(kbeg + 32 * c + 8 * lg, K - 8),
                       ring + ((size_t)slot * TS + t) * 64);
@@ -607,7 +453,7 @@ __global__ void gemm_reduce_kernel(GemmArgs a, int S) {
 // ------------------------------------------------------------- host side
 
 size_t packed_elems(int32_t N, int32_t K) {
-  return (size_t)((N + 15) / 16) * (size_t)((K + 31) / 32) * 512;
+  return (size_t)((N + 255) / 256) * 16 * (size_t)((K + 31) / 32) * 512;
 }
 
 __global__ void pack_kernel(const uint16_t* __restrict__ W, int N, int K,
@@ -623,7 +469,7 @@ __global__ void pack_kernel(const uint16_t* __restrict__ W, int N, int K,
   const int k = kb * 32 + 8 * (lane >> 4);
   uint4 v = make_uint4(0, 0, 0, 0);
   if (n < N && k < K) v = *reinterpret_cast<const uint4*>(W + (size_t)n * K + k);
-  reinterpret_cast<uint4*>(out)[i] = v;
+  reinterpret_cast<uint4*>(out)[(wtile(nb, kb, KT) >> 3) + lane] = v;
 }
 
 hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, hipStream_t st) {
@@ -632,18 +478,17 @@ hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, h
   return hipGetLastError();
 }
 
-// How one projection runs: the per-wave kernel (RT = 1: up to 16 rows; KW
-// waves of a workgroup split K and reduce through LDS) or the stream kernel
-// (RT = 2 or 4 row fragments; 4 column-split waves share the activation
-// tile), with S workgroups splitting K further (partials summed by a second
-// kernel in split order). Chosen from the row count and the matrix shape
-// after measuring the step's matrices on MI355X: small weight reads are
-// dominated by the first loads' latency and the launch, so they want many
-// waves each reading a few tens of KB, in a single launch where possible.
+// How one projection runs. Up to 64 rows: the stream kernel with RT row
+// fragments (16, 32 or 64 rows), 4 waves of NT column fragments sharing the
+// activation tile, S workgroups splitting K. Measured on the 8B shapes at
+// 1-64 rows on MI355X: the LM head wants 64-column waves (its 256-column
+// workgroups read one contiguous run per stage); the gate/up pair 16-column
+// waves over the whole K (no partials, no separate SwiGLU pass); the single
+// matrices 32-column waves with K split until the grid would pass one
+// workgroup per CU. More rows: the dense kernel (see above).
 struct GemmPlan {
-  bool stream;
   bool dense;
-  int RT, NT, KW, D, S;
+  int RT, NT, D, S;
 };
 
 // Rows at or above which the dense path runs: past one stream row group
@@ -652,7 +497,6 @@ struct GemmPlan {
 
 static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
   GemmPlan p{};
-  const bool vocab = logits && N >= 32768;  // the LM head: wide, argmax fused
   // Row fragments per dense workgroup: the fewest padded rows, then the
   // larger tile (fewer weight re-reads).
   int best = 0, waste = 1 << 30;
@@ -678,37 +522,14 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
       while (dense_tiles * p.S < 256 && K / (p.S * 2) >= 256) p.S *= 2;
     return p;
   }
-  if (R <= 16) {
-    p.stream = false;
-    p.RT = 1;
-    p.D = 0;
-    if (vocab) {
-      p.NT = R <= 8 ? 1 : 4;
-      p.KW = R <= 8 ? 4 : 1;
-      p.S = 1;
-    } else {
-      const bool long_k = K >= 8192;
-      p.NT = R <= 8 ? 1 : 2;
-      p.KW = long_k ? (R <= 8 ? 4 : 8) : (NM == 2 && R <= 8 ? 8 : 4);
-      p.S = long_k && R > 8 ? 2 : 1;
-    }
-  } else {
-    // Measured at 32 and 64 rows on the 8B shapes: the gate/up pair runs
-    // best as 16-column waves over the whole K (224 workgroups, no partials
-    // and no separate SwiGLU pass); single matrices as 32-column waves with
-    // K split until the grid would pass one workgroup per CU.
-    p.stream = true;
-    p.KW = 1;
-    p.RT = R <= 32 ? 2 : 4;
-    p.NT = (vocab || logits) ? 4 : (NM == 2 ? 1 : 2);
-    p.D = 4;
-    p.S = 1;
-    if (!logits) {
-      const int groups = (N + 64 * p.NT - 1) / (64 * p.NT) * ((R + 16 * p.RT - 1) / (16 * p.RT));
-      while (groups * p.S * 2 <= 256 && K / (p.S * 2) >= 512) p.S *= 2;
-    }
+  p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
+  p.NT = logits ? 4 : (NM == 2 ? 1 : 2);
+  p.D = 4;
+  p.S = 1;
+  if (!logits) {
+    const int groups = (N + 64 * p.NT - 1) / (64 * p.NT) * ((R + 16 * p.RT - 1) / (16 * p.RT));
+    while (groups * p.S * 2 <= 256 && K / (p.S * 2) >= 512) p.S *= 2;
   }
-  if (logits) p.S = 1;
   return p;
 }
 
@@ -716,8 +537,7 @@ int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K) {
   const GemmPlan p = plan_gemm(R, N, K, 1, true);
   if (p.dense) return (N + DENSE_TN - 1) / DENSE_TN * 2;
   const int cols = 16 * p.NT;
-  if (p.stream) return (N + cols * STREAM_NW - 1) / (cols * STREAM_NW) * STREAM_NW;
-  return (N + cols - 1) / cols;
+  return (N + cols * STREAM_NW - 1) / (cols * STREAM_NW) * STREAM_NW;
 }
 
 template <int EPI>
@@ -746,19 +566,6 @@ static int split_k(int K, int S, int align, int* kc) {
   c = (c + align - 1) / align * align;
   *kc = c;
   return (K + c - 1) / c;
-}
-
-template <int NT, int KW, int EPI>
-static hipError_t launch_per_wave(const GemmArgs& a, int S, hipStream_t st) {
-  constexpr int NM = EpiTraits<EPI>::NM;
-  const int n_tiles = (a.N + 16 * NT - 1) / (16 * NT);
-  const int r_groups = (a.R + 15) / 16;
-  int kc;
-  S = split_k(a.K, S, 64 * KW, &kc);
-  if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 64 * KW, &kc);
-  const size_t lds = KW > 1 ? (size_t)(KW - 1) * 64 * NM * NT * 4 * sizeof(float) : 0;
-  gemm_kernel<1, NT, KW, EPI><<<dim3(n_tiles, S, r_groups), 64 * KW, lds, st>>>(a, kc, S);
-  return finish_splits<EPI>(a, S, st);
 }
 
 template <int RT, int NT, int D, int EPI>
@@ -806,21 +613,14 @@ static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
     if (p.RT == 12) return launch_dense<12, 3, EPI>(a, p.S, st);
     return launch_dense<8, 4, EPI>(a, p.S, st);
   }
-  if (!p.stream) {
-#define PW(NT_, KW_) \
-  if (p.NT == NT_ && p.KW == KW_) return launch_per_wave<NT_, KW_, EPI>(a, p.S, st);
-    PW(1, 4) PW(1, 8) PW(2, 4) PW(2, 8) PW(4, 1)
-#undef PW
-    return launch_per_wave<2, 4, EPI>(a, p.S, st);
-  }
 #define ST(RT_, NT_, D_) \
   if (p.RT == RT_ && p.NT == NT_ && p.D == D_) return launch_stream<RT_, NT_, D_, EPI>(a, p.S, st);
   if constexpr (NM == 2) {
-    ST(2, 1, 4) ST(4, 1, 4)
+    ST(1, 1, 4) ST(2, 1, 4)
     return launch_stream<4, 1, 4, EPI>(a, p.S, st);
   } else {
-    ST(2, 2, 4) ST(2, 4, 4) ST(4, 2, 4) ST(4, 4, 4)
-    return launch_stream<4, 2, 4, EPI>(a, p.S, st);
+    ST(1, 2, 4) ST(1, 4, 4) ST(2, 2, 4) ST(2, 4, 4) ST(4, 2, 4)
+    return launch_stream<4, 4, 4, EPI>(a, p.S, st);
   }
 #undef ST
 }
