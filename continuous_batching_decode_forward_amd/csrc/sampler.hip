@@ -69,7 +69,10 @@ struct SmpShared {
   double wave_d[SMP_WAVES];
   float red_f[SMP_WAVES];
   int red_i[SMP_WAVES];
+  int red_i2[SMP_WAVES];
   int wave_i[SMP_WAVES];
+  int n_cand;
+  float cand[SMP_THREADS];  // threshold candidates, one per thread
 };
 
 // An fp32 product rounded on its own: the empty asm hides it from
@@ -188,24 +191,56 @@ struct RowVals {
   }
 };
 
+// Block sums of one double and one int, sharing the barriers.
+__device__ void smp_block_sum2(double& f, int& a, SmpShared& sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    f += __shfl_xor(f, o, 64);
+    a += __shfl_xor(a, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sh.red_d[threadIdx.x >> 6] = f;
+    sh.red_i[threadIdx.x >> 6] = a;
+  }
+  __syncthreads();
+  f = 0.0;
+  a = 0;
+#pragma unroll
+  for (int w = 0; w < SMP_WAVES; ++w) {
+    f += sh.red_d[w];
+    a += sh.red_i[w];
+  }
+  __syncthreads();
+}
+
 // Largest bit pattern tau (non-negative floats) with F(tau) >= need, where
 // F(tau) = count (BY_MASS false) or mass (true) of the kept values >= tau.
-// Bisection between the smallest and largest kept pattern; each step is one
-// reduction over the row.
+// Bisection between the smallest and largest kept pattern. Each step over
+// the row is one pass and one reduction of F(mid) and C(mid), the number of
+// kept values >= mid; C at both ends of the range gives the number of
+// values left inside it. Once that is at most one per thread, those values
+// are gathered into LDS and the bisection finishes on them alone: F(mid) =
+// F(hi) + the candidates in [mid, hi) (those at or above a lowered hi are in
+// F(hi) already), where F(hi) was computed when hi was last lowered (0 for
+// the initial hi above every value).
 template <bool BY_MASS, bool REGS>
 __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K, int base, double need,
                                   SmpShared& sh) {
   uint32_t lo = 0x7f800000u, hi = 0u;
+  int kept = 0;
   SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
     const float v = e.get(k, base + 64 * k);
     if (v >= 0.f) {
       lo = min(lo, __float_as_uint(v));
       hi = max(hi, __float_as_uint(v));
+      ++kept;
     }
   }
   lo = (uint32_t)-smp_block_max_i(-(int)lo, sh);  // block min (patterns < 2^31)
   hi = (uint32_t)smp_block_max_i((int)hi, sh) + 1u;  // F(hi) = 0 < need
-  while (hi - lo > 1u) {
+  int c_lo = smp_block_sum_i(kept, sh), c_hi = 0;
+  double f_hi = 0.0;
+  while (hi - lo > 1u && c_lo - c_hi > SMP_THREADS) {
     const uint32_t mid = lo + (hi - lo) / 2u;
     double f = 0.0;
     int c = 0;
@@ -213,14 +248,44 @@ __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K,
       const float v = e.get(k, base + 64 * k);
       if (v >= 0.f && __float_as_uint(v) >= mid) {
         if (BY_MASS) f += v;
-        else ++c;
+        ++c;
       }
     }
-    const bool ok = BY_MASS ? (smp_block_sum_d(f, sh) >= need) : (smp_block_sum_i(c, sh) >= (int)need);
-    if (ok)
+    smp_block_sum2(f, c, sh);
+    if (!BY_MASS) f = (double)c;
+    if (f >= need) {
       lo = mid;
-    else
+      c_lo = c;
+    } else {
       hi = mid;
+      f_hi = f;
+      c_hi = c;
+    }
+  }
+  if (hi - lo <= 1u) return lo;
+  // Gather the values in [lo, hi) (their order does not matter: only sums
+  // over them are taken); slots come from an LDS counter.
+  if (threadIdx.x == 0) sh.n_cand = 0;
+  __syncthreads();
+  SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
+    const float v = e.get(k, base + 64 * k);
+    const uint32_t u = __float_as_uint(v);
+    if (v >= 0.f && u >= lo && u < hi) sh.cand[atomicAdd(&sh.n_cand, 1)] = v;
+  }
+  __syncthreads();
+  const float cv = (int)threadIdx.x < sh.n_cand ? sh.cand[threadIdx.x] : -1.f;
+  __syncthreads();
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + (hi - lo) / 2u;
+    const uint32_t u = __float_as_uint(cv);
+    const double c = (cv >= 0.f && u >= mid && u < hi) ? (BY_MASS ? (double)cv : 1.0) : 0.0;
+    const double f = f_hi + smp_block_sum_d(c, sh);
+    if (f >= need) {
+      lo = mid;
+    } else {
+      hi = mid;
+      f_hi = f;
+    }
   }
   return lo;
 }
