@@ -167,22 +167,23 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a,
 // barrier orders the stages. Stages are padded to a multiple of D; the
 // activation pieces at or beyond kend (padding, a K tail) are zeroed in LDS
 // after their copy lands, so the weights read there meet zeros.
-// Two waves per SIMD (256 registers, accumulators included): with the 64 KB
-// LDS ring of 64-row workgroups that is two workgroups per CU, so a grid of
-// up to 512 workgroups (the LM head's) runs in one round.
-#define STREAM_NW 4
-
-template <int RT, int NT, int D, int EPI>
-__global__ __launch_bounds__(64 * STREAM_NW) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_kernel(GemmArgs a, int kc, int S) {
+// Two waves per SIMD (256 registers, accumulators included). A workgroup
+// has NW = 4 or 8 waves: 8 halve the activation copies per weight byte, which
+// pays on the LM head at 64 rows (173 -> 163 us) but not on the narrower
+// layer matrices, whose grids then leave CUs idle.
+template <int RT, int NT, int D, int NW, int EPI>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_kernel(GemmArgs a, int kc, int S) {
   constexpr int NM = EpiTraits<EPI>::NM;
   constexpr int BLK = RT * 4;                 // 1 KB LDS blocks per stage
-  constexpr int LPS = NM * NT * 2 + RT;       // loads per stage per wave
+  constexpr int CPW = BLK / NW;               // activation copies per wave per stage
+  static_assert(BLK % NW == 0, "activation blocks per wave");
+  constexpr int LPS = NM * NT * 2 + CPW;      // loads per stage per wave
   static_assert(D >= 3, "ring depth");
   extern __shared__ uint4 xs[];               // [D][BLK][64]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int tile = blockIdx.x * STREAM_NW + wave;
+  const int tile = blockIdx.x * NW + wave;
   const int n0 = tile * (16 * NT);
   const int ks = blockIdx.y;
   const int r0 = blockIdx.z * (16 * RT);
@@ -202,13 +203,13 @@ __global__ __launch_bounds__(64 * STREAM_NW) __attribute__((amdgpu_waves_per_eu(
     wp[0][nt] = a.W + off;
     if (NM == 2) wp[NM - 1][nt] = a.W2 + off;
   }
-  // This wave copies blocks b = wave + 4 i of every stage; lane `lane` of
+  // This wave copies blocks b = wave + NW i of every stage; lane `lane` of
   // block (rt, pl, h) is row r0 + 16 rt + lr, k + 32 h + 8 lg. Rows past R
   // read row R - 1 (their outputs are never stored).
-  const uint16_t* xsrc[RT];
+  const uint16_t* xsrc[CPW];
 #pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    const int b = wave + STREAM_NW * i;
+  for (int i = 0; i < CPW; ++i) {
+    const int b = wave + NW * i;
     const int rt = b >> 2, pl = (b >> 1) & 1;
     const int r = min(r0 + 16 * rt + lr, R - 1);
     xsrc[i] = (pl ? a.Xlo : a.X) + (size_t)r * K;
@@ -235,8 +236,8 @@ __global__ __launch_bounds__(64 * STREAM_NW) __attribute__((amdgpu_waves_per_eu(
           w[j][m][nt][h] = load_stream16(wp[m][nt] + (size_t)t * WT_NEXT);
     }
 #pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const int b = wave + STREAM_NW * i;
+    for (int i = 0; i < CPW; ++i) {
+      const int b = wave + NW * i;
       const int k = min(kbeg + 64 * c + 32 * (b & 1) + 8 * lg, K - 8);
       copy16_to_lds(xsrc[i] + k, xs + ((size_t)j * BLK + b) * 64);
     }
@@ -274,8 +275,8 @@ __global__ __launch_bounds__(64 * STREAM_NW) __attribute__((amdgpu_waves_per_eu(
         wait_vmem<(D - 2) * LPS>();
         if (kbeg + 64 * c + 64 > kend) {  // K tail or padding: zero what lies past kend
 #pragma unroll
-          for (int i = 0; i < RT; ++i) {
-            const int b = wave + STREAM_NW * i;
+          for (int i = 0; i < CPW; ++i) {
+            const int b = wave + NW * i;
             if (kbeg + 64 * c + 32 * (b & 1) + 8 * lg >= kend)
               xs[((size_t)j * BLK + b) * 64 + lane] = make_uint4(0, 0, 0, 0);
           }
@@ -488,7 +489,7 @@ hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, h
 // workgroup per CU. More rows: the dense kernel (see above).
 struct GemmPlan {
   bool dense;
-  int RT, NT, D, S;
+  int RT, NT, D, NW, S;
 };
 
 // Rows at or above which the dense path runs: past one stream row group
@@ -525,9 +526,11 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
   p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
   p.NT = logits ? 4 : (NM == 2 ? 1 : 2);
   p.D = 4;
+  p.NW = logits && p.RT == 4 ? 8 : 4;
   p.S = 1;
   if (!logits) {
-    const int groups = (N + 64 * p.NT - 1) / (64 * p.NT) * ((R + 16 * p.RT - 1) / (16 * p.RT));
+    const int cols = 16 * p.NW * p.NT;
+    const int groups = (N + cols - 1) / cols * ((R + 16 * p.RT - 1) / (16 * p.RT));
     while (groups * p.S * 2 <= 256 && K / (p.S * 2) >= 512) p.S *= 2;
   }
   return p;
@@ -537,7 +540,7 @@ int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K) {
   const GemmPlan p = plan_gemm(R, N, K, 1, true);
   if (p.dense) return (N + DENSE_TN - 1) / DENSE_TN * 2;
   const int cols = 16 * p.NT;
-  return (N + cols * STREAM_NW - 1) / (cols * STREAM_NW) * STREAM_NW;
+  return (N + cols * p.NW - 1) / (cols * p.NW) * p.NW;
 }
 
 template <int EPI>
@@ -568,17 +571,17 @@ static int split_k(int K, int S, int align, int* kc) {
   return (K + c - 1) / c;
 }
 
-template <int RT, int NT, int D, int EPI>
+template <int RT, int NT, int D, int NW, int EPI>
 static hipError_t launch_stream(const GemmArgs& a, int S, hipStream_t st) {
   constexpr int NM = EpiTraits<EPI>::NM;
-  const int cols = 16 * NT * STREAM_NW;
+  const int cols = 16 * NT * NW;
   const int n_groups = (a.N + cols - 1) / cols;
   const int r_groups = (a.R + 16 * RT - 1) / (16 * RT);
   int kc;
   S = split_k(a.K, S, 64, &kc);
   if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 64, &kc);
   const size_t lds = (size_t)D * RT * 4 * 1024;  // <= 64 KB for the shapes instantiated
-  gemm_stream_kernel<RT, NT, D, EPI><<<dim3(n_groups, S, r_groups), 64 * STREAM_NW, lds, st>>>(
+  gemm_stream_kernel<RT, NT, D, NW, EPI><<<dim3(n_groups, S, r_groups), 64 * NW, lds, st>>>(
       a, kc, S);
   return finish_splits<EPI>(a, S, st);
 }
@@ -613,14 +616,18 @@ static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
     if (p.RT == 12) return launch_dense<12, 3, EPI>(a, p.S, st);
     return launch_dense<8, 4, EPI>(a, p.S, st);
   }
-#define ST(RT_, NT_, D_) \
-  if (p.RT == RT_ && p.NT == NT_ && p.D == D_) return launch_stream<RT_, NT_, D_, EPI>(a, p.S, st);
+#define ST(RT_, NT_, NW_)                                \
+  if (p.RT == RT_ && p.NT == NT_ && p.NW == NW_) \
+    return launch_stream<RT_, NT_, 4, NW_, EPI>(a, p.S, st);
   if constexpr (NM == 2) {
     ST(1, 1, 4) ST(2, 1, 4)
-    return launch_stream<4, 1, 4, EPI>(a, p.S, st);
+    return launch_stream<4, 1, 4, 4, EPI>(a, p.S, st);
+  } else if constexpr (EPI == EPI_LOGITS) {
+    ST(1, 4, 4) ST(2, 4, 4)
+    return launch_stream<4, 4, 4, 8, EPI>(a, p.S, st);
   } else {
-    ST(1, 2, 4) ST(1, 4, 4) ST(2, 2, 4) ST(2, 4, 4) ST(4, 2, 4)
-    return launch_stream<4, 4, 4, EPI>(a, p.S, st);
+    ST(1, 2, 4) ST(2, 2, 4)
+    return launch_stream<4, 2, 4, 4, EPI>(a, p.S, st);
   }
 #undef ST
 }
