@@ -462,10 +462,8 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
   uint16_t* ffn_lo = ffn + MR * c.ffn_dim;
   float* gpart = e->wsp<float>(e->ws.gemm_part);
 
-  HIP_TRY(launch_prep(m, maps, e->md, ap, status, st));
   HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
-  HIP_TRY(launch_embed_norm(s->tokens, maps.row_seq, R, e->embed, e->attn_norm[0], e->md, x, h,
-                            h_lo, status, st));
+  HIP_TRY(launch_prep_embed(m, maps, e->md, ap, e->embed, e->attn_norm[0], x, h, h_lo, status, st));
   HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
   // The norm in front of each projection is fused into the kernel that
   // finishes the previous residual projection (or the embedding gather):

@@ -66,8 +66,12 @@ struct AttnPlan {
   int32_t block_min, block_rows, grid_items_b;
 };
 
-hipError_t launch_prep(const StepMeta& m, const RowMaps& maps, const ModelDims& md,
-                       const AttnPlan& ap, uint32_t* status, hipStream_t st);
+// Row maps and attention schedule (one workgroup) together with the
+// embedding gather + first RMSNorm of every row (x, and h as hi/lo planes).
+hipError_t launch_prep_embed(const StepMeta& m, const RowMaps& maps, const ModelDims& md,
+                             const AttnPlan& ap, const uint16_t* embed, const uint16_t* gain,
+                             float* x, uint16_t* h_hi, uint16_t* h_lo, uint32_t* status,
+                             hipStream_t st);
 
 // Activation storage. The residual stream x and the QKV projection are fp32
 // [rows][width]. Activations that feed an MFMA contraction (norm outputs,
@@ -76,10 +80,6 @@ hipError_t launch_prep(const StepMeta& m, const RowMaps& maps, const ModelDims& 
 // (split_bf in common.h).
 
 // x[r] = embed[tokens[r]] (fp32), h[r] = rmsnorm(x[r]) * gain (split).
-hipError_t launch_embed_norm(const int32_t* tokens, const int32_t* row_seq, int32_t R,
-                             const uint16_t* embed, const uint16_t* gain, const ModelDims& md,
-                             float* x, uint16_t* h_hi, uint16_t* h_lo, uint32_t* status,
-                             hipStream_t st);
 
 // h[j] = rmsnorm(x[rows ? rows[j] : j]) * gain for j < R (rows[j] < 0: zeros).
 hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int32_t R, const uint16_t* gain,

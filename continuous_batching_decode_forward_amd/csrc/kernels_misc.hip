@@ -74,9 +74,8 @@ __device__ __forceinline__ void prep_write_row(const RowMaps& maps, int row, int
   maps.row_out[row] = out;
 }
 
-__global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps maps,
-                                                            ModelDims md, AttnPlan ap,
-                                                            uint32_t* status) {
+__device__ void prep_body(const StepMeta& m, const RowMaps& maps, const ModelDims& md,
+                          const AttnPlan& ap, uint32_t* status) {
   __shared__ int4 wave_tot[PREP_WAVES];
   __shared__ PrepQueued queue[PREP_QUEUE];
   __shared__ int q_cnt;
@@ -186,9 +185,81 @@ __global__ __launch_bounds__(PREP_THREADS) void prep_kernel(StepMeta m, RowMaps 
   }
 }
 
-hipError_t launch_prep(const StepMeta& m, const RowMaps& maps, const ModelDims& md,
-                       const AttnPlan& ap, uint32_t* status, hipStream_t st) {
-  prep_kernel<<<1, PREP_THREADS, 0, st>>>(m, maps, md, ap, status);
+// The embedding rows of the step, gathered by the other workgroups of the
+// prep launch: row r = blockIdx.x - 1 becomes x[r] = E[tokens[r]] (fp32) and
+// its RMSNorm, split into hi and lo planes (a token outside the vocabulary
+// gives a zero row and ST_BAD_TOKEN). Rows of refused sequences are gathered
+// too: prep runs beside this, and nothing downstream reads them.
+#define EN_MAX_CHUNKS 4  // d_model <= 4 * 4 * PREP_THREADS
+
+__device__ void embed_row(int r, const int32_t* __restrict__ tokens,
+                          const uint16_t* __restrict__ embed, const uint16_t* __restrict__ gain,
+                          int d, int vocab, float eps, float* __restrict__ x,
+                          uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
+                          uint32_t* status) {
+  __shared__ float red[PREP_WAVES];
+  const int t = threadIdx.x;
+  const int nch = d >> 2;
+  const int tok = tokens[r];
+  const bool ok = tok >= 0 && tok < vocab;
+  if (!ok && t == 0) raise_status(status, ST_BAD_TOKEN);
+  float* xr = x + (size_t)r * d;
+  float4 xv[EN_MAX_CHUNKS];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < EN_MAX_CHUNKS; ++c) {
+    const int ch = t + c * PREP_THREADS;
+    xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ch < nch) {
+      if (ok) {
+        const uint2 e = reinterpret_cast<const uint2*>(embed + (size_t)tok * d)[ch];
+        xv[c] = make_float4(lo_bf(e.x), hi_bf(e.x), lo_bf(e.y), hi_bf(e.y));
+      }
+      reinterpret_cast<float4*>(xr)[ch] = xv[c];
+      ss += xv[c].x * xv[c].x + xv[c].y * xv[c].y + xv[c].z * xv[c].z + xv[c].w * xv[c].w;
+    }
+  }
+  ss = wave_sum(ss);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < PREP_WAVES; ++w) tot += red[w];
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  uint16_t* hh = h_hi + (size_t)r * d;
+  uint16_t* hl = h_lo + (size_t)r * d;
+#pragma unroll
+  for (int c = 0; c < EN_MAX_CHUNKS; ++c) {
+    const int ch = t + c * PREP_THREADS;
+    if (ch < nch) {
+      const uint2 gv = reinterpret_cast<const uint2*>(gain)[ch];
+      store_split4(hh, hl, (size_t)ch * 4, xv[c].x * inv * lo_bf(gv.x), xv[c].y * inv * hi_bf(gv.x),
+                   xv[c].z * inv * lo_bf(gv.y), xv[c].w * inv * hi_bf(gv.y));
+    }
+  }
+}
+
+// One launch for the step's start: workgroup 0 builds the row maps and the
+// attention schedule, workgroups 1 .. n_rows gather and normalise the
+// embedding rows (the two depend on nothing of each other).
+__global__ __launch_bounds__(PREP_THREADS) void prep_embed_kernel(
+    StepMeta m, RowMaps maps, ModelDims md, AttnPlan ap, const uint16_t* __restrict__ embed,
+    const uint16_t* __restrict__ gain, float* __restrict__ x, uint16_t* __restrict__ h_hi,
+    uint16_t* __restrict__ h_lo, uint32_t* status) {
+  if (blockIdx.x == 0)
+    prep_body(m, maps, md, ap, status);
+  else
+    embed_row(blockIdx.x - 1, m.tokens, embed, gain, md.d_model, md.vocab, md.rms_eps, x, h_hi,
+              h_lo, status);
+}
+
+hipError_t launch_prep_embed(const StepMeta& m, const RowMaps& maps, const ModelDims& md,
+                             const AttnPlan& ap, const uint16_t* embed, const uint16_t* gain,
+                             float* x, uint16_t* h_hi, uint16_t* h_lo, uint32_t* status,
+                             hipStream_t st) {
+  if ((md.d_model >> 2) > EN_MAX_CHUNKS * PREP_THREADS) return hipErrorInvalidValue;
+  prep_embed_kernel<<<1 + m.n_rows, PREP_THREADS, 0, st>>>(m, maps, md, ap, embed, gain, x, h_hi,
+                                                            h_lo, status);
   return hipGetLastError();
 }
 
@@ -239,43 +310,6 @@ __device__ void norm_row(const float* __restrict__ x, const uint16_t* __restrict
                    xv[c].w * inv * hi_bf(gv.y));
     }
   }
-}
-
-__global__ __launch_bounds__(NORM_THREADS) void embed_norm_kernel(
-    const int32_t* __restrict__ tokens, const int32_t* __restrict__ row_seq,
-    const uint16_t* __restrict__ embed, const uint16_t* __restrict__ gain, int d, int vocab,
-    float eps, float* __restrict__ x, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
-    uint32_t* status) {
-  __shared__ float red[4];
-  const int r = blockIdx.x;
-  float* xr = x + (size_t)r * d;
-  int tok = tokens[r];
-  bool ok = row_seq[r] >= 0;
-  if (ok && (tok < 0 || tok >= vocab)) {
-    if (threadIdx.x == 0) raise_status(status, ST_BAD_TOKEN);
-    ok = false;
-  }
-  // Each thread writes exactly the chunks norm_row reads back in this thread.
-  const int nch = d >> 2;
-  for (int ch = threadIdx.x; ch < nch; ch += NORM_THREADS) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ok) {
-      uint2 e = reinterpret_cast<const uint2*>(embed + (size_t)tok * d)[ch];
-      v = make_float4(lo_bf(e.x), hi_bf(e.x), lo_bf(e.y), hi_bf(e.y));
-    }
-    reinterpret_cast<float4*>(xr)[ch] = v;
-  }
-  norm_row(xr, gain, d, eps, h_hi + (size_t)r * d, h_lo + (size_t)r * d, red);
-}
-
-hipError_t launch_embed_norm(const int32_t* tokens, const int32_t* row_seq, int32_t R,
-                             const uint16_t* embed, const uint16_t* gain, const ModelDims& md,
-                             float* x, uint16_t* h_hi, uint16_t* h_lo, uint32_t* status,
-                             hipStream_t st) {
-  if (R <= 0) return hipSuccess;
-  embed_norm_kernel<<<R, NORM_THREADS, 0, st>>>(tokens, row_seq, embed, gain, md.d_model,
-                                                 md.vocab, md.rms_eps, x, h_hi, h_lo, status);
-  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(NORM_THREADS) void rmsnorm_kernel(
