@@ -496,7 +496,23 @@ struct GemmPlan {
 // (64 rows) the stream path would fetch every weight once per group.
 #define DENSE_MIN_ROWS 65
 
-static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
+// Estimated time (us) of a dense launch: rounds of one workgroup per CU
+// (every dense ring needs 96-144 KB of LDS) times the 32-k stages of a
+// workgroup times the stage time, which grows with the tile height (fitted
+// on the 8B matrices at 128-560 rows: 0.87, 1.19 and 1.5 us at RF = 8, 12,
+// 16), plus the split partials written and read back at about 6 TB/s, plus
+// the reduce launch a split SwiGLU needs.
+static double dense_cost(int R, int N, int K, int NM, int rf, int S) {
+  const long long tiles = (long long)((N + DENSE_TN / NM - 1) / (DENSE_TN / NM)) *
+                          ((R + 16 * rf - 1) / (16 * rf));
+  const long long rounds = (tiles * S + 255) / 256;
+  const int stages = ((K + S - 1) / S + 31) / 32;
+  double t = (double)rounds * stages * (0.25 + 0.078 * rf);
+  if (S > 1) t += (double)S * R * N * NM * 8.0 / 6e6 + (NM == 2 ? 5.0 : 0.0);
+  return t;
+}
+
+static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits, size_t partials_cap) {
   GemmPlan p{};
   // Row fragments per dense workgroup: the fewest padded rows, then the
   // larger tile (fewer weight re-reads).
@@ -514,13 +530,24 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
   // long K, where splitting is cheap); narrow matrices at moderate row
   // counts stay on the stream path.
   if (R >= DENSE_MIN_ROWS && (dense_tiles >= 32 || K >= 8192)) {
+    // The tile height and K split with the lowest estimate (the logits
+    // epilogue never splits; splits must fit the partial buffer and keep at
+    // least 256 k each).
+    double t_best = 1e30;
+    for (int rf : {16, 12, 8}) {
+      for (int S = 1; S <= (logits ? 1 : 16); ++S) {
+        if (S > 1 && (K / S < 256 || (size_t)S * NM * R * N > partials_cap)) break;
+        const double t = dense_cost(R, N, K, NM, rf, S);
+        if (t < t_best) {
+          t_best = t;
+          p.RT = rf;
+          p.S = S;
+        }
+      }
+    }
     p.dense = true;
-    p.RT = best;
     p.NT = 4 / NM;
-    p.D = best == 8 ? 4 : 3;
-    p.S = 1;
-    if (!logits)
-      while (dense_tiles * p.S < 256 && K / (p.S * 2) >= 256) p.S *= 2;
+    p.D = p.RT == 8 ? 4 : 3;
     return p;
   }
   p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
@@ -537,7 +564,7 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits) {
 }
 
 int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K) {
-  const GemmPlan p = plan_gemm(R, N, K, 1, true);
+  const GemmPlan p = plan_gemm(R, N, K, 1, true, 0);
   if (p.dense) return (N + DENSE_TN - 1) / DENSE_TN * 2;
   const int cols = 16 * p.NT;
   return (N + cols * p.NW - 1) / (cols * p.NW) * p.NW;
@@ -610,7 +637,7 @@ static hipError_t launch_dense(const GemmArgs& a, int S, hipStream_t st) {
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
   constexpr int NM = EpiTraits<EPI>::NM;
-  const GemmPlan p = plan_gemm(a.R, a.N, a.K, NM, EPI == EPI_LOGITS);
+  const GemmPlan p = plan_gemm(a.R, a.N, a.K, NM, EPI == EPI_LOGITS, a.partials_cap);
   if (p.dense) {
     if (p.RT == 16) return launch_dense<16, 3, EPI>(a, p.S, st);
     if (p.RT == 12) return launch_dense<12, 3, EPI>(a, p.S, st);
