@@ -67,9 +67,13 @@ def decode_step(big, B, seed, sample_rows, lo=512, hi=4096, ctx=None):
 
 # One case per GEMM shape: 16-row fragments (1, 8, 16), 32 rows (24: a
 # partly filled second fragment), 64 rows (40: partly filled; 64: the 8-wave
-# LM head) and the dense path (96).
+# LM head) and the dense path, whose tile height and K split depend on the
+# row count: 96 (128-row tiles, down in 16 splits), 150 (192-row tiles, a
+# partly filled tile), 300 (QKV in 5 splits, O on 128-row tiles), 400
+# (256-row tiles, O in 4 splits, a partly filled second row group).
 @pytest.mark.parametrize("B,rows", [(1, [0]), (8, [0, 3, 7]), (16, [0, 15]), (24, [0, 11, 23]),
-                                    (40, [0, 39]), (64, [0, 17, 40, 63]), (96, [0, 65, 95])])
+                                    (40, [0, 39]), (64, [0, 17, 40, 63]), (96, [0, 65, 95]),
+                                    (150, [0, 77, 149]), (300, [0, 299]), (400, [0, 211, 399])])
 def test_8b_layer_decode_step_matches_oracle(big, B, rows):
     ok, mx, res, g_tk, r_tk, own, all_tk = decode_step(big, B, seed=B, sample_rows=rows)
     print(f"B={B}: max abs logit error {mx:.4f}, resolvable rows {int(res.sum())}/{len(rows)}")
