@@ -72,6 +72,25 @@ struct PieceSched {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Issue priority from a wave's progress: 3 in the first quarter of its key
+// steps, down to 0 in the last. Two waves share each SIMD, and at equal
+// priority the older one wins every arbitration once the memory pipeline is
+// full, so with a fixed schedule the younger workgroup on a CU finished about
+// 1.5x later than the older one and ran its tail at half occupancy. Ranking by
+// progress lets the wave that is behind catch up (the schedule, and so the
+// result, does not change).
+__device__ __forceinline__ void progress_prio(int done, int total) {
+  const int lvl = min(3, (4 * done) / max(total, 1));
+  if (lvl == 0)
+    __builtin_amdgcn_s_setprio(3);
+  else if (lvl == 1)
+    __builtin_amdgcn_s_setprio(2);
+  else if (lvl == 2)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // The fewest rounds of P waves whose pieces fit in `hi` steps, then the
 // shortest pieces (not below `lo`) that cover T in that many rounds.
 __device__ __forceinline__ PieceSched piece_sched(int T, const AttnPlan& ap, int kvh) {
@@ -102,7 +121,7 @@ __device__ __forceinline__ void attend_segment(
     const RowMaps& maps, const ModelDims& md, const AttnPlan& ap,
     const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v,
     float* __restrict__ part_ml, float* __restrict__ part_o, uint32_t* status, int* tbl, int s,
-    int g, int qt, int nn, int ctx, int k_lo, int k_hi, int sp) {
+    int g, int qt, int nn, int ctx, int k_lo, int k_hi, int sp, int done, int total) {
   constexpr int QK_STEPS = HD / 32;  // MFMAs over head_dim
   constexpr int DT = HD / 16;        // output d tiles
   const int lane = threadIdx.x & 63;
@@ -320,6 +339,7 @@ __device__ __forceinline__ void attend_segment(
     load(A, k_lo);
     int i = 0;
     for (; i + 2 <= n_it; i += 2) {
+      progress_prio(done + i, total);
       load(B, k_lo + 32 * (i + 1));
       compute(A, k_lo + 32 * i);
       load(A, min(k_lo + 32 * (i + 2), last_step));
@@ -368,7 +388,10 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   const PieceSched ps = piece_sched(T, ap, md.n_kv_heads);
   const int n_pieces = ps.per_head * md.n_kv_heads;
   const int rpt = 16 / (md.n_heads / md.n_kv_heads);
-  for (int p = blockIdx.x * ATT_WAVES + wave; p < n_pieces; p += ap.grid_items) {
+  const int first = blockIdx.x * ATT_WAVES + wave;
+  const int total = first < n_pieces ? ceil_div(n_pieces - first, ap.grid_items) * ps.len : 0;
+  int done = 0;  // key steps of this wave so far
+  for (int p = first; p < n_pieces; p += ap.grid_items) {
     const int g = p / ps.per_head, q = p % ps.per_head;
     int b = q * ps.len;
     const int b_end = min(T, b + ps.len);
@@ -391,9 +414,10 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
       } else {
         attend_segment<HD, BS>(q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o,
                                status, s_tbl[wave], s, g, qt, nn, ctx, 32 * rel,
-                               min(keys, 32 * (rel + seg)), sp);
+                               min(keys, 32 * (rel + seg)), sp, done, total);
       }
       b += seg;
+      done += seg;
     }
   }
 }
