@@ -718,8 +718,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= R * md.n_heads) return;
   const int r = w / md.n_heads, h = w % md.n_heads;
-  constexpr int PER = HD / 64;  // dims per lane
-  const size_t at = ((size_t)r * md.n_heads + h) * HD + lane * PER;
+  constexpr int PER = HD / 64;  // dims per lane (consecutive: one 8-column run of a tile)
+  const size_t at = tile_at(r, h * HD + lane * PER, (md.n_heads * HD + 31) / 32);
   const int s = maps.row_seq[r];
   if (s < 0) {
 #pragma unroll

@@ -42,8 +42,22 @@ __device__ __forceinline__ void split_bf(float v, bf16_t& hi, bf16_t& lo) {
   lo = f2bf(v - bf2f(hi));
 }
 
+// Split activations that feed a contraction are kept in operand tiles: each
+// plane [rows][w] is cut into 1 KB tiles of 16 rows x 32 columns, tile
+// (f, kb) at element (f * KB + kb) * 512 with KB = ceil(w / 32), and inside
+// a tile columns 32 kb + 8 j .. + 7 of row 16 f + i sit at (16 j + i) * 8.
+// A 64-lane copy of 16 bytes per lane then moves one whole tile, contiguous,
+// into exactly the order the MFMA B operand is read in (lane 16 j + i: row
+// i, columns 8 j ..). Row-major rows instead make every copy touch 16 rows
+// of 64 bytes, which the vector memory path serves at about a third of the
+// rate of a contiguous kilobyte.
+__host__ __device__ __forceinline__ size_t tile_at(int r, int k, int KB) {
+  return (((size_t)(r >> 4) * KB + (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (r & 15)) * 8 + (k & 7);
+}
+
 // Split four consecutive values and store them to the hi and lo planes
-// (8-byte stores; p must be 8-byte aligned in both planes).
+// (8-byte stores; `at` must be a multiple of 4: in operand tiles the four
+// columns 4 m .. 4 m + 3 of a row are contiguous).
 __device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, size_t at, float a,
                                              float b, float c, float d) {
   bf16_t h[4], l[4];

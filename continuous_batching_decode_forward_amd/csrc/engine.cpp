@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "runtime.h"
@@ -74,15 +75,16 @@ WorkspaceLayout workspace_layout(const cbd_config& c) {
   L.item0 = take((S + 1) * 4);
   L.row_out = take(R * 4);
   L.item0b = take((S + 1) * 4);
-  // fp32 buffers [rows][w] and split buffers (hi plane [rows][w] bf16, then
-  // the lo plane) both take 4 bytes per element.
+  // fp32 buffers [rows][w] and split buffers (hi plane bf16, then the lo
+  // plane) both take 4 bytes per element; the split inputs of the
+  // projections are in operand tiles, rows and columns padded to 16 and 32.
   L.x = take(R * d * 4);
-  L.h = take(R * d * 4);
+  L.h = take(tile_plane_elems(R, d) * 4);
   L.qkv = take(R * qkv_n * 4);
   L.q = take(R * qd * 4);
-  L.attn = take(R * qd * 4);
-  L.ffn = take(R * (size_t)c.ffn_dim * 4);
-  L.lm_in = take(S * d * 4);
+  L.attn = take(tile_plane_elems(R, qd) * 4);
+  L.ffn = take(tile_plane_elems(R, c.ffn_dim) * 4);
+  L.lm_in = take(tile_plane_elems(S, d) * 4);
   L.logits = take(S * (size_t)c.vocab * 4);
   L.amax_stride = (c.vocab + 15) / 16;
   L.amax_val = take(S * (size_t)L.amax_stride * 4);
@@ -299,6 +301,17 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* packed_
     he = launch_pack(e->lm_head, cfg->vocab, cfg->d_model, e->packed + e->pl.lm_head, e->stream);
   if (he == hipSuccess)
     he = launch_fill_u32(e->wsp<uint32_t>(e->ws.status), 0u, 1, e->stream);
+  // The operand-tile buffers start as zeros: their padding columns are read
+  // by the contractions (against zero weights) and never written.
+  {
+    const size_t R = (size_t)cfg->max_rows, S = (size_t)cfg->max_seqs;
+    const size_t qd = (size_t)cfg->n_heads * cfg->head_dim;
+    const std::pair<size_t, size_t> tiled[] = {
+        {e->ws.h, tile_plane_elems(R, cfg->d_model)}, {e->ws.attn, tile_plane_elems(R, qd)},
+        {e->ws.ffn, tile_plane_elems(R, cfg->ffn_dim)}, {e->ws.lm_in, tile_plane_elems(S, cfg->d_model)}};
+    for (const auto& t : tiled)  // two bf16 planes: one u32 per element
+      if (he == hipSuccess) he = launch_fill_u32(e->wsp<uint32_t>(t.first), 0u, t.second, e->stream);
+  }
   if (he == hipSuccess)
     he = launch_fill_u32((uint32_t*)e->slot_state, 0u, e->sl.total / 4, e->stream);
   if (he == hipSuccess) he = hipStreamSynchronize(e->stream);
@@ -453,13 +466,13 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
   float* qkv = e->wsp<float>(e->ws.qkv);
   // split buffers: the lo plane follows the hi plane
   uint16_t* h = e->wsp<uint16_t>(e->ws.h);
-  uint16_t* h_lo = h + MR * c.d_model;
+  uint16_t* h_lo = h + tile_plane_elems(MR, c.d_model);
   uint16_t* q = e->wsp<uint16_t>(e->ws.q);
   uint16_t* q_lo = q + MR * qd;
   uint16_t* attn = e->wsp<uint16_t>(e->ws.attn);
-  uint16_t* attn_lo = attn + MR * qd;
+  uint16_t* attn_lo = attn + tile_plane_elems(MR, qd);
   uint16_t* ffn = e->wsp<uint16_t>(e->ws.ffn);
-  uint16_t* ffn_lo = ffn + MR * c.ffn_dim;
+  uint16_t* ffn_lo = ffn + tile_plane_elems(MR, c.ffn_dim);
   float* gpart = e->wsp<float>(e->ws.gemm_part);
 
   HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
@@ -470,7 +483,7 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
   // per layer QKV -> RoPE/append (+ the QKV split sum) -> attention -> O ->
   // residual + pre-FFN norm -> gate/up -> down -> residual + the next norm.
   uint16_t* lm_in = e->wsp<uint16_t>(e->ws.lm_in);
-  uint16_t* lm_in_lo = lm_in + (size_t)c.max_seqs * c.d_model;
+  uint16_t* lm_in_lo = lm_in + tile_plane_elems(c.max_seqs, c.d_model);
   int32_t splits = 1;
   for (int l = 0; l < c.n_layers; ++l) {
     GemmArgs g{};
@@ -569,12 +582,12 @@ int cbd_debug_buffer(cbd_engine* e, int32_t which, void** ptr, size_t* bytes) {
   size_t off, n;
   switch (which) {
     case CBD_BUF_X: off = e->ws.x; n = R * c.d_model; break;
-    case CBD_BUF_H: off = e->ws.h; n = R * c.d_model; break;
+    case CBD_BUF_H: off = e->ws.h; n = tile_plane_elems(R, c.d_model); break;
     case CBD_BUF_QKV: off = e->ws.qkv; n = R * qkv_n; break;
     case CBD_BUF_Q: off = e->ws.q; n = R * qd; break;
-    case CBD_BUF_ATTN: off = e->ws.attn; n = R * qd; break;
-    case CBD_BUF_FFN: off = e->ws.ffn; n = R * c.ffn_dim; break;
-    case CBD_BUF_LM_IN: off = e->ws.lm_in; n = (size_t)c.max_seqs * c.d_model; break;
+    case CBD_BUF_ATTN: off = e->ws.attn; n = tile_plane_elems(R, qd); break;
+    case CBD_BUF_FFN: off = e->ws.ffn; n = tile_plane_elems(R, c.ffn_dim); break;
+    case CBD_BUF_LM_IN: off = e->ws.lm_in; n = tile_plane_elems(c.max_seqs, c.d_model); break;
     default: return fail(CBD_E_INVAL, "unknown buffer");
   }
   *ptr = e->workspace + off;

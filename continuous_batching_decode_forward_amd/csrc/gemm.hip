@@ -71,7 +71,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& a, int r, int n, const
     x.w += v0[3];
     *p = x;
   } else if (EPI == EPI_SWIGLU) {
-    store_split4(a.Yh, a.Yl, at, silu_f(v0[0]) * v1[0], silu_f(v0[1]) * v1[1],
+    store_split4(a.Yh, a.Yl, tile_at(r, n, (a.N + 31) / 32), silu_f(v0[0]) * v1[0], silu_f(v0[1]) * v1[1],
                  silu_f(v0[2]) * v1[2], silu_f(v0[3]) * v1[3]);
   } else {  // EPI_LOGITS
     if (a.logits)
@@ -203,16 +203,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     wp[0][nt] = a.W + off;
     if (NM == 2) wp[NM - 1][nt] = a.W2 + off;
   }
-  // This wave copies blocks b = wave + NW i of every stage; lane `lane` of
-  // block (rt, pl, h) is row r0 + 16 rt + lr, k + 32 h + 8 lg. Rows past R
-  // read row R - 1 (their outputs are never stored).
+  // This wave copies blocks b = wave + NW i of every stage; block (rt, pl, h)
+  // of stage c is the operand tile (row fragment r0 / 16 + rt, k-block
+  // kbeg / 32 + 2 c + h) of plane pl: lane `lane` holds row r0 + 16 rt + lr,
+  // k + 32 h + 8 lg. Fragments past R read the last one (their outputs are
+  // never stored).
   const uint16_t* xsrc[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int b = wave + NW * i;
     const int rt = b >> 2, pl = (b >> 1) & 1;
-    const int r = min(r0 + 16 * rt + lr, R - 1);
-    xsrc[i] = (pl ? a.Xlo : a.X) + (size_t)r * K;
+    const int f = min(r0 / 16 + rt, (R - 1) >> 4);
+    xsrc[i] = (pl ? a.Xlo : a.X) + (size_t)f * KT * 512 + lane * 8;
   }
 
   floatx4_t acc[NM][NT][RT];
@@ -238,8 +240,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int b = wave + NW * i;
-      const int k = min(kbeg + 64 * c + 32 * (b & 1) + 8 * lg, K - 8);
-      copy16_to_lds(xsrc[i] + k, xs + ((size_t)j * BLK + b) * 64);
+      const int kb = min(kbeg / 32 + 2 * c + (b & 1), KT - 1);
+      copy16_to_lds(xsrc[i] + (size_t)kb * 512, xs + ((size_t)j * BLK + b) * 64);
     }
   };
   auto compute = [&](int j, int c) {
@@ -309,9 +311,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 // The workgroups that share a weight tile (its row groups and K splits) are
 // numbered so that they land on one XCD (workgroup i runs on XCD i mod 8):
 // their repeated weight reads meet in that XCD's L2. Past K the packed
-// weights are zero and activation reads are clamped into the row, so a K
-// tail needs no masking (K is a multiple of 8 and every split but the last
-// ends on a 32-k boundary).
+// weights and the operand tiles' padding columns are zero, so a K tail
+// needs no masking (every split but the last ends on a 32-k boundary).
 #define DENSE_TN 256
 
 #define DENSE_WAVES 8
@@ -348,8 +349,9 @@ __global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a
   constexpr int CB = 2 * NT;  // 16-column blocks per matrix per workgroup
 
   // Copy sources: this wave issues tiles t = wave + 8 i; t < 16 are weight
-  // tiles (matrix t / CB, column block t % CB), the rest activation
-  // fragments (u = t - 16: row fragment u / 2, plane u % 2).
+  // tiles (matrix t / CB, column block t % CB), the rest activation operand
+  // tiles (u = t - 16: row fragment u / 2, plane u % 2; fragments past R
+  // read the last one, whose outputs are never stored).
   const uint16_t* src[LPS];
 #pragma unroll
   for (int i = 0; i < LPS; ++i) {
@@ -361,8 +363,8 @@ __global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a
       src[i] = (m ? a.W2 : a.W) + wtile(nb, kbeg / 32, KT) + lane * 8;
     } else {
       const int u = t - TW;
-      const int r = min(r_base + 16 * (u >> 1) + lr, R - 1);
-      src[i] = ((u & 1) ? a.Xlo : a.X) + (size_t)r * K;
+      const int f = min(r_base / 16 + (u >> 1), (R - 1) >> 4);
+      src[i] = ((u & 1) ? a.Xlo : a.X) + (size_t)f * KT * 512 + lane * 8;
     }
   }
   auto issue = [&](int slot, int c) {
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a
       if (i < TW / DENSE_WAVES)  // weights: streamed once, kept out of L2's way
         copy16_to_lds_nt(src[i] + (size_t)c * WT_NEXT, ring + ((size_t)slot * TS + t) * 64);
       else  // activations: re-read by every column tile, kept in L2
-        copy16_to_lds(src[i] + min(kbeg + 32 * c + 8 * lg, K - 8),
+        copy16_to_lds(src[i] + (size_t)min(kbeg / 32 + c, KT - 1) * 512,
                       ring + ((size_t)slot * TS + t) * 64);
     }
   };

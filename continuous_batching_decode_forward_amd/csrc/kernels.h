@@ -76,14 +76,11 @@ hipError_t launch_prep_embed(const StepMeta& m, const RowMaps& maps, const Model
 // Activation storage. The residual stream x and the QKV projection are fp32
 // [rows][width]. Activations that feed an MFMA contraction (norm outputs,
 // rotated queries, attention output, SwiGLU product) are "split": two bf16
-// planes hi [rows][width] and lo [rows][width] with hi + lo = the fp32 value
-// (split_bf in common.h).
+// planes hi and lo with hi + lo = the fp32 value (split_bf in common.h). The
+// rotated queries are row-major planes [rows][width]; the inputs of the
+// projections are in operand tiles (tile_at in common.h).
 
 // x[r] = embed[tokens[r]] (fp32), h[r] = rmsnorm(x[r]) * gain (split).
-
-// h[j] = rmsnorm(x[rows ? rows[j] : j]) * gain for j < R (rows[j] < 0: zeros).
-hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int32_t R, const uint16_t* gain,
-                          int32_t d, float eps, uint16_t* h_hi, uint16_t* h_lo, hipStream_t st);
 
 // The end of a residual projection and the norm that follows it, per row r:
 // x[r] += sum over s < S of part[s][r] (S > 1: the projection's split-K
@@ -126,17 +123,25 @@ enum GemmEpilogue { EPI_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 }
 size_t packed_elems(int32_t N, int32_t K);
 hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, hipStream_t st);
 
+// Elements of one plane of a split activation buffer in operand tiles
+// (rows and columns rounded up to 16 and 32; the padding columns must hold
+// zeros -- the engine clears these buffers once -- because the contractions
+// read whole tiles).
+inline size_t tile_plane_elems(size_t rows, size_t w) {
+  return (rows + 15) / 16 * 16 * ((w + 31) / 32 * 32);
+}
+
 struct GemmArgs {
-  const uint16_t* X;    // [R][K] split activation: hi plane
-  const uint16_t* Xlo;  //                          lo plane
+  const uint16_t* X;    // [R][K] split activation in operand tiles: hi plane
+  const uint16_t* Xlo;  //                                             lo plane
   int32_t R, K;
   const uint16_t* W;    // [N][K] bf16, packed
   const uint16_t* W2;   // second packed matrix for EPI_SWIGLU (up), [N][K]
   int32_t N;
   int32_t epi;
   float* Y;             // EPI_F32 out [R][N]; EPI_RESID in/out [R][N] (fp32)
-  uint16_t* Yh;         // EPI_SWIGLU out [R][N] split: hi plane
-  uint16_t* Yl;         //                              lo plane
+  uint16_t* Yh;         // EPI_SWIGLU out [R][N] split, operand tiles: hi plane
+  uint16_t* Yl;         //                                         lo plane
   float* logits;        // EPI_LOGITS out [R][N] (nullable: argmax only)
   float* amax_val;      // EPI_LOGITS per-(row, column tile) maxima [R][amax_stride]
   int32_t* amax_idx;

@@ -226,15 +226,15 @@ __device__ void embed_row(int r, const int32_t* __restrict__ tokens,
 #pragma unroll
   for (int w = 0; w < PREP_WAVES; ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-  uint16_t* hh = h_hi + (size_t)r * d;
-  uint16_t* hl = h_lo + (size_t)r * d;
+  const int KB = (d + 31) / 32;
 #pragma unroll
   for (int c = 0; c < EN_MAX_CHUNKS; ++c) {
     const int ch = t + c * PREP_THREADS;
     if (ch < nch) {
       const uint2 gv = reinterpret_cast<const uint2*>(gain)[ch];
-      store_split4(hh, hl, (size_t)ch * 4, xv[c].x * inv * lo_bf(gv.x), xv[c].y * inv * hi_bf(gv.x),
-                   xv[c].z * inv * lo_bf(gv.y), xv[c].w * inv * hi_bf(gv.y));
+      store_split4(h_hi, h_lo, tile_at(r, 4 * ch, KB), xv[c].x * inv * lo_bf(gv.x),
+                   xv[c].y * inv * hi_bf(gv.x), xv[c].z * inv * lo_bf(gv.y),
+                   xv[c].w * inv * hi_bf(gv.y));
     }
   }
 }
@@ -265,77 +265,6 @@ hipError_t launch_prep_embed(const StepMeta& m, const RowMaps& maps, const Model
 
 // ---------------------------------------------------------------- RMSNorm
 //
-// One workgroup of 256 threads per row. Each thread holds up to 32 fp32
-// values (d_model <= 8192, d_model % 4 == 0), in 16-byte chunks t, t + 256,
-// ...: mean of squares in fp32, then y = x * (1 / sqrt(ms + eps)) * g,
-// stored split (hi, lo planes) for the GEMM that consumes it.
-
-#define NORM_THREADS 256
-#define NORM_MAX_CHUNKS 8  // float4 chunks per thread: d <= 256 * 4 * 8
-
-__device__ float block_sum_256(float v, float* red) {
-  v = wave_sum(v);
-  int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float s = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
-  return s;
-}
-
-__device__ void norm_row(const float* __restrict__ x, const uint16_t* __restrict__ g, int d,
-                         float eps, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
-                         float* red) {
-  const int nch = d >> 2;
-  float4 xv[NORM_MAX_CHUNKS];
-  float ss = 0.f;
-#pragma unroll
-  for (int c = 0; c < NORM_MAX_CHUNKS; ++c) {
-    int ch = threadIdx.x + c * NORM_THREADS;
-    xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ch < nch) {
-      xv[c] = reinterpret_cast<const float4*>(x)[ch];
-      ss += xv[c].x * xv[c].x + xv[c].y * xv[c].y + xv[c].z * xv[c].z + xv[c].w * xv[c].w;
-    }
-  }
-  float tot = block_sum_256(ss, red);
-  float inv = 1.0f / sqrtf(tot / (float)d + eps);
-#pragma unroll
-  for (int c = 0; c < NORM_MAX_CHUNKS; ++c) {
-    int ch = threadIdx.x + c * NORM_THREADS;
-    if (ch < nch) {
-      uint2 gv = reinterpret_cast<const uint2*>(g)[ch];
-      store_split4(h_hi, h_lo, (size_t)ch * 4, xv[c].x * inv * lo_bf(gv.x),
-                   xv[c].y * inv * hi_bf(gv.x), xv[c].z * inv * lo_bf(gv.y),
-                   xv[c].w * inv * hi_bf(gv.y));
-    }
-  }
-}
-
-__global__ __launch_bounds__(NORM_THREADS) void rmsnorm_kernel(
-    const float* __restrict__ x, const int32_t* __restrict__ rows,
-    const uint16_t* __restrict__ gain, int d, float eps, uint16_t* __restrict__ h_hi,
-    uint16_t* __restrict__ h_lo) {
-  __shared__ float red[4];
-  const int j = blockIdx.x;
-  int src = rows ? rows[j] : j;
-  if (src < 0) {  // refused row: zeros, so later stages see finite values
-    for (int ch = threadIdx.x; ch < (d >> 2); ch += NORM_THREADS) {
-      reinterpret_cast<uint2*>(h_hi + (size_t)j * d)[ch] = make_uint2(0, 0);
-      reinterpret_cast<uint2*>(h_lo + (size_t)j * d)[ch] = make_uint2(0, 0);
-    }
-    return;
-  }
-  norm_row(x + (size_t)src * d, gain, d, eps, h_hi + (size_t)j * d, h_lo + (size_t)j * d, red);
-}
-
-hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int32_t R, const uint16_t* gain,
-                          int32_t d, float eps, uint16_t* h_hi, uint16_t* h_lo, hipStream_t st) {
-  if (R <= 0) return hipSuccess;
-  rmsnorm_kernel<<<R, NORM_THREADS, 0, st>>>(x, rows, gain, d, eps, h_hi, h_lo);
-  return hipGetLastError();
-}
-
 // One workgroup per row, one float4 chunk of the row per thread (up to
 // RN_MAX_CHUNKS when the row is wider than the workgroup): the residual sum
 // (the split partials of a chunk are all loaded, then added in split order),
@@ -355,9 +284,10 @@ __global__ __launch_bounds__(1024) void resid_norm_kernel(
   if (r >= R) {  // output o = r - R with no row (refused): zeros, finite downstream
     const int o = r - R;
     if (out_row[o] >= 0) return;
+    const int KB = (d + 31) / 32;
     for (int ch = t; ch < nch; ch += T) {
-      reinterpret_cast<uint2*>(h_hi + (size_t)o * d)[ch] = make_uint2(0, 0);
-      reinterpret_cast<uint2*>(h_lo + (size_t)o * d)[ch] = make_uint2(0, 0);
+      *reinterpret_cast<uint2*>(h_hi + tile_at(o, 4 * ch, KB)) = make_uint2(0, 0);
+      *reinterpret_cast<uint2*>(h_lo + tile_at(o, 4 * ch, KB)) = make_uint2(0, 0);
     }
     return;
   }
@@ -401,15 +331,15 @@ __global__ __launch_bounds__(1024) void resid_norm_kernel(
   float tot = 0.f;
   for (int w = 0; w < (T >> 6); ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-  uint16_t* hh = h_hi + (size_t)dst * d;
-  uint16_t* hl = h_lo + (size_t)dst * d;
+  const int KB = (d + 31) / 32;
 #pragma unroll
   for (int c = 0; c < RN_MAX_CHUNKS; ++c) {
     const int ch = t + c * T;
     if (ch < nch) {
       const uint2 gv = reinterpret_cast<const uint2*>(gain)[ch];
-      store_split4(hh, hl, (size_t)ch * 4, xv[c].x * inv * lo_bf(gv.x), xv[c].y * inv * hi_bf(gv.x),
-                   xv[c].z * inv * lo_bf(gv.y), xv[c].w * inv * hi_bf(gv.y));
+      store_split4(h_hi, h_lo, tile_at(dst, 4 * ch, KB), xv[c].x * inv * lo_bf(gv.x),
+                   xv[c].y * inv * hi_bf(gv.x), xv[c].z * inv * lo_bf(gv.y),
+                   xv[c].w * inv * hi_bf(gv.y));
     }
   }
 }

@@ -35,6 +35,16 @@ class StepMeta:
     n_out: int
 
 
+def untile_plane(flat: np.ndarray, rows: int, width: int) -> np.ndarray:
+    """[rows][width] from one plane in operand tiles (1 KB tiles of 16 rows x
+    32 columns, rows padded to 16 and columns to 32; see cbd.h)."""
+    kb = (width + 31) // 32
+    f = flat.size // (kb * 512)
+    # [fragment][k-block][8-column group][row in fragment][8] -> [row][column]
+    v = flat.reshape(f, kb, 4, 16, 8).transpose(0, 3, 1, 2, 4).reshape(f * 16, kb * 32)
+    return v[:rows, :width]
+
+
 class Engine:
     def __init__(self, shape, weights: dict, *, block_size: int, num_blocks: int,
                  max_blocks_per_seq: int, max_slots: int, max_rows: int, max_seqs: int,
@@ -135,8 +145,10 @@ class Engine:
         return self.slot_state[params_bytes:params_bytes + s.max_slots * s.vocab * 4].view(
             torch.float32).view(s.max_slots, s.vocab)
 
-    # Buffers that hold fp32 values as two bf16 planes (hi, then lo).
+    # Buffers that hold fp32 values as two bf16 planes (hi, then lo), and
+    # those of them whose planes are in operand tiles (16 x 32 tiles of 1 KB).
     _SPLIT = (B.CBD_BUF_H, B.CBD_BUF_Q, B.CBD_BUF_ATTN, B.CBD_BUF_FFN, B.CBD_BUF_LM_IN)
+    _TILED = (B.CBD_BUF_H, B.CBD_BUF_ATTN, B.CBD_BUF_FFN, B.CBD_BUF_LM_IN)
 
     def debug_buffer(self, which: int, rows: int, width: int) -> np.ndarray:
         """The first `rows` rows of an internal activation buffer as float64
@@ -149,10 +161,13 @@ class Engine:
             return buf[:rows * width * 4].view(torch.float32).view(rows, width).cpu().numpy() \
                 .astype(np.float64)
         plane = nbytes // 2
-        def part(o):
-            u = buf[o:o + rows * width * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+        def part(o, n):
+            u = buf[o:o + n * 2].view(torch.int16).cpu().numpy().view(np.uint16)
             return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-        return (part(0) + part(plane)).reshape(rows, width)
+        if which not in self._TILED:
+            return (part(0, rows * width) + part(plane, rows * width)).reshape(rows, width)
+        n = plane // 2  # elements per plane: rows padded to 16, columns to 32
+        return untile_plane(part(0, n) + part(plane, n), rows, width)
 
     def close(self):
         if getattr(self, "handle", None):

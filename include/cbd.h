@@ -230,17 +230,21 @@ const char* cbd_last_error(void);
  * multi-layer models: the last layer's). Row i is the i-th row of the step
  * (for CBD_BUF_LM_IN: the i-th emitting sequence). Activations are fp32
  * values. "fp32" buffers hold float [rows][w]. "split" buffers hold the
- * value as two bf16 terms: a hi plane [rows][w] followed by a lo plane
- * [rows][w], value = hi + lo (hi = bf16(v), lo = bf16(v - hi)); the
- * contractions consume them that way. rows = max_rows (max_seqs for
- * CBD_BUF_LM_IN). */
+ * value as two bf16 terms, a hi plane followed by a lo plane, value = hi +
+ * lo (hi = bf16(v), lo = bf16(v - hi)); the contractions consume them that
+ * way. A "row-major" split plane is [rows][w]. A "tiled" split plane (the
+ * inputs of the projections) is in operand tiles: rows padded to a multiple
+ * of 16 (R16) and columns to a multiple of 32 (KB = w32 / 32 blocks), element
+ * (r, k) at ((r / 16 * KB + k / 32) * 64 + (k / 8 % 4) * 16 + r % 16) * 8 +
+ * k % 8, i.e. 1 KB tiles of 16 rows x 32 columns; each plane holds
+ * R16 * w32 elements. rows = max_rows (max_seqs for CBD_BUF_LM_IN). */
 #define CBD_BUF_X 1      /* fp32: residual stream after the step [rows][d_model] */
-#define CBD_BUF_H 2      /* split: last RMSNorm output, the FFN input [rows][d_model] */
+#define CBD_BUF_H 2      /* split, tiled: last RMSNorm output, the FFN input [rows][d_model] */
 #define CBD_BUF_QKV 3    /* fp32: QKV projection [rows][(n_heads+2*n_kv_heads)*head_dim] */
-#define CBD_BUF_Q 4      /* split: rotated queries [rows][n_heads*head_dim] */
-#define CBD_BUF_ATTN 5   /* split: attention output [rows][n_heads*head_dim] */
-#define CBD_BUF_FFN 6    /* split: SwiGLU output [rows][ffn_dim] */
-#define CBD_BUF_LM_IN 7  /* split: final-norm rows fed to the LM head [rows][d_model] */
+#define CBD_BUF_Q 4      /* split, row-major: rotated queries [rows][n_heads*head_dim] */
+#define CBD_BUF_ATTN 5   /* split, tiled: attention output [rows][n_heads*head_dim] */
+#define CBD_BUF_FFN 6    /* split, tiled: SwiGLU output [rows][ffn_dim] */
+#define CBD_BUF_LM_IN 7  /* split, tiled: final-norm rows fed to the LM head [rows][d_model] */
 /* Device address and size in bytes of one of them (no copy, no sync). */
 int cbd_debug_buffer(cbd_engine* e, int32_t which, void** ptr, size_t* bytes);
 

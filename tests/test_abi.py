@@ -74,3 +74,21 @@ def test_engine_create_rejects_null_buffers():
 def test_step_rejects_null_engine():
     st = B.cbd_step()
     assert B.lib().cbd_step_forward(None, C.byref(st), None, None, None) == B.CBD_E_INVAL
+
+
+@pytest.mark.parametrize("rows,width", [(37, 688), (16, 256), (1, 4096), (560, 128)])
+def test_operand_tile_layout_reader_inverts_the_documented_layout(rows, width):
+    # The layout cbd.h documents for "tiled" split planes: element (r, k) at
+    # ((r / 16 * KB + k / 32) * 64 + (k / 8 % 4) * 16 + r % 16) * 8 + k % 8.
+    import numpy as np
+    from continuous_batching_decode_forward_amd.engine import untile_plane
+    r16, w32 = -(-rows // 16) * 16, -(-width // 32) * 32
+    kb = w32 // 32
+    vals = np.arange(rows * width, dtype=np.float64).reshape(rows, width) + 1.0
+    flat = np.zeros(r16 * w32)
+    for r in range(rows):
+        for k in range(width):
+            at = ((r // 16 * kb + k // 32) * 64 + (k // 8 % 4) * 16 + r % 16) * 8 + k % 8
+            assert flat[at] == 0.0
+            flat[at] = vals[r, k]
+    assert np.array_equal(untile_plane(flat, rows, width), vals)
