@@ -706,7 +706,8 @@ __global__ __launch_bounds__(64 * ATB_WAVES) void attention_block_kernel(
 
 // Combine the splits of one (row, head): out = sum_j 2^(m_j - M) o_j /
 // sum_j 2^(m_j - M) l_j over the partial results that hold keys of this row,
-// in key order. One wave per (row, head), 4 per workgroup.
+// in key order. HD / 8 lanes per (row, head), 8 consecutive dims each, so
+// that every lane writes one whole 16-byte run of an operand tile per plane.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps maps, ModelDims md,
                                                            AttnPlan ap, int R,
@@ -714,16 +715,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
                                                            const float* __restrict__ part_o,
                                                            uint16_t* __restrict__ out_hi,
                                                            uint16_t* __restrict__ out_lo) {
-  const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int LPP = HD / 8;     // lanes per (row, head)
+  constexpr int PPB = 256 / LPP;  // (row, head) pairs per workgroup
+  const int sl = threadIdx.x % LPP;
+  const int w = blockIdx.x * PPB + threadIdx.x / LPP;
   if (w >= R * md.n_heads) return;
   const int r = w / md.n_heads, h = w % md.n_heads;
-  constexpr int PER = HD / 64;  // dims per lane (consecutive: one 8-column run of a tile)
-  const size_t at = tile_at(r, h * HD + lane * PER, (md.n_heads * HD + 31) / 32);
+  const size_t at = tile_at(r, h * HD + 8 * sl, (md.n_heads * HD + 31) / 32);
   const int s = maps.row_seq[r];
   if (s < 0) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) out_hi[at + e] = out_lo[at + e] = 0;
+    *reinterpret_cast<uint4*>(out_hi + at) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(out_lo + at) = make_uint4(0, 0, 0, 0);
     return;
   }
   const int pos = maps.row_pos[r];
@@ -743,24 +745,27 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
   const size_t base = ((size_t)r * md.n_heads + h) * ap.max_splits;
   float M = -INFINITY;
   for (int j = 0; j < n_sp; ++j) M = fmaxf(M, part_ml[2 * (base + j)]);
-  float acc[PER], den = 0.f;
+  float acc[8], den = 0.f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   for (int j = 0; j < n_sp; ++j) {
     const float wj = exp2f(part_ml[2 * (base + j)] - M);
     den += wj * part_ml[2 * (base + j) + 1];
-    const float* op = part_o + (base + j) * HD + lane * PER;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += wj * op[e];
+    const float4* op = reinterpret_cast<const float4*>(part_o + (base + j) * HD + 8 * sl);
+    const float4 a = op[0], b = op[1];
+    acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
+    acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
   }
   const float inv = 1.0f / den;
+  bf16_t hi[8], lo[8];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    bf16_t hi, lo;
-    split_bf(acc[e] * inv, hi, lo);
-    out_hi[at + e] = hi;
-    out_lo[at + e] = lo;
-  }
+  for (int e = 0; e < 8; ++e) split_bf(acc[e] * inv, hi[e], lo[e]);
+  *reinterpret_cast<uint4*>(out_hi + at) =
+      make_uint4((uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16),
+                 (uint32_t)hi[4] | ((uint32_t)hi[5] << 16), (uint32_t)hi[6] | ((uint32_t)hi[7] << 16));
+  *reinterpret_cast<uint4*>(out_lo + at) =
+      make_uint4((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16),
+                 (uint32_t)lo[4] | ((uint32_t)lo[5] << 16), (uint32_t)lo[6] | ((uint32_t)lo[7] << 16));
 }
 
 template <int HD, int BS>
@@ -814,9 +819,9 @@ static hipError_t launch_hd(const uint16_t* q_hi, const uint16_t* q_lo, int32_t 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int waves = R * md.n_heads;
-  attn_combine_kernel<HD><<<(waves + 3) / 4, 256, 0, st>>>(m, maps, md, ap, R, part_ml, part_o,
-                                                            out_hi, out_lo);
+  const int pairs = R * md.n_heads, per_block = 256 / (HD / 8);
+  attn_combine_kernel<HD><<<(pairs + per_block - 1) / per_block, 256, 0, st>>>(
+      m, maps, md, ap, R, part_ml, part_o, out_hi, out_lo);
   return hipGetLastError();
 }
 

@@ -71,6 +71,20 @@ __device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, size_t 
       make_uint2((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16));
 }
 
+// Split eight consecutive values and store them to the hi and lo planes
+// (16-byte stores: one whole 8-column run of an operand tile per plane).
+__device__ __forceinline__ void store_split8(uint16_t* hi, uint16_t* lo, size_t at, const float* v) {
+  bf16_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) split_bf(v[e], h[e], l[e]);
+  *reinterpret_cast<uint4*>(hi + at) =
+      make_uint4((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16),
+                 (uint32_t)h[4] | ((uint32_t)h[5] << 16), (uint32_t)h[6] | ((uint32_t)h[7] << 16));
+  *reinterpret_cast<uint4*>(lo + at) =
+      make_uint4((uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16),
+                 (uint32_t)l[4] | ((uint32_t)l[5] << 16), (uint32_t)l[6] | ((uint32_t)l[7] << 16));
+}
+
 // 16-byte load that asks the memory system not to keep the line (weights
 // are streamed once per step).
 __device__ __forceinline__ uint4 load_stream16(const uint16_t* p) {

@@ -190,7 +190,7 @@ __device__ void prep_body(const StepMeta& m, const RowMaps& maps, const ModelDim
 // its RMSNorm, split into hi and lo planes (a token outside the vocabulary
 // gives a zero row and ST_BAD_TOKEN). Rows of refused sequences are gathered
 // too: prep runs beside this, and nothing downstream reads them.
-#define EN_MAX_CHUNKS 4  // d_model <= 4 * 4 * PREP_THREADS
+#define EN_MAX_CHUNKS 2  // 8-column chunks per thread: d_model <= 8 * 2 * PREP_THREADS
 
 __device__ void embed_row(int r, const int32_t* __restrict__ tokens,
                           const uint16_t* __restrict__ embed, const uint16_t* __restrict__ gain,
@@ -199,24 +199,32 @@ __device__ void embed_row(int r, const int32_t* __restrict__ tokens,
                           uint32_t* status) {
   __shared__ float red[PREP_WAVES];
   const int t = threadIdx.x;
-  const int nch = d >> 2;
+  const int nch = d >> 3;
   const int tok = tokens[r];
   const bool ok = tok >= 0 && tok < vocab;
   if (!ok && t == 0) raise_status(status, ST_BAD_TOKEN);
   float* xr = x + (size_t)r * d;
-  float4 xv[EN_MAX_CHUNKS];
+  float xv[EN_MAX_CHUNKS][8];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < EN_MAX_CHUNKS; ++c) {
     const int ch = t + c * PREP_THREADS;
-    xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[c][e] = 0.f;
     if (ch < nch) {
       if (ok) {
-        const uint2 e = reinterpret_cast<const uint2*>(embed + (size_t)tok * d)[ch];
-        xv[c] = make_float4(lo_bf(e.x), hi_bf(e.x), lo_bf(e.y), hi_bf(e.y));
+        const uint4 q = reinterpret_cast<const uint4*>(embed + (size_t)tok * d)[ch];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[c][2 * e] = lo_bf(w[e]);
+          xv[c][2 * e + 1] = hi_bf(w[e]);
+        }
       }
-      reinterpret_cast<float4*>(xr)[ch] = xv[c];
-      ss += xv[c].x * xv[c].x + xv[c].y * xv[c].y + xv[c].z * xv[c].z + xv[c].w * xv[c].w;
+      reinterpret_cast<float4*>(xr)[2 * ch] = make_float4(xv[c][0], xv[c][1], xv[c][2], xv[c][3]);
+      reinterpret_cast<float4*>(xr)[2 * ch + 1] = make_float4(xv[c][4], xv[c][5], xv[c][6], xv[c][7]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += xv[c][e] * xv[c][e];
     }
   }
   ss = wave_sum(ss);
@@ -231,10 +239,15 @@ __device__ void embed_row(int r, const int32_t* __restrict__ tokens,
   for (int c = 0; c < EN_MAX_CHUNKS; ++c) {
     const int ch = t + c * PREP_THREADS;
     if (ch < nch) {
-      const uint2 gv = reinterpret_cast<const uint2*>(gain)[ch];
-      store_split4(h_hi, h_lo, tile_at(r, 4 * ch, KB), xv[c].x * inv * lo_bf(gv.x),
-                   xv[c].y * inv * hi_bf(gv.x), xv[c].z * inv * lo_bf(gv.y),
-                   xv[c].w * inv * hi_bf(gv.y));
+      const uint4 q = reinterpret_cast<const uint4*>(gain)[ch];
+      const uint32_t g[4] = {q.x, q.y, q.z, q.w};
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[2 * e] = xv[c][2 * e] * inv * lo_bf(g[e]);
+        y[2 * e + 1] = xv[c][2 * e + 1] * inv * hi_bf(g[e]);
+      }
+      store_split8(h_hi, h_lo, tile_at(r, 8 * ch, KB), y);
     }
   }
 }
@@ -257,7 +270,7 @@ hipError_t launch_prep_embed(const StepMeta& m, const RowMaps& maps, const Model
                              const AttnPlan& ap, const uint16_t* embed, const uint16_t* gain,
                              float* x, uint16_t* h_hi, uint16_t* h_lo, uint32_t* status,
                              hipStream_t st) {
-  if ((md.d_model >> 2) > EN_MAX_CHUNKS * PREP_THREADS) return hipErrorInvalidValue;
+  if ((md.d_model >> 3) > EN_MAX_CHUNKS * PREP_THREADS) return hipErrorInvalidValue;
   prep_embed_kernel<<<1 + m.n_rows, PREP_THREADS, 0, st>>>(m, maps, md, ap, embed, gain, x, h_hi,
                                                             h_lo, status);
   return hipGetLastError();
@@ -265,12 +278,13 @@ hipError_t launch_prep_embed(const StepMeta& m, const RowMaps& maps, const Model
 
 // ---------------------------------------------------------------- RMSNorm
 //
-// One workgroup per row, one float4 chunk of the row per thread (up to
+// One workgroup per row, one 8-column chunk of the row per thread (up to
 // RN_MAX_CHUNKS when the row is wider than the workgroup): the residual sum
-// (the split partials of a chunk are all loaded, then added in split order),
-// then the norm of the new x. Wide workgroups keep many loads in flight,
+// (the split partials of a chunk are loaded four splits at a time and added
+// in split order), then the norm of the new x, stored as one 16-byte run of
+// an operand tile per plane. Wide workgroups keep many loads in flight,
 // since only one workgroup per row works here.
-#define RN_MAX_CHUNKS 4
+#define RN_MAX_CHUNKS 2
 
 __global__ __launch_bounds__(1024) void resid_norm_kernel(
     float* __restrict__ x, const float* __restrict__ part, int S, int R,
@@ -279,48 +293,53 @@ __global__ __launch_bounds__(1024) void resid_norm_kernel(
     uint16_t* __restrict__ h_lo) {
   __shared__ float red[16];
   const int T = blockDim.x, t = threadIdx.x;
-  const int nch = d >> 2;
+  const int nch = d >> 3;
+  const int KB = (d + 31) / 32;
   const int r = blockIdx.x;
   if (r >= R) {  // output o = r - R with no row (refused): zeros, finite downstream
     const int o = r - R;
     if (out_row[o] >= 0) return;
-    const int KB = (d + 31) / 32;
     for (int ch = t; ch < nch; ch += T) {
-      *reinterpret_cast<uint2*>(h_hi + tile_at(o, 4 * ch, KB)) = make_uint2(0, 0);
-      *reinterpret_cast<uint2*>(h_lo + tile_at(o, 4 * ch, KB)) = make_uint2(0, 0);
+      *reinterpret_cast<uint4*>(h_hi + tile_at(o, 8 * ch, KB)) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(h_lo + tile_at(o, 8 * ch, KB)) = make_uint4(0, 0, 0, 0);
     }
     return;
   }
   float* xr = x + (size_t)r * d;
-  const size_t pstride = (size_t)R * d;
-  float4 xv[RN_MAX_CHUNKS];
+  const size_t pstride = (size_t)R * d / 4;  // one split's partials, in float4
+  float4 xa[RN_MAX_CHUNKS], xb[RN_MAX_CHUNKS];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < RN_MAX_CHUNKS; ++c) {
     const int ch = t + c * T;
-    xv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    xa[c] = xb[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (ch < nch) {
-      float4 v = reinterpret_cast<const float4*>(xr)[ch];
+      float4 a = reinterpret_cast<const float4*>(xr)[2 * ch];
+      float4 b = reinterpret_cast<const float4*>(xr)[2 * ch + 1];
       if (S > 1) {
-        const float4* p = reinterpret_cast<const float4*>(part + (size_t)r * d) + ch;
+        const float4* p = reinterpret_cast<const float4*>(part + (size_t)r * d) + 2 * ch;
         for (int k0 = 0; k0 < S; k0 += 4) {
-          float4 q[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (k0 + u < S) q[u] = p[(k0 + u) * (pstride / 4)];
+          float4 qa[4], qb[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u)
             if (k0 + u < S) {
-              v.x += q[u].x;
-              v.y += q[u].y;
-              v.z += q[u].z;
-              v.w += q[u].w;
+              qa[u] = p[(k0 + u) * pstride];
+              qb[u] = p[(k0 + u) * pstride + 1];
+            }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (k0 + u < S) {
+              a.x += qa[u].x; a.y += qa[u].y; a.z += qa[u].z; a.w += qa[u].w;
+              b.x += qb[u].x; b.y += qb[u].y; b.z += qb[u].z; b.w += qb[u].w;
             }
         }
-        reinterpret_cast<float4*>(xr)[ch] = v;
+        reinterpret_cast<float4*>(xr)[2 * ch] = a;
+        reinterpret_cast<float4*>(xr)[2 * ch + 1] = b;
       }
-      xv[c] = v;
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      xa[c] = a;
+      xb[c] = b;
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
+            b.w * b.w;
     }
   }
   const int dst = row_out ? row_out[r] : r;
@@ -331,15 +350,16 @@ __global__ __launch_bounds__(1024) void resid_norm_kernel(
   float tot = 0.f;
   for (int w = 0; w < (T >> 6); ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-  const int KB = (d + 31) / 32;
 #pragma unroll
   for (int c = 0; c < RN_MAX_CHUNKS; ++c) {
     const int ch = t + c * T;
     if (ch < nch) {
-      const uint2 gv = reinterpret_cast<const uint2*>(gain)[ch];
-      store_split4(h_hi, h_lo, tile_at(dst, 4 * ch, KB), xv[c].x * inv * lo_bf(gv.x),
-                   xv[c].y * inv * hi_bf(gv.x), xv[c].z * inv * lo_bf(gv.y),
-                   xv[c].w * inv * hi_bf(gv.y));
+      const uint4 g = reinterpret_cast<const uint4*>(gain)[ch];
+      const float y[8] = {xa[c].x * inv * lo_bf(g.x), xa[c].y * inv * hi_bf(g.x),
+                          xa[c].z * inv * lo_bf(g.y), xa[c].w * inv * hi_bf(g.y),
+                          xb[c].x * inv * lo_bf(g.z), xb[c].y * inv * hi_bf(g.z),
+                          xb[c].z * inv * lo_bf(g.w), xb[c].w * inv * hi_bf(g.w)};
+      store_split8(h_hi, h_lo, tile_at(dst, 8 * ch, KB), y);
     }
   }
 }
@@ -349,7 +369,7 @@ hipError_t launch_resid_norm(float* x, const float* part, int32_t S, int32_t R,
                              const uint16_t* gain, int32_t d, float eps, uint16_t* h_hi,
                              uint16_t* h_lo, hipStream_t st) {
   if (R <= 0) return hipSuccess;
-  const int nch = d / 4;
+  const int nch = d / 8;
   int T = (nch + RN_MAX_CHUNKS - 1) / RN_MAX_CHUNKS;  // threads for at most RN_MAX_CHUNKS each
   T = std::max(T, std::min(nch, 1024));               // and up to one chunk per thread
   T = std::min(1024, (T + 63) / 64 * 64);
