@@ -742,19 +742,40 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
     for (int t = 0; t < qt; ++t) start += tile_steps(t, nn, ctx, rpt);
     n_sp = (start + pos / 32) / ps.len - start / ps.len + 1;
   }
+  // Both passes load four partial results at a time (one round trip per
+  // four instead of one per partial) and use them in key order.
   const size_t base = ((size_t)r * md.n_heads + h) * ap.max_splits;
   float M = -INFINITY;
-  for (int j = 0; j < n_sp; ++j) M = fmaxf(M, part_ml[2 * (base + j)]);
+  for (int j0 = 0; j0 < n_sp; j0 += 4) {
+    float mv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mv[u] = j0 + u < n_sp ? part_ml[2 * (base + j0 + u)] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) M = fmaxf(M, mv[u]);
+  }
   float acc[8], den = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int j = 0; j < n_sp; ++j) {
-    const float wj = exp2f(part_ml[2 * (base + j)] - M);
-    den += wj * part_ml[2 * (base + j) + 1];
-    const float4* op = reinterpret_cast<const float4*>(part_o + (base + j) * HD + 8 * sl);
-    const float4 a = op[0], b = op[1];
-    acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
-    acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+  for (int j0 = 0; j0 < n_sp; j0 += 4) {
+    float2 ml[4];
+    float4 oa[4], ob[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + u < n_sp) {
+        ml[u] = reinterpret_cast<const float2*>(part_ml)[base + j0 + u];
+        const float4* op = reinterpret_cast<const float4*>(part_o + (base + j0 + u) * HD + 8 * sl);
+        oa[u] = op[0];
+        ob[u] = op[1];
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + u < n_sp) {
+        const float wj = exp2f(ml[u].x - M);
+        den += wj * ml[u].y;
+        const float4 a = oa[u], b = ob[u];
+        acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
+        acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+      }
   }
   const float inv = 1.0f / den;
   bf16_t hi[8], lo[8];
