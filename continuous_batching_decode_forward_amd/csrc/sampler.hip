@@ -273,20 +273,43 @@ __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K,
     if (v >= 0.f && u >= lo && u < hi) sh.cand[atomicAdd(&sh.n_cand, 1)] = v;
   }
   __syncthreads();
-  const float cv = (int)threadIdx.x < sh.n_cand ? sh.cand[threadIdx.x] : -1.f;
-  __syncthreads();
-  while (hi - lo > 1u) {
-    const uint32_t mid = lo + (hi - lo) / 2u;
-    const uint32_t u = __float_as_uint(cv);
-    const double c = (cv >= 0.f && u >= mid && u < hi) ? (BY_MASS ? (double)cv : 1.0) : 0.0;
-    const double f = f_hi + smp_block_sum_d(c, sh);
-    if (f >= need) {
-      lo = mid;
-    } else {
-      hi = mid;
-      f_hi = f;
+  // Wave 0 alone finishes the bisection on the (at most SMP_THREADS)
+  // candidates, 16 per lane, with wave reductions only; every lane decides
+  // on lane 0's sum, and the result goes to the other waves through LDS.
+  // (A block reduction per step -- about 20 steps at top-p 0.3 over 65536
+  // ids -- cost two barriers each.)
+  if (threadIdx.x < 64) {
+    constexpr int CPL = SMP_THREADS / 64;
+    const int n = sh.n_cand;
+    float cv[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int j = (int)threadIdx.x + 64 * i;
+      cv[i] = j < n ? sh.cand[j] : -1.f;
     }
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      double c = 0.0;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const uint32_t u = __float_as_uint(cv[i]);
+        if (cv[i] >= 0.f && u >= mid && u < hi) c += BY_MASS ? (double)cv[i] : 1.0;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+      const double f = f_hi + __shfl(c, 0, 64);
+      if (f >= need) {
+        lo = mid;
+      } else {
+        hi = mid;
+        f_hi = f;
+      }
+    }
+    if (threadIdx.x == 0) sh.red_i[0] = (int)lo;  // patterns of non-negative floats: < 2^31
   }
+  __syncthreads();
+  lo = (uint32_t)sh.red_i[0];
+  __syncthreads();  // red_i is reused by the next reduction
   return lo;
 }
 
