@@ -169,6 +169,13 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
   _Pragma("unroll") for (int k = 0; k < (REGS ? SMP_KREG : K); ++k) \
     if (!REGS || k < K)
 
+// The same over groups of SMP_LB values (k0 = 0, SMP_LB, ...): the body
+// handles k0 .. k0 + SMP_LB - 1 and checks k < K itself.
+#define SMP_LB 8
+#define SMP_FOR_KB(k0)                                                              \
+  _Pragma("unroll") for (int k0 = 0; k0 < (REGS ? SMP_KREG : K); k0 += SMP_LB) \
+    if (!REGS || k0 < K)
+
 template <bool REGS>
 struct RowVals {
   float r[REGS ? SMP_KR : 1];
@@ -356,19 +363,35 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
   RowVals<REGS> e;
   e.g = scratch_row;  // REGS: the caller passes its LDS slice base + threadIdx.x
 
-  // S1 penalties (+ S2 division)
+  // S1 penalties (+ S2 division). The two row reads go out SMP_LB ids at a
+  // time: with the scheduling barrier of every id they waited one memory
+  // round trip per id.
   float zmax = -INFINITY;
-  SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
-    const int id = base + 64 * k;
-    float z = -INFINITY;
-    if (id < V) {
-      const float c = crow[id];
-      float l = lrow[id] - mul_rounded(P.freq_penalty, c);
-      if (c > 0.f) l = l - P.presence_penalty;
-      z = P.temperature == 0.f ? l : l / P.temperature;
+  SMP_FOR_KB(k0) { __builtin_amdgcn_sched_barrier(0);
+    float cv[SMP_LB], lv[SMP_LB];
+#pragma unroll
+    for (int u = 0; u < SMP_LB; ++u) {
+      const int id = base + 64 * (k0 + u);
+      const bool ok = k0 + u < K && id < V;
+      cv[u] = ok ? crow[id] : 0.f;
+      lv[u] = ok ? lrow[id] : 0.f;
     }
-    e.set(k, id, z);
-    zmax = fmaxf(zmax, z);
+#pragma unroll
+    for (int u = 0; u < SMP_LB; ++u) {
+      const int k = k0 + u;
+      if (k < K) {
+        const int id = base + 64 * k;
+        float z = -INFINITY;
+        if (id < V) {
+          const float c = cv[u];
+          float l = lv[u] - mul_rounded(P.freq_penalty, c);
+          if (c > 0.f) l = l - P.presence_penalty;
+          z = P.temperature == 0.f ? l : l / P.temperature;
+        }
+        e.set(k, id, z);
+        zmax = fmaxf(zmax, z);
+      }
+    }
   }
   zmax = smp_block_max(zmax, sh);
   int token;
@@ -462,13 +485,23 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
     if (token == 0x7fffffff) token = smp_block_max_i(last, sh);
     if (token < 0) token = 0;
   }
-  // S7 counts: decay every id, then count the token
-  SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
-    const int id = base + 64 * k;
-    if (id < V) {
-      float c = mul_rounded(crow[id], P.penalty_decay);
-      if (id == token) c = c + 1.0f;
-      crow[id] = c;
+  // S7 counts: decay every id, then count the token (reads SMP_LB ids at a
+  // time, as in S1)
+  SMP_FOR_KB(k0) { __builtin_amdgcn_sched_barrier(0);
+    float cv[SMP_LB];
+#pragma unroll
+    for (int u = 0; u < SMP_LB; ++u) {
+      const int id = base + 64 * (k0 + u);
+      cv[u] = k0 + u < K && id < V ? crow[id] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < SMP_LB; ++u) {
+      const int id = base + 64 * (k0 + u);
+      if (k0 + u < K && id < V) {
+        float c = mul_rounded(cv[u], P.penalty_decay);
+        if (id == token) c = c + 1.0f;
+        crow[id] = c;
+      }
     }
   }
   if (threadIdx.x == 0) *token_out = token;
