@@ -3,7 +3,9 @@
     python -m continuous_batching_decode_forward_amd.build [--force]
 
 Every source in csrc/ is compiled with hipcc for gfx950 only; the shared
-library lands next to this file, in-tree.
+library lands next to this file, in-tree. csrc/check/ holds a host-only
+replay of the attention schedule (the kernels' own schedule arithmetic from
+csrc/attn_sched.h), built into libcbd_schedcheck.so for the tests.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcbd.so")
+CHECK_LIB = os.path.join(HERE, "libcbd_schedcheck.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.environ.get("HIPCC", os.path.join(ROCM, "bin", "hipcc"))
@@ -45,12 +48,30 @@ def _compile(src: str) -> str:
     return obj
 
 
+def check_sources():
+    return sorted(glob.glob(os.path.join(CSRC, "check", "*.cpp")))
+
+
 def _stale() -> bool:
-    if not os.path.exists(LIB):
-        return True
-    t = os.path.getmtime(LIB)
-    deps = sources() + glob.glob(os.path.join(CSRC, "*.h")) + [os.path.join(INCLUDE, "cbd.h")]
-    return any(os.path.getmtime(p) > t for p in deps)
+    deps = sources() + check_sources() + glob.glob(os.path.join(CSRC, "*.h")) + \
+        [os.path.join(INCLUDE, "cbd.h")]
+    for lib in (LIB, CHECK_LIB):
+        if not os.path.exists(lib):
+            return True
+        t = os.path.getmtime(lib)
+        if any(os.path.getmtime(p) > t for p in deps):
+            return True
+    return False
+
+
+def _build_check() -> None:
+    tmp = CHECK_LIB + ".tmp"
+    cmd = [HIPCC] + COMMON + ["-x", "c++", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include",
+                              "-shared", "-o", tmp] + check_sources()
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"schedule checker build failed:\n{r.stderr}")
+    os.replace(tmp, CHECK_LIB)
 
 
 def build(force: bool = False, jobs: int = 8) -> str:
@@ -65,6 +86,7 @@ def build(force: bool = False, jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    _build_check()
     return LIB
 
 

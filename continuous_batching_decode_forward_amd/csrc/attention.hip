@@ -25,25 +25,13 @@
 // online in base 2 (scores pre-scaled by log2(e)/sqrt(hd)); P enters the PV
 // MFMA as three bf16 terms that sum to its fp32 value, and the running sums
 // use fp32 P.
+#include "attn_sched.h"
 #include "common.h"
 #include "kernels.h"
 
 namespace cbd {
 
 #define ATT_LDS_SEQS 1024  // item0 staged in LDS for up to this many sequences
-
-// Largest s with item0[s] <= item (item0 ascending, item0[0] = 0).
-__device__ __forceinline__ int find_seq(const int32_t* item0, int n, int item) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (item0[mid] <= item)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
 
 // A value the whole wave shares, moved to a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -55,22 +43,6 @@ struct KVTile {
   uint4 k[2][HD / 32];
   uint4 v[HD / 16];
 };
-
-// The per-tile schedule. The key steps (32 keys) of every (sequence, query
-// tile) on this kernel are laid end to end in sequence order, the same for
-// each KV head: T steps per head, sequence s starting at step item0[s]. Each
-// head's T steps are cut into pieces of `len` steps, and piece q of head g
-// is run by wave g * per_head + q (mod the P launched waves, which take at
-// most `rounds` pieces each). A piece may cross (sequence, tile) boundaries;
-// each run of it inside one (sequence, tile) is a segment with its own
-// partial result, stored at split index "piece - first piece of that
-// (sequence, tile)". Equal pieces give every wave the same number of K/V
-// bytes, whatever the mix of context lengths.
-struct PieceSched {
-  int len, per_head;
-};
-
-__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Issue priority from a wave's progress: 3 in the first quarter of its key
 // steps, down to 0 in the last. Two waves share each SIMD, and at equal
@@ -89,22 +61,6 @@ __device__ __forceinline__ void progress_prio(int done, int total) {
     __builtin_amdgcn_s_setprio(1);
   else
     __builtin_amdgcn_s_setprio(0);
-}
-
-// The fewest rounds of P waves whose pieces fit in `hi` steps, then the
-// shortest pieces (not below `lo`) that cover T in that many rounds.
-__device__ __forceinline__ PieceSched piece_sched(int T, const AttnPlan& ap, int kvh) {
-  const int wh = max(1, ap.grid_items / kvh);  // waves per KV head
-  int rounds = max(1, ceil_div(ceil_div(max(T, 1), wh), ap.piece_hi));
-  while (ceil_div(T, rounds * wh) > ap.piece_hi) ++rounds;
-  const int len = min(ap.piece_hi, max(ap.piece_lo, ceil_div(T, rounds * wh)));
-  return PieceSched{len, ceil_div(T, len)};
-}
-
-// Key steps of query tile qt of a sequence (its keys are positions
-// 0 .. ctx + its last row).
-__device__ __forceinline__ int tile_steps(int qt, int nn, int ctx, int rpt) {
-  return ceil_div(ctx + min(nn, (qt + 1) * rpt), 32);
 }
 
 // The loads are unconditional and branch-free: a key past the item's range
@@ -399,25 +355,16 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
       const int s = uniform(find_seq(step0, n_seqs, b));
       const int nn = uniform(m.n_new[s]), ctx = uniform(m.ctx_lens[s]);
       const int s0 = uniform(step0[s]);
-      const int off = b - s0;
-      int qt = 0, qstart = 0, st = tile_steps(0, nn, ctx, rpt);
-      while (off >= qstart + st) {
-        qstart += st;
-        st = tile_steps(++qt, nn, ctx, rpt);
-      }
-      const int rel = off - qstart;
-      const int seg = min(st - rel, b_end - b);
-      const int keys = ctx + min(nn, (qt + 1) * rpt);
-      const int sp = q - (s0 + qstart) / ps.len;
-      if (sp >= ap.max_splits) {  // the host's piece_lo rules this out
+      const Segment sg = piece_segment(b, b_end, s0, nn, ctx, q, ps.len, rpt);
+      if (sg.sp >= ap.max_splits) {  // the host's piece_lo rules this out
         if ((threadIdx.x & 63) == 0) raise_status(status, ST_BAD_SHAPE);
       } else {
         attend_segment<HD, BS>(q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o,
-                               status, s_tbl[wave], s, g, qt, nn, ctx, 32 * rel,
-                               min(keys, 32 * (rel + seg)), sp, done, total);
+                               status, s_tbl[wave], s, g, sg.qt, nn, ctx, sg.k_lo, sg.k_hi, sg.sp,
+                               done, total);
       }
-      b += seg;
-      done += seg;
+      b += sg.steps;
+      done += sg.steps;
     }
   }
 }
@@ -469,19 +416,10 @@ __global__ __launch_bounds__(64 * ATB_WAVES) void attention_block_kernel(
   const int s = uniform(find_seq(maps.item0b, n_seqs, item));
   const int G = md.n_heads / md.n_kv_heads;
   const int rpt = 16 / G;               // rows per 16-column tile
-  const int rpb = ATB_COLS / G;         // rows per item
   const int nn = uniform(m.n_new[s]), ctx = uniform(m.ctx_lens[s]);
-  const int qblocks = (nn + rpb - 1) / rpb;
-  const int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
-  int local = item - uniform(maps.item0b[s]);
-  const int qb = local % qblocks;
-  local /= qblocks;
-  const int sp = local % splits;
-  const int g = local / splits;
-  const int row_lo = qb * rpb;
-  const int last_row = min(nn, row_lo + rpb) - 1;
-  const int k_lo = sp * ap.split_len;
-  const int k_hi = min(k_lo + ap.split_len, ctx + last_row + 1);
+  const BlockItem bi = block_item(item - uniform(maps.item0b[s]), nn, ctx, ap);
+  const int g = bi.g, sp = bi.sp, row_lo = bi.row_lo, last_row = bi.last_row;
+  const int k_lo = bi.k_lo, k_hi = bi.k_hi;
   if (k_lo >= k_hi) return;  // no keys of this split for these rows: the whole workgroup
 
   // The item's block-table slice.
@@ -731,16 +669,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
   const int pos = maps.row_pos[r];
   const int nn = m.n_new[s];
   int n_sp;  // partial results holding keys 0..pos
-  if (ap.block_rows > 0 && nn >= ap.block_min) {  // block kernel: splits of split_len keys
-    n_sp = pos / ap.split_len + 1;
+  if (attn_on_block_kernel(nn, ap)) {  // block kernel: splits of split_len keys
+    n_sp = block_partials(pos, ap);
   } else {  // per-tile kernel: the pieces over this row's (sequence, tile) steps
     const PieceSched ps = piece_sched(maps.item0[m.n_seqs], ap, md.n_kv_heads);
     const int rpt = 16 / (md.n_heads / md.n_kv_heads);
     const int qt = (r - maps.seq_row0[s]) / rpt;
-    const int ctx = m.ctx_lens[s];
-    int start = maps.item0[s];
-    for (int t = 0; t < qt; ++t) start += tile_steps(t, nn, ctx, rpt);
-    n_sp = (start + pos / 32) / ps.len - start / ps.len + 1;
+    n_sp = piece_partials(tile_start(maps.item0[s], qt, nn, m.ctx_lens[s], rpt), pos, ps.len);
   }
   // Both passes load four partial results at a time (one round trip per
   // four instead of one per partial) and use them in key order.

@@ -185,10 +185,17 @@ int cbd_sched_create(const cbd_sched_config* cfg, cbd_engine* engine, const int3
       cfg->max_blocks_per_seq < 1 || cfg->max_rows < 1 || cfg->chunk_size < 1 ||
       cfg->policy < CBD_ADMIT_RESERVE || cfg->policy > CBD_ADMIT_REQUEST_LEVEL)
     return fail(CBD_E_INVAL, "composer config out of range");
+  // With an engine, every plan the composer can make must be a step the
+  // engine accepts: its sequences (at most max_slots) fit max_seqs, and a
+  // sequence's positions (at most max_blocks_per_seq blocks) fit the RoPE
+  // table, so the loop cannot fail in the middle of a run.
   if (engine && (engine->cfg.block_size != cfg->block_size ||
                  engine->cfg.num_blocks != cfg->num_blocks ||
                  engine->cfg.max_slots < cfg->max_slots ||
+                 engine->cfg.max_seqs < cfg->max_slots ||
                  engine->cfg.max_blocks_per_seq < cfg->max_blocks_per_seq ||
+                 (int64_t)engine->cfg.max_position <
+                     (int64_t)cfg->max_blocks_per_seq * cfg->block_size ||
                  engine->cfg.max_rows < cfg->max_rows))
     return fail(CBD_E_INVAL, "composer config does not match the engine");
   std::unique_ptr<cbd_sched> s(new cbd_sched());
@@ -397,7 +404,13 @@ int cbd_sched_step(cbd_sched* s, int32_t mode, int32_t* meta_dev, int32_t* host_
   hipError_t he = hipMemcpyAsync(meta_dev, host_stage, o * sizeof(int32_t), hipMemcpyHostToDevice, hs);
   if (he != hipSuccess) return fail(CBD_E_DEVICE, std::string("step metadata upload: ") + hipGetErrorString(he));
   rc = cbd_step_forward(s->engine, &st, logits_out, tokens_dev, stream);
-  if (rc != CBD_OK) return rc;
+  if (rc != CBD_OK) {
+    // The upload may still be reading host_stage: drain the stream before
+    // handing the buffer back (the error message of the step is kept).
+    const std::string msg = cbd_last_error();
+    (void)hipStreamSynchronize(hs);
+    return fail(rc, msg);
+  }
   if (p.n_out > 0) {
     he = hipMemcpyAsync(host_stage, tokens_dev, (size_t)p.n_out * sizeof(int32_t),
                         hipMemcpyDeviceToHost, hs);

@@ -9,24 +9,12 @@
 #include <utility>
 #include <vector>
 
+#include "attn_sched.h"
 #include "runtime.h"
 
 namespace cbd {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Key splits per (row, head) the partial buffers hold.
-// Partial-result slots per (row, head): one per 128 positions (at most 64),
-// plus one for a piece of the per-tile schedule that starts inside the range.
-static int32_t attn_cap_splits(const cbd_config& c) {
-  int32_t s = (c.max_position + 127) / 128;
-  return std::max(1, std::min(64, s)) + 1;
-}
-
-// Longest key split: a split spans at most ATT_TBL blocks.
-static int32_t attn_split_cap(const cbd_config& c) {
-  return (ATT_TBL - 1) * c.block_size / 32 * 32;
-}
 
 int validate_config(const cbd_config* c) {
   if (!c) return fail(CBD_E_INVAL, "config is NULL");
@@ -49,7 +37,8 @@ int validate_config(const cbd_config* c) {
     return fail(CBD_E_UNSUPPORTED, "d_model, ffn_dim and vocab must be multiples of 16");
   if (c->d_model > 8192) return fail(CBD_E_UNSUPPORTED, "d_model above 8192");
   if (c->max_seqs > c->max_rows) return fail(CBD_E_INVAL, "max_seqs exceeds max_rows");
-  if ((long long)(attn_cap_splits(*c) - 1) * attn_split_cap(*c) < c->max_position)
+  if ((long long)(attn_cap_splits(c->max_position) - 1) * attn_split_cap(c->block_size) <
+      c->max_position)
     return fail(CBD_E_UNSUPPORTED, "max_position too long for this block size");
   return CBD_OK;
 }
@@ -92,7 +81,7 @@ WorkspaceLayout workspace_layout(const cbd_config& c) {
   size_t maxn = std::max({(size_t)2 * c.ffn_dim, qkv_n, d});
   L.gemm_part_floats = std::max<size_t>((size_t)16 << 20, 4 * R * maxn);
   L.gemm_part = take(L.gemm_part_floats * 4);
-  L.attn_max_splits = attn_cap_splits(c);
+  L.attn_max_splits = attn_cap_splits(c.max_position);
   const size_t cols = R * (size_t)c.n_heads * (size_t)L.attn_max_splits;
   L.attn_ml = take(cols * 2 * 4);
   L.attn_o = take(cols * hd * 4);
@@ -388,49 +377,6 @@ int cbd_engine_status(cbd_engine* e, void* stream, uint32_t* flags) {
 
 // ---------------------------------------------------------------- the step
 
-static AttnPlan plan_attention(const cbd_engine* e, const cbd_step* s) {
-  const cbd_config& c = e->cfg;
-  AttnPlan ap;
-  ap.max_splits = e->ws.attn_max_splits;
-  ap.max_ctx = s->max_ctx;
-  // Block kernel (prefill chunks): keys split into split_len pieces, enough
-  // items to fill the chip (about 4096) without slivers shorter than 64
-  // keys; never more splits than the partial buffers hold.
-  long long want = (long long)s->max_ctx * s->n_seqs * c.n_kv_heads / 4096;
-  int32_t len = (int32_t)std::max<long long>(64, std::min<long long>(4096, want));
-  len = (len + 31) / 32 * 32;
-  int32_t floor_len = (s->max_ctx + ap.max_splits - 1) / ap.max_splits;
-  floor_len = (floor_len + 31) / 32 * 32;
-  ap.split_len = std::max(std::min(len, attn_split_cap(c)), floor_len);
-  const int G = c.n_heads / c.n_kv_heads;
-  const long long qt = ((long long)s->n_rows * G + 15) / 16 + s->n_seqs;
-  const long long sp = (s->max_ctx + ap.split_len - 1) / ap.split_len;
-  // Per-tile kernel: equal pieces of each KV head's key steps (a piece at
-  // least 4 steps, and long enough that the pieces over one (sequence, tile)
-  // fit the partial slots; at most what a block-table slice in LDS covers),
-  // run by the chip's resident waves, or fewer when the step has few keys.
-  const int32_t steps_max = (s->max_ctx + 31) / 32;
-  ap.piece_hi = attn_split_cap(c) / 32;
-  ap.piece_lo = std::max<int32_t>(4, (steps_max + ap.max_splits - 2) / (ap.max_splits - 1));
-  const long long unit = (long long)c.n_kv_heads * ATT_WAVES;
-  const long long p_max = std::max<long long>(1, e->attn_waves / unit) * unit;
-  const long long p_want = c.n_kv_heads * ((qt * steps_max + ap.piece_lo - 1) / ap.piece_lo);
-  ap.grid_items = (int32_t)std::min(p_max, (p_want + unit - 1) / unit * unit);
-  // Prefill chunks of 32+ rows run on the block kernel (block sizes that
-  // are multiples of 32). Every sequence has at least one row, so a step
-  // with fewer than block_min + n_seqs - 1 rows has no such chunk: it
-  // launches no block kernel and every sequence runs on the per-tile kernel.
-  ap.block_min = 32;
-  ap.block_rows = c.block_size % 32 == 0 ? ATT_BLOCK_COLS / G : 0;
-  if ((long long)s->n_rows - s->n_seqs + 1 < ap.block_min) ap.block_rows = 0;
-  ap.grid_items_b = 0;
-  if (ap.block_rows > 0) {
-    const long long qb = s->n_rows / ap.block_rows + s->n_seqs;
-    ap.grid_items_b = (int32_t)std::min<long long>(qb * sp * c.n_kv_heads, 1LL << 30);
-  }
-  return ap;
-}
-
 int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_t* tokens_out,
                      void* stream) {
   if (!e || !s) return fail(CBD_E_INVAL, "NULL engine or step");
@@ -458,7 +404,8 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
                e->wsp<int32_t>(e->ws.seq_row0), e->wsp<int32_t>(e->ws.out_row),
                e->wsp<int32_t>(e->ws.out_seq), e->wsp<int32_t>(e->ws.item0),
                e->wsp<int32_t>(e->ws.row_out), e->wsp<int32_t>(e->ws.item0b)};
-  const AttnPlan ap = plan_attention(e, s);
+  const AttnPlan ap = plan_attention(c.n_heads, c.n_kv_heads, c.block_size, c.max_position,
+                                     e->attn_waves, s->n_seqs, s->n_rows, s->max_ctx);
   const int qkv_n = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   const int qd = c.n_heads * c.head_dim;
   const size_t MR = (size_t)c.max_rows;

@@ -2,6 +2,7 @@
 // RMSNorm, RoPE + KV append, argmax combine, fills.
 #include <algorithm>
 
+#include "attn_sched.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -88,25 +89,13 @@ __device__ void prep_body(const StepMeta& m, const RowMaps& maps, const ModelDim
   if (t == 0) q_cnt = 0;  // ordered before any use by the scan's barrier
 
   // A sequence is served when its counts fit the cache, the key splits, the
-  // positions and its slot; its attention goes to the block kernel when it
-  // has block_min rows or more and the plan has block items.
+  // positions and its slot; its attention goes to the block kernel (block
+  // items) or the per-tile kernel (key steps of its query tiles).
   auto valid = [&](int s, int nn, int ctx) {
-    const int slot = m.slots[s];
-    return nn >= 1 && ctx >= 0 && ctx + nn <= cap && ctx + nn <= ap.max_splits * ap.split_len &&
-           ctx + nn <= md.max_position && ctx + nn <= ap.max_ctx && slot >= 0 &&
-           slot < md.max_slots;
+    return attn_seq_valid(nn, ctx, m.slots[s], cap, ap, md.max_position, md.max_slots);
   };
-  // Block kernel: (row block, split, KV head) items. Per-tile kernel: the
-  // key steps of the sequence's query tiles (per KV head), tile qt holding
-  // keys 0 .. ctx + its last row.
   auto add_items = [&](int nn, int ctx, int& steps, int& items_b) {
-    if (ap.block_rows > 0 && nn >= ap.block_min) {
-      const int splits = (ctx + nn + ap.split_len - 1) / ap.split_len;
-      items_b += md.n_kv_heads * ((nn + ap.block_rows - 1) / ap.block_rows) * splits;
-    } else {
-      const int rpt = 16 / G, qtiles = (nn * G + 15) / 16;
-      for (int qt = 0; qt < qtiles; ++qt) steps += (ctx + min(nn, (qt + 1) * rpt) + 31) / 32;
-    }
+    attn_seq_work(nn, ctx, G, md.n_kv_heads, ap, &steps, &items_b);
   };
 
   int4 cnt = make_int4(0, 0, 0, 0);  // rows, key steps, block items, outputs

@@ -148,8 +148,9 @@ typedef struct cbd_engine cbd_engine;
  * permutation of 0..num_blocks-1 (NULL: ascending). stream: where the
  * engine's own set-up work and slot resets are enqueued. Returns
  * CBD_E_UNSUPPORTED for shapes the kernels do not handle (head_dim not in
- * {64, 128}, n_heads/n_kv_heads not dividing 16, d_model or ffn_dim not a
- * multiple of 64, ...). */
+ * {64, 128}, n_heads/n_kv_heads not dividing 16, block_size not in {4, 8,
+ * 16, 32, 64}, d_model, ffn_dim or vocab not a multiple of 16, d_model above
+ * 8192, max_position beyond the key splits of that block size). */
 int cbd_engine_create(const cbd_config* cfg, const cbd_weights* weights, void* packed_weights,
                       void* kv_pool, void* slot_state, void* workspace,
                       const int32_t* block_order, void* stream, cbd_engine** out);
@@ -166,10 +167,20 @@ int cbd_slot_alloc(cbd_engine* e, const cbd_sampling* params, uint64_t request_i
                    int32_t* slot_out);
 int cbd_slot_free(cbd_engine* e, int32_t slot);
 
-/* Blocks. cbd_block_alloc is all-or-nothing: it pops n ids from the front
- * of the FIFO free list into ids_out (host) or returns CBD_E_NOBLOCKS and
- * takes none. cbd_block_free appends ids (host) to the back, in order;
- * freeing an id that is not allocated is CBD_E_INVAL. */
+/* Blocks: the paged KV pool's fixed-size blocks, handed out by id (Go under
+ * the hood section 20.3.2: PagedAttention stores the KV cache in fixed-size
+ * blocks allocated as sequences grow, and Forma's scheduler takes a
+ * request's blocks from one shared pool at admission, waiting -- never
+ * evicting -- when the pool is short).
+ * cbd_block_alloc (n >= 0, ids_out: host int32[n]) is all-or-nothing: it
+ * pops n ids from the front of the FIFO free list into ids_out, or returns
+ * CBD_E_NOBLOCKS and takes none (the caller waits for blocks to be freed).
+ * cbd_block_free (ids: host int32[n]) appends the ids to the back of the
+ * list, in the given order; if any id is out of range or not allocated
+ * (a double free) it returns CBD_E_INVAL and frees none.
+ * cbd_blocks_available returns the number of free blocks (or CBD_E_INVAL
+ * for a NULL engine). The free list starts as the engine's block_order.
+ * The ids index the pool for every layer. Host-only; nothing is enqueued. */
 int cbd_block_alloc(cbd_engine* e, int32_t n, int32_t* ids_out);
 int cbd_block_free(cbd_engine* e, int32_t n, const int32_t* ids);
 int cbd_blocks_available(const cbd_engine* e);
@@ -193,7 +204,8 @@ typedef struct cbd_step {
   int32_t max_ctx;            /* host upper bound of ctx_lens[s] + n_new[s] */
   int32_t max_blocks_per_seq; /* row stride of block_tables */
   int32_t mode;               /* CBD_MODE_GREEDY or CBD_MODE_SAMPLE */
-  const int32_t* slots;        /* [n_seqs] sampler slot of each sequence */
+  const int32_t* slots;        /* [n_seqs] sampler slot of each sequence
+                                  (distinct within a sampled step) */
   const int32_t* block_tables; /* [n_seqs][max_blocks_per_seq] block ids */
   const int32_t* ctx_lens;     /* [n_seqs] */
   const int32_t* n_new;        /* [n_seqs] */
@@ -214,7 +226,9 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* step, float* logits_out,
 
 /* The batched sampler alone, over caller-given fp32 logits [n][vocab]
  * (device): row j uses slot slots[j] and draw counter step_ids[j] (device
- * arrays). Updates the slots' penalty counts like a sampled step. */
+ * arrays). Updates the slots' penalty counts like a sampled step. The slots
+ * of one call must be distinct (each row rewrites its slot's counts; rows
+ * sharing a slot race). */
 int cbd_sample_logits(cbd_engine* e, const float* logits, int32_t n, const int32_t* slots,
                       const int32_t* step_ids, int32_t* tokens_out, void* stream);
 
@@ -326,7 +340,12 @@ typedef struct cbd_sched cbd_sched;
 /* engine (nullable): when given, slots and blocks come from the engine's
  * allocators (slot allocation resets the slot's sampler state on the
  * device), and block_order is ignored; when NULL the composer keeps its own
- * host-only allocators seeded by block_order (nullable, ascending). */
+ * host-only allocators seeded by block_order (nullable, ascending).
+ * With an engine the configs must agree: the same block_size and
+ * num_blocks, and max_slots, max_rows and max_blocks_per_seq no larger than
+ * the engine's (max_slots also within its max_seqs, and
+ * max_blocks_per_seq * block_size within its max_position); otherwise
+ * CBD_E_INVAL. */
 int cbd_sched_create(const cbd_sched_config* cfg, cbd_engine* engine,
                      const int32_t* block_order, cbd_sched** out);
 int cbd_sched_destroy(cbd_sched* s);
@@ -369,8 +388,9 @@ int cbd_sched_stats_get(const cbd_sched* s, cbd_sched_stats* out);
  * stalled under CBD_ADMIT_FREE_SLOT: see plan_out->stalled) runs nothing and
  * commits an empty step. All buffers are the caller's. Blocks until the
  * step's tokens are on the host. Errors: CBD_E_INVAL (NULL argument, no
- * engine, bad mode), CBD_E_DEVICE; after an error inside the step the plan
- * stays uncommitted and the composer should be destroyed. */
+ * engine, bad mode), CBD_E_DEVICE; after an error inside the step the
+ * stream has been drained (host_stage is free again), the plan stays
+ * uncommitted and the composer should be destroyed. */
 int cbd_sched_meta_ints(const cbd_sched_config* cfg, size_t* ints_out);
 int cbd_sched_step(cbd_sched* s, int32_t mode, int32_t* meta_dev, int32_t* host_stage,
                    int32_t* tokens_dev, float* logits_out, void* stream, cbd_plan* plan_out);

@@ -7,6 +7,8 @@ import torch
 
 import oracle as O
 from continuous_batching_decode_forward_amd import synth
+from continuous_batching_decode_forward_amd.binding import CBD_BUF_ATTN as B_CBD_BUF_ATTN
+from continuous_batching_decode_forward_amd.binding import CBD_BUF_Q as B_CBD_BUF_Q
 from continuous_batching_decode_forward_amd.engine import Engine
 
 # Logit tolerance (elementwise allclose form): |gpu - oracle| <= ATOL + RTOL*|oracle|.
@@ -96,3 +98,67 @@ def resolvable_rows(ref: np.ndarray, row_err: np.ndarray):
     top2 = np.sort(ref, axis=-1)[:, -2:]
     gap = top2[:, 1] - top2[:, 0]
     return gap > 2.0 * np.maximum(row_err, 1e-6)
+
+
+def stage_error(gpu: np.ndarray, ref: np.ndarray, slack=None) -> float:
+    """max_i (|gpu_i - ref_i| - slack_i) / (|ref_i| + rms(ref)): relative for
+    large elements, relative to the vector's scale for small ones."""
+    g = np.asarray(gpu, np.float64).reshape(-1)
+    o = np.asarray(ref, np.float64).reshape(-1)
+    rms = float(np.sqrt(np.mean(o * o))) or 1.0
+    d = np.abs(g - o)
+    if slack is not None:
+        d = np.maximum(d - slack.reshape(-1), 0.0)
+    return float((d / (np.abs(o) + rms)).max())
+
+
+def gather_kv(eng: Engine, layer: int, table, n_pos: int):
+    """One sequence's first n_pos cached K and V positions of a layer, read
+    from the engine's pool through its block table: two uint16 arrays
+    [n_pos][Hkv][hd] (bf16 bits)."""
+    s = eng.shape
+    bs = eng.block_size
+    nb = -(-n_pos // bs)
+    k, v = eng.kv_views(layer)
+    blocks = torch.as_tensor(np.asarray(table[:nb], np.int64), device=k.device)
+    # K [blocks][Hkv][bs][hd] and V [blocks][Hkv][hd][bs] -> [positions][Hkv][hd]
+    kk = k[blocks].permute(0, 2, 1, 3).reshape(nb * bs, s.n_kv_heads, s.head_dim)[:n_pos]
+    vv = v[blocks].permute(0, 3, 1, 2).reshape(nb * bs, s.n_kv_heads, s.head_dim)[:n_pos]
+    return O.as_u16(kk.contiguous().cpu()), O.as_u16(vv.contiguous().cpu())
+
+
+def attention_rows_vs_oracle(eng: Engine, tables, ctx, n_new, threads: int = 16):
+    """Every row's attention output after a step (the last layer's, as the
+    engine keeps it) against the oracle's dense attention over the same
+    inputs: the row's rotated query as the device computed it and the K/V
+    the device's pool holds for positions 0..pos (the cached prefix plus
+    what the step appended), so the comparison isolates the attention
+    kernels, the key schedule and the combine. Returns the per-row error
+    measure (stage_error) as an array in row order."""
+    from concurrent.futures import ThreadPoolExecutor
+    s = eng.shape
+    hq, hkv, hd = s.n_heads, s.n_kv_heads, s.head_dim
+    R = int(sum(n_new))
+    q = eng.debug_buffer(B_CBD_BUF_Q, R, hq * hd)
+    att = eng.debug_buffer(B_CBD_BUF_ATTN, R, hq * hd)
+    layer = s.n_layers - 1
+    err = np.full(R, np.inf)
+
+    def one(r, pos, K, V):
+        ref = O.attention_dense(q[r], K[:pos + 1], V[:pos + 1], hq, hkv, hd)
+        err[r] = stage_error(att[r], ref)
+
+    pending = []
+    r0 = 0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for i, (c, n) in enumerate(zip(ctx, n_new)):
+            c, n = int(c), int(n)
+            K, V = gather_kv(eng, layer, tables[i], c + n)
+            for j in range(n):
+                pending.append(ex.submit(one, r0 + j, c + j, K, V))
+            r0 += n
+            while len(pending) > 2 * threads:  # bound the K/V copies held on the host
+                pending.pop(0).result()
+        for f in pending:
+            f.result()
+    return err

@@ -3,8 +3,11 @@ heads, head_dim 128, FFN 14336, vocab 128256): one greedy decode step over
 B rows whose contexts (512..4096) are synthetic N(0,1) KV in 32-position
 blocks reached through shuffled block tables. The full step runs at full
 size on the GPU in the benchmark's launch configuration; the oracle checks a
-sample of rows one by one (on a compact copy of their blocks -- paging is
-addressing only, which the oracle's own tests pin)."""
+sample of rows' logits one by one (on a compact copy of their blocks --
+paging is addressing only, which the oracle's own tests pin), and every
+row's attention output against its dense attention over the same query and
+K/V (the attention schedule cuts pieces across sequence and tile
+boundaries, so every row is checked, not a sample)."""
 import numpy as np
 import pytest
 import torch
@@ -12,7 +15,14 @@ import torch
 import oracle as O
 from continuous_batching_decode_forward_amd import configs, synth
 
-from gpu_util import (compare_logits, fill_pool, make_engine, oracle_pool, resolvable_rows)
+from gpu_util import (attention_rows_vs_oracle, compare_logits, fill_pool, make_engine,
+                      oracle_pool, resolvable_rows)
+
+# Attention output against the oracle's dense attention on identical inputs:
+# fp32 online softmax and accumulation over at most 4097 keys; 2^-12 is 16
+# times below a bf16 ulp, while a key step left out or counted twice moves a
+# row's output by more than 2^-7 of its scale.
+ATTN_TOL = 2.0 ** -12
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +63,7 @@ def decode_step(big, B, seed, sample_rows, lo=512, hi=4096, ctx=None):
     torch.cuda.synchronize()
     assert eng.status() == 0
     g_lg, g_tk = lg.cpu().numpy(), tk.cpu().numpy()
+    att_err = attention_rows_vs_oracle(eng, tables, ctx, [1] * B)
     eng.close()
     rows = list(sample_rows)
     pool, compact = oracle_pool(SHAPE, seed, [tables[i] for i in rows], [int(ctx[i]) for i in rows],
@@ -62,7 +73,7 @@ def decode_step(big, B, seed, sample_rows, lo=512, hi=4096, ctx=None):
     ok, mx, row_err = compare_logits(g_lg[rows], ref_lg)
     res = resolvable_rows(ref_lg, row_err)
     own = np.array([O.argmax_f32(r) for r in g_lg])
-    return ok, mx, res, g_tk[rows], ref_tk, own, g_tk
+    return ok, mx, res, g_tk[rows], ref_tk, own, g_tk, att_err
 
 
 # One case per GEMM shape: 16-row fragments (1, 8, 16), 32 rows (24: a
@@ -75,9 +86,11 @@ def decode_step(big, B, seed, sample_rows, lo=512, hi=4096, ctx=None):
                                     (40, [0, 39]), (64, [0, 17, 40, 63]), (96, [0, 65, 95]),
                                     (150, [0, 77, 149]), (300, [0, 299]), (400, [0, 211, 399])])
 def test_8b_layer_decode_step_matches_oracle(big, B, rows):
-    ok, mx, res, g_tk, r_tk, own, all_tk = decode_step(big, B, seed=B, sample_rows=rows)
-    print(f"B={B}: max abs logit error {mx:.4f}, resolvable rows {int(res.sum())}/{len(rows)}")
+    ok, mx, res, g_tk, r_tk, own, all_tk, att = decode_step(big, B, seed=B, sample_rows=rows)
+    print(f"B={B}: max abs logit error {mx:.4f}, resolvable rows {int(res.sum())}/{len(rows)}, "
+          f"attention of all {B} rows: largest error {att.max():.2e}")
     assert ok, f"max abs logit error {mx:.3g}"
+    assert att.max() <= ATTN_TOL, f"attention rows {np.nonzero(att > ATTN_TOL)[0][:8].tolist()}"
     assert np.array_equal(g_tk[res], r_tk[res])
     # every row: the fused argmax equals the lowest-id argmax of the logits
     assert np.array_equal(own, all_tk)
@@ -85,7 +98,8 @@ def test_8b_layer_decode_step_matches_oracle(big, B, rows):
 
 def test_8b_layer_short_contexts_and_block_edges(big):
     # contexts 31, 32, 33, 63, 64 around 32-position block edges
-    ok, mx, res, g_tk, r_tk, own, all_tk = decode_step(big, 5, seed=77, sample_rows=range(5),
-                                                       lo=31, hi=64, ctx=[31, 32, 33, 63, 64])
+    ok, mx, res, g_tk, r_tk, own, all_tk, att = decode_step(big, 5, seed=77, sample_rows=range(5),
+                                                            lo=31, hi=64, ctx=[31, 32, 33, 63, 64])
     assert ok, f"max abs logit error {mx:.3g}"
+    assert att.max() <= ATTN_TOL
     assert np.array_equal(g_tk[res], r_tk[res])

@@ -24,21 +24,11 @@ from continuous_batching_decode_forward_amd import configs, synth
 from continuous_batching_decode_forward_amd.engine import ComposerLoop, Engine
 from oracle.composer_ref import ComposerRef
 
+from cb_streams import (Q_BS, Q_CHUNK, Q_MBPS, Q_POOL, Q_ROWS, Q_SEED, Q_SLOTS, Q_STEPS, QWEN,
+                        qwen_loop_stream, request_stream)
 from gpu_util import compare_logits, resolvable_rows, weights_to
 
 pytestmark = pytest.mark.gpu
-
-
-def request_stream(seed, n, prompt_range, new_range, vocab, first_prompt=None):
-    lens = synth.uniform_ints(seed, "plen", n, *prompt_range)
-    if first_prompt is not None:
-        lens[0] = first_prompt
-    news = synth.uniform_ints(seed, "maxnew", n, *new_range)
-    out = []
-    for i in range(n):
-        toks = synth.uniform_ints(seed, f"prompt{i}", int(lens[i]), 0, vocab - 1)
-        out.append((i, [int(t) for t in toks], int(news[i])))
-    return out
 
 
 def plan_arrays(p):
@@ -196,21 +186,9 @@ def test_native_loop_step_equals_the_written_out_loop(tiny):
     print(f"native loop: {len(t1)} steps identical to the written-out loop")
 
 
-QWEN = configs.QWEN2B
-Q_SLOTS, Q_BS, Q_CHUNK = 8, 32, 512
-Q_POOL = 16 * Q_SLOTS
-Q_MBPS = -(-(512 + 300) // Q_BS)
-Q_ROWS = Q_CHUNK + Q_SLOTS
-
-
-@pytest.mark.skip(reason="faulted (illegal address) before the fix of the attention kernel's "
-                         "empty (query tile, key split) items, whose prologue load read an "
-                         "unstaged block-table entry; the cause is shown on the host by replaying "
-                         "the item enumeration for this test's first plans (1408 empty items). "
-                         "Held off the GPU until it can be run again with the fix.")
 def test_2b_28layer_loop_full_size():
     torch.cuda.set_device(0)
-    seed, n_steps, n_check = 4, 48, 4
+    seed, n_steps, n_check = Q_SEED, Q_STEPS, 4
     wg = synth.make_weights(QWEN, seed=seed, device="cuda")
     order = synth.permutation(seed, "blocks", Q_POOL).astype(np.int32)
     eng = Engine(QWEN, wg, block_size=Q_BS, num_blocks=Q_POOL, max_blocks_per_seq=Q_MBPS,
@@ -221,7 +199,7 @@ def test_2b_28layer_loop_full_size():
     # keeps its own copy of the same FIFO
     ref = ComposerRef(Q_SLOTS, Q_BS, Q_POOL, Q_ROWS, Q_CHUNK, 0, B.CBD_ADMIT_RESERVE,
                       block_order=list(order), max_blocks_per_seq=Q_MBPS)
-    reqs = request_stream(seed, 24, (16, 512), (2, 300), QWEN.vocab, first_prompt=16)
+    reqs = qwen_loop_stream()
     for rid, prompt, mx in reqs:
         loop.submit(prompt, mx, None, rid)
         ref.submit(rid, prompt, mx)

@@ -76,3 +76,69 @@ def test_long_chunks_span_several_key_splits(shape):
     finally:
         eng.close()
     print(f"{shape.name}: long chunks, max abs logit error {worst:.2e}, {n_res} decidable rows")
+
+
+def test_8b_layer_512_row_chunk_at_offset_3584():
+    """The last 512-token chunk of a 4096-token prompt on one 8B-shaped layer
+    + LM head: the chunk at offset 3584 over a paged prefix of 3584 cached
+    positions, emitting its last row (the request's first answer token),
+    beside 4 decode rows with contexts 1024..4096. The chunk runs on the
+    block attention kernel at its real shape (256-column items over 7 key
+    splits) and the projections on the dense GEMM at 516 rows. Checks: every
+    row's attention output against the oracle's dense attention over the
+    same query and K/V (2^-12 of its scale), and the emitting rows' logits
+    against the oracle's paged step over all 516 rows."""
+    from continuous_batching_decode_forward_amd.engine import Engine
+
+    from gpu_util import attention_rows_vs_oracle, fill_pool, oracle_pool
+
+    torch.cuda.set_device(0)
+    shape, seed, bs, off, chunk = configs.LLAMA8B_1L, 5, 32, 3584, 512
+    wg = synth.make_weights(shape, seed=seed, device="cuda")
+    dec_ctx = [int(c) for c in synth.uniform_ints(seed, "ctx", 4, 1024, 4096)]
+    ctx = [off] + dec_ctx
+    nn = [chunk] + [1] * len(dec_ctx)
+    need = [-(-(c + n) // bs) for c, n in zip(ctx, nn)]
+    perm = synth.permutation(seed, "blocks", int(sum(need)))
+    mbps = max(need)
+    tables = np.full((len(ctx), mbps), -1, np.int32)
+    at = 0
+    for i, k in enumerate(need):
+        tables[i, :k] = perm[at:at + k]
+        at += k
+    cached = np.concatenate([tables[i, :-(-c // bs)] for i, c in enumerate(ctx)])
+    prompt = synth.uniform_ints(seed, "prompt", off + chunk, 0, shape.vocab - 1)
+    toks = [int(t) for t in prompt[off:]] + \
+        [int(t) for t in synth.uniform_ints(seed, "dec", len(dec_ctx), 0, shape.vocab - 1)]
+    want = [1] * len(ctx)
+    eng = Engine(shape, wg, block_size=bs, num_blocks=len(perm), max_blocks_per_seq=mbps,
+                 max_slots=len(ctx), max_rows=sum(nn), max_seqs=len(ctx),
+                 max_position=mbps * bs)
+    try:
+        fill_pool(eng, seed, cached)
+        meta = eng.upload_step(slots=list(range(len(ctx))), block_tables=tables, ctx_lens=ctx,
+                               n_new=nn, tokens=toks, want_token=want)
+        lg = torch.empty((len(ctx), shape.vocab), dtype=torch.float32, device="cuda")
+        tk = torch.empty(len(ctx), dtype=torch.int32, device="cuda")
+        eng.step_forward(meta, lg, tk)
+        torch.cuda.synchronize()
+        assert eng.status() == 0
+        g_lg, g_tk = lg.cpu().numpy(), tk.cpu().numpy()
+        att = attention_rows_vs_oracle(eng, tables, ctx, nn)
+    finally:
+        eng.close()
+    print(f"512-row chunk at offset {off}: attention of all {len(att)} rows, largest error "
+          f"{att.max():.2e}")
+    assert att.max() <= 2.0 ** -12, f"attention rows {np.nonzero(att > 2.0 ** -12)[0][:8].tolist()}"
+    assert np.array_equal(g_tk, np.argmax(g_lg, axis=1))
+    wc = {k: ([t.cpu() for t in v] if isinstance(v, list) else v.cpu()) for k, v in wg.items()}
+    del wg
+    model = O.Model(shape, wc)
+    pool, compact = oracle_pool(shape, seed, list(tables), ctx, bs, nn)
+    ref_lg, ref_tok = O.paged_step(model, pool, compact, ctx, nn, toks, want)
+    ok, mx, row_err = compare_logits(g_lg, ref_lg)
+    res = resolvable_rows(ref_lg, row_err)
+    print(f"512-row chunk at offset {off}: emitting rows' max abs logit error {mx:.2e}, "
+          f"{int(res.sum())}/{len(ctx)} decidable")
+    assert ok, f"max abs logit error {mx:.3g}"
+    assert np.array_equal(g_tk[res], ref_tok[res])

@@ -128,8 +128,11 @@ def test_sampler_matches_oracle_on_identical_logits(engine, engine_wide, vocab, 
 
 
 def test_sampler_distribution_over_many_draws(engine):
-    """One row sampled at 4000 step ids: the GPU's empirical distribution
-    over the kept set matches the renormalised softmax (top_p 0.9)."""
+    """One request's row sampled at 4000 step ids: the GPU's empirical
+    distribution over the kept set matches the renormalised softmax (top_p
+    0.9). Each call samples 256 rows on 256 distinct slots (slots of one
+    call must be distinct: each row updates its slot's counts) that share
+    the request id and parameters, so the draws differ only by step id."""
     n_draw = 4000
     z = np.full(V, -30.0, np.float32)
     z[:6] = [2.0, 1.5, 1.0, 0.5, 0.0, -3.0]
@@ -137,11 +140,12 @@ def test_sampler_distribution_over_many_draws(engine):
     c = B.cbd_sampling()
     c.temperature, c.top_p, c.top_k = sp.temperature, sp.top_p, sp.top_k
     c.freq_penalty, c.presence_penalty, c.penalty_decay, c.seed = 0.0, 0.0, 1.0, 77
-    slot = B.cbd_slot_alloc(engine.handle, c, 999)
+    slots = [B.cbd_slot_alloc(engine.handle, c, 999) for _ in range(256)]
+    assert len(set(slots)) == 256
     lg = torch.from_numpy(np.tile(z, (256, 1))).cuda()
     counts = np.zeros(6)
+    sl = torch.tensor(slots, dtype=torch.int32, device="cuda")
     for b in range(0, n_draw, 256):
-        sl = torch.full((256,), slot, dtype=torch.int32, device="cuda")
         st = torch.arange(b, b + 256, dtype=torch.int32, device="cuda")
         out = torch.empty(256, dtype=torch.int32, device="cuda")
         engine.sample_logits(lg, sl, st, out)
@@ -157,4 +161,5 @@ def test_sampler_distribution_over_many_draws(engine):
     exp = pk * counts.sum()
     chi2 = ((counts[:k] - exp) ** 2 / exp).sum()
     assert chi2 < 30, chi2
-    B.cbd_slot_free(engine.handle, slot)
+    for s_ in slots:
+        B.cbd_slot_free(engine.handle, s_)

@@ -26,22 +26,11 @@ import oracle as O
 from continuous_batching_decode_forward_amd import binding as B
 from continuous_batching_decode_forward_amd import configs, synth
 
-from gpu_util import fill_pool, make_engine
+from gpu_util import fill_pool, make_engine, stage_error
 
 pytestmark = pytest.mark.gpu
 
 SHAPE = configs.LLAMA8B_1L
-
-
-def stage_error(gpu: np.ndarray, ref: np.ndarray, slack=None) -> float:
-    """max_i (|gpu_i - ref_i| - slack_i) / (|ref_i| + rms(ref))."""
-    g = np.asarray(gpu, np.float64).reshape(-1)
-    o = np.asarray(ref, np.float64).reshape(-1)
-    rms = float(np.sqrt(np.mean(o * o))) or 1.0
-    d = np.abs(g - o)
-    if slack is not None:
-        d = np.maximum(d - slack.reshape(-1), 0.0)
-    return float((d / (np.abs(o) + rms)).max())
 
 
 STAGE_TOL = 2.0 ** -12

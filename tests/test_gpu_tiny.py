@@ -109,12 +109,14 @@ def test_tiny_chunked_prefill_mixed_with_decode(tiny):
     check(res)
 
 
-@pytest.mark.parametrize("bs", [8, 16, 32])
-def test_tiny_block_sizes_and_ragged_contexts(tiny, bs):
+# chunk 7 keeps every sequence on the per-tile attention kernel; chunks of
+# 32+ rows on 32- and 64-position blocks take the block kernel.
+@pytest.mark.parametrize("bs,chunk", [(8, 7), (16, 7), (32, 7), (64, 7), (32, 40), (64, 64)])
+def test_tiny_block_sizes_and_ragged_contexts(tiny, bs, chunk):
     # contexts around block boundaries: bs-1, bs, bs+1, and a single token
     prompts = [synth.uniform_ints(bs, f"p{i}", L, 0, CFG.vocab - 1)
                for i, L in enumerate([bs - 1, bs, bs + 1, 1])]
-    res = run_schedule(tiny, prompts, 5, chunk=7, bs=bs, nb=64 if bs < 32 else 32, seed=bs)
+    res = run_schedule(tiny, prompts, 5, chunk=chunk, bs=bs, nb=64 if bs < 32 else 32, seed=bs)
     check(res)
 
 

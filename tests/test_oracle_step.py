@@ -209,3 +209,50 @@ def test_layers_apply_in_order_with_their_own_weights():
             wz[k][1 - keep] = torch.zeros_like(wz[k][1 - keep])
         w1 = {k: ([v[keep]] if isinstance(v, list) else v) for k, v in w.items()}
         assert np.array_equal(run(cfg2, wz), run(CFG.with_layers(1), w1))
+
+
+def test_in_step_greedy_takes_the_lowest_id_of_planted_ties():
+    """Exact ties planted in the step's logits: a row of the LM head copied
+    onto another id gives that id the same dot product, summed in the same
+    order, so its logit equals the original's bit for bit. The step's greedy
+    id must be the lowest id among the maxima of the binary32 logits, i.e.
+    numpy's first-index argmax (the batched-equals-serial claim of the
+    Kestrel page, "0.8MB 跑通 Qwen" 14-1 section 3, covers greedy ids).
+    Copies land both above and below the original maximum, and on ids 0 and
+    V - 1, so a highest-id rule (>=) or a first-row-only rule fails."""
+    cfg = CFG.with_layers(1)
+    w = synth.make_weights(cfg, seed=8)
+    prompts = [synth.uniform_ints(8, f"tie.{i}", n, 0, cfg.vocab - 1)
+               for i, n in enumerate((3, 7, 5, 2))]
+    nn = [len(p) for p in prompts]
+    toks = np.concatenate(prompts)
+    tables = np.arange(16, dtype=np.int32).reshape(4, 4)
+
+    def step(weights):
+        m = O.Model(cfg, weights)
+        return O.paged_step(m, m.paged_pool(16, 4), tables, [0] * 4, nn, toks, [1] * 4)
+
+    lg, g = step(w)
+    assert np.array_equal(g, np.argmax(lg.astype(np.float32), axis=1))
+    best = [int(i) for i in np.argmax(lg, axis=1)]
+    assert len(set(best)) == 4, "choose another seed: two rows share their maximum"
+    V = cfg.vocab
+    # partner ids: above, below, the first and the last id of the vocabulary
+    partners = [best[0] + 1, best[1] - 1, 0, V - 1]
+    taken = set(best)
+    for r, j in enumerate(partners):
+        while j in taken or not 0 <= j < V:
+            j = (j + 17) % V
+        partners[r] = j
+        taken.add(j)
+    wt = dict(w)
+    lm_head = w["lm_head"].clone()
+    for r, j in enumerate(partners):
+        lm_head[j] = lm_head[best[r]]
+    wt["lm_head"] = lm_head
+    lg2, g2 = step(wt)
+    for r, j in enumerate(partners):
+        assert lg2[r, j] == lg2[r, best[r]] == lg[r, best[r]], f"row {r}: no exact tie"
+        assert int(g2[r]) == min(j, best[r]), f"row {r}: ties must go to the lowest id"
+    assert any(j > b for j, b in zip(partners, best)) and any(j < b for j, b in zip(partners, best))
+    assert np.array_equal(g2, np.argmax(lg2.astype(np.float32), axis=1))
