@@ -152,41 +152,93 @@ def time_steps(eng, meta, lg, tk, steps, warmup, stream, profile_class=None):
     return ms, wall, kern
 
 
-def cpu_baseline(shape, wg, wl, seed, budget_s):
-    """The oracle, as it stands, on a bounded sample of the same step: decode
-    rows of the B=64 workload, one at a time, until about budget_s seconds of
-    CPU work."""
+def cpu_info():
+    """The host CPU's model name and the cores this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return model, os.cpu_count(), usable
+
+
+def oracle_kv_pool(shape, seed, tables, n_cached, n_new, bs, device):
+    """The oracle's pool ([L][2][blocks][bs][Hkv][hd] bf16 bits, host) for
+    the given sequences, blocks renumbered 0.. in table order, holding the
+    same synthetic cached K/V as the engine's pool (values keyed by the
+    physical block), generated on `device`; returns (pool, compact tables)."""
     import torch
     import oracle as O
     from continuous_batching_decode_forward_amd import synth
-    wc = {k: ([t.cpu() for t in v] if isinstance(v, list) else v.cpu()) for k, v in wg.items()}
-    om = O.Model(shape, wc)
-    bs, hkv, hd = wl["bs"], shape.n_kv_heads, shape.head_dim
-    done, spent = 0, 0.0
-    for i in range(len(wl["ctx"])):
-        c = int(wl["ctx"][i])
-        nb = -(-(c + 1) // bs)
-        pool = np.zeros((shape.n_layers, 2, nb, bs, hkv, hd), np.uint16)
-        ncached = -(-c // bs)
-        phys = torch.as_tensor(wl["tables"][i, :ncached].astype(np.int64))
+    hkv, hd = shape.n_kv_heads, shape.head_dim
+    need = [-(-(int(c) + int(n)) // bs) for c, n in zip(n_cached, n_new)]
+    pool = np.zeros((shape.n_layers, 2, max(sum(need), 1), bs, hkv, hd), np.uint16)
+    compact = np.full((len(need), max(need)), -1, np.int32)
+    kh = torch.arange(hkv, device=device).view(1, 1, -1, 1)
+    off = torch.arange(bs, device=device).view(1, -1, 1, 1)
+    dim = torch.arange(hd, device=device).view(1, 1, 1, -1)
+    nxt = 0
+    for i, (tab, c) in enumerate(zip(tables, n_cached)):
+        ids = np.arange(nxt, nxt + need[i], dtype=np.int32)
+        compact[i, :need[i]] = ids
+        nxt += need[i]
+        nbc = -(-int(c) // bs)
+        if nbc == 0:
+            continue
+        phys = torch.as_tensor(np.asarray(tab[:nbc], np.int64), device=device).view(-1, 1, 1, 1)
         for layer in range(shape.n_layers):
             for kind in (0, 1):
-                vals = synth.kv_values(seed, layer, kind, phys.view(-1, 1, 1, 1),
-                                       torch.arange(hkv).view(1, 1, -1, 1),
-                                       torch.arange(bs).view(1, -1, 1, 1),
-                                       torch.arange(hd).view(1, 1, 1, -1), hkv, bs, hd)
-                pool[layer, kind, :ncached] = O.as_u16(vals).reshape(ncached, bs, hkv, hd)
-        table = np.arange(nb, dtype=np.int32).reshape(1, nb)
-        t0 = time.perf_counter()
-        O.paged_step(om, pool, table, [c], [1], [int(wl["tokens"][i])], [1])
-        spent += time.perf_counter() - t0
-        done += 1
-        if spent >= budget_s:
-            break
-    return {"value": done / spent, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{done} decode rows of the B=64 step (8B layer + LM head, contexts "
-                      f"U[512,4096]), each alone through the oracle's paged step; "
-                      f"{spent:.1f} s of CPU work"}
+                vals = synth.kv_values(seed, layer, kind, phys, kh, off, dim, hkv, bs, hd)
+                pool[layer, kind, ids[:nbc]] = O.as_u16(vals.cpu()).reshape(nbc, bs, hkv, hd)
+    return pool, compact
+
+
+def cpu_baseline(shape, wg, wl, seed, B, budget_s):
+    """The oracle, as it stands, on the same step: all B decode rows of the
+    8B layer + LM head step in one paged step on every core the oracle's
+    OpenMP loops use (rows, heads and vocabulary in parallel), then a
+    bounded 1-thread sample (rows one at a time) for the per-core rate."""
+    import oracle as O
+    wc = {k: ([t.cpu() for t in v] if isinstance(v, list) else v.cpu()) for k, v in wg.items()}
+    om = O.Model(shape, wc)
+    ctx = [int(c) for c in wl["ctx"][:B]]
+    toks = [int(t) for t in wl["tokens"][:B]]
+    pool, compact = oracle_kv_pool(shape, seed, list(wl["tables"][:B]), ctx, [1] * B, wl["bs"],
+                                   "cuda")
+    threads = O.num_threads()
+    t0 = time.perf_counter()
+    O.paged_step(om, pool, compact, ctx, [1] * B, toks, [1] * B)
+    whole = time.perf_counter() - t0
+    # one thread: rows alone, until about a third of the budget
+    O.set_num_threads(1)
+    done, spent = 0, 0.0
+    try:
+        for i in range(B):
+            t0 = time.perf_counter()
+            O.paged_step(om, pool, compact[i:i + 1], [ctx[i]], [1], [toks[i]], [1])
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= budget_s / 3:
+                break
+    finally:
+        O.set_num_threads(threads)
+    model, n_cpu, usable = cpu_info()
+    return {"value": B / whole, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole B={B} step (8B layer + LM head, contexts U[512,4096]) in one "
+                      f"oracle paged step on {threads} threads: {whole:.1f} s",
+            "ms_per_step": whole * 1e3,
+            "single_thread": {"value": done / spent, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{done} rows of the same step, each alone, "
+                                        f"{spent:.1f} s"},
+            "cpu_model": model, "nproc": n_cpu, "usable_cores": usable}
 
 
 def penalty_history(seed, B, V, n_hist, decay):
@@ -204,6 +256,10 @@ def penalty_history(seed, B, V, n_hist, decay):
 
 
 def bench_sampled(args):
+    print(json.dumps(run_sampled(args.steps, args.warmup)), flush=True)
+
+
+def run_sampled(steps, warmup):
     """The KV-dominated sampled step: one 8B-shaped layer + LM head over a
     65536-token vocabulary, B = 256 decode rows with contexts uniform in
     8192..32768, sampler T = 1.0, top_p = 0.3, top_k = 0, frequency penalty
@@ -238,7 +294,7 @@ def bench_sampled(args):
                            step_ids=[64] * Bn, mode=B.CBD_MODE_SAMPLE)
     tk = torch.empty(Bn, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
-    ms, wall, kern = time_steps(eng, meta, None, tk, args.steps, args.warmup, stream)
+    ms, wall, kern = time_steps(eng, meta, None, tk, steps, warmup, stream)
     times = {}
     for name in ("ATTN", "LM_HEAD", "SAMPLE", "GATEUP", "DOWN", "QKV", "O"):
         _, _, k = time_steps(eng, meta, None, tk, 5, 1, stream,
@@ -254,9 +310,11 @@ def bench_sampled(args):
            "roofline_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
            "kv_bytes": kv, "attention_gbs": kv / (times["attn_us"] * 1e-6) / 1e9,
            "sampler_gbs": 3 * Bn * shape.vocab * 4 / (times["sample_us"] * 1e-6) / 1e9,
-           "kernel_us": times}
+           "kernel_us": times, "steps": steps, "warmup": warmup}
     eng.close()
-    print(json.dumps(out), flush=True)
+    del eng, wg
+    torch.cuda.empty_cache()
+    return out
 
 
 def build_mixed(shape, seed, n_dec=48, ctx_range=(1024, 8192), prompt=4096, chunk=512, bs=32):
@@ -302,6 +360,10 @@ def mixed_step(wl, j, with_chunk=True):
 
 
 def bench_mixed8b(args):
+    print(json.dumps(run_mixed8b(max(args.steps, 8))), flush=True)
+
+
+def run_mixed8b(reps):
     """The mixed step on the full 8B shape (32 layers, d_model 4096, 32/8
     heads, FFN 14336, vocab 128256): 48 decode rows with contexts uniform in
     1024..8192 plus one 512-token chunk of a 4096-token prompt, 560 rows per
@@ -326,7 +388,6 @@ def bench_mixed8b(args):
         f"({len(wl['cached']) * shape.kv_bytes_per_pos * wl['bs'] / 1e9:.1f} GB)")
     fill_pool(eng, seed, wl["cached"])
     tk = torch.empty(n_dec + 1, dtype=torch.int32, device="cuda")
-    reps = max(args.steps, 8)
     d, hq, hd, L = shape.d_model, shape.n_heads, shape.head_dim, shape.n_layers
     ws = synth.weight_shapes(shape)
     lin = 2 * L * sum(int(np.prod(ws[k])) for k in ("w_qkv", "w_o", "w_gate", "w_up", "w_down"))
@@ -372,9 +433,11 @@ def bench_mixed8b(args):
            "decode_gbs_mean": mean("decode_gbs"),
            "decode_roofline_frac": mean("decode_gbs") / PEAK_HBM_GBS,
            "decode_tokens_per_s_mixed": n_dec / (mean("ms_mixed") * 1e-3),
-           "steps": rows}
+           "reps_per_offset": reps, "steps": rows}
     eng.close()
-    print(json.dumps(out), flush=True)
+    del eng, wg
+    torch.cuda.empty_cache()
+    return out
 
 
 def cb_requests(seed, n, vocab, prompt_range=(16, 512), new_range=(2, 300)):
@@ -469,6 +532,10 @@ def main():
     ap.add_argument("--sweep", default="1,8,32,64")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the long-context sampled and the mixed 32-layer workloads")
+    ap.add_argument("--mixed-reps", type=int, default=8,
+                    help="timed repetitions per chunk offset of the mixed workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--print-sources-digest", action="store_true")
@@ -565,11 +632,16 @@ def main():
     log(f"[bench] B={Bn}: {ms:.3f} ms/step ({wall / args.steps * 1e3:.3f} ms wall), "
         f"{tokps:.0f} tok/s, {gbs:.0f} GB/s; LM head {lm_ms * 1e3:.1f} us, {lm_gbs:.0f} GB/s")
 
+    eng.close()
+    del eng
+    torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(shape, wg, wl, seed, args.cpu_seconds)
-        log(f"[bench] CPU oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads")
+        cpu = cpu_baseline(shape, wg, wl, seed, Bn, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {cpu['value']:.3f} tokens/s on {cpu['cores']} threads, "
+            f"{cpu['single_thread']['value']:.3f} tokens/s on one ({cpu['cpu_model']})")
 
     out = {
         "metric": "decode tokens/s per step and HBM GB/s vs (W+B*A)/beta roofline, 8B-shape, 1 GPU",
@@ -599,7 +671,20 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep,
     }
-    eng.close()
+    del wg
+    torch.cuda.empty_cache()
+    if not args.headline_only:
+        # The other measured workloads, each timed on its own stream with HIP
+        # events like the headline: the KV-dominated sampled step and the
+        # 32-layer mixed step (decode rows + a prefill chunk).
+        log("[bench] long-context sampled step (B=256, contexts 8k..32k, vocab 65536)")
+        out["long_context_sampled"] = run_sampled(max(10, args.steps // 2), 3)
+        log(f"[bench] long-context sampled: {out['long_context_sampled']['ms_per_step']:.3f} ms/step, "
+            f"{out['long_context_sampled']['roofline_frac']:.3f} of peak")
+        log("[bench] 32-layer 8B mixed step (48 decode rows + 512-token chunk)")
+        out["mixed_8b_32layer"] = run_mixed8b(args.mixed_reps)
+        log(f"[bench] mixed: {out['mixed_8b_32layer']['ms_per_step_mean']:.2f} ms/step mean, "
+            f"chunk MFMA use {out['mixed_8b_32layer']['chunk_mfma_util_mean']:.3f}")
     print(json.dumps(out), flush=True)
 
 

@@ -105,6 +105,7 @@ def _declare(L):
                                 C.c_uint32, C.POINTER(OrSampleInfo)]
     L.or_sample_f32.restype = C.c_int32
     L.or_num_threads.restype = C.c_int32
+    L.or_set_num_threads.argtypes = [C.c_int32]
 
 
 def _p(a: np.ndarray, t):
@@ -298,3 +299,8 @@ def sample(logits, counts, sp, request_id: int, step_id: int):
 
 def num_threads() -> int:
     return lib().or_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (rows, heads, vocabulary)."""
+    lib().or_set_num_threads(int(n))

@@ -745,3 +745,12 @@ int32_t or_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads the oracle's parallel loops use from now on (n >= 1). */
+void or_set_num_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
