@@ -270,16 +270,36 @@ __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K,
     }
   }
   if (hi - lo <= 1u) return lo;
-  // Gather the values in [lo, hi) (their order does not matter: only sums
-  // over them are taken); slots come from an LDS counter.
-  if (threadIdx.x == 0) sh.n_cand = 0;
-  __syncthreads();
-  SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
-    const float v = e.get(k, base + 64 * k);
-    const uint32_t u = __float_as_uint(v);
-    if (v >= 0.f && u >= lo && u < hi) sh.cand[atomicAdd(&sh.n_cand, 1)] = v;
+  // Gather the values in [lo, hi) (at most SMP_THREADS of them) in (thread,
+  // k) order: each thread's first slot is the block prefix of the per-thread
+  // counts, so the candidates, and every sum taken over them below, come out
+  // in the same order on every run.
+  {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int cnt = 0;
+    SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
+      const float v = e.get(k, base + 64 * k);
+      const uint32_t u = __float_as_uint(v);
+      if (v >= 0.f && u >= lo && u < hi) ++cnt;
+    }
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += t;
+    }
+    if (lane == 63) sh.wave_i[w] = inc;
+    __syncthreads();
+    int at = inc - cnt;
+    for (int x = 0; x < w; ++x) at += sh.wave_i[x];
+    SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
+      const float v = e.get(k, base + 64 * k);
+      const uint32_t u = __float_as_uint(v);
+      if (v >= 0.f && u >= lo && u < hi) sh.cand[at++] = v;
+    }
+    if (threadIdx.x == SMP_THREADS - 1) sh.n_cand = at;
+    __syncthreads();
   }
-  __syncthreads();
   // Wave 0 alone finishes the bisection on the (at most SMP_THREADS)
   // candidates, 16 per lane, with wave reductions only; every lane decides
   // on lane 0's sum, and the result goes to the other waves through LDS.
