@@ -130,6 +130,7 @@ SIGNATURES = [
     ("cbd_blocks_available", C.c_int, [VP]),
     ("cbd_step_forward", C.c_int, [VP, C.POINTER(cbd_step), VP, VP, VP]),
     ("cbd_sample_logits", C.c_int, [VP, VP, C.c_int32, VP, VP, VP, VP]),
+    ("cbd_sample_logits_noalloc", C.c_int, [VP, VP, C.c_int32, VP, VP, VP, VP]),
     ("cbd_engine_status", C.c_int, [VP, VP, C.POINTER(C.c_uint32)]),
     ("cbd_last_error", C.c_char_p, []),
     ("cbd_debug_buffer", C.c_int, [VP, C.c_int32, C.POINTER(VP), C.POINTER(C.c_size_t)]),
@@ -252,6 +253,12 @@ def cbd_step_forward(engine, step: cbd_step, logits_out, tokens_out, stream) -> 
 
 def cbd_sample_logits(engine, logits, n: int, slots, step_ids, tokens_out, stream) -> None:
     _call("cbd_sample_logits", engine, logits, int(n), slots, step_ids, tokens_out, stream)
+
+
+def cbd_sample_logits_noalloc(engine, logits, n: int, slots, step_ids, tokens_out,
+                              stream) -> None:
+    _call("cbd_sample_logits_noalloc", engine, logits, int(n), slots, step_ids, tokens_out,
+          stream)
 
 
 def cbd_engine_status(engine, stream) -> int:

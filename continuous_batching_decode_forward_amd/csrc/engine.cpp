@@ -249,6 +249,15 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* packed_
         cus < 1)
       cus = 256;
     e->attn_waves = cus * 4 * 2;
+    e->device = dev;
+  }
+  {  // the fixed sampler scratch of this device, looked up at set-up
+    float* p = nullptr;
+    size_t n = 0;
+    if (noalloc_scratch(&p, &n) != hipSuccess) {
+      delete e;
+      return fail(CBD_E_DEVICE, "sampler scratch symbol lookup failed");
+    }
   }
   e->slots.reset(cfg->max_slots);
   if (!e->blocks.reset(cfg->num_blocks, block_order)) {
@@ -516,6 +525,33 @@ int cbd_sample_logits(cbd_engine* e, const float* logits, int32_t n, const int32
                          reinterpret_cast<const SlotParams*>(e->slot_state + e->sl.params),
                          reinterpret_cast<float*>(e->slot_state + e->sl.counts), e->cfg.max_slots,
                          e->wsp<float>(e->ws.smp), tokens_out, e->wsp<uint32_t>(e->ws.status),
+                         (hipStream_t)stream));
+  return CBD_OK;
+}
+
+int cbd_sample_logits_noalloc(cbd_engine* e, const float* logits, int32_t n,
+                              const int32_t* slots, const int32_t* step_ids, int32_t* tokens_out,
+                              void* stream) {
+  if (!e || !logits || !slots || !step_ids || !tokens_out || n < 1 || n > e->cfg.max_seqs)
+    return fail(CBD_E_INVAL, "bad sample_logits_noalloc arguments");
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != e->device)
+    return fail(CBD_E_INVAL, "the engine's device is not the current device");
+  float* scratch = nullptr;
+  size_t cap = 0;
+  HIP_TRY(noalloc_scratch(&scratch, &cap));
+  // rows of vocabularies above 65536 are staged in the scratch, one
+  // sampler_row_floats(vocab) run per row; smaller rows stay on chip
+  const size_t need = e->cfg.vocab > 65536 ? (size_t)n * sampler_row_floats(e->cfg.vocab) : 0;
+  if (need > cap)
+    return fail(CBD_E_INVAL, "sample_logits_noalloc: " + std::to_string(n) + " rows of vocab " +
+                                 std::to_string(e->cfg.vocab) + " need " + std::to_string(need) +
+                                 " scratch floats, above the fixed " + std::to_string(cap));
+  HIP_TRY(launch_sampler(logits, n, e->cfg.vocab, slots, step_ids, nullptr,
+                         reinterpret_cast<const SlotParams*>(e->slot_state + e->sl.params),
+                         reinterpret_cast<float*>(e->slot_state + e->sl.counts), e->cfg.max_slots,
+                         scratch, tokens_out, e->wsp<uint32_t>(e->ws.status),
                          (hipStream_t)stream));
   return CBD_OK;
 }

@@ -178,6 +178,11 @@ hipError_t launch_sampler(const float* logits, int32_t n, int32_t V, const int32
                           float* counts, int32_t max_slots, float* scratch, int32_t* tokens,
                           uint32_t* status, hipStream_t st);
 
+// The current device's fixed sampler scratch (a static device array of
+// *floats floats), for the allocation-free sampler entry point; looked up once
+// per device.
+hipError_t noalloc_scratch(float** ptr, size_t* floats);
+
 // -------------------------------------------------------------------- misc
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t st);

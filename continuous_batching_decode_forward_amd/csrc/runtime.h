@@ -133,6 +133,7 @@ struct cbd_engine {
   uint8_t* workspace;
   hipStream_t stream;
   int32_t attn_waves;  // resident waves of the per-tile attention kernel (2 per SIMD)
+  int32_t device;      // the device the engine was created on
   cbd::SlotAllocator slots;
   cbd::BlockAllocator blocks;
   std::vector<cbd::SlotParams> host_params;

@@ -232,6 +232,22 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* step, float* logits_out,
 int cbd_sample_logits(cbd_engine* e, const float* logits, int32_t n, const int32_t* slots,
                       const int32_t* step_ids, int32_t* tokens_out, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * cbd_sample_logits with the same arguments, results and errors, except that
+ * the per-row scratch of vocabularies above 65536 comes from a fixed static
+ * device array of 4 Mi floats (16 MiB) per GPU instead of the engine's
+ * workspace, so n * 1024 * ceil(vocab / 1024) must stay within 4 Mi
+ * (vocab 151936: at most 27 rows), else CBD_E_INVAL before anything is
+ * enqueued; vocabularies up to 65536 use no scratch (n up to max_seqs).
+ * Allocates nothing. The engine's device must be the current device. All
+ * calls on one GPU share its array and leave its contents behind (nothing
+ * needs clearing: each row's scratch is written before it is read); calls
+ * that overlap on one GPU race. */
+int cbd_sample_logits_noalloc(cbd_engine* e, const float* logits, int32_t n,
+                              const int32_t* slots, const int32_t* step_ids, int32_t* tokens_out,
+                              void* stream);
+
 /* Wait for the engine's device status word on `stream`, return it in
  * *flags and clear it (CBD_STATUS_* bits). */
 int cbd_engine_status(cbd_engine* e, void* stream, uint32_t* flags);
