@@ -451,23 +451,32 @@ def cb_requests(seed, n, vocab, prompt_range=(16, 512), new_range=(2, 300)):
 
 
 def bench_cb2b(args):
+    for line in run_cb2b([int(b) for b in args.cb_slots.split(",")], args.cb_steps,
+                         [int(x) for x in args.cb_pacing.split(",")]):
+        print(json.dumps(line), flush=True)
+
+
+def run_cb2b(slot_counts, n_steps, pacings):
     """Continuous batching on the full 2B-shaped decoder (28 layers, d_model
     2048, 16/8 heads, FFN 6144, vocab 151936): B slots, prompts 16..512,
     answers 2..300 tokens (EOS id 0), 32-position blocks, 16 blocks per slot,
     answer blocks reserved at admission, 512-token chunks, 512 + B rows per
     step, a closed-loop queue (never empty), greedy. Each step is one native
     cbd_sched_step (plan, upload, step, tokens back, commit), timed on the
-    host clock around the call."""
+    host clock around the call. Each pacing of prefill against decode runs
+    the same request stream: time to first token is taken from a request's
+    submission to the end of the step that emitted its first token."""
     import torch
     from continuous_batching_decode_forward_amd import configs, synth
     from continuous_batching_decode_forward_amd.engine import ComposerLoop, Engine
     shape, wlc = configs.QWEN2B, configs.CB_2B
     seed, bs, chunk = 0, wlc.block_size, 512
-    n_steps = args.cb_steps
+    names = {0: "prefill-first", 1: "albatross", 2: "separate"}
     log(f"[bench] weights {shape.name} on GPU")
     wg = synth.make_weights(shape, seed=seed, device="cuda")
     mbps = -(-(wlc.ctx_range[1] + 300) // bs)
-    for Bn in [int(b) for b in args.cb_slots.split(",")]:
+    out = []
+    for Bn in slot_counts:
         pool = 16 * Bn
         order = synth.permutation(seed, "blocks", pool).astype(np.int32)
         eng = Engine(shape, wg, block_size=bs, num_blocks=pool, max_blocks_per_seq=mbps,
@@ -475,52 +484,67 @@ def bench_cb2b(args):
                      block_order=order)
         reqs = cb_requests(seed + Bn, 4096, shape.vocab)
 
-        def run(steps, first):
-            loop = ComposerLoop(eng, max_rows=chunk + Bn, chunk_size=chunk, eos_id=0)
-            nxt, rec = first, []
+        def run(steps, first, pacing):
+            loop = ComposerLoop(eng, max_rows=chunk + Bn, chunk_size=chunk, eos_id=0,
+                                pacing=pacing)
+            nxt, rec, submitted, ttft = first, [], {}, []
             try:
                 for _ in range(steps):
                     while loop.stats().queued < Bn:  # closed loop: the queue never empties
                         rid, prompt, mx = reqs[nxt % len(reqs)]
                         loop.submit(prompt, mx, None, nxt)
+                        submitted[nxt] = time.perf_counter()
                         nxt += 1
                     t0 = time.perf_counter()
                     p = loop.step()
-                    dt = time.perf_counter() - t0
+                    t1 = time.perf_counter()
                     n = p.n_seqs
+                    for i in range(n):
+                        if p.want_token[i] and p.step_ids[i] == 0:
+                            ttft.append(t1 - submitted.pop(int(p.request_ids[i])))
                     ctx = list(p.ctx_lens[:n]) if p.n_prefill_rows == 0 else []
-                    rec.append((dt, p.n_prefill_rows, p.n_decode_rows, p.n_out, ctx))
+                    rec.append((t1 - t0, p.n_prefill_rows, p.n_decode_rows, p.n_out, ctx))
                 fin = loop.pop_finished()
             finally:
                 loop.close()
-            return rec, fin
+            return rec, fin, ttft
 
-        run(8, 10_000)  # warm-up on its own composer; closing it frees every slot and block
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        rec, fin = run(n_steps, 0)
-        wall = time.perf_counter() - t0
-        if eng.status():
-            raise RuntimeError("device status set")
-        gen = sum(r[3] for r in rec)
-        dec = [r for r in rec if r[1] == 0 and r[2] > 0]
-        mixed = [r for r in rec if r[1] > 0]
-        d_time = sum(r[0] for r in dec)
-        d_rows = sum(r[2] for r in dec)
-        d_bytes = sum(step_bytes(shape, r[4], r[3]) for r in dec)
-        out = {"workload": wlc.name, "slots": Bn, "steps": n_steps, "wall_s": wall,
-               "generated_tokens": gen, "tokens_per_s": gen / wall,
-               "finished_requests": len(fin),
-               "decode_only_steps": len(dec),
-               "decode_ms_per_step": 1e3 * d_time / max(len(dec), 1),
-               "decode_tokens_per_s": d_rows / d_time if d_time else None,
-               "decode_hbm_gbs": d_bytes / d_time / 1e9 if d_time else None,
-               "decode_roofline_frac": d_bytes / d_time / 1e9 / PEAK_HBM_GBS if d_time else None,
-               "mixed_steps": len(mixed),
-               "mixed_ms_per_step": 1e3 * sum(r[0] for r in mixed) / max(len(mixed), 1),
-               "prefill_rows": sum(r[1] for r in rec)}
+        for pacing in pacings:
+            run(8, 10_000, pacing)  # warm-up on its own composer; closing it frees every slot and block
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            rec, fin, ttft = run(n_steps, 0, pacing)
+            wall = time.perf_counter() - t0
+            if eng.status():
+                raise RuntimeError("device status set")
+            gen = sum(r[3] for r in rec)
+            dec = [r for r in rec if r[1] == 0 and r[2] > 0]
+            mixed = [r for r in rec if r[1] > 0]
+            d_time = sum(r[0] for r in dec)
+            d_rows = sum(r[2] for r in dec)
+            d_bytes = sum(step_bytes(shape, r[4], r[3]) for r in dec)
+            tt = np.array(ttft) * 1e3
+            line = {"workload": wlc.name, "slots": Bn, "pacing": names[pacing], "steps": n_steps,
+                    "wall_s": wall, "generated_tokens": gen, "tokens_per_s": gen / wall,
+                    "finished_requests": len(fin),
+                    "ttft_ms": {"n": int(tt.size), "mean": float(tt.mean()) if tt.size else None,
+                                "p50": float(np.percentile(tt, 50)) if tt.size else None,
+                                "p90": float(np.percentile(tt, 90)) if tt.size else None},
+                    "decode_only_steps": len(dec),
+                    "decode_ms_per_step": 1e3 * d_time / max(len(dec), 1),
+                    "decode_tokens_per_s": d_rows / d_time if d_time else None,
+                    "decode_hbm_gbs": d_bytes / d_time / 1e9 if d_time else None,
+                    "decode_roofline_frac": d_bytes / d_time / 1e9 / PEAK_HBM_GBS if d_time else None,
+                    "mixed_steps": len(mixed),
+                    "mixed_ms_per_step": 1e3 * sum(r[0] for r in mixed) / max(len(mixed), 1),
+                    "prefill_rows": sum(r[1] for r in rec)}
+            log(f"[bench] 2B loop B={Bn} {names[pacing]}: {line['tokens_per_s']:.0f} tok/s, "
+                f"decode {line['decode_ms_per_step']:.3f} ms/step, ttft p50 {line['ttft_ms']['p50']}")
+            out.append(line)
         eng.close()
-        print(json.dumps(out), flush=True)
+    del wg
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -546,6 +570,9 @@ def main():
                     help="the headline decode sweep (default) or another configured workload")
     ap.add_argument("--cb-slots", default="8,32", help="slot counts of the 2B loop workload")
     ap.add_argument("--cb-steps", type=int, default=256, help="steps of the 2B loop workload")
+    ap.add_argument("--cb-pacing", default="0,1,2",
+                    help="pacings of the 2B loop workload: 0 prefill first, 1 Albatross, "
+                         "2 prefill apart from decode")
     args = ap.parse_args()
     if args.print_sources_digest:
         print(sources_digest())

@@ -31,6 +31,10 @@ CBD_ADMIT_RESERVE = 0
 CBD_ADMIT_FREE_SLOT = 1
 CBD_ADMIT_REQUEST_LEVEL = 2
 
+CBD_PACE_PREFILL_FIRST = 0
+CBD_PACE_ALBATROSS = 1
+CBD_PACE_SEPARATE = 2
+
 CBD_KERNEL_QKV = 1
 CBD_KERNEL_ROPE = 2
 CBD_KERNEL_ATTN = 3
@@ -96,7 +100,9 @@ class cbd_step(C.Structure):
 class cbd_sched_config(C.Structure):
     _fields_ = [("max_slots", C.c_int32), ("block_size", C.c_int32), ("num_blocks", C.c_int32),
                 ("max_blocks_per_seq", C.c_int32), ("max_rows", C.c_int32),
-                ("chunk_size", C.c_int32), ("eos_id", C.c_int32), ("policy", C.c_int32)]
+                ("chunk_size", C.c_int32), ("eos_id", C.c_int32), ("policy", C.c_int32),
+                ("pacing", C.c_int32), ("max_prefill", C.c_int32),
+                ("decode_prefill_ratio", C.c_int32), ("min_forward_seq_len", C.c_int32)]
 
 
 class cbd_plan(C.Structure):

@@ -8,6 +8,12 @@
 //     waited longest for a row go first (ties by ascending slot), so a row
 //     that does not fit waits one step and is then served -- nothing is ever
 //     evicted.
+// Other pacings (cbd_sched_config.pacing) compose the step differently:
+// CBD_PACE_ALBATROSS puts decode rows first, feeds short prompts one token
+// per step beside them, advances long prompts by a chunk only on every
+// (ratio + 1)-th step while decode rows exist, and admits no more than
+// max_prefill sequences into prefill at once; CBD_PACE_SEPARATE runs prefill
+// chunks in steps of their own, without decode rows.
 // Admission under CBD_ADMIT_RESERVE takes ceil((prompt + max_new) / block)
 // blocks up front, which guarantees that every admitted request can finish
 // (the deadlock the section describes -- all slots busy, pool empty, nobody
@@ -78,6 +84,19 @@ struct cbd_sched {
   std::deque<Finished> finished;
   int64_t steps = 0, n_finished = 0;
   bool planned = false;
+  // CBD_PACE_ALBATROSS: decode-carrying steps left before the next step
+  // that may advance a long prompt
+  int32_t seq_countdown = 0;
+  int32_t max_prefill() const {
+    return cfg.max_prefill > 0 ? cfg.max_prefill : std::max(cfg.max_slots / 8, 1);
+  }
+  int32_t ratio() const { return cfg.decode_prefill_ratio > 0 ? cfg.decode_prefill_ratio : 5; }
+  int32_t min_fwd() const { return cfg.min_forward_seq_len > 0 ? cfg.min_forward_seq_len : 10; }
+  int32_t n_prefilling() const {
+    int32_t n = 0;
+    for (const Request* r : order) n += r->prefilled < (int32_t)r->prompt.size();
+    return n;
+  }
   // the last plan
   std::vector<int32_t> p_slots, p_tables, p_ctx, p_new, p_tokens, p_want, p_step;
   std::vector<uint64_t> p_ids;
@@ -131,7 +150,9 @@ struct cbd_sched {
 
   void admit() {
     if (cfg.policy == CBD_ADMIT_REQUEST_LEVEL && !active.empty()) return;
+    int32_t prefilling = n_prefilling();
     while (!queue.empty() && slots_free() > 0) {
+      if (cfg.pacing == CBD_PACE_ALBATROSS && prefilling >= max_prefill()) break;
       Request& r = *queue.front();
       std::vector<int32_t> blocks;
       if (cfg.policy != CBD_ADMIT_FREE_SLOT) {
@@ -148,6 +169,7 @@ struct cbd_sched {
       up->slot = slot;
       up->blocks = std::move(blocks);
       order.push_back(up.get());
+      ++prefilling;
       active[slot] = std::move(up);
     }
   }
@@ -183,7 +205,9 @@ int cbd_sched_create(const cbd_sched_config* cfg, cbd_engine* engine, const int3
   if (!cfg || !out) return fail(CBD_E_INVAL, "NULL config or output");
   if (cfg->max_slots < 1 || cfg->block_size < 1 || cfg->num_blocks < 1 ||
       cfg->max_blocks_per_seq < 1 || cfg->max_rows < 1 || cfg->chunk_size < 1 ||
-      cfg->policy < CBD_ADMIT_RESERVE || cfg->policy > CBD_ADMIT_REQUEST_LEVEL)
+      cfg->policy < CBD_ADMIT_RESERVE || cfg->policy > CBD_ADMIT_REQUEST_LEVEL ||
+      cfg->pacing < CBD_PACE_PREFILL_FIRST || cfg->pacing > CBD_PACE_SEPARATE ||
+      cfg->max_prefill < 0 || cfg->decode_prefill_ratio < 0 || cfg->min_forward_seq_len < 0)
     return fail(CBD_E_INVAL, "composer config out of range");
   // With an engine, every plan the composer can make must be a step the
   // engine accepts: its sequences (at most max_slots) fit max_seqs, and a
@@ -243,29 +267,58 @@ int cbd_sched_plan(cbd_sched* s, cbd_plan* out) {
   s->p_tokens.clear(); s->p_want.clear(); s->p_step.clear(); s->p_ids.clear();
   s->p_reqs.clear();
   int32_t budget = s->cfg.max_rows, n_prefill = 0, n_decode = 0;
-  for (Request* r : s->order) {  // prefill chunks first, arrival order
-    if (budget <= 0) break;
+  const int32_t pacing = s->cfg.pacing;
+  // A prefill chunk of r: up to chunk_size rows (cut to the row budget);
+  // under CBD_ADMIT_FREE_SLOT only when its blocks can be had.
+  auto chunk = [&](Request* r, int32_t limit) {
     const int32_t left = (int32_t)r->prompt.size() - r->prefilled;
-    if (left <= 0) continue;
-    const int32_t n = std::min({s->cfg.chunk_size, left, budget});
-    if (s->cfg.policy == CBD_ADMIT_FREE_SLOT && !s->grow(*r, (int64_t)r->ctx + n)) continue;
+    const int32_t n = std::min({limit, left, budget});
+    if (n <= 0) return false;
+    if (s->cfg.policy == CBD_ADMIT_FREE_SLOT && !s->grow(*r, (int64_t)r->ctx + n)) return false;
     s->emit(*r, r->prompt.data() + r->prefilled, n, n == left);
     budget -= n;
     n_prefill += n;
-  }
-  std::vector<Request*> dec;
-  for (auto& kv : s->active)
-    if (kv.second->prefilled >= (int32_t)kv.second->prompt.size()) dec.push_back(kv.second.get());
-  std::stable_sort(dec.begin(), dec.end(), [](const Request* a, const Request* b) {
-    if (a->last_row_step != b->last_row_step) return a->last_row_step < b->last_row_step;
-    return a->slot < b->slot;
-  });
-  for (Request* r : dec) {  // then one row per decoding sequence
-    if (budget <= 0) break;
-    if (s->cfg.policy == CBD_ADMIT_FREE_SLOT && !s->grow(*r, (int64_t)r->ctx + 1)) continue;
-    s->emit(*r, &r->generated.back(), 1, true);
-    budget -= 1;
-    ++n_decode;
+    return true;
+  };
+  auto prefilling = [](const Request* r) { return r->prefilled < (int32_t)r->prompt.size(); };
+  // One row per decoding sequence while rows remain, longest-waiting first.
+  auto decode_rows = [&]() {
+    std::vector<Request*> dec;
+    for (auto& kv : s->active)
+      if (!prefilling(kv.second.get())) dec.push_back(kv.second.get());
+    std::stable_sort(dec.begin(), dec.end(), [](const Request* a, const Request* b) {
+      if (a->last_row_step != b->last_row_step) return a->last_row_step < b->last_row_step;
+      return a->slot < b->slot;
+    });
+    for (Request* r : dec) {
+      if (budget <= 0) break;
+      if (s->cfg.policy == CBD_ADMIT_FREE_SLOT && !s->grow(*r, (int64_t)r->ctx + 1)) continue;
+      s->emit(*r, &r->generated.back(), 1, true);
+      budget -= 1;
+      ++n_decode;
+    }
+  };
+  if (pacing == CBD_PACE_ALBATROSS) {
+    decode_rows();
+    for (Request* r : s->order)  // short prompts: one token per step
+      if (budget > 0 && prefilling(r) && (int32_t)r->prompt.size() < s->min_fwd()) chunk(r, 1);
+    if (s->seq_countdown == 0 || n_decode == 0) {
+      bool ran = false;
+      for (Request* r : s->order)  // long prompts: a chunk on this step
+        if (budget > 0 && prefilling(r) && (int32_t)r->prompt.size() >= s->min_fwd())
+          ran |= chunk(r, s->cfg.chunk_size);
+      if (ran && n_decode > 0) s->seq_countdown = s->ratio();
+    } else {
+      --s->seq_countdown;
+    }
+  } else if (pacing == CBD_PACE_SEPARATE) {
+    for (Request* r : s->order)
+      if (budget > 0 && prefilling(r)) chunk(r, s->cfg.chunk_size);
+    if (n_prefill == 0) decode_rows();
+  } else {  // prefill first, arrival order; then the decode rows
+    for (Request* r : s->order)
+      if (budget > 0 && prefilling(r)) chunk(r, s->cfg.chunk_size);
+    decode_rows();
   }
   out->n_seqs = (int32_t)s->p_slots.size();
   out->n_rows = (int32_t)s->p_tokens.size();

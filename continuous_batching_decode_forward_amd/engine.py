@@ -189,12 +189,16 @@ class ComposerLoop:
 
     def __init__(self, eng: Engine, *, max_rows: int, chunk_size: int, eos_id: int,
                  policy: int = B.CBD_ADMIT_RESERVE, max_slots: int | None = None,
-                 max_blocks_per_seq: int | None = None):
+                 max_blocks_per_seq: int | None = None, pacing: int = B.CBD_PACE_PREFILL_FIRST,
+                 max_prefill: int = 0, decode_prefill_ratio: int = 0,
+                 min_forward_seq_len: int = 0):
         cfg = B.cbd_sched_config()
         cfg.max_slots = max_slots or eng.cfg.max_slots
         cfg.block_size, cfg.num_blocks = eng.block_size, eng.num_blocks
         cfg.max_blocks_per_seq = max_blocks_per_seq or eng.max_blocks_per_seq
         cfg.max_rows, cfg.chunk_size, cfg.eos_id, cfg.policy = max_rows, chunk_size, eos_id, policy
+        cfg.pacing, cfg.max_prefill = pacing, max_prefill
+        cfg.decode_prefill_ratio, cfg.min_forward_seq_len = decode_prefill_ratio, min_forward_seq_len
         self.cfg, self.eng = cfg, eng
         self.handle = B.cbd_sched_create(cfg, eng.handle)
         n = B.cbd_sched_meta_ints(cfg)

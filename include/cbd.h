@@ -317,6 +317,27 @@ int cbd_profile_end(cbd_engine* e, double* total_ms, int32_t* launches);
 #define CBD_FINISH_LENGTH 2
 #define CBD_FINISH_ABORT 3
 
+/* How prefill work is paced against decode rows (step composition). */
+#define CBD_PACE_PREFILL_FIRST 0 /* Forma (Go under the hood 20.3.2): every step
+                                    takes prefill chunks first (arrival order),
+                                    then one row per decoding sequence */
+#define CBD_PACE_ALBATROSS 1     /* the Albatross worker loop (RWKV-Runner
+                                    Albatross article, worker main loop steps 4
+                                    and 5 and the pacing parameters after it):
+                                    at most max_prefill sequences in prefill at
+                                    once (admission waits otherwise); decode rows
+                                    first; prompts shorter than
+                                    min_forward_seq_len are fed one token per
+                                    step beside the decode rows; longer prompts
+                                    advance by a chunk only on every
+                                    (decode_prefill_ratio + 1)-th step while
+                                    decode rows exist (every step otherwise) */
+#define CBD_PACE_SEPARATE 2      /* prefill apart from decode (the Kestrel
+                                    engine prefills under the engine mutex,
+                                    outside the batched forward: "0.8MB 跑通
+                                    Qwen" 14-1 section 2): a step that carries
+                                    prefill chunks carries no decode rows */
+
 typedef struct cbd_sched_config {
   int32_t max_slots;
   int32_t block_size;
@@ -326,6 +347,13 @@ typedef struct cbd_sched_config {
   int32_t chunk_size; /* prefill chunk length (Forma: 512) */
   int32_t eos_id;
   int32_t policy;     /* CBD_ADMIT_* */
+  int32_t pacing;     /* CBD_PACE_* (0: prefill first) */
+  /* CBD_PACE_ALBATROSS parameters; 0 takes the article's value:
+   * max_prefill = max(floor(0.125 * max_slots), 1), decode_prefill_ratio = 5,
+   * min_forward_seq_len = 10 */
+  int32_t max_prefill;
+  int32_t decode_prefill_ratio;
+  int32_t min_forward_seq_len;
 } cbd_sched_config;
 
 /* One planned step, in host memory owned by the composer and valid until

@@ -22,6 +22,24 @@ Policy (Go under the hood, section 20.3.2, Forma's scheduler and batch):
     schedule is stalled: slots full, pool empty, no sequence can grow.
   * Request-level batching (the figure's first case): a new group is
     admitted only when the batch is empty; blocks are reserved as above.
+Pacing of prefill against decode (the step's composition), three readings:
+  * PREFILL_FIRST (Forma, Go under the hood 20.3.2): as above.
+  * ALBATROSS (RWKV-Runner Albatross article, worker main loop steps 4-5 and
+    the pacing parameters after them): no more than max_prefill sequences
+    may be in prefill at once -- admission stops there (default
+    max(floor(0.125 * slots), 1)); a step takes the decode rows first; then
+    every prompt shorter than min_forward_seq_len (default 10) advances by
+    one token (single-token prefill beside the decode rows); then, only on a
+    "sequence-prefill" step, the longer prompts advance by a chunk each. A
+    step is a sequence-prefill step when the countdown is 0 or the step has
+    no decode rows; a sequence-prefill step that ran a chunk beside decode
+    rows sets the countdown to decode_prefill_ratio (default 5), and every
+    other step with decode rows lowers it by one -- so about five decode
+    steps pass between chunks of a long prompt.
+  * SEPARATE (the Kestrel engine prefills under the engine mutex, apart from
+    the batched forward: "0.8MB 跑通 Qwen" 14-1 section 2): while any
+    admitted sequence still has prompt left, the step carries only prefill
+    chunks (arrival order); otherwise only decode rows.
 Allocators: slots go lowest free id first; blocks come from a FIFO free
 list seeded with a given order; freed blocks are appended in table order.
 Positions, ctx_len and step ids: a sequence's ctx_len counts positions
@@ -34,6 +52,7 @@ from collections import deque
 from dataclasses import dataclass, field
 
 RESERVE, FREE_SLOT, REQUEST_LEVEL = 0, 1, 2
+PREFILL_FIRST, ALBATROSS, SEPARATE = 0, 1, 2
 FINISH_EOS, FINISH_LENGTH, FINISH_ABORT = 1, 2, 3
 
 
@@ -74,7 +93,14 @@ def ceil_div(a, b):
 
 class ComposerRef:
     def __init__(self, max_slots, block_size, num_blocks, max_rows, chunk_size,
-                 eos_id, policy=RESERVE, block_order=None, max_blocks_per_seq=None):
+                 eos_id, policy=RESERVE, block_order=None, max_blocks_per_seq=None,
+                 pacing=PREFILL_FIRST, max_prefill=0, decode_prefill_ratio=0,
+                 min_forward_seq_len=0):
+        self.pacing = pacing
+        self.max_prefill = max_prefill or max(int(max_slots * 0.125), 1)
+        self.decode_prefill_ratio = decode_prefill_ratio or 5
+        self.min_forward_seq_len = min_forward_seq_len or 10
+        self.countdown = 0
         self.max_slots, self.bs, self.num_blocks = max_slots, block_size, num_blocks
         self.max_rows, self.chunk, self.eos, self.policy = max_rows, chunk_size, eos_id, policy
         self.max_blocks_per_seq = max_blocks_per_seq or num_blocks
@@ -113,6 +139,9 @@ class ComposerRef:
         if self.policy == REQUEST_LEVEL and self.active:
             return
         while self.queue and self.free_slots:
+            if self.pacing == ALBATROSS and \
+                    sum(1 for x in self.order if x.prefilled < len(x.prompt)) >= self.max_prefill:
+                break
             r = self.queue[0]
             if self.policy in (RESERVE, REQUEST_LEVEL):
                 need = ceil_div(len(r.prompt) + r.max_new, self.bs)
@@ -139,31 +168,62 @@ class ComposerRef:
     def plan(self) -> Plan:
         self._admit()
         p = Plan([], [], [], [], [], [], [], [])
-        budget = self.max_rows
-        # prefill chunks first, FCFS by arrival
-        for r in self.order:
-            if budget <= 0:
-                break
-            if r.slot < 0 or r.prefilled >= len(r.prompt):
-                continue
-            n = min(self.chunk, len(r.prompt) - r.prefilled, budget)
-            if self.policy == FREE_SLOT and not self._grow(r, r.ctx + n):
-                continue
-            done = r.prefilled + n == len(r.prompt)
-            self._emit(p, r, r.prompt[r.prefilled:r.prefilled + n], done)
-            budget -= n
-        # then one row per decoding sequence, longest-waiting first
+        self._budget = self.max_rows
+        if self.pacing == ALBATROSS:
+            n_dec = self._decode_rows(p)
+            for r in self.order:      # short prompts: one token per step
+                if len(r.prompt) < self.min_forward_seq_len:
+                    self._chunk(p, r, 1)
+            if self.countdown == 0 or n_dec == 0:
+                ran = False
+                for r in self.order:  # long prompts: a chunk on this step
+                    if len(r.prompt) >= self.min_forward_seq_len:
+                        ran = self._chunk(p, r, self.chunk) or ran
+                if ran and n_dec > 0:
+                    self.countdown = self.decode_prefill_ratio
+            else:
+                self.countdown -= 1
+        elif self.pacing == SEPARATE:
+            for r in self.order:
+                self._chunk(p, r, self.chunk)
+            if not p.n_new:
+                self._decode_rows(p)
+        else:
+            # prefill chunks first, FCFS by arrival; then the decode rows
+            for r in self.order:
+                self._chunk(p, r, self.chunk)
+            self._decode_rows(p)
+        p.stalled = (not p.n_new) and bool(self.active)
+        self.last_plan = p
+        return p
+
+    def _chunk(self, p, r, limit):
+        """A prefill chunk of r: up to `limit` prompt tokens, cut to the row
+        budget; free-slot admission takes its blocks first."""
+        left = len(r.prompt) - r.prefilled
+        n = min(limit, left, self._budget)
+        if r.slot < 0 or n <= 0:
+            return False
+        if self.policy == FREE_SLOT and not self._grow(r, r.ctx + n):
+            return False
+        self._emit(p, r, r.prompt[r.prefilled:r.prefilled + n], r.prefilled + n == len(r.prompt))
+        self._budget -= n
+        return True
+
+    def _decode_rows(self, p):
+        """One row per decoding sequence while rows remain, the sequences
+        that waited longest first (ties by slot). Returns the rows taken."""
+        taken = 0
         dec = [r for r in self.active.values() if r.prefilled >= len(r.prompt)]
         for r in sorted(dec, key=lambda r: (r.last_row_step, r.slot)):
-            if budget <= 0:
+            if self._budget <= 0:
                 break
             if self.policy == FREE_SLOT and not self._grow(r, r.ctx + 1):
                 continue
             self._emit(p, r, [r.generated[-1]], True)
-            budget -= 1
-        p.stalled = (not p.n_new) and bool(self.active)
-        self.last_plan = p
-        return p
+            self._budget -= 1
+            taken += 1
+        return taken
 
     def _emit(self, p, r, toks, want):
         r.last_row_step = self.step

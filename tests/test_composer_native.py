@@ -19,14 +19,16 @@ def fake_token(rid, pos, n_gen, eos_every):
 
 
 def run_both(requests, *, slots, bs, pool, rows, chunk, policy, mbps, order, steps=300,
-             eos_every=0):
+             eos_every=0, pacing=0, pace_args=(0, 0, 0), trace=None):
     cfg = B.cbd_sched_config()
     cfg.max_slots, cfg.block_size, cfg.num_blocks = slots, bs, pool
     cfg.max_blocks_per_seq, cfg.max_rows, cfg.chunk_size = mbps, rows, chunk
-    cfg.eos_id, cfg.policy = 0, policy
+    cfg.eos_id, cfg.policy, cfg.pacing = 0, policy, pacing
+    cfg.max_prefill, cfg.decode_prefill_ratio, cfg.min_forward_seq_len = pace_args
     nat = B.cbd_sched_create(cfg, None, order)
     ref = ComposerRef(slots, bs, pool, rows, chunk, 0, policy, block_order=list(order),
-                      max_blocks_per_seq=mbps)
+                      max_blocks_per_seq=mbps, pacing=pacing, max_prefill=pace_args[0],
+                      decode_prefill_ratio=pace_args[1], min_forward_seq_len=pace_args[2])
     pending = sorted(range(len(requests)), key=lambda i: requests[i][0])
     fin_nat, fin_ref = [], []
     try:
@@ -53,6 +55,12 @@ def run_both(requests, *, slots, bs, pool, rows, chunk, policy, mbps, order, ste
                 k = len(q.block_tables[s])
                 assert list(row[:k]) == q.block_tables[s] and np.all(row[k:] == -1)
             assert bool(p.stalled) == q.stalled
+            if trace is not None:
+                prompt_len = {i: len(requests[i][1]) for i in range(len(requests))}
+                trace.append([(q.request_ids[s], q.n_new[s], q.ctx_lens[s] < prompt_len[q.request_ids[s]],
+                               prompt_len[q.request_ids[s]])
+                              for s in range(n)] + [("prefilling", sum(
+                                  1 for r in ref.order if r.prefilled < len(r.prompt)))])
             if q.stalled:
                 return "stalled", fin_nat, fin_ref
             toks = []
@@ -140,3 +148,86 @@ def test_submit_and_commit_errors():
         assert st.free_blocks == 8 and st.free_slots == 2
     finally:
         B.cbd_sched_destroy(s)
+
+
+PACINGS = [B.CBD_PACE_PREFILL_FIRST, B.CBD_PACE_ALBATROSS, B.CBD_PACE_SEPARATE]
+
+
+def pacing_stream(seed, n=40):
+    arr = synth.uniform_ints(seed, "arrive", n, 0, 60)
+    plen = synth.uniform_ints(seed, "plen", n, 1, 70)
+    mx = synth.uniform_ints(seed, "maxnew", n, 1, 40)
+    return [(int(arr[i]), list(synth.uniform_ints(seed, f"p{i}", int(plen[i]), 1, 500)),
+             int(mx[i])) for i in range(n)]
+
+
+@pytest.mark.parametrize("seed", [4, 5])
+@pytest.mark.parametrize("pace_args", [(0, 0, 0), (3, 2, 6)])
+@pytest.mark.parametrize("pacing", PACINGS[1:])
+@pytest.mark.parametrize("policy", [B.CBD_ADMIT_RESERVE, B.CBD_ADMIT_FREE_SLOT])
+def test_pacing_policies_match_reference(seed, pace_args, pacing, policy):
+    reqs = pacing_stream(seed)
+    pool = 160
+    state, fin, _ = run_both(reqs, slots=8, bs=8, pool=pool, rows=40, chunk=16, policy=policy,
+                             mbps=20, order=list(synth.permutation(seed, "b", pool)),
+                             eos_every=9, steps=800, pacing=pacing, pace_args=pace_args)
+    if policy == B.CBD_ADMIT_RESERVE:
+        assert state == "done" and len(fin) == len(reqs)
+
+
+def test_albatross_pacing_limits_prefill_and_spaces_long_chunks():
+    """The Albatross worker's pacing: at most max_prefill sequences in
+    prefill at once; prompts under min_forward_seq_len only ever advance one
+    token per step; a long prompt's chunk runs beside decode rows at most once
+    every decode_prefill_ratio + 1 steps."""
+    reqs = pacing_stream(6, n=50)
+    trace = []
+    max_prefill, ratio, min_fwd = 2, 3, 8
+    state, fin, _ = run_both(reqs, slots=8, bs=8, pool=200, rows=40, chunk=16,
+                             policy=B.CBD_ADMIT_RESERVE, mbps=20,
+                             order=list(range(200)), steps=1500, pacing=B.CBD_PACE_ALBATROSS,
+                             pace_args=(max_prefill, ratio, min_fwd), trace=trace)
+    assert state == "done" and len(fin) == len(reqs)
+    last_long = None
+    long_steps = 0
+    for j, rows in enumerate(trace):
+        assert rows[-1][1] <= max_prefill
+        rows = rows[:-1]
+        has_decode = any(not pre for _, _, pre, _ in rows)
+        long_chunk = any(pre and plen >= min_fwd for _, _, pre, plen in rows)
+        for rid, nn, pre, plen in rows:
+            if pre and plen < min_fwd:
+                assert nn == 1
+        if long_chunk and has_decode:
+            if last_long is not None:
+                assert j - last_long >= ratio + 1, (j, last_long)
+            last_long = j
+            long_steps += 1
+    assert long_steps > 5
+
+
+def test_separate_pacing_never_mixes_prefill_and_decode():
+    reqs = pacing_stream(7)
+    trace = []
+    state, fin, _ = run_both(reqs, slots=8, bs=8, pool=160, rows=40, chunk=16,
+                             policy=B.CBD_ADMIT_RESERVE, mbps=20, order=list(range(160)),
+                             steps=1500, pacing=B.CBD_PACE_SEPARATE, trace=trace)
+    assert state == "done" and len(fin) == len(reqs)
+    for rows in trace:
+        kinds = {pre for _, _, pre, _ in rows[:-1]}
+        assert len(kinds) <= 1
+
+
+def test_pacing_config_is_checked():
+    cfg = B.cbd_sched_config()
+    cfg.max_slots, cfg.block_size, cfg.num_blocks = 2, 4, 8
+    cfg.max_blocks_per_seq, cfg.max_rows, cfg.chunk_size, cfg.eos_id = 4, 8, 8, 0
+    for field, value in (("pacing", 3), ("pacing", -1), ("max_prefill", -1),
+                         ("decode_prefill_ratio", -2), ("min_forward_seq_len", -1)):
+        bad = B.cbd_sched_config()
+        for k, _ in B.cbd_sched_config._fields_:
+            setattr(bad, k, getattr(cfg, k))
+        setattr(bad, field, value)
+        with pytest.raises(B.CbdError) as ei:
+            B.cbd_sched_create(bad, None, None)
+        assert ei.value.code == B.CBD_E_INVAL
