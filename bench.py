@@ -281,10 +281,7 @@ def run_sampled(steps, warmup):
         f"({wl['total'] * shape.kv_bytes_per_pos * wl['bs'] / 1e9:.1f} GB)")
     fill_pool(eng, seed, wl["perm"])
     sp = wlc.sampling
-    params = B.cbd_sampling()
-    params.temperature, params.top_p, params.top_k = sp.temperature, sp.top_p, sp.top_k
-    params.freq_penalty, params.presence_penalty = sp.freq_penalty, sp.presence_penalty
-    params.penalty_decay, params.seed = sp.penalty_decay, sp.seed
+    params = B.cbd_sampling.from_params(sp)
     slots = [B.cbd_slot_alloc(eng.handle, params, r) for r in range(Bn)]
     counts0 = torch.from_numpy(penalty_history(seed, Bn, shape.vocab, 64, sp.penalty_decay))
     counts0 = counts0.to("cuda")

@@ -84,10 +84,27 @@ class cbd_weights(C.Structure):
                 ("w_down", C.POINTER(VP))]
 
 
+CBD_MAX_FORBIDDEN = 8
+
+
 class cbd_sampling(C.Structure):
     _fields_ = [("temperature", C.c_float), ("top_p", C.c_float), ("top_k", C.c_int32),
                 ("freq_penalty", C.c_float), ("presence_penalty", C.c_float),
-                ("penalty_decay", C.c_float), ("seed", C.c_uint64)]
+                ("penalty_decay", C.c_float), ("seed", C.c_uint64),
+                ("n_forbidden", C.c_int32), ("forbidden", C.c_int32 * CBD_MAX_FORBIDDEN)]
+
+    @classmethod
+    def from_params(cls, sp) -> "cbd_sampling":
+        """From any object with the fields' names (forbidden: a sequence)."""
+        c = cls()
+        c.temperature, c.top_p, c.top_k = sp.temperature, sp.top_p, sp.top_k
+        c.freq_penalty, c.presence_penalty = sp.freq_penalty, sp.presence_penalty
+        c.penalty_decay, c.seed = sp.penalty_decay, sp.seed
+        ids = list(getattr(sp, "forbidden", ()))
+        c.n_forbidden = len(ids)
+        for i, t in enumerate(ids):
+            c.forbidden[i] = int(t)
+        return c
 
 
 class cbd_step(C.Structure):

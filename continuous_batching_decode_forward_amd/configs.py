@@ -50,6 +50,7 @@ class SamplingParams:
     presence_penalty: float = 0.0
     penalty_decay: float = 0.996
     seed: int = 0
+    forbidden: tuple = ()  # ids the sampler never draws
 
 
 @dataclass(frozen=True)

@@ -329,14 +329,36 @@ int cbd_engine_destroy(cbd_engine* e) {
 
 int cbd_slot_alloc(cbd_engine* e, const cbd_sampling* p, uint64_t request_id, int32_t* slot_out) {
   if (!e || !slot_out) return fail(CBD_E_INVAL, "NULL engine or output");
-  cbd_sampling sp = p ? *p : cbd_sampling{0.f, 1.f, 0, 0.f, 0.f, 1.f, 0};
+  cbd_sampling sp{};
+  if (p) {
+    sp = *p;
+  } else {
+    sp.temperature = 0.f;
+    sp.top_p = 1.f;
+    sp.penalty_decay = 1.f;
+  }
   if (!(sp.temperature >= 0.f) || sp.top_k < 0 || !(sp.penalty_decay >= 0.f))
     return fail(CBD_E_INVAL, "sampling parameters out of range");
+  static_assert(CBD_MAX_FORBIDDEN == SLOT_MAX_FORBIDDEN, "forbidden-id capacity");
+  if (sp.n_forbidden < 0 || sp.n_forbidden > CBD_MAX_FORBIDDEN)
+    return fail(CBD_E_INVAL, "n_forbidden out of range");
+  for (int i = 0; i < sp.n_forbidden; ++i)
+    if (sp.forbidden[i] < 0 || sp.forbidden[i] >= e->cfg.vocab)
+      return fail(CBD_E_INVAL, "a forbidden id is outside the vocabulary");
   int32_t s = e->slots.alloc();
   if (s < 0) return fail(CBD_E_NOSLOT, "every slot is taken");
   SlotParams& hp = e->host_params[(size_t)s];
-  hp = SlotParams{sp.temperature, sp.top_p, sp.top_k, sp.freq_penalty, sp.presence_penalty,
-                  sp.penalty_decay, sp.seed, request_id};
+  hp = SlotParams{};
+  hp.temperature = sp.temperature;
+  hp.top_p = sp.top_p;
+  hp.top_k = sp.top_k;
+  hp.freq_penalty = sp.freq_penalty;
+  hp.presence_penalty = sp.presence_penalty;
+  hp.penalty_decay = sp.penalty_decay;
+  hp.seed = sp.seed;
+  hp.request_id = request_id;
+  hp.n_forbidden = sp.n_forbidden;
+  for (int i = 0; i < sp.n_forbidden; ++i) hp.forbidden[i] = sp.forbidden[i];
   hipError_t he = hipMemcpyAsync(e->slot_state + e->sl.params + (size_t)s * sizeof(SlotParams),
                                  &hp, sizeof(SlotParams), hipMemcpyHostToDevice, e->stream);
   if (he == hipSuccess)

@@ -163,13 +163,18 @@ hipError_t launch_argmax_reduce(const float* amax_val, const int32_t* amax_idx, 
 // ------------------------------------------------------------------ sampler
 
 // Per-slot sampler state in the caller's slot buffer.
+#define SLOT_MAX_FORBIDDEN 8
 struct SlotParams {
   float temperature, top_p;
   int32_t top_k;
   float freq_penalty, presence_penalty, penalty_decay;
   uint64_t seed;
   uint64_t request_id;
+  int32_t n_forbidden;
+  int32_t forbidden[SLOT_MAX_FORBIDDEN];  // ids whose penalised logit is -inf
+  int32_t pad_;
 };
+static_assert(sizeof(SlotParams) == 80, "slot parameter layout");
 
 // Floats of sampler scratch per row for a vocabulary of V.
 int32_t sampler_row_floats(int32_t V);

@@ -406,6 +406,8 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
           const float c = cv[u];
           float l = lv[u] - mul_rounded(P.freq_penalty, c);
           if (c > 0.f) l = l - P.presence_penalty;
+          for (int f = 0; f < P.n_forbidden; ++f)  // forbidden ids: never drawn
+            if (id == P.forbidden[f]) l = -INFINITY;
           z = P.temperature == 0.f ? l : l / P.temperature;
         }
         e.set(k, id, z);

@@ -141,7 +141,7 @@ class Engine:
     def slot_counts(self) -> torch.Tensor:
         """The per-slot penalty counts [max_slots][vocab] fp32 (a view)."""
         s = self.cfg
-        params_bytes = (s.max_slots * 40 + 255) // 256 * 256
+        params_bytes = (s.max_slots * 80 + 255) // 256 * 256  # 80-byte slot parameters
         return self.slot_state[params_bytes:params_bytes + s.max_slots * s.vocab * 4].view(
             torch.float32).view(s.max_slots, s.vocab)
 

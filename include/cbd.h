@@ -111,7 +111,13 @@ typedef struct cbd_weights {
 } cbd_weights;
 
 /* Per-slot sampling parameters (Albatross adapter defaults: temperature
- * 1.0, top_p 0.3, top_k 0, frequency penalty 1, penalty decay 0.996). */
+ * 1.0, top_p 0.3, top_k 0, frequency penalty 1, penalty decay 0.996).
+ * Forbidden ids (the Albatross worker masks forbidden tokens on the decode
+ * segment before the penalties and the draw, worker main loop step 6): the
+ * sampler sets their penalised logits to -infinity, so they are never drawn
+ * (and never the greedy pick of temperature 0). Up to CBD_MAX_FORBIDDEN ids
+ * in [0, vocab); the greedy step mode (CBD_MODE_GREEDY) does not read them. */
+#define CBD_MAX_FORBIDDEN 8
 typedef struct cbd_sampling {
   float temperature;      /* 0 = greedy on the penalised logits */
   float top_p;            /* >= 1 disables top-p */
@@ -120,6 +126,8 @@ typedef struct cbd_sampling {
   float presence_penalty;
   float penalty_decay;
   uint64_t seed;          /* key of the counter-based draw */
+  int32_t n_forbidden;    /* 0 .. CBD_MAX_FORBIDDEN */
+  int32_t forbidden[CBD_MAX_FORBIDDEN];
 } cbd_sampling;
 
 /* Buffer sizes for a configuration (bytes). The KV pool layout is
@@ -160,7 +168,8 @@ int cbd_engine_destroy(cbd_engine* e);
  * and the sampling parameters; the Albatross worker keeps them as
  * preallocated per-slot tensors). cbd_slot_alloc returns the lowest free
  * slot id, stores params and request_id (the draw's counter) and enqueues a
- * reset of the slot's counts to zero on the engine stream.
+ * reset of the slot's counts to zero on the engine stream. CBD_E_INVAL for
+ * a negative temperature, top_k or decay, or forbidden ids out of range.
  * cbd_slot_free may be called at any step boundary (a request aborted by
  * its client stops alone). */
 int cbd_slot_alloc(cbd_engine* e, const cbd_sampling* params, uint64_t request_id,

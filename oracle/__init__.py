@@ -65,7 +65,8 @@ class OrModel(C.Structure):
 class OrSampling(C.Structure):
     _fields_ = [("temperature", C.c_float), ("top_p", C.c_float), ("top_k", C.c_int32),
                 ("freq_penalty", C.c_float), ("presence_penalty", C.c_float),
-                ("penalty_decay", C.c_float), ("seed", C.c_uint64)]
+                ("penalty_decay", C.c_float), ("seed", C.c_uint64),
+                ("n_forbidden", C.c_int32), ("forbidden", C.c_int32 * 8)]
 
 
 class OrSampleInfo(C.Structure):
@@ -279,6 +280,11 @@ def sampling_struct(sp) -> OrSampling:
     s.temperature, s.top_p, s.top_k = sp.temperature, sp.top_p, sp.top_k
     s.freq_penalty, s.presence_penalty = sp.freq_penalty, sp.presence_penalty
     s.penalty_decay, s.seed = sp.penalty_decay, sp.seed
+    ids = list(getattr(sp, "forbidden", ()))
+    assert len(ids) <= 8
+    s.n_forbidden = len(ids)
+    for i, t in enumerate(ids):
+        s.forbidden[i] = int(t)
     return s
 
 

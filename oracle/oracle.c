@@ -564,11 +564,14 @@ float or_uniform24(uint64_t seed, uint64_t request_id, uint32_t step_id) {
 
 /* ------------------------------------------------------------ sampler */
 
+#define OR_MAX_FORBIDDEN 8
 typedef struct {
   float temperature, top_p;
   int32_t top_k;
   float freq_penalty, presence_penalty, penalty_decay;
   uint64_t seed;
+  int32_t n_forbidden;               /* ids never drawn: their l' is -inf */
+  int32_t forbidden[OR_MAX_FORBIDDEN];
 } or_sampling;
 
 /* What decided the draw; lets a comparison skip rows whose outcome sits
@@ -604,7 +607,9 @@ static int cmp_desc(const void* a, const void* b) {
 }
 
 /* One row of the batched sampler, in this order:
- *  S1 penalty   l' = l - f*c - q*[c > 0]                       (fp32)
+ *  S1 penalty   l' = l - f*c - q*[c > 0]                       (fp32);
+ *               a forbidden id's l' is -inf (the Albatross worker masks
+ *               forbidden tokens before the penalties and the draw)
  *  S2 T == 0    greedy on l' (lowest id); else z = l' / T       (fp32)
  *  S3 softmax   e = exp(z - max z), unnormalised               (fp32)
  *  S4 top-k     keep the k largest by (e desc, id asc) when 0 < k < V
@@ -638,6 +643,8 @@ int32_t or_sample_f32(const float* logits, int32_t V, float* counts,
     }
     lp[v] = l;
   }
+  for (int32_t f = 0; f < sp->n_forbidden && f < OR_MAX_FORBIDDEN; ++f)
+    if (sp->forbidden[f] >= 0 && sp->forbidden[f] < V) lp[sp->forbidden[f]] = -INFINITY;
   int32_t token;
   if (sp->temperature == 0.0f) {
     token = or_argmax_f32(lp, V);

@@ -114,3 +114,24 @@ def test_composer_rejects_an_engine_it_could_overrun(eng):
         with pytest.raises(B.CbdError) as ei:
             B.cbd_sched_create(bad, e.handle)
         assert ei.value.code == B.CBD_E_INVAL, field
+
+
+def test_slot_alloc_checks_the_forbidden_ids(eng):
+    e, _ = eng
+    h = e.handle
+    for n, ids in ((9, [1] * 8), (1, [configs.TINY.vocab]), (2, [3, -1]), (-1, [])):
+        c = B.cbd_sampling()
+        c.temperature, c.top_p, c.penalty_decay = 1.0, 1.0, 1.0
+        c.n_forbidden = n
+        for i, t in enumerate(ids[:8]):
+            c.forbidden[i] = t
+        with pytest.raises(B.CbdError) as ei:
+            B.cbd_slot_alloc(h, c, 1)
+        assert ei.value.code == B.CBD_E_INVAL
+    c = B.cbd_sampling()
+    c.temperature, c.top_p, c.penalty_decay, c.n_forbidden = 1.0, 1.0, 1.0, 8
+    for i in range(8):
+        c.forbidden[i] = configs.TINY.vocab - 1 - i
+    s = B.cbd_slot_alloc(h, c, 2)
+    B.cbd_slot_free(h, s)
+    torch.cuda.synchronize()

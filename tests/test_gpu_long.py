@@ -70,10 +70,7 @@ def test_sampled_b256_long_contexts():
     try:
         bench.fill_pool(eng, seed, wl["perm"])
         sp = WL.sampling
-        params = B.cbd_sampling()
-        params.temperature, params.top_p, params.top_k = sp.temperature, sp.top_p, sp.top_k
-        params.freq_penalty, params.presence_penalty = sp.freq_penalty, sp.presence_penalty
-        params.penalty_decay, params.seed = sp.penalty_decay, sp.seed
+        params = B.cbd_sampling.from_params(sp)
         slots = [B.cbd_slot_alloc(eng.handle, params, r) for r in range(Bn)]
         c0 = bench.penalty_history(seed, Bn, SHAPE.vocab, 64, sp.penalty_decay)
         eng.slot_counts()[slots] = torch.from_numpy(c0).cuda()

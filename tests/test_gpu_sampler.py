@@ -1,7 +1,8 @@
 """GPU parity of the batched sampler on identical fp32 logits (vocab 65536,
 whose rows the kernel holds on chip, and 151936, whose rows it keeps in the
 workspace; temperature 1.0, top_p 0.3, top_k 0, frequency penalty 1.0, decay
-0.996 and variants), against the oracle's fp32 sampler. Token ids must agree wherever
+0.996 and variants, some rows with forbidden ids), against the oracle's fp32
+sampler. Token ids must agree wherever
 the draw is not within 1e-3 (relative mass) of a boundary that decides it:
 the chosen id's CDF interval and the top-p cut. The penalty counts after the
 update must agree bit for bit on rows whose tokens agree."""
@@ -87,14 +88,15 @@ def test_sampler_matches_oracle_on_identical_logits(engine, engine_wide, vocab, 
             counts[i] *= np.float32(0.996)
             counts[i, t] += np.float32(1.0)
     params = [VARIANTS[i % len(VARIANTS)] for i in range(n)]
+    # every fifth row forbids the three ids of its largest logits (and id 0),
+    # under the base parameters or greedy: the masked ids must never come out
+    for i in range(0, n, 5):
+        top3 = tuple(int(t) for t in np.argsort(-logits[i].astype(np.float64), kind="stable")[:3])
+        params[i] = replace(params[i] if i % 2 else replace(BASE, temperature=0.0),
+                            forbidden=(0,) + top3)
     slots = []
     for i in range(n):
-        sp = params[i]
-        c = B.cbd_sampling()
-        c.temperature, c.top_p, c.top_k = sp.temperature, sp.top_p, sp.top_k
-        c.freq_penalty, c.presence_penalty = sp.freq_penalty, sp.presence_penalty
-        c.penalty_decay, c.seed = sp.penalty_decay, sp.seed
-        slots.append(B.cbd_slot_alloc(engine.handle, c, i))
+        slots.append(B.cbd_slot_alloc(engine.handle, B.cbd_sampling.from_params(params[i]), i))
     torch.cuda.synchronize()
     cview = engine.slot_counts()
     cview[torch.tensor(slots, device="cuda").long()] = torch.from_numpy(counts).cuda()
@@ -120,6 +122,7 @@ def test_sampler_matches_oracle_on_identical_logits(engine, engine_wide, vocab, 
         if g_tok[i] == tok:
             agree += 1
             assert np.array_equal(g_counts[i], c), f"row {i}: counts differ"
+        assert g_tok[i] not in params[i].forbidden, f"row {i} drew a forbidden id"
     print(f"sampler rows decidable (vocab {V_}): {checked} of {n}")
     # flat kept sets (top_p 1.0 or 0.9) have ids worth ~1e-5 of the mass each,
     # so many of their draws land within the bound of an interval edge

@@ -143,3 +143,39 @@ def test_penalised_distribution():
     pen = lg.astype(np.float64) - 0.5 * counts - 0.25 * (counts > 0)
     ok, stat = chi2_ok(toks, softmax(pen))
     assert ok, stat
+
+
+def test_forbidden_ids_are_masked_before_the_draw():
+    """Forbidden ids (the Albatross worker masks forbidden tokens before the
+    penalties and the draw): forbidding the greedy pick makes temperature 0,
+    top_k 1 and a tiny top_p pick the best remaining id; unrestricted draws
+    follow the softmax renormalised over the allowed ids and never return a
+    forbidden one."""
+    rng = np.random.default_rng(3)
+    lg = rng.standard_normal(3000).astype(np.float32)
+    order = np.argsort(-lg.astype(np.float64), kind="stable")
+    forbid = (int(order[0]), int(order[1]))
+    for sp in (replace(PLAIN, top_k=1), replace(PLAIN, top_p=1e-7),
+               replace(PLAIN, temperature=0.0)):
+        sp = replace(sp, forbidden=forbid)
+        for step in range(10):
+            tok, _ = O.sample(lg, None, sp, 1, step)
+            assert tok == int(order[2])
+    small = np.array([0.3, -1.0, 2.0, 0.0, 1.1, -0.2], np.float32)
+    sp = replace(PLAIN, forbidden=(2, 4))
+    p = softmax(small.astype(np.float64))
+    p[[2, 4]] = 0.0
+    p /= p.sum()
+    toks = draws(small, sp, n=12000)
+    assert not np.isin(toks, [2, 4]).any()
+    ok, stat = chi2_ok(toks, p)
+    assert ok, stat
+    # penalties still apply to the allowed ids, and counts still decay and
+    # count the drawn token
+    c = np.zeros(6, np.float32)
+    c[0] = 3.0
+    sp2 = replace(PLAIN, temperature=0.0, freq_penalty=10.0, penalty_decay=0.5,
+                  forbidden=(2, 4))
+    tok, _ = O.sample(small, c, sp2, 1, 0)
+    assert tok == 3  # 0.3 - 30 for id 0; ids 2 and 4 masked; then 0.0 at id 3
+    assert c[0] == np.float32(1.5) and c[3] == np.float32(1.0)
