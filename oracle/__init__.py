@@ -53,13 +53,14 @@ U64P = C.POINTER(C.c_uint64)
 class OrModel(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
-                ("vocab", C.c_int32), ("pad_", C.c_int32),
+                ("vocab", C.c_int32), ("kv_fp8", C.c_int32),
                 ("rms_eps", C.c_double), ("rope_base", C.c_double),
                 ("embed", U16P), ("final_norm", U16P), ("lm_head", U16P),
                 ("attn_norm", C.POINTER(U16P)), ("w_qkv", C.POINTER(U16P)),
                 ("w_o", C.POINTER(U16P)), ("ffn_norm", C.POINTER(U16P)),
                 ("w_gate", C.POINTER(U16P)), ("w_up", C.POINTER(U16P)),
-                ("w_down", C.POINTER(U16P))]
+                ("w_down", C.POINTER(U16P)),
+                ("k_scale", C.c_double), ("v_scale", C.c_double)]
 
 
 class OrSampling(C.Structure):
@@ -91,10 +92,17 @@ def _declare(L):
     L.or_rope.argtypes = [F64P, C.c_int32, C.c_int32, C.c_double]
     L.or_attention_dense.argtypes = [F64P, U16P, U16P, C.c_int32, C.c_int32, C.c_int32,
                                      C.c_int32, F64P]
-    L.or_serial_forward.argtypes = [C.POINTER(OrModel), U16P, C.c_int32, I32P, C.c_int32,
+    L.or_attention_dense_kv.argtypes = [F64P, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                        C.c_int32, C.c_int32, C.c_int32, C.c_double,
+                                        C.c_double, F64P]
+    L.or_serial_forward.argtypes = [C.POINTER(OrModel), C.c_void_p, C.c_int32, I32P, C.c_int32,
                                     C.c_int32, C.c_int32, F64P]
-    L.or_paged_step.argtypes = [C.POINTER(OrModel), U16P, C.c_int32, C.c_int32, C.c_int32,
+    L.or_paged_step.argtypes = [C.POINTER(OrModel), C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                 I32P, C.c_int32, I32P, I32P, I32P, I32P, F64P, I32P]
+    L.or_e4m3_to_f64.argtypes = [C.c_uint8]
+    L.or_e4m3_to_f64.restype = C.c_double
+    L.or_f64_to_e4m3.argtypes = [C.c_double]
+    L.or_f64_to_e4m3.restype = C.c_uint8
     L.or_argmax_f32.argtypes = [F32P, C.c_int32]
     L.or_argmax_f32.restype = C.c_int32
     L.or_argmax_f64.argtypes = [F64P, C.c_int32]
@@ -133,8 +141,11 @@ class Model:
     """Holds the oracle's view of a weight set (uint16 bf16 arrays) and the
     ctypes struct pointing at them. Keep the object alive while in use."""
 
-    def __init__(self, shape, weights: dict):
+    def __init__(self, shape, weights: dict, kv_fp8: bool = False, k_scale: float = 1.0,
+                 v_scale: float = 1.0):
+        """kv_fp8: the KV cache holds E4M3 codes of value / scale (else bf16)."""
         self.shape = shape
+        self.kv_fp8 = bool(kv_fp8)
         self.arrays = {}
         for k, v in weights.items():
             self.arrays[k] = [as_u16(x) for x in v] if isinstance(v, list) else as_u16(v)
@@ -142,6 +153,7 @@ class Model:
         m.n_layers, m.d_model, m.n_heads = shape.n_layers, shape.d_model, shape.n_heads
         m.n_kv_heads, m.head_dim, m.ffn_dim = shape.n_kv_heads, shape.head_dim, shape.ffn_dim
         m.vocab, m.rms_eps, m.rope_base = shape.vocab, shape.rms_eps, shape.rope_base
+        m.kv_fp8, m.k_scale, m.v_scale = int(self.kv_fp8), float(k_scale), float(v_scale)
         m.embed = _p(self.arrays["embed"], U16P)
         m.final_norm = _p(self.arrays["final_norm"], U16P)
         m.lm_head = _p(self.arrays["lm_head"], U16P)
@@ -152,14 +164,18 @@ class Model:
             setattr(m, k, C.cast(arr, C.POINTER(U16P)))
         self.struct = m
 
+    @property
+    def kv_dtype(self):
+        return np.uint8 if self.kv_fp8 else np.uint16
+
     def dense_kv(self, max_pos: int) -> np.ndarray:
         s = self.shape
-        return np.zeros((s.n_layers, 2, max_pos, s.n_kv_heads, s.head_dim), np.uint16)
+        return np.zeros((s.n_layers, 2, max_pos, s.n_kv_heads, s.head_dim), self.kv_dtype)
 
     def paged_pool(self, num_blocks: int, block_size: int) -> np.ndarray:
         s = self.shape
         return np.zeros((s.n_layers, 2, num_blocks, block_size, s.n_kv_heads, s.head_dim),
-                        np.uint16)
+                        self.kv_dtype)
 
 
 def serial_forward(model: Model, kv_dense: np.ndarray, tokens, start_pos: int,
@@ -170,7 +186,8 @@ def serial_forward(model: Model, kv_dense: np.ndarray, tokens, start_pos: int,
     n = len(toks)
     V = model.shape.vocab
     out = np.empty((V,) if last_only else (n, V), np.float64)
-    rc = lib().or_serial_forward(C.byref(model.struct), _p(kv_dense, U16P), kv_dense.shape[2],
+    assert kv_dense.dtype == model.kv_dtype and kv_dense.flags["C_CONTIGUOUS"]
+    rc = lib().or_serial_forward(C.byref(model.struct), kv_dense.ctypes.data, kv_dense.shape[2],
                                  _p(toks, I32P), n, start_pos, int(last_only), _p(out, F64P))
     if rc != 0:
         raise ValueError(f"or_serial_forward failed ({rc})")
@@ -190,7 +207,8 @@ def paged_step(model: Model, pool: np.ndarray, block_tables: np.ndarray, ctx_len
     V = model.shape.vocab
     logits = np.empty((max(n_out, 1), V), np.float64)
     greedy = np.empty(max(n_out, 1), np.int32)
-    rc = lib().or_paged_step(C.byref(model.struct), _p(pool, U16P), pool.shape[2], pool.shape[3],
+    assert pool.dtype == model.kv_dtype and pool.flags["C_CONTIGUOUS"]
+    rc = lib().or_paged_step(C.byref(model.struct), pool.ctypes.data, pool.shape[2], pool.shape[3],
                              len(ctx), _p(bt, I32P), bt.shape[1], _p(ctx, I32P), _p(nn, I32P),
                              _p(tk, I32P), _p(wt, I32P), _p(logits, F64P), _p(greedy, I32P))
     if rc != 0:
@@ -237,6 +255,29 @@ def attention_dense(q, K, V, n_heads: int, n_kv_heads: int, head_dim: int) -> np
     if rc != 0:
         raise ValueError("or_attention_dense failed")
     return out
+
+
+def attention_dense_fp8(q, K, V, n_heads: int, n_kv_heads: int, head_dim: int,
+                        k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """q [Hq*hd] double, K/V [n][Hkv][hd] E4M3 codes of value / scale."""
+    q = _f64(q)
+    K = np.ascontiguousarray(K, dtype=np.uint8)
+    V = np.ascontiguousarray(V, dtype=np.uint8)
+    out = np.empty(n_heads * head_dim, np.float64)
+    rc = lib().or_attention_dense_kv(_p(q, F64P), K.ctypes.data, V.ctypes.data, K.shape[0],
+                                     n_heads, n_kv_heads, head_dim, 1, k_scale, v_scale,
+                                     _p(out, F64P))
+    if rc != 0:
+        raise ValueError("or_attention_dense_kv failed")
+    return out
+
+
+def e4m3_to_float(code: int) -> float:
+    return lib().or_e4m3_to_f64(int(code))
+
+
+def float_to_e4m3(x: float) -> int:
+    return lib().or_f64_to_e4m3(float(x))
 
 
 def bf16_round(x) -> np.ndarray:

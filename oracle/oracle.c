@@ -102,11 +102,48 @@ uint16_t or_f64_to_bf16(double x) {
 static inline double bf(uint16_t h) { return or_bf16_to_f64(h); }
 static inline uint16_t tobf(double x) { return or_f64_to_bf16(x); }
 
+/* ------------------------------------------------------------ fp8 e4m3 */
+
+/* The OCP 8-bit float E4M3 (the KV-cache quantisation the "Continuous
+ * Batching" practice article recommends, section 6): 1 sign bit, 4 exponent
+ * bits (bias 7), 3 mantissa bits. Exponent field 0 holds the subnormals
+ * m * 2^-9; exponent field 15 with mantissa 7 is NaN; there is no infinity,
+ * and the largest magnitude is 1.75 * 2^8 = 448. */
+double or_e4m3_to_f64(uint8_t c) {
+  int e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = m * ldexp(1.0, -9);
+  else
+    v = (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+  return (c & 0x80) ? -v : v;
+}
+
+/* double -> E4M3: the finite code nearest to x (on a tie the code with an
+ * even mantissa), so magnitudes beyond 448 saturate to 448; NaN -> 0x7f.
+ * Found by comparing |x| with every non-negative finite code. */
+uint8_t or_f64_to_e4m3(double x) {
+  if (isnan(x)) return 0x7f;
+  const uint8_t sign = signbit(x) ? 0x80 : 0;
+  const double a = fabs(x);
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c < 0x7f; ++c) {
+    const double d = fabs(a - or_e4m3_to_f64((uint8_t)c));
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
 /* ------------------------------------------------------------ the model */
 
 typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
-  int32_t pad_;
+  int32_t kv_fp8; /* 0: the KV cache holds bf16; 1: E4M3 codes of value / scale */
   double rms_eps, rope_base;
   const uint16_t* embed;      /* [vocab][d_model] */
   const uint16_t* final_norm; /* [d_model] */
@@ -118,6 +155,7 @@ typedef struct {
   const uint16_t* const* w_gate;    /* per layer [ffn][d_model] */
   const uint16_t* const* w_up;      /* per layer [ffn][d_model] */
   const uint16_t* const* w_down;    /* per layer [d_model][ffn] */
+  double k_scale, v_scale;          /* fp8 cache: value = decode(code) * scale */
 } or_model;
 
 /* RMSNorm: y_i = x_i / sqrt(mean(x^2) + eps) * g_i. */
@@ -152,16 +190,28 @@ void or_rope(double* v, int32_t hd, int32_t pos, double base) {
   }
 }
 
+/* How the cache stores one K or V vector: bf16 values, or E4M3 codes of
+ * value / scale. */
+typedef struct {
+  int32_t fp8;
+  double k_scale, v_scale;
+} or_kvfmt;
+
+static inline double kv_elem(const void* p, int32_t i, int32_t fp8, double scale) {
+  if (fp8) return or_e4m3_to_f64(((const uint8_t*)p)[i]) * scale;
+  return bf(((const uint16_t*)p)[i]);
+}
+
 /* One query head over n keys: softmax(q.k_j / sqrt(hd)) weighted sum of v_j.
- * keys[j] / vals[j] point at hd bf16 values each. */
-static void attend_head(const double* q, const uint16_t* const* keys,
-                        const uint16_t* const* vals, int32_t n, int32_t hd,
-                        double* s /* scratch [n] */, double* out) {
+ * keys[j] / vals[j] point at hd stored values each (format f). */
+static void attend_head(const double* q, const void* const* keys, const void* const* vals,
+                        int32_t n, int32_t hd, or_kvfmt f, double* s /* scratch [n] */,
+                        double* out) {
   double scale = 1.0 / sqrt((double)hd);
   double m = -INFINITY;
   for (int32_t j = 0; j < n; ++j) {
     double dot = 0.0;
-    for (int32_t i = 0; i < hd; ++i) dot += q[i] * bf(keys[j][i]);
+    for (int32_t i = 0; i < hd; ++i) dot += q[i] * kv_elem(keys[j], i, f.fp8, f.k_scale);
     s[j] = dot * scale;
     if (s[j] > m) m = s[j];
   }
@@ -172,31 +222,40 @@ static void attend_head(const double* q, const uint16_t* const* keys,
   }
   for (int32_t i = 0; i < hd; ++i) {
     double acc = 0.0;
-    for (int32_t j = 0; j < n; ++j) acc += s[j] * bf(vals[j][i]);
+    for (int32_t j = 0; j < n; ++j) acc += s[j] * kv_elem(vals[j], i, f.fp8, f.v_scale);
     out[i] = acc / den;
   }
 }
 
-/* Dense attention for tests: q [Hq][hd] (double), K/V [n][Hkv][hd] bf16;
- * query head h reads KV head h*Hkv/Hq (query heads grouped contiguously). */
-int or_attention_dense(const double* q, const uint16_t* K, const uint16_t* V, int32_t n,
-                       int32_t n_heads, int32_t n_kv_heads, int32_t hd, double* out) {
+/* Dense attention for tests: q [Hq][hd] (double), K/V [n][Hkv][hd] stored
+ * values (fp8 = 0: bf16; 1: E4M3 codes of value / scale); query head h
+ * reads KV head h*Hkv/Hq (query heads grouped contiguously). */
+int or_attention_dense_kv(const double* q, const void* K, const void* V, int32_t n,
+                          int32_t n_heads, int32_t n_kv_heads, int32_t hd, int32_t fp8,
+                          double k_scale, double v_scale, double* out) {
   if (n <= 0 || n_heads % n_kv_heads) return OR_EINVAL;
-  const uint16_t** kp = malloc(sizeof(*kp) * (size_t)n);
-  const uint16_t** vp = malloc(sizeof(*vp) * (size_t)n);
+  const size_t esz = fp8 ? 1 : 2;
+  or_kvfmt f = {fp8, k_scale, v_scale};
+  const void** kp = malloc(sizeof(*kp) * (size_t)n);
+  const void** vp = malloc(sizeof(*vp) * (size_t)n);
   double* s = malloc(sizeof(double) * (size_t)n);
   for (int32_t h = 0; h < n_heads; ++h) {
     int32_t g = h * n_kv_heads / n_heads;
     for (int32_t j = 0; j < n; ++j) {
-      kp[j] = K + ((size_t)j * n_kv_heads + g) * hd;
-      vp[j] = V + ((size_t)j * n_kv_heads + g) * hd;
+      kp[j] = (const uint8_t*)K + ((size_t)j * n_kv_heads + g) * hd * esz;
+      vp[j] = (const uint8_t*)V + ((size_t)j * n_kv_heads + g) * hd * esz;
     }
-    attend_head(q + (size_t)h * hd, kp, vp, n, hd, s, out + (size_t)h * hd);
+    attend_head(q + (size_t)h * hd, kp, vp, n, hd, f, s, out + (size_t)h * hd);
   }
   free(kp);
   free(vp);
   free(s);
   return OR_OK;
+}
+
+int or_attention_dense(const double* q, const uint16_t* K, const uint16_t* V, int32_t n,
+                       int32_t n_heads, int32_t n_kv_heads, int32_t hd, double* out) {
+  return or_attention_dense_kv(q, K, V, n, n_heads, n_kv_heads, hd, 0, 1.0, 1.0, out);
 }
 
 /* ------------------------------------------------------- KV addressing */
@@ -208,22 +267,23 @@ int or_attention_dense(const double* q, const uint16_t* K, const uint16_t* V, in
 typedef struct {
   int32_t paged;
   int32_t max_pos;    /* dense */
-  uint16_t* base;     /* dense store or pool */
+  void* base;         /* dense store or pool (bf16 values, or fp8 codes) */
   int32_t num_blocks; /* paged */
   int32_t block_size; /* paged */
   const int32_t* table;
   int32_t table_len;
 } or_kv;
 
-static uint16_t* kv_at(const or_model* m, const or_kv* kv, int32_t layer,
-                       int32_t kind, int32_t pos, int32_t g) {
+static void* kv_at(const or_model* m, const or_kv* kv, int32_t layer, int32_t kind,
+                   int32_t pos, int32_t g) {
   size_t vec = (size_t)m->n_kv_heads * m->head_dim;
+  const size_t esz = m->kv_fp8 ? 1 : 2;  /* bytes per stored value */
   if (pos < 0) return NULL;
   if (!kv->paged) {
     if (pos >= kv->max_pos) return NULL;
     size_t off = (((size_t)layer * 2 + kind) * kv->max_pos + pos) * vec +
                  (size_t)g * m->head_dim;
-    return kv->base + off;
+    return (uint8_t*)kv->base + off * esz;
   }
   int32_t bi = pos / kv->block_size;
   if (bi >= kv->table_len) return NULL;
@@ -232,7 +292,12 @@ static uint16_t* kv_at(const or_model* m, const or_kv* kv, int32_t layer,
   size_t off = ((((size_t)layer * 2 + kind) * kv->num_blocks + blk) *
                     kv->block_size + (size_t)(pos % kv->block_size)) * vec +
                (size_t)g * m->head_dim;
-  return kv->base + off;
+  return (uint8_t*)kv->base + off * esz;
+}
+
+static or_kvfmt kv_format(const or_model* m) {
+  or_kvfmt f = {m->kv_fp8, m->k_scale, m->v_scale};
+  return f;
 }
 
 /* ----------------------------------------------------- one decoder row */
@@ -253,14 +318,20 @@ static int row_pre_attention(const or_model* m, int32_t layer, const or_kv* kv,
   memcpy(q, acc, sizeof(double) * (size_t)hq * hd);
   for (int32_t h = 0; h < hq; ++h) or_rope(q + (size_t)h * hd, hd, pos, m->rope_base);
   for (int32_t g = 0; g < hkv; ++g) {
-    uint16_t* kd = kv_at(m, kv, layer, 0, pos, g);
-    uint16_t* vd = kv_at(m, kv, layer, 1, pos, g);
+    void* kd = kv_at(m, kv, layer, 0, pos, g);
+    void* vd = kv_at(m, kv, layer, 1, pos, g);
     if (!kd || !vd) return OR_EINVAL;
     double* k = acc + (size_t)(hq + g) * hd;
+    const double* v = acc + (size_t)(hq + hkv + g) * hd;
     or_rope(k, hd, pos, m->rope_base);
     for (int32_t i = 0; i < hd; ++i) {
-      kd[i] = tobf(k[i]);
-      vd[i] = tobf(acc[(size_t)(hq + hkv + g) * hd + i]);
+      if (m->kv_fp8) {  /* the cache's E4M3 code of value / scale */
+        ((uint8_t*)kd)[i] = or_f64_to_e4m3(k[i] / m->k_scale);
+        ((uint8_t*)vd)[i] = or_f64_to_e4m3(v[i] / m->v_scale);
+      } else {
+        ((uint16_t*)kd)[i] = tobf(k[i]);
+        ((uint16_t*)vd)[i] = tobf(v[i]);
+      }
     }
   }
   return OR_OK;
@@ -270,8 +341,8 @@ static int row_pre_attention(const or_model* m, int32_t layer, const or_kv* kv,
 static int row_attention(const or_model* m, int32_t layer, const or_kv* kv,
                          const double* q, int32_t pos, double* o) {
   int32_t n = pos + 1, hd = m->head_dim;
-  const uint16_t** kp = malloc(sizeof(*kp) * (size_t)n);
-  const uint16_t** vp = malloc(sizeof(*vp) * (size_t)n);
+  const void** kp = malloc(sizeof(*kp) * (size_t)n);
+  const void** vp = malloc(sizeof(*vp) * (size_t)n);
   double* s = malloc(sizeof(double) * (size_t)n);
   int rc = OR_OK;
   for (int32_t h = 0; h < m->n_heads && rc == OR_OK; ++h) {
@@ -285,7 +356,7 @@ static int row_attention(const or_model* m, int32_t layer, const or_kv* kv,
       }
     }
     if (rc == OR_OK)
-      attend_head(q + (size_t)h * hd, kp, vp, n, hd, s, o + (size_t)h * hd);
+      attend_head(q + (size_t)h * hd, kp, vp, n, hd, kv_format(m), s, o + (size_t)h * hd);
   }
   free(kp);
   free(vp);
@@ -363,7 +434,8 @@ static void scratch_free(scratch_t* s) {
 }
 
 static int model_ok(const or_model* m) {
-  return m && m->n_layers > 0 && m->d_model > 0 && m->n_heads > 0 &&
+  return m && (m->kv_fp8 == 0 || (m->kv_fp8 == 1 && m->k_scale > 0 && m->v_scale > 0)) &&
+         m->n_layers > 0 && m->d_model > 0 && m->n_heads > 0 &&
          m->n_kv_heads > 0 && m->n_heads % m->n_kv_heads == 0 &&
          m->head_dim > 0 && m->head_dim % 2 == 0 && m->ffn_dim > 0 &&
          m->vocab > 0;
@@ -380,7 +452,7 @@ static void embed_row(const or_model* m, int32_t tok, double* x) {
  * start_pos.., appending to the dense store kv[L][2][max_pos][Hkv][hd].
  * If logits is non-NULL it receives [n][vocab] (or only the last token's
  * [vocab] when last_only is set). Returns 0 or OR_EINVAL. */
-int or_serial_forward(const or_model* m, uint16_t* kv_dense, int32_t max_pos,
+int or_serial_forward(const or_model* m, void* kv_dense, int32_t max_pos,
                       const int32_t* tokens, int32_t n, int32_t start_pos,
                       int32_t last_only, double* logits) {
   if (!model_ok(m) || n <= 0 || start_pos < 0 || start_pos + n > max_pos)
@@ -422,7 +494,7 @@ int or_serial_forward(const or_model* m, uint16_t* kv_dense, int32_t max_pos,
  * want_token[s] != 0 emit logits for their last row, in sequence order,
  * into logits_out [n_out][vocab]; greedy_out (optional) gets the greedy id.
  * pool: [L][2][num_blocks][bs][Hkv][hd]. */
-int or_paged_step(const or_model* m, uint16_t* pool, int32_t num_blocks,
+int or_paged_step(const or_model* m, void* pool, int32_t num_blocks,
                   int32_t block_size, int32_t n_seqs, const int32_t* block_tables,
                   int32_t max_blocks_per_seq, const int32_t* ctx_lens,
                   const int32_t* n_new, const int32_t* tokens,
