@@ -34,17 +34,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kv_bytes_per_pos(shape):
-    return 2 * shape.n_kv_heads * shape.head_dim * 2 * shape.n_layers
+def kv_bytes_per_pos(shape, elem=2):
+    """K and V bytes of one position over all layers (elem: bytes per value,
+    2 for bf16, 1 for E4M3)."""
+    return 2 * shape.n_kv_heads * shape.head_dim * elem * shape.n_layers
 
 
-def step_bytes(shape, ctx, n_out):
+def step_bytes(shape, ctx, n_out, kv_elem=2):
     """Algorithmic HBM bytes of one decode step: every weight once, the
     embedding rows, each row's cached KV (ctx + 1 positions read, one
     appended) and the fp32 logits written."""
     from continuous_batching_decode_forward_amd import synth
     W = synth.weight_bytes(shape) + len(ctx) * shape.d_model * 2
-    kvb = kv_bytes_per_pos(shape)
+    kvb = kv_bytes_per_pos(shape, kv_elem)
     A = sum((int(c) + 1) * kvb + kvb for c in ctx)
     return W + A + n_out * shape.vocab * 4
 
@@ -108,8 +110,11 @@ def build_workload(shape, B, seed, ctx_range=(512, 4096), bs=32):
 
 
 def fill_pool(eng, seed, blocks):
+    """Seeded cached K/V in the engine's pool layout: N(0, 1) bf16 values, or
+    E4M3 codes (magnitudes 0..7.5) for an 8-bit cache."""
     import torch
     from continuous_batching_decode_forward_amd import synth
+    gen = synth.kv_codes_fp8 if eng.kv_fp8 else synth.kv_values
     s = eng.shape
     bs, hkv, hd = eng.block_size, s.n_kv_heads, s.head_dim
     dev = eng.kv_pool.device
@@ -121,10 +126,10 @@ def fill_pool(eng, seed, blocks):
         k, v = eng.kv_views(layer)
         for c0 in range(0, len(blocks), 2048):
             b = blocks[c0:c0 + 2048]
-            k[b] = synth.kv_values(seed, layer, 0, b.view(-1, 1, 1, 1), kh.view(1, -1, 1, 1),
-                                   off.view(1, 1, -1, 1), dim.view(1, 1, 1, -1), hkv, bs, hd)
-            v[b] = synth.kv_values(seed, layer, 1, b.view(-1, 1, 1, 1), kh.view(1, -1, 1, 1),
-                                   off.view(1, 1, 1, -1), dim.view(1, 1, -1, 1), hkv, bs, hd)
+            k[b] = gen(seed, layer, 0, b.view(-1, 1, 1, 1), kh.view(1, -1, 1, 1),
+                       off.view(1, 1, -1, 1), dim.view(1, 1, 1, -1), hkv, bs, hd)
+            v[b] = gen(seed, layer, 1, b.view(-1, 1, 1, 1), kh.view(1, -1, 1, 1),
+                       off.view(1, 1, 1, -1), dim.view(1, 1, -1, 1), hkv, bs, hd)
 
 
 def time_steps(eng, meta, lg, tk, steps, warmup, stream, profile_class=None):
@@ -256,14 +261,20 @@ def penalty_history(seed, B, V, n_hist, decay):
 
 
 def bench_sampled(args):
-    print(json.dumps(run_sampled(args.steps, args.warmup)), flush=True)
+    print(json.dumps(run_sampled(args.steps, args.warmup, kv_fp8=args.kv_fp8)), flush=True)
 
 
-def run_sampled(steps, warmup):
+# The 8-bit cache's scales for the seeded codes (magnitudes 0..7.5): keys
+# and values of about unit size after dequantisation.
+FP8_KV = {"k_scale": 0.25, "v_scale": 0.25}
+
+
+def run_sampled(steps, warmup, kv_fp8=False):
     """The KV-dominated sampled step: one 8B-shaped layer + LM head over a
     65536-token vocabulary, B = 256 decode rows with contexts uniform in
     8192..32768, sampler T = 1.0, top_p = 0.3, top_k = 0, frequency penalty
-    1.0, decay 0.996 on a seeded 64-token history per row."""
+    1.0, decay 0.996 on a seeded 64-token history per row. kv_fp8: the same
+    step over an 8-bit (E4M3) cache, half the KV bytes."""
     import torch
     from continuous_batching_decode_forward_amd import binding as B
     from continuous_batching_decode_forward_amd import configs, synth
@@ -274,11 +285,14 @@ def run_sampled(steps, warmup):
     log(f"[bench] weights {shape.name} on GPU")
     wg = synth.make_weights(shape, seed=seed, device="cuda")
     wl = build_workload(shape, Bn, seed, ctx_range=wlc.ctx_range, bs=wlc.block_size)
+    elem = 1 if kv_fp8 else 2
+    kv_args = dict(kv_dtype=B.CBD_KV_FP8_E4M3, **FP8_KV) if kv_fp8 else {}
     eng = Engine(shape, wg, block_size=wl["bs"], num_blocks=wl["total"],
                  max_blocks_per_seq=wl["mbps"], max_slots=Bn, max_rows=Bn, max_seqs=Bn,
-                 max_position=wl["max_position"])
+                 max_position=wl["max_position"], **kv_args)
     log(f"[bench] filling {wl['total']} KV blocks "
-        f"({wl['total'] * shape.kv_bytes_per_pos * wl['bs'] / 1e9:.1f} GB)")
+        f"({wl['total'] * kv_bytes_per_pos(shape, elem) * wl['bs'] / 1e9:.1f} GB"
+        f"{', E4M3' if kv_fp8 else ''})")
     fill_pool(eng, seed, wl["perm"])
     sp = wlc.sampling
     params = B.cbd_sampling.from_params(sp)
@@ -299,9 +313,10 @@ def run_sampled(steps, warmup):
         times[name.lower() + "_us"] = round(k[0] * 1e3, 1)
     if eng.status():
         raise RuntimeError("device status set")
-    byts = step_bytes(shape, wl["ctx"], Bn) + 3 * Bn * shape.vocab * 4  # + sampler state r/w
-    kv = sum((int(c) + 1) * shape.kv_bytes_per_pos for c in wl["ctx"])
-    out = {"workload": wlc.name, "batch": Bn, "ctx_range": list(wlc.ctx_range),
+    byts = step_bytes(shape, wl["ctx"], Bn, elem) + 3 * Bn * shape.vocab * 4  # + sampler r/w
+    kv = sum((int(c) + 1) * kv_bytes_per_pos(shape, elem) for c in wl["ctx"])
+    out = {"workload": wlc.name + ("-e4m3kv" if kv_fp8 else ""), "batch": Bn,
+           "ctx_range": list(wlc.ctx_range), "kv_cache": "e4m3" if kv_fp8 else "bf16",
            "ms_per_step": ms, "tokens_per_s": Bn / (ms * 1e-3),
            "step_algorithmic_bytes": byts, "hbm_gbs": byts / (ms * 1e-3) / 1e9,
            "roofline_frac": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -565,6 +580,8 @@ def main():
                              "2b-28layer-continuous-batching",
                              "8b-32layer-mixed-48dec+512chunk"],
                     help="the headline decode sweep (default) or another configured workload")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="the sampled workload over an 8-bit (E4M3) KV cache")
     ap.add_argument("--cb-slots", default="8,32", help="slot counts of the 2B loop workload")
     ap.add_argument("--cb-steps", type=int, default=256, help="steps of the 2B loop workload")
     ap.add_argument("--cb-pacing", default="0,1,2",
@@ -705,6 +722,12 @@ def main():
         out["long_context_sampled"] = run_sampled(max(10, args.steps // 2), 3)
         log(f"[bench] long-context sampled: {out['long_context_sampled']['ms_per_step']:.3f} ms/step, "
             f"{out['long_context_sampled']['roofline_frac']:.3f} of peak")
+        log("[bench] the same step over an 8-bit (E4M3) KV cache")
+        out["long_context_sampled_e4m3kv"] = run_sampled(max(10, args.steps // 2), 3,
+                                                         kv_fp8=True)
+        log(f"[bench] long-context sampled, E4M3 cache: "
+            f"{out['long_context_sampled_e4m3kv']['ms_per_step']:.3f} ms/step, "
+            f"{out['long_context_sampled_e4m3kv']['roofline_frac']:.3f} of peak")
         log("[bench] 32-layer 8B mixed step (48 decode rows + 512-token chunk)")
         out["mixed_8b_32layer"] = run_mixed8b(args.mixed_reps)
         log(f"[bench] mixed: {out['mixed_8b_32layer']['ms_per_step_mean']:.2f} ms/step mean, "

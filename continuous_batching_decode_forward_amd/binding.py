@@ -24,6 +24,9 @@ CBD_STATUS_BAD_TOKEN = 0x2
 CBD_STATUS_BAD_SLOT = 0x4
 CBD_STATUS_BAD_SHAPE = 0x8
 
+CBD_KV_BF16 = 0
+CBD_KV_FP8_E4M3 = 1
+
 CBD_MODE_GREEDY = 0
 CBD_MODE_SAMPLE = 1
 
@@ -74,7 +77,9 @@ class cbd_config(C.Structure):
                 ("vocab", C.c_int32), ("block_size", C.c_int32), ("num_blocks", C.c_int32),
                 ("max_blocks_per_seq", C.c_int32), ("max_slots", C.c_int32),
                 ("max_rows", C.c_int32), ("max_seqs", C.c_int32), ("max_position", C.c_int32),
-                ("rms_eps", C.c_float), ("pad0_", C.c_float), ("rope_base", C.c_double)]
+                ("rms_eps", C.c_float), ("pad0_", C.c_float), ("rope_base", C.c_double),
+                ("kv_dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
+                ("pad1_", C.c_int32)]
 
 
 class cbd_weights(C.Structure):

@@ -25,6 +25,8 @@
 // online in base 2 (scores pre-scaled by log2(e)/sqrt(hd)); P enters the PV
 // MFMA as three bf16 terms that sum to its fp32 value, and the running sums
 // use fp32 P.
+#include <type_traits>
+
 #include "attn_sched.h"
 #include "common.h"
 #include "kernels.h"
@@ -36,13 +38,25 @@ namespace cbd {
 // A value the whole wave shares, moved to a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// One 32-key step's operands in registers: K rows of the two S tiles and
-// the V^T pieces.
-template <int HD>
+// One 32-key step's operands in registers, as loaded: K rows of the two S
+// tiles and the V^T pieces, 8 values each -- bf16 (16 bytes) or E4M3 codes
+// (8 bytes, widened to bf16 when the step is computed).
+template <int HD, bool F8>
 struct KVTile {
-  uint4 k[2][HD / 32];
-  uint4 v[HD / 16];
+  using Frag = typename std::conditional<F8, uint2, uint4>::type;
+  Frag k[2][HD / 32];
+  Frag v[HD / 16];
 };
+
+__device__ __forceinline__ uint4 widen(uint4 v) { return v; }
+__device__ __forceinline__ uint4 widen(uint2 v) { return e4m3x8_to_bf16x8(v); }
+template <bool F8>
+__device__ __forceinline__ auto load_frag(const void* base, size_t elem) {
+  if constexpr (F8)
+    return load_stream8(static_cast<const uint8_t*>(base) + elem);
+  else
+    return load_stream16(static_cast<const uint16_t*>(base) + elem);
+}
 
 // Issue priority from a wave's progress: 3 in the first quarter of its key
 // steps, down to 0 in the last. Two waves share each SIMD, and at equal
@@ -71,11 +85,11 @@ __device__ __forceinline__ void progress_prio(int done, int total) {
 // The kernel is held to 256 registers (accumulators included) so that two
 // waves share each SIMD: one wave's loads stay in flight while the other
 // computes (at one wave per SIMD the key stream stalls on every step).
-template <int HD, int BS>
+template <int HD, int BS, bool F8>
 __device__ __forceinline__ void attend_segment(
     const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, const StepMeta& m,
     const RowMaps& maps, const ModelDims& md, const AttnPlan& ap,
-    const uint16_t* __restrict__ pool_k, const uint16_t* __restrict__ pool_v,
+    const void* __restrict__ pool_k, const void* __restrict__ pool_v,
     float* __restrict__ part_ml, float* __restrict__ part_o, uint32_t* status, int* tbl, int s,
     int g, int qt, int nn, int ctx, int k_lo, int k_hi, int sp, int done, int total) {
   constexpr int QK_STEPS = HD / 32;  // MFMAs over head_dim
@@ -129,52 +143,55 @@ __device__ __forceinline__ void attend_segment(
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+  // Offsets below count stored values (bf16 or E4M3 codes).
   const size_t head_stride = (size_t)BS * HD;  // one (block, kv head) tile
   const size_t kv_off = (size_t)g * head_stride;
   const size_t blk_stride = (size_t)md.n_kv_heads * head_stride;
-  const float scale = 1.4426950408889634f / sqrtf((float)HD);
+  // An 8-bit cache holds K / k_scale: the scale joins the softmax scale.
+  const float scale = 1.4426950408889634f / sqrtf((float)HD) * (F8 ? md.k_scale : 1.0f);
   const int last = k_hi - 1;
 
   // Per-lane constant parts of the K and V^T addresses inside a block.
   // K row of tile t for this lane: key 8 (lr / 4) + lr % 4 + 4 t of the step.
   const int krow0 = 8 * (lr >> 2) + (lr & 3);
-  auto load = [&](KVTile<HD>& T, int p0) {
+  auto load = [&](KVTile<HD, F8>& T, int p0) {
     if constexpr (BS >= 32) {
       // A 32-key step lies in one block (steps start on multiples of 32):
       // one block id for the wave, keys past the range read stale but valid
       // slots of the same block.
       const int blk = uniform(tbl[p0 / BS - b0]);
-      const uint16_t* kb = pool_k + (size_t)blk * blk_stride + kv_off + (size_t)(p0 % BS) * HD;
-      const uint16_t* vb = pool_v + (size_t)blk * blk_stride + kv_off + (p0 % BS);
+      const size_t kb = (size_t)blk * blk_stride + kv_off + (size_t)(p0 % BS) * HD;
+      const size_t vb = (size_t)blk * blk_stride + kv_off + (p0 % BS);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int j = 0; j < QK_STEPS; ++j)
-          T.k[t][j] = load_stream16(kb + (size_t)(krow0 + 4 * t) * HD + 8 * lg + 32 * j);
+          T.k[t][j] = load_frag<F8>(pool_k, kb + (size_t)(krow0 + 4 * t) * HD + 8 * lg + 32 * j);
 #pragma unroll
       for (int t = 0; t < DT; ++t)
-        T.v[t] = load_stream16(vb + (size_t)(16 * t + lr) * BS + 8 * lg);
+        T.v[t] = load_frag<F8>(pool_v, vb + (size_t)(16 * t + lr) * BS + 8 * lg);
     } else {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int p = min(p0 + krow0 + 4 * t, last);
         const int blk = tbl[p / BS - b0];
-        const uint16_t* kp = pool_k + (size_t)blk * blk_stride + kv_off + (size_t)(p % BS) * HD + 8 * lg;
+        const size_t kp = (size_t)blk * blk_stride + kv_off + (size_t)(p % BS) * HD + 8 * lg;
 #pragma unroll
-        for (int j = 0; j < QK_STEPS; ++j) T.k[t][j] = load_stream16(kp + 32 * j);
+        for (int j = 0; j < QK_STEPS; ++j) T.k[t][j] = load_frag<F8>(pool_k, kp + 32 * j);
       }
       // V^T pieces: row d = 16 t + lr, keys pv .. pv + 7 (pv = p0 + 8 lg)
       const int pv = min(p0 + 8 * lg, last & ~7);
       if constexpr (BS >= 8) {
         const int blk = tbl[pv / BS - b0];
-        const uint16_t* vp = pool_v + (size_t)blk * blk_stride + kv_off + (size_t)lr * BS + (pv % BS);
+        const size_t vp = (size_t)blk * blk_stride + kv_off + (size_t)lr * BS + (pv % BS);
 #pragma unroll
-        for (int t = 0; t < DT; ++t) T.v[t] = load_stream16(vp + (size_t)16 * t * BS);
-      } else {  // 4-position blocks: two 8-byte halves
+        for (int t = 0; t < DT; ++t) T.v[t] = load_frag<F8>(pool_v, vp + (size_t)16 * t * BS);
+      } else {  // 4-position blocks (bf16 only): two 8-byte halves
+        static_assert(!F8, "an 8-bit cache needs blocks of 8 positions or more");
         const int blk0 = tbl[pv / BS - b0];
         const int blk1 = tbl[min(pv + 4, last) / BS - b0];
-        const uint16_t* v0 = pool_v + (size_t)blk0 * blk_stride + kv_off + (size_t)lr * BS;
-        const uint16_t* v1 = pool_v + (size_t)blk1 * blk_stride + kv_off + (size_t)lr * BS;
+        const uint16_t* v0 = static_cast<const uint16_t*>(pool_v) + (size_t)blk0 * blk_stride + kv_off + (size_t)lr * BS;
+        const uint16_t* v1 = static_cast<const uint16_t*>(pool_v) + (size_t)blk1 * blk_stride + kv_off + (size_t)lr * BS;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
           const uint2 a = *reinterpret_cast<const uint2*>(v0 + (size_t)16 * t * BS);
@@ -197,17 +214,21 @@ __device__ __forceinline__ void attend_segment(
   for (int o_ = 1; o_ < 16; o_ <<= 1) mask_from = min(mask_from, __shfl_xor(mask_from, o_, 64));
   mask_from = uniform(mask_from);
 
-  auto compute = [&](KVTile<HD>& T, int p0) {
+  auto compute = [&](KVTile<HD, F8>& T, int p0) {
     floatx4_t sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sacc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < QK_STEPS; ++j) {
-        sacc[t] = mfma16x16x32(as_bf16x8(T.k[t][j]), qf[0][j], sacc[t]);
-        sacc[t] = mfma16x16x32(as_bf16x8(T.k[t][j]), qf[1][j], sacc[t]);
+        const bf16x8_t kf = as_bf16x8(widen(T.k[t][j]));
+        sacc[t] = mfma16x16x32(kf, qf[0][j], sacc[t]);
+        sacc[t] = mfma16x16x32(kf, qf[1][j], sacc[t]);
       }
     }
+    uint4 vw[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) vw[t] = widen(T.v[t]);
     // lane (lr, lg) holds column lr for keys p0 + 8 lg + i + 4 t
     float sv[8];
 #pragma unroll
@@ -235,13 +256,13 @@ __device__ __forceinline__ void attend_segment(
       const int valid = k_hi - (p0 + 8 * lg);  // keys of this lane's piece in range
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        uint32_t w[4] = {T.v[t].x, T.v[t].y, T.v[t].z, T.v[t].w};
+        uint32_t w[4] = {vw[t].x, vw[t].y, vw[t].z, vw[t].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t keep = 2 * e + 1 < valid ? 0xffffffffu : (2 * e < valid ? 0xffffu : 0u);
           w[e] &= keep;
         }
-        T.v[t] = make_uint4(w[0], w[1], w[2], w[3]);
+        vw[t] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
     // P = P1 + P2 + P3 exactly: each term keeps the top 8 significant bits
@@ -276,11 +297,11 @@ __device__ __forceinline__ void attend_segment(
     const bf16x8_t pf2 = as_bf16x8(make_uint4(p2[0], p2[1], p2[2], p2[3]));
     const bf16x8_t pf3 = as_bf16x8(make_uint4(p3[0], p3[1], p3[2], p3[3]));
 #pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] = mfma16x16x32(as_bf16x8(T.v[t]), pf1, o[t]);
+    for (int t = 0; t < DT; ++t) o[t] = mfma16x16x32(as_bf16x8(vw[t]), pf1, o[t]);
 #pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] = mfma16x16x32(as_bf16x8(T.v[t]), pf2, o[t]);
+    for (int t = 0; t < DT; ++t) o[t] = mfma16x16x32(as_bf16x8(vw[t]), pf2, o[t]);
 #pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] = mfma16x16x32(as_bf16x8(T.v[t]), pf3, o[t]);
+    for (int t = 0; t < DT; ++t) o[t] = mfma16x16x32(as_bf16x8(vw[t]), pf3, o[t]);
   };
 
   // Two tiles in flight: the loads of step i + 1 are issued before step i is
@@ -291,7 +312,7 @@ __device__ __forceinline__ void attend_segment(
   {
     const int n_it = (k_hi - k_lo + 31) / 32;
     const int last_step = k_lo + 32 * (n_it - 1);
-    KVTile<HD> A, B;
+    KVTile<HD, F8> A, B;
     load(A, k_lo);
     int i = 0;
     for (; i + 2 <= n_it; i += 2) {
@@ -313,21 +334,24 @@ __device__ __forceinline__ void attend_segment(
     part_ml[2 * idx] = m_run;
     part_ml[2 * idx + 1] = l_run;
   }
-  // lane holds O^T[d = 16 t + 4 lg + i][col lr]
+  // lane holds O^T[d = 16 t + 4 lg + i][col lr]; an 8-bit cache holds
+  // V / v_scale
+  const float vs = F8 ? md.v_scale : 1.0f;
   float* op = part_o + idx * HD + 4 * lg;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
-    *reinterpret_cast<float4*>(op + 16 * t) = make_float4(o[t][0], o[t][1], o[t][2], o[t][3]);
+    *reinterpret_cast<float4*>(op + 16 * t) =
+        make_float4(o[t][0] * vs, o[t][1] * vs, o[t][2] * vs, o[t][3] * vs);
 }
 
 // The kernel is held to 256 registers (accumulators included) so that two
 // waves share each SIMD: one wave's loads stay in flight while the other
 // computes (at one wave per SIMD the key stream stalls on every step).
-template <int HD, int BS>
+template <int HD, int BS, bool F8>
 __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(
     const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, StepMeta m,
-    RowMaps maps, ModelDims md, AttnPlan ap, const uint16_t* __restrict__ pool_k,
-    const uint16_t* __restrict__ pool_v, float* __restrict__ part_ml,
+    RowMaps maps, ModelDims md, AttnPlan ap, const void* __restrict__ pool_k,
+    const void* __restrict__ pool_v, float* __restrict__ part_ml,
     float* __restrict__ part_o, uint32_t* status) {
   __shared__ int s_item0[ATT_LDS_SEQS + 1];
   __shared__ int s_tbl[ATT_WAVES][ATT_TBL];
@@ -359,7 +383,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
       if (sg.sp >= ap.max_splits) {  // the host's piece_lo rules this out
         if ((threadIdx.x & 63) == 0) raise_status(status, ST_BAD_SHAPE);
       } else {
-        attend_segment<HD, BS>(q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o,
+        attend_segment<HD, BS, F8>(q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o,
                                status, s_tbl[wave], s, g, sg.qt, nn, ctx, sg.k_lo, sg.k_hi, sg.sp,
                                done, total);
       }
@@ -727,10 +751,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
 template <int HD, int BS>
 static void launch_items(int blocks, const uint16_t* q_hi, const uint16_t* q_lo, const StepMeta& m,
                          const RowMaps& maps, const ModelDims& md, const AttnPlan& ap,
-                         const uint16_t* pool_k, const uint16_t* pool_v, float* part_ml,
+                         const void* pool_k, const void* pool_v, float* part_ml,
                          float* part_o, uint32_t* status, hipStream_t st) {
-  attention_kernel<HD, BS><<<blocks, 64 * ATT_WAVES, 0, st>>>(q_hi, q_lo, m, maps, md, ap, pool_k,
-                                                             pool_v, part_ml, part_o, status);
+  if constexpr (BS >= 8) {
+    if (md.kv_fp8) {
+      attention_kernel<HD, BS, true><<<blocks, 64 * ATT_WAVES, 0, st>>>(
+          q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status);
+      return;
+    }
+  }
+  attention_kernel<HD, BS, false><<<blocks, 64 * ATT_WAVES, 0, st>>>(
+      q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status);
 }
 
 // Dynamic LDS above 64 KB must be allowed per kernel before its first launch.
@@ -741,10 +772,14 @@ static hipError_t allow_lds(const void* kernel, size_t bytes) {
 template <int HD>
 static hipError_t launch_hd(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R,
                             const StepMeta& m, const RowMaps& maps, const ModelDims& md,
-                            const AttnPlan& ap, const uint16_t* pool_k, const uint16_t* pool_v,
+                            const AttnPlan& ap, const void* pool_k_, const void* pool_v_,
                             float* part_ml, float* part_o, uint16_t* out_hi, uint16_t* out_lo,
                             uint32_t* status, hipStream_t st) {
+  // the block kernel reads a bf16 cache (an 8-bit cache plans no block items)
+  const uint16_t* pool_k = static_cast<const uint16_t*>(pool_k_);
+  const uint16_t* pool_v = static_cast<const uint16_t*>(pool_v_);
   if (ap.block_rows > 0 && ap.grid_items_b > 0) {
+    if (md.kv_fp8) return hipErrorInvalidValue;
     const size_t lds = (size_t)ATB_STAGES * 8 * HD * 16;  // the K/V ring
     if (md.block_size == 32) {
       hipError_t e = allow_lds(reinterpret_cast<const void*>(&attention_block_kernel<HD, 32>), lds);
@@ -783,7 +818,7 @@ static hipError_t launch_hd(const uint16_t* q_hi, const uint16_t* q_lo, int32_t 
 
 hipError_t launch_attention(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R,
                             const StepMeta& m, const RowMaps& maps, const ModelDims& md,
-                            const AttnPlan& ap, const uint16_t* pool_k, const uint16_t* pool_v,
+                            const AttnPlan& ap, const void* pool_k, const void* pool_v,
                             float* part_ml, float* part_o, uint16_t* out_hi, uint16_t* out_lo,
                             uint32_t* status, hipStream_t st) {
   if (R <= 0) return hipSuccess;

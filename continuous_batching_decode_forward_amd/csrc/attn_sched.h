@@ -49,9 +49,11 @@ CBD_HD int attn_split_cap(int block_size) { return (ATT_TBL - 1) * block_size / 
 
 // The launch plan of one step (host). cus_waves: resident waves of the
 // per-tile kernel on the device (two per SIMD). n_rows, n_seqs, max_ctx: the
-// step's host scalars.
+// step's host scalars. kv_fp8: an 8-bit cache, whose chunks stay on the
+// per-tile kernel.
 inline AttnPlan plan_attention(int n_heads, int n_kv_heads, int block_size, int max_position,
-                               int cus_waves, int n_seqs, int n_rows, int max_ctx) {
+                               int cus_waves, int n_seqs, int n_rows, int max_ctx,
+                               int kv_fp8 = 0) {
   AttnPlan ap;
   ap.max_splits = attn_cap_splits(max_position);
   ap.max_ctx = max_ctx;
@@ -87,7 +89,7 @@ inline AttnPlan plan_attention(int n_heads, int n_kv_heads, int block_size, int 
   // with fewer than block_min + n_seqs - 1 rows has no such chunk: it
   // launches no block kernel and every sequence runs on the per-tile kernel.
   ap.block_min = 32;
-  ap.block_rows = block_size % 32 == 0 ? ATT_BLOCK_COLS / G : 0;
+  ap.block_rows = block_size % 32 == 0 && !kv_fp8 ? ATT_BLOCK_COLS / G : 0;
   if ((long long)n_rows - n_seqs + 1 < ap.block_min) ap.block_rows = 0;
   ap.grid_items_b = 0;
   if (ap.block_rows > 0) {

@@ -43,7 +43,7 @@ struct Checker {
 extern "C" {
 
 // cfg: n_heads, n_kv_heads, head_dim, block_size, num_blocks, max_position,
-// max_rows, max_slots, cus_waves. Step arrays are host int32:
+// max_rows, max_slots, cus_waves, kv_fp8. Step arrays are host int32:
 // slots[n_seqs], block_tables[n_seqs][mbps], ctx_lens[n_seqs],
 // n_new[n_seqs]. stats (int64[8], nullable): per-tile segments, per-tile
 // pieces, block items with keys, launched per-tile waves, block workgroups,
@@ -60,7 +60,7 @@ int cbd_check_attention_schedule(const int32_t* cfg, int32_t n_seqs, int32_t n_r
   Checker ck;
   char buf[256];
   const AttnPlan ap =
-      plan_attention(n_heads, kvh, bs, max_position, cus_waves, n_seqs, n_rows, max_ctx);
+      plan_attention(n_heads, kvh, bs, max_position, cus_waves, n_seqs, n_rows, max_ctx, cfg[9]);
   int64_t st[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
   // The prep kernel: row layout, served sequences, schedule starts.

@@ -24,6 +24,28 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
 
 __device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }
 
+// fp32 -> OCP E4M3 code (the 8-bit cache format): round to nearest even,
+// magnitudes beyond 448 saturated to 448, NaN to 0x7f (the conversion
+// instruction alone turns out-of-range values into NaN, hence the clamp).
+__device__ __forceinline__ uint8_t f2e4m3(float f) {
+  if (f != f) return 0x7f;
+  f = fminf(fmaxf(f, -448.0f), 448.0f);
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(f, 0.0f, 0, false) & 0xff);
+}
+
+// Eight E4M3 codes (a uint2, code i in byte i) -> eight bf16 values in MFMA
+// operand order (a uint4, value i in half-word i). Every E4M3 value is
+// exactly a bf16 value.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.x, 1.0f, true);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.y, 1.0f, false);
+  const bf16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, d), __builtin_bit_cast(uint32_t, e));
+}
+
 // Two bf16 packed in a uint32 (low half first).
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -90,6 +112,13 @@ __device__ __forceinline__ void store_split8(uint16_t* hi, uint16_t* lo, size_t 
 __device__ __forceinline__ uint4 load_stream16(const uint16_t* p) {
   u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The same for 8 bytes.
+__device__ __forceinline__ uint2 load_stream8(const uint8_t* p) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane i of the

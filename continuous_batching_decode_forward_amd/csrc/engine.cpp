@@ -2,6 +2,8 @@
 // and block allocation, and the per-step launch sequence.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <cmath>
 #include <string.h>
 
 #include <algorithm>
@@ -36,6 +38,13 @@ int validate_config(const cbd_config* c) {
   if (c->d_model % 16 || c->ffn_dim % 16 || c->vocab % 16)
     return fail(CBD_E_UNSUPPORTED, "d_model, ffn_dim and vocab must be multiples of 16");
   if (c->d_model > 8192) return fail(CBD_E_UNSUPPORTED, "d_model above 8192");
+  if (c->kv_dtype != CBD_KV_BF16 && c->kv_dtype != CBD_KV_FP8_E4M3)
+    return fail(CBD_E_INVAL, "unknown kv_dtype");
+  if (!(c->k_scale >= 0.f) || !(c->v_scale >= 0.f) || !std::isfinite(c->k_scale) ||
+      !std::isfinite(c->v_scale))
+    return fail(CBD_E_INVAL, "k_scale and v_scale must be finite and non-negative");
+  if (c->kv_dtype == CBD_KV_FP8_E4M3 && c->block_size < 8)
+    return fail(CBD_E_UNSUPPORTED, "an FP8 KV cache needs block_size 8, 16, 32 or 64");
   if (c->max_seqs > c->max_rows) return fail(CBD_E_INVAL, "max_seqs exceeds max_rows");
   if ((long long)(attn_cap_splits(c->max_position) - 1) * attn_split_cap(c->block_size) <
       c->max_position)
@@ -123,22 +132,27 @@ PackedLayout packed_layout(const cbd_config& c) {
 }
 
 size_t kv_pool_bytes(const cbd_config& c) {
+  const size_t esz = c.kv_dtype == CBD_KV_FP8_E4M3 ? 1 : 2;
   return (size_t)c.n_layers * 2 * (size_t)c.num_blocks * (size_t)c.n_kv_heads *
-         (size_t)c.block_size * (size_t)c.head_dim * 2;
+         (size_t)c.block_size * (size_t)c.head_dim * esz;
 }
 
 }  // namespace cbd
 
 using namespace cbd;
 
-uint16_t* cbd_engine::pool_k(int layer) const {
-  size_t region = (size_t)cfg.num_blocks * cfg.n_kv_heads * cfg.block_size * cfg.head_dim;
-  return reinterpret_cast<uint16_t*>(kv_pool) + (size_t)layer * 2 * region;
+// One layer's K or V region of the pool (bytes: values x element size).
+static size_t kv_region_bytes(const cbd_config& c) {
+  return (size_t)c.num_blocks * c.n_kv_heads * c.block_size * c.head_dim *
+         (c.kv_dtype == CBD_KV_FP8_E4M3 ? 1 : 2);
 }
 
-uint16_t* cbd_engine::pool_v(int layer) const {
-  size_t region = (size_t)cfg.num_blocks * cfg.n_kv_heads * cfg.block_size * cfg.head_dim;
-  return reinterpret_cast<uint16_t*>(kv_pool) + ((size_t)layer * 2 + 1) * region;
+void* cbd_engine::pool_k(int layer) const {
+  return kv_pool + (size_t)layer * 2 * kv_region_bytes(cfg);
+}
+
+void* cbd_engine::pool_v(int layer) const {
+  return kv_pool + ((size_t)layer * 2 + 1) * kv_region_bytes(cfg);
 }
 
 cbd_engine::~cbd_engine() {
@@ -221,7 +235,9 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* packed_
   e->cfg = *cfg;
   e->md = ModelDims{cfg->d_model, cfg->n_heads, cfg->n_kv_heads, cfg->head_dim, cfg->ffn_dim,
                     cfg->vocab, cfg->block_size, cfg->num_blocks, cfg->max_slots,
-                    cfg->max_position, cfg->rms_eps};
+                    cfg->max_position, cfg->rms_eps, cfg->kv_dtype == CBD_KV_FP8_E4M3,
+                    cfg->kv_dtype == CBD_KV_FP8_E4M3 && cfg->k_scale > 0.f ? cfg->k_scale : 1.f,
+                    cfg->kv_dtype == CBD_KV_FP8_E4M3 && cfg->v_scale > 0.f ? cfg->v_scale : 1.f};
   e->ws = workspace_layout(*cfg);
   e->sl = slot_layout(*cfg);
   e->embed = (const uint16_t*)w->embed;
@@ -436,7 +452,8 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
                e->wsp<int32_t>(e->ws.out_seq), e->wsp<int32_t>(e->ws.item0),
                e->wsp<int32_t>(e->ws.row_out), e->wsp<int32_t>(e->ws.item0b)};
   const AttnPlan ap = plan_attention(c.n_heads, c.n_kv_heads, c.block_size, c.max_position,
-                                     e->attn_waves, s->n_seqs, s->n_rows, s->max_ctx);
+                                     e->attn_waves, s->n_seqs, s->n_rows, s->max_ctx,
+                                     c.kv_dtype == CBD_KV_FP8_E4M3);
   const int qkv_n = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   const int qd = c.n_heads * c.head_dim;
   const size_t MR = (size_t)c.max_rows;

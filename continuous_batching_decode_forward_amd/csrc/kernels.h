@@ -37,6 +37,8 @@ struct ModelDims {
   int32_t d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
   int32_t block_size, num_blocks, max_slots, max_position;
   float rms_eps;
+  int32_t kv_fp8;          // the KV pool holds E4M3 codes of value / scale (else bf16)
+  float k_scale, v_scale;  // fp8 scales (1 for bf16)
 };
 
 // Waves per workgroup of the per-tile attention kernel.
@@ -101,14 +103,13 @@ hipError_t launch_resid_norm(float* x, const float* part, int32_t S, int32_t R,
 hipError_t launch_rope_append(float* qkv, const float* part, int32_t S, int32_t R,
                               const StepMeta& m, const RowMaps& maps, const double* rope_cs,
                               const ModelDims& md, uint16_t* q_hi, uint16_t* q_lo,
-                              uint16_t* pool_k, uint16_t* pool_v, uint32_t* status,
-                              hipStream_t st);
+                              void* pool_k, void* pool_v, uint32_t* status, hipStream_t st);
 
 // Paged GQA attention for every row (decode rows and prefill chunks), split
 // over keys, then the split combine into out [R][n_heads*head_dim] (split).
 hipError_t launch_attention(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R,
                             const StepMeta& m, const RowMaps& maps, const ModelDims& md,
-                            const AttnPlan& ap, const uint16_t* pool_k, const uint16_t* pool_v,
+                            const AttnPlan& ap, const void* pool_k, const void* pool_v,
                             float* part_ml, float* part_o, uint16_t* out_hi, uint16_t* out_lo,
                             uint32_t* status, hipStream_t st);
 

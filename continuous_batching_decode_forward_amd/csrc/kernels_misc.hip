@@ -386,8 +386,9 @@ __global__ void rope_append_kernel(float* __restrict__ qkv, const float* __restr
                                    const int32_t* __restrict__ tables, int max_blocks_per_seq,
                                    const double2* __restrict__ rope_cs, int hq, int hkv, int hd,
                                    int bs, int num_blocks, uint16_t* __restrict__ q_hi,
-                                   uint16_t* __restrict__ q_lo, uint16_t* __restrict__ pool_k,
-                                   uint16_t* __restrict__ pool_v, uint32_t* status) {
+                                   uint16_t* __restrict__ q_lo, void* __restrict__ pool_k,
+                                   void* __restrict__ pool_v, int kv_fp8, float k_scale,
+                                   float v_scale, uint32_t* status) {
   const int slots = hq + 2 * hkv;
   const int groups = (slots + 3) / 4;
   const int r = blockIdx.x / groups;
@@ -440,14 +441,28 @@ __global__ void rope_append_kernel(float* __restrict__ qkv, const float* __restr
     return;
   }
   const int off = pos % bs;
+  if (kv_fp8) {  // E4M3 codes of value / scale
+    if (j < hq + hkv) {
+      const int g = j - hq;
+      uint8_t* dst = static_cast<uint8_t*>(pool_k) + (((size_t)blk * hkv + g) * bs + off) * hd;
+      dst[i] = f2e4m3(a / k_scale);
+      dst[i + half] = f2e4m3(b / k_scale);
+    } else {
+      const int g = j - hq - hkv;
+      uint8_t* dst = static_cast<uint8_t*>(pool_v) + ((size_t)blk * hkv + g) * hd * bs + off;
+      dst[(size_t)i * bs] = f2e4m3(a / v_scale);
+      dst[(size_t)(i + half) * bs] = f2e4m3(b / v_scale);
+    }
+    return;
+  }
   if (j < hq + hkv) {
     const int g = j - hq;
-    uint16_t* dst = pool_k + (((size_t)blk * hkv + g) * bs + off) * hd;
+    uint16_t* dst = static_cast<uint16_t*>(pool_k) + (((size_t)blk * hkv + g) * bs + off) * hd;
     dst[i] = f2bf(a);
     dst[i + half] = f2bf(b);
   } else {
     const int g = j - hq - hkv;
-    uint16_t* dst = pool_v + ((size_t)blk * hkv + g) * hd * bs + off;
+    uint16_t* dst = static_cast<uint16_t*>(pool_v) + ((size_t)blk * hkv + g) * hd * bs + off;
     dst[(size_t)i * bs] = f2bf(a);
     dst[(size_t)(i + half) * bs] = f2bf(b);
   }
@@ -456,8 +471,7 @@ __global__ void rope_append_kernel(float* __restrict__ qkv, const float* __restr
 hipError_t launch_rope_append(float* qkv, const float* part, int32_t S, int32_t R,
                               const StepMeta& m, const RowMaps& maps, const double* rope_cs,
                               const ModelDims& md, uint16_t* q_hi, uint16_t* q_lo,
-                              uint16_t* pool_k, uint16_t* pool_v, uint32_t* status,
-                              hipStream_t st) {
+                              void* pool_k, void* pool_v, uint32_t* status, hipStream_t st) {
   if (R <= 0) return hipSuccess;
   const int slots = md.n_heads + 2 * md.n_kv_heads;
   const int groups = (slots + 3) / 4;
@@ -465,7 +479,8 @@ hipError_t launch_rope_append(float* qkv, const float* part, int32_t S, int32_t 
   rope_append_kernel<<<R * groups, block, 0, st>>>(
       qkv, part, S, R, maps.row_seq, maps.row_pos, m.block_tables, m.max_blocks_per_seq,
       reinterpret_cast<const double2*>(rope_cs), md.n_heads, md.n_kv_heads, md.head_dim,
-      md.block_size, md.num_blocks, q_hi, q_lo, pool_k, pool_v, status);
+      md.block_size, md.num_blocks, q_hi, q_lo, pool_k, pool_v, md.kv_fp8, md.k_scale,
+      md.v_scale, status);
   return hipGetLastError();
 }
 

@@ -148,6 +148,6 @@ struct cbd_engine {
   T* wsp(size_t off) const {
     return reinterpret_cast<T*>(workspace + off);
   }
-  uint16_t* pool_k(int layer) const;
-  uint16_t* pool_v(int layer) const;
+  void* pool_k(int layer) const;  // bf16 values or E4M3 codes (cfg.kv_dtype)
+  void* pool_v(int layer) const;
 };

@@ -48,7 +48,8 @@ def untile_plane(flat: np.ndarray, rows: int, width: int) -> np.ndarray:
 class Engine:
     def __init__(self, shape, weights: dict, *, block_size: int, num_blocks: int,
                  max_blocks_per_seq: int, max_slots: int, max_rows: int, max_seqs: int,
-                 max_position: int, block_order=None, device="cuda", stream=None):
+                 max_position: int, block_order=None, device="cuda", stream=None,
+                 kv_dtype: int = B.CBD_KV_BF16, k_scale: float = 0.0, v_scale: float = 0.0):
         self.shape = shape
         self.device = torch.device(device)
         cfg = B.cbd_config()
@@ -58,7 +59,9 @@ class Engine:
         cfg.max_blocks_per_seq, cfg.max_slots, cfg.max_rows = max_blocks_per_seq, max_slots, max_rows
         cfg.max_seqs, cfg.max_position = max_seqs, max_position
         cfg.rms_eps, cfg.rope_base = shape.rms_eps, shape.rope_base
+        cfg.kv_dtype, cfg.k_scale, cfg.v_scale = kv_dtype, k_scale, v_scale
         self.cfg = cfg
+        self.kv_fp8 = kv_dtype == B.CBD_KV_FP8_E4M3
         self.block_size, self.num_blocks = block_size, num_blocks
         self.max_blocks_per_seq = max_blocks_per_seq
         self.packed = torch.empty(B.cbd_packed_weights_bytes(cfg), dtype=torch.uint8,
@@ -87,11 +90,12 @@ class Engine:
 
     # ---------------------------------------------------------- pool views
     def kv_views(self, layer: int):
-        """(K, V) bf16 views of one layer's pool regions:
-        K [num_blocks][Hkv][block_size][hd], V [num_blocks][Hkv][hd][block_size]."""
+        """(K, V) views of one layer's pool regions, bf16 (or uint8 E4M3 codes
+        for an 8-bit cache): K [num_blocks][Hkv][block_size][hd],
+        V [num_blocks][Hkv][hd][block_size]."""
         s = self.shape
         per = self.num_blocks * s.n_kv_heads * self.block_size * s.head_dim
-        flat = self.kv_pool.view(torch.bfloat16)
+        flat = self.kv_pool if self.kv_fp8 else self.kv_pool.view(torch.bfloat16)
         k = flat[(2 * layer) * per:(2 * layer + 1) * per].view(
             self.num_blocks, s.n_kv_heads, self.block_size, s.head_dim)
         v = flat[(2 * layer + 1) * per:(2 * layer + 2) * per].view(

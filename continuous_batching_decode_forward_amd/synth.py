@@ -155,6 +155,23 @@ def kv_values(seed: int, layer: int, kind: int, block: torch.Tensor, kvh: torch.
     return normal_like(key, idx, std)
 
 
+def kv_codes_fp8(seed: int, layer: int, kind: int, block: torch.Tensor, kvh: torch.Tensor,
+                 off: torch.Tensor, dim: torch.Tensor, n_kv_heads: int, block_size: int,
+                 head_dim: int) -> torch.Tensor:
+    """Cached K or V of an 8-bit (E4M3) cache as raw codes (uint8), keyed by
+    the physical location like kv_values: a random sign, an exponent field
+    uniform on 0..9 (field 0: the subnormal codes, zero among them) and a
+    random 3-bit mantissa -- magnitudes from 0 to 7.5, never the NaN codes.
+    Each side decodes the codes by its own rules."""
+    key = tag_key(seed, f"kv8.{layer}.{kind}")
+    idx = ((block.to(torch.int64) * n_kv_heads + kvh) * block_size + off) * head_dim + dim
+    h = hash_stream(key, idx)
+    sign = (h >> 31) & 1
+    expo = (h >> 8) % 10
+    mant = h & 7
+    return ((sign << 7) | (expo << 3) | mant).to(torch.uint8)
+
+
 def logical_kv(seed: int, layer: int, kind: int, table: np.ndarray, n_pos: int,
                n_kv_heads: int, block_size: int, head_dim: int) -> torch.Tensor:
     """The cached K or V of one sequence as [n_pos][Hkv][hd] bf16 (CPU), for

@@ -91,7 +91,23 @@ typedef struct cbd_config {
   float rms_eps;
   float pad0_;
   double rope_base;
+  /* KV cache storage: CBD_KV_BF16, or CBD_KV_FP8_E4M3 (an 8-bit float per
+   * value, halving the per-sequence bytes the step streams; the "Continuous
+   * Batching" practice article, section 6, recommends FP8 KV quantisation).
+   * FP8 stores the OCP E4M3 code of value / scale (round to nearest even,
+   * magnitudes past 448 saturated), read back as code value * scale; the
+   * scales (0 means 1.0; powers of two keep the division exact) are per
+   * engine, k_scale for keys (after RoPE) and v_scale for values. FP8 needs
+   * block_size 8, 16, 32 or 64, and prefill chunks attend on the per-tile
+   * kernel. */
+  int32_t kv_dtype;
+  float k_scale;
+  float v_scale;
+  int32_t pad1_;
 } cbd_config;
+
+#define CBD_KV_BF16 0
+#define CBD_KV_FP8_E4M3 1
 
 /* Weights: every pointer is device memory holding bf16, row-major.
  * Per-layer fields are HOST arrays of n_layers device pointers; the engine
@@ -133,8 +149,8 @@ typedef struct cbd_sampling {
 /* Buffer sizes for a configuration (bytes). The KV pool layout is
  * [n_layers][2][num_blocks][n_kv_heads][tile], one tile per (block, KV
  * head): K tiles are [block_size][head_dim] (position-major), V tiles are
- * [head_dim][block_size] (dimension-major), all bf16. The block-id space is
- * shared by all layers. */
+ * [head_dim][block_size] (dimension-major), bf16 or E4M3 bytes (kv_dtype).
+ * The block-id space is shared by all layers. */
 int cbd_kv_pool_bytes(const cbd_config* cfg, size_t* bytes);
 /* The packed-weights buffer: every projection matrix (QKV, O, gate, up,
  * down per layer, and the LM head) rearranged once, at engine creation, into

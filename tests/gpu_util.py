@@ -23,16 +23,23 @@ def weights_to(weights: dict, device) -> dict:
 
 
 def make_engine(shape, weights_gpu, *, block_size, num_blocks, max_blocks_per_seq, max_rows,
-                max_seqs, max_position, max_slots=None, block_order=None):
+                max_seqs, max_position, max_slots=None, block_order=None, **kv):
+    """kv: the cache format (kv_dtype, k_scale, v_scale), bf16 by default."""
     return Engine(shape, weights_gpu, block_size=block_size, num_blocks=num_blocks,
                   max_blocks_per_seq=max_blocks_per_seq, max_slots=max_slots or max_seqs,
                   max_rows=max_rows, max_seqs=max_seqs, max_position=max_position,
-                  block_order=block_order)
+                  block_order=block_order, **kv)
+
+
+def _kv(seed, layer, kind, b, kh, off, dim, hkv, bs, hd, fp8):
+    gen = synth.kv_codes_fp8 if fp8 else synth.kv_values
+    return gen(seed, layer, kind, b, kh, off, dim, hkv, bs, hd)
 
 
 def fill_pool(eng: Engine, seed: int, blocks: np.ndarray) -> None:
     """Write synthetic cached K/V (keyed by physical location) into the given
-    blocks of every layer of the engine's pool, in the pool's layout."""
+    blocks of every layer of the engine's pool, in the pool's layout: bf16
+    values, or E4M3 codes for an 8-bit cache."""
     s = eng.shape
     bs, hkv, hd = eng.block_size, s.n_kv_heads, s.head_dim
     dev = eng.kv_pool.device
@@ -44,23 +51,23 @@ def fill_pool(eng: Engine, seed: int, blocks: np.ndarray) -> None:
             kh = torch.arange(hkv, device=dev)
             off = torch.arange(bs, device=dev)
             dim = torch.arange(hd, device=dev)
-            kv_k = synth.kv_values(seed, layer, 0, b.view(-1, 1, 1, 1), kh.view(1, -1, 1, 1),
-                                   off.view(1, 1, -1, 1), dim.view(1, 1, 1, -1), hkv, bs, hd)
-            k[b] = kv_k
-            kv_v = synth.kv_values(seed, layer, 1, b.view(-1, 1, 1, 1), kh.view(1, -1, 1, 1),
-                                   off.view(1, 1, 1, -1), dim.view(1, 1, -1, 1), hkv, bs, hd)
-            v[b] = kv_v
+            k[b] = _kv(seed, layer, 0, b.view(-1, 1, 1, 1), kh.view(1, -1, 1, 1),
+                       off.view(1, 1, -1, 1), dim.view(1, 1, 1, -1), hkv, bs, hd, eng.kv_fp8)
+            v[b] = _kv(seed, layer, 1, b.view(-1, 1, 1, 1), kh.view(1, -1, 1, 1),
+                       off.view(1, 1, 1, -1), dim.view(1, 1, -1, 1), hkv, bs, hd, eng.kv_fp8)
 
 
 def oracle_pool(shape, seed: int, tables: list, n_cached: list, block_size: int,
-                n_new: list):
+                n_new: list, kv_fp8: bool = False):
     """An oracle-layout pool holding the cached positions of the given
-    sequences. Block ids are renumbered 0.. in table order (paging is pure
-    addressing); returns (pool, compact tables)."""
+    sequences (bf16 bits, or E4M3 codes when kv_fp8). Block ids are
+    renumbered 0.. in table order (paging is pure addressing); returns
+    (pool, compact tables)."""
     hkv, hd = shape.n_kv_heads, shape.head_dim
     need = [-(-(c + n) // block_size) for c, n in zip(n_cached, n_new)]
     total = sum(need)
-    pool = np.zeros((shape.n_layers, 2, max(total, 1), block_size, hkv, hd), np.uint16)
+    pool = np.zeros((shape.n_layers, 2, max(total, 1), block_size, hkv, hd),
+                    np.uint8 if kv_fp8 else np.uint16)
     width = max(need)
     compact = np.full((len(tables), width), -1, np.int32)
     nxt = 0
@@ -77,11 +84,11 @@ def oracle_pool(shape, seed: int, tables: list, n_cached: list, block_size: int,
         dim = torch.arange(hd)
         for layer in range(shape.n_layers):
             for kind in (0, 1):
-                vals = synth.kv_values(seed, layer, kind, phys.view(-1, 1, 1, 1),
-                                       kh.view(1, 1, -1, 1), off.view(1, -1, 1, 1),
-                                       dim.view(1, 1, 1, -1), hkv, block_size, hd)
-                pool[layer, kind, ids[:nb_cached]] = O.as_u16(vals).reshape(
-                    nb_cached, block_size, hkv, hd)
+                vals = _kv(seed, layer, kind, phys.view(-1, 1, 1, 1), kh.view(1, 1, -1, 1),
+                           off.view(1, -1, 1, 1), dim.view(1, 1, 1, -1), hkv, block_size, hd,
+                           kv_fp8)
+                vals = vals.numpy() if kv_fp8 else O.as_u16(vals)
+                pool[layer, kind, ids[:nb_cached]] = vals.reshape(nb_cached, block_size, hkv, hd)
     return pool, compact
 
 
@@ -114,8 +121,9 @@ def stage_error(gpu: np.ndarray, ref: np.ndarray, slack=None) -> float:
 
 def gather_kv(eng: Engine, layer: int, table, n_pos: int):
     """One sequence's first n_pos cached K and V positions of a layer, read
-    from the engine's pool through its block table: two uint16 arrays
-    [n_pos][Hkv][hd] (bf16 bits)."""
+    from the engine's pool through its block table: two arrays
+    [n_pos][Hkv][hd], uint16 bf16 bits (uint8 E4M3 codes for an 8-bit
+    cache)."""
     s = eng.shape
     bs = eng.block_size
     nb = -(-n_pos // bs)
@@ -124,6 +132,8 @@ def gather_kv(eng: Engine, layer: int, table, n_pos: int):
     # K [blocks][Hkv][bs][hd] and V [blocks][Hkv][hd][bs] -> [positions][Hkv][hd]
     kk = k[blocks].permute(0, 2, 1, 3).reshape(nb * bs, s.n_kv_heads, s.head_dim)[:n_pos]
     vv = v[blocks].permute(0, 3, 1, 2).reshape(nb * bs, s.n_kv_heads, s.head_dim)[:n_pos]
+    if eng.kv_fp8:
+        return kk.contiguous().cpu().numpy(), vv.contiguous().cpu().numpy()
     return O.as_u16(kk.contiguous().cpu()), O.as_u16(vv.contiguous().cpu())
 
 
@@ -145,7 +155,11 @@ def attention_rows_vs_oracle(eng: Engine, tables, ctx, n_new, threads: int = 16)
     err = np.full(R, np.inf)
 
     def one(r, pos, K, V):
-        ref = O.attention_dense(q[r], K[:pos + 1], V[:pos + 1], hq, hkv, hd)
+        if eng.kv_fp8:
+            ref = O.attention_dense_fp8(q[r], K[:pos + 1], V[:pos + 1], hq, hkv, hd,
+                                        eng.cfg.k_scale or 1.0, eng.cfg.v_scale or 1.0)
+        else:
+            ref = O.attention_dense(q[r], K[:pos + 1], V[:pos + 1], hq, hkv, hd)
         err[r] = stage_error(att[r], ref)
 
     pending = []

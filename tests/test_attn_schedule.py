@@ -49,11 +49,11 @@ def lib():
 
 
 def check_step(shape, *, block_size, num_blocks, max_position, max_rows, max_slots, slots,
-               tables, ctx, n_new, mbps, waves=WAVES_MI355X):
+               tables, ctx, n_new, mbps, waves=WAVES_MI355X, kv_fp8=0):
     """Run the replay; returns (violations, first message, stats dict)."""
     i32 = lambda a: np.ascontiguousarray(np.asarray(a, np.int64).astype(np.int32))
     cfg = i32([shape.n_heads, shape.n_kv_heads, shape.head_dim, block_size, num_blocks,
-               max_position, max_rows, max_slots, waves])
+               max_position, max_rows, max_slots, waves, kv_fp8])
     slots, ctx, n_new = i32(slots), i32(ctx), i32(n_new)
     tab = np.full((len(ctx), mbps), -1, np.int32)
     for i, t in enumerate(tables):
@@ -214,7 +214,7 @@ def test_random_step_mixes_replay_cleanly():
         v, msg, st = check_step(shape, block_size=bs, num_blocks=sum(need),
                                 max_position=max_position, max_rows=sum(nn), max_slots=n,
                                 slots=list(range(n)), tables=tables, ctx=ctx, n_new=nn,
-                                mbps=max(need), waves=waves)
+                                mbps=max(need), waves=waves, kv_fp8=trial % 3 == 0)
         assert v == 0, f"trial {trial}: {msg}"
         assert st["served"] == n
 

@@ -36,8 +36,11 @@ def big():
     return wg, O.Model(SHAPE, wc)
 
 
-def decode_step(big, B, seed, sample_rows, lo=512, hi=4096, ctx=None):
-    wg, om = big
+def decode_step(big, B, seed, sample_rows, lo=512, hi=4096, ctx=None, kv=None, om=None):
+    """kv: the engine's cache format, om: the oracle model of that format."""
+    wg, om0 = big
+    om = om or om0
+    kv = kv or {}
     bs = 32
     if ctx is None:
         ctx = synth.uniform_ints(seed, "ctx", B, lo, hi)
@@ -53,7 +56,7 @@ def decode_step(big, B, seed, sample_rows, lo=512, hi=4096, ctx=None):
         o += need[i]
     tokens = synth.uniform_ints(seed, "tok", B, 0, SHAPE.vocab - 1)
     eng = make_engine(SHAPE, wg, block_size=bs, num_blocks=total, max_blocks_per_seq=mbps,
-                      max_rows=max(B, 16), max_seqs=max(B, 16), max_position=hi + 1)
+                      max_rows=max(B, 16), max_seqs=max(B, 16), max_position=hi + 1, **kv)
     fill_pool(eng, seed, perm)
     meta = eng.upload_step(slots=list(range(B)), block_tables=tables, ctx_lens=ctx,
                            n_new=[1] * B, tokens=tokens, want_token=[1] * B)
@@ -67,7 +70,7 @@ def decode_step(big, B, seed, sample_rows, lo=512, hi=4096, ctx=None):
     eng.close()
     rows = list(sample_rows)
     pool, compact = oracle_pool(SHAPE, seed, [tables[i] for i in rows], [int(ctx[i]) for i in rows],
-                                bs, [1] * len(rows))
+                                bs, [1] * len(rows), kv_fp8=om.kv_fp8)
     ref_lg, ref_tk = O.paged_step(om, pool, compact, [int(ctx[i]) for i in rows], [1] * len(rows),
                                   [int(tokens[i]) for i in rows], [1] * len(rows))
     ok, mx, row_err = compare_logits(g_lg[rows], ref_lg)

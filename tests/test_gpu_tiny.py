@@ -25,15 +25,17 @@ def tiny():
     return w, O.Model(CFG, w), weights_to(w, "cuda")
 
 
-def run_schedule(tiny, prompts, n_decode, chunk, bs, nb, seed, order=None):
-    """Drive both sides through the same steps; return per-step stats."""
+def run_schedule(tiny, prompts, n_decode, chunk, bs, nb, seed, order=None, kv=None, final=None):
+    """Drive both sides through the same steps; return per-step stats.
+    kv: the engine's cache format (the oracle model in `tiny` must match);
+    final(eng, pool, tables, ctx) runs after the last step."""
     w, om, wg = tiny
     n = len(prompts)
     perm = synth.permutation(seed, "blocks", nb)
     per = nb // n
     tables = np.stack([perm[i * per:(i + 1) * per] for i in range(n)]).astype(np.int32)
     eng = make_engine(CFG, wg, block_size=bs, num_blocks=nb, max_blocks_per_seq=per,
-                      max_rows=256, max_seqs=8, max_position=per * bs)
+                      max_rows=256, max_seqs=8, max_position=per * bs, **(kv or {}))
     pool = om.paged_pool(nb, bs)
     ctx = [0] * n
     last = [None] * n
@@ -78,6 +80,8 @@ def run_schedule(tiny, prompts, n_decode, chunk, bs, nb, seed, order=None):
             if wt:
                 last[i] = int(ref_tok[o])  # teacher forcing with the oracle's token
                 o += 1
+    if final is not None:
+        final(eng, pool, tables, ctx)
     eng.close()
     return results
 
