@@ -463,12 +463,48 @@ def cb_requests(seed, n, vocab, prompt_range=(16, 512), new_range=(2, 300)):
 
 
 def bench_cb2b(args):
-    for line in run_cb2b([int(b) for b in args.cb_slots.split(",")], args.cb_steps,
-                         [int(x) for x in args.cb_pacing.split(",")]):
+    runs = [(int(x), False, 0) for x in args.cb_pacing.split(",")]
+    if args.cb_graph:  # graph replay against the same loop eagerly, both with max_ctx rounded
+        runs += [(0, False, 256), (0, True, 256)]
+    for line in run_cb2b([int(b) for b in args.cb_slots.split(",")], args.cb_steps, runs):
         print(json.dumps(line), flush=True)
 
 
-def run_cb2b(slot_counts, n_steps, pacings):
+def host_enqueue_cost(eng, Bn, ctx=256, n=8):
+    """Host time to enqueue one decode step of B rows (contexts `ctx`),
+    eagerly (every launch) and as one graph launch (after its recording),
+    each over n steps queued back to back; the GPU work is then drained.
+    Block contents are whatever the pool holds: only the host side is timed."""
+    import torch
+    bs = eng.block_size
+    nb = -(-(ctx + 1) // bs)
+    tables = np.arange(Bn * nb, dtype=np.int32).reshape(Bn, nb) % eng.num_blocks
+    meta = eng.upload_step(slots=list(range(Bn)), block_tables=tables, ctx_lens=[ctx] * Bn,
+                           n_new=[1] * Bn, tokens=[1] * Bn, want_token=[1] * Bn)
+    tk = torch.empty(Bn, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    res = {"workload": "2b-28layer host enqueue cost", "slots": Bn, "ctx": ctx, "steps": n}
+    with torch.cuda.stream(s):
+        eng.step_forward_graph(meta, None, tk, s)  # recorded here, outside the timing
+        s.synchronize()
+        for name, fn in (("eager", eng.step_forward), ("graph", eng.step_forward_graph)):
+            fn(meta, None, tk, s)
+            s.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn(meta, None, tk, s)
+            t1 = time.perf_counter()
+            s.synchronize()
+            t2 = time.perf_counter()
+            res[f"{name}_enqueue_us_per_step"] = 1e6 * (t1 - t0) / n
+            res[f"{name}_ms_per_step"] = 1e3 * (t2 - t0) / n
+    log(f"[bench] 2B B={Bn} host enqueue per step: eager {res['eager_enqueue_us_per_step']:.0f} us, "
+        f"graph {res['graph_enqueue_us_per_step']:.0f} us; queued steps {res['eager_ms_per_step']:.3f} "
+        f"vs {res['graph_ms_per_step']:.3f} ms")
+    return res
+
+
+def run_cb2b(slot_counts, n_steps, runs):
     """Continuous batching on the full 2B-shaped decoder (28 layers, d_model
     2048, 16/8 heads, FFN 6144, vocab 151936): B slots, prompts 16..512,
     answers 2..300 tokens (EOS id 0), 32-position blocks, 16 blocks per slot,
@@ -477,7 +513,10 @@ def run_cb2b(slot_counts, n_steps, pacings):
     cbd_sched_step (plan, upload, step, tokens back, commit), timed on the
     host clock around the call. Each pacing of prefill against decode runs
     the same request stream: time to first token is taken from a request's
-    submission to the end of the step that emitted its first token."""
+    submission to the end of the step that emitted its first token.
+    runs: (pacing, graph replay of decode-only steps, max_ctx rounding of
+    decode-only steps). With a graph run, the host's enqueue cost of one
+    decode step, eager and graph, is measured too."""
     import torch
     from continuous_batching_decode_forward_amd import configs, synth
     from continuous_batching_decode_forward_amd.engine import ComposerLoop, Engine
@@ -496,9 +535,11 @@ def run_cb2b(slot_counts, n_steps, pacings):
                      block_order=order)
         reqs = cb_requests(seed + Bn, 4096, shape.vocab)
 
-        def run(steps, first, pacing):
+        def run(steps, first, pacing, graph, ctx_round):
             loop = ComposerLoop(eng, max_rows=chunk + Bn, chunk_size=chunk, eos_id=0,
-                                pacing=pacing)
+                                pacing=pacing, ctx_round=ctx_round, graph_decode=graph)
+            if loop.stream is None:  # eager loops step on a side stream too
+                loop.stream = torch.cuda.Stream()
             nxt, rec, submitted, ttft = first, [], {}, []
             try:
                 for _ in range(steps):
@@ -521,11 +562,13 @@ def run_cb2b(slot_counts, n_steps, pacings):
                 loop.close()
             return rec, fin, ttft
 
-        for pacing in pacings:
-            run(8, 10_000, pacing)  # warm-up on its own composer; closing it frees every slot and block
+        for pacing, graph, ctx_round in runs:
+            # warm-up on its own composer; closing it frees every slot and block
+            run(8, 10_000, pacing, graph, ctx_round)
             torch.cuda.synchronize()
+            g0 = eng.graph_stats()
             t0 = time.perf_counter()
-            rec, fin, ttft = run(n_steps, 0, pacing)
+            rec, fin, ttft = run(n_steps, 0, pacing, graph, ctx_round)
             wall = time.perf_counter() - t0
             if eng.status():
                 raise RuntimeError("device status set")
@@ -536,7 +579,10 @@ def run_cb2b(slot_counts, n_steps, pacings):
             d_rows = sum(r[2] for r in dec)
             d_bytes = sum(step_bytes(shape, r[4], r[3]) for r in dec)
             tt = np.array(ttft) * 1e3
+            g1 = eng.graph_stats()
             line = {"workload": wlc.name, "slots": Bn, "pacing": names[pacing], "steps": n_steps,
+                    "graph_replay": bool(graph), "ctx_round": ctx_round,
+                    "graphs_recorded": g1[0] - g0[0], "graph_replays": g1[1] - g0[1],
                     "wall_s": wall, "generated_tokens": gen, "tokens_per_s": gen / wall,
                     "finished_requests": len(fin),
                     "ttft_ms": {"n": int(tt.size), "mean": float(tt.mean()) if tt.size else None,
@@ -550,9 +596,13 @@ def run_cb2b(slot_counts, n_steps, pacings):
                     "mixed_steps": len(mixed),
                     "mixed_ms_per_step": 1e3 * sum(r[0] for r in mixed) / max(len(mixed), 1),
                     "prefill_rows": sum(r[1] for r in rec)}
-            log(f"[bench] 2B loop B={Bn} {names[pacing]}: {line['tokens_per_s']:.0f} tok/s, "
-                f"decode {line['decode_ms_per_step']:.3f} ms/step, ttft p50 {line['ttft_ms']['p50']}")
+            log(f"[bench] 2B loop B={Bn} {names[pacing]}{' graph' if graph else ''}"
+                f"{f' ctx_round {ctx_round}' if ctx_round else ''}: {line['tokens_per_s']:.0f} tok/s, "
+                f"decode {line['decode_ms_per_step']:.3f} ms/step, "
+                f"ttft p50 {line['ttft_ms']['p50']}")
             out.append(line)
+        if any(g for _, g, _ in runs):
+            out.append(host_enqueue_cost(eng, Bn))
         eng.close()
     del wg
     torch.cuda.empty_cache()
@@ -584,6 +634,9 @@ def main():
                     help="the sampled workload over an 8-bit (E4M3) KV cache")
     ap.add_argument("--cb-slots", default="8,32", help="slot counts of the 2B loop workload")
     ap.add_argument("--cb-steps", type=int, default=256, help="steps of the 2B loop workload")
+    ap.add_argument("--cb-graph", type=int, default=1,
+                    help="also run the loop with graph replay of decode-only steps, against the "
+                         "same loop eagerly (both with max_ctx rounded up to 256)")
     ap.add_argument("--cb-pacing", default="0,1,2",
                     help="pacings of the 2B loop workload: 0 prefill first, 1 Albatross, "
                          "2 prefill apart from decode")

@@ -27,6 +27,8 @@ CBD_STATUS_BAD_SHAPE = 0x8
 CBD_KV_BF16 = 0
 CBD_KV_FP8_E4M3 = 1
 
+CBD_GRAPH_CACHE = 16
+
 CBD_MODE_GREEDY = 0
 CBD_MODE_SAMPLE = 1
 
@@ -124,7 +126,8 @@ class cbd_sched_config(C.Structure):
                 ("max_blocks_per_seq", C.c_int32), ("max_rows", C.c_int32),
                 ("chunk_size", C.c_int32), ("eos_id", C.c_int32), ("policy", C.c_int32),
                 ("pacing", C.c_int32), ("max_prefill", C.c_int32),
-                ("decode_prefill_ratio", C.c_int32), ("min_forward_seq_len", C.c_int32)]
+                ("decode_prefill_ratio", C.c_int32), ("min_forward_seq_len", C.c_int32),
+                ("ctx_round", C.c_int32), ("graph_decode", C.c_int32)]
 
 
 class cbd_plan(C.Structure):
@@ -157,6 +160,8 @@ SIGNATURES = [
     ("cbd_block_free", C.c_int, [VP, C.c_int32, I32P]),
     ("cbd_blocks_available", C.c_int, [VP]),
     ("cbd_step_forward", C.c_int, [VP, C.POINTER(cbd_step), VP, VP, VP]),
+    ("cbd_step_forward_graph", C.c_int, [VP, C.POINTER(cbd_step), VP, VP, VP]),
+    ("cbd_graph_stats", C.c_int, [VP, C.POINTER(C.c_int64)]),
     ("cbd_sample_logits", C.c_int, [VP, VP, C.c_int32, VP, VP, VP, VP]),
     ("cbd_sample_logits_noalloc", C.c_int, [VP, VP, C.c_int32, VP, VP, VP, VP]),
     ("cbd_engine_status", C.c_int, [VP, VP, C.POINTER(C.c_uint32)]),
@@ -277,6 +282,17 @@ def cbd_blocks_available(engine) -> int:
 
 def cbd_step_forward(engine, step: cbd_step, logits_out, tokens_out, stream) -> None:
     _call("cbd_step_forward", engine, C.byref(step), logits_out, tokens_out, stream)
+
+
+def cbd_step_forward_graph(engine, step: cbd_step, logits_out, tokens_out, stream) -> None:
+    _call("cbd_step_forward_graph", engine, C.byref(step), logits_out, tokens_out, stream)
+
+
+def cbd_graph_stats(engine) -> tuple:
+    """(graphs recorded, graphs replayed, graphs cached)."""
+    out = (C.c_int64 * 3)()
+    _call("cbd_graph_stats", engine, out)
+    return tuple(int(v) for v in out)
 
 
 def cbd_sample_logits(engine, logits, n: int, slots, step_ids, tokens_out, stream) -> None:

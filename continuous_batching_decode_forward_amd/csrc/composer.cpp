@@ -207,7 +207,8 @@ int cbd_sched_create(const cbd_sched_config* cfg, cbd_engine* engine, const int3
       cfg->max_blocks_per_seq < 1 || cfg->max_rows < 1 || cfg->chunk_size < 1 ||
       cfg->policy < CBD_ADMIT_RESERVE || cfg->policy > CBD_ADMIT_REQUEST_LEVEL ||
       cfg->pacing < CBD_PACE_PREFILL_FIRST || cfg->pacing > CBD_PACE_SEPARATE ||
-      cfg->max_prefill < 0 || cfg->decode_prefill_ratio < 0 || cfg->min_forward_seq_len < 0)
+      cfg->max_prefill < 0 || cfg->decode_prefill_ratio < 0 || cfg->min_forward_seq_len < 0 ||
+      cfg->ctx_round < 0 || cfg->graph_decode < 0 || cfg->graph_decode > 1)
     return fail(CBD_E_INVAL, "composer config out of range");
   // With an engine, every plan the composer can make must be a step the
   // engine accepts: its sequences (at most max_slots) fit max_seqs, and a
@@ -453,10 +454,21 @@ int cbd_sched_step(cbd_sched* s, int32_t mode, int32_t* meta_dev, int32_t* host_
   st.tokens = put(p.tokens, (size_t)p.n_rows);
   st.want_token = put(p.want_token, n);
   st.step_ids = put(p.step_ids, n);
+  // A decode-only step may take a rounded-up max_ctx (any upper bound is
+  // valid) so that consecutive steps share one launch plan, and replay a
+  // recorded graph of it.
+  const bool decode_only = p.n_prefill_rows == 0;
+  if (decode_only && s->cfg.ctx_round > 0) {
+    const int64_t q = s->cfg.ctx_round;
+    const int64_t r = ((int64_t)st.max_ctx + q - 1) / q * q;
+    st.max_ctx = (int32_t)std::min<int64_t>(r, s->engine->cfg.max_position);
+  }
   hipStream_t hs = (hipStream_t)stream;
   hipError_t he = hipMemcpyAsync(meta_dev, host_stage, o * sizeof(int32_t), hipMemcpyHostToDevice, hs);
   if (he != hipSuccess) return fail(CBD_E_DEVICE, std::string("step metadata upload: ") + hipGetErrorString(he));
-  rc = cbd_step_forward(s->engine, &st, logits_out, tokens_dev, stream);
+  rc = decode_only && s->cfg.graph_decode
+           ? cbd_step_forward_graph(s->engine, &st, logits_out, tokens_dev, stream)
+           : cbd_step_forward(s->engine, &st, logits_out, tokens_dev, stream);
   if (rc != CBD_OK) {
     // The upload may still be reading host_stage: drain the stream before
     // handing the buffer back (the error message of the step is kept).

@@ -157,6 +157,7 @@ void* cbd_engine::pool_v(int layer) const {
 
 cbd_engine::~cbd_engine() {
   for (hipEvent_t ev : prof_events) (void)hipEventDestroy(ev);
+  for (GraphEntry& g : graphs) (void)hipGraphExecDestroy(g.exec);
 }
 
 // Record one event of a start/stop pair when `cls` is being profiled.
@@ -424,8 +425,8 @@ int cbd_engine_status(cbd_engine* e, void* stream, uint32_t* flags) {
 
 // ---------------------------------------------------------------- the step
 
-int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_t* tokens_out,
-                     void* stream) {
+// Host-side checks of a step (before anything is enqueued).
+static int check_step(cbd_engine* e, const cbd_step* s, const int32_t* tokens_out) {
   if (!e || !s) return fail(CBD_E_INVAL, "NULL engine or step");
   const cbd_config& c = e->cfg;
   if (s->n_seqs < 1 || s->n_seqs > c.max_seqs) return fail(CBD_E_INVAL, "n_seqs out of range");
@@ -441,8 +442,13 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
       !s->want_token || (s->mode == CBD_MODE_SAMPLE && !s->step_ids))
     return fail(CBD_E_INVAL, "a step array is NULL");
   if (s->n_out > 0 && !tokens_out) return fail(CBD_E_INVAL, "tokens_out is NULL");
+  return CBD_OK;
+}
 
-  hipStream_t st = (hipStream_t)stream;
+// The step's launches on `st` (a checked step).
+static int enqueue_step(cbd_engine* e, const cbd_step* s, float* logits_out, int32_t* tokens_out,
+                        hipStream_t st) {
+  const cbd_config& c = e->cfg;
   const int R = s->n_rows;
   uint32_t* status = e->wsp<uint32_t>(e->ws.status);
   StepMeta m{s->n_seqs, s->n_rows, s->n_out, s->max_blocks_per_seq, s->slots, s->block_tables,
@@ -553,6 +559,79 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_
                            e->wsp<float>(e->ws.smp), tokens_out, status, st));
   }
   HIP_TRY(e->prof_mark(CBD_KERNEL_SAMPLE, st));
+  return CBD_OK;
+}
+
+int cbd_step_forward(cbd_engine* e, const cbd_step* s, float* logits_out, int32_t* tokens_out,
+                     void* stream) {
+  const int rc = check_step(e, s, tokens_out);
+  if (rc != CBD_OK) return rc;
+  return enqueue_step(e, s, logits_out, tokens_out, (hipStream_t)stream);
+}
+
+// Graph replay: a step shape is every field of the step (host scalars and
+// the device pointers the kernels are given) and the two output pointers;
+// the launch plan and every kernel argument follow from it, so one recorded
+// graph serves every step of that shape.
+int cbd_step_forward_graph(cbd_engine* e, const cbd_step* s, float* logits_out,
+                           int32_t* tokens_out, void* stream) {
+  int rc = check_step(e, s, tokens_out);
+  if (rc != CBD_OK) return rc;
+  if (!stream) return fail(CBD_E_INVAL, "graph replay needs a stream other than the null stream");
+  if (e->prof_class != 0) return fail(CBD_E_INVAL, "graph replay while a kernel class is profiled");
+  hipStream_t st = (hipStream_t)stream;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIP_TRY(hipStreamIsCapturing(st, &cs));
+  if (cs != hipStreamCaptureStatusNone) return enqueue_step(e, s, logits_out, tokens_out, st);
+  cbd_engine::GraphKey key;
+  memset(&key, 0, sizeof key);
+  key.step = *s;
+  key.logits = logits_out;
+  key.tokens = tokens_out;
+  ++e->graph_clock;
+  for (cbd_engine::GraphEntry& g : e->graphs) {
+    if (memcmp(&g.key, &key, sizeof key) == 0) {
+      g.used = e->graph_clock;
+      HIP_TRY(hipGraphLaunch(g.exec, st));
+      ++e->graph_replays;
+      return CBD_OK;
+    }
+  }
+  // Record the step's launches (relaxed mode: the first launch of a kernel
+  // with more than 64 KB of LDS sets its attribute during the capture).
+  HIP_TRY(hipStreamBeginCapture(st, hipStreamCaptureModeRelaxed));
+  rc = enqueue_step(e, s, logits_out, tokens_out, st);
+  const std::string msg = rc != CBD_OK ? std::string(cbd_last_error()) : std::string();
+  hipGraph_t graph = nullptr;
+  const hipError_t ee = hipStreamEndCapture(st, &graph);
+  if (rc != CBD_OK || ee != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    if (rc != CBD_OK) return fail(rc, msg);
+    return fail(CBD_E_DEVICE, std::string("graph capture: ") + hipGetErrorString(ee));
+  }
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (ei != hipSuccess) return fail(CBD_E_DEVICE, std::string("graph instantiate: ") + hipGetErrorString(ei));
+  if (e->graphs.size() >= CBD_GRAPH_CACHE) {  // drop the least recently used
+    size_t old = 0;
+    for (size_t i = 1; i < e->graphs.size(); ++i)
+      if (e->graphs[i].used < e->graphs[old].used) old = i;
+    HIP_TRY(hipStreamSynchronize(st));  // it may still be running
+    (void)hipGraphExecDestroy(e->graphs[old].exec);
+    e->graphs.erase(e->graphs.begin() + old);
+  }
+  e->graphs.push_back(cbd_engine::GraphEntry{key, exec, e->graph_clock});
+  ++e->graph_captures;
+  HIP_TRY(hipGraphLaunch(exec, st));
+  return CBD_OK;
+}
+
+int cbd_graph_stats(const cbd_engine* e, int64_t out[3]) {
+  if (!e || !out) return fail(CBD_E_INVAL, "NULL engine or output");
+  out[0] = e->graph_captures;
+  out[1] = e->graph_replays;
+  out[2] = (int64_t)e->graphs.size();
   return CBD_OK;
 }
 

@@ -171,8 +171,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a,
 // has NW = 4 or 8 waves: 8 halve the activation copies per weight byte, which
 // pays on the LM head at 64 rows (173 -> 163 us) but not on the narrower
 // layer matrices, whose grids then leave CUs idle.
+// The grid is one-dimensional with the K split varying fastest: workgroup i
+// runs on XCD i mod 8, so at 8 splits each XCD holds one split (and reads
+// one eighth of the activation into its L2), at 4 splits each split sits on
+// two XCDs. Numbered column-group first, every XCD would fetch the whole
+// activation: at 64 rows that was 8 of the 46 MB the O projection moved.
 template <int RT, int NT, int D, int NW, int EPI>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_kernel(GemmArgs a, int kc, int S) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_kernel(GemmArgs a, int kc, int S, int n_groups) {
   constexpr int NM = EpiTraits<EPI>::NM;
   constexpr int BLK = RT * 4;                 // 1 KB LDS blocks per stage
   constexpr int CPW = BLK / NW;               // activation copies per wave per stage
@@ -183,10 +188,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int tile = blockIdx.x * NW + wave;
+  const int ks = blockIdx.x % S;
+  const int grp = blockIdx.x / S;
+  const int tile = (grp % n_groups) * NW + wave;
   const int n0 = tile * (16 * NT);
-  const int ks = blockIdx.y;
-  const int r0 = blockIdx.z * (16 * RT);
+  const int r0 = (grp / n_groups) * (16 * RT);
   const int K = a.K, N = a.N, R = a.R;
   const int kbeg = ks * kc;                   // a multiple of 64
   const int kend = min(K, kbeg + kc);
@@ -658,8 +664,8 @@ static hipError_t launch_stream(const GemmArgs& a, int S, hipStream_t st) {
   S = split_k(a.K, S, 64, &kc);
   if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 64, &kc);
   const size_t lds = (size_t)D * RT * 4 * 1024;  // <= 64 KB for the shapes instantiated
-  gemm_stream_kernel<RT, NT, D, NW, EPI><<<dim3(n_groups, S, r_groups), 64 * NW, lds, st>>>(
-      a, kc, S);
+  gemm_stream_kernel<RT, NT, D, NW, EPI><<<(unsigned)(n_groups * S * r_groups), 64 * NW, lds, st>>>(
+      a, kc, S, n_groups);
   return finish_splits<EPI>(a, S, st);
 }
 

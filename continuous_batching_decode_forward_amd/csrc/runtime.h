@@ -137,6 +137,20 @@ struct cbd_engine {
   cbd::SlotAllocator slots;
   cbd::BlockAllocator blocks;
   std::vector<cbd::SlotParams> host_params;
+  // recorded step graphs (cbd_step_forward_graph), least recently used first out
+  struct GraphKey {
+    cbd_step step;
+    float* logits;
+    int32_t* tokens;
+  };
+  struct GraphEntry {
+    GraphKey key;
+    hipGraphExec_t exec;
+    uint64_t used;
+  };
+  std::vector<GraphEntry> graphs;
+  uint64_t graph_clock = 0;
+  int64_t graph_captures = 0, graph_replays = 0;
   // profiling: event pairs around launches of one kernel class
   int32_t prof_class = 0;
   std::vector<hipEvent_t> prof_events;  // created lazily, reused

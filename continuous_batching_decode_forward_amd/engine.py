@@ -134,6 +134,16 @@ class Engine:
         B.cbd_step_forward(self.handle, meta.step, _ptr(logits_out), _ptr(tokens_out),
                            _stream_ptr(stream))
 
+    def step_forward_graph(self, meta: StepMeta, logits_out: torch.Tensor | None,
+                           tokens_out: torch.Tensor, stream) -> None:
+        """The step replayed from a recorded HIP graph (one per step shape);
+        `stream` must be a side stream, not the null stream."""
+        B.cbd_step_forward_graph(self.handle, meta.step, _ptr(logits_out), _ptr(tokens_out),
+                                 _stream_ptr(stream))
+
+    def graph_stats(self) -> tuple:
+        return B.cbd_graph_stats(self.handle)
+
     def sample_logits(self, logits: torch.Tensor, slots: torch.Tensor, step_ids: torch.Tensor,
                       tokens_out: torch.Tensor, stream=None) -> None:
         B.cbd_sample_logits(self.handle, _ptr(logits), logits.shape[0], _ptr(slots),
@@ -195,7 +205,7 @@ class ComposerLoop:
                  policy: int = B.CBD_ADMIT_RESERVE, max_slots: int | None = None,
                  max_blocks_per_seq: int | None = None, pacing: int = B.CBD_PACE_PREFILL_FIRST,
                  max_prefill: int = 0, decode_prefill_ratio: int = 0,
-                 min_forward_seq_len: int = 0):
+                 min_forward_seq_len: int = 0, ctx_round: int = 0, graph_decode: bool = False):
         cfg = B.cbd_sched_config()
         cfg.max_slots = max_slots or eng.cfg.max_slots
         cfg.block_size, cfg.num_blocks = eng.block_size, eng.num_blocks
@@ -203,12 +213,16 @@ class ComposerLoop:
         cfg.max_rows, cfg.chunk_size, cfg.eos_id, cfg.policy = max_rows, chunk_size, eos_id, policy
         cfg.pacing, cfg.max_prefill = pacing, max_prefill
         cfg.decode_prefill_ratio, cfg.min_forward_seq_len = decode_prefill_ratio, min_forward_seq_len
+        cfg.ctx_round, cfg.graph_decode = ctx_round, int(graph_decode)
         self.cfg, self.eng = cfg, eng
         self.handle = B.cbd_sched_create(cfg, eng.handle)
         n = B.cbd_sched_meta_ints(cfg)
         self.meta_dev = torch.empty(n, dtype=torch.int32, device=eng.device)
         self.host = torch.empty(n, dtype=torch.int32, pin_memory=True)
         self.tokens_dev = torch.empty(cfg.max_slots, dtype=torch.int32, device=eng.device)
+        # graph replay records by stream capture, which the null stream does
+        # not allow: such a loop steps on its own side stream by default
+        self.stream = torch.cuda.Stream(device=eng.device) if graph_decode else None
 
     def submit(self, prompt, max_new: int, params=None, request_id: int = 0) -> None:
         B.cbd_sched_submit(self.handle, prompt, max_new, params, request_id)
@@ -218,7 +232,7 @@ class ComposerLoop:
         return B.cbd_sched_step(self.handle, mode, self.meta_dev.data_ptr(),
                                 self.host.data_ptr(), self.tokens_dev.data_ptr(),
                                 None if logits_out is None else logits_out.data_ptr(),
-                                _stream_ptr(stream).value)
+                                _stream_ptr(stream if stream is not None else self.stream).value)
 
     def last_tokens(self, n: int) -> np.ndarray:
         """The tokens the last step committed (host staging copy)."""

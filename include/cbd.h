@@ -249,6 +249,29 @@ typedef struct cbd_step {
 int cbd_step_forward(cbd_engine* e, const cbd_step* step, float* logits_out,
                      int32_t* tokens_out, void* stream);
 
+/* The same step replayed from a HIP graph (the RWKV-Runner Albatross
+ * article's follow-up route, "边界与后续路线": graph-captured decode).
+ * Contract, checks and results are those of cbd_step_forward. The first
+ * call for a step shape -- every field of `step` (the host scalars and the
+ * device array pointers) together with logits_out and tokens_out -- records
+ * the step's launches into a graph on `stream` and instantiates it; every
+ * later call with the same shape launches that graph, which reads the
+ * step's current metadata through the same device pointers. A caller that
+ * wants replays keeps its metadata buffer in place and passes a max_ctx
+ * that stays fixed across steps (any upper bound of ctx_lens + n_new is
+ * valid, e.g. rounded up to a multiple of 256). The engine keeps the
+ * CBD_GRAPH_CACHE most recently used graphs, destroying the oldest.
+ * `stream` must not be the null stream (CBD_E_INVAL; a graph is recorded
+ * by stream capture). On a stream that is already being captured the
+ * launches are recorded into the caller's capture, as cbd_step_forward's
+ * would be. Not while a kernel class is being profiled (CBD_E_INVAL). */
+#define CBD_GRAPH_CACHE 16
+int cbd_step_forward_graph(cbd_engine* e, const cbd_step* step, float* logits_out,
+                           int32_t* tokens_out, void* stream);
+/* Graphs recorded (out[0]) and replayed (out[1]) by cbd_step_forward_graph
+ * since the engine was created, and graphs cached now (out[2]). */
+int cbd_graph_stats(const cbd_engine* e, int64_t out[3]);
+
 /* The batched sampler alone, over caller-given fp32 logits [n][vocab]
  * (device): row j uses slot slots[j] and draw counter step_ids[j] (device
  * arrays). Updates the slots' penalty counts like a sampled step. The slots
@@ -379,6 +402,12 @@ typedef struct cbd_sched_config {
   int32_t max_prefill;
   int32_t decode_prefill_ratio;
   int32_t min_forward_seq_len;
+  /* Decode-only steps (no prefill rows) in cbd_sched_step: ctx_round > 0
+   * rounds the step's max_ctx up to a multiple of ctx_round (at most the
+   * engine's max_position), so that it stays fixed over many steps;
+   * graph_decode = 1 runs them through cbd_step_forward_graph. */
+  int32_t ctx_round;
+  int32_t graph_decode;
 } cbd_sched_config;
 
 /* One planned step, in host memory owned by the composer and valid until
