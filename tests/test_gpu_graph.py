@@ -218,3 +218,54 @@ def test_composer_loop_with_graph_replay_equals_the_eager_loop():
           f"{s1[1]} replays")
     assert t0 == t1
     assert f0 == f1 and len(f0) == len(reqs)
+
+
+def test_graph_cache_keeps_the_16_most_recent_shapes():
+    """Eighteen step shapes (1..6 sequences x three max_ctx bounds) through
+    cbd_step_forward_graph, each equal to the eager step bit for bit; the
+    cache then holds the 16 most recent, and the first shape, evicted, is
+    recorded again (and still equal)."""
+    from continuous_batching_decode_forward_amd import binding as Bd
+    torch.cuda.set_device(0)
+    shape, Bmax = configs.TINY, 6
+    wg = synth.make_weights(shape, seed=4, device="cuda")
+    wl = bench.build_workload(shape, Bmax, 4, ctx_range=(20, 200), bs=32)
+    eng = Engine(shape, wg, block_size=32, num_blocks=wl["total"], max_blocks_per_seq=wl["mbps"],
+                 max_slots=Bmax, max_rows=Bmax, max_seqs=Bmax, max_position=1024)
+    s = torch.cuda.Stream()
+    lg = torch.empty((Bmax, shape.vocab), dtype=torch.float32, device="cuda")
+    tk = torch.empty(Bmax, dtype=torch.int32, device="cuda")
+    try:
+        bench.fill_pool(eng, 4, wl["perm"])
+        metas = []
+        for i in range(18):
+            n = 1 + i % 6
+            bound = int(wl["ctx"][:n].max()) + 1 + 64 * (i // 6)  # three distinct bounds
+            metas.append(eng.upload_step(slots=list(range(n)), block_tables=wl["tables"][:n],
+                                         ctx_lens=wl["ctx"][:n], n_new=[1] * n,
+                                         tokens=wl["tokens"][:n], want_token=[1] * n,
+                                         max_ctx=bound))
+
+        def both(m):
+            n = m.n_seqs
+            with torch.cuda.stream(s):
+                eng.step_forward(m, lg, tk, s)
+            torch.cuda.synchronize()
+            ref = (lg[:n].clone(), tk[:n].clone())
+            lg.fill_(float("nan"))
+            tk.fill_(-1)
+            with torch.cuda.stream(s):
+                eng.step_forward_graph(m, lg, tk, s)
+            torch.cuda.synchronize()
+            assert torch.equal(lg[:n], ref[0]) and torch.equal(tk[:n], ref[1])
+
+        for m in metas:
+            both(m)
+        assert eng.graph_stats() == (18, 0, Bd.CBD_GRAPH_CACHE)
+        both(metas[-1])                      # the most recent: replayed
+        assert eng.graph_stats() == (18, 1, Bd.CBD_GRAPH_CACHE)
+        both(metas[0])                       # evicted: recorded again
+        assert eng.graph_stats() == (19, 1, Bd.CBD_GRAPH_CACHE)
+        assert eng.status() == 0
+    finally:
+        eng.close()
