@@ -478,7 +478,11 @@ int cbd_sched_stats_get(const cbd_sched* s, cbd_sched_stats* out);
  * block tables, ctx_lens, n_new, tokens, want_token, step_ids, in that
  * order) into host_stage (host, cbd_sched_meta_ints int32; page-locked
  * memory makes the upload asynchronous) and copy them to meta_dev (device,
- * same size); run cbd_step_forward with `mode` on `stream`; copy the step's
+ * same size); run cbd_step_forward with `mode` on `stream` (a decode-only
+ * step with graph_decode set: cbd_step_forward_graph, which needs a stream
+ * other than the null stream, with max_ctx rounded up by ctx_round; the
+ * staging buffers' fixed addresses let one recorded graph serve every such
+ * step of a batch size); copy the step's
  * tokens (tokens_dev: device int32 [max_slots]) back into host_stage; wait
  * for the stream; commit them. logits_out (device [max_slots][vocab] fp32)
  * is nullable. plan_out (nullable) receives the plan that ran; its arrays
