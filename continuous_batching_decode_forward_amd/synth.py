@@ -135,6 +135,55 @@ def make_weights(cfg, seed: int, device="cpu", std: float = 0.02) -> dict:
     return w
 
 
+def int8_codes(seed: int, tag: str, shape, device="cpu", chunk: int = 1 << 26) -> torch.Tensor:
+    """int8 weight codes of the given shape, element i (row-major) depending
+    only on (seed, tag, i): the Irwin-Hall sum of 4 hash bytes scaled to a
+    standard deviation of about 40 in integer arithmetic, clamped to
+    [-127, 127]."""
+    n = int(np.prod(shape))
+    out = torch.empty(n, dtype=torch.int8, device=device)
+    key = tag_key(seed, tag)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        h = hash_stream(key, torch.arange(s, e, dtype=torch.int64, device=device))
+        t = (h & 255) + ((h >> 8) & 255) + ((h >> 16) & 255) + ((h >> 24) & 255) - 510
+        out[s:e] = torch.clamp(torch.div(t * 35 + 64, 128, rounding_mode="floor"), -127, 127).to(torch.int8)
+    return out.view(*shape)
+
+
+def row_scales(seed: int, tag: str, n: int, std: float, device="cpu") -> torch.Tensor:
+    """float32 per-row scales std / 40 * (0.75 + 0.5 u), u uniform on [0, 1)
+    from the hash, so that codes of standard deviation 40 dequantise to
+    about `std`, with rows of different scales."""
+    h = hash_stream(tag_key(seed, tag), torch.arange(n, dtype=torch.int64, device=device))
+    u = (h & 0xFFFF).to(torch.float32) / 65536.0
+    return (np.float32(std / 40.0) * (0.75 + 0.5 * u)).to(torch.float32)
+
+
+def make_weights_int8(cfg, seed: int, device="cpu", std: float = 0.02) -> dict:
+    """Weight-only int8: every projection (QKV, O, gate, up, down per layer,
+    and the LM head) as int8 codes [rows][cols] with one float32 scale per
+    row (s_qkv ... s_down, lm_head_scale); the embedding (bf16 ~N(0, std^2))
+    and the RMSNorm gains (1.0) as make_weights makes them."""
+    shapes = weight_shapes(cfg)
+    w = {"embed": normal_tensor(seed, "embed", shapes["embed"], std, device),
+         "final_norm": torch.ones(shapes["final_norm"], dtype=torch.bfloat16, device=device),
+         "lm_head": int8_codes(seed, "q.lm_head", shapes["lm_head"], device),
+         "lm_head_scale": row_scales(seed, "s.lm_head", shapes["lm_head"][0], std, device)}
+    for name in PER_LAYER:
+        w[name] = []
+        if not name.endswith("norm"):
+            w["s" + name[1:]] = []
+        for layer in range(cfg.n_layers):
+            if name.endswith("norm"):
+                w[name].append(torch.ones(shapes[name], dtype=torch.bfloat16, device=device))
+            else:
+                w[name].append(int8_codes(seed, f"q.{name}.{layer}", shapes[name], device))
+                w["s" + name[1:]].append(row_scales(seed, f"s.{name}.{layer}", shapes[name][0],
+                                                    std, device))
+    return w
+
+
 def weight_bytes(cfg) -> int:
     """Bytes of every weight read by one step (embedding rows excluded)."""
     s = weight_shapes(cfg)

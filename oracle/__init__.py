@@ -60,7 +60,11 @@ class OrModel(C.Structure):
                 ("w_o", C.POINTER(U16P)), ("ffn_norm", C.POINTER(U16P)),
                 ("w_gate", C.POINTER(U16P)), ("w_up", C.POINTER(U16P)),
                 ("w_down", C.POINTER(U16P)),
-                ("k_scale", C.c_double), ("v_scale", C.c_double)]
+                ("k_scale", C.c_double), ("v_scale", C.c_double),
+                ("w_int8", C.c_int32), ("pad_", C.c_int32), ("lm_head_scale", F32P),
+                ("s_qkv", C.POINTER(F32P)), ("s_o", C.POINTER(F32P)),
+                ("s_gate", C.POINTER(F32P)), ("s_up", C.POINTER(F32P)),
+                ("s_down", C.POINTER(F32P))]
 
 
 class OrSampling(C.Structure):
@@ -89,6 +93,7 @@ def _declare(L):
     L.or_f64_to_bf16.restype = C.c_uint16
     L.or_rmsnorm.argtypes = [F64P, U16P, C.c_int32, C.c_double, F64P]
     L.or_linear.argtypes = [F64P, C.c_int32, U16P, C.c_int32, F64P]
+    L.or_linear_i8.argtypes = [F64P, C.c_int32, C.c_void_p, F32P, C.c_int32, F64P]
     L.or_rope.argtypes = [F64P, C.c_int32, C.c_int32, C.c_double]
     L.or_attention_dense.argtypes = [F64P, U16P, U16P, C.c_int32, C.c_int32, C.c_int32,
                                      C.c_int32, F64P]
@@ -137,18 +142,39 @@ def bf16_to_f64(a) -> np.ndarray:
 
 # ------------------------------------------------------------------ model
 
+PROJ = ("w_qkv", "w_o", "w_gate", "w_up", "w_down")
+SCALES = {"w_qkv": "s_qkv", "w_o": "s_o", "w_gate": "s_gate", "w_up": "s_up", "w_down": "s_down",
+          "lm_head": "lm_head_scale"}
+
+
+def _as_np(x, dtype):
+    if isinstance(x, np.ndarray):
+        return np.ascontiguousarray(x, dtype=dtype)
+    return np.ascontiguousarray(x.detach().cpu().contiguous().numpy().astype(dtype, copy=False))
+
+
 class Model:
-    """Holds the oracle's view of a weight set (uint16 bf16 arrays) and the
-    ctypes struct pointing at them. Keep the object alive while in use."""
+    """Holds the oracle's view of a weight set (uint16 bf16 arrays, or int8
+    codes with float32 row scales for the projections) and the ctypes
+    struct pointing at them. Keep the object alive while in use."""
 
     def __init__(self, shape, weights: dict, kv_fp8: bool = False, k_scale: float = 1.0,
                  v_scale: float = 1.0):
-        """kv_fp8: the KV cache holds E4M3 codes of value / scale (else bf16)."""
+        """kv_fp8: the KV cache holds E4M3 codes of value / scale (else bf16).
+        Weights with "s_qkv" etc. entries are int8 codes read as q * scale
+        per matrix row (the LM head's scales under "lm_head_scale")."""
         self.shape = shape
         self.kv_fp8 = bool(kv_fp8)
+        self.w_int8 = "s_qkv" in weights
         self.arrays = {}
         for k, v in weights.items():
-            self.arrays[k] = [as_u16(x) for x in v] if isinstance(v, list) else as_u16(v)
+            if self.w_int8 and (k in PROJ or k == "lm_head"):
+                conv = lambda x: _as_np(x, np.int8)
+            elif self.w_int8 and k in SCALES.values():
+                conv = lambda x: _as_np(x, np.float32)
+            else:
+                conv = as_u16
+            self.arrays[k] = [conv(x) for x in v] if isinstance(v, list) else conv(v)
         m = OrModel()
         m.n_layers, m.d_model, m.n_heads = shape.n_layers, shape.d_model, shape.n_heads
         m.n_kv_heads, m.head_dim, m.ffn_dim = shape.n_kv_heads, shape.head_dim, shape.ffn_dim
@@ -156,12 +182,20 @@ class Model:
         m.kv_fp8, m.k_scale, m.v_scale = int(self.kv_fp8), float(k_scale), float(v_scale)
         m.embed = _p(self.arrays["embed"], U16P)
         m.final_norm = _p(self.arrays["final_norm"], U16P)
-        m.lm_head = _p(self.arrays["lm_head"], U16P)
+        m.lm_head = C.cast(self.arrays["lm_head"].ctypes.data, U16P)
         self._ptr_arrays = {}
         for k in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate", "w_up", "w_down"):
-            arr = (U16P * shape.n_layers)(*[_p(a, U16P) for a in self.arrays[k]])
+            arr = (U16P * shape.n_layers)(*[C.cast(a.ctypes.data, U16P) for a in self.arrays[k]])
             self._ptr_arrays[k] = arr
             setattr(m, k, C.cast(arr, C.POINTER(U16P)))
+        m.w_int8 = int(self.w_int8)
+        if self.w_int8:
+            m.lm_head_scale = _p(self.arrays["lm_head_scale"], F32P)
+            for k in PROJ:
+                sk = SCALES[k]
+                arr = (F32P * shape.n_layers)(*[_p(a, F32P) for a in self.arrays[sk]])
+                self._ptr_arrays[sk] = arr
+                setattr(m, sk, C.cast(arr, C.POINTER(F32P)))
         self.struct = m
 
     @property
@@ -236,6 +270,18 @@ def linear(x, W) -> np.ndarray:
     assert W.shape[1] == x.size
     y = np.empty(W.shape[0], np.float64)
     lib().or_linear(_p(x, F64P), W.shape[1], _p(W, U16P), W.shape[0], _p(y, F64P))
+    return y
+
+
+def linear_i8(x, Q, scale) -> np.ndarray:
+    """Q (int8 [N][K]) with row scales (float32 [N]) times x (double [K])."""
+    x = _f64(x)
+    Q = np.ascontiguousarray(Q, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    assert Q.shape[1] == x.size and scale.size == Q.shape[0]
+    y = np.empty(Q.shape[0], np.float64)
+    lib().or_linear_i8(_p(x, F64P), Q.shape[1], Q.ctypes.data, _p(scale, F32P), Q.shape[0],
+                       _p(y, F64P))
     return y
 
 

@@ -46,6 +46,12 @@
  * rounded to binary32, the precision in which the GPU takes that decision.
  * OpenMP runs only across independent rows, heads or output elements,
  * never inside a reduction.
+ *
+ * Storage formats beyond bf16 (follow-ups the pages name): an 8-bit KV cache
+ * (OCP E4M3 codes of value / scale, the "Continuous Batching" practice
+ * article, section 6) and int8 weights (codes q with one scale per matrix
+ * row, read as q * scale; the RWKV-Runner Albatross article's follow-up
+ * list). Both are defined here by their decoded values, in double.
  */
 #include <math.h>
 #include <stdint.h>
@@ -156,6 +162,17 @@ typedef struct {
   const uint16_t* const* w_up;      /* per layer [ffn][d_model] */
   const uint16_t* const* w_down;    /* per layer [d_model][ffn] */
   double k_scale, v_scale;          /* fp8 cache: value = decode(code) * scale */
+  /* w_int8: the projection matrices (QKV, O, gate, up, down, LM head) hold
+   * int8 codes q (the pointers above point at int8 [rows][cols]) read as
+   * q * scale[row]; the embedding and the norm gains stay bf16. */
+  int32_t w_int8;
+  int32_t pad_;
+  const float* lm_head_scale;       /* [vocab] */
+  const float* const* s_qkv;        /* per layer, one scale per matrix row */
+  const float* const* s_o;
+  const float* const* s_gate;
+  const float* const* s_up;
+  const float* const* s_down;
 } or_model;
 
 /* RMSNorm: y_i = x_i / sqrt(mean(x^2) + eps) * g_i. */
@@ -174,6 +191,28 @@ void or_linear(const double* x, int32_t K, const uint16_t* W, int32_t N, double*
     for (int32_t k = 0; k < K; ++k) s += x[k] * bf(w[k]);
     y[n] = s;
   }
+}
+
+/* Weight-only int8 (the RWKV-Runner Albatross article lists int8 weights
+ * as a follow-up): y[n] = scale[n] * sum_k x[k] * Q[n][k], Q row-major
+ * [N][K] int8, one scale per output row. */
+void or_linear_i8(const double* x, int32_t K, const int8_t* Q, const float* scale, int32_t N,
+                  double* y) {
+  for (int32_t n = 0; n < N; ++n) {
+    const int8_t* q = Q + (size_t)n * K;
+    double s = 0.0;
+    for (int32_t k = 0; k < K; ++k) s += x[k] * (double)q[k];
+    y[n] = (double)scale[n] * s;
+  }
+}
+
+/* A projection of the model: bf16 weights, or int8 codes with row scales. */
+static void project(const or_model* m, const uint16_t* W, const float* scale, const double* x,
+                    int32_t K, int32_t N, double* y) {
+  if (m->w_int8)
+    or_linear_i8(x, K, (const int8_t*)(const void*)W, scale, N, y);
+  else
+    or_linear(x, K, W, N, y);
 }
 
 /* RoPE, rotate-half pairing: element i pairs with i + hd/2, angle
@@ -314,7 +353,7 @@ static int row_pre_attention(const or_model* m, int32_t layer, const or_kv* kv,
                              double* acc) {
   int32_t d = m->d_model, hd = m->head_dim, hq = m->n_heads, hkv = m->n_kv_heads;
   or_rmsnorm(x, m->attn_norm[layer], d, m->rms_eps, hbuf);
-  or_linear(hbuf, d, m->w_qkv[layer], qkv_width(m), acc);
+  project(m, m->w_qkv[layer], m->w_int8 ? m->s_qkv[layer] : NULL, hbuf, d, qkv_width(m), acc);
   memcpy(q, acc, sizeof(double) * (size_t)hq * hd);
   for (int32_t h = 0; h < hq; ++h) or_rope(q + (size_t)h * hd, hd, pos, m->rope_base);
   for (int32_t g = 0; g < hkv; ++g) {
@@ -368,16 +407,16 @@ static int row_attention(const or_model* m, int32_t layer, const or_kv* kv,
 static void row_post_attention(const or_model* m, int32_t layer, double* x, const double* o,
                                double* hbuf, double* acc, double* acc2) {
   int32_t d = m->d_model, f = m->ffn_dim, qd = m->n_heads * m->head_dim;
-  or_linear(o, qd, m->w_o[layer], d, acc);
+  project(m, m->w_o[layer], m->w_int8 ? m->s_o[layer] : NULL, o, qd, d, acc);
   for (int32_t i = 0; i < d; ++i) x[i] += acc[i];
   or_rmsnorm(x, m->ffn_norm[layer], d, m->rms_eps, hbuf);
-  or_linear(hbuf, d, m->w_gate[layer], f, acc);
-  or_linear(hbuf, d, m->w_up[layer], f, acc2);
+  project(m, m->w_gate[layer], m->w_int8 ? m->s_gate[layer] : NULL, hbuf, d, f, acc);
+  project(m, m->w_up[layer], m->w_int8 ? m->s_up[layer] : NULL, hbuf, d, f, acc2);
   for (int32_t i = 0; i < f; ++i) {
     double g = acc[i];
     acc[i] = g / (1.0 + exp(-g)) * acc2[i]; /* silu(gate) * up */
   }
-  or_linear(acc, f, m->w_down[layer], d, acc2);
+  project(m, m->w_down[layer], m->w_int8 ? m->s_down[layer] : NULL, acc, f, d, acc2);
   for (int32_t i = 0; i < d; ++i) x[i] += acc2[i];
 }
 
@@ -388,9 +427,15 @@ static void row_logits(const or_model* m, const double* x, double* logits) {
   or_rmsnorm(x, m->final_norm, d, m->rms_eps, h);
 #pragma omp parallel for schedule(static)
   for (int32_t v = 0; v < m->vocab; ++v) {
-    const uint16_t* w = m->lm_head + (size_t)v * d;
     double s = 0.0;
-    for (int32_t k = 0; k < d; ++k) s += h[k] * bf(w[k]);
+    if (m->w_int8) {
+      const int8_t* q = (const int8_t*)(const void*)m->lm_head + (size_t)v * d;
+      for (int32_t k = 0; k < d; ++k) s += h[k] * (double)q[k];
+      s *= (double)m->lm_head_scale[v];
+    } else {
+      const uint16_t* w = m->lm_head + (size_t)v * d;
+      for (int32_t k = 0; k < d; ++k) s += h[k] * bf(w[k]);
+    }
     logits[v] = s;
   }
   free(h);
@@ -435,6 +480,8 @@ static void scratch_free(scratch_t* s) {
 
 static int model_ok(const or_model* m) {
   return m && (m->kv_fp8 == 0 || (m->kv_fp8 == 1 && m->k_scale > 0 && m->v_scale > 0)) &&
+         (m->w_int8 == 0 || (m->w_int8 == 1 && m->lm_head_scale && m->s_qkv && m->s_o &&
+                             m->s_gate && m->s_up && m->s_down)) &&
          m->n_layers > 0 && m->d_model > 0 && m->n_heads > 0 &&
          m->n_kv_heads > 0 && m->n_heads % m->n_kv_heads == 0 &&
          m->head_dim > 0 && m->head_dim % 2 == 0 && m->ffn_dim > 0 &&
