@@ -40,12 +40,13 @@ def kv_bytes_per_pos(shape, elem=2):
     return 2 * shape.n_kv_heads * shape.head_dim * elem * shape.n_layers
 
 
-def step_bytes(shape, ctx, n_out, kv_elem=2):
-    """Algorithmic HBM bytes of one decode step: every weight once, the
-    embedding rows, each row's cached KV (ctx + 1 positions read, one
-    appended) and the fp32 logits written."""
+def step_bytes(shape, ctx, n_out, kv_elem=2, w_int8=False):
+    """Algorithmic HBM bytes of one decode step: every weight once (int8
+    codes and their row scales for int8 weights), the embedding rows, each
+    row's cached KV (ctx + 1 positions read, one appended) and the fp32
+    logits written."""
     from continuous_batching_decode_forward_amd import synth
-    W = synth.weight_bytes(shape) + len(ctx) * shape.d_model * 2
+    W = synth.weight_bytes(shape, w_int8) + len(ctx) * shape.d_model * 2
     kvb = kv_bytes_per_pos(shape, kv_elem)
     A = sum((int(c) + 1) * kvb + kvb for c in ctx)
     return W + A + n_out * shape.vocab * 4
@@ -373,6 +374,52 @@ def mixed_step(wl, j, with_chunk=True):
 
 def bench_mixed8b(args):
     print(json.dumps(run_mixed8b(max(args.steps, 8))), flush=True)
+
+
+def run_int8_weights(steps, warmup, batches=(1, 8, 32, 64)):
+    """The headline step (one 8B-shaped layer + LM head, contexts U[512,
+    4096], greedy) with int8 weights: every projection and the LM head as
+    int8 codes with a float32 scale per row, the same KV cache. W falls from
+    1.49 to 0.74 GB per step."""
+    import torch
+    from continuous_batching_decode_forward_amd import binding as B
+    from continuous_batching_decode_forward_amd import configs, synth
+    from continuous_batching_decode_forward_amd.engine import Engine
+    shape, seed = configs.LLAMA8B_1L, 0
+    stream = torch.cuda.current_stream()
+    log(f"[bench] int8 weights {shape.name} on GPU")
+    wg = synth.make_weights_int8(shape, seed=seed, device="cuda")
+    Bmax = max(batches)
+    wl = build_workload(shape, Bmax, seed)
+    eng = Engine(shape, wg, block_size=wl["bs"], num_blocks=wl["total"],
+                 max_blocks_per_seq=wl["mbps"], max_slots=Bmax, max_rows=Bmax, max_seqs=Bmax,
+                 max_position=4097)
+    fill_pool(eng, seed, wl["perm"])
+    torch.cuda.synchronize()
+    out = {"workload": "8b-layer+lmhead-decode-int8-weights", "weights": "int8 + fp32 row scales",
+           "weight_bytes": synth.weight_bytes(shape, True), "sweep": []}
+    for Bn in batches:
+        meta = eng.upload_step(slots=list(range(Bn)), block_tables=wl["tables"][:Bn],
+                               ctx_lens=wl["ctx"][:Bn], n_new=[1] * Bn, tokens=wl["tokens"][:Bn],
+                               want_token=[1] * Bn)
+        lg = torch.empty((Bn, shape.vocab), dtype=torch.float32, device="cuda")
+        tk = torch.empty(Bn, dtype=torch.int32, device="cuda")
+        ms, _, _ = time_steps(eng, meta, lg, tk, steps, warmup, stream)
+        _, _, k = time_steps(eng, meta, lg, tk, 5, 1, stream, profile_class=B.CBD_KERNEL_LM_HEAD)
+        if eng.status():
+            raise RuntimeError("device status set")
+        byts = step_bytes(shape, wl["ctx"][:Bn], Bn, w_int8=True)
+        gbs = byts / (ms * 1e-3) / 1e9
+        out["sweep"].append({"batch": Bn, "ms_per_step": ms, "tokens_per_s": Bn / (ms * 1e-3),
+                             "step_algorithmic_bytes": byts, "hbm_gbs": gbs,
+                             "roofline_frac": gbs / PEAK_HBM_GBS,
+                             "lm_head_us": round(k[0] * 1e3, 1)})
+        log(f"[bench] int8 weights B={Bn}: {ms:.3f} ms/step, {Bn / (ms * 1e-3):.0f} tok/s, "
+            f"{gbs:.0f} GB/s; LM head {k[0] * 1e3:.1f} us")
+    eng.close()
+    del eng, wg
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_mixed8b(reps):
@@ -781,6 +828,8 @@ def main():
         log(f"[bench] long-context sampled, E4M3 cache: "
             f"{out['long_context_sampled_e4m3kv']['ms_per_step']:.3f} ms/step, "
             f"{out['long_context_sampled_e4m3kv']['roofline_frac']:.3f} of peak")
+        log("[bench] the headline step with int8 weights")
+        out["decode_8b_layer_int8_weights"] = run_int8_weights(max(10, args.steps // 2), 3)
         log("[bench] 32-layer 8B mixed step (48 decode rows + 512-token chunk)")
         out["mixed_8b_32layer"] = run_mixed8b(args.mixed_reps)
         log(f"[bench] mixed: {out['mixed_8b_32layer']['ms_per_step_mean']:.2f} ms/step mean, "

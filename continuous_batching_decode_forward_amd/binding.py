@@ -26,6 +26,8 @@ CBD_STATUS_BAD_SHAPE = 0x8
 
 CBD_KV_BF16 = 0
 CBD_KV_FP8_E4M3 = 1
+CBD_W_BF16 = 0
+CBD_W_INT8 = 1
 
 CBD_GRAPH_CACHE = 16
 
@@ -81,14 +83,16 @@ class cbd_config(C.Structure):
                 ("max_rows", C.c_int32), ("max_seqs", C.c_int32), ("max_position", C.c_int32),
                 ("rms_eps", C.c_float), ("pad0_", C.c_float), ("rope_base", C.c_double),
                 ("kv_dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
-                ("pad1_", C.c_int32)]
+                ("weight_dtype", C.c_int32)]
 
 
 class cbd_weights(C.Structure):
     _fields_ = [("embed", VP), ("final_norm", VP), ("lm_head", VP),
                 ("attn_norm", C.POINTER(VP)), ("w_qkv", C.POINTER(VP)), ("w_o", C.POINTER(VP)),
                 ("ffn_norm", C.POINTER(VP)), ("w_gate", C.POINTER(VP)), ("w_up", C.POINTER(VP)),
-                ("w_down", C.POINTER(VP))]
+                ("w_down", C.POINTER(VP)),
+                ("lm_head_scale", VP), ("s_qkv", C.POINTER(VP)), ("s_o", C.POINTER(VP)),
+                ("s_gate", C.POINTER(VP)), ("s_up", C.POINTER(VP)), ("s_down", C.POINTER(VP))]
 
 
 CBD_MAX_FORBIDDEN = 8

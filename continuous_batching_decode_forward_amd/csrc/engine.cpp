@@ -43,6 +43,8 @@ int validate_config(const cbd_config* c) {
   if (!(c->k_scale >= 0.f) || !(c->v_scale >= 0.f) || !std::isfinite(c->k_scale) ||
       !std::isfinite(c->v_scale))
     return fail(CBD_E_INVAL, "k_scale and v_scale must be finite and non-negative");
+  if (c->weight_dtype != CBD_W_BF16 && c->weight_dtype != CBD_W_INT8)
+    return fail(CBD_E_INVAL, "unknown weight_dtype");
   if (c->kv_dtype == CBD_KV_FP8_E4M3 && c->block_size < 8)
     return fail(CBD_E_UNSUPPORTED, "an FP8 KV cache needs block_size 8, 16, 32 or 64");
   if (c->max_seqs > c->max_rows) return fail(CBD_E_INVAL, "max_seqs exceeds max_rows");
@@ -113,9 +115,10 @@ PackedLayout packed_layout(const cbd_config& c) {
   const int qkv_n = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   const int qd = c.n_heads * c.head_dim;
   size_t o = 0;
-  auto take = [&](int N, int K) {
+  const bool w8 = c.weight_dtype == CBD_W_INT8;
+  auto take = [&](int N, int K) {  // offsets in 16-bit units
     size_t at = o;
-    o += packed_elems(N, K);
+    o += w8 ? (packed8_bytes(N, K) + 1) / 2 : packed_elems(N, K);
     o = (o + 127) & ~(size_t)127;  // 256-byte aligned
     return at;
   };
@@ -228,6 +231,14 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* packed_
     if (!w->attn_norm[l] || !w->w_qkv[l] || !w->w_o[l] || !w->ffn_norm[l] || !w->w_gate[l] ||
         !w->w_up[l] || !w->w_down[l])
       return fail(CBD_E_INVAL, "a per-layer weight pointer is NULL");
+  const bool w8 = cfg->weight_dtype == CBD_W_INT8;
+  if (w8) {
+    if (!w->lm_head_scale || !w->s_qkv || !w->s_o || !w->s_gate || !w->s_up || !w->s_down)
+      return fail(CBD_E_INVAL, "int8 weights need their scale pointers");
+    for (int l = 0; l < cfg->n_layers; ++l)
+      if (!w->s_qkv[l] || !w->s_o[l] || !w->s_gate[l] || !w->s_up[l] || !w->s_down[l])
+        return fail(CBD_E_INVAL, "a per-layer scale pointer is NULL");
+  }
   for (const void* p : {(const void*)packed_weights, (const void*)kv_pool,
                         (const void*)slot_state, (const void*)workspace})
     if ((uintptr_t)p % 256) return fail(CBD_E_INVAL, "device buffers must be 256-byte aligned");
@@ -299,7 +310,25 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* packed_
   // Pack every projection matrix into the GEMM's tile order.
   const int qkv_n = (cfg->n_heads + 2 * cfg->n_kv_heads) * cfg->head_dim;
   const int qd = cfg->n_heads * cfg->head_dim;
-  for (int l = 0; l < cfg->n_layers && he == hipSuccess; ++l) {
+  if (w8) {  // int8 codes in k-pairs, each matrix followed by its row scales
+    auto pack8 = [&](const void* q, const void* sc, int N, int K, size_t off) {
+      return launch_pack8((const int8_t*)q, (const float*)sc, N, K, (uint8_t*)(e->packed + off),
+                          e->stream);
+    };
+    for (int l = 0; l < cfg->n_layers && he == hipSuccess; ++l) {
+      he = pack8(w->w_qkv[l], w->s_qkv[l], qkv_n, cfg->d_model, e->pl.qkv[l]);
+      if (he == hipSuccess) he = pack8(w->w_o[l], w->s_o[l], cfg->d_model, qd, e->pl.o[l]);
+      if (he == hipSuccess)
+        he = pack8(w->w_gate[l], w->s_gate[l], cfg->ffn_dim, cfg->d_model, e->pl.gate[l]);
+      if (he == hipSuccess)
+        he = pack8(w->w_up[l], w->s_up[l], cfg->ffn_dim, cfg->d_model, e->pl.up[l]);
+      if (he == hipSuccess)
+        he = pack8(w->w_down[l], w->s_down[l], cfg->d_model, cfg->ffn_dim, e->pl.down[l]);
+    }
+    if (he == hipSuccess)
+      he = pack8(w->lm_head, w->lm_head_scale, cfg->vocab, cfg->d_model, e->pl.lm_head);
+  }
+  for (int l = 0; l < cfg->n_layers && he == hipSuccess && !w8; ++l) {
     he = launch_pack(e->w_qkv[l], qkv_n, cfg->d_model, e->packed + e->pl.qkv[l], e->stream);
     if (he == hipSuccess)
       he = launch_pack(e->w_o[l], cfg->d_model, qd, e->packed + e->pl.o[l], e->stream);
@@ -312,7 +341,7 @@ int cbd_engine_create(const cbd_config* cfg, const cbd_weights* w, void* packed_
       he = launch_pack(e->w_down[l], cfg->d_model, cfg->ffn_dim, e->packed + e->pl.down[l],
                        e->stream);
   }
-  if (he == hipSuccess)
+  if (he == hipSuccess && !w8)
     he = launch_pack(e->lm_head, cfg->vocab, cfg->d_model, e->packed + e->pl.lm_head, e->stream);
   if (he == hipSuccess)
     he = launch_fill_u32(e->wsp<uint32_t>(e->ws.status), 0u, 1, e->stream);
@@ -449,6 +478,13 @@ static int check_step(cbd_engine* e, const cbd_step* s, const int32_t* tokens_ou
 static int enqueue_step(cbd_engine* e, const cbd_step* s, float* logits_out, int32_t* tokens_out,
                         hipStream_t st) {
   const cbd_config& c = e->cfg;
+  // int8 weights: each packed matrix's row scales follow its codes
+  const bool w8 = c.weight_dtype == CBD_W_INT8;
+  auto scales8 = [&](size_t off, int N, int K) -> const float* {
+    if (!w8) return nullptr;
+    return reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(e->packed + off) +
+                                          packed8_codes_bytes(N, K));
+  };
   const int R = s->n_rows;
   uint32_t* status = e->wsp<uint32_t>(e->ws.status);
   StepMeta m{s->n_seqs, s->n_rows, s->n_out, s->max_blocks_per_seq, s->slots, s->block_tables,
@@ -493,6 +529,8 @@ static int enqueue_step(cbd_engine* e, const cbd_step* s, float* logits_out, int
     g.splits_out = &splits;
     g.X = h; g.Xlo = h_lo; g.R = R; g.K = c.d_model; g.W = e->packed + e->pl.qkv[l]; g.N = qkv_n;
     g.epi = EPI_F32; g.Y = qkv;
+    g.w8 = w8;
+    g.Ws = scales8(e->pl.qkv[l], qkv_n, c.d_model);
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
@@ -507,6 +545,7 @@ static int enqueue_step(cbd_engine* e, const cbd_step* s, float* logits_out, int
     HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
     g.X = attn; g.Xlo = attn_lo; g.K = qd; g.W = e->packed + e->pl.o[l]; g.N = c.d_model;
     g.epi = EPI_RESID; g.Y = x;
+    g.Ws = scales8(e->pl.o[l], c.d_model, qd);
     HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_O, st));
@@ -516,11 +555,15 @@ static int enqueue_step(cbd_engine* e, const cbd_step* s, float* logits_out, int
     HIP_TRY(e->prof_mark(CBD_KERNEL_NORM, st));
     g.X = h; g.Xlo = h_lo; g.K = c.d_model; g.W = e->packed + e->pl.gate[l];
     g.W2 = e->packed + e->pl.up[l]; g.N = c.ffn_dim;
+    g.Ws = scales8(e->pl.gate[l], c.ffn_dim, c.d_model);
+    g.Ws2 = scales8(e->pl.up[l], c.ffn_dim, c.d_model);
     g.epi = EPI_SWIGLU; g.Y = nullptr; g.Yh = ffn; g.Yl = ffn_lo; g.splits_out = nullptr;
     HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_GATEUP, st));
     g.X = ffn; g.Xlo = ffn_lo; g.K = c.ffn_dim; g.W = e->packed + e->pl.down[l]; g.W2 = nullptr;
+    g.Ws = scales8(e->pl.down[l], c.d_model, c.ffn_dim);
+    g.Ws2 = nullptr;
     g.N = c.d_model; g.epi = EPI_RESID; g.Y = x; g.Yh = g.Yl = nullptr; g.splits_out = &splits;
     HIP_TRY(e->prof_mark(CBD_KERNEL_DOWN, st));
     HIP_TRY(launch_gemm(g, st));
@@ -539,6 +582,8 @@ static int enqueue_step(cbd_engine* e, const cbd_step* s, float* logits_out, int
   if (!logits && s->mode == CBD_MODE_SAMPLE) logits = e->wsp<float>(e->ws.logits);
   GemmArgs g{};
   g.X = lm_in; g.Xlo = lm_in_lo; g.R = s->n_out; g.K = c.d_model; g.W = e->packed + e->pl.lm_head; g.N = c.vocab;
+  g.w8 = w8;
+  g.Ws = scales8(e->pl.lm_head, c.vocab, c.d_model);
   g.epi = EPI_LOGITS; g.logits = logits;
   g.amax_val = e->wsp<float>(e->ws.amax_val);
   g.amax_idx = e->wsp<int32_t>(e->ws.amax_idx);
@@ -550,7 +595,7 @@ static int enqueue_step(cbd_engine* e, const cbd_step* s, float* logits_out, int
   HIP_TRY(e->prof_mark(CBD_KERNEL_LM_HEAD, st));
   HIP_TRY(e->prof_mark(CBD_KERNEL_SAMPLE, st));
   if (s->mode == CBD_MODE_GREEDY) {
-    HIP_TRY(launch_argmax_reduce(g.amax_val, g.amax_idx, gemm_amax_tiles(s->n_out, c.vocab, c.d_model),
+    HIP_TRY(launch_argmax_reduce(g.amax_val, g.amax_idx, gemm_amax_tiles(s->n_out, c.vocab, c.d_model, w8),
                                  e->ws.amax_stride, s->n_out, tokens_out, st));
   } else {
     HIP_TRY(launch_sampler(logits, s->n_out, c.vocab, s->slots, s->step_ids, maps.out_seq,

@@ -48,6 +48,30 @@ __device__ __forceinline__ size_t wtile(int nb, int kt, int KT) {
 }
 #define WT_NEXT (16 * 512)
 
+// int8 codes are packed in k-pairs: two consecutive 32-k tiles of one
+// 16-column block, lane l's 16 bytes holding its 8 codes of the first tile
+// and then its 8 codes of the second, so one 16-byte load per lane feeds a
+// whole 64-k stage. Byte offset of pair kp of block nb (KP pairs per
+// block), grouped by 16 blocks like the bf16 tiles, and the distance
+// between consecutive pairs of one block. The matrix's float32 row scales
+// follow its codes.
+__device__ __forceinline__ size_t wpair8(int nb, int kp, int KP) {
+  return (((size_t)(nb >> 4) * KP + kp) * 16 + (nb & 15)) * 1024;
+}
+#define WP8_NEXT (16 * 1024)
+
+// Eight int8 codes (a uint2, code i in byte i) -> eight bf16 values in MFMA
+// operand order (a uint4, value i in half-word i). |q| <= 127 has at most 8
+// significant bits, so the float of q truncated to bf16 is exact.
+__device__ __forceinline__ uint4 i8x8_to_bf16x8(uint2 c) {
+  auto two = [](uint32_t w, int b) {  // bytes b and b + 1 of w
+    const float x = (float)((int32_t)(w << (24 - 8 * b)) >> 24);
+    const float y = (float)((int32_t)(w << (16 - 8 * b)) >> 24);
+    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+  };
+  return make_uint4(two(c.x, 0), two(c.x, 2), two(c.y, 0), two(c.y, 2));
+}
+
 template <int EPI>
 struct EpiTraits {
   static constexpr int NM = EPI == EPI_SWIGLU ? 2 : 1;  // weight matrices
@@ -176,13 +200,17 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a,
 // one eighth of the activation into its L2), at 4 splits each split sits on
 // two XCDs. Numbered column-group first, every XCD would fetch the whole
 // activation: at 64 rows that was 8 of the 46 MB the O projection moved.
-template <int RT, int NT, int D, int NW, int EPI>
+// W8: int8 weights (k-pair packing above; one 16-byte load per column
+// fragment per stage, widened to bf16 in registers), the row scales applied
+// to the accumulators before the epilogue.
+template <int RT, int NT, int D, int NW, int EPI, bool W8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_kernel(GemmArgs a, int kc, int S, int n_groups) {
   constexpr int NM = EpiTraits<EPI>::NM;
   constexpr int BLK = RT * 4;                 // 1 KB LDS blocks per stage
   constexpr int CPW = BLK / NW;               // activation copies per wave per stage
   static_assert(BLK % NW == 0, "activation blocks per wave");
-  constexpr int LPS = NM * NT * 2 + CPW;      // loads per stage per wave
+  constexpr int WL = W8 ? 1 : 2;              // weight loads per column fragment per stage
+  constexpr int LPS = NM * NT * WL + CPW;     // loads per stage per wave
   static_assert(D >= 3, "ring depth");
   extern __shared__ uint4 xs[];               // [D][BLK][64]
   const int lane = threadIdx.x & 63;
@@ -200,14 +228,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int nst = (nst0 + D - 1) / D * D;     // padded to whole ring turns
 
   const int KT = (K + 31) / 32;
+  const int KP = (K + 63) / 64;  // int8 k-pairs per block
   const uint16_t* wp[NM][NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     int nb = (n0 >> 4) + nt;
     if (nb * 16 >= N) nb = 0;  // past N: read block 0, never stored
-    const size_t off = wtile(nb, kbeg / 32, KT) + lane * 8;
-    wp[0][nt] = a.W + off;
-    if (NM == 2) wp[NM - 1][nt] = a.W2 + off;
+    if constexpr (W8) {  // byte offsets into the int8 codes
+      const size_t off = wpair8(nb, kbeg / 64, KP) + lane * 16;
+      wp[0][nt] = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.W) + off);
+      if (NM == 2)
+        wp[NM - 1][nt] = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.W2) + off);
+    } else {
+      const size_t off = wtile(nb, kbeg / 32, KT) + lane * 8;
+      wp[0][nt] = a.W + off;
+      if (NM == 2) wp[NM - 1][nt] = a.W2 + off;
+    }
   }
   // This wave copies blocks b = wave + NW i of every stage; block (rt, pl, h)
   // of stage c is the operand tile (row fragment r0 / 16 + rt, k-block
@@ -231,17 +267,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[m][nt][rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 w[D][NM][NT][2];
+  uint4 w[D][NM][NT][WL];
   // Issue every load of stage c (clamped into range; see above) into slot j.
   auto issue = [&](int j, int c) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = min(kbeg / 32 + 2 * c + h, KT - 1) - kbeg / 32;
+    if constexpr (W8) {
+      const int t = min(kbeg / 64 + c, KP - 1) - kbeg / 64;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          w[j][m][nt][h] = load_stream16(wp[m][nt] + (size_t)t * WT_NEXT);
+          w[j][m][nt][0] = load_stream16(reinterpret_cast<const uint16_t*>(
+              reinterpret_cast<const uint8_t*>(wp[m][nt]) + (size_t)t * WP8_NEXT));
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = min(kbeg / 32 + 2 * c + h, KT - 1) - kbeg / 32;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            w[j][m][nt][h] = load_stream16(wp[m][nt] + (size_t)t * WT_NEXT);
+      }
     }
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
@@ -259,6 +305,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl) xf[rt][pl] = buf[((rt * 2 + pl) * 2 + h) * 64 + lane];
+      bf16x8_t wf[NM][NT];
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if constexpr (W8) {
+            const uint4 q = w[j][m][nt][0];
+            wf[m][nt] = as_bf16x8(i8x8_to_bf16x8(h ? make_uint2(q.z, q.w) : make_uint2(q.x, q.y)));
+          } else {
+            wf[m][nt] = as_bf16x8(w[j][m][nt][h]);
+          }
+        }
 #pragma unroll
       for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
@@ -267,8 +325,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
           for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-              acc[m][nt][rt] = mfma16x16x32(as_bf16x8(w[j][m][nt][h]), as_bf16x8(xf[rt][pl]),
-                                            acc[m][nt][rt]);
+              acc[m][nt][rt] = mfma16x16x32(wf[m][nt], as_bf16x8(xf[rt][pl]), acc[m][nt][rt]);
     }
   };
 
@@ -296,6 +353,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   }
   wait_vmem<0>();  // no LDS copy may land after the workgroup exits
+  if constexpr (W8) {  // the row scales of the weights (this lane's 4 output columns)
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = n0 + 16 * nt + 4 * lg;
+        float4 sc = make_float4(0.f, 0.f, 0.f, 0.f);  // past N (never stored)
+        if (n < N) sc = *reinterpret_cast<const float4*>((m ? a.Ws2 : a.Ws) + n);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          acc[m][nt][rt][0] *= sc.x;
+          acc[m][nt][rt][1] *= sc.y;
+          acc[m][nt][rt][2] *= sc.z;
+          acc[m][nt][rt][3] *= sc.w;
+        }
+      }
+  }
   store_tile<RT, NT, EPI>(a, acc, r0, n0, ks, S, tile);
 }
 
@@ -492,6 +566,55 @@ hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, h
   return hipGetLastError();
 }
 
+// int8: codes of the padded matrix (N up to a multiple of 256, K up to 64),
+// then its float32 row scales (zero past N).
+size_t packed8_codes_bytes(int32_t N, int32_t K) {
+  return (size_t)((N + 255) / 256) * 256 * (size_t)((K + 63) / 64) * 64;
+}
+size_t packed8_bytes(int32_t N, int32_t K) {
+  return packed8_codes_bytes(N, K) + (size_t)((N + 255) / 256) * 256 * 4;
+}
+
+// One 16-byte piece per thread: lane `lane` of k-pair (nb, kp) holds codes
+// k0 .. k0 + 7 and k0 + 32 .. k0 + 39 of row 16 nb + lane % 16, k0 = 64 kp +
+// 8 (lane / 16); K is a multiple of 16, so an 8-code run is all in or all
+// out of the matrix.
+__global__ void pack8_kernel(const int8_t* __restrict__ W, int N, int K, uint8_t* __restrict__ out,
+                             size_t n16) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n16) return;
+  const int KP = (K + 63) / 64;
+  const int lane = (int)(i & 63);
+  const size_t pair = i >> 6;
+  const int kp = (int)(pair % KP);
+  const int nb = (int)(pair / KP);
+  const int n = nb * 16 + (lane & 15);
+  const int k0 = kp * 64 + 8 * (lane >> 4);
+  uint2 a = make_uint2(0, 0), b = make_uint2(0, 0);
+  if (n < N && k0 < K) a = *reinterpret_cast<const uint2*>(W + (size_t)n * K + k0);
+  if (n < N && k0 + 32 < K) b = *reinterpret_cast<const uint2*>(W + (size_t)n * K + k0 + 32);
+  *reinterpret_cast<uint4*>(out + wpair8(nb, kp, KP) + (size_t)lane * 16) = make_uint4(a.x, a.y, b.x, b.y);
+}
+
+__global__ void pack_scales_kernel(const float* __restrict__ scale, int N, float* __restrict__ out,
+                                   int n_pad) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_pad) out[i] = i < N ? scale[i] : 0.f;
+}
+
+hipError_t launch_pack8(const int8_t* W, const float* scale, int32_t N, int32_t K, uint8_t* out,
+                        hipStream_t st) {
+  const size_t codes = packed8_codes_bytes(N, K);
+  const size_t n16 = codes / 16;
+  pack8_kernel<<<(unsigned)((n16 + 255) / 256), 256, 0, st>>>(W, N, K, out, n16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_pad = (N + 255) / 256 * 256;
+  pack_scales_kernel<<<(n_pad + 255) / 256, 256, 0, st>>>(scale, N,
+                                                          reinterpret_cast<float*>(out + codes), n_pad);
+  return hipGetLastError();
+}
+
 // How one projection runs. Up to 64 rows: the stream kernel with RT row
 // fragments (16, 32 or 64 rows), 4 waves of NT column fragments sharing the
 // activation tile, S workgroups splitting K. Measured on the 8B shapes at
@@ -525,7 +648,8 @@ static double dense_cost(int R, int N, int K, int NM, int rf, int S) {
   return t;
 }
 
-static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits, size_t partials_cap) {
+static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits, size_t partials_cap,
+                          bool w8) {
   GemmPlan p{};
   // Row fragments per dense workgroup: the fewest padded rows, then the
   // larger tile (fewer weight re-reads).
@@ -542,7 +666,8 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits, size_t parti
   // The dense path wants enough tiles to spread without deep K splits (or a
   // long K, where splitting is cheap); narrow matrices at moderate row
   // counts stay on the stream path.
-  if (R >= DENSE_MIN_ROWS && (dense_tiles >= 32 || K >= 8192)) {
+  // int8 weights always stream (row groups of 64 rows past 64 rows).
+  if (!w8 && R >= DENSE_MIN_ROWS && (dense_tiles >= 32 || K >= 8192)) {
     // The tile height and K split with the lowest estimate (the logits
     // epilogue never splits; splits must fit the partial buffer and keep at
     // least 256 k each).
@@ -576,8 +701,8 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits, size_t parti
   return p;
 }
 
-int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K) {
-  const GemmPlan p = plan_gemm(R, N, K, 1, true, 0);
+int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K, int32_t w8) {
+  const GemmPlan p = plan_gemm(R, N, K, 1, true, 0, w8 != 0);
   if (p.dense) return (N + DENSE_TN - 1) / DENSE_TN * 2;
   const int cols = 16 * p.NT;
   return (N + cols * p.NW - 1) / (cols * p.NW) * p.NW;
@@ -654,7 +779,7 @@ static int split_k(int K, int S, int align, int* kc) {
   return (K + c - 1) / c;
 }
 
-template <int RT, int NT, int D, int NW, int EPI>
+template <int RT, int NT, int D, int NW, int EPI, bool W8>
 static hipError_t launch_stream(const GemmArgs& a, int S, hipStream_t st) {
   constexpr int NM = EpiTraits<EPI>::NM;
   const int cols = 16 * NT * NW;
@@ -664,7 +789,7 @@ static hipError_t launch_stream(const GemmArgs& a, int S, hipStream_t st) {
   S = split_k(a.K, S, 64, &kc);
   if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 64, &kc);
   const size_t lds = (size_t)D * RT * 4 * 1024;  // <= 64 KB for the shapes instantiated
-  gemm_stream_kernel<RT, NT, D, NW, EPI><<<(unsigned)(n_groups * S * r_groups), 64 * NW, lds, st>>>(
+  gemm_stream_kernel<RT, NT, D, NW, EPI, W8><<<(unsigned)(n_groups * S * r_groups), 64 * NW, lds, st>>>(
       a, kc, S, n_groups);
   return finish_splits<EPI>(a, S, st);
 }
@@ -690,29 +815,36 @@ static hipError_t launch_dense(const GemmArgs& a, int S, hipStream_t st) {
   return finish_splits<EPI>(a, S, st);
 }
 
+template <int EPI, bool W8>
+static hipError_t launch_stream_plan(const GemmArgs& a, const GemmPlan& p, hipStream_t st) {
+  constexpr int NM = EpiTraits<EPI>::NM;
+#define ST(RT_, NT_, NW_)                                \
+  if (p.RT == RT_ && p.NT == NT_ && p.NW == NW_) \
+    return launch_stream<RT_, NT_, 4, NW_, EPI, W8>(a, p.S, st);
+  if constexpr (NM == 2) {
+    ST(1, 1, 4) ST(2, 1, 4)
+    return launch_stream<4, 1, 4, 4, EPI, W8>(a, p.S, st);
+  } else if constexpr (EPI == EPI_LOGITS) {
+    ST(1, 4, 4) ST(2, 4, 4)
+    return launch_stream<4, 4, 4, 8, EPI, W8>(a, p.S, st);
+  } else {
+    ST(1, 2, 4) ST(2, 2, 4)
+    return launch_stream<4, 2, 4, 4, EPI, W8>(a, p.S, st);
+  }
+#undef ST
+}
+
 template <int EPI>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
   constexpr int NM = EpiTraits<EPI>::NM;
-  const GemmPlan p = plan_gemm(a.R, a.N, a.K, NM, EPI == EPI_LOGITS, a.partials_cap);
+  const GemmPlan p = plan_gemm(a.R, a.N, a.K, NM, EPI == EPI_LOGITS, a.partials_cap, a.w8 != 0);
+  if (a.w8) return launch_stream_plan<EPI, true>(a, p, st);
   if (p.dense) {
     if (p.RT == 16) return launch_dense<16, 3, EPI>(a, p.S, st);
     if (p.RT == 12) return launch_dense<12, 3, EPI>(a, p.S, st);
     return launch_dense<8, 4, EPI>(a, p.S, st);
   }
-#define ST(RT_, NT_, NW_)                                \
-  if (p.RT == RT_ && p.NT == NT_ && p.NW == NW_) \
-    return launch_stream<RT_, NT_, 4, NW_, EPI>(a, p.S, st);
-  if constexpr (NM == 2) {
-    ST(1, 1, 4) ST(2, 1, 4)
-    return launch_stream<4, 1, 4, 4, EPI>(a, p.S, st);
-  } else if constexpr (EPI == EPI_LOGITS) {
-    ST(1, 4, 4) ST(2, 4, 4)
-    return launch_stream<4, 4, 4, 8, EPI>(a, p.S, st);
-  } else {
-    ST(1, 2, 4) ST(2, 2, 4)
-    return launch_stream<4, 2, 4, 4, EPI>(a, p.S, st);
-  }
-#undef ST
+  return launch_stream_plan<EPI, false>(a, p, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {

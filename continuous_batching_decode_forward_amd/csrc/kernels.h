@@ -122,6 +122,11 @@ enum GemmEpilogue { EPI_F32 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 }
 // lane l's 8 values (row nb*16 + l%16, k kb*32 + 8*(l/16) .. +8) at l * 8.
 // Rows past N and k past K are zero.
 size_t packed_elems(int32_t N, int32_t K);
+// int8 weights: the padded codes (k-pair order), then the float32 row scales.
+size_t packed8_codes_bytes(int32_t N, int32_t K);
+size_t packed8_bytes(int32_t N, int32_t K);
+hipError_t launch_pack8(const int8_t* W, const float* scale, int32_t N, int32_t K, uint8_t* out,
+                        hipStream_t st);
 hipError_t launch_pack(const uint16_t* W, int32_t N, int32_t K, uint16_t* out, hipStream_t st);
 
 // Elements of one plane of a split activation buffer in operand tiles
@@ -136,8 +141,11 @@ struct GemmArgs {
   const uint16_t* X;    // [R][K] split activation in operand tiles: hi plane
   const uint16_t* Xlo;  //                                             lo plane
   int32_t R, K;
-  const uint16_t* W;    // [N][K] bf16, packed
+  const uint16_t* W;    // [N][K] bf16, packed (int8 k-pairs when w8)
   const uint16_t* W2;   // second packed matrix for EPI_SWIGLU (up), [N][K]
+  const float* Ws;      // w8: float32 row scales of W (padded to 256 rows)
+  const float* Ws2;     //     and of W2
+  int32_t w8;           // the weights are int8 codes
   int32_t N;
   int32_t epi;
   float* Y;             // EPI_F32 out [R][N]; EPI_RESID in/out [R][N] (fp32)
@@ -154,7 +162,7 @@ struct GemmArgs {
 };
 
 // Number of argmax partials per row the logits GEMM writes (column tiles).
-int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K);
+int32_t gemm_amax_tiles(int32_t R, int32_t N, int32_t K, int32_t w8);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 
 // tokens[j] = lowest id of the row maximum over the argmax partials.

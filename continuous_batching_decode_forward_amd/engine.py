@@ -60,6 +60,9 @@ class Engine:
         cfg.max_seqs, cfg.max_position = max_seqs, max_position
         cfg.rms_eps, cfg.rope_base = shape.rms_eps, shape.rope_base
         cfg.kv_dtype, cfg.k_scale, cfg.v_scale = kv_dtype, k_scale, v_scale
+        # int8 projections: weights with per-row scales (synth.make_weights_int8)
+        self.w_int8 = "s_qkv" in weights
+        cfg.weight_dtype = B.CBD_W_INT8 if self.w_int8 else B.CBD_W_BF16
         self.cfg = cfg
         self.kv_fp8 = kv_dtype == B.CBD_KV_FP8_E4M3
         self.block_size, self.num_blocks = block_size, num_blocks
@@ -77,7 +80,11 @@ class Engine:
                                             weights["final_norm"].data_ptr(),
                                             weights["lm_head"].data_ptr())
         self._arrs = {}
-        for k in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate", "w_up", "w_down"):
+        per_layer = ["attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate", "w_up", "w_down"]
+        if self.w_int8:
+            per_layer += ["s_qkv", "s_o", "s_gate", "s_up", "s_down"]
+            w.lm_head_scale = weights["lm_head_scale"].data_ptr()
+        for k in per_layer:
             arr = (C.c_void_p * shape.n_layers)(*[t.data_ptr() for t in weights[k]])
             self._arrs[k] = arr
             setattr(w, k, C.cast(arr, C.POINTER(C.c_void_p)))

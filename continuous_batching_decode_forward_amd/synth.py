@@ -184,11 +184,17 @@ def make_weights_int8(cfg, seed: int, device="cpu", std: float = 0.02) -> dict:
     return w
 
 
-def weight_bytes(cfg) -> int:
-    """Bytes of every weight read by one step (embedding rows excluded)."""
+def weight_bytes(cfg, int8: bool = False) -> int:
+    """Bytes of every weight read by one step (embedding rows excluded):
+    bf16 throughout, or int8 projections with a float32 scale per row (the
+    norm gains stay bf16)."""
     s = weight_shapes(cfg)
-    per_layer = sum(int(np.prod(s[k])) for k in PER_LAYER)
-    return 2 * (cfg.n_layers * per_layer + int(np.prod(s["lm_head"])) + cfg.d_model)
+    if not int8:
+        per_layer = sum(int(np.prod(s[k])) for k in PER_LAYER)
+        return 2 * (cfg.n_layers * per_layer + int(np.prod(s["lm_head"])) + cfg.d_model)
+    proj = [k for k in PER_LAYER if not k.endswith("norm")]
+    per_layer = sum(int(np.prod(s[k])) + 4 * s[k][0] for k in proj) + 2 * 2 * cfg.d_model
+    return cfg.n_layers * per_layer + int(np.prod(s["lm_head"])) + 4 * cfg.vocab + 2 * cfg.d_model
 
 
 # ------------------------------------------------------ cached K/V contents

@@ -103,15 +103,24 @@ typedef struct cbd_config {
   int32_t kv_dtype;
   float k_scale;
   float v_scale;
-  int32_t pad1_;
+  /* Projection weights (QKV, O, gate, up, down, LM head): CBD_W_BF16, or
+   * CBD_W_INT8 -- int8 codes q with one float32 scale per matrix row, read
+   * as q * scale (weight-only quantisation, the follow-up "int8 weights" the
+   * RWKV-Runner Albatross article lists; it halves W, the bytes every
+   * decode step streams). The embedding and the norm gains stay bf16. The
+   * int8 projections run on the streaming GEMM at every row count. */
+  int32_t weight_dtype;
 } cbd_config;
 
 #define CBD_KV_BF16 0
 #define CBD_KV_FP8_E4M3 1
+#define CBD_W_BF16 0
+#define CBD_W_INT8 1
 
-/* Weights: every pointer is device memory holding bf16, row-major.
- * Per-layer fields are HOST arrays of n_layers device pointers; the engine
- * copies the pointer values at create time. */
+/* Weights: every pointer is device memory holding bf16, row-major (the
+ * projections int8 under CBD_W_INT8). Per-layer fields are HOST arrays of
+ * n_layers device pointers; the engine copies the pointer values at create
+ * time. */
 typedef struct cbd_weights {
   const void* embed;        /* [vocab][d_model] */
   const void* final_norm;   /* [d_model] */
@@ -124,6 +133,14 @@ typedef struct cbd_weights {
   const void* const* w_gate;    /* [ffn_dim][d_model] */
   const void* const* w_up;      /* [ffn_dim][d_model] */
   const void* const* w_down;    /* [d_model][ffn_dim] */
+  /* CBD_W_INT8 only (NULL otherwise): float32 scales, one per row of the
+   * matching matrix above; copied into the packed buffer at creation. */
+  const void* lm_head_scale;    /* [vocab] */
+  const void* const* s_qkv;     /* [(n_heads + 2*n_kv_heads)*head_dim] */
+  const void* const* s_o;       /* [d_model] */
+  const void* const* s_gate;    /* [ffn_dim] */
+  const void* const* s_up;      /* [ffn_dim] */
+  const void* const* s_down;    /* [d_model] */
 } cbd_weights;
 
 /* Per-slot sampling parameters (Albatross adapter defaults: temperature
@@ -154,10 +171,11 @@ typedef struct cbd_sampling {
 int cbd_kv_pool_bytes(const cbd_config* cfg, size_t* bytes);
 /* The packed-weights buffer: every projection matrix (QKV, O, gate, up,
  * down per layer, and the LM head) rearranged once, at engine creation, into
- * the GEMM's tile order (16 rows x 32 k tiles in MFMA operand order; see the
- * engine source). After cbd_engine_create returns, the engine reads only the
- * embedding, the norm gains and this buffer, so the caller may release the
- * row-major projection matrices. */
+ * the GEMM's tile order (16 rows x 32 k tiles in MFMA operand order; int8
+ * codes as 16 rows x 64 k pairs of such tiles, followed by the matrix's row
+ * scales; see the engine source). After cbd_engine_create returns, the
+ * engine reads only the embedding, the norm gains and this buffer, so the
+ * caller may release the row-major projection matrices (and their scales). */
 int cbd_packed_weights_bytes(const cbd_config* cfg, size_t* bytes);
 int cbd_slot_state_bytes(const cbd_config* cfg, size_t* bytes);
 int cbd_workspace_bytes(const cbd_config* cfg, size_t* bytes);
