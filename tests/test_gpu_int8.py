@@ -67,3 +67,21 @@ def test_8b_layer_int8_weights_decode_step(big8w, Bn, rows):
     assert att.max() <= ATTN_TOL
     assert np.array_equal(g_tk[res], r_tk[res])
     assert np.array_equal(own, all_tk)
+
+
+def test_tiny_int8_weights_with_an_e4m3_cache():
+    """Both storage formats at once: int8 weights and an 8-bit KV cache, on
+    the tiny decoder end to end, against the oracle run with both."""
+    from continuous_batching_decode_forward_amd import binding as B
+    cfg = configs.TINY
+    w = synth.make_weights_int8(cfg, seed=2)
+    kv = dict(kv_dtype=B.CBD_KV_FP8_E4M3, k_scale=0.05, v_scale=0.03)
+    om = O.Model(cfg, w, kv_fp8=True, k_scale=kv["k_scale"], v_scale=kv["v_scale"])
+    bs, chunk = 16, 40
+    prompts = [synth.uniform_ints(5, f"p{i}", L, 0, cfg.vocab - 1)
+               for i, L in enumerate([bs - 1, 1, 90, 37])]
+    res = test_gpu_tiny.run_schedule((w, om, weights_to(w, "cuda")), prompts, 6, chunk=chunk,
+                                     bs=bs, nb=80, seed=7, kv=kv)
+    test_gpu_tiny.check(res)
+    print(f"tiny int8 weights + e4m3 cache: {len(res)} steps, max abs logit error "
+          f"{max(r[2] for r in res):.2e}")
