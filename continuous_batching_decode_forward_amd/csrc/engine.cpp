@@ -662,7 +662,9 @@ int cbd_step_forward_graph(cbd_engine* e, const cbd_step* s, float* logits_out,
     size_t old = 0;
     for (size_t i = 1; i < e->graphs.size(); ++i)
       if (e->graphs[i].used < e->graphs[old].used) old = i;
-    HIP_TRY(hipStreamSynchronize(st));  // it may still be running
+    // It may still be running, on this stream or on another one the caller
+    // launched it on: wait for the device before destroying it.
+    HIP_TRY(hipDeviceSynchronize());
     (void)hipGraphExecDestroy(e->graphs[old].exec);
     e->graphs.erase(e->graphs.begin() + old);
   }

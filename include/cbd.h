@@ -278,7 +278,8 @@ int cbd_step_forward(cbd_engine* e, const cbd_step* step, float* logits_out,
  * wants replays keeps its metadata buffer in place and passes a max_ctx
  * that stays fixed across steps (any upper bound of ctx_lens + n_new is
  * valid, e.g. rounded up to a multiple of 256). The engine keeps the
- * CBD_GRAPH_CACHE most recently used graphs, destroying the oldest.
+ * CBD_GRAPH_CACHE most recently used graphs, destroying the oldest (after
+ * waiting for the device, since it may still run on some stream).
  * `stream` must not be the null stream (CBD_E_INVAL; a graph is recorded
  * by stream capture). On a stream that is already being captured the
  * launches are recorded into the caller's capture, as cbd_step_forward's
