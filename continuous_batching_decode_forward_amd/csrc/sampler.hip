@@ -171,7 +171,7 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
 
 // The same over groups of SMP_LB values (k0 = 0, SMP_LB, ...): the body
 // handles k0 .. k0 + SMP_LB - 1 and checks k < K itself.
-#define SMP_LB 8
+#define SMP_LB 16
 #define SMP_FOR_KB(k0)                                                              \
   _Pragma("unroll") for (int k0 = 0; k0 < (REGS ? SMP_KREG : K); k0 += SMP_LB) \
     if (!REGS || k0 < K)
@@ -220,43 +220,55 @@ __device__ void smp_block_sum2(double& f, int& a, SmpShared& sh) {
   __syncthreads();
 }
 
+// Kept values are non-negative floats, whose bit patterns read as signed
+// ints are >= 0 and order like the values; dropped ids hold -1.0f, whose
+// pattern is negative. So "kept and at least tau" is one signed compare, and
+// every pass below is free of branches.
+__device__ __forceinline__ int smp_bits(float v) { return __float_as_int(v); }
+
+// Sum over the 64 lanes of a wave, the same in every lane (lane 0's).
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return __shfl(v, 0, 64);
+}
+
 // Largest bit pattern tau (non-negative floats) with F(tau) >= need, where
 // F(tau) = count (BY_MASS false) or mass (true) of the kept values >= tau.
 // Bisection between the smallest and largest kept pattern. Each step over
 // the row is one pass and one reduction of F(mid) and C(mid), the number of
 // kept values >= mid; C at both ends of the range gives the number of
 // values left inside it. Once that is at most one per thread, those values
-// are gathered into LDS and the bisection finishes on them alone: F(mid) =
-// F(hi) + the candidates in [mid, hi) (those at or above a lowered hi are in
-// F(hi) already), where F(hi) was computed when hi was last lowered (0 for
-// the initial hi above every value).
+// are gathered into LDS and the search finishes on them alone: F(m) = F(hi)
+// + the candidates in [m, hi) (those at or above a lowered hi are in F(hi)
+// already), where F(hi) was computed when hi was last lowered (0 for the
+// initial hi above every value). The result is the same whatever cut points
+// the search takes, so the final phase takes three per step (a four-way
+// split) to halve its steps.
 template <bool BY_MASS, bool REGS>
 __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K, int base, double need,
                                   SmpShared& sh) {
-  uint32_t lo = 0x7f800000u, hi = 0u;
+  int lo = 0x7f800000, hi = 0;
   int kept = 0;
   SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
-    const float v = e.get(k, base + 64 * k);
-    if (v >= 0.f) {
-      lo = min(lo, __float_as_uint(v));
-      hi = max(hi, __float_as_uint(v));
-      ++kept;
-    }
+    const int u = smp_bits(e.get(k, base + 64 * k));
+    lo = min(lo, u >= 0 ? u : 0x7f800000);
+    hi = max(hi, u);
+    kept += u >= 0;
   }
-  lo = (uint32_t)-smp_block_max_i(-(int)lo, sh);  // block min (patterns < 2^31)
-  hi = (uint32_t)smp_block_max_i((int)hi, sh) + 1u;  // F(hi) = 0 < need
+  lo = -smp_block_max_i(-lo, sh);    // block min
+  hi = smp_block_max_i(hi, sh) + 1;  // F(hi) = 0 < need
   int c_lo = smp_block_sum_i(kept, sh), c_hi = 0;
   double f_hi = 0.0;
-  while (hi - lo > 1u && c_lo - c_hi > SMP_THREADS) {
-    const uint32_t mid = lo + (hi - lo) / 2u;
+  while (hi - lo > 1 && c_lo - c_hi > SMP_THREADS) {
+    const int mid = lo + (hi - lo) / 2;
     double f = 0.0;
     int c = 0;
     SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
       const float v = e.get(k, base + 64 * k);
-      if (v >= 0.f && __float_as_uint(v) >= mid) {
-        if (BY_MASS) f += v;
-        ++c;
-      }
+      const bool in = smp_bits(v) >= mid;
+      if (BY_MASS) f += in ? (double)v : 0.0;
+      c += in;
     }
     smp_block_sum2(f, c, sh);
     if (!BY_MASS) f = (double)c;
@@ -269,7 +281,7 @@ __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K,
       c_hi = c;
     }
   }
-  if (hi - lo <= 1u) return lo;
+  if (hi - lo <= 1) return (uint32_t)lo;
   // Gather the values in [lo, hi) (at most SMP_THREADS of them) in (thread,
   // k) order: each thread's first slot is the block prefix of the per-thread
   // counts, so the candidates, and every sum taken over them below, come out
@@ -278,9 +290,8 @@ __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K,
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int cnt = 0;
     SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
-      const float v = e.get(k, base + 64 * k);
-      const uint32_t u = __float_as_uint(v);
-      if (v >= 0.f && u >= lo && u < hi) ++cnt;
+      const int u = smp_bits(e.get(k, base + 64 * k));
+      cnt += u >= lo && u < hi;
     }
     int inc = cnt;
 #pragma unroll
@@ -294,17 +305,20 @@ __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K,
     for (int x = 0; x < w; ++x) at += sh.wave_i[x];
     SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
       const float v = e.get(k, base + 64 * k);
-      const uint32_t u = __float_as_uint(v);
-      if (v >= 0.f && u >= lo && u < hi) sh.cand[at++] = v;
+      const int u = smp_bits(v);
+      if (u >= lo && u < hi) sh.cand[at++] = v;
     }
     if (threadIdx.x == SMP_THREADS - 1) sh.n_cand = at;
     __syncthreads();
   }
-  // Wave 0 alone finishes the bisection on the (at most SMP_THREADS)
+  // Wave 0 alone finishes the search on the (at most SMP_THREADS)
   // candidates, 16 per lane, with wave reductions only; every lane decides
-  // on lane 0's sum, and the result goes to the other waves through LDS.
+  // on lane 0's sums, and the result goes to the other waves through LDS.
   // (A block reduction per step -- about 20 steps at top-p 0.3 over 65536
-  // ids -- cost two barriers each.)
+  // ids -- cost two barriers each.) Each step sums the candidates in [m, hi)
+  // for three cuts m1 <= m2 <= m3 in (lo, hi); these sums, and so F, do not
+  // increase from m1 to m3 (the same terms in the same order, fewer of them),
+  // so the largest cut with F >= need is well defined.
   if (threadIdx.x < 64) {
     constexpr int CPL = SMP_THREADS / 64;
     const int n = sh.n_cand;
@@ -314,30 +328,49 @@ __device__ __forceinline__ uint32_t smp_threshold(const RowVals<REGS>& e, int K,
       const int j = (int)threadIdx.x + 64 * i;
       cv[i] = j < n ? sh.cand[j] : -1.f;
     }
-    while (hi - lo > 1u) {
-      const uint32_t mid = lo + (hi - lo) / 2u;
-      double c = 0.0;
+    while (hi - lo > 1) {
+      const int d = hi - lo;
+      const int m0 = lo + max(1, d / 4), m1 = lo + max(1, d / 2);
+      const int m2 = lo + max(1, (int)((3LL * d) / 4));
+      double c0 = 0.0, c1 = 0.0, c2 = 0.0;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        const uint32_t u = __float_as_uint(cv[i]);
-        if (cv[i] >= 0.f && u >= mid && u < hi) c += BY_MASS ? (double)cv[i] : 1.0;
+        const int u = smp_bits(cv[i]);
+        const double x = BY_MASS ? (double)cv[i] : 1.0;
+        const bool below_hi = u < hi;
+        c0 += below_hi && u >= m0 ? x : 0.0;
+        c1 += below_hi && u >= m1 ? x : 0.0;
+        c2 += below_hi && u >= m2 ? x : 0.0;
       }
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-      const double f = f_hi + __shfl(c, 0, 64);
-      if (f >= need) {
-        lo = mid;
+      for (int o = 32; o > 0; o >>= 1) {
+        c0 += __shfl_xor(c0, o, 64);
+        c1 += __shfl_xor(c1, o, 64);
+        c2 += __shfl_xor(c2, o, 64);
+      }
+      const double f0 = f_hi + __shfl(c0, 0, 64), f1 = f_hi + __shfl(c1, 0, 64);
+      const double f2 = f_hi + __shfl(c2, 0, 64);
+      if (f2 >= need) {
+        lo = m2;
+      } else if (f1 >= need) {
+        lo = m1;
+        hi = m2;
+        f_hi = f2;
+      } else if (f0 >= need) {
+        lo = m0;
+        hi = m1;
+        f_hi = f1;
       } else {
-        hi = mid;
-        f_hi = f;
+        hi = m0;
+        f_hi = f0;
       }
     }
-    if (threadIdx.x == 0) sh.red_i[0] = (int)lo;  // patterns of non-negative floats: < 2^31
+    if (threadIdx.x == 0) sh.red_i[0] = lo;
   }
   __syncthreads();
-  lo = (uint32_t)sh.red_i[0];
+  lo = sh.red_i[0];
   __syncthreads();  // red_i is reused by the next reduction
-  return lo;
+  return (uint32_t)lo;
 }
 
 // Keep the values above tau and the first eq_keep values equal to tau in
@@ -346,11 +379,11 @@ template <bool REGS>
 __device__ __forceinline__ double smp_keep(RowVals<REGS>& e, int K, int base, uint32_t tau, int eq_keep,
                           SmpShared& sh) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = (int)tau;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int eq_wave = 0;  // equals in this wave's range (same in every lane)
   SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
-    const float v = e.get(k, base + 64 * k);
-    eq_wave += __popcll(__ballot(v >= 0.f && __float_as_uint(v) == tau));
+    eq_wave += __popcll(__ballot(smp_bits(e.get(k, base + 64 * k)) == t));
   }
   if (lane == 0) sh.wave_i[w] = eq_wave;
   __syncthreads();
@@ -361,15 +394,12 @@ __device__ __forceinline__ double smp_keep(RowVals<REGS>& e, int K, int base, ui
   SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
     const int id = base + 64 * k;
     const float v = e.get(k, id);
-    const bool is_eq = v >= 0.f && __float_as_uint(v) == tau;
-    const uint64_t m = __ballot(is_eq);
-    bool keep = v >= 0.f && __float_as_uint(v) > tau;
-    if (is_eq) keep = eq_before + __popcll(m & below) < eq_keep;
+    const int u = smp_bits(v);
+    const uint64_t m = __ballot(u == t);
+    const bool keep = u > t || (u == t && eq_before + __popcll(m & below) < eq_keep);
     eq_before += __popcll(m);
-    if (keep)
-      own += v;
-    else if (v >= 0.f)
-      e.set(k, id, -1.f);
+    own += keep ? (double)v : 0.0;
+    e.set(k, id, keep ? v : -1.f);
   }
   return own;
 }
@@ -383,9 +413,12 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
   RowVals<REGS> e;
   e.g = scratch_row;  // REGS: the caller passes its LDS slice base + threadIdx.x
 
-  // S1 penalties (+ S2 division). The two row reads go out SMP_LB ids at a
-  // time: with the scheduling barrier of every id they waited one memory
-  // round trip per id.
+  // S1 penalties (+ S2 division), and the decay of S7 in the same pass:
+  // penalties read the counts before the step, and nothing below reads them
+  // again, so each id's decayed count is written as soon as it is read (the
+  // token's +1 follows once it is drawn). The two row reads go out SMP_LB
+  // ids at a time: with the scheduling barrier of every id they waited one
+  // memory round trip per id.
   float zmax = -INFINITY;
   SMP_FOR_KB(k0) { __builtin_amdgcn_sched_barrier(0);
     float cv[SMP_LB], lv[SMP_LB];
@@ -404,6 +437,7 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
         float z = -INFINITY;
         if (id < V) {
           const float c = cv[u];
+          crow[id] = mul_rounded(c, P.penalty_decay);
           float l = lv[u] - mul_rounded(P.freq_penalty, c);
           if (c > 0.f) l = l - P.presence_penalty;
           for (int f = 0; f < P.n_forbidden; ++f)  // forbidden ids: never drawn
@@ -443,8 +477,7 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
       const uint32_t tau = smp_threshold<false>(e, K, base, (float)P.top_k, sh);
       int above = 0;
       SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
-        const float v = e.get(k, base + 64 * k);
-        if (v >= 0.f && __float_as_uint(v) > tau) ++above;
+        above += smp_bits(e.get(k, base + 64 * k)) > (int)tau;
       }
       above = smp_block_sum_i(above, sh);
       own = smp_keep(e, K, base, tau, P.top_k - above, sh);
@@ -458,7 +491,7 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
       double above = 0.0;
       SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
         const float v = e.get(k, base + 64 * k);
-        if (v >= 0.f && __float_as_uint(v) > tau) above += v;
+        above += smp_bits(v) > (int)tau ? (double)v : 0.0;
       }
       above = smp_block_sum_d(above, sh);
       // ids equal to tau needed to reach the target, in ascending id order
@@ -484,8 +517,37 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
     const double r = (double)u * total;
     int cand = 0x7fffffff, last = -1;
     if (prefix + wsum > r) {  // this wave's range reaches past r
+      // The wave's totals over groups of SMP_LB consecutive k (64 SMP_LB
+      // consecutive ids each), in ascending order, find the group where the
+      // running mass passes r; one wave prefix per k then runs from there
+      // (from k = 0 with the wave's prefix if no group total passes r, as
+      // rounding may have it).
       double carry = prefix;
+      int k_from = -1;
+      SMP_FOR_KB(k0) { __builtin_amdgcn_sched_barrier(0);
+        if (k_from < 0) {
+          double gs = 0.0;
+#pragma unroll
+          for (int uu = 0; uu < SMP_LB; ++uu) {
+            const int k = k0 + uu;
+            if (k < K) {
+              const float v = e.get(k, base + 64 * k);
+              gs += v >= 0.f ? (double)v : 0.0;
+            }
+          }
+          gs = wave_sum_d(gs);
+          if (carry + gs > r)
+            k_from = k0;
+          else
+            carry += gs;
+        }
+      }
+      if (k_from < 0) {
+        k_from = 0;
+        carry = prefix;
+      }
       SMP_FOR_K(k) { __builtin_amdgcn_sched_barrier(0);
+        if (k < k_from) continue;
         const int id = base + 64 * k;
         const float v = e.get(k, id);
         const double kv = v >= 0.f ? (double)v : 0.0;
@@ -507,24 +569,11 @@ __device__ __forceinline__ void sampler_row(const float* __restrict__ lrow, floa
     if (token == 0x7fffffff) token = smp_block_max_i(last, sh);
     if (token < 0) token = 0;
   }
-  // S7 counts: decay every id, then count the token (reads SMP_LB ids at a
-  // time, as in S1)
-  SMP_FOR_KB(k0) { __builtin_amdgcn_sched_barrier(0);
-    float cv[SMP_LB];
-#pragma unroll
-    for (int u = 0; u < SMP_LB; ++u) {
-      const int id = base + 64 * (k0 + u);
-      cv[u] = k0 + u < K && id < V ? crow[id] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < SMP_LB; ++u) {
-      const int id = base + 64 * (k0 + u);
-      if (k0 + u < K && id < V) {
-        float c = mul_rounded(cv[u], P.penalty_decay);
-        if (id == token) c = c + 1.0f;
-        crow[id] = c;
-      }
-    }
+  // S7: every id's count was decayed in the S1 pass; the token's owner
+  // thread (the one that wrote it) adds the token's count.
+  {
+    const int rem = token % (64 * K);
+    if (w == token / (64 * K) && lane == rem % 64) crow[token] = crow[token] + 1.0f;
   }
   if (threadIdx.x == 0) *token_out = token;
 }
