@@ -158,6 +158,34 @@ def time_steps(eng, meta, lg, tk, steps, warmup, stream, profile_class=None):
     return ms, wall, kern
 
 
+def hbm_read_probe(nbytes=4 << 30, blocks=512, reps=10, rounds=3):
+    """The bandwidth a plain streaming read of a 4 GiB buffer reaches
+    (cbd_read_probe: 512 x 1024 threads, non-temporal 16-byte loads), timed
+    with HIP events on the current stream, the best of a few rounds: the
+    practical ceiling beside the published 8 TB/s peak."""
+    import torch
+    from continuous_batching_decode_forward_amd import binding as B
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(blocks * 1024, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    B.cbd_read_probe(buf.data_ptr(), nbytes, out.data_ptr(), blocks, st.cuda_stream)
+    best = None
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            B.cbd_read_probe(buf.data_ptr(), nbytes, out.data_ptr(), blocks, st.cuda_stream)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        best = ms if best is None else min(best, ms)
+    del buf, out
+    torch.cuda.empty_cache()
+    gbs = nbytes / (best * 1e-3) / 1e9
+    return {"gbs": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS, "bytes": nbytes, "ms": best,
+            "blocks": blocks, "threads_per_block": 1024, "reps": reps, "rounds": rounds}
+
+
 def cpu_info():
     """The host CPU's model name and the cores this process may use."""
     model = None
@@ -422,6 +450,42 @@ def run_int8_weights(steps, warmup, batches=(1, 8, 32, 64)):
     return out
 
 
+def vendor_gemm_reference(shape, rows, reps=20):
+    """The vendor BLAS (torch.nn.functional.linear on bf16 operands, which
+    ROCm serves with hipBLASLt) at the layer projections' shapes, timed with HIP
+    events at `rows` rows and at twice as many. The second is the executed
+    MFMA work of this library's dense GEMM over `rows` rows, whose fp32
+    activations enter as two bf16 planes (hi + lo). A comparison point for
+    the dense path only; nothing of the step runs through it."""
+    import torch
+    import torch.nn.functional as F
+    d, hd = shape.d_model, shape.head_dim
+    shapes = {"qkv": ((shape.n_heads + 2 * shape.n_kv_heads) * hd, d),
+              "o": (d, shape.n_heads * hd), "gateup": (2 * shape.ffn_dim, d),
+              "down": (d, shape.ffn_dim)}
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for name, (N, K) in shapes.items():
+        w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        for M in (rows, 2 * rows):
+            x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+            for _ in range(3):
+                y = F.linear(x, w)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                y = F.linear(x, w)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            out[f"{name}_{M}rows_us"] = round(us, 1)
+            out[f"{name}_{M}rows_pflops"] = round(2 * M * N * K / (us * 1e-6) / 1e15, 3)
+            del x, y
+        del w
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_mixed8b(reps):
     """The mixed step on the full 8B shape (32 layers, d_model 4096, 32/8
     heads, FFN 14336, vocab 128256): 48 decode rows with contexts uniform in
@@ -496,6 +560,12 @@ def run_mixed8b(reps):
     eng.close()
     del eng, wg
     torch.cuda.empty_cache()
+    # This library's dense GEMMs per layer at the step's rows (first offset;
+    # gate/up with its split-K sum + SwiGLU pass), beside the vendor BLAS.
+    k0 = rows[0]["kernel_ms"]
+    out["dense_gemm_per_layer_us"] = {k: round(k0[k + "_ms"] / L * 1e3, 1)
+                                      for k in ("qkv", "o", "gateup", "down")}
+    out["vendor_gemm_reference"] = vendor_gemm_reference(shape, wl["chunk"] + n_dec)
     return out
 
 
@@ -776,6 +846,9 @@ def main():
     eng.close()
     del eng
     torch.cuda.empty_cache()
+    probe = hbm_read_probe()
+    log(f"[bench] streaming-read probe: {probe['gbs']:.0f} GB/s "
+        f"({probe['frac_of_peak']:.3f} of the 8 TB/s peak)")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -808,7 +881,9 @@ def main():
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": lm_gbs / PEAK_HBM_GBS,
                      "traffic": measured_traffic(Bn), "avg_launch_us": lm_ms * 1e3,
                      "launches": lm_n,
-                     "bytes_per_launch": lm_bytes},
+                     "bytes_per_launch": lm_bytes,
+                     "frac_of_read_probe": lm_gbs / probe["gbs"]},
+        "hbm_read_probe": probe,
         "cpu_baseline": cpu,
         "sweep": sweep,
     }

@@ -166,6 +166,7 @@ SIGNATURES = [
     ("cbd_step_forward", C.c_int, [VP, C.POINTER(cbd_step), VP, VP, VP]),
     ("cbd_step_forward_graph", C.c_int, [VP, C.POINTER(cbd_step), VP, VP, VP]),
     ("cbd_graph_stats", C.c_int, [VP, C.POINTER(C.c_int64)]),
+    ("cbd_read_probe", C.c_int, [VP, C.c_size_t, VP, C.c_int32, VP]),
     ("cbd_sample_logits", C.c_int, [VP, VP, C.c_int32, VP, VP, VP, VP]),
     ("cbd_sample_logits_noalloc", C.c_int, [VP, VP, C.c_int32, VP, VP, VP, VP]),
     ("cbd_engine_status", C.c_int, [VP, VP, C.POINTER(C.c_uint32)]),
@@ -290,6 +291,10 @@ def cbd_step_forward(engine, step: cbd_step, logits_out, tokens_out, stream) -> 
 
 def cbd_step_forward_graph(engine, step: cbd_step, logits_out, tokens_out, stream) -> None:
     _call("cbd_step_forward_graph", engine, C.byref(step), logits_out, tokens_out, stream)
+
+
+def cbd_read_probe(buf, nbytes: int, out, blocks: int, stream) -> None:
+    _call("cbd_read_probe", buf, int(nbytes), out, int(blocks), stream)
 
 
 def cbd_graph_stats(engine) -> tuple:

@@ -682,6 +682,13 @@ int cbd_graph_stats(const cbd_engine* e, int64_t out[3]) {
   return CBD_OK;
 }
 
+int cbd_read_probe(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, void* stream) {
+  if (!buf || !out || blocks < 1 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(CBD_E_INVAL, "bad read_probe arguments");
+  HIP_TRY(launch_read_probe(buf, bytes, out, blocks, (hipStream_t)stream));
+  return CBD_OK;
+}
+
 int cbd_sample_logits(cbd_engine* e, const float* logits, int32_t n, const int32_t* slots,
                       const int32_t* step_ids, int32_t* tokens_out, void* stream) {
   if (!e || !logits || !slots || !step_ids || !tokens_out || n < 1 || n > e->cfg.max_seqs)

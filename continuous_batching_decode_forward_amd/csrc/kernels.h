@@ -192,6 +192,11 @@ hipError_t launch_sampler(const float* logits, int32_t n, int32_t V, const int32
                           float* counts, int32_t max_slots, float* scratch, int32_t* tokens,
                           uint32_t* status, hipStream_t st);
 
+// Streaming-read probe (probe.hip): `blocks` x 1024 threads read `bytes`
+// (a multiple of 16) at `buf` once; one XOR fold per thread to `out`.
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, int32_t blocks,
+                             hipStream_t st);
+
 // The current device's fixed sampler scratch (a static device array of
 // *floats floats), for the allocation-free sampler entry point; looked up once
 // per device.

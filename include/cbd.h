@@ -291,6 +291,19 @@ int cbd_step_forward_graph(cbd_engine* e, const cbd_step* step, float* logits_ou
  * since the engine was created, and graphs cached now (out[2]). */
 int cbd_graph_stats(const cbd_engine* e, int64_t out[3]);
 
+/* Streaming-read probe of the device's HBM, for reading the step's rooflines
+ * (not part of the step). The cost model of the step is bytes over the
+ * memory bandwidth beta (Go under the hood 20.3.2, one weight read shared by
+ * the batch); this measures the beta a plain stream reaches on the device,
+ * beside the published peak. Reads the `bytes` bytes at `buf` (device,
+ * 16-byte aligned, `bytes` a multiple of 16) once, front to back, with
+ * `blocks` workgroups of 1024 threads and non-temporal 16-byte loads, on
+ * `stream`, and writes each thread's XOR fold of the words it read to `out`
+ * (device, blocks * 1024 uint32; the caller's). Asynchronous: time it with
+ * events on `stream`. Errors: CBD_E_INVAL (NULL pointer, blocks < 1, a
+ * misaligned `buf` or `bytes`), CBD_E_DEVICE (launch). */
+int cbd_read_probe(const void* buf, size_t bytes, uint32_t* out, int32_t blocks, void* stream);
+
 /* The batched sampler alone, over caller-given fp32 logits [n][vocab]
  * (device): row j uses slot slots[j] and draw counter step_ids[j] (device
  * arrays). Updates the slots' penalty counts like a sampled step. The slots

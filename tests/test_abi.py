@@ -76,6 +76,17 @@ def test_step_rejects_null_engine():
     assert B.lib().cbd_step_forward(None, C.byref(st), None, None, None) == B.CBD_E_INVAL
 
 
+@pytest.mark.parametrize("buf,nbytes,out,blocks", [(None, 16, 256, 1), (256, 16, None, 1),
+                                                  (256, 16, 256, 0), (264, 16, 256, 1),
+                                                  (256, 24, 256, 1)])
+def test_read_probe_rejects_bad_arguments(buf, nbytes, out, blocks):
+    """NULL pointers, no workgroups, a buffer not 16-byte aligned or a size
+    not a multiple of 16: refused before any launch (no device memory is
+    touched, the addresses are never dereferenced)."""
+    rc = B.lib().cbd_read_probe(buf, nbytes, out, blocks, None)
+    assert rc == B.CBD_E_INVAL
+
+
 @pytest.mark.parametrize("rows,width", [(37, 688), (16, 256), (1, 4096), (560, 128)])
 def test_operand_tile_layout_reader_inverts_the_documented_layout(rows, width):
     # The layout cbd.h documents for "tiled" split planes: element (r, k) at
