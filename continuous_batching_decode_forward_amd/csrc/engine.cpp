@@ -86,7 +86,10 @@ WorkspaceLayout workspace_layout(const cbd_config& c) {
   L.ffn = take(tile_plane_elems(R, c.ffn_dim) * 4);
   L.lm_in = take(tile_plane_elems(S, d) * 4);
   L.logits = take(S * (size_t)c.vocab * 4);
-  L.amax_stride = (c.vocab + 15) / 16;
+  // Per-row argmax partials of the LM head: one per 64-column wave tile of
+  // the stream path (in 8-wave groups, ceil(vocab / 512) * 8 <= vocab / 64
+  // + 8) or per 128-column half tile of the dense path.
+  L.amax_stride = (c.vocab + 15) / 16 + 8;
   L.amax_val = take(S * (size_t)L.amax_stride * 4);
   L.amax_idx = take(S * (size_t)L.amax_stride * 4);
   size_t maxn = std::max({(size_t)2 * c.ffn_dim, qkv_n, d});

@@ -193,8 +193,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a,
 // after their copy lands, so the weights read there meet zeros.
 // Two waves per SIMD (256 registers, accumulators included). A workgroup
 // has NW = 4 or 8 waves: 8 halve the activation copies per weight byte, which
-// pays on the LM head at 64 rows (173 -> 163 us) but not on the narrower
-// layer matrices, whose grids then leave CUs idle.
+// pays on the LM head (64 rows: 173 -> 163 us) but not on the narrower layer
+// matrices, whose grids then leave CUs idle. The LM head's 8-wave
+// workgroups cover 512 columns, 251 of them, one per CU at every row count:
+// at 17-32 rows, 501 workgroups of 4 waves finished unevenly (per-workgroup
+// timestamps: half by about 105 us, the rest at up to 168) and the launch
+// took 172 us against 161 with 8 waves.
 // The grid is one-dimensional with the K split varying fastest: workgroup i
 // runs on XCD i mod 8, so at 8 splits each XCD holds one split (and reads
 // one eighth of the activation into its L2), at 4 splits each split sits on
@@ -206,13 +210,13 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a,
 template <int RT, int NT, int D, int NW, int EPI, bool W8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_kernel(GemmArgs a, int kc, int S, int n_groups) {
   constexpr int NM = EpiTraits<EPI>::NM;
-  constexpr int BLK = RT * 4;                 // 1 KB LDS blocks per stage
-  constexpr int CPW = BLK / NW;               // activation copies per wave per stage
-  static_assert(BLK % NW == 0, "activation blocks per wave");
+  constexpr int BLK = RT * 4;                 // 1 KB activation blocks per stage
+  constexpr int CPW = (BLK + NW - 1) / NW;    // activation copies per wave per stage
+  constexpr int BLKP = CPW * NW;              // LDS blocks per stage (see below)
   constexpr int WL = W8 ? 1 : 2;              // weight loads per column fragment per stage
   constexpr int LPS = NM * NT * WL + CPW;     // loads per stage per wave
   static_assert(D >= 3, "ring depth");
-  extern __shared__ uint4 xs[];               // [D][BLK][64]
+  extern __shared__ uint4 xs[];               // [D][BLKP][64]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -249,7 +253,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // of stage c is the operand tile (row fragment r0 / 16 + rt, k-block
   // kbeg / 32 + 2 c + h) of plane pl: lane `lane` holds row r0 + 16 rt + lr,
   // k + 32 h + 8 lg. Fragments past R read the last one (their outputs are
-  // never stored).
+  // never stored). With more waves than blocks (one row fragment, 8 waves)
+  // the waves past BLK copy such a clamped tile into a spare LDS block that
+  // is never read, so that every wave issues the same loads per stage and
+  // the vector-memory wait counts stay exact.
   const uint16_t* xsrc[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
@@ -293,11 +300,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int i = 0; i < CPW; ++i) {
       const int b = wave + NW * i;
       const int kb = min(kbeg / 32 + 2 * c + (b & 1), KT - 1);
-      copy16_to_lds(xsrc[i] + (size_t)kb * 512, xs + ((size_t)j * BLK + b) * 64);
+      copy16_to_lds(xsrc[i] + (size_t)kb * 512, xs + ((size_t)j * BLKP + b) * 64);
     }
   };
   auto compute = [&](int j, int c) {
-    const uint4* buf = xs + (size_t)j * BLK * 64;
+    const uint4* buf = xs + (size_t)j * BLKP * 64;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint4 xf[RT][2];
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
           for (int i = 0; i < CPW; ++i) {
             const int b = wave + NW * i;
             if (kbeg + 64 * c + 32 * (b & 1) + 8 * lg >= kend)
-              xs[((size_t)j * BLK + b) * 64 + lane] = make_uint4(0, 0, 0, 0);
+              xs[((size_t)j * BLKP + b) * 64 + lane] = make_uint4(0, 0, 0, 0);
           }
         }
         __syncthreads();
@@ -618,8 +625,9 @@ hipError_t launch_pack8(const int8_t* W, const float* scale, int32_t N, int32_t 
 // How one projection runs. Up to 64 rows: the stream kernel with RT row
 // fragments (16, 32 or 64 rows), 4 waves of NT column fragments sharing the
 // activation tile, S workgroups splitting K. Measured on the 8B shapes at
-// 1-64 rows on MI355X: the LM head wants 64-column waves (its 256-column
-// workgroups read one contiguous run per stage); the gate/up pair 16-column
+// 1-64 rows on MI355X: the LM head wants 64-column waves, 8 to a workgroup
+// (each 256-column half of it reads one contiguous run per stage); the
+// gate/up pair 16-column
 // waves over the whole K (no partials, no separate SwiGLU pass); the single
 // matrices 32-column waves with K split until the grid would pass one
 // workgroup per CU. More rows: the dense kernel (see above).
@@ -691,7 +699,7 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits, size_t parti
   p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
   p.NT = logits ? 4 : (NM == 2 ? 1 : 2);
   p.D = 4;
-  p.NW = logits && p.RT == 4 ? 8 : 4;
+  p.NW = logits ? 8 : 4;
   p.S = 1;
   if (!logits) {
     const int cols = 16 * p.NW * p.NT;
@@ -788,7 +796,7 @@ static hipError_t launch_stream(const GemmArgs& a, int S, hipStream_t st) {
   int kc;
   S = split_k(a.K, S, 64, &kc);
   if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 64, &kc);
-  const size_t lds = (size_t)D * RT * 4 * 1024;  // <= 64 KB for the shapes instantiated
+  const size_t lds = (size_t)D * ((RT * 4 + NW - 1) / NW * NW) * 1024;  // <= 64 KB as instantiated
   gemm_stream_kernel<RT, NT, D, NW, EPI, W8><<<(unsigned)(n_groups * S * r_groups), 64 * NW, lds, st>>>(
       a, kc, S, n_groups);
   return finish_splits<EPI>(a, S, st);
@@ -825,7 +833,7 @@ static hipError_t launch_stream_plan(const GemmArgs& a, const GemmPlan& p, hipSt
     ST(1, 1, 4) ST(2, 1, 4)
     return launch_stream<4, 1, 4, 4, EPI, W8>(a, p.S, st);
   } else if constexpr (EPI == EPI_LOGITS) {
-    ST(1, 4, 4) ST(2, 4, 4)
+    ST(1, 4, 8) ST(2, 4, 8)
     return launch_stream<4, 4, 4, 8, EPI, W8>(a, p.S, st);
   } else {
     ST(1, 2, 4) ST(2, 2, 4)

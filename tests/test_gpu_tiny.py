@@ -25,16 +25,18 @@ def tiny():
     return w, O.Model(CFG, w), weights_to(w, "cuda")
 
 
-def run_schedule(tiny, prompts, n_decode, chunk, bs, nb, seed, order=None, kv=None, final=None):
+def run_schedule(tiny, prompts, n_decode, chunk, bs, nb, seed, order=None, kv=None, final=None,
+                 cfg=CFG):
     """Drive both sides through the same steps; return per-step stats.
     kv: the engine's cache format (the oracle model in `tiny` must match);
-    final(eng, pool, tables, ctx) runs after the last step."""
+    final(eng, pool, tables, ctx) runs after the last step; cfg: the shape
+    the weights in `tiny` have."""
     w, om, wg = tiny
     n = len(prompts)
     perm = synth.permutation(seed, "blocks", nb)
     per = nb // n
     tables = np.stack([perm[i * per:(i + 1) * per] for i in range(n)]).astype(np.int32)
-    eng = make_engine(CFG, wg, block_size=bs, num_blocks=nb, max_blocks_per_seq=per,
+    eng = make_engine(cfg, wg, block_size=bs, num_blocks=nb, max_blocks_per_seq=per,
                       max_rows=256, max_seqs=8, max_position=per * bs, **(kv or {}))
     pool = om.paged_pool(nb, bs)
     ctx = [0] * n
@@ -61,7 +63,7 @@ def run_schedule(tiny, prompts, n_decode, chunk, bs, nb, seed, order=None, kv=No
                                ctx_lens=[ctx[i] for i in seqs], n_new=nn, tokens=toks,
                                want_token=want)
         n_out = meta.n_out
-        lg = torch.empty((max(n_out, 1), CFG.vocab), dtype=torch.float32, device="cuda")
+        lg = torch.empty((max(n_out, 1), cfg.vocab), dtype=torch.float32, device="cuda")
         tk = torch.full((max(n_out, 1),), -1, dtype=torch.int32, device="cuda")
         eng.step_forward(meta, lg, tk)
         torch.cuda.synchronize()
@@ -103,6 +105,20 @@ def prompts_for(seed, n=4, lo=5, hi=40):
 def test_tiny_prefill_then_20_greedy_steps(tiny):
     res = run_schedule(tiny, prompts_for(0), 20, chunk=64, bs=4, nb=64, seed=0)
     assert len(res) == 21
+    check(res)
+
+
+@pytest.mark.parametrize("vocab", [16, 48, 528])
+def test_tiny_small_vocabularies(vocab):
+    """Vocabularies narrower than one LM-head workgroup (512 columns): the
+    argmax partials of every wave tile, most of them past the vocabulary,
+    fit their buffer, and the ids stay the lowest maximum."""
+    from dataclasses import replace
+    cfg = replace(CFG, vocab=vocab, name=f"tiny-v{vocab}")
+    w = synth.make_weights(cfg, seed=4)
+    prompts = [synth.uniform_ints(4, f"p{i}", L, 0, vocab - 1) for i, L in enumerate([9, 30, 1, 17])]
+    res = run_schedule((w, O.Model(cfg, w), weights_to(w, "cuda")), prompts, 6, chunk=64, bs=4,
+                       nb=64, seed=4, cfg=cfg)
     check(res)
 
 
