@@ -177,7 +177,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a,
 
 // ------------------------------------------------------- the stream path
 //
-// One kernel for any row count. A workgroup is 4 waves side by side along N
+// One kernel for any row count. A workgroup is NW waves side by side along N
 // (each NT column fragments, RT row fragments) over one K range. Per 64-k
 // stage the workgroup's activation tile (RT x 16 rows x 64 k, hi and lo:
 // RT x 4 KB, kept in MFMA operand order -- block (rt, plane, 32-k half) is
@@ -383,12 +383,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 // ------------------------------------------------------- the dense path
 //
 // For many rows (a prefill chunk, a large batch) the projection is a dense
-// contraction and the aim is MFMA time. A workgroup of 4 waves (2 along N
-// x 2 along R) owns a 256-column x 16 RF-row tile; each wave a 128-column x
-// 8 RF-row block: per 32-k stage it reads 8 weight fragments and RF
-// activation fragments (RF/2 row fragments x hi, lo) from LDS and issues
-// 8 RF MFMAs, so the MFMA time of a stage is twice its LDS read time and
-// the activation tile is fetched once per 256 columns. Both operands reach
+// contraction and the aim is MFMA time. A workgroup of 8 waves (2 along N
+// x 4 along R) owns a 256-column x 16 RF-row tile; each wave a 128-column x
+// 4 RF-row block: per 32-k stage it reads 8 weight fragments and RF/2
+// activation fragments (RF/4 row fragments x hi, lo) from LDS and issues
+// 4 RF MFMAs, and the activation tile is fetched once per 256 columns. Both operands reach
 // LDS by direct global->LDS copies into a D-stage ring: 16 weight tiles
 // (1 KB each, straight from the packed layout) and RF fragments per plane.
 // The ring discipline is the stream path's: stage c + D - 1 is issued right
@@ -623,14 +622,14 @@ hipError_t launch_pack8(const int8_t* W, const float* scale, int32_t N, int32_t 
 }
 
 // How one projection runs. Up to 64 rows: the stream kernel with RT row
-// fragments (16, 32 or 64 rows), 4 waves of NT column fragments sharing the
-// activation tile, S workgroups splitting K. Measured on the 8B shapes at
-// 1-64 rows on MI355X: the LM head wants 64-column waves, 8 to a workgroup
-// (each 256-column half of it reads one contiguous run per stage); the
-// gate/up pair 16-column
-// waves over the whole K (no partials, no separate SwiGLU pass); the single
-// matrices 32-column waves with K split until the grid would pass one
-// workgroup per CU. More rows: the dense kernel (see above).
+// fragments (16, 32 or 64 rows), NW waves of NT column fragments sharing
+// the activation tile, S workgroups splitting K. Measured on the 8B shapes
+// at 1-64 rows on MI355X: the LM head wants 64-column waves, 8 to a
+// workgroup (each 256-column half of it reads one contiguous run per
+// stage); the gate/up pair 16-column waves, 4 to a workgroup, over the
+// whole K (no partials, no separate SwiGLU pass); the single matrices
+// 32-column waves, 4 to a workgroup, with K split until the grid would
+// pass one workgroup per CU. More rows: the dense kernel (see above).
 struct GemmPlan {
   bool dense;
   int RT, NT, D, NW, S;
