@@ -52,6 +52,20 @@ def step_bytes(shape, ctx, n_out, kv_elem=2, w_int8=False):
     return W + A + n_out * shape.vocab * 4
 
 
+def class_bytes(shape, ctx, n_out):
+    """Algorithmic HBM bytes per step of each kernel class of the decode step:
+    each projection's bf16 weights (every layer), the batch's K/V read and
+    appended for attention, the LM head's weights and fp32 logits."""
+    from continuous_batching_decode_forward_amd import synth
+    ws = synth.weight_shapes(shape)
+    L = shape.n_layers
+    mat = lambda *names: L * sum(2 * int(np.prod(ws[k])) for k in names)
+    kvb = 2 * shape.n_kv_heads * shape.head_dim * 2  # K and V of one position, one layer
+    return {"qkv": mat("w_qkv"), "o": mat("w_o"), "gateup": mat("w_gate", "w_up"),
+            "down": mat("w_down"), "attn": L * sum((int(c) + 2) * kvb for c in ctx),
+            "lm_head": lm_head_bytes(shape, n_out)}
+
+
 def lm_head_bytes(shape, n_out):
     """LM head per launch: the bf16 weight once, the fp32 activation rows
     (as their bf16 hi and lo halves) and the fp32 logits written."""
@@ -839,6 +853,20 @@ def main():
     sweep.sort(key=lambda r: r["batch"])
     lm_ms, lm_n = kern
     lm_bytes = lm_head_bytes(shape, Bn)
+    # Each kernel class of the same step timed on its own (HIP events around
+    # its launches, 10 steps), with its algorithmic bytes where it streams.
+    cb = class_bytes(shape, wl["ctx"][:Bn], Bn)
+    classes = {}
+    for name in ("QKV", "ROPE", "ATTN", "O", "GATEUP", "DOWN", "LM_HEAD", "SAMPLE", "NORM"):
+        _, _, k, _ = run(Bn, 10, 2, profile_class=getattr(B, "CBD_KERNEL_" + name))
+        key = name.lower()
+        us = k[0] * 1e3 * k[1] / 10  # per step
+        rec = {"us_per_step": us}
+        if key in cb:
+            rec["bytes"] = cb[key]
+            rec["gbs"] = cb[key] / (us * 1e-6) / 1e9
+            rec["frac"] = rec["gbs"] / PEAK_HBM_GBS
+        classes[key] = rec
     lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
     log(f"[bench] B={Bn}: {ms:.3f} ms/step ({wall / args.steps * 1e3:.3f} ms wall), "
         f"{tokps:.0f} tok/s, {gbs:.0f} GB/s; LM head {lm_ms * 1e3:.1f} us, {lm_gbs:.0f} GB/s")
@@ -885,6 +913,7 @@ def main():
                      "frac_of_read_probe": lm_gbs / probe["gbs"]},
         "hbm_read_probe": probe,
         "cpu_baseline": cpu,
+        "kernel_classes": classes,
         "sweep": sweep,
     }
     del wg
