@@ -79,18 +79,25 @@ def _advance(eng, meta, wl, B, j, max_ctx, mode, step_ids=None):
     return meta
 
 
-@pytest.mark.parametrize("shape,B,mode", [(configs.LLAMA8B_1L, 32, 0), (configs.TINY, 6, 1)],
-                         ids=["8b-layer-b32-greedy", "tiny-b6-sampled"])
-def test_graph_entry_point_replays_equal_eager_steps(shape, B, mode):
+@pytest.mark.parametrize("shape,B,mode,fmt", [(configs.LLAMA8B_1L, 32, 0, None),
+                                              (configs.TINY, 6, 1, None),
+                                              (configs.LLAMA8B_1L, 32, 0, "int8-e4m3")],
+                         ids=["8b-layer-b32-greedy", "tiny-b6-sampled", "8b-layer-b32-int8w-e4m3kv"])
+def test_graph_entry_point_replays_equal_eager_steps(shape, B, mode, fmt):
     """Eight decode steps with advancing contexts and fresh tokens, once
     eagerly and once through cbd_step_forward_graph (one recording, seven
     replays reading the updated metadata), from the same pool contents and
     sampler state: logits and tokens equal bit for bit at every step. Then
     a second step shape records a second graph, and the first shape replays
-    its cached graph again."""
+    its cached graph again. Also with int8 weights over an E4M3 cache."""
     from continuous_batching_decode_forward_amd import binding as Bd
     torch.cuda.set_device(0)
-    wg = synth.make_weights(shape, seed=3, device="cuda")
+    if fmt:
+        wg = synth.make_weights_int8(shape, seed=3, device="cuda")
+        kv = dict(kv_dtype=Bd.CBD_KV_FP8_E4M3, **bench.FP8_KV)
+    else:
+        wg = synth.make_weights(shape, seed=3, device="cuda")
+        kv = {}
     wl = bench.build_workload(shape, B, 3, ctx_range=(40, 900), bs=32)
     n_steps = 8
     # room for the appended positions: each table gets blocks past its context
@@ -107,7 +114,7 @@ def test_graph_entry_point_replays_equal_eager_steps(shape, B, mode):
         o += need[i]
     wl["tables"] = tables
     eng = Engine(shape, wg, block_size=32, num_blocks=total, max_blocks_per_seq=mbps,
-                 max_slots=B, max_rows=B, max_seqs=B, max_position=mbps * 32)
+                 max_slots=B, max_rows=B, max_seqs=B, max_position=mbps * 32, **kv)
     s = torch.cuda.Stream()
     try:
         bench.fill_pool(eng, 3, perm)
