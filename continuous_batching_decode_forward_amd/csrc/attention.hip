@@ -39,17 +39,38 @@ namespace cbd {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // One 32-key step's operands in registers, as loaded: K rows of the two S
-// tiles and the V^T pieces, 8 values each -- bf16 (16 bytes) or E4M3 codes
-// (8 bytes, widened to bf16 when the step is computed).
+// tiles and the V^T pieces -- bf16, 8 values (16 bytes) per MFMA operand,
+// or E4M3 codes, widened to bf16 when the step is computed: V^T 8 codes (8
+// bytes) per operand, K 16 codes (16 bytes) per load, the operands of two
+// MFMAs (see kdim below).
 template <int HD, bool F8>
 struct KVTile {
   using Frag = typename std::conditional<F8, uint2, uint4>::type;
-  Frag k[2][HD / 32];
+  uint4 k[2][F8 ? HD / 64 : HD / 32];
   Frag v[HD / 16];
 };
 
+// The head dimensions that lane group lg holds (8 consecutive ones) for the
+// j-th 32-wide slice of the S = K.Q^T contraction. Any assignment works as
+// long as K and Q use the same one and it covers each dimension once: bf16
+// takes dims 32 j + 8 lg; an 8-bit cache takes 64 (j / 2) + 16 lg + 8 (j % 2),
+// so that one 16-byte load per lane holds the codes of slices j and j + 1
+// and the four lane groups together read 64 consecutive bytes of a key row
+// (8-byte loads at dims 32 j + 8 lg read 32 bytes of every 128-byte row per
+// instruction).
+template <bool F8>
+__device__ __forceinline__ int kdim(int j, int lg) {
+  return F8 ? 64 * (j >> 1) + 16 * lg + 8 * (j & 1) : 32 * j + 8 * lg;
+}
+
 __device__ __forceinline__ uint4 widen(uint4 v) { return v; }
 __device__ __forceinline__ uint4 widen(uint2 v) { return e4m3x8_to_bf16x8(v); }
+// 16 bytes at element `elem` of the pool (bf16 values or E4M3 codes).
+template <bool F8>
+__device__ __forceinline__ uint4 load16(const void* base, size_t elem) {
+  return load_stream16(reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(base) +
+                                                         elem * (F8 ? 1 : 2)));
+}
 template <bool F8>
 __device__ __forceinline__ auto load_frag(const void* base, size_t elem) {
   if constexpr (F8)
@@ -109,11 +130,13 @@ __device__ __forceinline__ void attend_segment(
   // of its column for step j, as the hi and lo bf16 terms.
   bf16x8_t qf[2][QK_STEPS];
   {
-    const size_t at = ((size_t)(row0 + min(c_row, nn - 1)) * md.n_heads + c_head) * HD + 8 * lg;
+    const size_t at = ((size_t)(row0 + min(c_row, nn - 1)) * md.n_heads + c_head) * HD +
+                      (F8 ? 16 : 8) * lg;
 #pragma unroll
     for (int j = 0; j < QK_STEPS; ++j) {
-      qf[0][j] = as_bf16x8(*reinterpret_cast<const uint4*>(q_hi + at + 32 * j));
-      qf[1][j] = as_bf16x8(*reinterpret_cast<const uint4*>(q_lo + at + 32 * j));
+      const int d = kdim<F8>(j, 0);
+      qf[0][j] = as_bf16x8(*reinterpret_cast<const uint4*>(q_hi + at + d));
+      qf[1][j] = as_bf16x8(*reinterpret_cast<const uint4*>(q_lo + at + d));
     }
   }
 
@@ -162,11 +185,19 @@ __device__ __forceinline__ void attend_segment(
       const int blk = uniform(tbl[p0 / BS - b0]);
       const size_t kb = (size_t)blk * blk_stride + kv_off + (size_t)(p0 % BS) * HD;
       const size_t vb = (size_t)blk * blk_stride + kv_off + (p0 % BS);
+      if constexpr (F8) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < QK_STEPS; ++j)
-          T.k[t][j] = load_frag<F8>(pool_k, kb + (size_t)(krow0 + 4 * t) * HD + 8 * lg + 32 * j);
+          for (int j = 0; j < QK_STEPS; j += 2)
+            T.k[t][j / 2] = load16<F8>(pool_k, kb + (size_t)(krow0 + 4 * t) * HD + kdim<F8>(j, lg));
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < QK_STEPS; ++j)
+            T.k[t][j] = load_frag<F8>(pool_k, kb + (size_t)(krow0 + 4 * t) * HD + 8 * lg + 32 * j);
+      }
 #pragma unroll
       for (int t = 0; t < DT; ++t)
         T.v[t] = load_frag<F8>(pool_v, vb + (size_t)(16 * t + lr) * BS + 8 * lg);
@@ -175,9 +206,14 @@ __device__ __forceinline__ void attend_segment(
       for (int t = 0; t < 2; ++t) {
         const int p = min(p0 + krow0 + 4 * t, last);
         const int blk = tbl[p / BS - b0];
-        const size_t kp = (size_t)blk * blk_stride + kv_off + (size_t)(p % BS) * HD + 8 * lg;
+        const size_t kp = (size_t)blk * blk_stride + kv_off + (size_t)(p % BS) * HD;
+        if constexpr (F8) {
 #pragma unroll
-        for (int j = 0; j < QK_STEPS; ++j) T.k[t][j] = load_frag<F8>(pool_k, kp + 32 * j);
+          for (int j = 0; j < QK_STEPS; j += 2) T.k[t][j / 2] = load16<F8>(pool_k, kp + kdim<F8>(j, lg));
+        } else {
+#pragma unroll
+          for (int j = 0; j < QK_STEPS; ++j) T.k[t][j] = load_frag<F8>(pool_k, kp + 8 * lg + 32 * j);
+        }
       }
       // V^T pieces: row d = 16 t + lr, keys pv .. pv + 7 (pv = p0 + 8 lg)
       const int pv = min(p0 + 8 * lg, last & ~7);
@@ -221,7 +257,13 @@ __device__ __forceinline__ void attend_segment(
       sacc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < QK_STEPS; ++j) {
-        const bf16x8_t kf = as_bf16x8(widen(T.k[t][j]));
+        bf16x8_t kf;
+        if constexpr (F8) {
+          const uint4 c = T.k[t][j / 2];
+          kf = as_bf16x8(e4m3x8_to_bf16x8((j & 1) ? make_uint2(c.z, c.w) : make_uint2(c.x, c.y)));
+        } else {
+          kf = as_bf16x8(T.k[t][j]);
+        }
         sacc[t] = mfma16x16x32(kf, qf[0][j], sacc[t]);
         sacc[t] = mfma16x16x32(kf, qf[1][j], sacc[t]);
       }
