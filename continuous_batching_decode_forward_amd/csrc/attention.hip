@@ -743,40 +743,63 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(StepMeta m, RowMaps m
     const int qt = (r - maps.seq_row0[s]) / rpt;
     n_sp = piece_partials(tile_start(maps.item0[s], qt, nn, m.ctx_lens[s], rpt), pos, ps.len);
   }
-  // Both passes load four partial results at a time (one round trip per
-  // four instead of one per partial) and use them in key order.
+  // Up to CB_ONE partial results are loaded at once, all in flight
+  // together, then used in key order: one round trip. More take two passes
+  // (the maximum, then the sums) that load four at a time. Both ways add
+  // the same terms in the same order with the same maximum.
   const size_t base = ((size_t)r * md.n_heads + h) * ap.max_splits;
-  float M = -INFINITY;
-  for (int j0 = 0; j0 < n_sp; j0 += 4) {
-    float mv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) mv[u] = j0 + u < n_sp ? part_ml[2 * (base + j0 + u)] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) M = fmaxf(M, mv[u]);
-  }
   float acc[8], den = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int j0 = 0; j0 < n_sp; j0 += 4) {
-    float2 ml[4];
-    float4 oa[4], ob[4];
+  auto add = [&](float2 ml, float4 a, float4 b, float M) {
+    const float wj = exp2f(ml.x - M);
+    den += wj * ml.y;
+    acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
+    acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+  };
+  constexpr int CB_ONE = 16;
+  if (n_sp <= CB_ONE) {
+    float2 ml[CB_ONE];
+    float4 oa[CB_ONE], ob[CB_ONE];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (j0 + u < n_sp) {
-        ml[u] = reinterpret_cast<const float2*>(part_ml)[base + j0 + u];
-        const float4* op = reinterpret_cast<const float4*>(part_o + (base + j0 + u) * HD + 8 * sl);
+    for (int u = 0; u < CB_ONE; ++u)
+      if (u < n_sp) {
+        ml[u] = reinterpret_cast<const float2*>(part_ml)[base + u];
+        const float4* op = reinterpret_cast<const float4*>(part_o + (base + u) * HD + 8 * sl);
         oa[u] = op[0];
         ob[u] = op[1];
       }
+    float M = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (j0 + u < n_sp) {
-        const float wj = exp2f(ml[u].x - M);
-        den += wj * ml[u].y;
-        const float4 a = oa[u], b = ob[u];
-        acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
-        acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
-      }
+    for (int u = 0; u < CB_ONE; ++u)
+      if (u < n_sp) M = fmaxf(M, ml[u].x);
+#pragma unroll
+    for (int u = 0; u < CB_ONE; ++u)
+      if (u < n_sp) add(ml[u], oa[u], ob[u], M);
+  } else {
+    float M = -INFINITY;
+    for (int j0 = 0; j0 < n_sp; j0 += 4) {
+      float mv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mv[u] = j0 + u < n_sp ? part_ml[2 * (base + j0 + u)] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) M = fmaxf(M, mv[u]);
+    }
+    for (int j0 = 0; j0 < n_sp; j0 += 4) {
+      float2 ml[4];
+      float4 oa[4], ob[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u < n_sp) {
+          ml[u] = reinterpret_cast<const float2*>(part_ml)[base + j0 + u];
+          const float4* op = reinterpret_cast<const float4*>(part_o + (base + j0 + u) * HD + 8 * sl);
+          oa[u] = op[0];
+          ob[u] = op[1];
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u < n_sp) add(ml[u], oa[u], ob[u], M);
+    }
   }
   const float inv = 1.0f / den;
   bf16_t hi[8], lo[8];
