@@ -877,6 +877,8 @@ def main():
     probe = hbm_read_probe()
     log(f"[bench] streaming-read probe: {probe['gbs']:.0f} GB/s "
         f"({probe['frac_of_peak']:.3f} of the 8 TB/s peak)")
+    for rec in sweep:
+        rec["frac_of_read_probe"] = rec["hbm_gbs"] / probe["gbs"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -905,6 +907,8 @@ def main():
         "hbm_gbs": gbs,
         "step_algorithmic_bytes": byts,
         "step_roofline_frac": gbs / PEAK_HBM_GBS,
+        # the same step against the bandwidth a plain stream reaches here
+        "step_frac_of_read_probe": gbs / probe["gbs"],
         "roofline": {"bound": "hbm", "kernel": "lm_head_gemm", "achieved": lm_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": lm_gbs / PEAK_HBM_GBS,
                      "traffic": measured_traffic(Bn), "avg_launch_us": lm_ms * 1e3,
