@@ -479,7 +479,10 @@ int cbd_sched_step(cbd_sched* s, int32_t mode, int32_t* meta_dev, int32_t* host_
   if (p.n_out > 0) {
     he = hipMemcpyAsync(host_stage, tokens_dev, (size_t)p.n_out * sizeof(int32_t),
                         hipMemcpyDeviceToHost, hs);
-    if (he != hipSuccess) return fail(CBD_E_DEVICE, std::string("token download: ") + hipGetErrorString(he));
+    if (he != hipSuccess) {
+      (void)hipStreamSynchronize(hs);  // the upload may still read host_stage
+      return fail(CBD_E_DEVICE, std::string("token download: ") + hipGetErrorString(he));
+    }
   }
   he = hipStreamSynchronize(hs);
   if (he != hipSuccess) return fail(CBD_E_DEVICE, std::string("step: ") + hipGetErrorString(he));
