@@ -67,9 +67,9 @@ def class_bytes(shape, ctx, n_out):
 
 
 def lm_head_bytes(shape, n_out):
-    """LM head per launch: the bf16 weight once, the fp32 activation rows
-    (as their bf16 hi and lo halves) and the fp32 logits written."""
-    return shape.vocab * shape.d_model * 2 + n_out * shape.d_model * 4 + n_out * shape.vocab * 4
+    """LM head per launch: the bf16 weight once, the activation rows (the
+    final norm's output, read as bf16) and the fp32 logits written."""
+    return shape.vocab * shape.d_model * 2 + n_out * shape.d_model * 2 + n_out * shape.vocab * 4
 
 
 # The dominant kernel's HBM traffic comes from rocprofv3 counter runs kept in
@@ -746,7 +746,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--batch", type=int, default=64)
-    ap.add_argument("--sweep", default="1,8,32,64")
+    ap.add_argument("--sweep", default="1,8,32,64,128,256")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",

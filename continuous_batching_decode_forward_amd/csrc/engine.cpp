@@ -587,7 +587,9 @@ static int enqueue_step(cbd_engine* e, const cbd_step* s, float* logits_out, int
   float* logits = logits_out;
   if (!logits && s->mode == CBD_MODE_SAMPLE) logits = e->wsp<float>(e->ws.logits);
   GemmArgs g{};
-  g.X = lm_in; g.Xlo = lm_in_lo; g.R = s->n_out; g.K = c.d_model; g.W = e->packed + e->pl.lm_head; g.N = c.vocab;
+  // The LM head is a bf16 contraction: it reads the hi plane of its input
+  // alone (the final norm's output rounded to nearest bf16).
+  g.X = lm_in; g.Xlo = nullptr; g.R = s->n_out; g.K = c.d_model; g.W = e->packed + e->pl.lm_head; g.N = c.vocab;
   g.w8 = w8;
   g.Ws = scales8(e->pl.lm_head, c.vocab, c.d_model);
   g.epi = EPI_LOGITS; g.logits = logits;

@@ -21,13 +21,17 @@
 // long runs instead of 16 scattered ones; measured about 5-10% faster on the
 // LM head than blocks stored one after another).
 //
-// The activations are fp32 values carried as two bf16 planes (hi, lo), so
-// each weight fragment meets two B operands: acc += W.X_hi, acc += W.X_lo.
-// Both products are exact in the fp32 accumulator, and the result is the
-// fp32 dot product of W with X to within 2^-17 relative per term. The
-// second MFMA costs nothing while the weights stream from HBM (a 16 x 32
-// weight tile per 2 x 16 rows of MFMA work leaves the matrix cores idle
-// most of the time at these row counts).
+// The layer projections' activations are fp32 values carried as two bf16
+// planes (hi, lo), so each weight fragment meets two B operands: acc +=
+// W.X_hi, acc += W.X_lo. Both products are exact in the fp32 accumulator,
+// and the result is the fp32 dot product of W with X to within 2^-17
+// relative per term. The second MFMA costs nothing while the weights stream
+// from HBM (a 16 x 32 weight tile per 2 x 16 rows of MFMA work leaves the
+// matrix cores idle most of the time at these row counts). The LM head is a
+// bf16 contraction: its input is the hi plane alone (the final norm's
+// output rounded to nearest bf16), one MFMA per weight fragment and row
+// fragment, which halves its matrix work where that is what bounds it (at
+// 128-256 rows on the dense path).
 //
 // Up to 64 rows run on the stream path below, more rows on the dense path.
 // S workgroups along K leave fp32 partials that a second kernel (or the
@@ -75,6 +79,7 @@ __device__ __forceinline__ uint4 i8x8_to_bf16x8(uint2 c) {
 template <int EPI>
 struct EpiTraits {
   static constexpr int NM = EPI == EPI_SWIGLU ? 2 : 1;  // weight matrices
+  static constexpr int PL = EPI == EPI_LOGITS ? 1 : 2;  // activation planes (hi, lo)
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
@@ -179,9 +184,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a,
 //
 // One kernel for any row count. A workgroup is NW waves side by side along N
 // (each NT column fragments, RT row fragments) over one K range. Per 64-k
-// stage the workgroup's activation tile (RT x 16 rows x 64 k, hi and lo:
-// RT x 4 KB, kept in MFMA operand order -- block (rt, plane, 32-k half) is
-// 64 lanes x 16 bytes) is copied by direct global->LDS loads into a ring of
+// stage the workgroup's activation tile (RT x 16 rows x 64 k per plane:
+// RT x 4 KB with hi and lo, RT x 2 KB for the LM head's one plane, kept in
+// MFMA operand order -- block (rt, plane, 32-k half) is 64 lanes x 16
+// bytes) is copied by direct global->LDS loads into a ring of
 // D LDS stages, with no registers involved; each wave's weights stream
 // through a ring of D register stages. The loads of stage c + D - 1 are
 // issued right after the barrier of stage c, so D - 2 later stages stay in
@@ -210,7 +216,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a,
 template <int RT, int NT, int D, int NW, int EPI, bool W8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void gemm_stream_kernel(GemmArgs a, int kc, int S, int n_groups) {
   constexpr int NM = EpiTraits<EPI>::NM;
-  constexpr int BLK = RT * 4;                 // 1 KB activation blocks per stage
+  constexpr int PL = EpiTraits<EPI>::PL;
+  constexpr int BLK = RT * 2 * PL;            // 1 KB activation blocks per stage
   constexpr int CPW = (BLK + NW - 1) / NW;    // activation copies per wave per stage
   constexpr int BLKP = CPW * NW;              // LDS blocks per stage (see below)
   constexpr int WL = W8 ? 1 : 2;              // weight loads per column fragment per stage
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int b = wave + NW * i;
-    const int rt = b >> 2, pl = (b >> 1) & 1;
+    const int rt = b / (2 * PL), pl = (b >> 1) % PL;
     const int f = min(r0 / 16 + rt, (R - 1) >> 4);
     xsrc[i] = (pl ? a.Xlo : a.X) + (size_t)f * KT * 512 + lane * 8;
   }
@@ -307,11 +314,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const uint4* buf = xs + (size_t)j * BLKP * 64;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint4 xf[RT][2];
+      uint4 xf[RT][PL];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl) xf[rt][pl] = buf[((rt * 2 + pl) * 2 + h) * 64 + lane];
+        for (int pl = 0; pl < PL; ++pl) xf[rt][pl] = buf[((rt * PL + pl) * 2 + h) * 64 + lane];
       bf16x8_t wf[NM][NT];
 #pragma unroll
       for (int m = 0; m < NM; ++m)
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
           }
         }
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl)
+      for (int pl = 0; pl < PL; ++pl)
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -385,9 +392,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 // For many rows (a prefill chunk, a large batch) the projection is a dense
 // contraction and the aim is MFMA time. A workgroup of 8 waves (2 along N
 // x 4 along R) owns a 256-column x 16 RF-row tile; each wave a 128-column x
-// 4 RF-row block: per 32-k stage it reads 8 weight fragments and RF/2
-// activation fragments (RF/4 row fragments x hi, lo) from LDS and issues
-// 4 RF MFMAs, and the activation tile is fetched once per 256 columns. Both operands reach
+// 4 RF-row block: per 32-k stage it reads 8 weight fragments and RF/4
+// activation fragments per plane (hi and lo; the LM head's hi alone) from
+// LDS and issues 2 RF MFMAs per plane, and the activation tile is fetched
+// once per 256 columns. Both operands reach
 // LDS by direct global->LDS copies into a D-stage ring: 16 weight tiles
 // (1 KB each, straight from the packed layout) and RF fragments per plane.
 // The ring discipline is the stream path's: stage c + D - 1 is issued right
@@ -407,11 +415,12 @@ template <int RF, int D, int EPI>
 __global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a, int kc, int S,
                                                                       int n_tiles, int r_groups) {
   constexpr int NM = EpiTraits<EPI>::NM;
+  constexpr int PL = EpiTraits<EPI>::PL;
   constexpr int NT = 8 / NM;       // column fragments per matrix per wave
   constexpr int WR = DENSE_WAVES / 2;  // waves along R
   constexpr int RH = RF / WR;      // row fragments per wave
   constexpr int TW = 16;           // weight tiles per stage
-  constexpr int TS = TW + 2 * RF;  // 1 KB tiles per stage
+  constexpr int TS = TW + PL * RF; // 1 KB tiles per stage
   constexpr int LPS = TS / DENSE_WAVES;  // copies per stage per wave
   static_assert(TS % DENSE_WAVES == 0 && RF % WR == 0, "tile counts");
   static_assert(D >= 3 && (D - 2) * LPS < 64, "ring depth");
@@ -436,7 +445,7 @@ __global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a
 
   // Copy sources: this wave issues tiles t = wave + 8 i; t < 16 are weight
   // tiles (matrix t / CB, column block t % CB), the rest activation operand
-  // tiles (u = t - 16: row fragment u / 2, plane u % 2; fragments past R
+  // tiles (u = t - 16: row fragment u / PL, plane u % PL; fragments past R
   // read the last one, whose outputs are never stored).
   const uint16_t* src[LPS];
 #pragma unroll
@@ -449,8 +458,8 @@ __global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a
       src[i] = (m ? a.W2 : a.W) + wtile(nb, kbeg / 32, KT) + lane * 8;
     } else {
       const int u = t - TW;
-      const int f = min(r_base / 16 + (u >> 1), (R - 1) >> 4);
-      src[i] = ((u & 1) ? a.Xlo : a.X) + (size_t)f * KT * 512 + lane * 8;
+      const int f = min(r_base / 16 + u / PL, (R - 1) >> 4);
+      src[i] = (u % PL ? a.Xlo : a.X) + (size_t)f * KT * 512 + lane * 8;
     }
   }
   auto issue = [&](int slot, int c) {
@@ -474,13 +483,14 @@ __global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a
       for (int rh = 0; rh < RH; ++rh) acc[m][nt][rh] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   // The hi products of every accumulator, then the lo products: two MFMAs
-  // on one accumulator are 8 RH apart, never back to back. A wave raises its
+  // on one accumulator are 8 RH apart, never back to back (one plane: 8 RH
+  // independent accumulators in a row). A wave raises its
   // issue priority for its run of MFMAs, so that the matrix pipe stays fed
   // while the other wave of the SIMD issues its LDS reads and copies (2-5%
   // on the dense launches at 256-560 rows).
   auto compute = [&](int slot) {
     const uint4* buf = ring + (size_t)slot * TS * 64;
-    uint4 wf[NM][NT], xf[2][RH];
+    uint4 wf[NM][NT], xf[PL][RH];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -488,10 +498,10 @@ __global__ __launch_bounds__(64 * DENSE_WAVES) void gemm_dense_kernel(GemmArgs a
 #pragma unroll
     for (int rh = 0; rh < RH; ++rh)
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl) xf[pl][rh] = buf[(TW + 2 * (wr * RH + rh) + pl) * 64 + lane];
+      for (int pl = 0; pl < PL; ++pl) xf[pl][rh] = buf[(TW + PL * (wr * RH + rh) + pl) * 64 + lane];
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int pl = 0; pl < 2; ++pl)
+    for (int pl = 0; pl < PL; ++pl)
 #pragma unroll
       for (int rh = 0; rh < RH; ++rh)
 #pragma unroll
@@ -680,6 +690,7 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits, size_t parti
     // least 256 k each).
     double t_best = 1e30;
     for (int rf : {16, 12, 8}) {
+      if (logits && rf == 12) continue;  // the one-plane tile wants 8 or 16 fragments
       for (int S = 1; S <= (logits ? 1 : 16); ++S) {
         if (S > 1 && (K / S < 256 || (size_t)S * NM * R * N > partials_cap)) break;
         const double t = dense_cost(R, N, K, NM, rf, S);
@@ -692,7 +703,7 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits, size_t parti
     }
     p.dense = true;
     p.NT = 4 / NM;
-    p.D = p.RT == 8 ? 4 : 3;
+    p.D = p.RT == 8 && !logits ? 4 : 3;
     return p;
   }
   p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
@@ -795,7 +806,8 @@ static hipError_t launch_stream(const GemmArgs& a, int S, hipStream_t st) {
   int kc;
   S = split_k(a.K, S, 64, &kc);
   if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 64, &kc);
-  const size_t lds = (size_t)D * ((RT * 4 + NW - 1) / NW * NW) * 1024;  // <= 64 KB as instantiated
+  constexpr int PL = EpiTraits<EPI>::PL;
+  const size_t lds = (size_t)D * ((RT * 2 * PL + NW - 1) / NW * NW) * 1024;  // <= 64 KB as instantiated
   gemm_stream_kernel<RT, NT, D, NW, EPI, W8><<<(unsigned)(n_groups * S * r_groups), 64 * NW, lds, st>>>(
       a, kc, S, n_groups);
   return finish_splits<EPI>(a, S, st);
@@ -809,7 +821,7 @@ static hipError_t launch_dense(const GemmArgs& a, int S, hipStream_t st) {
   int kc;
   S = split_k(a.K, S, 32, &kc);
   if (S > 1 && (size_t)S * NM * a.R * a.N > a.partials_cap) S = split_k(a.K, 1, 32, &kc);
-  const size_t lds = (size_t)D * (16 + 2 * RF) * 1024;
+  const size_t lds = (size_t)D * (16 + EpiTraits<EPI>::PL * RF) * 1024;
   static bool lds_set = false;  // above 64 KB the launch must be allowed first
   if (!lds_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_dense_kernel<RF, D, EPI>),
@@ -848,8 +860,16 @@ static hipError_t launch_epi(const GemmArgs& a, hipStream_t st) {
   if (a.w8) return launch_stream_plan<EPI, true>(a, p, st);
   if (p.dense) {
     if (p.RT == 16) return launch_dense<16, 3, EPI>(a, p.S, st);
-    if (p.RT == 12) return launch_dense<12, 3, EPI>(a, p.S, st);
-    return launch_dense<8, 4, EPI>(a, p.S, st);
+    if constexpr (EPI == EPI_LOGITS) {
+      // One plane at 8 fragments: a 3-stage ring is 72 KB, two workgroups
+      // per CU, so the 501 column tiles of a 128k vocabulary run in one round
+      // (LM head at 96-128 rows 187-196 -> 178-187 us against 4 stages).
+      // 12 fragments do not split over 8 waves.
+      return launch_dense<8, 3, EPI>(a, p.S, st);
+    } else {
+      if (p.RT == 12) return launch_dense<12, 3, EPI>(a, p.S, st);
+      return launch_dense<8, 4, EPI>(a, p.S, st);
+    }
   }
   return launch_stream_plan<EPI, false>(a, p, st);
 }

@@ -140,6 +140,7 @@ inline size_t tile_plane_elems(size_t rows, size_t w) {
 struct GemmArgs {
   const uint16_t* X;    // [R][K] split activation in operand tiles: hi plane
   const uint16_t* Xlo;  //                                             lo plane
+                        // (not read by EPI_LOGITS: the LM head takes hi alone)
   int32_t R, K;
   const uint16_t* W;    // [N][K] bf16, packed (int8 k-pairs when w8)
   const uint16_t* W2;   // second packed matrix for EPI_SWIGLU (up), [N][K]

@@ -36,13 +36,14 @@
  *    step id, 0, 0), key = (seed, 0).
  *
  * Arithmetic: every dot product accumulates in double, in ascending index
- * order, and every activation stays a double: the norm outputs, the
- * projections, the rotated query, the attention output, the SwiGLU product
- * and the residual stream are never rounded. bf16 appears only where the
- * model stores values in memory that the step streams: the weights (given)
- * and the KV cache, where each appended K (after RoPE) and V is rounded to
- * bf16 (round to nearest even, directly from the double). Logits are
- * doubles; the greedy id is the lowest id of the maximum of the logits
+ * order, and every activation inside the layers stays a double: the norm
+ * outputs, the projections, the rotated query, the attention output, the
+ * SwiGLU product and the residual stream are never rounded. bf16 appears
+ * where the model stores values in memory that the step streams: the
+ * weights (given) and the KV cache, where each appended K (after RoPE) and
+ * V is rounded to bf16 (round to nearest even, directly from the double);
+ * and at the LM head, a bf16 contraction whose input (the final norm's
+ * output) is rounded to bf16 the same way. Logits are doubles; the greedy id is the lowest id of the maximum of the logits
  * rounded to binary32, the precision in which the GPU takes that decision.
  * OpenMP runs only across independent rows, heads or output elements,
  * never inside a reduction.
@@ -420,11 +421,16 @@ static void row_post_attention(const or_model* m, int32_t layer, double* x, cons
   for (int32_t i = 0; i < d; ++i) x[i] += acc2[i];
 }
 
-/* Final RMSNorm and LM head: logits[v] = sum_k norm(x)[k] * W_lm[v][k]. */
+/* Final RMSNorm and LM head: logits[v] = sum_k bf16(norm(x)[k]) * W_lm[v][k].
+ * The LM head is a bf16 contraction: its input, the final norm's output, is
+ * rounded once to bf16 like its weights, and the products accumulate in
+ * double. No stage follows it whose own rounding could turn this one's
+ * last-bit differences into larger ones. */
 static void row_logits(const or_model* m, const double* x, double* logits) {
   int32_t d = m->d_model;
   double* h = malloc(sizeof(double) * (size_t)d);
   or_rmsnorm(x, m->final_norm, d, m->rms_eps, h);
+  for (int32_t k = 0; k < d; ++k) h[k] = bf(tobf(h[k]));
 #pragma omp parallel for schedule(static)
   for (int32_t v = 0; v < m->vocab; ++v) {
     double s = 0.0;

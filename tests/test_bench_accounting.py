@@ -36,10 +36,10 @@ def test_class_bytes_sum_to_the_step_bytes():
     assert cb["qkv"] == 2 * 6144 * 4096 and cb["o"] == 2 * 4096 * 4096
     assert cb["gateup"] == 2 * 2 * 14336 * 4096 and cb["down"] == 2 * 4096 * 14336
     assert cb["attn"] == sum((c + 2) * 4096 for c in ctx)
-    assert cb["lm_head"] == 128256 * 4096 * 2 + 4 * 4096 * 4 + 4 * 128256 * 4
+    assert cb["lm_head"] == 128256 * 4096 * 2 + 4 * 4096 * 2 + 4 * 128256 * 4
     # the step adds the norm gains and embedding rows, and the LM head's
     # activation rows are counted only by its class
-    rest = 2 * (2 * 4096 + 4096) + len(ctx) * 4096 * 2 - len(ctx) * 4096 * 4
+    rest = 2 * (2 * 4096 + 4096) + len(ctx) * 4096 * 2 - len(ctx) * 4096 * 2
     assert sum(cb.values()) + rest == bench.step_bytes(shape, ctx, len(ctx))
 
 

@@ -126,5 +126,6 @@ def test_fp8_appends_are_the_rounded_rotated_keys_and_values():
                        o, rtol=0, atol=1e-12)
     t = O.bf16_to_f64(w["w_o"][0]).reshape(cfg.d_model, hq * hd) @ o
     hf = O.rmsnorm(x + t, w["final_norm"], cfg.rms_eps)
-    lm = O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ hf
+    # the LM head takes its input rounded to bf16
+    lm = O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ O.bf16_to_f64(O.bf16_round(hf))
     assert np.allclose(lg[1], lm, rtol=0, atol=1e-9)

@@ -123,7 +123,10 @@ def one_layer(seed, zero=()):
 
 
 def lm(w, cfg, hf):
-    return O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ hf
+    """The LM head as a bf16 contraction: its input rounded to bf16 (nearest
+    even), then a double product with the bf16 weights."""
+    hb = O.bf16_to_f64(O.bf16_round(hf))
+    return O.bf16_to_f64(w["lm_head"]).reshape(cfg.vocab, cfg.d_model) @ hb
 
 
 def test_zero_projections_make_the_layer_identity():
