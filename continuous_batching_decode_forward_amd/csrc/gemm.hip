@@ -650,7 +650,10 @@ struct GemmPlan {
 #define DENSE_MIN_ROWS 65
 
 // Estimated time (us) of a dense launch: rounds of one workgroup per CU
-// (every dense ring needs 96-144 KB of LDS) times the 32-k stages of a
+// (a projection's dense ring needs 96-144 KB of LDS; the LM head's 72 KB
+// ring at 8 fragments fits two per CU, which the estimate leaves out: for
+// the LM head it only picks the tile height, and measured at 96-256 rows
+// it picks the faster one) times the 32-k stages of a
 // workgroup times the stage time, which grows with the tile height (fitted
 // on the 8B matrices at 128-560 rows: 0.87, 1.19 and 1.5 us at RF = 8, 12,
 // 16), plus the split partials written and read back at about 6 TB/s, plus
