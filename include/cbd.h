@@ -34,9 +34,11 @@
  *  - Precision: the bytes the step streams -- weights and the KV cache --
  *    are bf16 (a cached K or V value is rounded to bf16 once, when it is
  *    appended). Activations between the step's kernels are fp32; the
- *    matrix-core contractions take them as two bf16 terms (hi + lo) and
- *    accumulate in fp32. Logits are fp32; the greedy id is the lowest id of
- *    their maximum.
+ *    matrix-core contractions of the layers take them as two bf16 terms
+ *    (hi + lo) and accumulate in fp32. The LM head is a bf16 contraction:
+ *    its input, the final norm's output, is rounded to nearest bf16, and it
+ *    accumulates in fp32. Logits are fp32; the greedy id is the lowest id
+ *    of their maximum.
  */
 #ifndef CBD_H
 #define CBD_H
@@ -354,7 +356,8 @@ const char* cbd_last_error(void);
 #define CBD_BUF_Q 4      /* split, row-major: rotated queries [rows][n_heads*head_dim] */
 #define CBD_BUF_ATTN 5   /* split, tiled: attention output [rows][n_heads*head_dim] */
 #define CBD_BUF_FFN 6    /* split, tiled: SwiGLU output [rows][ffn_dim] */
-#define CBD_BUF_LM_IN 7  /* split, tiled: final-norm rows fed to the LM head [rows][d_model] */
+#define CBD_BUF_LM_IN 7  /* split, tiled: final-norm rows [rows][d_model]; the LM head
+                            reads their hi plane (the rows rounded to bf16) */
 /* Device address and size in bytes of one of them (no copy, no sync). */
 int cbd_debug_buffer(cbd_engine* e, int32_t which, void** ptr, size_t* bytes);
 
