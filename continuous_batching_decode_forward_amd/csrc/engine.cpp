@@ -18,6 +18,11 @@ namespace cbd {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Per-row argmax partials of the LM head: one per 64-column wave tile of
+// the stream path (in 8-wave groups, ceil(vocab / 512) * 8 <= vocab / 64 +
+// 8) or per 128-column half tile of the dense path (ceil(vocab / 256) * 2).
+static int32_t amax_stride(int32_t vocab) { return (vocab + 63) / 64 + 8; }
+
 int validate_config(const cbd_config* c) {
   if (!c) return fail(CBD_E_INVAL, "config is NULL");
   if (c->n_layers < 1 || c->d_model < 1 || c->n_heads < 1 || c->n_kv_heads < 1 ||
@@ -51,6 +56,10 @@ int validate_config(const cbd_config* c) {
   if ((long long)(attn_cap_splits(c->max_position) - 1) * attn_split_cap(c->block_size) <
       c->max_position)
     return fail(CBD_E_UNSUPPORTED, "max_position too long for this block size");
+  for (int32_t r = 1; r <= c->max_seqs; ++r)  // the LM head's plans at every output count
+    if (gemm_amax_tiles(r, c->vocab, c->d_model, c->weight_dtype == CBD_W_INT8) >
+        amax_stride(c->vocab))
+      return fail(CBD_E_UNSUPPORTED, "LM-head argmax partials exceed their workspace stride");
   return CBD_OK;
 }
 
@@ -86,10 +95,7 @@ WorkspaceLayout workspace_layout(const cbd_config& c) {
   L.ffn = take(tile_plane_elems(R, c.ffn_dim) * 4);
   L.lm_in = take(tile_plane_elems(S, d) * 4);
   L.logits = take(S * (size_t)c.vocab * 4);
-  // Per-row argmax partials of the LM head: one per 64-column wave tile of
-  // the stream path (in 8-wave groups, ceil(vocab / 512) * 8 <= vocab / 64
-  // + 8) or per 128-column half tile of the dense path.
-  L.amax_stride = (c.vocab + 15) / 16 + 8;
+  L.amax_stride = amax_stride(c.vocab);
   L.amax_val = take(S * (size_t)L.amax_stride * 4);
   L.amax_idx = take(S * (size_t)L.amax_stride * 4);
   size_t maxn = std::max({(size_t)2 * c.ffn_dim, qkv_n, d});
