@@ -98,6 +98,55 @@ __device__ __forceinline__ void progress_prio(int done, int total) {
     __builtin_amdgcn_s_setprio(0);
 }
 
+// Where a segment's result goes. Each lane holds its query column's running
+// maximum m and sum l (base 2) and O^T[d = 16 t + 4 lg + i][col] for t <
+// HD / 16; `has_keys` is false for an idle column or one with no key in the
+// segment. SegPartials: the partial slot (row, head, split) in global
+// memory, merged later by the combine kernel.
+struct SegPartials {
+  float* part_ml;
+  float* part_o;
+  int max_splits, sp, n_heads;
+  template <int DT>
+  __device__ __forceinline__ void operator()(int row, int head, int lr, int lg, bool has_keys,
+                                             float m_run, float l_run, const floatx4_t (&o)[DT],
+                                             float vs) const {
+    if (!has_keys) return;
+    const size_t idx = ((size_t)row * n_heads + head) * max_splits + sp;
+    if (lg == 0) {
+      part_ml[2 * idx] = m_run;
+      part_ml[2 * idx + 1] = l_run;
+    }
+    float* op = part_o + idx * (16 * DT) + 4 * lg;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+      *reinterpret_cast<float4*>(op + 16 * t) =
+          make_float4(o[t][0] * vs, o[t][1] * vs, o[t][2] * vs, o[t][3] * vs);
+  }
+};
+
+// The row kernel's: the wave's slot in LDS, columns 0 .. ATT_ROW_G - 1 (one
+// decode row, its G heads), merged by the workgroup afterwards.
+struct SegLds {
+  float* ml;  // [ATT_ROW_G][2]
+  float* o;   // [ATT_ROW_G][HD]
+  template <int DT>
+  __device__ __forceinline__ void operator()(int row, int head, int lr, int lg, bool has_keys,
+                                             float m_run, float l_run, const floatx4_t (&o_)[DT],
+                                             float vs) const {
+    if (!has_keys || lr >= ATT_ROW_G) return;
+    if (lg == 0) {
+      ml[2 * lr] = m_run;
+      ml[2 * lr + 1] = l_run;
+    }
+    float* op = o + lr * (16 * DT) + 4 * lg;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+      *reinterpret_cast<float4*>(op + 16 * t) =
+          make_float4(o_[t][0] * vs, o_[t][1] * vs, o_[t][2] * vs, o_[t][3] * vs);
+  }
+};
+
 // The loads are unconditional and branch-free: a key past the item's range
 // reads a valid pool location (its score is masked to -inf, and its V
 // element is zeroed on the last step), and a block id outside the pool is
@@ -106,13 +155,12 @@ __device__ __forceinline__ void progress_prio(int done, int total) {
 // The kernel is held to 256 registers (accumulators included) so that two
 // waves share each SIMD: one wave's loads stay in flight while the other
 // computes (at one wave per SIMD the key stream stalls on every step).
-template <int HD, int BS, bool F8>
+template <int HD, int BS, bool F8, class Out>
 __device__ __forceinline__ void attend_segment(
     const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, const StepMeta& m,
-    const RowMaps& maps, const ModelDims& md, const AttnPlan& ap,
-    const void* __restrict__ pool_k, const void* __restrict__ pool_v,
-    float* __restrict__ part_ml, float* __restrict__ part_o, uint32_t* status, int* tbl, int s,
-    int g, int qt, int nn, int ctx, int k_lo, int k_hi, int sp, int done, int total) {
+    const RowMaps& maps, const ModelDims& md, const void* __restrict__ pool_k,
+    const void* __restrict__ pool_v, const Out& out, uint32_t* status, int* tbl, int s, int g,
+    int qt, int nn, int ctx, int k_lo, int k_hi, int done, int total) {
   constexpr int QK_STEPS = HD / 32;  // MFMAs over head_dim
   constexpr int DT = HD / 16;        // output d tiles
   const int lane = threadIdx.x & 63;
@@ -370,20 +418,10 @@ __device__ __forceinline__ void attend_segment(
 
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (!c_ok || k_lo >= c_end) return;  // this column has no keys in this segment
-  const size_t idx = ((size_t)(row0 + c_row) * md.n_heads + c_head) * ap.max_splits + sp;
-  if (lg == 0) {
-    part_ml[2 * idx] = m_run;
-    part_ml[2 * idx + 1] = l_run;
-  }
   // lane holds O^T[d = 16 t + 4 lg + i][col lr]; an 8-bit cache holds
   // V / v_scale
-  const float vs = F8 ? md.v_scale : 1.0f;
-  float* op = part_o + idx * HD + 4 * lg;
-#pragma unroll
-  for (int t = 0; t < DT; ++t)
-    *reinterpret_cast<float4*>(op + 16 * t) =
-        make_float4(o[t][0] * vs, o[t][1] * vs, o[t][2] * vs, o[t][3] * vs);
+  out(row0 + c_row, c_head, lr, lg, c_ok && k_lo < c_end, m_run, l_run, o,
+      F8 ? md.v_scale : 1.0f);
 }
 
 // The kernel is held to 256 registers (accumulators included) so that two
@@ -425,13 +463,92 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
       if (sg.sp >= ap.max_splits) {  // the host's piece_lo rules this out
         if ((threadIdx.x & 63) == 0) raise_status(status, ST_BAD_SHAPE);
       } else {
-        attend_segment<HD, BS, F8>(q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o,
-                               status, s_tbl[wave], s, g, sg.qt, nn, ctx, sg.k_lo, sg.k_hi, sg.sp,
-                               done, total);
+        const SegPartials out{part_ml, part_o, ap.max_splits, sg.sp, md.n_heads};
+        attend_segment<HD, BS, F8>(q_hi, q_lo, m, maps, md, pool_k, pool_v, out, status,
+                                   s_tbl[wave], s, g, sg.qt, nn, ctx, sg.k_lo, sg.k_hi, done,
+                                   total);
       }
       b += sg.steps;
       done += sg.steps;
     }
+  }
+}
+
+// -------------------------------------------------------------- row kernel
+//
+// Decode-only steps over short contexts (every sequence one row, at most
+// ATT_ROW_KEYS keys): workgroup (sequence s, KV head g) of ATT_ROW_WAVES
+// waves. Wave w takes the w-th equal run of the row's 32-key steps through
+// the same segment code, leaves its (m, l, O) in LDS, and the workgroup
+// merges the runs in key order with the combine kernel's arithmetic: no
+// partial results in global memory and no second launch. At these sizes a
+// step is a chain of short launches, so the launch it saves is most of its
+// gain. A sequence that does not have exactly one row is refused (status
+// BAD_SHAPE, zero outputs); a row no valid sequence owns gets zero outputs
+// from the workgroups whose sequence index equals it (rows number the
+// sequences here).
+template <int HD, int BS, bool F8>
+__global__ __launch_bounds__(64 * ATT_ROW_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void attention_row_kernel(
+    const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, StepMeta m,
+    RowMaps maps, ModelDims md, int R, const void* __restrict__ pool_k,
+    const void* __restrict__ pool_v, uint16_t* __restrict__ out_hi, uint16_t* __restrict__ out_lo,
+    uint32_t* status) {
+  __shared__ int s_tbl[ATT_ROW_WAVES][ATT_TBL];
+  __shared__ float s_ml[ATT_ROW_WAVES][ATT_ROW_G][2];
+  __shared__ float s_o[ATT_ROW_WAVES][ATT_ROW_G][HD];
+  constexpr int LPP = HD / 8;  // merge threads per head, 8 dimensions each
+  constexpr int T = 64 * ATT_ROW_WAVES;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int s = blockIdx.x / md.n_kv_heads, g = blockIdx.x % md.n_kv_heads;
+  const int G = md.n_heads / md.n_kv_heads;
+  const int KB = (md.n_heads * HD + 31) / 32;
+  auto zero_row = [&](int row) {  // this KV head's G outputs of one row
+    for (int t = threadIdx.x; t < G * LPP; t += T) {
+      const size_t at = tile_at(row, (g * G + t / LPP) * HD + 8 * (t % LPP), KB);
+      *reinterpret_cast<uint4*>(out_hi + at) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(out_lo + at) = make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (s < R && maps.row_seq[s] < 0) zero_row(s);
+  const int r = maps.seq_row0[s];
+  const int nn = m.n_new[s];
+  if (r < 0 || r >= R || maps.row_seq[r] != s) return;  // refused by prep (no rows to serve)
+  if (nn != 1) {  // served rows, but more than one: not a decode row
+    if (threadIdx.x == 0 && g == 0) raise_status(status, ST_BAD_SHAPE);
+    for (int i = 0; i < nn && r + i < R; ++i) zero_row(r + i);
+    return;
+  }
+  const int ctx = m.ctx_lens[s];
+  const int n_steps = ceil_div(ctx + 1, 32);  // keys 0 .. ctx, the row's own included
+  const int per = ceil_div(n_steps, ATT_ROW_WAVES);
+  const int st0 = wave * per, st1 = min(n_steps, st0 + per);
+  if (st0 < st1) {
+    const SegLds out{&s_ml[wave][0][0], &s_o[wave][0][0]};
+    attend_segment<HD, BS, F8>(q_hi, q_lo, m, maps, md, pool_k, pool_v, out, status, s_tbl[wave],
+                               s, g, 0, 1, ctx, 32 * st0, min(ctx + 1, 32 * st1), 0, st1 - st0);
+  }
+  __syncthreads();
+  const int n_used = ceil_div(n_steps, per);
+  for (int t = threadIdx.x; t < G * LPP; t += T) {
+    const int j = t / LPP, sl = t % LPP;
+    float M = -INFINITY;
+    for (int w = 0; w < n_used; ++w) M = fmaxf(M, s_ml[w][j][0]);
+    float acc[8], den = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int w = 0; w < n_used; ++w) {
+      const float wj = exp2f(s_ml[w][j][0] - M);
+      den += wj * s_ml[w][j][1];
+      const float4 a = *reinterpret_cast<const float4*>(&s_o[w][j][8 * sl]);
+      const float4 b = *reinterpret_cast<const float4*>(&s_o[w][j][8 * sl + 4]);
+      acc[0] += wj * a.x; acc[1] += wj * a.y; acc[2] += wj * a.z; acc[3] += wj * a.w;
+      acc[4] += wj * b.x; acc[5] += wj * b.y; acc[6] += wj * b.z; acc[7] += wj * b.w;
+    }
+    const float inv = 1.0f / den;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = acc[e] * inv;
+    store_split8(out_hi, out_lo, tile_at(r, (g * G + j) * HD + 8 * sl, KB), y);
   }
 }
 
@@ -829,6 +946,23 @@ static void launch_items(int blocks, const uint16_t* q_hi, const uint16_t* q_lo,
       q_hi, q_lo, m, maps, md, ap, pool_k, pool_v, part_ml, part_o, status);
 }
 
+template <int HD, int BS>
+static void launch_rows(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R, const StepMeta& m,
+                        const RowMaps& maps, const ModelDims& md, const void* pool_k,
+                        const void* pool_v, uint16_t* out_hi, uint16_t* out_lo, uint32_t* status,
+                        hipStream_t st) {
+  const unsigned grid = (unsigned)(m.n_seqs * md.n_kv_heads);
+  if constexpr (BS >= 8) {
+    if (md.kv_fp8) {
+      attention_row_kernel<HD, BS, true><<<grid, 64 * ATT_ROW_WAVES, 0, st>>>(
+          q_hi, q_lo, m, maps, md, R, pool_k, pool_v, out_hi, out_lo, status);
+      return;
+    }
+  }
+  attention_row_kernel<HD, BS, false><<<grid, 64 * ATT_ROW_WAVES, 0, st>>>(
+      q_hi, q_lo, m, maps, md, R, pool_k, pool_v, out_hi, out_lo, status);
+}
+
 // Dynamic LDS above 64 KB must be allowed per kernel before its first launch.
 static hipError_t allow_lds(const void* kernel, size_t bytes) {
   return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
@@ -840,6 +974,17 @@ static hipError_t launch_hd(const uint16_t* q_hi, const uint16_t* q_lo, int32_t 
                             const AttnPlan& ap, const void* pool_k_, const void* pool_v_,
                             float* part_ml, float* part_o, uint16_t* out_hi, uint16_t* out_lo,
                             uint32_t* status, hipStream_t st) {
+  if (ap.row_kernel) {
+    switch (md.block_size) {
+      case 4: launch_rows<HD, 4>(q_hi, q_lo, R, m, maps, md, pool_k_, pool_v_, out_hi, out_lo, status, st); break;
+      case 8: launch_rows<HD, 8>(q_hi, q_lo, R, m, maps, md, pool_k_, pool_v_, out_hi, out_lo, status, st); break;
+      case 16: launch_rows<HD, 16>(q_hi, q_lo, R, m, maps, md, pool_k_, pool_v_, out_hi, out_lo, status, st); break;
+      case 32: launch_rows<HD, 32>(q_hi, q_lo, R, m, maps, md, pool_k_, pool_v_, out_hi, out_lo, status, st); break;
+      case 64: launch_rows<HD, 64>(q_hi, q_lo, R, m, maps, md, pool_k_, pool_v_, out_hi, out_lo, status, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   // the block kernel reads a bf16 cache (an 8-bit cache plans no block items)
   const uint16_t* pool_k = static_cast<const uint16_t*>(pool_k_);
   const uint16_t* pool_v = static_cast<const uint16_t*>(pool_v_);

@@ -100,6 +100,18 @@ inline AttnPlan plan_attention(int n_heads, int n_kv_heads, int block_size, int 
     if (items > (1LL << 30)) items = 1LL << 30;
     ap.grid_items_b = (int32_t)items;
   }
+  // One row per sequence (every n_new is 1 when the rows number the
+  // sequences) over at most ATT_ROW_KEYS keys, one (sequence, KV head)
+  // workgroup per CU at most: the row kernel, whose workgroup merges its own
+  // waves' results, so no combine launch follows. Measured against the
+  // per-tile kernel + combine on the 8B layer over contexts U[16, 1023]:
+  // 256 workgroups 37 -> 28 us; 512 and 2048 (more than one per CU, rows of
+  // unequal length) 4 and 24 us slower; 8 (one row) 3 us slower. The 2B
+  // 28-layer decode step at 64 and 256 workgroups: 2.0-2.1 -> 1.91 ms and
+  // 2.41-2.43 -> 2.30 ms.
+  const int row_wgs = n_seqs * n_kv_heads;
+  ap.row_kernel = n_rows == n_seqs && max_ctx <= ATT_ROW_KEYS && G <= ATT_ROW_G &&
+                  row_wgs >= ATT_ROW_MIN_WG && row_wgs <= cus_waves / ATT_ROW_WAVES;
   return ap;
 }
 

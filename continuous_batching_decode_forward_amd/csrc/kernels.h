@@ -52,6 +52,14 @@ struct ModelDims {
 // Query columns (rows x heads of one KV head) per block-kernel work item.
 #define ATT_BLOCK_COLS 256
 
+// Row kernel: waves per workgroup, the longest context (keys) it takes, the
+// most query heads per KV head it merges, and the fewest workgroups
+// (sequences x KV heads) it runs with.
+#define ATT_ROW_WAVES 8
+#define ATT_ROW_KEYS 1024
+#define ATT_ROW_G 8
+#define ATT_ROW_MIN_WG 64
+
 // Attention work decomposition chosen by the host for one step.
 struct AttnPlan {
   int32_t split_len;   // keys per block-kernel work item (multiple of 32)
@@ -66,6 +74,9 @@ struct AttnPlan {
   // block kernel, block_rows rows per work item (0: every sequence runs on
   // the per-tile kernel); grid_items_b bounds its work items.
   int32_t block_min, block_rows, grid_items_b;
+  // Decode-only steps over short contexts: one workgroup per (sequence, KV
+  // head), its waves splitting the keys and merging in LDS (no combine).
+  int32_t row_kernel;
 };
 
 // Row maps and attention schedule (one workgroup) together with the

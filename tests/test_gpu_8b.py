@@ -99,6 +99,21 @@ def test_8b_layer_decode_step_matches_oracle(big, B, rows):
     assert np.array_equal(own, all_tk)
 
 
+@pytest.mark.parametrize("B,hi", [(8, 1023), (32, 1023), (32, 1024), (64, 1023)])
+def test_8b_layer_decode_over_contexts_up_to_1k(big, B, hi):
+    """Decode-only steps whose keys fit 1024, over 64 to 256 (sequence, KV
+    head) pairs, run on the row kernel (a workgroup per pair, merged in
+    LDS); one key more (hi 1024), or more pairs than CUs (B = 64), runs on
+    the per-tile kernel and its combine. Every row's attention is checked."""
+    rows = [0, B // 2, B - 1]
+    ok, mx, res, g_tk, r_tk, own, all_tk, att = decode_step(big, B, seed=B + hi, sample_rows=rows,
+                                                            lo=16, hi=hi)
+    assert ok, f"max abs logit error {mx:.3g}"
+    assert att.max() <= ATTN_TOL, f"attention rows {np.nonzero(att > ATTN_TOL)[0][:8].tolist()}"
+    assert np.array_equal(g_tk[res], r_tk[res])
+    assert np.array_equal(own, all_tk)
+
+
 def test_8b_layer_short_contexts_and_block_edges(big):
     # contexts 31, 32, 33, 63, 64 around 32-position block edges
     ok, mx, res, g_tk, r_tk, own, all_tk, att = decode_step(big, 5, seed=77, sample_rows=range(5),

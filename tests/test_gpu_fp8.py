@@ -131,11 +131,15 @@ def big8():
     return wg, om, wc
 
 
-@pytest.mark.parametrize("Bn,rows", [(8, [0, 3, 7]), (64, [0, 17, 40, 63])])
-def test_8b_layer_fp8_decode_step(big8, Bn, rows):
+# contexts U[512, 4096] run on the per-tile kernel; 32 rows over contexts
+# up to 1023 keys run on the row kernel
+@pytest.mark.parametrize("Bn,rows,hi", [(8, [0, 3, 7], 4096), (64, [0, 17, 40, 63], 4096),
+                                        (32, [0, 15, 31], 1023)])
+def test_8b_layer_fp8_decode_step(big8, Bn, rows, hi):
     wg, om, _ = big8
     ok, mx, res, g_tk, r_tk, own, all_tk, att = test_gpu_8b.decode_step(
-        (wg, om), Bn, seed=100 + Bn, sample_rows=rows, kv=LAYER_KV, om=om)
+        (wg, om), Bn, seed=100 + Bn, sample_rows=rows, lo=16 if hi < 4096 else 512, hi=hi,
+        kv=LAYER_KV, om=om)
     print(f"8b fp8 B={Bn}: max abs logit error {mx:.4f}, decidable rows {int(res.sum())}/"
           f"{len(rows)}, attention of all {Bn} rows: largest error {att.max():.2e}")
     assert ok, f"max abs logit error {mx:.3g}"

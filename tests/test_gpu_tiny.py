@@ -140,6 +140,31 @@ def test_tiny_block_sizes_and_ragged_contexts(tiny, bs, chunk):
     check(res)
 
 
+def test_row_kernel_refuses_a_sequence_that_is_not_one_decode_row(tiny):
+    """A step with as many rows as sequences runs attention on the row kernel
+    (32 sequences x 2 KV heads = 64 workgroups). If the device metadata does
+    not give every sequence one row (here 2 + 0 for the first two), that
+    sequence is refused with BAD_SHAPE and the step completes."""
+    w, om, wg = tiny
+    n = 32
+    eng = make_engine(CFG, wg, block_size=4, num_blocks=2 * n, max_blocks_per_seq=4,
+                      max_rows=2 * n, max_seqs=n, max_position=16)
+    tk = torch.zeros(n, dtype=torch.int32, device="cuda")
+    tables = [[2 * i, 2 * i + 1, -1, -1] for i in range(n)]
+    n_new = [2, 0] + [1] * (n - 2)
+    want = [1 if k > 0 else 0 for k in n_new]
+    meta = eng.upload_step(slots=list(range(n)), block_tables=tables, ctx_lens=[3] * n,
+                           n_new=n_new, tokens=[1] * n, want_token=want)
+    eng.step_forward(meta, None, tk)
+    assert eng.status() & B.CBD_STATUS_BAD_SHAPE
+    # the same sequences as decode rows run cleanly
+    meta = eng.upload_step(slots=list(range(n)), block_tables=tables, ctx_lens=[3] * n,
+                           n_new=[1] * n, tokens=[1] * n, want_token=[1] * n)
+    eng.step_forward(meta, None, tk)
+    assert eng.status() == 0
+    eng.close()
+
+
 def test_device_refuses_bad_metadata_without_faulting(tiny):
     w, om, wg = tiny
     eng = make_engine(CFG, wg, block_size=4, num_blocks=16, max_blocks_per_seq=4, max_rows=16,
