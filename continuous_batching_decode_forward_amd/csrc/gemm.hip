@@ -201,10 +201,11 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a,
 // has NW = 4 or 8 waves: 8 halve the activation copies per weight byte, which
 // pays on the LM head (64 rows: 173 -> 163 us) but not on the narrower layer
 // matrices, whose grids then leave CUs idle. The LM head's 8-wave
-// workgroups cover 512 columns, 251 of them, one per CU at every row count:
-// at 17-32 rows, 501 workgroups of 4 waves finished unevenly (per-workgroup
-// timestamps: half by about 105 us, the rest at up to 168) and the launch
-// took 172 us against 161 with 8 waves.
+// workgroups cover 512 columns, 251 of them for a 128256-column vocabulary,
+// one per CU at every row count: at 17-32 rows, 501 workgroups of 4 waves
+// finished unevenly (per-workgroup timestamps: half by about 105 us, the
+// rest at up to 168) and the launch took 172 us against 161 with 8 waves.
+// A vocabulary past 256 such workgroups takes 4-wave ones (see the plan).
 // The grid is one-dimensional with the K split varying fastest: workgroup i
 // runs on XCD i mod 8, so at 8 splits each XCD holds one split (and reads
 // one eighth of the activation into its L2), at 4 splits each split sits on
@@ -712,7 +713,11 @@ static GemmPlan plan_gemm(int R, int N, int K, int NM, bool logits, size_t parti
   p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
   p.NT = logits ? 4 : (NM == 2 ? 1 : 2);
   p.D = 4;
-  p.NW = logits ? 8 : 4;
+  // The LM head's 512-column workgroups while they fit one per CU (a
+  // 128256-column vocabulary: 251); past that, 256-column ones (a 151936-
+  // column vocabulary: 297 would leave 41 CUs running two, 126 us per launch
+  // at 2048 k against 104 with 594 of 4 waves).
+  p.NW = logits && (N + 511) / 512 <= 256 ? 8 : 4;
   p.S = 1;
   if (!logits) {
     const int cols = 16 * p.NW * p.NT;
@@ -847,7 +852,7 @@ static hipError_t launch_stream_plan(const GemmArgs& a, const GemmPlan& p, hipSt
     ST(1, 1, 4) ST(2, 1, 4)
     return launch_stream<4, 1, 4, 4, EPI, W8>(a, p.S, st);
   } else if constexpr (EPI == EPI_LOGITS) {
-    ST(1, 4, 8) ST(2, 4, 8)
+    ST(1, 4, 8) ST(2, 4, 8) ST(1, 4, 4) ST(2, 4, 4) ST(4, 4, 4)
     return launch_stream<4, 4, 4, 8, EPI, W8>(a, p.S, st);
   } else {
     ST(1, 2, 4) ST(2, 2, 4)
