@@ -12,7 +12,8 @@ import oracle as O
 from continuous_batching_decode_forward_amd import binding as B
 from continuous_batching_decode_forward_amd import configs, synth
 
-from gpu_util import compare_logits, make_engine, resolvable_rows, weights_to
+from gpu_util import (attention_rows_vs_oracle, compare_logits, fill_pool, make_engine,
+                      oracle_pool, resolvable_rows, weights_to)
 
 pytestmark = pytest.mark.gpu
 
@@ -138,6 +139,48 @@ def test_tiny_block_sizes_and_ragged_contexts(tiny, bs, chunk):
                for i, L in enumerate([bs - 1, bs, bs + 1, 1])]
     res = run_schedule(tiny, prompts, 5, chunk=chunk, bs=bs, nb=64 if bs < 32 else 32, seed=bs)
     check(res)
+
+
+@pytest.mark.parametrize("bs", [4, 8, 16, 32, 64])
+def test_row_kernel_decode_matches_oracle_at_every_block_size(tiny, bs):
+    """32 sequences x 2 KV heads = 64 (sequence, KV head) pairs, one decode
+    row each over 5..120 cached positions through shuffled block tables:
+    attention runs on the row kernel. Every row's attention output and
+    logits against the oracle."""
+    w, om, wg = tiny
+    n = 32
+    ctx = synth.uniform_ints(bs, "rowctx", n, 5, 120)
+    need = [-(-(int(c) + 1) // bs) for c in ctx]
+    total = int(sum(need))
+    perm = synth.permutation(bs, "rowblocks", total)
+    mbps = -(-121 // bs)
+    tables = np.full((n, mbps), -1, np.int32)
+    o = 0
+    for i in range(n):
+        tables[i, :need[i]] = perm[o:o + need[i]]
+        o += need[i]
+    tokens = synth.uniform_ints(bs, "rowtok", n, 0, CFG.vocab - 1)
+    eng = make_engine(CFG, wg, block_size=bs, num_blocks=total, max_blocks_per_seq=mbps,
+                      max_rows=n, max_seqs=n, max_position=mbps * bs)
+    fill_pool(eng, bs, perm)
+    meta = eng.upload_step(slots=list(range(n)), block_tables=tables, ctx_lens=ctx, n_new=[1] * n,
+                           tokens=tokens, want_token=[1] * n)
+    lg = torch.empty((n, CFG.vocab), dtype=torch.float32, device="cuda")
+    tk = torch.empty(n, dtype=torch.int32, device="cuda")
+    eng.step_forward(meta, lg, tk)
+    torch.cuda.synchronize()
+    assert eng.status() == 0
+    att = attention_rows_vs_oracle(eng, tables, ctx, [1] * n)
+    g_lg, g_tk = lg.cpu().numpy(), tk.cpu().numpy()
+    eng.close()
+    pool, compact = oracle_pool(CFG, bs, list(tables), [int(c) for c in ctx], bs, [1] * n)
+    ref_lg, ref_tk = O.paged_step(om, pool, compact, [int(c) for c in ctx], [1] * n,
+                                  [int(t) for t in tokens], [1] * n)
+    ok, mx, row_err = compare_logits(g_lg, ref_lg)
+    assert ok, f"max abs logit error {mx:.3g}"
+    assert att.max() <= 2.0 ** -12, f"attention rows {np.nonzero(att > 2.0 ** -12)[0][:8].tolist()}"
+    res = resolvable_rows(ref_lg, row_err)
+    assert np.array_equal(g_tk[res], np.asarray(ref_tk)[res])
 
 
 def test_row_kernel_refuses_a_sequence_that_is_not_one_decode_row(tiny):
