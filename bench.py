@@ -6,8 +6,8 @@ Workload (default): one 8B-shaped decoder layer + LM head (d_model 4096,
 ~N(0, 0.02), B decode rows with contexts uniform in 512..4096 held as
 synthetic N(0,1) bf16 KV in 32-position blocks through shuffled block
 tables, greedy argmax. A step is one cbd_step_forward over all B rows with
-every input already in HBM. The headline is B = 64; B in {1, 8, 32, 64} is
-also reported.
+every input already in HBM. The headline is B = 64; B in {1, 8, 32, 128,
+256} is also reported.
 
 Prints one JSON line: decode tokens/s, ms per step, achieved HBM GB/s under
 the (W + B*A)/beta cost model, the dominant kernel's roofline (timed with HIP
