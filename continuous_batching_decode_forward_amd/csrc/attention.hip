@@ -30,6 +30,7 @@
 #include "attn_sched.h"
 #include "common.h"
 #include "kernels.h"
+#include "rope_append.h"
 
 namespace cbd {
 
@@ -478,21 +479,24 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
 //
 // Decode-only steps over short contexts (every sequence one row, at most
 // ATT_ROW_KEYS keys): workgroup (sequence s, KV head g) of ATT_ROW_WAVES
-// waves. Wave w takes the w-th equal run of the row's 32-key steps through
-// the same segment code, leaves its (m, l, O) in LDS, and the workgroup
-// merges the runs in key order with the combine kernel's arithmetic: no
-// partial results in global memory and no second launch. At these sizes a
-// step is a chain of short launches, so the launch it saves is most of its
-// gain. A sequence that does not have exactly one row is refused (status
-// BAD_SHAPE, zero outputs); a row no valid sequence owns gets zero outputs
-// from the workgroups whose sequence index equals it (rows number the
-// sequences here).
+// waves. First the workgroup does the RoPE + KV append of its row for the
+// slots only it reads -- K and V of head g and the G query heads of g --
+// and a workgroup barrier orders those stores before its own loads (no
+// other workgroup reads them, so no wider fence is needed). Then wave w
+// takes the w-th equal run of the row's 32-key steps through the same
+// segment code, leaves its (m, l, O) in LDS, and the workgroup merges the
+// runs in key order with the combine kernel's arithmetic: no partial
+// results in global memory, no RoPE/append launch before and no combine
+// launch after. At these sizes a step is a chain of short launches, so the
+// launches it saves are most of its gain. A sequence that does not have
+// exactly one row is refused (status BAD_SHAPE, zero outputs; its rows are
+// still appended, as the standalone RoPE/append kernel would); a row no
+// valid sequence owns gets zero outputs from the workgroups whose sequence
+// index equals it (rows number the sequences here).
 template <int HD, int BS, bool F8>
 __global__ __launch_bounds__(64 * ATT_ROW_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void attention_row_kernel(
-    const uint16_t* __restrict__ q_hi, const uint16_t* __restrict__ q_lo, StepMeta m,
-    RowMaps maps, ModelDims md, int R, const void* __restrict__ pool_k,
-    const void* __restrict__ pool_v, uint16_t* __restrict__ out_hi, uint16_t* __restrict__ out_lo,
-    uint32_t* status) {
+    RopeAppendArgs ra, StepMeta m, RowMaps maps, ModelDims md, int R,
+    uint16_t* __restrict__ out_hi, uint16_t* __restrict__ out_lo, uint32_t* status) {
   __shared__ int s_tbl[ATT_ROW_WAVES][ATT_TBL];
   __shared__ float s_ml[ATT_ROW_WAVES][ATT_ROW_G][2];
   __shared__ float s_o[ATT_ROW_WAVES][ATT_ROW_G][HD];
@@ -509,23 +513,40 @@ __global__ __launch_bounds__(64 * ATT_ROW_WAVES) __attribute__((amdgpu_waves_per
       *reinterpret_cast<uint4*>(out_lo + at) = make_uint4(0, 0, 0, 0);
     }
   };
+  // RoPE + append of row `row` for this KV head's slots: its G query heads,
+  // its K head and its V head.
+  auto rope_row = [&](int row) {
+    constexpr int half = HD / 2;
+    const int pos = maps.row_pos[row];
+    for (int t = threadIdx.x; t < (G + 2) * half; t += T) {
+      const int js = t / half;
+      const int j = js < G ? g * G + js : md.n_heads + (js - G) * md.n_kv_heads + g;
+      rope_append_one(ra, row, s, pos, j, t % half, status);
+    }
+  };
   if (s < R && maps.row_seq[s] < 0) zero_row(s);
   const int r = maps.seq_row0[s];
   const int nn = m.n_new[s];
   if (r < 0 || r >= R || maps.row_seq[r] != s) return;  // refused by prep (no rows to serve)
   if (nn != 1) {  // served rows, but more than one: not a decode row
     if (threadIdx.x == 0 && g == 0) raise_status(status, ST_BAD_SHAPE);
-    for (int i = 0; i < nn && r + i < R; ++i) zero_row(r + i);
+    for (int i = 0; i < nn && r + i < R; ++i) {
+      rope_row(r + i);
+      zero_row(r + i);
+    }
     return;
   }
+  rope_row(r);
+  __syncthreads();  // the row's q, K and V stores before this workgroup reads them
   const int ctx = m.ctx_lens[s];
   const int n_steps = ceil_div(ctx + 1, 32);  // keys 0 .. ctx, the row's own included
   const int per = ceil_div(n_steps, ATT_ROW_WAVES);
   const int st0 = wave * per, st1 = min(n_steps, st0 + per);
   if (st0 < st1) {
     const SegLds out{&s_ml[wave][0][0], &s_o[wave][0][0]};
-    attend_segment<HD, BS, F8>(q_hi, q_lo, m, maps, md, pool_k, pool_v, out, status, s_tbl[wave],
-                               s, g, 0, 1, ctx, 32 * st0, min(ctx + 1, 32 * st1), 0, st1 - st0);
+    attend_segment<HD, BS, F8>(ra.q_hi, ra.q_lo, m, maps, md, ra.pool_k, ra.pool_v, out, status,
+                               s_tbl[wave], s, g, 0, 1, ctx, 32 * st0, min(ctx + 1, 32 * st1), 0,
+                               st1 - st0);
   }
   __syncthreads();
   const int n_used = ceil_div(n_steps, per);
@@ -947,20 +968,19 @@ static void launch_items(int blocks, const uint16_t* q_hi, const uint16_t* q_lo,
 }
 
 template <int HD, int BS>
-static void launch_rows(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R, const StepMeta& m,
-                        const RowMaps& maps, const ModelDims& md, const void* pool_k,
-                        const void* pool_v, uint16_t* out_hi, uint16_t* out_lo, uint32_t* status,
-                        hipStream_t st) {
+static void launch_rows(const RopeAppendArgs& ra, int32_t R, const StepMeta& m,
+                        const RowMaps& maps, const ModelDims& md, uint16_t* out_hi,
+                        uint16_t* out_lo, uint32_t* status, hipStream_t st) {
   const unsigned grid = (unsigned)(m.n_seqs * md.n_kv_heads);
   if constexpr (BS >= 8) {
     if (md.kv_fp8) {
       attention_row_kernel<HD, BS, true><<<grid, 64 * ATT_ROW_WAVES, 0, st>>>(
-          q_hi, q_lo, m, maps, md, R, pool_k, pool_v, out_hi, out_lo, status);
+          ra, m, maps, md, R, out_hi, out_lo, status);
       return;
     }
   }
   attention_row_kernel<HD, BS, false><<<grid, 64 * ATT_ROW_WAVES, 0, st>>>(
-      q_hi, q_lo, m, maps, md, R, pool_k, pool_v, out_hi, out_lo, status);
+      ra, m, maps, md, R, out_hi, out_lo, status);
 }
 
 // Dynamic LDS above 64 KB must be allowed per kernel before its first launch.
@@ -974,17 +994,7 @@ static hipError_t launch_hd(const uint16_t* q_hi, const uint16_t* q_lo, int32_t 
                             const AttnPlan& ap, const void* pool_k_, const void* pool_v_,
                             float* part_ml, float* part_o, uint16_t* out_hi, uint16_t* out_lo,
                             uint32_t* status, hipStream_t st) {
-  if (ap.row_kernel) {
-    switch (md.block_size) {
-      case 4: launch_rows<HD, 4>(q_hi, q_lo, R, m, maps, md, pool_k_, pool_v_, out_hi, out_lo, status, st); break;
-      case 8: launch_rows<HD, 8>(q_hi, q_lo, R, m, maps, md, pool_k_, pool_v_, out_hi, out_lo, status, st); break;
-      case 16: launch_rows<HD, 16>(q_hi, q_lo, R, m, maps, md, pool_k_, pool_v_, out_hi, out_lo, status, st); break;
-      case 32: launch_rows<HD, 32>(q_hi, q_lo, R, m, maps, md, pool_k_, pool_v_, out_hi, out_lo, status, st); break;
-      case 64: launch_rows<HD, 64>(q_hi, q_lo, R, m, maps, md, pool_k_, pool_v_, out_hi, out_lo, status, st); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
+  if (ap.row_kernel) return hipErrorInvalidValue;  // launch_rope_attention_rows runs that plan
   // the block kernel reads a bf16 cache (an 8-bit cache plans no block items)
   const uint16_t* pool_k = static_cast<const uint16_t*>(pool_k_);
   const uint16_t* pool_v = static_cast<const uint16_t*>(pool_v_);
@@ -1024,6 +1034,35 @@ static hipError_t launch_hd(const uint16_t* q_hi, const uint16_t* q_lo, int32_t 
   attn_combine_kernel<HD><<<(pairs + per_block - 1) / per_block, 256, 0, st>>>(
       m, maps, md, ap, R, part_ml, part_o, out_hi, out_lo);
   return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t launch_rows_hd(const RopeAppendArgs& ra, int32_t R, const StepMeta& m,
+                                 const RowMaps& maps, const ModelDims& md, uint16_t* out_hi,
+                                 uint16_t* out_lo, uint32_t* status, hipStream_t st) {
+  switch (md.block_size) {
+    case 4: launch_rows<HD, 4>(ra, R, m, maps, md, out_hi, out_lo, status, st); break;
+    case 8: launch_rows<HD, 8>(ra, R, m, maps, md, out_hi, out_lo, status, st); break;
+    case 16: launch_rows<HD, 16>(ra, R, m, maps, md, out_hi, out_lo, status, st); break;
+    case 32: launch_rows<HD, 32>(ra, R, m, maps, md, out_hi, out_lo, status, st); break;
+    case 64: launch_rows<HD, 64>(ra, R, m, maps, md, out_hi, out_lo, status, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_attention_rows(float* qkv, const float* part, int32_t S, int32_t R,
+                                      const StepMeta& m, const RowMaps& maps,
+                                      const double* rope_cs, const ModelDims& md,
+                                      const AttnPlan& ap, uint16_t* q_hi, uint16_t* q_lo,
+                                      void* pool_k, void* pool_v, uint16_t* out_hi,
+                                      uint16_t* out_lo, uint32_t* status, hipStream_t st) {
+  if (R <= 0) return hipSuccess;
+  if (!ap.row_kernel || R != m.n_seqs) return hipErrorInvalidValue;
+  const RopeAppendArgs ra =
+      rope_append_args(qkv, part, S, R, m, rope_cs, md, q_hi, q_lo, pool_k, pool_v);
+  if (md.head_dim == 128) return launch_rows_hd<128>(ra, R, m, maps, md, out_hi, out_lo, status, st);
+  return launch_rows_hd<64>(ra, R, m, maps, md, out_hi, out_lo, status, st);
 }
 
 hipError_t launch_attention(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R,

@@ -546,15 +546,23 @@ static int enqueue_step(cbd_engine* e, const cbd_step* s, float* logits_out, int
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
     HIP_TRY(launch_gemm(g, st));
     HIP_TRY(e->prof_mark(CBD_KERNEL_QKV, st));
-    HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
-    HIP_TRY(launch_rope_append(qkv, gpart, splits, R, m, maps, e->wsp<double>(e->ws.rope), e->md,
-                               q, q_lo, e->pool_k(l), e->pool_v(l), status, st));
-    HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
-    HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
-    HIP_TRY(launch_attention(q, q_lo, R, m, maps, e->md, ap, e->pool_k(l), e->pool_v(l),
-                             e->wsp<float>(e->ws.attn_ml), e->wsp<float>(e->ws.attn_o), attn,
-                             attn_lo, status, st));
-    HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
+    if (ap.row_kernel) {  // RoPE/append fused into the attention row kernel (timed as attention)
+      HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
+      HIP_TRY(launch_rope_attention_rows(qkv, gpart, splits, R, m, maps, e->wsp<double>(e->ws.rope),
+                                         e->md, ap, q, q_lo, e->pool_k(l), e->pool_v(l), attn,
+                                         attn_lo, status, st));
+      HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
+    } else {
+      HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
+      HIP_TRY(launch_rope_append(qkv, gpart, splits, R, m, maps, e->wsp<double>(e->ws.rope),
+                                 e->md, q, q_lo, e->pool_k(l), e->pool_v(l), status, st));
+      HIP_TRY(e->prof_mark(CBD_KERNEL_ROPE, st));
+      HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
+      HIP_TRY(launch_attention(q, q_lo, R, m, maps, e->md, ap, e->pool_k(l), e->pool_v(l),
+                               e->wsp<float>(e->ws.attn_ml), e->wsp<float>(e->ws.attn_o), attn,
+                               attn_lo, status, st));
+      HIP_TRY(e->prof_mark(CBD_KERNEL_ATTN, st));
+    }
     g.X = attn; g.Xlo = attn_lo; g.K = qd; g.W = e->packed + e->pl.o[l]; g.N = c.d_model;
     g.epi = EPI_RESID; g.Y = x;
     g.Ws = scales8(e->pl.o[l], c.d_model, qd);

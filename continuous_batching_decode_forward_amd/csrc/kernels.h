@@ -118,11 +118,24 @@ hipError_t launch_rope_append(float* qkv, const float* part, int32_t S, int32_t 
 
 // Paged GQA attention for every row (decode rows and prefill chunks), split
 // over keys, then the split combine into out [R][n_heads*head_dim] (split).
+// Not for a plan that takes the row kernel (ap.row_kernel): see below.
 hipError_t launch_attention(const uint16_t* q_hi, const uint16_t* q_lo, int32_t R,
                             const StepMeta& m, const RowMaps& maps, const ModelDims& md,
                             const AttnPlan& ap, const void* pool_k, const void* pool_v,
                             float* part_ml, float* part_o, uint16_t* out_hi, uint16_t* out_lo,
                             uint32_t* status, hipStream_t st);
+
+// Decode-only steps whose plan takes the row kernel (ap.row_kernel): the
+// step's RoPE + KV append and attention in one launch. Workgroup (sequence,
+// KV head g) rotates and appends its row's K and V of head g and its G
+// query heads (what launch_rope_append does for them), then attends over
+// the sequence's keys, merging its waves' results in LDS.
+hipError_t launch_rope_attention_rows(float* qkv, const float* part, int32_t S, int32_t R,
+                                      const StepMeta& m, const RowMaps& maps,
+                                      const double* rope_cs, const ModelDims& md,
+                                      const AttnPlan& ap, uint16_t* q_hi, uint16_t* q_lo,
+                                      void* pool_k, void* pool_v, uint16_t* out_hi,
+                                      uint16_t* out_lo, uint32_t* status, hipStream_t st);
 
 // --------------------------------------------------------------------- GEMM
 

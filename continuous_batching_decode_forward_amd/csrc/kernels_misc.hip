@@ -5,6 +5,7 @@
 #include "attn_sched.h"
 #include "common.h"
 #include "kernels.h"
+#include "rope_append.h"
 
 namespace cbd {
 
@@ -371,101 +372,30 @@ hipError_t launch_resid_norm(float* x, const float* part, int32_t S, int32_t R,
 
 // ------------------------------------------------------- RoPE + KV append
 //
-// Block (hd/2, 4): x = pair index i (element i pairs with i + hd/2), y = one
-// of four head slots. Head slots 0..Hq-1 are query heads (rotated into
-// q_out, split), then Hkv key heads (rotated, rounded to bf16 into the K
-// tile [block][kvh][pos % bs][hd]) and Hkv value heads (rounded to bf16,
-// dimension-major, into the V tile [block][kvh][hd][pos % bs]). The rotation
-// reads a host-built fp64 table of (cos, sin) per (position, i) and is
-// evaluated in fp64, so a cached key is its exact rotation rounded once.
+// Block (hd/2, 4): x = pair index i, y = one of four head slots of row r;
+// each thread does one element pair (rope_append.h: the QKV split-K sum, the
+// rotation in fp64, the query split into hi and lo planes, the K/V rounded
+// once into the sequence's block).
 
-__global__ void rope_append_kernel(float* __restrict__ qkv, const float* __restrict__ part, int S,
-                                   int R,
-                                   const int32_t* __restrict__ row_seq,
-                                   const int32_t* __restrict__ row_pos,
-                                   const int32_t* __restrict__ tables, int max_blocks_per_seq,
-                                   const double2* __restrict__ rope_cs, int hq, int hkv, int hd,
-                                   int bs, int num_blocks, uint16_t* __restrict__ q_hi,
-                                   uint16_t* __restrict__ q_lo, void* __restrict__ pool_k,
-                                   void* __restrict__ pool_v, int kv_fp8, float k_scale,
-                                   float v_scale, uint32_t* status) {
-  const int slots = hq + 2 * hkv;
+__global__ void rope_append_kernel(RopeAppendArgs a, const int32_t* __restrict__ row_seq,
+                                   const int32_t* __restrict__ row_pos, uint32_t* status) {
+  const int slots = a.hq + 2 * a.hkv;
   const int groups = (slots + 3) / 4;
   const int r = blockIdx.x / groups;
   const int j = (blockIdx.x % groups) * 4 + threadIdx.y;
-  const int i = threadIdx.x;
-  const int half = hd >> 1;
-  if (r >= R || j >= slots) return;
+  if (r >= a.R || j >= slots) return;
   const int s = row_seq[r];
   if (s < 0) return;
-  const int pos = row_pos[r];
-  float* src = qkv + (size_t)r * slots * hd + (size_t)j * hd;
-  float a, b;
-  if (S > 1) {  // the projection's split partials, summed in split order
-    const size_t stride = (size_t)R * slots * hd;
-    const float* p = part + (size_t)r * slots * hd + (size_t)j * hd;
-    a = p[i];
-    b = p[i + half];
-    for (int k = 1; k < S; ++k) {
-      a += p[k * stride + i];
-      b += p[k * stride + i + half];
-    }
-    src[i] = a;  // the projection itself, for inspection
-    src[i + half] = b;
-  } else {
-    a = src[i];
-    b = src[i + half];
-  }
-  if (j < hq + hkv) {
-    const double2 cs = rope_cs[(size_t)pos * half + i];
-    const double da = a, db = b;
-    // fp64 -> fp32 -> bf16 for keys: the double rounding can only matter
-    // within 2^-29 of a bf16 halfway point.
-    a = (float)(da * cs.x - db * cs.y);
-    b = (float)(db * cs.x + da * cs.y);
-  }
-  if (j < hq) {
-    const size_t at = (size_t)r * hq * hd + (size_t)j * hd;
-    bf16_t h, l;
-    split_bf(a, h, l);
-    q_hi[at + i] = h;
-    q_lo[at + i] = l;
-    split_bf(b, h, l);
-    q_hi[at + i + half] = h;
-    q_lo[at + i + half] = l;
-    return;
-  }
-  const int blk = tables[(size_t)s * max_blocks_per_seq + pos / bs];
-  if (blk < 0 || blk >= num_blocks) {
-    if (i == 0) raise_status(status, ST_BAD_BLOCK);
-    return;
-  }
-  const int off = pos % bs;
-  if (kv_fp8) {  // E4M3 codes of value / scale
-    if (j < hq + hkv) {
-      const int g = j - hq;
-      uint8_t* dst = static_cast<uint8_t*>(pool_k) + (((size_t)blk * hkv + g) * bs + off) * hd;
-      dst[i] = f2e4m3(a / k_scale);
-      dst[i + half] = f2e4m3(b / k_scale);
-    } else {
-      const int g = j - hq - hkv;
-      uint8_t* dst = static_cast<uint8_t*>(pool_v) + ((size_t)blk * hkv + g) * hd * bs + off;
-      dst[(size_t)i * bs] = f2e4m3(a / v_scale);
-      dst[(size_t)(i + half) * bs] = f2e4m3(b / v_scale);
-    }
-    return;
-  }
-  if (j < hq + hkv) {
-    const int g = j - hq;
-    uint16_t* dst = static_cast<uint16_t*>(pool_k) + (((size_t)blk * hkv + g) * bs + off) * hd;
-    dst[i] = f2bf(a);
-    dst[i + half] = f2bf(b);
-  } else {
-    const int g = j - hq - hkv;
-    uint16_t* dst = static_cast<uint16_t*>(pool_v) + ((size_t)blk * hkv + g) * hd * bs + off;
-    dst[(size_t)i * bs] = f2bf(a);
-    dst[(size_t)(i + half) * bs] = f2bf(b);
-  }
+  rope_append_one(a, r, s, row_pos[r], j, threadIdx.x, status);
+}
+
+RopeAppendArgs rope_append_args(float* qkv, const float* part, int32_t S, int32_t R,
+                                const StepMeta& m, const double* rope_cs, const ModelDims& md,
+                                uint16_t* q_hi, uint16_t* q_lo, void* pool_k, void* pool_v) {
+  return RopeAppendArgs{qkv, part, S, R, reinterpret_cast<const double2*>(rope_cs),
+                        m.block_tables, m.max_blocks_per_seq, md.n_heads, md.n_kv_heads,
+                        md.head_dim, md.block_size, md.num_blocks, q_hi, q_lo, pool_k, pool_v,
+                        md.kv_fp8, md.k_scale, md.v_scale};
 }
 
 hipError_t launch_rope_append(float* qkv, const float* part, int32_t S, int32_t R,
@@ -477,10 +407,8 @@ hipError_t launch_rope_append(float* qkv, const float* part, int32_t S, int32_t 
   const int groups = (slots + 3) / 4;
   dim3 block(md.head_dim / 2, 4);
   rope_append_kernel<<<R * groups, block, 0, st>>>(
-      qkv, part, S, R, maps.row_seq, maps.row_pos, m.block_tables, m.max_blocks_per_seq,
-      reinterpret_cast<const double2*>(rope_cs), md.n_heads, md.n_kv_heads, md.head_dim,
-      md.block_size, md.num_blocks, q_hi, q_lo, pool_k, pool_v, md.kv_fp8, md.k_scale,
-      md.v_scale, status);
+      rope_append_args(qkv, part, S, R, m, rope_cs, md, q_hi, q_lo, pool_k, pool_v), maps.row_seq,
+      maps.row_pos, status);
   return hipGetLastError();
 }
 
